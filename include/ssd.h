@@ -1,0 +1,155 @@
+/*
+ * ssd.h -- C ABI of libssd.so: the forward pass of the SSD (state space
+ * duality) layer of Mamba-2 on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as published):
+ *   [T] "Transformers是SSMs：通过结构化状态空间对偶性的广义模型和高效算法(一)"
+ *       (nxbn.cn/automobile/1783.html): sections 1-5 of "Transformers are SSMs".
+ *   [M] "LLM(十一)——Mamba" (mztchaoqun.com.cn/posts/D49_Mamba).
+ *
+ * The operation ([T] §2.4 recurrent form and §5.1; [M] §3.1.2): for every
+ * sequence and head h, with a_t = exp(dt_t * A_h),
+ *     h_t = a_t * h_{t-1} + x_t (outer) B_t       (state (P, N), zero before
+ *                                                   the first token)
+ *     y_t = h_t . C_t                              (P values)
+ * computed exactly (up to rounding) by the chunked block decomposition of the
+ * 1-semiseparable matrix M = L o (C B^T) of [M] §3.5: diagonal blocks in the
+ * quadratic (attention-like) form, chunk states, a scan that passes states
+ * between chunks, and a state-to-output product.  Head h reads B/C group
+ * g = h * G / H (G divides H; [M] §3.6.2 grouped heads).  The first token's
+ * a_t of every sequence multiplies a zero state and has no effect.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *     and dense.  x, B, C, y and final_state must be 16-byte aligned; dt,
+ *     A_head and cu_seqlens 4-byte aligned.  y must not alias an input.
+ *   - Element dtype (x, B, C, y): SSD_DTYPE_F32 or SSD_DTYPE_BF16.  dt, A_head
+ *     and final_state are always fp32.  Accumulation is fp32; on the bf16 path
+ *     the matrix-core operands (masked C B^T tiles, passed states) are rounded
+ *     to bf16, y is rounded to bf16 by round-to-nearest-even.
+ *   - dt * A_h <= 0 is expected (a_t in (0, 1], [T] §2.4); inputs must be
+ *     finite, else results are undefined.
+ *   - Supported shapes: headdim P = 64; dstate N in {16, 32, 64, 128, 256};
+ *     chunk_len Q in {64, 128, 256}, minus the (dtype, Q, N) pairs whose tiles
+ *     exceed the 160 KB of LDS per workgroup (ssd_config_supported tells).
+ *     Any sequence length >= 0; a partial last chunk is handled.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation failure nothing is written and no HIP call is made.
+ *   - Execution is asynchronous on `stream` (a hipStream_t, NULL = default
+ *     stream) with no host synchronisation.  Workspace is taken with
+ *     hipMallocAsync from the device's default memory pool and released with
+ *     hipFreeAsync on the same stream.  Errors of kernels that already ran
+ *     surface at the caller's next synchronisation, as for any stream work.
+ *   - Re-entrant: no global state except the optional kernel timing below.
+ *   - Return value: SSD_OK or an error code; nothing is thrown or aborted.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, H % G != 0 */
+  SSD_ERR_UNSUPPORTED = 2,      /* shape/dtype outside the built set, or not a gfx950 device */
+  SSD_ERR_HIP = 3,              /* a HIP runtime call or kernel launch failed */
+  SSD_ERR_OUT_OF_MEMORY = 4     /* workspace allocation failed */
+} ssd_status;
+
+typedef enum ssd_dtype { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
+
+/*
+ * Batched forward: `batch` sequences of `seqlen` tokens each.
+ *   x           (batch, seqlen, nheads, headdim)  element dtype
+ *   dt          (batch, seqlen, nheads)           fp32, step sizes
+ *   A_head      (nheads)                          fp32, a_t = exp(dt * A_head)
+ *   B, C        (batch, seqlen, ngroups, dstate)  element dtype
+ *   chunk_len   Q of the block decomposition ([M] §3.5: Q x Q blocks of M)
+ *   y           (batch, seqlen, nheads, headdim)  element dtype, overwritten
+ *   final_state (batch, nheads, headdim, dstate)  fp32, state after the last
+ *               token ([M] §3.5.2 center factors; listing's bchpn order), or
+ *               NULL to skip.  seqlen == 0 gives a zero final state.
+ */
+ssd_status ssd_chunked_fwd(const void* x, const float* dt, const float* A_head,
+                           const void* B, const void* C, int64_t batch, int64_t seqlen,
+                           int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                           int32_t chunk_len, ssd_dtype dtype, void* y, float* final_state,
+                           void* stream);
+
+/*
+ * Variable-length forward ([M] §3.7.3: the batch is one packed sequence with
+ * the state reset at every boundary, no padding).
+ *   x           (total_len, nheads, headdim)
+ *   dt          (total_len, nheads)
+ *   B, C        (total_len, ngroups, dstate)
+ *   cu_seqlens  (nseqs + 1) int32 DEVICE array: cu[0] = 0, non-decreasing,
+ *               cu[nseqs] = total_len.  Sequence s is tokens [cu[s], cu[s+1]);
+ *               it starts from a zero state.  Read on the device only (no
+ *               host copy).  Invalid contents give unspecified y but every
+ *               access stays inside the buffers sized above.
+ *   y           (total_len, nheads, headdim)
+ *   final_state (nseqs, nheads, headdim, dstate) fp32 or NULL; an empty
+ *               sequence gets a zero state.
+ */
+ssd_status ssd_chunked_fwd_varlen(const void* x, const float* dt, const float* A_head,
+                                  const void* B, const void* C, const int32_t* cu_seqlens,
+                                  int64_t nseqs, int64_t total_len, int32_t nheads,
+                                  int32_t headdim, int32_t dstate, int32_t ngroups,
+                                  int32_t chunk_len, ssd_dtype dtype, void* y,
+                                  float* final_state, void* stream);
+
+/*
+ * The same pass, also copying the intermediates of the block decomposition
+ * ([M] §3.5.2 "SSD algorithm: chunking and state passing") into caller
+ * buffers, for checking each kernel on its own.  cu_seqlens == NULL selects
+ * the batched form (nseqs sequences of total_len / nseqs tokens).  Chunks are
+ * numbered in packed order, ceil(len_s / Q) per sequence; K_slots =
+ * ssd_chunk_slots(...).  Each output may be NULL.
+ *   acs    (K_slots, nheads, Q)  fp32: chunk-local inclusive cumsum of dt*A
+ *          (entries past a partial chunk's end repeat its last value)
+ *   states (K_slots, nheads, headdim, dstate) fp32: chunk state from a zero
+ *          initial state ([M] §3.5.2 right factors)
+ *   hin    (K_slots, nheads, headdim, dstate) fp32: state entering the chunk
+ *          ([M] §3.5.2 center factors), as the output kernel reads it (bf16
+ *          values on the bf16 path)
+ * Slots past the real chunk count are left unwritten.
+ */
+ssd_status ssd_chunked_fwd_intermediates(const void* x, const float* dt, const float* A_head,
+                                         const void* B, const void* C,
+                                         const int32_t* cu_seqlens, int64_t nseqs,
+                                         int64_t total_len, int32_t nheads, int32_t headdim,
+                                         int32_t dstate, int32_t ngroups, int32_t chunk_len,
+                                         ssd_dtype dtype, void* y, float* final_state,
+                                         float* acs, float* states, float* hin, void* stream);
+
+/* Chunk slots the intermediates use: nseqs * ceil(total_len / nseqs / Q) for the
+ * batched form (varlen == 0), ceil(total_len / Q) + nseqs for varlen. */
+int64_t ssd_chunk_slots(int64_t nseqs, int64_t total_len, int32_t chunk_len, int32_t varlen);
+
+/* 1 if (dtype, dstate, chunk_len) is in the built set for headdim 64, else 0. */
+int32_t ssd_config_supported(ssd_dtype dtype, int32_t dstate, int32_t chunk_len);
+
+/* Human-readable name of a status code (static string). */
+const char* ssd_status_string(ssd_status status);
+
+/*
+ * Optional per-kernel timing (process-wide, off by default).  While enabled,
+ * every launch is bracketed by two HIP events recorded on the launch stream.
+ * ssd_kernel_timing_read synchronises those events, adds their elapsed times
+ * to per-kernel totals and, if reset != 0, clears the totals afterwards.
+ * kernel ids: 0 sequence table, 1 chunk cumsum, 2 chunk states, 3 state
+ * passing, 4 chunk output.  Not re-entrant with concurrent forward calls.
+ */
+ssd_status ssd_kernel_timing_enable(int32_t enable);
+ssd_status ssd_kernel_timing_read(int32_t kernel, double* total_ms, int64_t* launches,
+                                  int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

@@ -1,0 +1,220 @@
+"""ctypes binding of libssd.so (include/ssd.h) for torch tensors.
+
+Argument marshalling only: shapes and dtypes are checked, outputs allocated
+with torch on the input's device, and the C entry point is called on torch's
+current stream.  Every step of the forward pass runs in the library's HIP
+kernels; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssd.so")
+_lib = None
+
+SSD_OK = 0
+SSD_DTYPE_F32 = 0
+SSD_DTYPE_BF16 = 1
+_STATUS = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARGUMENT", 2: "SSD_ERR_UNSUPPORTED",
+           3: "SSD_ERR_HIP", 4: "SSD_ERR_OUT_OF_MEMORY"}
+
+# Every function include/ssd.h declares, with its ctypes signature.
+_vp, _fp, _i32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+_i64, _i32 = ctypes.c_int64, ctypes.c_int32
+SIGNATURES = {
+    "ssd_chunked_fwd": ([_vp, _fp, _fp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                         _i32, _vp, _fp, _vp], ctypes.c_int),
+    "ssd_chunked_fwd_varlen": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _vp, _fp, _vp], ctypes.c_int),
+    "ssd_chunked_fwd_intermediates": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32,
+                                       _i32, _i32, _i32, _i32, _vp, _fp, _fp, _fp, _fp, _vp],
+                                      ctypes.c_int),
+    "ssd_chunk_slots": ([_i64, _i64, _i32, _i32], ctypes.c_int64),
+    "ssd_config_supported": ([_i32, _i32, _i32], ctypes.c_int32),
+    "ssd_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "ssd_kernel_timing_enable": ([_i32], ctypes.c_int),
+    "ssd_kernel_timing_read": ([_i32, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_int64), _i32], ctypes.c_int),
+}
+
+KERNEL_NAMES = ["seq_table", "chunk_cumsum", "chunk_state", "state_pass", "chunk_output"]
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise SSDError(-1, f"libssd.so not built at {_LIB_PATH} "
+                               "(run python -m mamba_ssd_layer_amd.build)")
+        l = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = l
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != SSD_OK:
+        raise SSDError(rc, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSD_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SSD_DTYPE_F32
+    raise TypeError("x/B/C must be bfloat16 or float32")
+
+
+def _need(t: torch.Tensor, name: str, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def ssd_chunked_fwd(x, dt, A_head, B, C, chunk_len: int, y=None, final_state=None,
+                    return_final_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Batched SSD forward. x (b,T,H,P), dt (b,T,H) fp32, A_head (H,) fp32,
+    B/C (b,T,G,N) in x's dtype.  Returns (y (b,T,H,P), final_state (b,H,P,N) fp32 or None)."""
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, nheads, headdim)")
+    b, T, H, P = x.shape
+    G, N = B.shape[-2:]
+    dev = x.device
+    _need(x, "x", x.dtype, dev)
+    _need(dt, "dt", torch.float32, dev)
+    _need(A_head, "A_head", torch.float32, dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev)
+    if tuple(dt.shape) != (b, T, H) or tuple(A_head.shape) != (H,) or \
+            tuple(B.shape) != (b, T, G, N) or tuple(C.shape) != (b, T, G, N):
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, dev)
+        if y.shape != x.shape:
+            raise ValueError("y must have x's shape")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, dev)
+        if tuple(final_state.shape) != (b, H, P, N):
+            raise ValueError("final_state must be (b,H,P,N)")
+    rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), b, T, H, P, N,
+                               G, int(chunk_len), _dtype_code(x), _ptr(y), _ptr(final_state),
+                               ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_chunked_fwd")
+    return y, final_state
+
+
+def ssd_chunked_fwd_varlen(x, dt, A_head, B, C, cu_seqlens, chunk_len: int, y=None,
+                           final_state=None, return_final_state: bool = True):
+    """Packed variable-length SSD forward. x (Ttot,H,P), dt (Ttot,H), B/C (Ttot,G,N),
+    cu_seqlens (S+1,) int32 on the device.  Returns (y, final_state (S,H,P,N) or None)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (total_len, nheads, headdim)")
+    Tt, H, P = x.shape
+    G, N = B.shape[-2:]
+    dev = x.device
+    _need(x, "x", x.dtype, dev)
+    _need(dt, "dt", torch.float32, dev)
+    _need(A_head, "A_head", torch.float32, dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    S = cu_seqlens.shape[0] - 1
+    if tuple(dt.shape) != (Tt, H) or tuple(B.shape) != (Tt, G, N) or tuple(C.shape) != (Tt, G, N):
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    rc = lib().ssd_chunked_fwd_varlen(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C),
+                                      _ptr(cu_seqlens), S, Tt, H, P, N, G, int(chunk_len),
+                                      _dtype_code(x), _ptr(y), _ptr(final_state),
+                                      ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_chunked_fwd_varlen")
+    return y, final_state
+
+
+def ssd_chunked_fwd_intermediates(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None):
+    """Forward pass that also returns the per-chunk intermediates (fp32):
+    acs (K,H,Q), states (K,H,P,N), hin (K,H,P,N), with K = chunk slots.
+    Batched inputs (4-D x) or packed inputs with cu_seqlens."""
+    dev = x.device
+    if x.dim() == 4:
+        b, T = x.shape[:2]
+        S, Tt = b, b * T
+        varlen = 0
+    else:
+        Tt = x.shape[0]
+        S = cu_seqlens.shape[0] - 1
+        varlen = 1
+    H, P = x.shape[-2:]
+    G, N = B.shape[-2:]
+    Q = int(chunk_len)
+    K = int(lib().ssd_chunk_slots(S, Tt, Q, varlen))
+    y = torch.empty_like(x)
+    fs = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    acs = torch.full((K, H, Q), float("nan"), dtype=torch.float32, device=dev)
+    states = torch.full((K, H, P, N), float("nan"), dtype=torch.float32, device=dev)
+    hin = torch.full((K, H, P, N), float("nan"), dtype=torch.float32, device=dev)
+    rc = lib().ssd_chunked_fwd_intermediates(
+        _ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), _ptr(cu_seqlens) if varlen else None,
+        S, Tt, H, P, N, G, Q, _dtype_code(x), _ptr(y), _ptr(fs), _ptr(acs), _ptr(states),
+        _ptr(hin), ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_chunked_fwd_intermediates")
+    return dict(y=y, final_state=fs, acs=acs, states=states, hin=hin)
+
+
+def config_supported(dtype: torch.dtype, dstate: int, chunk_len: int) -> bool:
+    code = SSD_DTYPE_BF16 if dtype == torch.bfloat16 else SSD_DTYPE_F32
+    return bool(lib().ssd_config_supported(code, int(dstate), int(chunk_len)))
+
+
+def kernel_timing_enable(on: bool):
+    _check(lib().ssd_kernel_timing_enable(1 if on else 0), "ssd_kernel_timing_enable")
+
+
+def kernel_timing_read(reset: bool = True) -> dict:
+    """{kernel name: (total ms, launches)} of the timed launches since the last reset."""
+    out = {}
+    for k, name in enumerate(KERNEL_NAMES):
+        ms = ctypes.c_double(0.0)
+        n = ctypes.c_int64(0)
+        _check(lib().ssd_kernel_timing_read(k, ctypes.byref(ms), ctypes.byref(n), 1 if reset else 0),
+               "ssd_kernel_timing_read")
+        out[name] = (ms.value, n.value)
+    return out

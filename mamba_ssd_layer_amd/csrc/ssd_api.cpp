@@ -1,0 +1,344 @@
+// ssd_api.cpp -- the C ABI of libssd.so (declared in include/ssd.h).
+//
+// Host side only: argument validation (before any HIP call), workspace
+// layout, the launch sequence of the five kernels on the caller's stream, and
+// the optional per-kernel event timing.  The sequence follows the four steps of
+// the block decomposition in "LLM(十一)——Mamba" (mztchaoqun.com.cn) §3.5.2
+// "SSD algorithm: chunking and state passing", with the chunk tables first:
+//   K0 sequence table -> K1 chunk cumsum -> K3 chunk states -> K4 state passing
+//   -> K2+K5 diagonal blocks fused with state-to-output.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+#include <vector>
+
+#include "../../include/ssd.h"
+#include "ssd_internal.hpp"
+
+namespace ssd {
+
+bool chunk_state_supported(Dtype dt, int Q, int N);
+bool chunk_output_supported(Dtype dt, int Q, int N);
+hipError_t launch_state_pass_impl(const Problem& p, const Workspace& ws, float* hin_f32,
+                                  hipStream_t s);
+
+bool config_supported(Dtype dt, int Q, int N) {
+  return chunk_state_supported(dt, Q, N) && chunk_output_supported(dt, Q, N);
+}
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
+  const size_t S = (size_t)p.nseq, K = (size_t)p.kmax, H = (size_t)p.H;
+  const size_t PN = (size_t)p.P * p.N;
+  const size_t esz = p.dtype == Dtype::BF16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return base ? base + at : nullptr;
+  };
+  char* seq_off = take((S + 1) * sizeof(int32_t));
+  char* seq_start = take(S * sizeof(int64_t));
+  char* seq_len = take(S * sizeof(int64_t));
+  char* chunks = take(K * sizeof(ChunkDesc));
+  char* acs = take(K * H * p.Q * sizeof(float));
+  char* lam = take(K * H * sizeof(float));
+  char* states = take(K * H * PN * sizeof(float));
+  char* hin = take(K * H * PN * esz);
+  if (ws && base) {
+    ws->seq_off = reinterpret_cast<int32_t*>(seq_off);
+    ws->seq_start = reinterpret_cast<int64_t*>(seq_start);
+    ws->seq_len = reinterpret_cast<int64_t*>(seq_len);
+    ws->chunks = reinterpret_cast<ChunkDesc*>(chunks);
+    ws->acs = reinterpret_cast<float*>(acs);
+    ws->lam = reinterpret_cast<float*>(lam);
+    ws->states = reinterpret_cast<float*>(states);
+    ws->hin = hin;
+  }
+  return off;
+}
+
+// ------------------------------------------------------------ timing ----
+namespace {
+struct TimedLaunch {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_mu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_pending;
+std::vector<hipEvent_t> g_free_events;
+double g_total_ms[kNumKernels] = {0};
+int64_t g_launches[kNumKernels] = {0};
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
+  bool timing;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    timing = g_timing;
+  }
+  if (!timing) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    a = take_event();
+    b = take_event();
+  }
+  if (a == nullptr || b == nullptr) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_pending.push_back({kernel, a, b});
+  return hipSuccess;
+}
+}  // namespace
+
+// ----------------------------------------------------------- device check ----
+static ssd_status check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 gfx950, -1 other
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SSD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SSD_ERR_HIP;
+    known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (known[dev] == 1) {
+      // keep freed workspace cached in the default pool between calls
+      hipMemPool_t pool;
+      if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t thr = ~0ull;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+      }
+    }
+  }
+  return known[dev] == 1 ? SSD_OK : SSD_ERR_UNSUPPORTED;
+}
+
+static bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+// Validates everything that can be checked on the host.  No HIP call.
+static ssd_status validate(const Problem& p) {
+  if (p.H <= 0 || p.G <= 0 || p.H % p.G != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.P <= 0 || p.N <= 0 || p.Q <= 0 || p.nseq < 0 || p.total < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.dtype != Dtype::F32 && p.dtype != Dtype::BF16) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.P != kHeadDim) return SSD_ERR_UNSUPPORTED;
+  if (!(p.N == 16 || p.N == 32 || p.N == 64 || p.N == 128 || p.N == 256)) return SSD_ERR_UNSUPPORTED;
+  if (!(p.Q == 64 || p.Q == 128 || p.Q == 256)) return SSD_ERR_UNSUPPORTED;
+  if (!config_supported(p.dtype, p.Q, p.N)) return SSD_ERR_UNSUPPORTED;
+  if (p.A == nullptr || !aligned(p.A, 4)) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.total > 0) {
+    if (!p.x || !p.dt || !p.B || !p.C || !p.y) return SSD_ERR_INVALID_ARGUMENT;
+    if (!aligned(p.x, 16) || !aligned(p.B, 16) || !aligned(p.C, 16) || !aligned(p.y, 16) ||
+        !aligned(p.dt, 4))
+      return SSD_ERR_INVALID_ARGUMENT;
+  }
+  if (p.final_state && !aligned(p.final_state, 16)) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.cu && !aligned(p.cu, 4)) return SSD_ERR_INVALID_ARGUMENT;
+  // sizes must keep every index and grid inside 32/64-bit ranges
+  const int64_t lim = (int64_t)1 << 40;
+  if (p.total > lim || p.nseq > ((int64_t)1 << 30) || p.kmax > ((int64_t)1 << 30)) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.kmax * p.H > 0x7fffffffLL || p.nseq * p.H * 16 > 0x7fffffffLL) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.total * p.H * p.P > ((int64_t)1 << 46)) return SSD_ERR_INVALID_ARGUMENT;
+  return SSD_OK;
+}
+
+static ssd_status map_err(hipError_t e) {
+  if (e == hipSuccess) return SSD_OK;
+  if (e == hipErrorOutOfMemory) return SSD_ERR_OUT_OF_MEMORY;
+  return SSD_ERR_HIP;
+}
+
+struct DebugOut {
+  float* acs = nullptr;
+  float* states = nullptr;
+  float* hin = nullptr;
+};
+
+static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg) {
+  ssd_status st = validate(p);
+  if (st != SSD_OK) return st;
+  st = check_device();
+  if (st != SSD_OK) return st;
+  if (p.nseq == 0) return SSD_OK;
+  const size_t bytes = workspace_layout(p, nullptr, nullptr);
+  void* base = nullptr;
+  hipError_t e = hipMallocAsync(&base, bytes, stream);
+  if (e != hipSuccess || base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  Workspace ws;
+  workspace_layout(p, static_cast<char*>(base), &ws);
+  const size_t KH = (size_t)p.kmax * p.H;
+  const size_t PN = (size_t)p.P * p.N;
+  do {
+    e = timed_launch(kK0SeqTable, stream, [&] { return launch_seq_table(p, ws, stream); });
+    if (e != hipSuccess) break;
+    if (p.kmax > 0) {
+      e = timed_launch(kK1Cumsum, stream, [&] { return launch_chunk_cumsum(p, ws, stream); });
+      if (e != hipSuccess) break;
+      if (dbg && dbg->acs) {
+        e = hipMemcpyAsync(dbg->acs, ws.acs, KH * p.Q * sizeof(float), hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) break;
+      }
+      e = timed_launch(kK3ChunkState, stream, [&] { return launch_chunk_state(p, ws, stream); });
+      if (e != hipSuccess) break;
+      if (dbg && dbg->states) {
+        e = hipMemcpyAsync(dbg->states, ws.states, KH * PN * sizeof(float), hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) break;
+      }
+    }
+    e = timed_launch(kK4StatePass, stream, [&] {
+      return launch_state_pass_impl(p, ws, dbg ? dbg->hin : nullptr, stream);
+    });
+    if (e != hipSuccess) break;
+    if (p.kmax > 0) {
+      e = timed_launch(kK25ChunkOutput, stream, [&] { return launch_chunk_output(p, ws, stream); });
+      if (e != hipSuccess) break;
+    }
+  } while (false);
+  const hipError_t ef = hipFreeAsync(base, stream);
+  if (e != hipSuccess) return map_err(e);
+  return map_err(ef);
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace ssd
+
+using namespace ssd;
+
+extern "C" {
+
+int64_t ssd_chunk_slots(int64_t nseqs, int64_t total_len, int32_t chunk_len, int32_t varlen) {
+  if (nseqs <= 0 || total_len < 0 || chunk_len <= 0) return 0;
+  if (varlen) return ceil_div(total_len, chunk_len) + nseqs;
+  return nseqs * ceil_div(total_len / nseqs, chunk_len);
+}
+
+int32_t ssd_config_supported(ssd_dtype dtype, int32_t dstate, int32_t chunk_len) {
+  if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return 0;
+  return config_supported(static_cast<Dtype>(dtype), chunk_len, dstate) ? 1 : 0;
+}
+
+static Problem make_problem(const void* x, const float* dt, const float* A_head, const void* B,
+                            const void* C, const int32_t* cu, int64_t nseq, int64_t seqlen,
+                            int64_t total, int32_t nheads, int32_t headdim, int32_t dstate,
+                            int32_t ngroups, int32_t chunk_len, ssd_dtype dtype, void* y,
+                            float* final_state) {
+  Problem p;
+  p.x = x; p.dt = dt; p.A = A_head; p.B = B; p.C = C; p.cu = cu; p.y = y;
+  p.final_state = final_state;
+  p.nseq = nseq; p.seqlen = seqlen; p.total = total;
+  p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups; p.Q = chunk_len;
+  p.dtype = static_cast<Dtype>(dtype);
+  p.kmax = 0;
+  if (chunk_len > 0 && nseq >= 0 && total >= 0)
+    p.kmax = cu ? ceil_div(total, chunk_len) + nseq : nseq * ceil_div(seqlen, chunk_len);
+  return p;
+}
+
+ssd_status ssd_chunked_fwd(const void* x, const float* dt, const float* A_head, const void* B,
+                           const void* C, int64_t batch, int64_t seqlen, int32_t nheads,
+                           int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk_len,
+                           ssd_dtype dtype, void* y, float* final_state, void* stream) {
+  if (batch < 0 || seqlen < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return SSD_ERR_INVALID_ARGUMENT;
+  const Problem p = make_problem(x, dt, A_head, B, C, nullptr, batch, seqlen, batch * seqlen,
+                                 nheads, headdim, dstate, ngroups, chunk_len, dtype, y, final_state);
+  return run(p, static_cast<hipStream_t>(stream), nullptr);
+}
+
+ssd_status ssd_chunked_fwd_varlen(const void* x, const float* dt, const float* A_head,
+                                  const void* B, const void* C, const int32_t* cu_seqlens,
+                                  int64_t nseqs, int64_t total_len, int32_t nheads,
+                                  int32_t headdim, int32_t dstate, int32_t ngroups,
+                                  int32_t chunk_len, ssd_dtype dtype, void* y,
+                                  float* final_state, void* stream) {
+  if (nseqs < 0 || total_len < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (nseqs > 0 && cu_seqlens == nullptr) return SSD_ERR_INVALID_ARGUMENT;
+  const Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, 0, total_len, nheads,
+                                 headdim, dstate, ngroups, chunk_len, dtype, y, final_state);
+  return run(p, static_cast<hipStream_t>(stream), nullptr);
+}
+
+ssd_status ssd_chunked_fwd_intermediates(const void* x, const float* dt, const float* A_head,
+                                         const void* B, const void* C,
+                                         const int32_t* cu_seqlens, int64_t nseqs,
+                                         int64_t total_len, int32_t nheads, int32_t headdim,
+                                         int32_t dstate, int32_t ngroups, int32_t chunk_len,
+                                         ssd_dtype dtype, void* y, float* final_state,
+                                         float* acs, float* states, float* hin, void* stream) {
+  if (nseqs < 0 || total_len < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs > 0 && total_len % nseqs != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs == 0 && total_len != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if ((acs && !aligned(acs, 16)) || (states && !aligned(states, 16)) || (hin && !aligned(hin, 16)))
+    return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t seqlen = (cu_seqlens == nullptr && nseqs > 0) ? total_len / nseqs : 0;
+  const Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, seqlen, total_len, nheads,
+                                 headdim, dstate, ngroups, chunk_len, dtype, y, final_state);
+  DebugOut dbg;
+  dbg.acs = acs; dbg.states = states; dbg.hin = hin;
+  return run(p, static_cast<hipStream_t>(stream), &dbg);
+}
+
+const char* ssd_status_string(ssd_status status) {
+  switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_INVALID_ARGUMENT: return "SSD_ERR_INVALID_ARGUMENT";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    case SSD_ERR_OUT_OF_MEMORY: return "SSD_ERR_OUT_OF_MEMORY";
+  }
+  return "SSD_ERR_UNKNOWN";
+}
+
+ssd_status ssd_kernel_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing = enable != 0;
+  return SSD_OK;
+}
+
+ssd_status ssd_kernel_timing_read(int32_t kernel, double* total_ms, int64_t* launches,
+                                  int32_t reset) {
+  if (kernel < 0 || kernel >= kNumKernels) return SSD_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lk(g_mu);
+  ssd_status st = SSD_OK;
+  for (auto& t : g_pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess)
+      st = SSD_ERR_HIP;
+    g_total_ms[t.kernel] += ms;
+    g_launches[t.kernel] += 1;
+    g_free_events.push_back(t.start);
+    g_free_events.push_back(t.stop);
+  }
+  g_pending.clear();
+  if (total_ms) *total_ms = g_total_ms[kernel];
+  if (launches) *launches = g_launches[kernel];
+  if (reset) {
+    g_total_ms[kernel] = 0.0;
+    g_launches[kernel] = 0;
+  }
+  return st;
+}
+
+}  // extern "C"

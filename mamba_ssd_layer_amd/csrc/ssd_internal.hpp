@@ -1,0 +1,71 @@
+// ssd_internal.hpp -- problem description, workspace layout and kernel
+// launchers shared by the C-ABI (ssd_api.cpp) and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kHeadDim = 64;            // P: the head dim built (two MFMA tiles of 32)
+constexpr int kLdsLimit = 160 * 1024;   // LDS per workgroup on gfx950
+constexpr int kThreads = 256;           // 4 waves per workgroup in every SSD kernel
+
+enum class Dtype : int { F32 = 0, BF16 = 1 };
+
+// Chunk descriptor: sequence index (-1: slot unused), first packed token, length.
+struct ChunkDesc {
+  int32_t seq;
+  int32_t len;
+  int64_t t0;
+};
+
+// One forward problem.  The token axis is packed: a batched call with b
+// sequences of length T is the packed axis of b*T tokens, sequence s at
+// [s*T, (s+1)*T).  cu == nullptr selects that batched form.
+struct Problem {
+  const void* x;          // (Ttot, H, P)  element dtype
+  const float* dt;        // (Ttot, H)
+  const float* A;         // (H)
+  const void* B;          // (Ttot, G, N)  element dtype
+  const void* C;          // (Ttot, G, N)  element dtype
+  const int32_t* cu;      // (S+1) on the device, or nullptr (batched)
+  void* y;                // (Ttot, H, P)  element dtype
+  float* final_state;     // (S, H, P, N) or nullptr
+  int64_t nseq;           // S
+  int64_t seqlen;         // T (batched form only)
+  int64_t total;          // Ttot
+  int H, P, N, G, Q;
+  Dtype dtype;
+  int64_t kmax;           // chunk slots: exact when batched, a bound when varlen
+};
+
+// Device workspace, carved out of one allocation (256-byte aligned pieces).
+struct Workspace {
+  int32_t* seq_off = nullptr;    // (S+1) first chunk slot of each sequence; [S] = chunk count
+  int64_t* seq_start = nullptr;  // (S)   first token of each sequence (clamped to [0,Ttot])
+  int64_t* seq_len = nullptr;    // (S)   tokens of each sequence (clamped, >= 0)
+  ChunkDesc* chunks = nullptr;   // (kmax)
+  float* acs = nullptr;          // (kmax, H, Q) chunk-local cumsum of dt*A
+  float* lam = nullptr;          // (kmax, H)    its last entry (log of the chunk's decay)
+  float* states = nullptr;       // (kmax, H, P, N) chunk states, fp32
+  void* hin = nullptr;           // (kmax, H, P, N) state entering each chunk, element dtype
+};
+
+// Bytes of workspace for p; fills *ws from base when base != nullptr.
+size_t workspace_layout(const Problem& p, char* base, Workspace* ws);
+
+// Whether (dtype, Q, N) has an instantiated kernel set that fits in LDS.
+bool config_supported(Dtype dt, int Q, int N);
+
+// Kernel launchers; each returns the launch status.  Kernel ids for timing:
+enum KernelId { kK0SeqTable = 0, kK1Cumsum = 1, kK3ChunkState = 2, kK4StatePass = 3,
+                kK25ChunkOutput = 4, kNumKernels = 5 };
+hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
+hipError_t launch_chunk_cumsum(const Problem& p, const Workspace& ws, hipStream_t s);
+hipError_t launch_chunk_state(const Problem& p, const Workspace& ws, hipStream_t s);
+hipError_t launch_state_pass(const Problem& p, const Workspace& ws, hipStream_t s);
+hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s);
+
+}  // namespace ssd

@@ -1,0 +1,118 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+symbol include/ssd.h declares, and rejects invalid arguments on the host before
+any HIP call (so these calls are safe without a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mamba_ssd_layer_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+INVALID, UNSUPPORTED = 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.library_path()):
+        import mamba_ssd_layer_amd.build as b
+        b.build()
+    return bd.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in bd.SIGNATURES, f"binding lacks a signature for {n}"
+
+
+def test_status_strings(lib):
+    assert lib.ssd_status_string(0) == b"SSD_OK"
+    assert lib.ssd_status_string(2) == b"SSD_ERR_UNSUPPORTED"
+    assert lib.ssd_status_string(99) == b"SSD_ERR_UNKNOWN"
+
+
+def test_chunk_slots(lib):
+    assert lib.ssd_chunk_slots(8, 8 * 2048, 256, 0) == 64
+    assert lib.ssd_chunk_slots(2, 2 * 300, 256, 0) == 4
+    assert lib.ssd_chunk_slots(16, 34000, 256, 1) == (34000 + 255) // 256 + 16
+    assert lib.ssd_chunk_slots(0, 0, 256, 1) == 0
+
+
+def test_supported_set(lib):
+    # the benchmark workloads
+    assert lib.ssd_config_supported(1, 128, 256) == 1
+    assert lib.ssd_config_supported(1, 256, 128) == 1
+    assert lib.ssd_config_supported(0, 16, 64) == 1
+    # tiles that cannot fit in 160 KB of LDS
+    assert lib.ssd_config_supported(1, 256, 256) == 0
+    assert lib.ssd_config_supported(0, 128, 256) == 0
+    assert lib.ssd_config_supported(0, 48, 64) == 0
+    assert lib.ssd_config_supported(5, 128, 64) == 0
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def call_fwd(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, b=1, T=256, H=4, P=64, N=128, G=1, Q=256,
+             dtype=1, y=FAKE, fs=None)
+    a.update(kw)
+    return lib.ssd_chunked_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["b"], a["T"], a["H"],
+                               a["P"], a["N"], a["G"], a["Q"], a["dtype"], a["y"], a["fs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=3, G=2), INVALID),          # H % G != 0
+    (dict(G=0), INVALID),
+    (dict(H=0), INVALID),
+    (dict(b=-1), INVALID),
+    (dict(T=-5), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(P=128), UNSUPPORTED),
+    (dict(N=48), UNSUPPORTED),
+    (dict(Q=100), UNSUPPORTED),
+    (dict(Q=0), INVALID),
+    (dict(N=256, Q=256), UNSUPPORTED),  # LDS
+    (dict(x=FAKE + 4), INVALID),        # misaligned
+    (dict(y=FAKE + 8), INVALID),
+    (dict(fs=FAKE + 4), INVALID),
+    (dict(dt=FAKE + 2), INVALID),
+    (dict(x=None), INVALID),
+    (dict(A=None), INVALID),
+])
+def test_fwd_rejects_invalid_arguments(lib, kw, code):
+    assert call_fwd(lib, **kw) == code
+
+
+def test_varlen_rejects_invalid_arguments(lib):
+    # null cu_seqlens with sequences
+    assert lib.ssd_chunked_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 100, 4, 64, 128, 1,
+                                      256, 1, FAKE, None, None) == INVALID
+    # misaligned cu_seqlens
+    assert lib.ssd_chunked_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 2, 100, 4, 64, 128,
+                                      1, 256, 1, FAKE, None, None) == INVALID
+    assert lib.ssd_chunked_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 100, 4, 64, 128, 1,
+                                      256, 1, FAKE, None, None) == INVALID
+
+
+def test_intermediates_rejects_uneven_batch(lib):
+    assert lib.ssd_chunked_fwd_intermediates(FAKE, FAKE, FAKE, FAKE, FAKE, None, 3, 100, 4, 64, 128,
+                                             1, 256, 1, FAKE, None, None, None, None, None) == INVALID
+
+
+def test_timing_read_rejects_bad_kernel(lib):
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    assert lib.ssd_kernel_timing_read(9, ctypes.byref(ms), ctypes.byref(n), 0) == INVALID

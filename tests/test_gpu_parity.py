@@ -1,0 +1,180 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max relative L2 error over (sequence, head) slices <= 1e-5 for fp32
+inputs and <= 2e-2 for bf16 inputs (fp32 accumulation), for y and for the
+final state.  Inputs are the seeded synthetic workloads; the oracle reads the
+same cast values.  Every case names itself on stdout before it touches the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mamba_ssd_layer_amd import _binding as bd
+from mamba_ssd_layer_amd.workloads import WORKLOADS, Workload, make_inputs
+
+from gpu_common import TOL, check_parity, log, max_rel_l2, require_gpu, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+# ------------------------------------------------------------ workloads ----
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_fp32(dev, seed):
+    check_parity(make_inputs(WORKLOADS["tiny_fp32"], seed), dev, label=f"tiny_fp32 seed {seed}")
+
+
+@pytest.mark.parametrize("name", ["mamba2_2p7b_T2k", "large_state_T4k", "long_T16k", "varlen_16seq"])
+def test_full_workload_bf16(dev, name):
+    """The benchmark workloads at full size, in the launch configuration bench.py times."""
+    check_parity(make_inputs(WORKLOADS[name], 0), dev, label=f"{name} full bf16")
+
+
+@pytest.mark.parametrize("name,Q", [("mamba2_2p7b_T2k", 128), ("large_state_T4k", 64),
+                                    ("long_T16k", 128), ("varlen_16seq", 128)])
+def test_full_shape_fp32(dev, name, Q):
+    """The same shapes with fp32 inputs at 1e-5: a stronger check of state passing
+    than bf16 rounding allows (chunk sizes the fp32 tiles fit in LDS)."""
+    w = WORKLOADS[name].with_(dtype="f32", chunk_len=Q)
+    check_parity(make_inputs(w, 0), dev, label=f"{name} full fp32")
+
+
+# ------------------------------------------------------- shapes / edges ----
+SMALL = Workload("small", batch=2, seqlen=300, nheads=4, headdim=64, dstate=64, ngroups=2,
+                 chunk_len=64, dtype="bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("Q", [64, 128, 256])
+def test_ragged_shapes(dev, dtype, N, Q):
+    if not bd.config_supported(torch.bfloat16 if dtype == "bf16" else torch.float32, N, Q):
+        pytest.skip("(dtype, N, Q) outside the built set (LDS)")
+    w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=1000 if Q == 256 else 517)
+    check_parity(make_inputs(w, 3), dev, label=f"ragged {dtype} N={N} Q={Q}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 31, 33, 64, 65, 255, 257])
+def test_short_sequences(dev, T):
+    for dtype in ("f32", "bf16"):
+        w = SMALL.with_(dtype=dtype, seqlen=T, chunk_len=128, batch=3)
+        check_parity(make_inputs(w, T), dev, label=f"short T={T} {dtype}")
+
+
+def test_empty_batch_zero_state(dev):
+    log("[edge] seqlen 0")
+    w = SMALL.with_(seqlen=0, batch=2)
+    inp = make_inputs(w, 0)
+    d = to_device(inp, dev)
+    y, fs = bd.ssd_chunked_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], 64)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.all(fs == 0)
+
+
+def test_chunk_len_invariance(dev):
+    """y does not depend on the chunk length beyond rounding (the block
+    decomposition is exact for any partition)."""
+    w = SMALL.with_(dtype="f32", dstate=64, seqlen=777, batch=2)
+    inp = make_inputs(w, 11)
+    yr, fr = run_oracle(inp)
+    outs = []
+    for Q in (64, 128, 256):
+        log(f"[invariance] Q={Q}")
+        yg, fg = run_gpu(inp, dev, Q)
+        ey, ef = max_rel_l2(yg, yr, fg, fr, inp.packed_cu_seqlens())
+        assert ey < 1e-5 and ef < 1e-5
+        outs.append(yg)
+    assert np.max(np.abs(outs[0] - outs[2])) / np.max(np.abs(outs[0])) < 1e-5
+
+
+def test_varlen_equals_separate_runs(dev):
+    """Packed sequences (with empty ones) equal independent batched runs, bit for bit."""
+    lens = [300, 0, 1, 513, 64, 0, 77]
+    w = SMALL.with_(varlen=True, batch=len(lens), dstate=128, chunk_len=128, nheads=8, ngroups=2)
+    inp = make_inputs(w, 21, seqlens=lens)
+    log("[varlen] packed run")
+    yg, fg = run_gpu(inp, dev)
+    cu = inp.packed_cu_seqlens()
+    yr, fr = run_oracle(inp)
+    ey, ef = max_rel_l2(yg, yr, fg, fr, cu)
+    assert ey < 2e-2 and ef < 2e-2
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert np.all(fg[s] == 0)
+            continue
+        a, b = cu[s], cu[s + 1]
+        ws = w.with_(varlen=False, batch=1, seqlen=L)
+        from mamba_ssd_layer_amd.workloads import Inputs
+        one = Inputs(ws, inp.x[None, a:b], inp.dt[None, a:b], inp.A, inp.B[None, a:b], inp.C[None, a:b])
+        log(f"[varlen] sequence {s} alone (L={L})")
+        ys, fs = run_gpu(one, dev)
+        np.testing.assert_array_equal(ys[0], yg[a:b])
+        np.testing.assert_array_equal(fs[0], fg[s])
+
+
+def test_group_replication(dev):
+    """G = H with B, C replicated per head equals G = 1, bit for bit."""
+    w = SMALL.with_(ngroups=1, nheads=4, seqlen=400, dstate=128, chunk_len=128)
+    inp = make_inputs(w, 5)
+    log("[groups] G=1")
+    y1, f1 = run_gpu(inp, dev)
+    from mamba_ssd_layer_amd.workloads import Inputs
+    rep = Inputs(w.with_(ngroups=4), inp.x, inp.dt, inp.A, np.repeat(inp.B, 4, axis=2),
+                 np.repeat(inp.C, 4, axis=2))
+    log("[groups] G=H replicated")
+    y4, f4 = run_gpu(rep, dev)
+    np.testing.assert_array_equal(y1, y4)
+    np.testing.assert_array_equal(f1, f4)
+
+
+def test_decay_extremes(dev):
+    """a == 0 (dt*A = -1e4: y_t = (C_t.B_t) x_t) and a == 1 (A = 0: causal linear
+    attention, no decay at all, so state passing carries everything)."""
+    from mamba_ssd_layer_amd.workloads import Inputs
+    w = SMALL.with_(dtype="f32", seqlen=600, dstate=64, chunk_len=128, nheads=2, ngroups=1)
+    inp = make_inputs(w, 9)
+    z = Inputs(w, inp.x, np.full_like(inp.dt, 1e4), -np.ones_like(inp.A), inp.B, inp.C)
+    log("[extreme] a == 0")
+    yg, fg = run_gpu(z, dev)
+    cb = np.einsum("btgn,btgn->bt", inp.B, inp.C)
+    np.testing.assert_allclose(yg, cb[:, :, None, None] * inp.x, rtol=1e-4, atol=1e-4)
+    one = Inputs(w, inp.x * 0.05, inp.dt, np.zeros_like(inp.A), inp.B, inp.C)
+    log("[extreme] a == 1")
+    check_parity(one, dev, label="a == 1")
+
+
+def test_intermediates_match_chunked_reference(dev):
+    """Each kernel on its own: chunk cumsum, chunk states and passed states
+    against the oracle's four-step chunked reference."""
+    for dtype in ("f32", "bf16"):
+        lens = [200, 77, 0, 300]
+        w = SMALL.with_(dtype=dtype, varlen=True, batch=len(lens), dstate=32, chunk_len=64,
+                        nheads=4, ngroups=2)
+        inp = make_inputs(w, 4, seqlens=lens)
+        d = to_device(inp, dev)
+        log(f"[intermediates] {dtype}")
+        out = bd.ssd_chunked_fwd_intermediates(d["x"], d["dt"], d["A"], d["B"], d["C"], 64,
+                                               cu_seqlens=d["cu"])
+        torch.cuda.synchronize()
+        ref = oracle.chunked_steps(inp.x, inp.dt, inp.A, inp.B, inp.C, 64,
+                                   cu_seqlens=inp.packed_cu_seqlens())
+        K = ref["table"].shape[0]
+        acs = out["acs"][:K].cpu().numpy()
+        np.testing.assert_allclose(acs, ref["acs"], rtol=1e-5, atol=1e-5)
+        tol = 1e-5 if dtype == "f32" else 2e-2
+        st = out["states"][:K].cpu().numpy()
+        e = oracle.rel_l2_per_slice(st, ref["states"], slice_axes=(0, 1))
+        assert np.max(e) < tol, np.max(e)
+        hin = out["hin"][:K].cpu().numpy()
+        nz = np.array([np.any(ref["hin"][k] != 0) for k in range(K)])
+        assert np.all(hin[~nz] == 0)
+        e = oracle.rel_l2_per_slice(hin[nz], ref["hin"][nz], slice_axes=(0, 1))
+        assert np.max(e) < tol, np.max(e)
