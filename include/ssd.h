@@ -112,7 +112,8 @@ ssd_status ssd_chunked_fwd_varlen(const void* x, const float* dt, const float* A
  *   acs    (K_slots, nheads, Q)  fp32: chunk-local inclusive cumsum of dt*A
  *          (entries past a partial chunk's end repeat its last value)
  *   states (K_slots, nheads, headdim, dstate) fp32: chunk state from a zero
- *          initial state ([M] §3.5.2 right factors)
+ *          initial state ([M] §3.5.2 right factors), as stored for the state
+ *          passing (bf16 values on the bf16 path)
  *   hin    (K_slots, nheads, headdim, dstate) fp32: state entering the chunk
  *          ([M] §3.5.2 center factors), as the output kernel reads it (bf16
  *          values on the bf16 path)
@@ -141,8 +142,9 @@ const char* ssd_status_string(ssd_status status);
  * every launch is bracketed by two HIP events recorded on the launch stream.
  * ssd_kernel_timing_read synchronises those events, adds their elapsed times
  * to per-kernel totals and, if reset != 0, clears the totals afterwards.
- * kernel ids: 0 sequence table, 1 chunk cumsum, 2 chunk states, 3 state
- * passing, 4 chunk output.  Not re-entrant with concurrent forward calls.
+ * kernel ids: 0 sequence table (varlen calls only), 1 chunk cumsum + chunk
+ * states, 2 state passing, 3 chunk output (diagonal blocks + state-to-output).
+ * Not re-entrant with concurrent forward calls.
  */
 ssd_status ssd_kernel_timing_enable(int32_t enable);
 ssd_status ssd_kernel_timing_read(int32_t kernel, double* total_ms, int64_t* launches,

@@ -10,112 +10,131 @@
 // the final state.  [M] §3.5.3 prices this scan at T*N*P/Q work, a small part
 // of the whole.
 //
-// Design (gfx950): pure HBM streaming.  A thread owns 4 consecutive (p, n)
-// channels of one (sequence, head) and walks the sequence's chunks in order;
-// the loads of the next chunks' states are independent of the running state,
-// so they are issued ahead (unroll by 4) and only the FMA chain is serial.
-// Lanes of a wave cover 256 consecutive channels: every access is a fully
-// coalesced 16-byte (fp32) or 8-byte (bf16) vector.  Hin is written in the
-// element dtype: the output kernel feeds it to the matrix cores in that dtype.
+// Design (gfx950): pure HBM streaming, bound by how many bytes are in flight.
+// A thread owns 2 consecutive (p, n) channels of one (sequence, head) and walks
+// the sequence's chunks in order; the loads of later chunks' states do not
+// depend on the running state, so they are issued a block of 8 chunks ahead
+// and only the FMA chain is serial.  Lanes of a wave cover 128 consecutive
+// channels: every access is a fully coalesced 4-byte (bf16) or 8-byte (fp32)
+// vector.  Chunk states are read and
+// Hin is written in the element dtype (the output kernel feeds Hin to the
+// matrix cores in that dtype); the running state stays fp32.
 #include "ssd_device.hpp"
 
 namespace ssd {
 
+constexpr int kCh = 2;      // channels per thread
+constexpr int kDepth = 8;   // chunks per block; one block of loads is in flight ahead of the scan
+
 template <class E>
+__device__ __forceinline__ float2 load2(const typename E::storage* ptr) {
+  if constexpr (E::kBytes == 2) {
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(ptr);
+    return make_float2(bf16_lo(q), bf16_hi(q));
+  } else {
+    return *reinterpret_cast<const float2*>(ptr);
+  }
+}
+
+// Stores 2 channels in the element dtype; returns the stored values as fp32.
+template <class E>
+__device__ __forceinline__ float2 store2(typename E::storage* ptr, float2 v) {
+  if constexpr (E::kBytes == 2) {
+    const uint32_t o = pack_bf16x2(v.x, v.y);
+    *reinterpret_cast<uint32_t*>(ptr) = o;
+    return make_float2(bf16_lo(o), bf16_hi(o));
+  } else {
+    *reinterpret_cast<float2*>(ptr) = v;
+    return v;
+  }
+}
+
+template <class E, bool kDebug>
 __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspace ws,
                                                               float* __restrict__ hin_f32) {
+  using T = typename E::storage;
   const int PN = p.P * p.N;
-  const int cblocks = (PN + 4 * kThreads - 1) / (4 * kThreads);
+  const int cblocks = (PN + kCh * kThreads - 1) / (kCh * kThreads);
   const int64_t bid = blockIdx.x;
   const int cb = (int)(bid % cblocks);
   const int h = (int)((bid / cblocks) % p.H);
   const int64_t s = bid / ((int64_t)cblocks * p.H);
-  const int ch = (cb * kThreads + threadIdx.x) * 4;
+  const int ch = (cb * kThreads + threadIdx.x) * kCh;
   if (ch >= PN) return;
   const int H = p.H;
-  const int32_t k0 = ws.seq_off[s], k1 = ws.seq_off[s + 1];
-  float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
-  using T = typename E::storage;
-  T* hin = reinterpret_cast<T*>(ws.hin);
-  int32_t k = k0;
-  for (; k + 4 <= k1; k += 4) {
-    float4 sv[4];
-    float dec[4];
+  int64_t k0, k1;
+  seq_chunk_range(p, ws, s, &k0, &k1);
+  const int nk = (int)(k1 - k0);
+  const int stride = H * PN;  // elements between consecutive chunks of one head
+  // uniform (per-block) bases; the lane's own offset stays a 32-bit add
+  const int64_t blk0 = (k0 * H + h) * PN + (int64_t)cb * kThreads * kCh;
+  const int lo = threadIdx.x * kCh;
+  const T* st_in = reinterpret_cast<const T*>(ws.states) + blk0;
+  T* hin = reinterpret_cast<T*>(ws.hin) + blk0;
+  float* hin32 = kDebug ? hin_f32 + blk0 : nullptr;
+  const float* lam = ws.lam + k0 * H + h;
+  float2 st = make_float2(0.f, 0.f);
+  // Software pipeline over blocks of kDepth chunks with two register buffers
+  // used in turn (no copies between them): the loads of the next block are in
+  // flight while the current block is scanned, so only the FMA chain is serial.
+  float2 bufA[kDepth], bufB[kDepth];
+  float decA[kDepth], decB[kDepth];
+  // Loads are unconditional (indices past the end are clamped to the last
+  // chunk and never used) so that the loop body is straight-line code and each
+  // wait covers exactly the block it needs.
+  auto load_block = [&](int kb, float2 (&sv)[kDepth], float (&dec)[kDepth]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t base = ((int64_t)(k + u) * H + h) * PN + ch;
-      sv[u] = *reinterpret_cast<const float4*>(ws.states + base);
-      dec[u] = __expf(ws.lam[(int64_t)(k + u) * H + h]);
+    for (int u = 0; u < kDepth; ++u) {
+      const int kk = min(kb + u, nk - 1);
+      sv[u] = load2<E>(st_in + (int64_t)kk * stride + lo);
+      dec[u] = lam[(int64_t)kk * H];
     }
+  };
+  auto step = [&](int kk, float2 sv, float dec) {
+    const float2 r = store2<E>(hin + (int64_t)kk * stride + lo, st);
+    if constexpr (kDebug) *reinterpret_cast<float2*>(hin32 + (int64_t)kk * stride + lo) = r;
+    const float a = __expf(dec);
+    st.x = a * st.x + sv.x;
+    st.y = a * st.y + sv.y;
+  };
+  const int nfull = nk / kDepth;
+  if (nfull > 0) {
+    load_block(0, bufA, decA);
+    int b = 0;
+    for (; b + 2 <= nfull; b += 2) {
+      load_block((b + 1) * kDepth, bufB, decB);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t base = ((int64_t)(k + u) * H + h) * PN + ch;
-      if constexpr (E::kBytes == 2) {
-        uint2 o;
-        o.x = pack_bf16x2(st.x, st.y);
-        o.y = pack_bf16x2(st.z, st.w);
-        *reinterpret_cast<uint2*>(hin + base) = o;
-      } else {
-        *reinterpret_cast<float4*>(hin + base) = st;
-      }
-      if (hin_f32 != nullptr) {
-        if constexpr (E::kBytes == 2) {
-          float4 r;
-          r.x = bf16_lo(pack_bf16x2(st.x, st.y)); r.y = bf16_hi(pack_bf16x2(st.x, st.y));
-          r.z = bf16_lo(pack_bf16x2(st.z, st.w)); r.w = bf16_hi(pack_bf16x2(st.z, st.w));
-          *reinterpret_cast<float4*>(hin_f32 + base) = r;
-        } else {
-          *reinterpret_cast<float4*>(hin_f32 + base) = st;
-        }
-      }
-      st.x = dec[u] * st.x + sv[u].x;
-      st.y = dec[u] * st.y + sv[u].y;
-      st.z = dec[u] * st.z + sv[u].z;
-      st.w = dec[u] * st.w + sv[u].w;
+      for (int u = 0; u < kDepth; ++u) step(b * kDepth + u, bufA[u], decA[u]);
+      load_block((b + 2) * kDepth, bufA, decA);
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) step((b + 1) * kDepth + u, bufB[u], decB[u]);
+    }
+    if (b < nfull) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) step(b * kDepth + u, bufA[u], decA[u]);
     }
   }
-  for (; k < k1; ++k) {
-    const int64_t base = ((int64_t)k * H + h) * PN + ch;
-    const float4 sv = *reinterpret_cast<const float4*>(ws.states + base);
-    const float dec = __expf(ws.lam[(int64_t)k * H + h]);
-    if constexpr (E::kBytes == 2) {
-      uint2 o;
-      o.x = pack_bf16x2(st.x, st.y);
-      o.y = pack_bf16x2(st.z, st.w);
-      *reinterpret_cast<uint2*>(hin + base) = o;
-      if (hin_f32 != nullptr) {
-        float4 r;
-        r.x = bf16_lo(o.x); r.y = bf16_hi(o.x); r.z = bf16_lo(o.y); r.w = bf16_hi(o.y);
-        *reinterpret_cast<float4*>(hin_f32 + base) = r;
-      }
-    } else {
-      *reinterpret_cast<float4*>(hin + base) = st;
-      if (hin_f32 != nullptr) *reinterpret_cast<float4*>(hin_f32 + base) = st;
-    }
-    st.x = dec * st.x + sv.x;
-    st.y = dec * st.y + sv.y;
-    st.z = dec * st.z + sv.z;
-    st.w = dec * st.w + sv.w;
-  }
+  for (int kk = nfull * kDepth; kk < nk; ++kk)
+    step(kk, load2<E>(st_in + (int64_t)kk * stride + lo), lam[(int64_t)kk * H]);
   if (p.final_state != nullptr)
-    *reinterpret_cast<float4*>(p.final_state + (s * H + h) * (int64_t)PN + ch) = st;
+    *reinterpret_cast<float2*>(p.final_state + (s * H + h) * (int64_t)PN + ch) = st;
 }
 
-hipError_t launch_state_pass_impl(const Problem& p, const Workspace& ws, float* hin_f32,
-                                  hipStream_t s) {
+hipError_t launch_state_pass(const Problem& p, const Workspace& ws, float* hin_f32,
+                             hipStream_t s) {
   const int PN = p.P * p.N;
-  const int64_t cblocks = (PN + 4 * kThreads - 1) / (4 * kThreads);
+  const int64_t cblocks = (PN + kCh * kThreads - 1) / (kCh * kThreads);
   const int64_t blocks = p.nseq * p.H * cblocks;
   if (blocks == 0) return hipSuccess;
-  if (p.dtype == Dtype::BF16)
-    hipLaunchKernelGGL(state_pass_kernel<Bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, ws, hin_f32);
-  else
-    hipLaunchKernelGGL(state_pass_kernel<F32>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, ws, hin_f32);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (p.dtype == Dtype::BF16) {
+    if (hin_f32) hipLaunchKernelGGL((state_pass_kernel<Bf16, true>), grid, block, 0, s, p, ws, hin_f32);
+    else hipLaunchKernelGGL((state_pass_kernel<Bf16, false>), grid, block, 0, s, p, ws, hin_f32);
+  } else {
+    if (hin_f32) hipLaunchKernelGGL((state_pass_kernel<F32, true>), grid, block, 0, s, p, ws, hin_f32);
+    else hipLaunchKernelGGL((state_pass_kernel<F32, false>), grid, block, 0, s, p, ws, hin_f32);
+  }
   return hipGetLastError();
-}
-
-hipError_t launch_state_pass(const Problem& p, const Workspace& ws, hipStream_t s) {
-  return launch_state_pass_impl(p, ws, nullptr, s);
 }
 
 }  // namespace ssd

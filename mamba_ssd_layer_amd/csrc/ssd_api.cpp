@@ -5,23 +5,18 @@
 // the optional per-kernel event timing.  The sequence follows the four steps of
 // the block decomposition in "LLM(十一)——Mamba" (mztchaoqun.com.cn) §3.5.2
 // "SSD algorithm: chunking and state passing", with the chunk tables first:
-//   K0 sequence table -> K1 chunk cumsum -> K3 chunk states -> K4 state passing
-//   -> K2+K5 diagonal blocks fused with state-to-output.
+//   [K0 sequence table, varlen only] -> K1+K3 chunk cumsum and chunk states ->
+//   K4 state passing -> K2+K5 diagonal blocks fused with state-to-output.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
 #include <string.h>
 #include <vector>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "ssd_internal.hpp"
 
 namespace ssd {
-
-bool chunk_state_supported(Dtype dt, int Q, int N);
-bool chunk_output_supported(Dtype dt, int Q, int N);
-hipError_t launch_state_pass_impl(const Problem& p, const Workspace& ws, float* hin_f32,
-                                  hipStream_t s);
 
 bool config_supported(Dtype dt, int Q, int N) {
   return chunk_state_supported(dt, Q, N) && chunk_output_supported(dt, Q, N);
@@ -45,7 +40,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   char* chunks = take(K * sizeof(ChunkDesc));
   char* acs = take(K * H * p.Q * sizeof(float));
   char* lam = take(K * H * sizeof(float));
-  char* states = take(K * H * PN * sizeof(float));
+  char* states = take(K * H * PN * esz);
   char* hin = take(K * H * PN * esz);
   if (ws && base) {
     ws->seq_off = reinterpret_cast<int32_t*>(seq_off);
@@ -54,7 +49,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->chunks = reinterpret_cast<ChunkDesc*>(chunks);
     ws->acs = reinterpret_cast<float*>(acs);
     ws->lam = reinterpret_cast<float*>(lam);
-    ws->states = reinterpret_cast<float*>(states);
+    ws->states = states;
     ws->hin = hin;
   }
   return off;
@@ -188,26 +183,23 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
   Workspace ws;
   workspace_layout(p, static_cast<char*>(base), &ws);
   const size_t KH = (size_t)p.kmax * p.H;
-  const size_t PN = (size_t)p.P * p.N;
   do {
-    e = timed_launch(kK0SeqTable, stream, [&] { return launch_seq_table(p, ws, stream); });
-    if (e != hipSuccess) break;
+    if (p.cu != nullptr) {
+      e = timed_launch(kK0SeqTable, stream, [&] { return launch_seq_table(p, ws, stream); });
+      if (e != hipSuccess) break;
+    }
     if (p.kmax > 0) {
-      e = timed_launch(kK1Cumsum, stream, [&] { return launch_chunk_cumsum(p, ws, stream); });
+      e = timed_launch(kK13ChunkState, stream, [&] {
+        return launch_chunk_state(p, ws, dbg ? dbg->states : nullptr, stream);
+      });
       if (e != hipSuccess) break;
       if (dbg && dbg->acs) {
         e = hipMemcpyAsync(dbg->acs, ws.acs, KH * p.Q * sizeof(float), hipMemcpyDeviceToDevice, stream);
         if (e != hipSuccess) break;
       }
-      e = timed_launch(kK3ChunkState, stream, [&] { return launch_chunk_state(p, ws, stream); });
-      if (e != hipSuccess) break;
-      if (dbg && dbg->states) {
-        e = hipMemcpyAsync(dbg->states, ws.states, KH * PN * sizeof(float), hipMemcpyDeviceToDevice, stream);
-        if (e != hipSuccess) break;
-      }
     }
     e = timed_launch(kK4StatePass, stream, [&] {
-      return launch_state_pass_impl(p, ws, dbg ? dbg->hin : nullptr, stream);
+      return launch_state_pass(p, ws, dbg ? dbg->hin : nullptr, stream);
     });
     if (e != hipSuccess) break;
     if (p.kmax > 0) {

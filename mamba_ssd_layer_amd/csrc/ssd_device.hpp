@@ -71,6 +71,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * q + (xcd < r ? xcd : r) + slot;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a workgroup
+// fence on every address space, which makes each wave wait for all of its
+// outstanding global loads and stores (vmcnt(0)) before the barrier; that would
+// serialise the next tile's prefetch and the output stores with every barrier.
+// Kernels that share only LDS between waves use this instead.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum of one float per lane across a 64-lane wave.
 __device__ __forceinline__ float wave_inclusive_sum(float v) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -82,5 +93,59 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
   return v;
 }
 
+// Chunk descriptor of slot k.  Batched problems (no cu_seqlens) compute it:
+// sequence s = k / nc owns slots [s*nc, (s+1)*nc), nc = ceil(T/Q); varlen
+// problems read the table the cumsum kernel filled.
+__device__ __forceinline__ ChunkDesc chunk_desc(const Problem& p, const Workspace& ws, int64_t k) {
+  if (p.cu == nullptr) {
+    const int64_t nc = (p.seqlen + p.Q - 1) / p.Q;
+    const int64_t s = k / nc, c = k % nc;
+    const int64_t rem = p.seqlen - c * p.Q;
+    ChunkDesc d;
+    d.seq = (int32_t)s;
+    d.len = (int32_t)(rem < p.Q ? rem : p.Q);
+    d.t0 = s * p.seqlen + c * p.Q;
+    return d;
+  }
+  return ws.chunks[k];
+}
+
+// Chunk descriptor of slot k found from the sequence table: the last sequence
+// s with seq_off[s] <= k (sequences without chunks share their offset with the
+// next one, so the last match is the one that owns slot k).
+__device__ __forceinline__ ChunkDesc chunk_desc_search(const Problem& p, const Workspace& ws,
+                                                       int64_t k) {
+  if (p.cu == nullptr) return chunk_desc(p, ws, k);
+  ChunkDesc d;
+  d.seq = -1;
+  d.len = 0;
+  d.t0 = 0;
+  const int64_t nch = ws.seq_off[p.nseq];
+  if (k >= nch) return d;
+  int64_t lo = 0, hi = p.nseq;  // seq_off[lo] <= k < seq_off[hi]
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (ws.seq_off[mid] <= k) lo = mid; else hi = mid;
+  }
+  const int64_t c = k - ws.seq_off[lo];
+  const int64_t rem = ws.seq_len[lo] - c * p.Q;
+  d.len = (int32_t)(rem < p.Q ? (rem > 0 ? rem : 0) : p.Q);
+  d.seq = d.len > 0 ? (int32_t)lo : -1;
+  d.t0 = ws.seq_start[lo] + c * p.Q;
+  return d;
+}
+
+// First chunk slot of sequence s and one past its last.
+__device__ __forceinline__ void seq_chunk_range(const Problem& p, const Workspace& ws, int64_t s,
+                                                int64_t* k0, int64_t* k1) {
+  if (p.cu == nullptr) {
+    const int64_t nc = (p.seqlen + p.Q - 1) / p.Q;
+    *k0 = s * nc;
+    *k1 = (s + 1) * nc;
+  } else {
+    *k0 = ws.seq_off[s];
+    *k1 = ws.seq_off[s + 1];
+  }
+}
 
 }  // namespace ssd

@@ -46,10 +46,10 @@ struct Workspace {
   int32_t* seq_off = nullptr;    // (S+1) first chunk slot of each sequence; [S] = chunk count
   int64_t* seq_start = nullptr;  // (S)   first token of each sequence (clamped to [0,Ttot])
   int64_t* seq_len = nullptr;    // (S)   tokens of each sequence (clamped, >= 0)
-  ChunkDesc* chunks = nullptr;   // (kmax)
+  ChunkDesc* chunks = nullptr;   // (kmax) varlen only: written by the chunk-state kernel
   float* acs = nullptr;          // (kmax, H, Q) chunk-local cumsum of dt*A
   float* lam = nullptr;          // (kmax, H)    its last entry (log of the chunk's decay)
-  float* states = nullptr;       // (kmax, H, P, N) chunk states, fp32
+  void* states = nullptr;        // (kmax, H, P, N) chunk states, element dtype
   void* hin = nullptr;           // (kmax, H, P, N) state entering each chunk, element dtype
 };
 
@@ -59,13 +59,20 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws);
 // Whether (dtype, Q, N) has an instantiated kernel set that fits in LDS.
 bool config_supported(Dtype dt, int Q, int N);
 
-// Kernel launchers; each returns the launch status.  Kernel ids for timing:
-enum KernelId { kK0SeqTable = 0, kK1Cumsum = 1, kK3ChunkState = 2, kK4StatePass = 3,
-                kK25ChunkOutput = 4, kNumKernels = 5 };
+// Kernel launchers; each returns the launch status.  Kernel ids for timing.
+enum KernelId { kK0SeqTable = 0, kK13ChunkState = 1, kK4StatePass = 2, kK25ChunkOutput = 3,
+                kNumKernels = 4 };
+// K0 (varlen only): per-sequence first token, length and first chunk slot.
 hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
-hipError_t launch_chunk_cumsum(const Problem& p, const Workspace& ws, hipStream_t s);
-hipError_t launch_chunk_state(const Problem& p, const Workspace& ws, hipStream_t s);
-hipError_t launch_state_pass(const Problem& p, const Workspace& ws, hipStream_t s);
+// K1 + K3: chunk-local log-decay cumsum (-> acs, lam), chunk states (-> states);
+// states_f32 (nullable) receives an fp32 copy of the stored states.
+hipError_t launch_chunk_state(const Problem& p, const Workspace& ws, float* states_f32,
+                              hipStream_t s);
+// K4: state passing (-> hin, final_state); hin_f32 (nullable) receives an fp32 copy.
+hipError_t launch_state_pass(const Problem& p, const Workspace& ws, float* hin_f32, hipStream_t s);
+// K2 + K5: diagonal blocks and state-to-output (-> y).
 hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s);
+bool chunk_state_supported(Dtype dt, int Q, int N);
+bool chunk_output_supported(Dtype dt, int Q, int N);
 
 }  // namespace ssd

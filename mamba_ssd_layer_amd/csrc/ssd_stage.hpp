@@ -1,111 +1,133 @@
-// ssd_stage.hpp -- global -> LDS staging of chunk tiles for the SSD kernels.
+// ssd_stage.hpp -- global -> register -> LDS staging of chunk tiles.
 //
-// A chunk tile is `rows` consecutive packed tokens (zero past the chunk length
-// L) of `COLS` contiguous elements each, rows `ld` elements apart in global
-// memory.  Two forms:
-//   stage_rows:       LDS[r][c]  (row pitch DP elements), same orientation;
-//   stage_transposed: LDS[c][r]  (row pitch DP elements), optionally scaling
-//                     row r by scale[r] (fp32) before rounding to the element
-//                     type (round-to-nearest-even for bf16).
-// Transposition is what lets a matrix-core product contract over tokens: an
-// MFMA operand lane needs consecutive K (token) values in its registers.
+// A chunk tile is ROWS consecutive packed tokens (zero past the chunk length
+// L) of COLS contiguous elements, rows `ld` elements apart in global memory.
+// Staging is split into load() (every global load of the thread issued back to
+// back into registers, so their latencies overlap) and store() (registers ->
+// LDS), so that a kernel can issue the loads of its next tile before computing
+// on the current one.
+//   RowTile:   LDS[r][c]  with row pitch DP elements;
+//   TransTile: LDS[c][r]  with row pitch DP elements (tokens contiguous, the
+//              layout an MFMA operand needs to contract over tokens), with an
+//              optional per-row fp32 scale applied before rounding back to the
+//              element type (round-to-nearest-even for bf16).
 #pragma once
 
 #include "ssd_device.hpp"
 
 namespace ssd {
 
-template <class E, int ROWS, int COLS, int DP>
-__device__ __forceinline__ void stage_rows(typename E::storage* __restrict__ lds,
-                                           const typename E::storage* __restrict__ g,
-                                           int64_t ld, int L) {
+template <class E, int ROWS, int COLS, int NTHR = kThreads>
+struct RowTile {
   using T = typename E::storage;
-  constexpr int VEC = 16 / sizeof(T);
+  static constexpr int VEC = 16 / sizeof(T);
   static_assert(COLS % VEC == 0, "row length must be a multiple of 16 bytes");
-  constexpr int VPR = COLS / VEC;  // vectors per row
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += kThreads) {
-    const int r = idx / VPR, v = idx % VPR;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < L) val = *reinterpret_cast<const uint4*>(g + r * ld + v * VEC);
-    *reinterpret_cast<uint4*>(lds + r * DP + v * VEC) = val;
-  }
-}
+  static constexpr int VPR = COLS / VEC;
+  static constexpr int NV = ROWS * VPR;
+  static constexpr int NPT = (NV + NTHR - 1) / NTHR;
+  uint4 v[NPT];
 
-// bf16: 8x8 element blocks (eight 16-byte row loads -> eight 16-byte column stores).
-template <int ROWS, int COLS, int DP, bool SCALE>
-__device__ __forceinline__ void stage_transposed_bf16(uint16_t* __restrict__ lds,
-                                                      const uint16_t* __restrict__ g, int64_t ld,
-                                                      int L, const float* __restrict__ scale) {
-  static_assert(ROWS % 8 == 0 && COLS % 8 == 0, "8x8 blocks");
-  constexpr int CB = COLS / 8;
-  for (int blk = threadIdx.x; blk < (ROWS / 8) * CB; blk += kThreads) {
-    const int cb = blk % CB, rb = blk / CB;
-    uint4 in[8];
+  __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = rb * 8 + i;
-      in[i] = make_uint4(0, 0, 0, 0);
-      if (r < L) in[i] = *reinterpret_cast<const uint4*>(g + r * ld + cb * 8);
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = threadIdx.x + i * NTHR;
+      const int r = idx / VPR, c = idx % VPR;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (idx < NV && r < L) v[i] = *reinterpret_cast<const uint4*>(g + r * ld + c * VEC);
     }
-    float sc[8];
+  }
+  template <int DP>
+  __device__ __forceinline__ void store(T* __restrict__ lds) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sc[i] = SCALE ? scale[rb * 8 + i] : 1.0f;
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = threadIdx.x + i * NTHR;
+      const int r = idx / VPR, c = idx % VPR;
+      if (idx < NV) *reinterpret_cast<uint4*>(lds + r * DP + c * VEC) = v[i];
+    }
+  }
+};
+
+template <class E, int ROWS, int COLS, int NTHR = kThreads>
+struct TransTile {
+  using T = typename E::storage;
+  static constexpr bool kBf16 = E::kBytes == 2;
+  static constexpr int BS = kBf16 ? 8 : 4;  // square block edge (one 16-byte vector per row)
+  static_assert(ROWS % BS == 0 && COLS % BS == 0, "tile must be whole blocks");
+  static constexpr int CB = COLS / BS;
+  static constexpr int NB = (ROWS / BS) * CB;
+  static constexpr int NPT = (NB + NTHR - 1) / NTHR;
+  uint4 v[NPT][BS];
+
+  __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v[8];
+    for (int i = 0; i < NPT; ++i) {
+      const int blk = threadIdx.x + i * NTHR;
+      const int cb = blk % CB, rb = blk / CB;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w = (c >> 1) == 0 ? in[i].x : (c >> 1) == 1 ? in[i].y : (c >> 1) == 2 ? in[i].z : in[i].w;
-        const float f = (c & 1) ? bf16_hi(w) : bf16_lo(w);
-        v[i] = SCALE ? f * sc[i] : f;
+      for (int rr = 0; rr < BS; ++rr) {
+        const int r = rb * BS + rr;
+        v[i][rr] = make_uint4(0, 0, 0, 0);
+        if (blk < NB && r < L) v[i][rr] = *reinterpret_cast<const uint4*>(g + r * ld + cb * BS);
       }
-      uint4 out;
-      out.x = pack_bf16x2(v[0], v[1]);
-      out.y = pack_bf16x2(v[2], v[3]);
-      out.z = pack_bf16x2(v[4], v[5]);
-      out.w = pack_bf16x2(v[6], v[7]);
-      *reinterpret_cast<uint4*>(lds + (cb * 8 + c) * DP + rb * 8) = out;
     }
   }
-}
 
-// fp32: 4x4 element blocks.
-template <int ROWS, int COLS, int DP, bool SCALE>
-__device__ __forceinline__ void stage_transposed_f32(float* __restrict__ lds,
-                                                     const float* __restrict__ g, int64_t ld,
-                                                     int L, const float* __restrict__ scale) {
-  static_assert(ROWS % 4 == 0 && COLS % 4 == 0, "4x4 blocks");
-  constexpr int CB = COLS / 4;
-  for (int blk = threadIdx.x; blk < (ROWS / 4) * CB; blk += kThreads) {
-    const int cb = blk % CB, rb = blk / CB;
-    float4 in[4];
+  // scale: per-row factors in LDS (read only when SCALE).
+  // PERM16 (bf16 only): within every 16-token group the tokens are stored in
+  // the order 0-3, 8-11, 4-7, 12-15, so that lane group g of a 32x32x16 MFMA
+  // finds its tokens {4g..4g+3, 8+4g..8+4g+3} as one contiguous 16-byte run.
+  template <int DP, bool SCALE, bool PERM16 = false>
+  __device__ __forceinline__ void store(T* __restrict__ lds, const float* __restrict__ scale) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rb * 4 + i;
-      in[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < L) {
-        in[i] = *reinterpret_cast<const float4*>(g + r * ld + cb * 4);
-        if (SCALE) {
-          const float s = scale[r];
-          in[i].x *= s; in[i].y *= s; in[i].z *= s; in[i].w *= s;
+    for (int i = 0; i < NPT; ++i) {
+      const int blk = threadIdx.x + i * NTHR;
+      if (blk >= NB) continue;
+      const int cb = blk % CB, rb = blk / CB;
+      float sc[BS];
+#pragma unroll
+      for (int rr = 0; rr < BS; ++rr) sc[rr] = SCALE ? scale[rb * BS + rr] : 1.0f;
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float f[8];
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr) {
+            const uint4 q = v[i][rr];
+            const uint32_t w = (c >> 1) == 0 ? q.x : (c >> 1) == 1 ? q.y : (c >> 1) == 2 ? q.z : q.w;
+            const float e = (c & 1) ? bf16_hi(w) : bf16_lo(w);
+            f[rr] = SCALE ? e * sc[rr] : e;
+          }
+          uint4 o;
+          o.x = pack_bf16x2(f[0], f[1]);
+          o.y = pack_bf16x2(f[2], f[3]);
+          o.z = pack_bf16x2(f[4], f[5]);
+          o.w = pack_bf16x2(f[6], f[7]);
+          T* row = lds + (cb * 8 + c) * DP;
+          if constexpr (PERM16) {
+            const int base = (rb >> 1) * 16 + (rb & 1) * 4;
+            *reinterpret_cast<uint2*>(row + base) = make_uint2(o.x, o.y);
+            *reinterpret_cast<uint2*>(row + base + 8) = make_uint2(o.z, o.w);
+          } else {
+            *reinterpret_cast<uint4*>(row + rb * 8) = o;
+          }
         }
+      } else {
+        float f[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint4 q = v[i][rr];
+          f[rr][0] = __uint_as_float(q.x) * sc[rr];
+          f[rr][1] = __uint_as_float(q.y) * sc[rr];
+          f[rr][2] = __uint_as_float(q.z) * sc[rr];
+          f[rr][3] = __uint_as_float(q.w) * sc[rr];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(lds) + (cb * 4 + c) * DP + rb * 4) =
+              make_float4(f[0][c], f[1][c], f[2][c], f[3][c]);
       }
     }
-    *reinterpret_cast<float4*>(lds + (cb * 4 + 0) * DP + rb * 4) = make_float4(in[0].x, in[1].x, in[2].x, in[3].x);
-    *reinterpret_cast<float4*>(lds + (cb * 4 + 1) * DP + rb * 4) = make_float4(in[0].y, in[1].y, in[2].y, in[3].y);
-    *reinterpret_cast<float4*>(lds + (cb * 4 + 2) * DP + rb * 4) = make_float4(in[0].z, in[1].z, in[2].z, in[3].z);
-    *reinterpret_cast<float4*>(lds + (cb * 4 + 3) * DP + rb * 4) = make_float4(in[0].w, in[1].w, in[2].w, in[3].w);
   }
-}
-
-template <class E, int ROWS, int COLS, int DP, bool SCALE>
-__device__ __forceinline__ void stage_transposed(typename E::storage* __restrict__ lds,
-                                                 const typename E::storage* __restrict__ g,
-                                                 int64_t ld, int L, const float* __restrict__ scale) {
-  if constexpr (E::kBytes == 2)
-    stage_transposed_bf16<ROWS, COLS, DP, SCALE>(lds, g, ld, L, scale);
-  else
-    stage_transposed_f32<ROWS, COLS, DP, SCALE>(lds, g, ld, L, scale);
-}
+};
 
 }  // namespace ssd
