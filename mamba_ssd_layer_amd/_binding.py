@@ -42,7 +42,7 @@ SIGNATURES = {
                                 ctypes.POINTER(ctypes.c_int64), _i32], ctypes.c_int),
 }
 
-KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output"]
+KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb"]
 
 
 class SSDError(RuntimeError):

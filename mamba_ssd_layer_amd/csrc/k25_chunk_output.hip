@@ -12,23 +12,22 @@
 // whole sequence.
 //
 // Design (gfx950):
-//  * One workgroup of 8 waves (two per SIMD, so one wave's VALU and LDS work
-//    overlaps the other's MFMAs) per (chunk, block of HB heads of one B/C
-//    group).  Waves w and w+4 own the same two row tiles of 32 output tokens
-//    and split the 64 output channels in halves; both form the kernel tile
-//    G^T they share (duplicated MFMA work bought for latency hiding).
-//    The chunk's B tile is staged in LDS once and each wave's C rows are held
-//    in registers once, for all HB heads; the x tile and passed state of the
-//    next head are loaded into registers while the current head computes, so
-//    their HBM latency is hidden behind MFMA work.  Blocks are ordered so that
-//    the head blocks of one chunk land on one XCD and share its L2.
-//  * The output is built transposed, Y^T (P x Q), on 32x32 MFMA tiles.  The
-//    kernel tile G^T = B_J C_I^T (32 x 32, contraction over N) leaves each lane
-//    holding ONE output token i and 16 input tokens j, which is exactly the
-//    register layout of the B operand of the next product Y^T += X^T (L o G)^T:
-//    the masked tile never leaves the registers, and the K (token) order of
-//    that product is chosen to match.
-//  * Causality: only tiles J <= I are formed.  The mask factors as
+//  * The kernel matrix tiles G = C B^T of the chunk's B/C group come from the
+//    chunk kernel-matrix kernel (formed once per chunk and group, not per
+//    head), already in the per-lane MFMA register layout: each lane reloads a
+//    tile with coalesced 16-byte loads, two tiles in flight (L2-resident).
+//  * One workgroup of 4 waves per (chunk, block of HB heads of one group),
+//    about 53 KB of LDS, so two or three workgroups share a CU and one's loads
+//    and barriers overlap another's MFMA work.  Each wave's C rows stay in
+//    registers for all HB heads; the next head's x tile and passed state are
+//    loaded into registers while the current head computes.  Blocks are
+//    ordered so that the head blocks of one chunk land on one XCD.
+//  * The output is built transposed, Y^T (P x Q), on 32x32 MFMA tiles.  A
+//    kernel tile as G^T leaves each lane ONE output token i and 16 input
+//    tokens j, which is exactly the B-operand layout of Y^T += X^T (L o G)^T;
+//    the K (token) order of that product is chosen to match, and x^T is staged
+//    with its tokens permuted in 16-groups so the A operand is one 16-byte read.
+//  * Causality: only tiles J <= I are used.  The mask factors as
 //    L[i,j] = exp(Acs_i - Acs_e) * exp(Acs_e - Acs_j), e the last token of j's
 //    32-token tile.  The second factor w_j (in (0, 1]) scales x when it is
 //    staged in LDS, once per head; the first is one exp per lane per tile, in
@@ -50,28 +49,27 @@ struct ChunkOutputCfg {
   using T = typename E::storage;
   static constexpr int P = kHeadDim;
   static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int NP = N + PAD;  // LDS pitch of B and Hin rows
+  static constexpr int NP = N + PAD;  // LDS pitch of Hin rows
   static constexpr int QP = Q + PAD;  // LDS pitch of X^T rows
   static constexpr size_t lds_bytes =
-      ((size_t)Q * NP + (size_t)P * QP + (size_t)P * NP) * sizeof(T) + 2 * Q * sizeof(float);
+      ((size_t)P * QP + (size_t)P * NP) * sizeof(T) + 2 * Q * sizeof(float);
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
   static constexpr int KS = N / E::kMfmaK;                  // MFMA steps over N
   static constexpr int CREG = E::kBytes == 2 ? KS * 4 : KS; // VGPRs of one row tile's C operand
-  static constexpr bool kKeepC = 2 * CREG <= 64;            // keep both row tiles' C across heads
+  static constexpr bool kKeepC = 2 * CREG <= 32;            // keep both row tiles' C across heads
+  static constexpr int NI = Q / 32;
+  static constexpr int NTILE = NI * (NI + 1) / 2;           // causal 32x32 kernel tiles
+  static constexpr int GV = E::kBytes == 2 ? 2 : 4;         // 16-byte vectors per lane per tile
 };
 
-constexpr int kOutThreads = 512;  // 8 waves: two per SIMD
-
 template <class E, int Q, int N>
-__global__ __launch_bounds__(kOutThreads) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
+__global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
   using Cfg = ChunkOutputCfg<E, Q, N>;
   using T = typename E::storage;
-  constexpr int P = Cfg::P, NP = Cfg::NP, QP = Cfg::QP, KS = Cfg::KS;
+  constexpr int P = Cfg::P, NP = Cfg::NP, QP = Cfg::QP, KS = Cfg::KS, GV = Cfg::GV;
   constexpr bool kBf16 = E::kBytes == 2;
-  constexpr int NI = Q / 32;  // row tiles of the chunk
-  constexpr int NTHR = kOutThreads;
+  constexpr int NI = Cfg::NI;
   using CReg = typename std::conditional<kBf16, uint4, float>::type;
-  __shared__ __attribute__((aligned(16))) T Bs[Q * NP];
   __shared__ __attribute__((aligned(16))) T XT[P * QP];
   __shared__ __attribute__((aligned(16))) T Hs[P * NP];
   __shared__ __attribute__((aligned(16))) float acs_s[Q];
@@ -89,23 +87,23 @@ __global__ __launch_bounds__(kOutThreads) void chunk_output_kernel(Problem p, Wo
   const int tid = threadIdx.x;
   const int wid = tid >> 6, lane = tid & 63;
   const int lr = lane & 31, lg = lane >> 5;
-  const int pt = wid >> 2;  // this wave's 32 output channels p: [32 pt, 32 pt + 32)
-  const int wq = wid & 3;   // this wave's row tiles: wq and 7 - wq
   const int nI = (L + 31) / 32;
 
   const T* xbase = reinterpret_cast<const T*>(p.x) + cd.t0 * H * P;
-  const T* bg = reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N;
   const T* cg = reinterpret_cast<const T*>(p.C) + (cd.t0 * G + g) * N;
   const T* hbase = reinterpret_cast<const T*>(ws.hin) + k * H * (int64_t)(P * N);
   const float* abase = ws.acs + k * H * Q;
+  // this lane's 16 values of every kernel tile of the chunk's group
+  const uint4* gtiles = reinterpret_cast<const uint4*>(
+      reinterpret_cast<const T*>(ws.cb) + (k * G + g) * (int64_t)(Cfg::NTILE * 64 * 16) + lane * 16);
   T* ybase = reinterpret_cast<T*>(p.y) + cd.t0 * H * P;
 
-  // row tiles of this wave: wq and 7-wq (balanced causal work: tile I costs
+  // row tiles of this wave: w and 7-w (balanced causal work: tile I costs
   // I+1 kernel tiles); chunks of 64 or 128 tokens have 2 or 4 row tiles
   constexpr int NT = NI == 8 ? 2 : 1;
-  auto row_tile = [&](int t) { return t == 0 ? wq : 7 - wq; };
+  auto row_tile = [&](int t) { return t == 0 ? wid : 7 - wid; };
 
-  // C rows of this wave's tokens as MFMA B-operand slices over N
+  // C row of this lane's token as MFMA B-operand slices over N
   auto load_c = [&](int I, CReg (&c)[KS]) {
     const int i_loc = I * 32 + lr;
     const bool ok = i_loc < L;
@@ -119,20 +117,14 @@ __global__ __launch_bounds__(kOutThreads) void chunk_output_kernel(Problem p, Wo
     }
   };
   CReg ckeep[NT][KS];
-
-  // ---- prologue: B tile, C rows, first head's x / state / cumsum
-  {
-    RowTile<E, Q, N, NTHR> bt;
-    bt.load(bg, (int64_t)G * N, L);
-    bt.template store<NP>(Bs);
-  }
   if constexpr (Cfg::kKeepC) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       if (row_tile(t) < nI) load_c(row_tile(t), ckeep[t]);
   }
-  TransTile<E, Q, P, NTHR> xt;
-  RowTile<E, P, N, NTHR> ht;
+
+  TransTile<E, Q, P> xt;
+  RowTile<E, P, N> ht;
   float a_own = 0.f, a_end = 0.f;
   auto prefetch = [&](int h) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
@@ -165,6 +157,13 @@ __global__ __launch_bounds__(kOutThreads) void chunk_output_kernel(Problem p, Wo
     else
       xt.template store<QP, false, kBf16>(XT, nullptr);
     lds_barrier();
+    // C rows (when not kept): the first row tile's are loaded before the next
+    // head's prefetch so that waiting for them does not also wait for the
+    // prefetch; the second row tile's after the first row tile's work
+    CReg cfresh[KS];
+    if constexpr (!Cfg::kKeepC) {
+      if (row_tile(0) < nI) load_c(row_tile(0), cfresh);
+    }
     if (hh + 1 < HB) prefetch(h + 1);
 
 #pragma unroll
@@ -172,38 +171,53 @@ __global__ __launch_bounds__(kOutThreads) void chunk_output_kernel(Problem p, Wo
       const int I = row_tile(t);
       if (I >= nI) continue;
       const int i_loc = I * 32 + lr;
-      CReg cfresh[KS];
-      if constexpr (!Cfg::kKeepC) load_c(I, cfresh);
+      if constexpr (!Cfg::kKeepC) {
+        if (t > 0) load_c(I, cfresh);
+      }
       const CReg (&creg)[KS] = Cfg::kKeepC ? ckeep[t] : cfresh;
-      floatx16_t acc = zero16();
+      floatx16_t acc0 = zero16(), acc1 = zero16();
       // Y_off^T = Hin C^T (contraction over N), then the exp(Acs_i) factor
-      const T* hrow = Hs + (pt * 32 + lr) * NP;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (kBf16)
-          acc = mfma32x32x16(*reinterpret_cast<const uint4*>(hrow + ks * 16 + lg * 8), creg[ks], acc);
-        else
-          acc = mfma32x32x2(hrow[ks * 2 + lg], creg[ks], acc);
+        if constexpr (kBf16) {
+          const uint4 a0 = *reinterpret_cast<const uint4*>(Hs + lr * NP + ks * 16 + lg * 8);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(Hs + (32 + lr) * NP + ks * 16 + lg * 8);
+          acc0 = mfma32x32x16(a0, creg[ks], acc0);
+          acc1 = mfma32x32x16(a1, creg[ks], acc1);
+        } else {
+          acc0 = mfma32x32x2(Hs[lr * NP + ks * 2 + lg], creg[ks], acc0);
+          acc1 = mfma32x32x2(Hs[(32 + lr) * NP + ks * 2 + lg], creg[ks], acc1);
+        }
       }
       const float ai = acs_s[i_loc];
       const float eo = __expf(ai);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] *= eo;
+      for (int r = 0; r < 16; ++r) { acc0[r] *= eo; acc1[r] *= eo; }
 
-      // diagonal block: kernel tiles J <= I
-      const T* xrow = XT + (pt * 32 + lr) * QP;
-      for (int J = 0; J <= I; ++J) {
-        floatx16_t gt = zero16();
+      // diagonal block: kernel tiles J <= I of row tile I (consecutive tiles)
+      const uint4* grow = gtiles + (int64_t)(I * (I + 1) / 2) * (64 * 16 * sizeof(T) / 16);
+      auto load_g = [&](int J, uint4 (&gv)[GV]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (kBf16) {
-            const uint4 b = *reinterpret_cast<const uint4*>(Bs + (J * 32 + lr) * NP + ks * 16 + lg * 8);
-            gt = mfma32x32x16(b, creg[ks], gt);
-          } else {
-            gt = mfma32x32x2(Bs[(J * 32 + lr) * NP + ks * 2 + lg], creg[ks], gt);
+        for (int q = 0; q < GV; ++q) gv[q] = grow[(int64_t)J * (64 * 16 * sizeof(T) / 16) + q];
+      };
+      auto tile = [&](int J, const uint4 (&gv)[GV]) {
+        // gt[r] = G[i_loc][j_r], j_r = 32J + 8(r/4) + 4 lg + r%4
+        float gt[16];
+        if constexpr (kBf16) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            gt[8 * q + 0] = bf16_lo(gv[q].x); gt[8 * q + 1] = bf16_hi(gv[q].x);
+            gt[8 * q + 2] = bf16_lo(gv[q].y); gt[8 * q + 3] = bf16_hi(gv[q].y);
+            gt[8 * q + 4] = bf16_lo(gv[q].z); gt[8 * q + 5] = bf16_hi(gv[q].z);
+            gt[8 * q + 6] = bf16_lo(gv[q].w); gt[8 * q + 7] = bf16_hi(gv[q].w);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gt[4 * q + 0] = __uint_as_float(gv[q].x); gt[4 * q + 1] = __uint_as_float(gv[q].y);
+            gt[4 * q + 2] = __uint_as_float(gv[q].z); gt[4 * q + 3] = __uint_as_float(gv[q].w);
           }
         }
-        // gt[r] = G[i_loc][j_r], j_r = 32J + 8(r/4) + 4 lg + r%4
         float v[16];
         if (fast) {
           // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
@@ -247,31 +261,51 @@ __global__ __launch_bounds__(kOutThreads) void chunk_output_kernel(Problem p, Wo
             bop.z = pack_bf16x2(v[8 * kk + 4], v[8 * kk + 5]);
             bop.w = pack_bf16x2(v[8 * kk + 6], v[8 * kk + 7]);
             // tokens are permuted within 16-groups: this lane group's 8 are contiguous
-            const uint4 a = *reinterpret_cast<const uint4*>(xrow + J * 32 + kk * 16 + lg * 8);
-            acc = mfma32x32x16(a, bop, acc);
+            const int col = J * 32 + kk * 16 + lg * 8;
+            const uint4 a0 = *reinterpret_cast<const uint4*>(XT + lr * QP + col);
+            const uint4 a1 = *reinterpret_cast<const uint4*>(XT + (32 + lr) * QP + col);
+            acc0 = mfma32x32x16(a0, bop, acc0);
+            acc1 = mfma32x32x16(a1, bop, acc1);
           }
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-            acc = mfma32x32x2(xrow[j], v[r], acc);
+            acc0 = mfma32x32x2(XT[lr * QP + j], v[r], acc0);
+            acc1 = mfma32x32x2(XT[(32 + lr) * QP + j], v[r], acc1);
           }
         }
+      };
+      // two register buffers used in turn: the next tile's loads are in flight
+      // while the current one is masked and multiplied (loads past I are clamped)
+      uint4 gA[GV], gB[GV];
+      load_g(0, gA);
+      for (int J = 0; J <= I; J += 2) {
+        load_g(min(J + 1, I), gB);
+        tile(J, gA);
+        if (J + 1 > I) break;
+        load_g(min(J + 2, I), gA);
+        tile(J + 1, gB);
       }
       // store: lane holds y[i_loc][p] for p = 32 pt + 8(r/4) + 4 lg + r%4
       if (i_loc < L) {
-        T* yrow = ybase + (int64_t)i_loc * H * P + h * P + pt * 32;
+        T* yrow = ybase + (int64_t)i_loc * H * P + h * P;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int pp = q * 8 + lg * 4;
           if constexpr (kBf16) {
-            uint2 o;
-            o.x = pack_bf16x2(acc[4 * q + 0], acc[4 * q + 1]);
-            o.y = pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
-            *reinterpret_cast<uint2*>(yrow + pp) = o;
+            uint2 o0, o1;
+            o0.x = pack_bf16x2(acc0[4 * q + 0], acc0[4 * q + 1]);
+            o0.y = pack_bf16x2(acc0[4 * q + 2], acc0[4 * q + 3]);
+            o1.x = pack_bf16x2(acc1[4 * q + 0], acc1[4 * q + 1]);
+            o1.y = pack_bf16x2(acc1[4 * q + 2], acc1[4 * q + 3]);
+            *reinterpret_cast<uint2*>(yrow + pp) = o0;
+            *reinterpret_cast<uint2*>(yrow + 32 + pp) = o1;
           } else {
             *reinterpret_cast<float4*>(yrow + pp) =
-                make_float4(acc[4 * q + 0], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+                make_float4(acc0[4 * q + 0], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]);
+            *reinterpret_cast<float4*>(yrow + 32 + pp) =
+                make_float4(acc1[4 * q + 0], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]);
           }
         }
       }
@@ -290,7 +324,7 @@ static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
     const int HB = chunk_output_heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    hipLaunchKernelGGL((chunk_output_kernel<E, Q, N>), dim3(blocks), dim3(kOutThreads), 0, s, p, ws, HB);
+    hipLaunchKernelGGL((chunk_output_kernel<E, Q, N>), dim3(blocks), dim3(kThreads), 0, s, p, ws, HB);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

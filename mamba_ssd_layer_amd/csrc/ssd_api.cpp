@@ -42,6 +42,8 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   char* lam = take(K * H * sizeof(float));
   char* states = take(K * H * PN * esz);
   char* hin = take(K * H * PN * esz);
+  const size_t NI = (size_t)p.Q / 32;
+  char* cb = take(K * (size_t)p.G * (NI * (NI + 1) / 2) * 64 * 16 * esz);
   if (ws && base) {
     ws->seq_off = reinterpret_cast<int32_t*>(seq_off);
     ws->seq_start = reinterpret_cast<int64_t*>(seq_start);
@@ -51,6 +53,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->lam = reinterpret_cast<float*>(lam);
     ws->states = states;
     ws->hin = hin;
+    ws->cb = cb;
   }
   return off;
 }
@@ -197,6 +200,10 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
         e = hipMemcpyAsync(dbg->acs, ws.acs, KH * p.Q * sizeof(float), hipMemcpyDeviceToDevice, stream);
         if (e != hipSuccess) break;
       }
+    }
+    if (p.kmax > 0) {
+      e = timed_launch(kK2ChunkCB, stream, [&] { return launch_chunk_cb(p, ws, stream); });
+      if (e != hipSuccess) break;
     }
     e = timed_launch(kK4StatePass, stream, [&] {
       return launch_state_pass(p, ws, dbg ? dbg->hin : nullptr, stream);

@@ -51,6 +51,8 @@ struct Workspace {
   float* lam = nullptr;          // (kmax, H)    its last entry (log of the chunk's decay)
   void* states = nullptr;        // (kmax, H, P, N) chunk states, element dtype
   void* hin = nullptr;           // (kmax, H, P, N) state entering each chunk, element dtype
+  void* cb = nullptr;            // (kmax, G, NI(NI+1)/2 tiles, 64 lanes, 16) kernel tiles of
+                                 // C B^T, element dtype, NI = Q/32
 };
 
 // Bytes of workspace for p; fills *ws from base when base != nullptr.
@@ -61,7 +63,7 @@ bool config_supported(Dtype dt, int Q, int N);
 
 // Kernel launchers; each returns the launch status.  Kernel ids for timing.
 enum KernelId { kK0SeqTable = 0, kK13ChunkState = 1, kK4StatePass = 2, kK25ChunkOutput = 3,
-                kNumKernels = 4 };
+                kK2ChunkCB = 4, kNumKernels = 5 };
 // K0 (varlen only): per-sequence first token, length and first chunk slot.
 hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
 // K1 + K3: chunk-local log-decay cumsum (-> acs, lam), chunk states (-> states);
@@ -70,6 +72,8 @@ hipError_t launch_chunk_state(const Problem& p, const Workspace& ws, float* stat
                               hipStream_t s);
 // K4: state passing (-> hin, final_state); hin_f32 (nullable) receives an fp32 copy.
 hipError_t launch_state_pass(const Problem& p, const Workspace& ws, float* hin_f32, hipStream_t s);
+// K2 (first half): kernel matrix tiles C B^T of every chunk and group (-> cb).
+hipError_t launch_chunk_cb(const Problem& p, const Workspace& ws, hipStream_t s);
 // K2 + K5: diagonal blocks and state-to-output (-> y).
 hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s);
 bool chunk_state_supported(Dtype dt, int Q, int N);
