@@ -32,21 +32,48 @@ METRIC = "SSD fwd tokens/s and TFLOP/s (% bf16 MFMA peak) at T=2K/16K, N=128"
 KERNELS = ["seq_table", "chunk_state", "state_pass", "chunk_output"]
 
 
-def kernel_flops(w, seqlens):
-    """Algorithmic FLOPs per launch of each kernel (pages' per-head accounting,
-    "LLM(十一)——Mamba" §3.5.3): chunk states 2QNP, state passing 2NP, chunk
-    output 2Q^2 N + 2Q^2 P + 2QNP per (chunk, head); ragged chunks count their
-    real length."""
-    H, P, N, Q = w.nheads, w.headdim, w.dstate, w.chunk_len
-    out = {"chunk_state": 0.0, "state_pass": 0.0, "chunk_output": 0.0}
+def kernel_work(w, seqlens):
+    """Algorithmic FLOPs and HBM bytes per launch of each kernel.
+
+    FLOPs follow the pages' batched-matmul count ("LLM(十一)——Mamba" §3.5.3),
+    split by the kernel that performs each product, with q the chunk's real
+    length: chunk_cb 2 q^2 N per (chunk, B/C group) (C B^T is formed once for
+    the heads that share B and C), chunk_output 2 q^2 P + 2 q N P per (chunk,
+    head) ((L o G) X and C h), chunk_state 2 q N P per (chunk, head),
+    state_pass 2 N P per (chunk, head).  The headline TFLOP/s keeps the pages'
+    per-head count for every term.
+    Bytes are each kernel's compulsory reads and writes (e = element bytes,
+    Q-padded tables count Q entries per chunk):
+      chunk_state  x, B, dt in; states (P N e per chunk-head), Acs (4Q), total (4) out
+      chunk_cb     B, C in; causal 32x32 C B^T tiles (e per element) out
+      state_pass   states, chunk totals in; passed states out, final state (fp32) out
+      chunk_output x, C, passed states, Acs, C B^T tiles in; y out
+    """
+    H, P, N, G, Q = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
+    e = 2 if w.dtype == "bf16" else 4
+    nt = (Q // 32) * (Q // 32 + 1) // 2
+    chunks = []
     for L in seqlens:
-        L = int(L)
-        full, rem = divmod(L, Q)
-        for q in [Q] * full + ([rem] if rem else []):
-            out["chunk_state"] += H * 2 * q * N * P
-            out["state_pass"] += H * 2 * N * P
-            out["chunk_output"] += H * (2 * q * q * N + 2 * q * q * P + 2 * q * N * P)
-    return out
+        full, rem = divmod(int(L), Q)
+        chunks += [Q] * full + ([rem] if rem else [])
+    T = sum(int(L) for L in seqlens)
+    K = len(chunks)
+    S = len(seqlens)
+    f = {"chunk_state": 0.0, "chunk_cb": 0.0, "state_pass": 0.0, "chunk_output": 0.0}
+    for q in chunks:
+        f["chunk_cb"] += G * 2 * q * q * N
+        f["chunk_output"] += H * (2 * q * q * P + 2 * q * N * P)
+        f["chunk_state"] += H * 2 * q * N * P
+        f["state_pass"] += H * 2 * N * P
+    state = K * H * P * N * e
+    b = {
+        "chunk_state": T * H * P * e + T * G * N * e + T * H * 4 + state + K * H * (Q + 1) * 4,
+        "chunk_cb": 2 * T * G * N * e + K * G * nt * 1024 * e,
+        "state_pass": state + K * H * 4 + state + S * H * P * N * 4,
+        "chunk_output": (T * H * P * e + T * G * N * e + state + K * H * Q * 4
+                         + K * G * nt * 1024 * e + T * H * P * e),
+    }
+    return f, b
 
 
 def min_io_bytes(w, total_tokens, nseq):
@@ -161,14 +188,29 @@ def main():
 
     tokens = int(inp.total_tokens)
     fl = flops_pages(w, tokens, seqlens)
-    kfl = kernel_flops(w, seqlens)
+    kfl, kby = kernel_work(w, seqlens)
     sec = ms / 1e3
     tflops_a = fl["A_pages"] / sec / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    dom = "chunk_output"
-    dom_ms = kernel_ms.get(dom)
-    achieved = kfl[dom] / (dom_ms / 1e3) / 1e12 if dom_ms else None
-    traffic = load_traffic("k25_chunk_output.hip", w.name)
+    # per-kernel roofline: the bound is whichever of HBM time and matrix-core
+    # time is longer for the kernel's algorithmic bytes and FLOPs
+    kroof = {}
+    for kname in kfl:
+        kms = kernel_ms.get(kname)
+        t_hbm = kby[kname] / (PEAK_HBM_GBS * 1e9)
+        t_mfma = kfl[kname] / (peak * 1e12)
+        bound = "hbm" if t_hbm >= t_mfma else "mfma"
+        if kms:
+            ach = (kby[kname] / (kms / 1e3) / 1e9) if bound == "hbm" else (kfl[kname] / (kms / 1e3) / 1e12)
+        else:
+            ach = None
+        pk = PEAK_HBM_GBS if bound == "hbm" else peak
+        kroof[kname] = {"bound": bound, "achieved": ach, "peak": pk,
+                        "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                        "frac": (ach / pk) if ach else None, "avg_launch_ms": kms,
+                        "bytes_per_launch": kby[kname], "flops_per_launch": kfl[kname]}
+    dom = max((k for k in kroof if kroof[k]["avg_launch_ms"]), key=lambda k: kroof[k]["avg_launch_ms"])
+    traffic = load_traffic("k25_chunk_output.hip", w.name) if dom == "chunk_output" else None
     mio = min_io_bytes(w, tokens, nseq)
 
     result = {
@@ -194,11 +236,8 @@ def main():
                        "pct_peak": 100.0 * mio / sec / 1e9 / PEAK_HBM_GBS},
         "kernel_ms": kernel_ms,
         "events_pass_ms_per_step": (te1 - te0) * 1e3 / args.steps,
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": (achieved / peak) if achieved else None,
-                     "traffic": traffic,
-                     "flops_per_launch": kfl[dom], "avg_launch_ms": dom_ms,
-                     "accounting": "pages' per-head count: 2Q^2N + 2Q^2P + 2QNP per (chunk, head)"},
+        "roofline": dict(kroof[dom], kernel=dom, traffic=traffic),
+        "kernel_roofline": kroof,
         "cpu_baseline": None,
     }
 
