@@ -39,6 +39,9 @@
 //    exp(-inf) arithmetic).
 //  * Y_off uses the same lane layout: Hin (P x N, element dtype) is the A
 //    operand, the lane's C row the B operand, exp(Acs_i) one scalar per lane.
+//  * C rows come in the same per-lane operand order from the kernel-matrix
+//    kernel (contiguous loads); each finished row tile of y is passed through
+//    the wave's own LDS rows and written as whole 128-byte rows.
 //  * fp32 accumulation; y rounded once to the element dtype.
 #include "ssd_stage.hpp"
 
@@ -51,8 +54,10 @@ struct ChunkOutputCfg {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int NP = N + PAD;  // LDS pitch of Hin rows
   static constexpr int QP = Q + PAD;  // LDS pitch of X^T rows
+  static constexpr int YP = P + PAD;  // LDS pitch of a wave's staged output rows
   static constexpr size_t lds_bytes =
-      ((size_t)P * QP + (size_t)P * NP) * sizeof(T) + 2 * Q * sizeof(float);
+      ((size_t)P * QP + (size_t)P * NP + (size_t)(kThreads / 64) * 32 * YP) * sizeof(T) +
+      2 * Q * sizeof(float);
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
   static constexpr int KS = N / E::kMfmaK;                  // MFMA steps over N
   static constexpr int CREG = E::kBytes == 2 ? KS * 4 : KS; // VGPRs of one row tile's C operand
@@ -66,12 +71,13 @@ template <class E, int Q, int N>
 __global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
   using Cfg = ChunkOutputCfg<E, Q, N>;
   using T = typename E::storage;
-  constexpr int P = Cfg::P, NP = Cfg::NP, QP = Cfg::QP, KS = Cfg::KS, GV = Cfg::GV;
+  constexpr int P = Cfg::P, NP = Cfg::NP, QP = Cfg::QP, KS = Cfg::KS, GV = Cfg::GV, YP = Cfg::YP;
   constexpr bool kBf16 = E::kBytes == 2;
   constexpr int NI = Cfg::NI;
   using CReg = typename std::conditional<kBf16, uint4, float>::type;
   __shared__ __attribute__((aligned(16))) T XT[P * QP];
   __shared__ __attribute__((aligned(16))) T Hs[P * NP];
+  __shared__ __attribute__((aligned(16))) T Ys[(kThreads / 64) * 32 * YP];
   __shared__ __attribute__((aligned(16))) float acs_s[Q];
   __shared__ __attribute__((aligned(16))) float w_s[Q];
 
@@ -90,7 +96,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Wo
   const int nI = (L + 31) / 32;
 
   const T* xbase = reinterpret_cast<const T*>(p.x) + cd.t0 * H * P;
-  const T* cg = reinterpret_cast<const T*>(p.C) + (cd.t0 * G + g) * N;
+  // C rows as MFMA operand slices, lane after lane (written by the kernel-matrix kernel)
+  const CReg* cop = reinterpret_cast<const CReg*>(ws.cop) + (k * G + g) * (int64_t)(NI * KS * 64) + lane;
   const T* hbase = reinterpret_cast<const T*>(ws.hin) + k * H * (int64_t)(P * N);
   const float* abase = ws.acs + k * H * Q;
   // this lane's 16 values of every kernel tile of the chunk's group
@@ -103,18 +110,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Wo
   constexpr int NT = NI == 8 ? 2 : 1;
   auto row_tile = [&](int t) { return t == 0 ? wid : 7 - wid; };
 
-  // C row of this lane's token as MFMA B-operand slices over N
+  // C row of this lane's token as MFMA B-operand slices over N (coalesced)
   auto load_c = [&](int I, CReg (&c)[KS]) {
-    const int i_loc = I * 32 + lr;
-    const bool ok = i_loc < L;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (kBf16)
-        c[ks] = ok ? *reinterpret_cast<const uint4*>(cg + (int64_t)i_loc * G * N + ks * 16 + lg * 8)
-                   : make_uint4(0, 0, 0, 0);
-      else
-        c[ks] = ok ? cg[(int64_t)i_loc * G * N + ks * 2 + lg] : 0.0f;
-    }
+    for (int ks = 0; ks < KS; ++ks) c[ks] = cop[(I * KS + ks) * 64];
   };
   CReg ckeep[NT][KS];
   if constexpr (Cfg::kKeepC) {
@@ -287,28 +286,41 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Wo
         load_g(min(J + 2, I), gA);
         tile(J + 1, gB);
       }
-      // store: lane holds y[i_loc][p] for p = 32 pt + 8(r/4) + 4 lg + r%4
-      if (i_loc < L) {
-        T* yrow = ybase + (int64_t)i_loc * H * P + h * P;
+      // store: lane holds y[i_loc][p] for p = 32 pt + 8(r/4) + 4 lg + r%4.  The
+      // row tile goes through this wave's LDS rows so that global stores are
+      // whole 128-byte rows (eight lanes per row) instead of 32 scattered pieces.
+      T* ys = Ys + wid * 32 * YP;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int pp = q * 8 + lg * 4;
-          if constexpr (kBf16) {
-            uint2 o0, o1;
-            o0.x = pack_bf16x2(acc0[4 * q + 0], acc0[4 * q + 1]);
-            o0.y = pack_bf16x2(acc0[4 * q + 2], acc0[4 * q + 3]);
-            o1.x = pack_bf16x2(acc1[4 * q + 0], acc1[4 * q + 1]);
-            o1.y = pack_bf16x2(acc1[4 * q + 2], acc1[4 * q + 3]);
-            *reinterpret_cast<uint2*>(yrow + pp) = o0;
-            *reinterpret_cast<uint2*>(yrow + 32 + pp) = o1;
-          } else {
-            *reinterpret_cast<float4*>(yrow + pp) =
-                make_float4(acc0[4 * q + 0], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]);
-            *reinterpret_cast<float4*>(yrow + 32 + pp) =
-                make_float4(acc1[4 * q + 0], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]);
-          }
+      for (int q = 0; q < 4; ++q) {
+        const int pp = q * 8 + lg * 4;
+        if constexpr (kBf16) {
+          uint2 o0, o1;
+          o0.x = pack_bf16x2(acc0[4 * q + 0], acc0[4 * q + 1]);
+          o0.y = pack_bf16x2(acc0[4 * q + 2], acc0[4 * q + 3]);
+          o1.x = pack_bf16x2(acc1[4 * q + 0], acc1[4 * q + 1]);
+          o1.y = pack_bf16x2(acc1[4 * q + 2], acc1[4 * q + 3]);
+          *reinterpret_cast<uint2*>(ys + lr * YP + pp) = o0;
+          *reinterpret_cast<uint2*>(ys + lr * YP + 32 + pp) = o1;
+        } else {
+          *reinterpret_cast<float4*>(ys + lr * YP + pp) =
+              make_float4(acc0[4 * q + 0], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]);
+          *reinterpret_cast<float4*>(ys + lr * YP + 32 + pp) =
+              make_float4(acc1[4 * q + 0], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]);
         }
       }
+      __builtin_amdgcn_wave_barrier();
+      constexpr int VPR = P * sizeof(T) / 16;   // 16-byte vectors per output row
+      constexpr int RPI = 64 / VPR;             // rows per store instruction
+#pragma unroll
+      for (int st = 0; st < 32 / RPI; ++st) {
+        const int row = st * RPI + lane / VPR;
+        const int vec = lane % VPR;
+        const int i_row = I * 32 + row;
+        const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
+        if (i_row < L)
+          *reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + vec * (16 / sizeof(T))) = val;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }

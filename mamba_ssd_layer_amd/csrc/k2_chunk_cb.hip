@@ -15,7 +15,10 @@
 // memory latency per wave); there are many more waves than CUs.  A tile is
 // stored exactly as the accumulator lies in the registers: lane l's 16 values,
 // lane after lane, so the output kernel reloads it with fully coalesced 16-byte
-// loads into the register layout its masked product needs.  Tiles are in the element dtype (bf16: rounded to
+// loads into the register layout its masked product needs.  The wave of tile
+// (I, 0) also stores the C rows of row tile I as MFMA operand slices in the same
+// lane-after-lane order (a straight C row load touches 32 rows per
+// instruction; this copy is read back 1 KB-contiguous per instruction).  Tiles are in the element dtype (bf16: rounded to
 // nearest even), numbered I(I+1)/2 + J per (chunk, group).
 #include "ssd_device.hpp"
 
@@ -64,6 +67,12 @@ __global__ __launch_bounds__(kThreads) void chunk_cb_kernel(Problem p, Workspace
   CReg creg[KS], breg[KS];
   load_rows(cg, I * 32 + lr, creg);
   load_rows(bg, J * 32 + lr, breg);
+  if (J == 0) {
+    // the C rows of row tile I in the same lane layout, for the output kernel
+    CReg* cop = reinterpret_cast<CReg*>(ws.cop) + ((kg * NI + I) * KS) * 64 + lane;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) cop[ks * 64] = creg[ks];
+  }
   floatx16_t acc = zero16();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {

@@ -44,6 +44,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   char* hin = take(K * H * PN * esz);
   const size_t NI = (size_t)p.Q / 32;
   char* cb = take(K * (size_t)p.G * (NI * (NI + 1) / 2) * 64 * 16 * esz);
+  char* cop = take(K * (size_t)p.G * p.Q * p.N * esz);
   if (ws && base) {
     ws->seq_off = reinterpret_cast<int32_t*>(seq_off);
     ws->seq_start = reinterpret_cast<int64_t*>(seq_start);
@@ -54,6 +55,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->states = states;
     ws->hin = hin;
     ws->cb = cb;
+    ws->cop = cop;
   }
   return off;
 }

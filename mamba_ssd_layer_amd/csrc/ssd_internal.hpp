@@ -53,6 +53,8 @@ struct Workspace {
   void* hin = nullptr;           // (kmax, H, P, N) state entering each chunk, element dtype
   void* cb = nullptr;            // (kmax, G, NI(NI+1)/2 tiles, 64 lanes, 16) kernel tiles of
                                  // C B^T, element dtype, NI = Q/32
+  void* cop = nullptr;           // (kmax, G, NI, N/K steps, 64 lanes, one MFMA operand slice)
+                                 // C rows in MFMA B-operand order, element dtype
 };
 
 // Bytes of workspace for p; fills *ws from base when base != nullptr.
