@@ -14,15 +14,19 @@
 //    one (P x Q) . (Q x N) matrix product per (chunk, head).
 //
 // Design (gfx950): one workgroup of 4 waves per (chunk, block of HB heads of
-// one B/C group).  The prologue scans the HB heads' log-decays (one wave per
-// head: Q/64 tokens per lane plus a wave-level scan) and writes Acs and the
-// chunk total for the later kernels.  The chunk's B tile is staged transposed
-// in LDS once (tokens contiguous, as an MFMA operand contracting over tokens
-// needs) and serves all HB heads; each head's x tile is loaded into registers
-// while the previous head computes, then scaled by its decay-to-chunk-end and
-// transposed into LDS.  32x32 output tiles (v_mfma_f32_32x32x16_bf16 /
-// _32x32x2_f32) accumulate in fp32; states are stored in the element dtype (the
-// state-passing kernel accumulates them in fp32).
+// one B/C group).  The prologue loads the HB heads' log-decays at once and
+// scans them (one wave per head: Q/64 tokens per lane plus a wave-level scan),
+// writes Acs and the chunk total for the later kernels and keeps each head's
+// decay-to-chunk-end weights w_l = exp(Acs_{L-1} - Acs_l) in LDS.  The chunk's
+// B tile is staged transposed in LDS once (tokens contiguous, as an MFMA
+// operand contracting over tokens needs) and serves all HB heads; each head's
+// x tile is loaded into registers while the previous head computes, then scaled
+// by w and transposed into LDS.  The product is formed as S^T (N x P) on 32x32
+// tiles (v_mfma_f32_32x32x16_bf16 / _32x32x2_f32, fp32 accumulation), so that
+// each lane ends with runs of 4 consecutive n of one p; the tile passes through
+// LDS in [p][n] order and leaves as whole 16-byte vectors, the (P x N) state
+// of a (chunk, head) being one contiguous block.  States are stored in the
+// element dtype (the state-passing kernel accumulates them in fp32).
 #include "ssd_stage.hpp"
 
 namespace ssd {
@@ -36,23 +40,25 @@ struct ChunkStateCfg {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int QP = Q + PAD;          // LDS pitch of the transposed tiles
   static constexpr int NT = N < 32 ? 32 : N;  // B^T rows, padded to an MFMA tile
-  static constexpr size_t lds_bytes =
-      (size_t)(P + NT) * QP * sizeof(T) + (2 * kMaxHB + 1) * Q * sizeof(float);
+  static constexpr int SP = N + PAD;          // LDS pitch of the staged state rows
+  static constexpr size_t lds_bytes = (size_t)(P + NT) * QP * sizeof(T) + (size_t)P * SP * sizeof(T) +
+                                      2 * kMaxHB * Q * sizeof(float);
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
 };
 
-template <class E, int Q, int N>
+template <class E, int Q, int N, bool kDebug>
 __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Workspace ws, int HB,
                                                                float* __restrict__ states_f32) {
   using Cfg = ChunkStateCfg<E, Q, N>;
   using T = typename E::storage;
-  constexpr int P = Cfg::P, QP = Cfg::QP, NT = Cfg::NT;
+  constexpr bool kBf16 = E::kBytes == 2;
+  constexpr int P = Cfg::P, QP = Cfg::QP, NT = Cfg::NT, SP = Cfg::SP;
   constexpr int R = Q / 64;  // tokens per lane in the cumsum
   __shared__ __attribute__((aligned(16))) T xwT[P * QP];
   __shared__ __attribute__((aligned(16))) T bT[NT * QP];
+  __shared__ __attribute__((aligned(16))) T Ss[P * SP];
   __shared__ float ell_s[kMaxHB * Q];
-  __shared__ float acs_s[kMaxHB * Q];
-  __shared__ float w_s[Q];
+  __shared__ float w_s[kMaxHB * Q];
 
   const int H = p.H, G = p.G;
   const int nhb = H / HB;
@@ -69,23 +75,32 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
   const int lr = lane & 31, lg = lane >> 5;
   const T* xbase = reinterpret_cast<const T*>(p.x) + cd.t0 * H * P;
 
-  // ---- issue the loads: B^T tile, the first head's x tile, the dt tile
+  // ---- issue the loads: log-decays of the HB heads, B^T tile, first x tile
+  // (clamped indices, so that every load is issued unconditionally and back to back)
+  float ell[kMaxHB];
+  const float* dtrow = p.dt + (cd.t0 + min(tid, L - 1)) * H + h0;
+#pragma unroll
+  for (int hh = 0; hh < kMaxHB; ++hh) {
+    const int hc = min(hh, HB - 1);
+    ell[hh] = dtrow[hc] * p.A[h0 + hc];
+  }
+#pragma unroll
+  for (int hh = 0; hh < kMaxHB; ++hh) ell[hh] = (tid < L && hh < HB) ? ell[hh] : 0.0f;
   TransTile<E, Q, N> bt;
   bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
   TransTile<E, Q, P> xt;
   xt.load(xbase + h0 * P, (int64_t)H * P, L);
   if (tid < Q) {
-    for (int hh = 0; hh < HB; ++hh) {
-      const int h = h0 + hh;
-      ell_s[hh * Q + tid] = (tid < L) ? p.dt[(cd.t0 + tid) * H + h] * p.A[h] : 0.0f;
-    }
+#pragma unroll
+    for (int hh = 0; hh < kMaxHB; ++hh) ell_s[hh * Q + tid] = ell[hh];
   }
   if (NT > N)
     for (int i = tid; i < (NT - N) * QP; i += kThreads) bT[N * QP + i] = T(0);
   bt.template store<QP, false>(bT, nullptr);
   lds_barrier();
 
-  // ---- K1: chunk-local inclusive cumsum, one wave per head
+  // ---- K1: chunk-local inclusive cumsum, one wave per head; entries past the
+  // chunk end repeat the last value (their log-decay is 0) and get weight 0
   if (wid < HB) {
     const int h = h0 + wid;
     float run[R];
@@ -97,60 +112,112 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
     }
     const float incl = wave_inclusive_sum(acc);
     const float excl = incl - acc;
+    const float lam = __shfl(incl, 63);
     float* gout = ws.acs + (k * H + h) * Q + lane * R;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float a = excl + run[i];
-      acs_s[wid * Q + lane * R + i] = a;
       gout[i] = a;
+      w_s[wid * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
     }
-    if (lane == 63) ws.lam[k * H + h] = incl;
+    if (lane == 63) ws.lam[k * H + h] = lam;
   }
 
+  // ---- K3: S^T = B^T (w o X) per head.  Tile assignment: with at least four
+  // n tiles, wave w takes n tiles w, w+4, ... for both p tiles (one B^T operand
+  // read serves two MFMAs); otherwise one (n, p) tile per wave.
   constexpr int NTN = NT / 32;
-  constexpr int NTILES = (P / 32) * NTN;
+  constexpr bool kWide = NTN >= 4;
+  constexpr int NPW = kWide ? NTN / 4 : 1;
+  constexpr int PPW = kWide ? P / 32 : 1;
+  const bool active = kWide || wid < NTN * (P / 32);
+  auto n_tile = [&](int i) { return kWide ? wid + 4 * i : wid % NTN; };
+  auto p_tile = [&](int j) { return kWide ? j : wid / NTN; };
+  // 16-byte vectors of one (P x N) state, and per thread
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int NV = P * N / VEC;
+  constexpr int VPT = (NV + kThreads - 1) / kThreads;
+
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
-    lds_barrier();  // Acs ready; previous head's x^T no longer read
-    if (tid < Q) {
-      const float lam = acs_s[hh * Q + Q - 1];  // entries past L repeat the last one
-      w_s[tid] = (tid < L) ? __expf(lam - acs_s[hh * Q + tid]) : 0.0f;
-    }
-    lds_barrier();
-    xt.template store<QP, true>(xwT, w_s);
+    lds_barrier();  // w ready; the previous head's x^T and state rows no longer read
+    xt.template store<QP, true>(xwT, w_s + hh * Q);
     lds_barrier();
     if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
 
-    T* out = reinterpret_cast<T*>(ws.states) + (k * H + h) * (int64_t)(P * N);
-    float* out32 = states_f32 ? states_f32 + (k * H + h) * (int64_t)(P * N) : nullptr;
-    for (int t = wid; t < NTILES; t += kThreads / 64) {
-      const int pt = t / NTN, nt = t % NTN;
-      floatx16_t acc = zero16();
-      const T* arow = xwT + (pt * 32 + lr) * QP;
-      const T* brow = bT + (nt * 32 + lr) * QP;
-      if constexpr (E::kBytes == 2) {
+    if (active) {
+      floatx16_t acc[NPW][PPW];
+#pragma unroll
+      for (int i = 0; i < NPW; ++i)
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) acc[i][j] = zero16();
+      if constexpr (kBf16) {
 #pragma unroll 4
         for (int ks = 0; ks < Q / 16; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(arow + ks * 16 + lg * 8);
-          const uint4 b = *reinterpret_cast<const uint4*>(brow + ks * 16 + lg * 8);
-          acc = mfma32x32x16(a, b, acc);
+          uint4 a[NPW], b[PPW];
+#pragma unroll
+          for (int i = 0; i < NPW; ++i)
+            a[i] = *reinterpret_cast<const uint4*>(bT + (n_tile(i) * 32 + lr) * QP + ks * 16 + lg * 8);
+#pragma unroll
+          for (int j = 0; j < PPW; ++j)
+            b[j] = *reinterpret_cast<const uint4*>(xwT + (p_tile(j) * 32 + lr) * QP + ks * 16 + lg * 8);
+#pragma unroll
+          for (int i = 0; i < NPW; ++i)
+#pragma unroll
+            for (int j = 0; j < PPW; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
         }
       } else {
 #pragma unroll 8
-        for (int ks = 0; ks < Q / 2; ++ks) acc = mfma32x32x2(arow[ks * 2 + lg], brow[ks * 2 + lg], acc);
-      }
-      const int n = nt * 32 + lr;
-      if (n < N) {
+        for (int ks = 0; ks < Q / 2; ++ks) {
+          float a[NPW], b[PPW];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int pp = pt * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-          if constexpr (E::kBytes == 2) {
-            const uint32_t b2 = pack_bf16x2(acc[r], 0.0f);
-            out[pp * N + n] = (uint16_t)(b2 & 0xffffu);
-            if (out32) out32[pp * N + n] = bf16_lo(b2);
+          for (int i = 0; i < NPW; ++i) a[i] = bT[(n_tile(i) * 32 + lr) * QP + ks * 2 + lg];
+#pragma unroll
+          for (int j = 0; j < PPW; ++j) b[j] = xwT[(p_tile(j) * 32 + lr) * QP + ks * 2 + lg];
+#pragma unroll
+          for (int i = 0; i < NPW; ++i)
+#pragma unroll
+            for (int j = 0; j < PPW; ++j) acc[i][j] = mfma32x32x2(a[i], b[j], acc[i][j]);
+        }
+      }
+      // acc[i][j][4q + e] = S[p = 32 p_tile(j) + lr][n = 32 n_tile(i) + 8q + 4lg + e]
+#pragma unroll
+      for (int i = 0; i < NPW; ++i)
+#pragma unroll
+        for (int j = 0; j < PPW; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n0 = n_tile(i) * 32 + 8 * q + 4 * lg;
+            if (NT == N || n0 < N) {
+              T* dst = Ss + (p_tile(j) * 32 + lr) * SP + n0;
+              const floatx16_t& c = acc[i][j];
+              if constexpr (kBf16)
+                *reinterpret_cast<uint2*>(dst) =
+                    make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
+              else
+                *reinterpret_cast<float4*>(dst) = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+            }
+          }
+    }
+    lds_barrier();
+    // the state of (chunk, head) is one contiguous (P x N) block: whole 16-byte vectors
+    T* out = reinterpret_cast<T*>(ws.states) + (k * H + h) * (int64_t)(P * N);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = tid + i * kThreads;
+      if (NV % kThreads == 0 || v < NV) {
+        const int row = v / (N / VEC), col = (v % (N / VEC)) * VEC;
+        const uint4 val = *reinterpret_cast<const uint4*>(Ss + row * SP + col);
+        reinterpret_cast<uint4*>(out)[v] = val;
+        if constexpr (kDebug) {
+          float* o32 = states_f32 + (k * H + h) * (int64_t)(P * N) + (int64_t)v * VEC;
+          if constexpr (kBf16) {
+            reinterpret_cast<float4*>(o32)[0] =
+                make_float4(bf16_lo(val.x), bf16_hi(val.x), bf16_lo(val.y), bf16_hi(val.y));
+            reinterpret_cast<float4*>(o32)[1] =
+                make_float4(bf16_lo(val.z), bf16_hi(val.z), bf16_lo(val.w), bf16_hi(val.w));
           } else {
-            out[pp * N + n] = acc[r];
-            if (out32) out32[pp * N + n] = acc[r];
+            reinterpret_cast<uint4*>(o32)[0] = val;
           }
         }
       }
@@ -169,8 +236,12 @@ static hipError_t launch_cs(const Problem& p, const Workspace& ws, float* states
   if constexpr (ChunkStateCfg<E, Q, N>::fits) {
     const int HB = chunk_state_heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    hipLaunchKernelGGL((chunk_state_kernel<E, Q, N>), dim3(blocks), dim3(kThreads), 0, s, p, ws, HB,
-                       states_f32);
+    if (states_f32)
+      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, true>), dim3(blocks), dim3(kThreads), 0, s, p, ws,
+                         HB, states_f32);
+    else
+      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, false>), dim3(blocks), dim3(kThreads), 0, s, p,
+                         ws, HB, states_f32);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

@@ -1,7 +1,11 @@
 // ssd_stage.hpp -- global -> register -> LDS staging of chunk tiles.
 //
 // A chunk tile is ROWS consecutive packed tokens (zero past the chunk length
-// L) of COLS contiguous elements, rows `ld` elements apart in global memory.
+// L, L >= 1) of COLS contiguous elements, rows `ld` elements apart in global
+// memory.  Every load is issued unconditionally (row index clamped to L-1; the
+// rows past L become zeros when the tile is stored, not in the load registers,
+// which would force a wait for the loads), so the loads of a tile stay one
+// uninterrupted run and later waits can count them exactly.
 // Staging is split into load() (every global load of the thread issued back to
 // back into registers, so their latencies overlap) and store() (registers ->
 // LDS), so that a kernel can issue the loads of its next tile before computing
@@ -26,15 +30,16 @@ struct RowTile {
   static constexpr int NV = ROWS * VPR;
   static constexpr int NPT = (NV + NTHR - 1) / NTHR;
   uint4 v[NPT];
+  int len;  // rows >= len are stored as zeros
 
   __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int idx = threadIdx.x + i * NTHR;
+      const int idx = min((int)threadIdx.x + i * NTHR, NV - 1);
       const int r = idx / VPR, c = idx % VPR;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (idx < NV && r < L) v[i] = *reinterpret_cast<const uint4*>(g + r * ld + c * VEC);
+      v[i] = *reinterpret_cast<const uint4*>(g + min(r, L - 1) * ld + c * VEC);
     }
+    len = L;
   }
   template <int DP>
   __device__ __forceinline__ void store(T* __restrict__ lds) const {
@@ -42,7 +47,7 @@ struct RowTile {
     for (int i = 0; i < NPT; ++i) {
       const int idx = threadIdx.x + i * NTHR;
       const int r = idx / VPR, c = idx % VPR;
-      if (idx < NV) *reinterpret_cast<uint4*>(lds + r * DP + c * VEC) = v[i];
+      if (idx < NV) *reinterpret_cast<uint4*>(lds + r * DP + c * VEC) = r < len ? v[i] : make_uint4(0, 0, 0, 0);
     }
   }
 };
@@ -57,19 +62,22 @@ struct TransTile {
   static constexpr int NB = (ROWS / BS) * CB;
   static constexpr int NPT = (NB + NTHR - 1) / NTHR;
   uint4 v[NPT][BS];
+  int len;  // rows >= len are stored as zeros
 
   __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int blk = threadIdx.x + i * NTHR;
+      const int blk = min((int)threadIdx.x + i * NTHR, NB - 1);
       const int cb = blk % CB, rb = blk / CB;
 #pragma unroll
-      for (int rr = 0; rr < BS; ++rr) {
-        const int r = rb * BS + rr;
-        v[i][rr] = make_uint4(0, 0, 0, 0);
-        if (blk < NB && r < L) v[i][rr] = *reinterpret_cast<const uint4*>(g + r * ld + cb * BS);
-      }
+      for (int rr = 0; rr < BS; ++rr)
+        v[i][rr] = *reinterpret_cast<const uint4*>(g + min(rb * BS + rr, L - 1) * ld + cb * BS);
     }
+    len = L;
+  }
+  // row rr of block i as loaded, or zeros past the tile's length
+  __device__ __forceinline__ uint4 row(int i, int rb, int rr) const {
+    return rb * BS + rr < len ? v[i][rr] : make_uint4(0, 0, 0, 0);
   }
 
   // scale: per-row factors in LDS (read only when SCALE).
@@ -92,7 +100,7 @@ struct TransTile {
           float f[8];
 #pragma unroll
           for (int rr = 0; rr < 8; ++rr) {
-            const uint4 q = v[i][rr];
+            const uint4 q = row(i, rb, rr);
             const uint32_t w = (c >> 1) == 0 ? q.x : (c >> 1) == 1 ? q.y : (c >> 1) == 2 ? q.z : q.w;
             const float e = (c & 1) ? bf16_hi(w) : bf16_lo(w);
             f[rr] = SCALE ? e * sc[rr] : e;
@@ -115,7 +123,7 @@ struct TransTile {
         float f[4][4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const uint4 q = v[i][rr];
+          const uint4 q = row(i, rb, rr);
           f[rr][0] = __uint_as_float(q.x) * sc[rr];
           f[rr][1] = __uint_as_float(q.y) * sc[rr];
           f[rr][2] = __uint_as_float(q.z) * sc[rr];
