@@ -21,7 +21,9 @@
 // B tile is staged transposed in LDS once (tokens contiguous, as an MFMA
 // operand contracting over tokens needs) and serves all HB heads; each head's
 // x tile is loaded into registers while the previous head computes, then scaled
-// by w and transposed into LDS.  The product is formed as S^T (N x P) on 32x32
+// by w and transposed into LDS (bf16 rows unpadded, their 16-byte blocks
+// XOR-swizzled by row so that neither the transposing stores nor the MFMA
+// operand reads meet LDS bank conflicts).  The product is formed as S^T (N x P) on 32x32
 // tiles (v_mfma_f32_32x32x16_bf16 / _32x32x2_f32, fp32 accumulation), so that
 // each lane ends with runs of 4 consecutive n of one p; the tile passes through
 // LDS in [p][n] order and leaves as whole 16-byte vectors, the (P x N) state
@@ -38,7 +40,8 @@ struct ChunkStateCfg {
   using T = typename E::storage;
   static constexpr int P = kHeadDim;
   static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int QP = Q + PAD;          // LDS pitch of the transposed tiles
+  static constexpr bool SWZ = E::kBytes == 2;  // bf16: swizzled, unpadded transposed tiles
+  static constexpr int QP = SWZ ? Q : Q + PAD;  // LDS pitch of the transposed tiles
   static constexpr int NT = N < 32 ? 32 : N;  // B^T rows, padded to an MFMA tile
   static constexpr int SP = N + PAD;          // LDS pitch of the staged state rows
   static constexpr size_t lds_bytes = (size_t)(P + NT) * QP * sizeof(T) + (size_t)P * SP * sizeof(T) +
@@ -53,6 +56,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
   using T = typename E::storage;
   constexpr bool kBf16 = E::kBytes == 2;
   constexpr int P = Cfg::P, QP = Cfg::QP, NT = Cfg::NT, SP = Cfg::SP;
+  constexpr bool SWZ = Cfg::SWZ;
   constexpr int R = Q / 64;  // tokens per lane in the cumsum
   __shared__ __attribute__((aligned(16))) T xwT[P * QP];
   __shared__ __attribute__((aligned(16))) T bT[NT * QP];
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
   }
   if (NT > N)
     for (int i = tid; i < (NT - N) * QP; i += kThreads) bT[N * QP + i] = T(0);
-  bt.template store<QP, false>(bT, nullptr);
+  bt.template store<QP, false, false, SWZ>(bT, nullptr);
   lds_barrier();
 
   // ---- K1: chunk-local inclusive cumsum, one wave per head; entries past the
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
     lds_barrier();  // w ready; the previous head's x^T and state rows no longer read
-    xt.template store<QP, true>(xwT, w_s + hh * Q);
+    xt.template store<QP, true, false, SWZ>(xwT, w_s + hh * Q);
     lds_barrier();
     if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
 
@@ -152,19 +156,37 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
 #pragma unroll
         for (int j = 0; j < PPW; ++j) acc[i][j] = zero16();
       if constexpr (kBf16) {
-#pragma unroll 4
-        for (int ks = 0; ks < Q / 16; ++ks) {
-          uint4 a[NPW], b[PPW];
+        // 16-byte block 2 ks + lg of each operand row, at its swizzled place
+        int akey[NPW], bkey[PPW];
+#pragma unroll
+        for (int i = 0; i < NPW; ++i) akey[i] = lds_swizzle<Q>(n_tile(i) * 32 + lr);
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) bkey[j] = lds_swizzle<Q>(p_tile(j) * 32 + lr);
+        // operands of step ks + 2 are read while step ks multiplies (LDS latency
+        // is several MFMA steps): a ring of three register sets, fully unrolled
+        constexpr int KSTEPS = Q / 16;
+        uint4 a[3][NPW], b[3][PPW];
+        auto read_ops = [&](int ks, uint4 (&ar)[NPW], uint4 (&br)[PPW]) {
 #pragma unroll
           for (int i = 0; i < NPW; ++i)
-            a[i] = *reinterpret_cast<const uint4*>(bT + (n_tile(i) * 32 + lr) * QP + ks * 16 + lg * 8);
+            ar[i] = *reinterpret_cast<const uint4*>(bT + (n_tile(i) * 32 + lr) * QP + ((2 * ks + lg) ^ akey[i]) * 8);
 #pragma unroll
           for (int j = 0; j < PPW; ++j)
-            b[j] = *reinterpret_cast<const uint4*>(xwT + (p_tile(j) * 32 + lr) * QP + ks * 16 + lg * 8);
+            br[j] = *reinterpret_cast<const uint4*>(xwT + (p_tile(j) * 32 + lr) * QP + ((2 * ks + lg) ^ bkey[j]) * 8);
+        };
+        read_ops(0, a[0], b[0]);
+        if (KSTEPS > 1) read_ops(1, a[1], b[1]);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          if (ks + 2 < KSTEPS) read_ops(ks + 2, a[(ks + 2) % 3], b[(ks + 2) % 3]);
+          // keep the reads ahead: the scheduler would otherwise sink each read
+          // next to its MFMA and wait for it there
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < NPW; ++i)
 #pragma unroll
-            for (int j = 0; j < PPW; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < PPW; ++j) acc[i][j] = mfma32x32x16(a[ks % 3][i], b[ks % 3][j], acc[i][j]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll 8

@@ -52,6 +52,22 @@ struct RowTile {
   }
 };
 
+// XOR swizzle of the 16-byte blocks of a transposed bf16 tile (rows of ROWS
+// tokens, no padding): block b of LDS row r is stored at block b ^ key(r).
+// key takes 4 bits of r (3 when a row has only 8 blocks):
+//   k0 = r0^r3, k1 = r1^r5^r6, k2 = r2^r4, k3 = r3^r5.
+// It makes both access patterns free of bank conflicts: the transposing
+// stores, where the lanes of one store phase write the same token block of
+// rows 8 apart, and the MFMA operand reads, where they read the same block of
+// consecutive rows.
+template <int ROWS>
+__device__ __forceinline__ int lds_swizzle(int r) {
+  constexpr int mask = (ROWS / 8 >= 16 ? 16 : ROWS / 8) - 1;
+  const int k = ((r ^ (r >> 3)) & 1) | ((((r >> 1) ^ (r >> 5) ^ (r >> 6)) & 1) << 1) |
+                ((((r >> 2) ^ (r >> 4)) & 1) << 2) | ((((r >> 3) ^ (r >> 5)) & 1) << 3);
+  return k & mask;
+}
+
 template <class E, int ROWS, int COLS, int NTHR = kThreads>
 struct TransTile {
   using T = typename E::storage;
@@ -84,8 +100,11 @@ struct TransTile {
   // PERM16 (bf16 only): within every 16-token group the tokens are stored in
   // the order 0-3, 8-11, 4-7, 12-15, so that lane group g of a 32x32x16 MFMA
   // finds its tokens {4g..4g+3, 8+4g..8+4g+3} as one contiguous 16-byte run.
-  template <int DP, bool SCALE, bool PERM16 = false>
+  // SWZ (bf16 only, DP == ROWS): 16-byte blocks placed by lds_swizzle<ROWS>.
+  template <int DP, bool SCALE, bool PERM16 = false, bool SWZ = false>
   __device__ __forceinline__ void store(T* __restrict__ lds, const float* __restrict__ scale) const {
+    static_assert(!SWZ || (kBf16 && DP == ROWS), "the swizzled layout is unpadded bf16");
+    static_assert(!PERM16 || kBf16, "the 16-token permutation is for bf16 tiles");
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int blk = threadIdx.x + i * NTHR;
@@ -110,13 +129,16 @@ struct TransTile {
           o.y = pack_bf16x2(f[2], f[3]);
           o.z = pack_bf16x2(f[4], f[5]);
           o.w = pack_bf16x2(f[6], f[7]);
-          T* row = lds + (cb * 8 + c) * DP;
+          const int r = cb * 8 + c;
+          T* row = lds + r * DP;
+          const int key = SWZ ? lds_swizzle<ROWS>(r) : 0;
           if constexpr (PERM16) {
-            const int base = (rb >> 1) * 16 + (rb & 1) * 4;
-            *reinterpret_cast<uint2*>(row + base) = make_uint2(o.x, o.y);
-            *reinterpret_cast<uint2*>(row + base + 8) = make_uint2(o.z, o.w);
+            // tokens 16g + {0-3, 8-11} -> block 2g, {4-7, 12-15} -> block 2g+1
+            const int off = (rb & 1) * 4;
+            *reinterpret_cast<uint2*>(row + (((rb >> 1) * 2) ^ key) * 8 + off) = make_uint2(o.x, o.y);
+            *reinterpret_cast<uint2*>(row + (((rb >> 1) * 2 + 1) ^ key) * 8 + off) = make_uint2(o.z, o.w);
           } else {
-            *reinterpret_cast<uint4*>(row + rb * 8) = o;
+            *reinterpret_cast<uint4*>(row + (rb ^ key) * 8) = o;
           }
         }
       } else {
