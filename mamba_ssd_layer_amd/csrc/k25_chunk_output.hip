@@ -12,16 +12,15 @@
 // whole sequence.
 //
 // Design (gfx950):
-//  * The kernel matrix tiles G = C B^T of the chunk's B/C group come from the
-//    chunk kernel-matrix kernel (formed once per chunk and group, not per
-//    head), already in the per-lane MFMA register layout: each lane reloads a
-//    tile with coalesced 16-byte loads, two tiles in flight (L2-resident).
-//  * One workgroup of 4 waves per (chunk, block of HB heads of one group),
-//    about 53 KB of LDS, so two or three workgroups share a CU and one's loads
-//    and barriers overlap another's MFMA work.  Each wave's C rows stay in
-//    registers for all HB heads; the next head's x tile and passed state are
-//    loaded into registers while the current head computes.  Blocks are
-//    ordered so that the head blocks of one chunk land on one XCD.
+//  * One workgroup of 4 waves per (chunk, block of HB heads of one group) and
+//    one workgroup per CU (HB is chosen so that the grid fills the CUs in few
+//    rounds).  The whole chunk's kernel-matrix tiles G = C B^T of the group
+//    (formed once per chunk and group by the kernel-matrix kernel) are copied
+//    into LDS when the workgroup starts and serve all HB heads; each wave's C
+//    rows stay in registers for all heads.  The next head's x tile and passed
+//    state are loaded into registers while the current head computes, so the
+//    compute phase reads only LDS and registers.  Blocks are ordered so that
+//    the head blocks of one chunk land on one XCD.
 //  * The output is built transposed, Y^T (P x Q), on 32x32 MFMA tiles.  A
 //    kernel tile as G^T leaves each lane ONE output token i and 16 input
 //    tokens j, which is exactly the B-operand layout of Y^T += X^T (L o G)^T;
@@ -39,45 +38,57 @@
 //    exp(-inf) arithmetic).
 //  * Y_off uses the same lane layout: Hin (P x N, element dtype) is the A
 //    operand, the lane's C row the B operand, exp(Acs_i) one scalar per lane.
-//  * C rows come in the same per-lane operand order from the kernel-matrix
-//    kernel (contiguous loads); each finished row tile of y is passed through
-//    the wave's own LDS rows and written as whole 128-byte rows.
-//  * fp32 accumulation; y rounded once to the element dtype.
+//  * LDS operand reads are issued ahead of the MFMAs that use them (pinned by
+//    scheduling barriers); each finished row tile of y is passed through the
+//    wave's own LDS rows and written as whole 128-byte rows.
+//  * fp32 accumulation; y rounded once to the element dtype.  (fp32 inputs:
+//    the kernel tiles do not fit in LDS next to the fp32 x tile and are read
+//    from global memory instead.)
+#include <cmath>
+
 #include "ssd_stage.hpp"
 
 namespace ssd {
 
+constexpr int kCoThreads = 512;  // 8 waves: two per SIMD, one workgroup per CU
+
 template <class E, int Q, int N>
 struct ChunkOutputCfg {
   using T = typename E::storage;
+  static constexpr bool kBf16 = E::kBytes == 2;
   static constexpr int P = kHeadDim;
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int NP = N + PAD;  // LDS pitch of Hin rows
   static constexpr int QP = Q + PAD;  // LDS pitch of X^T rows
   static constexpr int YP = P + PAD;  // LDS pitch of a wave's staged output rows
-  static constexpr size_t lds_bytes =
-      ((size_t)P * QP + (size_t)P * NP + (size_t)(kThreads / 64) * 32 * YP) * sizeof(T) +
-      2 * Q * sizeof(float);
-  static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
-  static constexpr int KS = N / E::kMfmaK;                  // MFMA steps over N
-  static constexpr int CREG = E::kBytes == 2 ? KS * 4 : KS; // VGPRs of one row tile's C operand
-  static constexpr bool kKeepC = 2 * CREG <= 32;            // keep both row tiles' C across heads
+  static constexpr int NW = kCoThreads / 64;
   static constexpr int NI = Q / 32;
-  static constexpr int NTILE = NI * (NI + 1) / 2;           // causal 32x32 kernel tiles
-  static constexpr int GV = E::kBytes == 2 ? 2 : 4;         // 16-byte vectors per lane per tile
+  static constexpr int NTILE = NI * (NI + 1) / 2;            // causal 32x32 kernel tiles
+  static constexpr int GV = kBf16 ? 2 : 4;                   // 16-byte vectors per lane per tile
+  static constexpr int KS = N / E::kMfmaK;                   // MFMA steps over N
+  // work of a wave: one row tile; with 8 row tiles both 32-wide halves of P,
+  // with fewer row tiles one half (two waves share a row tile)
+  static constexpr int NPH = NI == 8 ? 2 : 1;
+  static constexpr size_t base_bytes =
+      ((size_t)P * QP + (size_t)P * NP + (size_t)NW * 32 * YP) * sizeof(T) + 2 * Q * sizeof(float);
+  static constexpr size_t g_bytes = (size_t)NTILE * GV * 64 * 16;
+  static constexpr bool kGLds = base_bytes + g_bytes <= (size_t)kLdsLimit;  // kernel tiles in LDS
+  static constexpr size_t lds_bytes = base_bytes + (kGLds ? g_bytes : 0);
+  static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
 };
 
 template <class E, int Q, int N>
-__global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
+__global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
   using Cfg = ChunkOutputCfg<E, Q, N>;
   using T = typename E::storage;
   constexpr int P = Cfg::P, NP = Cfg::NP, QP = Cfg::QP, KS = Cfg::KS, GV = Cfg::GV, YP = Cfg::YP;
-  constexpr bool kBf16 = E::kBytes == 2;
-  constexpr int NI = Cfg::NI;
+  constexpr bool kBf16 = Cfg::kBf16;
+  constexpr int NI = Cfg::NI, NTILE = Cfg::NTILE, NPH = Cfg::NPH;
   using CReg = typename std::conditional<kBf16, uint4, float>::type;
   __shared__ __attribute__((aligned(16))) T XT[P * QP];
   __shared__ __attribute__((aligned(16))) T Hs[P * NP];
-  __shared__ __attribute__((aligned(16))) T Ys[(kThreads / 64) * 32 * YP];
+  __shared__ __attribute__((aligned(16))) T Ys[Cfg::NW * 32 * YP];
+  __shared__ __attribute__((aligned(16))) uint4 Gs[Cfg::kGLds ? NTILE * GV * 64 : 1];
   __shared__ __attribute__((aligned(16))) float acs_s[Q];
   __shared__ __attribute__((aligned(16))) float w_s[Q];
 
@@ -95,36 +106,46 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Wo
   const int lr = lane & 31, lg = lane >> 5;
   const int nI = (L + 31) / 32;
 
+  // this wave's row tile I and first half-tile of P.  8 row tiles: waves w and
+  // w+4 (one SIMD) take row tiles w and 7-w, so every SIMD does the same
+  // causal work; 4 or 2 row tiles: one half of P each.
+  int I, ph0;
+  if (NI == 8) {
+    I = wid < 4 ? wid : 11 - wid;
+    ph0 = 0;
+  } else if (wid < NI) {
+    I = wid;
+    ph0 = 0;
+  } else {
+    I = 2 * NI - 1 - wid;  // negative for waves beyond 2 NI: idle
+    ph0 = 1;
+  }
+  const bool active = I >= 0 && I < nI;
+
   const T* xbase = reinterpret_cast<const T*>(p.x) + cd.t0 * H * P;
   // C rows as MFMA operand slices, lane after lane (written by the kernel-matrix kernel)
   const CReg* cop = reinterpret_cast<const CReg*>(ws.cop) + (k * G + g) * (int64_t)(NI * KS * 64) + lane;
   const T* hbase = reinterpret_cast<const T*>(ws.hin) + k * H * (int64_t)(P * N);
   const float* abase = ws.acs + k * H * Q;
-  // this lane's 16 values of every kernel tile of the chunk's group
-  const uint4* gtiles = reinterpret_cast<const uint4*>(
-      reinterpret_cast<const T*>(ws.cb) + (k * G + g) * (int64_t)(Cfg::NTILE * 64 * 16) + lane * 16);
+  // kernel tiles of the chunk's group: [tile][16-byte vector q][lane]
+  const uint4* gsrc = reinterpret_cast<const uint4*>(ws.cb) + (k * G + g) * (int64_t)(NTILE * GV * 64);
   T* ybase = reinterpret_cast<T*>(p.y) + cd.t0 * H * P;
 
-  // row tiles of this wave: w and 7-w (balanced causal work: tile I costs
-  // I+1 kernel tiles); chunks of 64 or 128 tokens have 2 or 4 row tiles
-  constexpr int NT = NI == 8 ? 2 : 1;
-  auto row_tile = [&](int t) { return t == 0 ? wid : 7 - wid; };
-
-  // C row of this lane's token as MFMA B-operand slices over N (coalesced)
-  auto load_c = [&](int I, CReg (&c)[KS]) {
+  // ---- issue the loads: kernel tiles (to LDS), first head's x / Hin / Acs, C rows
+  constexpr int GNV = Cfg::kGLds ? NTILE * GV * 64 : 1;
+  constexpr int GVPT = (GNV + kCoThreads - 1) / kCoThreads;
+  uint4 gtmp[GVPT];
+  if constexpr (Cfg::kGLds) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) c[ks] = cop[(I * KS + ks) * 64];
-  };
-  CReg ckeep[NT][KS];
-  if constexpr (Cfg::kKeepC) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (row_tile(t) < nI) load_c(row_tile(t), ckeep[t]);
+    for (int i = 0; i < GVPT; ++i) gtmp[i] = gsrc[min(tid + i * kCoThreads, GNV - 1)];
   }
 
-  TransTile<E, Q, P> xt;
-  RowTile<E, P, N> ht;
-  float a_own = 0.f, a_end = 0.f;
+  // every thread stages a 4-token block of x^T (bf16) and part of Hin
+  using XTile = TransTile<E, Q, P, kCoThreads, 4>;
+  XTile xt;
+  RowTile<E, P, N, kCoThreads> ht;
+  float a_own = 0.f, a_end = 0.f, dmax = 0.f;
+  float xa4[XTile::NPT][4], xae[XTile::NPT];  // Acs of this thread's x rows and of their tile end
   auto prefetch = [&](int h) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
     ht.load(hbase + h * (int64_t)(P * N), N, P);
@@ -132,211 +153,277 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_kernel(Problem p, Wo
       a_own = abase[h * Q + tid];
       a_end = abase[h * Q + (tid | 31)];
     }
+#pragma unroll
+    for (int i = 0; i < XTile::NPT; ++i) {
+      const int r0 = XTile::first_row(i);
+      const float4 a4 = *reinterpret_cast<const float4*>(abase + h * Q + r0);
+      xa4[i][0] = a4.x; xa4[i][1] = a4.y; xa4[i][2] = a4.z; xa4[i][3] = a4.w;
+      xae[i] = abase[h * Q + (r0 | 31)];
+    }
+    dmax = ws.dmax[k * H + h];
   };
   prefetch(h0);
+
+  // C row of this lane's token as MFMA B-operand slices over N (coalesced),
+  // kept in registers for all heads
+  CReg creg[KS];
+  if (active) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) creg[ks] = cop[(I * KS + ks) * 64];
+  }
+  if constexpr (Cfg::kGLds) {
+#pragma unroll
+    for (int i = 0; i < GVPT; ++i)
+      if (tid + i * kCoThreads < GNV) Gs[tid + i * kCoThreads] = gtmp[i];
+  }
 
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
     lds_barrier();  // every wave is done with the previous head's tiles
-    ht.template store<NP>(Hs);
+    ht.template store<NP, kBf16>(Hs);
     if (tid < Q) {
       acs_s[tid] = a_own;
       w_s[tid] = __expf(a_end - a_own);  // exp(Acs_e - Acs_j), e = end of j's tile
     }
-    lds_barrier();
-    // Fast path when no 32-token tile decays by more than e^64: then x is
-    // staged pre-scaled by w_j and the mask needs no per-element exp (see the
+    // Fast path when no 32-token tile decays by more than e^64 (the largest
+    // tile decay comes from the chunk-state kernel): then x is staged
+    // pre-scaled by w_j and the mask needs no per-element exp (see the
     // header); otherwise x is staged as is and every mask entry is exact.
-    float dmax = 0.0f;
-#pragma unroll
-    for (int J = 0; J < NI; ++J) dmax = fmaxf(dmax, acs_s[J * 32] - acs_s[J * 32 + 31]);
     const bool fast = dmax <= 64.0f;
-    if (fast)
-      xt.template store<QP, true, kBf16>(XT, w_s);
-    else
-      xt.template store<QP, false, kBf16>(XT, nullptr);
-    lds_barrier();
-    // C rows (when not kept): the first row tile's are loaded before the next
-    // head's prefetch so that waiting for them does not also wait for the
-    // prefetch; the second row tile's after the first row tile's work
-    CReg cfresh[KS];
-    if constexpr (!Cfg::kKeepC) {
-      if (row_tile(0) < nI) load_c(row_tile(0), cfresh);
-    }
-    if (hh + 1 < HB) prefetch(h + 1);
-
+    if (fast) {
+      float sreg[XTile::NPT][4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int I = row_tile(t);
-      if (I >= nI) continue;
-      const int i_loc = I * 32 + lr;
-      if constexpr (!Cfg::kKeepC) {
-        if (t > 0) load_c(I, cfresh);
-      }
-      const CReg (&creg)[KS] = Cfg::kKeepC ? ckeep[t] : cfresh;
-      floatx16_t acc0 = zero16(), acc1 = zero16();
-      // Y_off^T = Hin C^T (contraction over N), then the exp(Acs_i) factor
+      for (int i = 0; i < XTile::NPT; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf(xae[i] - xa4[i][rr]);
+      xt.template store<QP, 2, kBf16, false, kBf16>(XT, nullptr, sreg);
+    } else {
+      xt.template store<QP, 0, kBf16, false, kBf16>(XT, nullptr);
+    }
+    lds_barrier();
+    if (hh + 1 < HB) prefetch(h + 1);
+    if (!active) continue;
+
+    const int i_loc = I * 32 + lr;
+    floatx16_t acc[NPH];
+#pragma unroll
+    for (int j = 0; j < NPH; ++j) acc[j] = zero16();
+    // rows of X^T and Hin (p) this wave's halves read
+    auto prow = [&](int j) { return (ph0 + j) * 32 + lr; };
+
+    // Y_off^T = Hin C^T (contraction over N), then the exp(Acs_i) factor
+    if constexpr (kBf16) {
+      // Hin operands of step ks + 2 are read while step ks multiplies
+      uint4 ha[3][NPH];
+      auto read_h = [&](int ks, uint4 (&r)[NPH]) {
+#pragma unroll
+        for (int j = 0; j < NPH; ++j)
+          r[j] = *reinterpret_cast<const uint4*>(Hs + prow(j) * NP + ks * 16 + lg * 8);
+      };
+      read_h(0, ha[0]);
+      if (KS > 1) read_h(1, ha[1]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (kBf16) {
-          const uint4 a0 = *reinterpret_cast<const uint4*>(Hs + lr * NP + ks * 16 + lg * 8);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(Hs + (32 + lr) * NP + ks * 16 + lg * 8);
-          acc0 = mfma32x32x16(a0, creg[ks], acc0);
-          acc1 = mfma32x32x16(a1, creg[ks], acc1);
-        } else {
-          acc0 = mfma32x32x2(Hs[lr * NP + ks * 2 + lg], creg[ks], acc0);
-          acc1 = mfma32x32x2(Hs[(32 + lr) * NP + ks * 2 + lg], creg[ks], acc1);
-        }
+        if (ks + 2 < KS) read_h(ks + 2, ha[(ks + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x16(ha[ks % 3][j], creg[ks], acc[j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const float ai = acs_s[i_loc];
-      const float eo = __expf(ai);
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { acc0[r] *= eo; acc1[r] *= eo; }
-
-      // diagonal block: kernel tiles J <= I of row tile I (consecutive tiles)
-      const uint4* grow = gtiles + (int64_t)(I * (I + 1) / 2) * (64 * 16 * sizeof(T) / 16);
-      auto load_g = [&](int J, uint4 (&gv)[GV]) {
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int q = 0; q < GV; ++q) gv[q] = grow[(int64_t)J * (64 * 16 * sizeof(T) / 16) + q];
-      };
-      auto tile = [&](int J, const uint4 (&gv)[GV]) {
-        // gt[r] = G[i_loc][j_r], j_r = 32J + 8(r/4) + 4 lg + r%4
-        float gt[16];
-        if constexpr (kBf16) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            gt[8 * q + 0] = bf16_lo(gv[q].x); gt[8 * q + 1] = bf16_hi(gv[q].x);
-            gt[8 * q + 2] = bf16_lo(gv[q].y); gt[8 * q + 3] = bf16_hi(gv[q].y);
-            gt[8 * q + 4] = bf16_lo(gv[q].z); gt[8 * q + 5] = bf16_hi(gv[q].z);
-            gt[8 * q + 6] = bf16_lo(gv[q].w); gt[8 * q + 7] = bf16_hi(gv[q].w);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            gt[4 * q + 0] = __uint_as_float(gv[q].x); gt[4 * q + 1] = __uint_as_float(gv[q].y);
-            gt[4 * q + 2] = __uint_as_float(gv[q].z); gt[4 * q + 3] = __uint_as_float(gv[q].w);
-          }
-        }
-        float v[16];
-        if (fast) {
-          // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
-          // exp(Acs_i - Acs_e) (<= 1 below the diagonal, <= e^64 on it)
-          const float u = __expf(ai - acs_s[J * 32 + 31]);
-          if (J < I) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = gt[r] * u;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
-              v[r] = (jr <= lr) ? gt[r] * u : 0.0f;
-            }
-          }
-        } else if (J < I) {
-          const float u = __expf(ai - acs_s[J * 32 + 31]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 w4 = *reinterpret_cast<const float4*>(w_s + J * 32 + q * 8 + lg * 4);
-            v[4 * q + 0] = gt[4 * q + 0] * (u * w4.x);
-            v[4 * q + 1] = gt[4 * q + 1] * (u * w4.y);
-            v[4 * q + 2] = gt[4 * q + 2] * (u * w4.z);
-            v[4 * q + 3] = gt[4 * q + 3] * (u * w4.w);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-            const float m = __expf(ai - acs_s[j]);
-            v[r] = (j <= i_loc) ? gt[r] * m : 0.0f;
-          }
-        }
-        // Y^T += X^T (L o G)^T over the 32 tokens of tile J
-        if constexpr (kBf16) {
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            uint4 bop;
-            bop.x = pack_bf16x2(v[8 * kk + 0], v[8 * kk + 1]);
-            bop.y = pack_bf16x2(v[8 * kk + 2], v[8 * kk + 3]);
-            bop.z = pack_bf16x2(v[8 * kk + 4], v[8 * kk + 5]);
-            bop.w = pack_bf16x2(v[8 * kk + 6], v[8 * kk + 7]);
-            // tokens are permuted within 16-groups: this lane group's 8 are contiguous
-            const int col = J * 32 + kk * 16 + lg * 8;
-            const uint4 a0 = *reinterpret_cast<const uint4*>(XT + lr * QP + col);
-            const uint4 a1 = *reinterpret_cast<const uint4*>(XT + (32 + lr) * QP + col);
-            acc0 = mfma32x32x16(a0, bop, acc0);
-            acc1 = mfma32x32x16(a1, bop, acc1);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-            acc0 = mfma32x32x2(XT[lr * QP + j], v[r], acc0);
-            acc1 = mfma32x32x2(XT[(32 + lr) * QP + j], v[r], acc1);
-          }
-        }
-      };
-      // two register buffers used in turn: the next tile's loads are in flight
-      // while the current one is masked and multiplied (loads past I are clamped)
-      uint4 gA[GV], gB[GV];
-      load_g(0, gA);
-      for (int J = 0; J <= I; J += 2) {
-        load_g(min(J + 1, I), gB);
-        tile(J, gA);
-        if (J + 1 > I) break;
-        load_g(min(J + 2, I), gA);
-        tile(J + 1, gB);
-      }
-      // store: lane holds y[i_loc][p] for p = 32 pt + 8(r/4) + 4 lg + r%4.  The
-      // row tile goes through this wave's LDS rows so that global stores are
-      // whole 128-byte rows (eight lanes per row) instead of 32 scattered pieces.
-      T* ys = Ys + wid * 32 * YP;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int pp = q * 8 + lg * 4;
-        if constexpr (kBf16) {
-          uint2 o0, o1;
-          o0.x = pack_bf16x2(acc0[4 * q + 0], acc0[4 * q + 1]);
-          o0.y = pack_bf16x2(acc0[4 * q + 2], acc0[4 * q + 3]);
-          o1.x = pack_bf16x2(acc1[4 * q + 0], acc1[4 * q + 1]);
-          o1.y = pack_bf16x2(acc1[4 * q + 2], acc1[4 * q + 3]);
-          *reinterpret_cast<uint2*>(ys + lr * YP + pp) = o0;
-          *reinterpret_cast<uint2*>(ys + lr * YP + 32 + pp) = o1;
-        } else {
-          *reinterpret_cast<float4*>(ys + lr * YP + pp) =
-              make_float4(acc0[4 * q + 0], acc0[4 * q + 1], acc0[4 * q + 2], acc0[4 * q + 3]);
-          *reinterpret_cast<float4*>(ys + lr * YP + 32 + pp) =
-              make_float4(acc1[4 * q + 0], acc1[4 * q + 1], acc1[4 * q + 2], acc1[4 * q + 3]);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      constexpr int VPR = P * sizeof(T) / 16;   // 16-byte vectors per output row
-      constexpr int RPI = 64 / VPR;             // rows per store instruction
-#pragma unroll
-      for (int st = 0; st < 32 / RPI; ++st) {
-        const int row = st * RPI + lane / VPR;
-        const int vec = lane % VPR;
-        const int i_row = I * 32 + row;
-        const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
-        if (i_row < L)
-          *reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + vec * (16 / sizeof(T))) = val;
-      }
-      __builtin_amdgcn_wave_barrier();
+        for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x2(Hs[prow(j) * NP + ks * 2 + lg], creg[ks], acc[j]);
     }
+    const float ai = acs_s[i_loc];
+    const float eo = __expf(ai);
+#pragma unroll
+    for (int j = 0; j < NPH; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] *= eo;
+
+    // diagonal block: kernel tiles J <= I of row tile I (consecutive tiles)
+    const int tile0 = I * (I + 1) / 2;
+    auto load_g = [&](int J, uint4 (&gv)[GV]) {
+#pragma unroll
+      for (int q = 0; q < GV; ++q) {
+        if constexpr (Cfg::kGLds)
+          gv[q] = Gs[((tile0 + J) * GV + q) * 64 + lane];
+        else
+          gv[q] = gsrc[((tile0 + J) * GV + q) * 64 + lane];
+      }
+    };
+    auto tile = [&](int J, const uint4 (&gv)[GV]) {
+      // this lane group's x^T operands of tile J (issued before the mask math)
+      uint4 xa[2][NPH];
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          // tokens are permuted within 16-groups: this lane group's 8 are contiguous
+          const int col = J * 32 + kk * 16 + lg * 8;
+#pragma unroll
+          for (int j = 0; j < NPH; ++j) xa[kk][j] = *reinterpret_cast<const uint4*>(XT + prow(j) * QP + col);
+        }
+      }
+      // gt[r] = G[i_loc][j_r], j_r = 32J + 8(r/4) + 4 lg + r%4
+      float gt[16];
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          gt[8 * q + 0] = bf16_lo(gv[q].x); gt[8 * q + 1] = bf16_hi(gv[q].x);
+          gt[8 * q + 2] = bf16_lo(gv[q].y); gt[8 * q + 3] = bf16_hi(gv[q].y);
+          gt[8 * q + 4] = bf16_lo(gv[q].z); gt[8 * q + 5] = bf16_hi(gv[q].z);
+          gt[8 * q + 6] = bf16_lo(gv[q].w); gt[8 * q + 7] = bf16_hi(gv[q].w);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gt[4 * q + 0] = __uint_as_float(gv[q].x); gt[4 * q + 1] = __uint_as_float(gv[q].y);
+          gt[4 * q + 2] = __uint_as_float(gv[q].z); gt[4 * q + 3] = __uint_as_float(gv[q].w);
+        }
+      }
+      float v[16];
+      if (fast) {
+        // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
+        // exp(Acs_i - Acs_e) (<= 1 below the diagonal, <= e^64 on it)
+        const float u = __expf(ai - acs_s[J * 32 + 31]);
+        if (J < I) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = gt[r] * u;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
+            v[r] = (jr <= lr) ? gt[r] * u : 0.0f;
+          }
+        }
+      } else if (J < I) {
+        const float u = __expf(ai - acs_s[J * 32 + 31]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 w4 = *reinterpret_cast<const float4*>(w_s + J * 32 + q * 8 + lg * 4);
+          v[4 * q + 0] = gt[4 * q + 0] * (u * w4.x);
+          v[4 * q + 1] = gt[4 * q + 1] * (u * w4.y);
+          v[4 * q + 2] = gt[4 * q + 2] * (u * w4.z);
+          v[4 * q + 3] = gt[4 * q + 3] * (u * w4.w);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+          const float m = __expf(ai - acs_s[j]);
+          v[r] = (j <= i_loc) ? gt[r] * m : 0.0f;
+        }
+      }
+      // Y^T += X^T (L o G)^T over the 32 tokens of tile J
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          uint4 bop;
+          bop.x = pack_bf16x2(v[8 * kk + 0], v[8 * kk + 1]);
+          bop.y = pack_bf16x2(v[8 * kk + 2], v[8 * kk + 3]);
+          bop.z = pack_bf16x2(v[8 * kk + 4], v[8 * kk + 5]);
+          bop.w = pack_bf16x2(v[8 * kk + 6], v[8 * kk + 7]);
+#pragma unroll
+          for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x16(xa[kk][j], bop, acc[j]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
+#pragma unroll
+          for (int jj = 0; jj < NPH; ++jj) acc[jj] = mfma32x32x2(XT[prow(jj) * QP + j], v[r], acc[jj]);
+        }
+      }
+    };
+    // two register buffers used in turn: the next tile's operands are being
+    // read while the current one is masked and multiplied (clamped past I)
+    uint4 gA[GV], gB[GV];
+    load_g(0, gA);
+    for (int J = 0; J <= I; J += 2) {
+      load_g(min(J + 1, I), gB);
+      tile(J, gA);
+      if (J + 1 > I) break;
+      load_g(min(J + 2, I), gA);
+      tile(J + 1, gB);
+    }
+    // store: lane holds Y^T row pr = 32 (ph0 + j) + 8(r/4) + 4 lg + r%4 of token
+    // i_loc; bf16 rows are permuted (lds_row_perm), so its p is pr ^ c with
+    // c = 4 ((ph0 + j) & 1) + r/4: the four values of a group r/4 = q land in
+    // the 4-group 8q + 4 (lg ^ ((ph0 + j) & 1)), value e at position e ^ q.
+    // The row tile goes through this wave's LDS rows so that global stores are
+    // whole rows (of the wave's part of P) instead of scattered pieces.
+    T* ys = Ys + wid * 32 * YP;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < NPH; ++j) {
+        if constexpr (kBf16) {
+          const int pp = q * 8 + 4 * (lg ^ ((ph0 + j) & 1));
+          const floatx16_t& a = acc[j];
+          *reinterpret_cast<uint2*>(ys + lr * YP + 32 * j + pp) =
+              make_uint2(pack_bf16x2(a[4 * q + (0 ^ q)], a[4 * q + (1 ^ q)]),
+                         pack_bf16x2(a[4 * q + (2 ^ q)], a[4 * q + (3 ^ q)]));
+        } else {
+          const int pp = q * 8 + lg * 4;
+          *reinterpret_cast<float4*>(ys + lr * YP + 32 * j + pp) =
+              make_float4(acc[j][4 * q + 0], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    constexpr int VPR = NPH * 32 * sizeof(T) / 16;  // 16-byte vectors per output row
+    constexpr int RPI = 64 / VPR;                   // rows per store instruction
+#pragma unroll
+    for (int s = 0; s < 32 / RPI; ++s) {
+      const int row = s * RPI + lane / VPR;
+      const int vec = lane % VPR;
+      const int i_row = I * 32 + row;
+      const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
+      if (i_row < L)
+        *reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))) =
+            val;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
-// Heads per workgroup: the largest of 4, 2, 1 that divides the heads of a group.
-int chunk_output_heads_per_block(const Problem& p) {
+// Heads per workgroup: a divisor of the heads of a group (8, 4, 2 or 1), one
+// workgroup per CU; the choice minimises rounds of workgroups x (heads per
+// workgroup + one head's worth of start-up work).
+int chunk_output_heads_per_block(const Problem& p, int num_cus) {
   const int hpg = p.H / p.G;
-  return hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
+  int best = 1;
+  double best_cost = -1.0;
+  for (int hb = 8; hb >= 1; hb /= 2) {
+    if (hpg % hb) continue;
+    const double wgs = (double)p.kmax * (p.H / hb);
+    const double rounds = std::ceil(wgs / (double)(num_cus > 0 ? num_cus : 256));
+    const double cost = rounds * (hb + 1);
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = hb; }
+  }
+  return best;
+}
+
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <class E, int Q, int N>
 static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s) {
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
-    const int HB = chunk_output_heads_per_block(p);
+    const int HB = chunk_output_heads_per_block(p, device_cus());
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    hipLaunchKernelGGL((chunk_output_kernel<E, Q, N>), dim3(blocks), dim3(kThreads), 0, s, p, ws, HB);
+    hipLaunchKernelGGL((chunk_output_kernel<E, Q, N>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

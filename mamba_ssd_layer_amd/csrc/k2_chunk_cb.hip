@@ -13,9 +13,10 @@
 // fp32 path).  Both operands are loaded straight from global memory into the
 // MFMA register layout, all loads of a wave issued at once (no LDS, a single
 // memory latency per wave); there are many more waves than CUs.  A tile is
-// stored exactly as the accumulator lies in the registers: lane l's 16 values,
-// lane after lane, so the output kernel reloads it with fully coalesced 16-byte
-// loads into the register layout its masked product needs.  The wave of tile
+// stored as the accumulator lies in the registers: lane l's 16 values as 16-byte
+// vectors, vector-major and lane after lane within a vector, so the output
+// kernel copies a tile with fully coalesced loads and reads it back (from LDS)
+// straight into the register layout its masked product needs.  The wave of tile
 // (I, 0) also stores the C rows of row tile I as MFMA operand slices in the same
 // lane-after-lane order (a straight C row load touches 32 rows per
 // instruction; this copy is read back 1 KB-contiguous per instruction).  Tiles are in the element dtype (bf16: rounded to
@@ -81,20 +82,22 @@ __global__ __launch_bounds__(kThreads) void chunk_cb_kernel(Problem p, Workspace
     else
       acc = mfma32x32x2(breg[ks], creg[ks], acc);
   }
-  // acc[r] = G[32I + lr][32J + 8(r/4) + 4 lg + r%4]
-  T* tile = reinterpret_cast<T*>(ws.cb) + (kg * NTILE + ti) * (int64_t)(64 * 16) + lane * 16;
+  // acc[r] = G[32I + lr][32J + 8(r/4) + 4 lg + r%4]; the lane's values leave as
+  // 16-byte vectors q, stored [tile][q][lane]
+  constexpr int GV = kBf16 ? 2 : 4;
+  uint4* tile = reinterpret_cast<uint4*>(ws.cb) + (kg * NTILE + ti) * (int64_t)(GV * 64) + lane;
   if constexpr (kBf16) {
     uint4 o0, o1;
     o0.x = pack_bf16x2(acc[0], acc[1]);   o0.y = pack_bf16x2(acc[2], acc[3]);
     o0.z = pack_bf16x2(acc[4], acc[5]);   o0.w = pack_bf16x2(acc[6], acc[7]);
     o1.x = pack_bf16x2(acc[8], acc[9]);   o1.y = pack_bf16x2(acc[10], acc[11]);
     o1.z = pack_bf16x2(acc[12], acc[13]); o1.w = pack_bf16x2(acc[14], acc[15]);
-    reinterpret_cast<uint4*>(tile)[0] = o0;
-    reinterpret_cast<uint4*>(tile)[1] = o1;
+    tile[0] = o0;
+    tile[64] = o1;
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      reinterpret_cast<float4*>(tile)[q] =
+      reinterpret_cast<float4*>(tile)[q * 64] =
           make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
   }
 }

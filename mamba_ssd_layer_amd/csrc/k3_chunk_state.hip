@@ -16,8 +16,9 @@
 // Design (gfx950): one workgroup of 4 waves per (chunk, block of HB heads of
 // one B/C group).  The prologue loads the HB heads' log-decays at once and
 // scans them (one wave per head: Q/64 tokens per lane plus a wave-level scan),
-// writes Acs and the chunk total for the later kernels and keeps each head's
-// decay-to-chunk-end weights w_l = exp(Acs_{L-1} - Acs_l) in LDS.  The chunk's
+// writes Acs, the chunk total and the largest 32-token-tile decay for the
+// later kernels and keeps each head's decay-to-chunk-end weights
+// w_l = exp(Acs_{L-1} - Acs_l) in LDS.  The chunk's
 // B tile is staged transposed in LDS once (tokens contiguous, as an MFMA
 // operand contracting over tokens needs) and serves all HB heads; each head's
 // x tile is loaded into registers while the previous head computes, then scaled
@@ -125,6 +126,16 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
       w_s[wid * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
     }
     if (lane == 63) ws.lam[k * H + h] = lam;
+    // largest decay over a 32-token tile, Acs[32J] - Acs[32J + 31] (the output
+    // kernel's choice of mask factorisation depends on it)
+    float dm = 0.0f;
+#pragma unroll
+    for (int J = 0; J < Q / 32; ++J) {
+      const float first = __shfl(excl + run[(32 * J) % R], (32 * J) / R);
+      const float last = __shfl(excl + run[(32 * J + 31) % R], (32 * J + 31) / R);
+      dm = fmaxf(dm, first - last);
+    }
+    if (lane == 0) ws.dmax[k * H + h] = dm;
   }
 
   // ---- K3: S^T = B^T (w o X) per head.  Tile assignment: with at least four

@@ -40,6 +40,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   char* chunks = take(K * sizeof(ChunkDesc));
   char* acs = take(K * H * p.Q * sizeof(float));
   char* lam = take(K * H * sizeof(float));
+  char* dmax = take(K * H * sizeof(float));
   char* states = take(K * H * PN * esz);
   char* hin = take(K * H * PN * esz);
   const size_t NI = (size_t)p.Q / 32;
@@ -52,6 +53,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->chunks = reinterpret_cast<ChunkDesc*>(chunks);
     ws->acs = reinterpret_cast<float*>(acs);
     ws->lam = reinterpret_cast<float*>(lam);
+    ws->dmax = reinterpret_cast<float*>(dmax);
     ws->states = states;
     ws->hin = hin;
     ws->cb = cb;

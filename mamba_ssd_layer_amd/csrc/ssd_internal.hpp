@@ -49,10 +49,11 @@ struct Workspace {
   ChunkDesc* chunks = nullptr;   // (kmax) varlen only: written by the chunk-state kernel
   float* acs = nullptr;          // (kmax, H, Q) chunk-local cumsum of dt*A
   float* lam = nullptr;          // (kmax, H)    its last entry (log of the chunk's decay)
+  float* dmax = nullptr;         // (kmax, H)    largest decay (Acs difference) over a 32-token tile
   void* states = nullptr;        // (kmax, H, P, N) chunk states, element dtype
   void* hin = nullptr;           // (kmax, H, P, N) state entering each chunk, element dtype
-  void* cb = nullptr;            // (kmax, G, NI(NI+1)/2 tiles, 64 lanes, 16) kernel tiles of
-                                 // C B^T, element dtype, NI = Q/32
+  void* cb = nullptr;            // (kmax, G, NI(NI+1)/2 tiles, 16-byte vector, 64 lanes) kernel
+                                 // tiles of C B^T, element dtype, NI = Q/32 (16 values per lane)
   void* cop = nullptr;           // (kmax, G, NI, N/K steps, 64 lanes, one MFMA operand slice)
                                  // C rows in MFMA B-operand order, element dtype
 };
@@ -68,7 +69,7 @@ enum KernelId { kK0SeqTable = 0, kK13ChunkState = 1, kK4StatePass = 2, kK25Chunk
                 kK2ChunkCB = 4, kNumKernels = 5 };
 // K0 (varlen only): per-sequence first token, length and first chunk slot.
 hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
-// K1 + K3: chunk-local log-decay cumsum (-> acs, lam), chunk states (-> states);
+// K1 + K3: chunk-local log-decay cumsum (-> acs, lam, dmax), chunk states (-> states);
 // states_f32 (nullable) receives an fp32 copy of the stored states.
 hipError_t launch_chunk_state(const Problem& p, const Workspace& ws, float* states_f32,
                               hipStream_t s);

@@ -21,6 +21,14 @@
 
 namespace ssd {
 
+// Row permutation of an LDS tile whose rows are MFMA operand rows: row r is
+// stored at row r ^ ((r >> 3) & 7), i.e. its low three bits are XORed with the
+// next three.  Rows 8 apart (which a transposing store writes in one phase)
+// then start in different banks, while 8 consecutive rows (which an operand
+// read touches in one phase) stay a permutation of 8 consecutive rows.  The
+// map is its own inverse.
+__device__ __forceinline__ int lds_row_perm(int r) { return r ^ ((r >> 3) & 7); }
+
 template <class E, int ROWS, int COLS, int NTHR = kThreads>
 struct RowTile {
   using T = typename E::storage;
@@ -32,22 +40,25 @@ struct RowTile {
   uint4 v[NPT];
   int len;  // rows >= len are stored as zeros
 
-  __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L) {
+  // t: this thread's index among the NTHR staging threads
+  __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L, int t = threadIdx.x) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int idx = min((int)threadIdx.x + i * NTHR, NV - 1);
+      const int idx = min(t + i * NTHR, NV - 1);
       const int r = idx / VPR, c = idx % VPR;
       v[i] = *reinterpret_cast<const uint4*>(g + min(r, L - 1) * ld + c * VEC);
     }
     len = L;
   }
-  template <int DP>
-  __device__ __forceinline__ void store(T* __restrict__ lds) const {
+  // ROWPERM: row r lands at row lds_row_perm(r)
+  template <int DP, bool ROWPERM = false>
+  __device__ __forceinline__ void store(T* __restrict__ lds, int t = threadIdx.x) const {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int idx = threadIdx.x + i * NTHR;
+      const int idx = t + i * NTHR;
       const int r = idx / VPR, c = idx % VPR;
-      if (idx < NV) *reinterpret_cast<uint4*>(lds + r * DP + c * VEC) = r < len ? v[i] : make_uint4(0, 0, 0, 0);
+      const int rs = ROWPERM ? lds_row_perm(r) : r;
+      if (idx < NV) *reinterpret_cast<uint4*>(lds + rs * DP + c * VEC) = r < len ? v[i] : make_uint4(0, 0, 0, 0);
     }
   }
 };
@@ -68,77 +79,107 @@ __device__ __forceinline__ int lds_swizzle(int r) {
   return k & mask;
 }
 
-template <class E, int ROWS, int COLS, int NTHR = kThreads>
+// A thread stages blocks of RPB rows x one 16-byte vector (bf16: RPB = 8 or
+// 4 rows of 8 elements; fp32: 4 x 4).
+template <class E, int ROWS, int COLS, int NTHR = kThreads, int RPB = (E::kBytes == 2 ? 8 : 4)>
 struct TransTile {
   using T = typename E::storage;
   static constexpr bool kBf16 = E::kBytes == 2;
-  static constexpr int BS = kBf16 ? 8 : 4;  // square block edge (one 16-byte vector per row)
-  static_assert(ROWS % BS == 0 && COLS % BS == 0, "tile must be whole blocks");
-  static constexpr int CB = COLS / BS;
-  static constexpr int NB = (ROWS / BS) * CB;
+  static constexpr int BC = kBf16 ? 8 : 4;  // block width: one 16-byte vector
+  static_assert(kBf16 ? (RPB == 8 || RPB == 4) : RPB == 4, "unsupported block height");
+  static_assert(ROWS % RPB == 0 && COLS % BC == 0, "tile must be whole blocks");
+  static constexpr int CB = COLS / BC;
+  static constexpr int NB = (ROWS / RPB) * CB;
   static constexpr int NPT = (NB + NTHR - 1) / NTHR;
-  uint4 v[NPT][BS];
+  uint4 v[NPT][RPB];
   int len;  // rows >= len are stored as zeros
 
-  __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L) {
+  // t: this thread's index among the NTHR staging threads
+  __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L, int t = threadIdx.x) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int blk = min((int)threadIdx.x + i * NTHR, NB - 1);
+      const int blk = min(t + i * NTHR, NB - 1);
       const int cb = blk % CB, rb = blk / CB;
 #pragma unroll
-      for (int rr = 0; rr < BS; ++rr)
-        v[i][rr] = *reinterpret_cast<const uint4*>(g + min(rb * BS + rr, L - 1) * ld + cb * BS);
+      for (int rr = 0; rr < RPB; ++rr)
+        v[i][rr] = *reinterpret_cast<const uint4*>(g + min(rb * RPB + rr, L - 1) * ld + cb * BC);
     }
     len = L;
   }
+  // first tile row of block i of thread t (the rows whose scales store() takes)
+  __device__ __forceinline__ static int first_row(int i, int t = threadIdx.x) {
+    return (min(t + i * NTHR, NB - 1) / CB) * RPB;
+  }
   // row rr of block i as loaded, or zeros past the tile's length
   __device__ __forceinline__ uint4 row(int i, int rb, int rr) const {
-    return rb * BS + rr < len ? v[i][rr] : make_uint4(0, 0, 0, 0);
+    return rb * RPB + rr < len ? v[i][rr] : make_uint4(0, 0, 0, 0);
   }
 
-  // scale: per-row factors in LDS (read only when SCALE).
+  // Transposed store.  Row scales: from LDS (scale[r], SCALE == 1), from
+  // registers (sreg[i][rr] for row first_row(i) + rr, SCALE == 2), or none.
   // PERM16 (bf16 only): within every 16-token group the tokens are stored in
   // the order 0-3, 8-11, 4-7, 12-15, so that lane group g of a 32x32x16 MFMA
   // finds its tokens {4g..4g+3, 8+4g..8+4g+3} as one contiguous 16-byte run.
   // SWZ (bf16 only, DP == ROWS): 16-byte blocks placed by lds_swizzle<ROWS>.
-  template <int DP, bool SCALE, bool PERM16 = false, bool SWZ = false>
-  __device__ __forceinline__ void store(T* __restrict__ lds, const float* __restrict__ scale) const {
+  // ROWPERM (bf16 only): LDS row c (a column of the global tile) lands at row
+  // lds_row_perm(c); with a row pitch of 4 (mod 32) dwords this stores without
+  // bank conflicts.
+  template <int DP, int SCALE, bool PERM16 = false, bool SWZ = false, bool ROWPERM = false>
+  __device__ __forceinline__ void store(T* __restrict__ lds, const float* __restrict__ scale,
+                                        const float (*sreg)[RPB] = nullptr, int t = threadIdx.x) const {
     static_assert(!SWZ || (kBf16 && DP == ROWS), "the swizzled layout is unpadded bf16");
+    static_assert(!ROWPERM || kBf16, "the row permutation is for bf16 tiles");
     static_assert(!PERM16 || kBf16, "the 16-token permutation is for bf16 tiles");
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int blk = threadIdx.x + i * NTHR;
+      const int blk = t + i * NTHR;
       if (blk >= NB) continue;
       const int cb = blk % CB, rb = blk / CB;
-      float sc[BS];
+      float sc[RPB];
 #pragma unroll
-      for (int rr = 0; rr < BS; ++rr) sc[rr] = SCALE ? scale[rb * BS + rr] : 1.0f;
+      for (int rr = 0; rr < RPB; ++rr)
+        sc[rr] = SCALE == 1 ? scale[rb * RPB + rr] : SCALE == 2 ? sreg[i][rr] : 1.0f;
       if constexpr (kBf16) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          float f[8];
+          float f[RPB];
 #pragma unroll
-          for (int rr = 0; rr < 8; ++rr) {
+          for (int rr = 0; rr < RPB; ++rr) {
             const uint4 q = row(i, rb, rr);
             const uint32_t w = (c >> 1) == 0 ? q.x : (c >> 1) == 1 ? q.y : (c >> 1) == 2 ? q.z : q.w;
             const float e = (c & 1) ? bf16_hi(w) : bf16_lo(w);
             f[rr] = SCALE ? e * sc[rr] : e;
           }
-          uint4 o;
-          o.x = pack_bf16x2(f[0], f[1]);
-          o.y = pack_bf16x2(f[2], f[3]);
-          o.z = pack_bf16x2(f[4], f[5]);
-          o.w = pack_bf16x2(f[6], f[7]);
           const int r = cb * 8 + c;
-          T* row = lds + r * DP;
+          T* lrow = lds + (ROWPERM ? lds_row_perm(r) : r) * DP;
           const int key = SWZ ? lds_swizzle<ROWS>(r) : 0;
-          if constexpr (PERM16) {
-            // tokens 16g + {0-3, 8-11} -> block 2g, {4-7, 12-15} -> block 2g+1
-            const int off = (rb & 1) * 4;
-            *reinterpret_cast<uint2*>(row + (((rb >> 1) * 2) ^ key) * 8 + off) = make_uint2(o.x, o.y);
-            *reinterpret_cast<uint2*>(row + (((rb >> 1) * 2 + 1) ^ key) * 8 + off) = make_uint2(o.z, o.w);
+          if constexpr (RPB == 8) {
+            uint4 o;
+            o.x = pack_bf16x2(f[0], f[1]);
+            o.y = pack_bf16x2(f[2], f[3]);
+            o.z = pack_bf16x2(f[4], f[5]);
+            o.w = pack_bf16x2(f[6], f[7]);
+            if constexpr (PERM16) {
+              // tokens 16g + {0-3, 8-11} -> block 2g, {4-7, 12-15} -> block 2g+1
+              const int off = (rb & 1) * 4;
+              *reinterpret_cast<uint2*>(lrow + (((rb >> 1) * 2) ^ key) * 8 + off) = make_uint2(o.x, o.y);
+              *reinterpret_cast<uint2*>(lrow + (((rb >> 1) * 2 + 1) ^ key) * 8 + off) = make_uint2(o.z, o.w);
+            } else {
+              *reinterpret_cast<uint4*>(lrow + (rb ^ key) * 8) = o;
+            }
           } else {
-            *reinterpret_cast<uint4*>(row + (rb ^ key) * 8) = o;
+            const uint2 o = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+            // four tokens 4 rb .. 4 rb + 3: 16-byte block and half within it
+            int blk16, half;
+            if constexpr (PERM16) {
+              const int t0 = (rb & 3) * 4;  // position within the 16-token group
+              blk16 = (rb >> 2) * 2 + ((t0 >> 2) & 1);
+              half = (t0 >> 3) & 1;
+            } else {
+              blk16 = rb >> 1;
+              half = rb & 1;
+            }
+            *reinterpret_cast<uint2*>(lrow + (blk16 ^ key) * 8 + half * 4) = o;
           }
         }
       } else {
