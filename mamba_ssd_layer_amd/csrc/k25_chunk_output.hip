@@ -254,9 +254,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           gv[q] = gsrc[((tile0 + J) * GV + q) * 64 + lane];
       }
     };
-    auto tile = [&](int J, const uint4 (&gv)[GV]) {
-      // this lane group's x^T operands of tile J (issued before the mask math)
-      uint4 xa[2][NPH];
+    // this lane group's x^T operands of tile J
+    auto load_x = [&](int J, uint4 (&xa)[2][NPH]) {
       if constexpr (kBf16) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -266,6 +265,23 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           for (int j = 0; j < NPH; ++j) xa[kk][j] = *reinterpret_cast<const uint4*>(XT + prow(j) * QP + col);
         }
       }
+    };
+    // operands of one kernel tile: G values, x^T operands, Acs at the tile's end
+    struct TileOps {
+      uint4 g[GV];
+      uint4 x[2][NPH];
+      float te;
+    };
+    auto load_ops = [&](int J, TileOps& o) {
+      load_g(J, o.g);
+      load_x(J, o.x);
+      o.te = acs_s[J * 32 + 31];
+    };
+    // kDiag: the diagonal tile J == I (causal mask inside the tile)
+    auto tile = [&](int J, const TileOps& o, auto diag_tag) {
+      constexpr bool kDiag = decltype(diag_tag)::value;
+      const uint4 (&gv)[GV] = o.g;
+      const uint4 (&xa)[2][NPH] = o.x;
       // gt[r] = G[i_loc][j_r], j_r = 32J + 8(r/4) + 4 lg + r%4
       float gt[16];
       if constexpr (kBf16) {
@@ -287,8 +303,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       if (fast) {
         // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
         // exp(Acs_i - Acs_e) (<= 1 below the diagonal, <= e^64 on it)
-        const float u = __expf(ai - acs_s[J * 32 + 31]);
-        if (J < I) {
+        const float u = __expf(ai - o.te);
+        if constexpr (!kDiag) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = gt[r] * u;
         } else {
@@ -298,8 +314,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
             v[r] = (jr <= lr) ? gt[r] * u : 0.0f;
           }
         }
-      } else if (J < I) {
-        const float u = __expf(ai - acs_s[J * 32 + 31]);
+      } else if constexpr (!kDiag) {
+        const float u = __expf(ai - o.te);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 w4 = *reinterpret_cast<const float4*>(w_s + J * 32 + q * 8 + lg * 4);
@@ -337,16 +353,26 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         }
       }
     };
-    // two register buffers used in turn: the next tile's operands are being
-    // read while the current one is masked and multiplied (clamped past I)
-    uint4 gA[GV], gB[GV];
-    load_g(0, gA);
-    for (int J = 0; J <= I; J += 2) {
-      load_g(min(J + 1, I), gB);
-      tile(J, gA);
-      if (J + 1 > I) break;
-      load_g(min(J + 2, I), gA);
-      tile(J + 1, gB);
+    // off-diagonal tiles J < I in pairs, then the diagonal tile J = I; two
+    // operand buffers used in turn, the next tile's being read while the
+    // current one is masked and multiplied
+    using Off = std::integral_constant<bool, false>;
+    using Diag = std::integral_constant<bool, true>;
+    TileOps ob0, ob1;
+    load_ops(0, ob0);
+    int J = 0;
+    for (; J + 1 < I; J += 2) {
+      load_ops(J + 1, ob1);
+      tile(J, ob0, Off());
+      load_ops(J + 2, ob0);
+      tile(J + 1, ob1, Off());
+    }
+    if (J < I) {
+      load_ops(I, ob1);
+      tile(J, ob0, Off());
+      tile(I, ob1, Diag());
+    } else {
+      tile(I, ob0, Diag());
     }
     // store: lane holds Y^T row pr = 32 (ph0 + j) + 8(r/4) + 4 lg + r%4 of token
     // i_loc; bf16 rows are permuted (lds_row_perm), so its p is pr ^ c with
