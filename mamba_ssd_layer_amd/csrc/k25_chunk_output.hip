@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   using XTile = TransTile<E, Q, P, kCoThreads, 4>;
   XTile xt;
   RowTile<E, P, N, kCoThreads> ht;
-  float a_own = 0.f, a_end = 0.f, dmax = 0.f;
+  float a_own = 0.f, a_end = 0.f;
   float xa4[XTile::NPT][4], xae[XTile::NPT];  // Acs of this thread's x rows and of their tile end
   auto prefetch = [&](int h) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
@@ -160,9 +160,12 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       xa4[i][0] = a4.x; xa4[i][1] = a4.y; xa4[i][2] = a4.z; xa4[i][3] = a4.w;
       xae[i] = abase[h * Q + (r0 | 31)];
     }
-    dmax = ws.dmax[k * H + h];
   };
   prefetch(h0);
+  // largest tile decay of head h0 + (lane % HB), read per head with readlane
+  // (a vector load, once: a scalar load in flight would hold up every later
+  // wait for LDS reads)
+  const float dmax_v = ws.dmax[k * H + h0 + lane % HB];
 
   // C row of this lane's token as MFMA B-operand slices over N (coalesced),
   // kept in registers for all heads
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // tile decay comes from the chunk-state kernel): then x is staged
     // pre-scaled by w_j and the mask needs no per-element exp (see the
     // header); otherwise x is staged as is and every mask entry is exact.
-    const bool fast = dmax <= 64.0f;
+    const bool fast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dmax_v), hh)) <= 64.0f;
     if (fast) {
       float sreg[XTile::NPT][4];
 #pragma unroll
