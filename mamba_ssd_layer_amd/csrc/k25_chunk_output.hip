@@ -44,8 +44,6 @@
 //  * fp32 accumulation; y rounded once to the element dtype.  (fp32 inputs:
 //    the kernel tiles do not fit in LDS next to the fp32 x tile and are read
 //    from global memory instead.)
-#include <cmath>
-
 #include "ssd_stage.hpp"
 
 namespace ssd {
@@ -418,39 +416,10 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   }
 }
 
-// Heads per workgroup: a divisor of the heads of a group (8, 4, 2 or 1), one
-// workgroup per CU; the choice minimises rounds of workgroups x (heads per
-// workgroup + one head's worth of start-up work).
-int chunk_output_heads_per_block(const Problem& p, int num_cus) {
-  const int hpg = p.H / p.G;
-  int best = 1;
-  double best_cost = -1.0;
-  for (int hb = 8; hb >= 1; hb /= 2) {
-    if (hpg % hb) continue;
-    const double wgs = (double)p.kmax * (p.H / hb);
-    const double rounds = std::ceil(wgs / (double)(num_cus > 0 ? num_cus : 256));
-    const double cost = rounds * (hb + 1);
-    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = hb; }
-  }
-  return best;
-}
-
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <class E, int Q, int N>
 static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s) {
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
-    const int HB = chunk_output_heads_per_block(p, device_cus());
+    const int HB = heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
     hipLaunchKernelGGL((chunk_output_kernel<E, Q, N>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     return hipGetLastError();

@@ -13,57 +13,69 @@
 //        S_c[p, n] = sum_{l < L} exp(Acs_{L-1} - Acs_l) * x_l[p] * B_l[n],
 //    one (P x Q) . (Q x N) matrix product per (chunk, head).
 //
-// Design (gfx950): one workgroup of 4 waves per (chunk, block of HB heads of
-// one B/C group).  The prologue loads the HB heads' log-decays at once and
-// scans them (one wave per head: Q/64 tokens per lane plus a wave-level scan),
-// writes Acs, the chunk total and the largest 32-token-tile decay for the
-// later kernels and keeps each head's decay-to-chunk-end weights
-// w_l = exp(Acs_{L-1} - Acs_l) in LDS.  The chunk's
+// Design (gfx950): one workgroup of 8 waves per (chunk, block of HB heads of
+// one B/C group), one workgroup per CU.  The prologue loads the HB heads'
+// log-decays at once and scans them (one wave per head: Q/64 tokens per lane
+// plus a wave-level scan), writes Acs, the chunk total and the largest
+// 32-token-tile decay for the later kernels and keeps each head's
+// decay-to-chunk-end weights w_l = exp(Acs_{L-1} - Acs_l) in LDS.  The chunk's
 // B tile is staged transposed in LDS once (tokens contiguous, as an MFMA
-// operand contracting over tokens needs) and serves all HB heads; each head's
-// x tile is loaded into registers while the previous head computes, then scaled
-// by w and transposed into LDS (bf16 rows unpadded, their 16-byte blocks
-// XOR-swizzled by row so that neither the transposing stores nor the MFMA
-// operand reads meet LDS bank conflicts).  The product is formed as S^T (N x P) on 32x32
-// tiles (v_mfma_f32_32x32x16_bf16 / _32x32x2_f32, fp32 accumulation), so that
-// each lane ends with runs of 4 consecutive n of one p; the tile passes through
-// LDS in [p][n] order and leaves as whole 16-byte vectors, the (P x N) state
-// of a (chunk, head) being one contiguous block.  States are stored in the
-// element dtype (the state-passing kernel accumulates them in fp32).
+// operand contracting over tokens needs); on the bf16 path every wave then
+// keeps its 32 rows of B^T as MFMA operands in registers for all HB heads and
+// the LDS space is reused for x.  Each head's x tile is loaded into registers
+// while the previous head computes, then scaled by w and transposed into LDS
+// (bf16 rows unpadded, their 16-byte blocks XOR-swizzled by row so that
+// neither the transposing stores nor the MFMA operand reads meet LDS bank
+// conflicts).  The product is formed as S^T (N x P) on 32x32 tiles
+// (v_mfma_f32_32x32x16_bf16 / _32x32x2_f32, fp32 accumulation), so that each
+// lane ends with runs of 4 consecutive n of one p; the tile passes through LDS
+// in [p][n] order and leaves as whole 16-byte vectors, the (P x N) state of a
+// (chunk, head) being one contiguous block.  States are stored in the element
+// dtype (the state-passing kernel accumulates them in fp32).
 #include "ssd_stage.hpp"
 
 namespace ssd {
 
-constexpr int kMaxHB = 4;
+constexpr int kCsThreads = 512;  // 8 waves: two per SIMD
+constexpr int kMaxHB = 8;
 
 template <class E, int Q, int N>
 struct ChunkStateCfg {
   using T = typename E::storage;
+  static constexpr bool kBf16 = E::kBytes == 2;
   static constexpr int P = kHeadDim;
   static constexpr int PAD = 16 / sizeof(T);
-  static constexpr bool SWZ = E::kBytes == 2;  // bf16: swizzled, unpadded transposed tiles
+  static constexpr bool SWZ = kBf16;            // bf16: swizzled, unpadded transposed tiles
+  static constexpr bool kRegB = kBf16;          // B^T operands kept in registers, LDS reused
   static constexpr int QP = SWZ ? Q : Q + PAD;  // LDS pitch of the transposed tiles
-  static constexpr int NT = N < 32 ? 32 : N;  // B^T rows, padded to an MFMA tile
-  static constexpr int SP = N + PAD;          // LDS pitch of the staged state rows
-  static constexpr size_t lds_bytes = (size_t)(P + NT) * QP * sizeof(T) + (size_t)P * SP * sizeof(T) +
-                                      2 * kMaxHB * Q * sizeof(float);
+  static constexpr int NT = N < 32 ? 32 : N;    // B^T rows, padded to an MFMA tile
+  static constexpr int SP = N + PAD;            // LDS pitch of the staged state rows
+  static constexpr int NTN = NT / 32;           // n tiles
+  static constexpr int NTILES = NTN * (P / 32);
+  // a wave's tiles: one n tile and, with more than 8 tiles, both p tiles
+  static constexpr int PPW = NTILES > 8 ? 2 : 1;
+  static constexpr int KSTEPS = Q / E::kMfmaK;
+  static constexpr size_t bt_bytes = (size_t)NT * QP * sizeof(T);
+  static constexpr size_t xs_bytes = ((size_t)P * QP + (size_t)P * SP) * sizeof(T);
+  static constexpr size_t tile_bytes = kRegB ? (bt_bytes > xs_bytes ? bt_bytes : xs_bytes) : bt_bytes + xs_bytes;
+  static constexpr size_t lds_bytes = tile_bytes + (size_t)kMaxHB * Q * sizeof(float);
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
 };
 
 template <class E, int Q, int N, bool kDebug>
-__global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Workspace ws, int HB,
-                                                               float* __restrict__ states_f32) {
+__global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, Workspace ws, int HB,
+                                                                    float* __restrict__ states_f32) {
   using Cfg = ChunkStateCfg<E, Q, N>;
   using T = typename E::storage;
-  constexpr bool kBf16 = E::kBytes == 2;
-  constexpr int P = Cfg::P, QP = Cfg::QP, NT = Cfg::NT, SP = Cfg::SP;
-  constexpr bool SWZ = Cfg::SWZ;
+  constexpr bool kBf16 = Cfg::kBf16, SWZ = Cfg::SWZ, kRegB = Cfg::kRegB;
+  constexpr int P = Cfg::P, QP = Cfg::QP, NT = Cfg::NT, SP = Cfg::SP, NTN = Cfg::NTN;
+  constexpr int PPW = Cfg::PPW, KSTEPS = Cfg::KSTEPS;
   constexpr int R = Q / 64;  // tokens per lane in the cumsum
-  __shared__ __attribute__((aligned(16))) T xwT[P * QP];
-  __shared__ __attribute__((aligned(16))) T bT[NT * QP];
-  __shared__ __attribute__((aligned(16))) T Ss[P * SP];
-  __shared__ float ell_s[kMaxHB * Q];
-  __shared__ float w_s[kMaxHB * Q];
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::tile_bytes];
+  __shared__ __attribute__((aligned(16))) float wbuf[kMaxHB * Q];  // log-decays, then weights w
+  T* bT = reinterpret_cast<T*>(smem);
+  T* xwT = reinterpret_cast<T*>(smem + (kRegB ? 0 : Cfg::bt_bytes));
+  T* Ss = xwT + P * QP;
 
   const int H = p.H, G = p.G;
   const int nhb = H / HB;
@@ -80,28 +92,37 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
   const int lr = lane & 31, lg = lane >> 5;
   const T* xbase = reinterpret_cast<const T*>(p.x) + cd.t0 * H * P;
 
-  // ---- issue the loads: log-decays of the HB heads, B^T tile, first x tile
-  // (clamped indices, so that every load is issued unconditionally and back to back)
+  // this wave's output tiles: n tile nt, p tiles pt0 .. pt0 + PPW - 1
+  const bool active = Cfg::NTILES > 8 || wid < Cfg::NTILES;
+  const int nt = Cfg::NTILES > 8 ? wid : wid % NTN;
+  const int pt0 = Cfg::NTILES > 8 ? 0 : wid / NTN;
+
+  // ---- issue the loads: log-decays of the HB heads (clamped indices, so that
+  // every load is issued unconditionally), B tile, first x tile
   float ell[kMaxHB];
-  const float* dtrow = p.dt + (cd.t0 + min(tid, L - 1)) * H + h0;
+  {
+    const float* dtrow = p.dt + (cd.t0 + min(tid, L - 1)) * H + h0;
 #pragma unroll
-  for (int hh = 0; hh < kMaxHB; ++hh) {
-    const int hc = min(hh, HB - 1);
-    ell[hh] = dtrow[hc] * p.A[h0 + hc];
+    for (int hh = 0; hh < kMaxHB; ++hh) {
+      const int hc = min(hh, HB - 1);
+      ell[hh] = dtrow[hc] * p.A[h0 + hc];
+    }
   }
+  using BTile = TransTile<E, Q, N, kCsThreads>;
+  using XTile = TransTile<E, Q, P, kCsThreads, 4>;
+  XTile xt;
+  {
+    BTile bt;
+    bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
+    xt.load(xbase + h0 * P, (int64_t)H * P, L);
+    if (tid < Q) {
 #pragma unroll
-  for (int hh = 0; hh < kMaxHB; ++hh) ell[hh] = (tid < L && hh < HB) ? ell[hh] : 0.0f;
-  TransTile<E, Q, N> bt;
-  bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
-  TransTile<E, Q, P> xt;
-  xt.load(xbase + h0 * P, (int64_t)H * P, L);
-  if (tid < Q) {
-#pragma unroll
-    for (int hh = 0; hh < kMaxHB; ++hh) ell_s[hh * Q + tid] = ell[hh];
+      for (int hh = 0; hh < kMaxHB; ++hh) wbuf[hh * Q + tid] = (tid < L && hh < HB) ? ell[hh] : 0.0f;
+    }
+    if (NT > N)
+      for (int i = tid; i < (NT - N) * QP; i += kCsThreads) bT[N * QP + i] = T(0);
+    bt.template store<QP, 0, false, SWZ>(bT, nullptr);
   }
-  if (NT > N)
-    for (int i = tid; i < (NT - N) * QP; i += kThreads) bT[N * QP + i] = T(0);
-  bt.template store<QP, false, false, SWZ>(bT, nullptr);
   lds_barrier();
 
   // ---- K1: chunk-local inclusive cumsum, one wave per head; entries past the
@@ -112,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      acc += ell_s[wid * Q + lane * R + i];
+      acc += wbuf[wid * Q + lane * R + i];
       run[i] = acc;
     }
     const float incl = wave_inclusive_sum(acc);
@@ -123,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
     for (int i = 0; i < R; ++i) {
       const float a = excl + run[i];
       gout[i] = a;
-      w_s[wid * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
+      wbuf[wid * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
     }
     if (lane == 63) ws.lam[k * H + h] = lam;
     // largest decay over a 32-token tile, Acs[32J] - Acs[32J + 31] (the output
@@ -138,107 +159,90 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
     if (lane == 0) ws.dmax[k * H + h] = dm;
   }
 
-  // ---- K3: S^T = B^T (w o X) per head.  Tile assignment: with at least four
-  // n tiles, wave w takes n tiles w, w+4, ... for both p tiles (one B^T operand
-  // read serves two MFMAs); otherwise one (n, p) tile per wave.
-  constexpr int NTN = NT / 32;
-  constexpr bool kWide = NTN >= 4;
-  constexpr int NPW = kWide ? NTN / 4 : 1;
-  constexpr int PPW = kWide ? P / 32 : 1;
-  const bool active = kWide || wid < NTN * (P / 32);
-  auto n_tile = [&](int i) { return kWide ? wid + 4 * i : wid % NTN; };
-  auto p_tile = [&](int j) { return kWide ? j : wid / NTN; };
+  // ---- B^T operands of this wave's n tile, for all heads (bf16)
+  uint4 bop[kRegB ? KSTEPS : 1];
+  if constexpr (kRegB) {
+    const int row = nt * 32 + lr;
+    const int key = lds_swizzle<Q>(row);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      bop[ks] = *reinterpret_cast<const uint4*>(bT + row * QP + ((2 * ks + lg) ^ key) * 8);
+  }
+
   // 16-byte vectors of one (P x N) state, and per thread
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int NV = P * N / VEC;
-  constexpr int VPT = (NV + kThreads - 1) / kThreads;
+  constexpr int VPT = (NV + kCsThreads - 1) / kCsThreads;
 
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
-    lds_barrier();  // w ready; the previous head's x^T and state rows no longer read
-    xt.template store<QP, true, false, SWZ>(xwT, w_s + hh * Q);
+    lds_barrier();  // w ready; B^T read; the previous head's x^T and state rows no longer read
+    xt.template store<QP, 1, false, SWZ>(xwT, wbuf + hh * Q);
     lds_barrier();
     if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
 
+    // ---- K3: S^T = B^T (w o X) on this wave's tiles
     if (active) {
-      floatx16_t acc[NPW][PPW];
+      floatx16_t acc[PPW];
 #pragma unroll
-      for (int i = 0; i < NPW; ++i)
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) acc[i][j] = zero16();
+      for (int j = 0; j < PPW; ++j) acc[j] = zero16();
       if constexpr (kBf16) {
-        // 16-byte block 2 ks + lg of each operand row, at its swizzled place
-        int akey[NPW], bkey[PPW];
+        // x^T operands of step ks + 2 are read while step ks multiplies (LDS
+        // latency is several MFMA steps): a ring of three register sets
+        int xkey[PPW];
 #pragma unroll
-        for (int i = 0; i < NPW; ++i) akey[i] = lds_swizzle<Q>(n_tile(i) * 32 + lr);
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) bkey[j] = lds_swizzle<Q>(p_tile(j) * 32 + lr);
-        // operands of step ks + 2 are read while step ks multiplies (LDS latency
-        // is several MFMA steps): a ring of three register sets, fully unrolled
-        constexpr int KSTEPS = Q / 16;
-        uint4 a[3][NPW], b[3][PPW];
-        auto read_ops = [&](int ks, uint4 (&ar)[NPW], uint4 (&br)[PPW]) {
-#pragma unroll
-          for (int i = 0; i < NPW; ++i)
-            ar[i] = *reinterpret_cast<const uint4*>(bT + (n_tile(i) * 32 + lr) * QP + ((2 * ks + lg) ^ akey[i]) * 8);
+        for (int j = 0; j < PPW; ++j) xkey[j] = lds_swizzle<Q>((pt0 + j) * 32 + lr);
+        uint4 b[3][PPW];
+        auto read_x = [&](int ks, uint4 (&br)[PPW]) {
 #pragma unroll
           for (int j = 0; j < PPW; ++j)
-            br[j] = *reinterpret_cast<const uint4*>(xwT + (p_tile(j) * 32 + lr) * QP + ((2 * ks + lg) ^ bkey[j]) * 8);
+            br[j] = *reinterpret_cast<const uint4*>(xwT + ((pt0 + j) * 32 + lr) * QP + ((2 * ks + lg) ^ xkey[j]) * 8);
         };
-        read_ops(0, a[0], b[0]);
-        if (KSTEPS > 1) read_ops(1, a[1], b[1]);
+        read_x(0, b[0]);
+        if (KSTEPS > 1) read_x(1, b[1]);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          if (ks + 2 < KSTEPS) read_ops(ks + 2, a[(ks + 2) % 3], b[(ks + 2) % 3]);
+          if (ks + 2 < KSTEPS) read_x(ks + 2, b[(ks + 2) % 3]);
           // keep the reads ahead: the scheduler would otherwise sink each read
           // next to its MFMA and wait for it there
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int i = 0; i < NPW; ++i)
-#pragma unroll
-            for (int j = 0; j < PPW; ++j) acc[i][j] = mfma32x32x16(a[ks % 3][i], b[ks % 3][j], acc[i][j]);
+          for (int j = 0; j < PPW; ++j) acc[j] = mfma32x32x16(bop[ks], b[ks % 3][j], acc[j]);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll 8
-        for (int ks = 0; ks < Q / 2; ++ks) {
-          float a[NPW], b[PPW];
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const float a = bT[(nt * 32 + lr) * QP + ks * 2 + lg];
 #pragma unroll
-          for (int i = 0; i < NPW; ++i) a[i] = bT[(n_tile(i) * 32 + lr) * QP + ks * 2 + lg];
-#pragma unroll
-          for (int j = 0; j < PPW; ++j) b[j] = xwT[(p_tile(j) * 32 + lr) * QP + ks * 2 + lg];
-#pragma unroll
-          for (int i = 0; i < NPW; ++i)
-#pragma unroll
-            for (int j = 0; j < PPW; ++j) acc[i][j] = mfma32x32x2(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < PPW; ++j)
+            acc[j] = mfma32x32x2(a, xwT[((pt0 + j) * 32 + lr) * QP + ks * 2 + lg], acc[j]);
         }
       }
-      // acc[i][j][4q + e] = S[p = 32 p_tile(j) + lr][n = 32 n_tile(i) + 8q + 4lg + e]
+      // acc[j][4q + e] = S[p = 32 (pt0 + j) + lr][n = 32 nt + 8q + 4lg + e]
 #pragma unroll
-      for (int i = 0; i < NPW; ++i)
+      for (int j = 0; j < PPW; ++j)
 #pragma unroll
-        for (int j = 0; j < PPW; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n0 = n_tile(i) * 32 + 8 * q + 4 * lg;
-            if (NT == N || n0 < N) {
-              T* dst = Ss + (p_tile(j) * 32 + lr) * SP + n0;
-              const floatx16_t& c = acc[i][j];
-              if constexpr (kBf16)
-                *reinterpret_cast<uint2*>(dst) =
-                    make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
-              else
-                *reinterpret_cast<float4*>(dst) = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
-            }
+        for (int q = 0; q < 4; ++q) {
+          const int n0 = nt * 32 + 8 * q + 4 * lg;
+          if (NT == N || n0 < N) {
+            T* dst = Ss + ((pt0 + j) * 32 + lr) * SP + n0;
+            const floatx16_t& c = acc[j];
+            if constexpr (kBf16)
+              *reinterpret_cast<uint2*>(dst) =
+                  make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
+            else
+              *reinterpret_cast<float4*>(dst) = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
           }
+        }
     }
     lds_barrier();
     // the state of (chunk, head) is one contiguous (P x N) block: whole 16-byte vectors
     T* out = reinterpret_cast<T*>(ws.states) + (k * H + h) * (int64_t)(P * N);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int v = tid + i * kThreads;
-      if (NV % kThreads == 0 || v < NV) {
+      const int v = tid + i * kCsThreads;
+      if (NV % kCsThreads == 0 || v < NV) {
         const int row = v / (N / VEC), col = (v % (N / VEC)) * VEC;
         const uint4 val = *reinterpret_cast<const uint4*>(Ss + row * SP + col);
         reinterpret_cast<uint4*>(out)[v] = val;
@@ -258,22 +262,16 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(Problem p, Worksp
   }
 }
 
-// Heads per workgroup: the largest of 4, 2, 1 that divides the heads of a group.
-int chunk_state_heads_per_block(const Problem& p) {
-  const int hpg = p.H / p.G;
-  return hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
-}
-
 template <class E, int Q, int N>
 static hipError_t launch_cs(const Problem& p, const Workspace& ws, float* states_f32, hipStream_t s) {
   if constexpr (ChunkStateCfg<E, Q, N>::fits) {
-    const int HB = chunk_state_heads_per_block(p);
+    const int HB = heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
     if (states_f32)
-      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, true>), dim3(blocks), dim3(kThreads), 0, s, p, ws,
+      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, true>), dim3(blocks), dim3(kCsThreads), 0, s, p, ws,
                          HB, states_f32);
     else
-      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, false>), dim3(blocks), dim3(kThreads), 0, s, p,
+      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, false>), dim3(blocks), dim3(kCsThreads), 0, s, p,
                          ws, HB, states_f32);
     return hipGetLastError();
   } else {

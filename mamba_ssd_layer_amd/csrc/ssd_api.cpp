@@ -9,6 +9,7 @@
 //   K4 state passing -> K2+K5 diagonal blocks fused with state-to-output.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <string.h>
 #include <vector>
@@ -23,6 +24,36 @@ bool config_supported(Dtype dt, int Q, int N) {
 }
 
 static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int heads_per_block(const Problem& p) {
+  const int hpg = p.H / p.G;
+  const int cus = device_cus();
+  int best = 1;
+  double best_cost = -1.0;
+  for (int hb = 8; hb >= 1; hb /= 2) {
+    if (hpg % hb) continue;
+    const double wgs = (double)p.kmax * (p.H / hb);
+    const double rounds = std::ceil(wgs / (double)cus);
+    const double cost = rounds * (hb + 1);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = hb;
+    }
+  }
+  return best;
+}
 
 size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   const size_t S = (size_t)p.nseq, K = (size_t)p.kmax, H = (size_t)p.H;

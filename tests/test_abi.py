@@ -55,9 +55,11 @@ def test_supported_set(lib):
     assert lib.ssd_config_supported(1, 128, 256) == 1
     assert lib.ssd_config_supported(1, 256, 128) == 1
     assert lib.ssd_config_supported(0, 16, 64) == 1
-    # tiles that cannot fit in 160 KB of LDS
-    assert lib.ssd_config_supported(1, 256, 256) == 0
+    # bf16: every (N, Q) of the table, N = 256 at Q = 256 included
+    assert all(lib.ssd_config_supported(1, n, q) == 1 for n in (16, 32, 64, 128, 256) for q in (64, 128, 256))
+    # fp32 tiles that cannot fit in 160 KB of LDS
     assert lib.ssd_config_supported(0, 128, 256) == 0
+    assert lib.ssd_config_supported(0, 256, 128) == 0
     assert lib.ssd_config_supported(0, 48, 64) == 0
     assert lib.ssd_config_supported(5, 128, 64) == 0
 
