@@ -86,7 +86,7 @@ def call_fwd(lib, **kw):
     (dict(N=48), UNSUPPORTED),
     (dict(Q=100), UNSUPPORTED),
     (dict(Q=0), INVALID),
-    (dict(N=256, Q=256), UNSUPPORTED),  # LDS
+    (dict(N=128, Q=256, dtype=0), UNSUPPORTED),  # fp32 tiles past LDS
     (dict(x=FAKE + 4), INVALID),        # misaligned
     (dict(y=FAKE + 8), INVALID),
     (dict(fs=FAKE + 4), INVALID),
