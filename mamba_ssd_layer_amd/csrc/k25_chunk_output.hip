@@ -67,10 +67,16 @@ struct ChunkOutputCfg {
   // work of a wave: one row tile; with 8 row tiles both 32-wide halves of P,
   // with fewer row tiles one half (two waves share a row tile)
   static constexpr int NPH = NI == 8 ? 2 : 1;
-  static constexpr size_t base_bytes =
-      ((size_t)P * QP + (size_t)P * NP + (size_t)NW * 32 * YP) * sizeof(T) + 2 * Q * sizeof(float);
+  // X^T | Hin | output staging, one region (it holds the chunk's B rows while
+  // the kernel tiles are formed)
+  static constexpr size_t tiles_bytes = ((size_t)P * QP + (size_t)P * NP + (size_t)NW * 32 * YP) * sizeof(T);
+  static constexpr size_t base_bytes = tiles_bytes + 2 * Q * sizeof(float);
   static constexpr size_t g_bytes = (size_t)NTILE * GV * 64 * 16;
   static constexpr bool kGLds = base_bytes + g_bytes <= (size_t)kLdsLimit;  // kernel tiles in LDS
+  static constexpr int BP = N + PAD;  // LDS pitch of the staged B rows
+  // bf16 with the kernel tiles in LDS: the tiles are formed here, from B and C
+  // (no kernel-matrix pass); otherwise they come from it (ws.cb, ws.cop)
+  static constexpr bool kGInline = kBf16 && kGLds && (size_t)Q * BP * sizeof(T) <= tiles_bytes;
   static constexpr size_t lds_bytes = base_bytes + (kGLds ? g_bytes : 0);
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
 };
@@ -83,9 +89,10 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   constexpr bool kBf16 = Cfg::kBf16;
   constexpr int NI = Cfg::NI, NTILE = Cfg::NTILE, NPH = Cfg::NPH;
   using CReg = typename std::conditional<kBf16, uint4, float>::type;
-  __shared__ __attribute__((aligned(16))) T XT[P * QP];
-  __shared__ __attribute__((aligned(16))) T Hs[P * NP];
-  __shared__ __attribute__((aligned(16))) T Ys[Cfg::NW * 32 * YP];
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::tiles_bytes];
+  T* XT = reinterpret_cast<T*>(smem);
+  T* Hs = XT + P * QP;
+  T* Ys = Hs + P * NP;
   __shared__ __attribute__((aligned(16))) uint4 Gs[Cfg::kGLds ? NTILE * GV * 64 : 1];
   __shared__ __attribute__((aligned(16))) float acs_s[Q];
   __shared__ __attribute__((aligned(16))) float w_s[Q];
@@ -121,22 +128,24 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   const bool active = I >= 0 && I < nI;
 
   const T* xbase = reinterpret_cast<const T*>(p.x) + cd.t0 * H * P;
-  // C rows as MFMA operand slices, lane after lane (written by the kernel-matrix kernel)
-  const CReg* cop = reinterpret_cast<const CReg*>(ws.cop) + (k * G + g) * (int64_t)(NI * KS * 64) + lane;
   const T* hbase = reinterpret_cast<const T*>(ws.hin) + k * H * (int64_t)(P * N);
   const float* abase = ws.acs + k * H * Q;
   // kernel tiles of the chunk's group: [tile][16-byte vector q][lane]
   const uint4* gsrc = reinterpret_cast<const uint4*>(ws.cb) + (k * G + g) * (int64_t)(NTILE * GV * 64);
   T* ybase = reinterpret_cast<T*>(p.y) + cd.t0 * H * P;
 
-  // ---- issue the loads: kernel tiles (to LDS), first head's x / Hin / Acs, C rows
-  constexpr int GNV = Cfg::kGLds ? NTILE * GV * 64 : 1;
+  // ---- issue the loads: B rows (kernel tiles formed here) or the kernel
+  // tiles themselves (to LDS), first head's x / Hin / Acs, C rows
+  constexpr bool kCopyG = Cfg::kGLds && !Cfg::kGInline;
+  constexpr int GNV = kCopyG ? NTILE * GV * 64 : 1;
   constexpr int GVPT = (GNV + kCoThreads - 1) / kCoThreads;
   uint4 gtmp[GVPT];
-  if constexpr (Cfg::kGLds) {
+  if constexpr (kCopyG) {
 #pragma unroll
     for (int i = 0; i < GVPT; ++i) gtmp[i] = gsrc[min(tid + i * kCoThreads, GNV - 1)];
   }
+  RowTile<E, Cfg::kGInline ? Q : 8, N, kCoThreads> brows;
+  if constexpr (Cfg::kGInline) brows.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
 
   // every thread stages a 4-token block of x^T (bf16) and part of Hin
   using XTile = TransTile<E, Q, P, kCoThreads, 4>;
@@ -165,17 +174,55 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // wait for LDS reads)
   const float dmax_v = ws.dmax[k * H + h0 + lane % HB];
 
-  // C row of this lane's token as MFMA B-operand slices over N (coalesced),
-  // kept in registers for all heads
+  // C row of this lane's token as MFMA B-operand slices over N, kept in
+  // registers for all heads: straight from C (rows past the chunk end clamped;
+  // their outputs are never stored), or in lane order from the kernel-matrix
+  // pass (coalesced)
   CReg creg[KS];
   if (active) {
+    if constexpr (Cfg::kGInline) {
+      const T* crow = reinterpret_cast<const T*>(p.C) + ((cd.t0 + min(I * 32 + lr, L - 1)) * G + g) * N + lg * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) creg[ks] = cop[(I * KS + ks) * 64];
+      for (int ks = 0; ks < KS; ++ks) creg[ks] = *reinterpret_cast<const CReg*>(crow + ks * 16);
+    } else {
+      const CReg* cop = reinterpret_cast<const CReg*>(ws.cop) + (k * G + g) * (int64_t)(NI * KS * 64) + lane;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) creg[ks] = cop[(I * KS + ks) * 64];
+    }
   }
-  if constexpr (Cfg::kGLds) {
+  if constexpr (kCopyG) {
 #pragma unroll
     for (int i = 0; i < GVPT; ++i)
       if (tid + i * kCoThreads < GNV) Gs[tid + i * kCoThreads] = gtmp[i];
+  }
+  if constexpr (Cfg::kGInline) {
+    // kernel tiles G^T = B_J C_I^T of this wave's row tile (one wave per row
+    // tile), B rows staged in LDS: acc[r] = G[32I + lr][32J + 8(r/4) + 4lg + r%4]
+    constexpr int BP = Cfg::BP;
+    T* Bs = reinterpret_cast<T*>(smem);
+    brows.template store<BP>(Bs);
+    lds_barrier();
+    if (active && ph0 == 0) {
+      for (int J = 0; J <= I; ++J) {
+        uint4 a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          a[ks] = *reinterpret_cast<const uint4*>(Bs + (J * 32 + lr) * BP + ks * 16 + lg * 8);
+        floatx16_t acc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(a[ks], creg[ks], acc);
+        uint4 o0, o1;
+        o0.x = pack_bf16x2(acc[0], acc[1]);   o0.y = pack_bf16x2(acc[2], acc[3]);
+        o0.z = pack_bf16x2(acc[4], acc[5]);   o0.w = pack_bf16x2(acc[6], acc[7]);
+        o1.x = pack_bf16x2(acc[8], acc[9]);   o1.y = pack_bf16x2(acc[10], acc[11]);
+        o1.z = pack_bf16x2(acc[12], acc[13]); o1.w = pack_bf16x2(acc[14], acc[15]);
+        const int tile = I * (I + 1) / 2 + J;
+        Gs[(tile * GV + 0) * 64 + lane] = o0;
+        Gs[(tile * GV + 1) * 64 + lane] = o1;
+      }
+    }
+    // the head loop's first barrier orders these tiles before their use and
+    // the B rows' last read before x^T and Hin overwrite them
   }
 
   for (int hh = 0; hh < HB; ++hh) {
@@ -452,6 +499,17 @@ static hipError_t launch_co_q(const Problem& p, const Workspace& ws, hipStream_t
 
 hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s) {
   return p.dtype == Dtype::BF16 ? launch_co_q<Bf16>(p, ws, s) : launch_co_q<F32>(p, ws, s);
+}
+
+bool chunk_output_reads_cb(Dtype dt, int Q, int N) {
+#define SSD_CO_CB(QQ, NN)                                                           \
+  if (Q == QQ && N == NN)                                                           \
+    return dt == Dtype::BF16 ? !ChunkOutputCfg<Bf16, QQ, NN>::kGInline : !ChunkOutputCfg<F32, QQ, NN>::kGInline;
+  SSD_CO_CB(64, 16) SSD_CO_CB(64, 32) SSD_CO_CB(64, 64) SSD_CO_CB(64, 128) SSD_CO_CB(64, 256)
+  SSD_CO_CB(128, 16) SSD_CO_CB(128, 32) SSD_CO_CB(128, 64) SSD_CO_CB(128, 128) SSD_CO_CB(128, 256)
+  SSD_CO_CB(256, 16) SSD_CO_CB(256, 32) SSD_CO_CB(256, 64) SSD_CO_CB(256, 128) SSD_CO_CB(256, 256)
+#undef SSD_CO_CB
+  return true;
 }
 
 bool chunk_output_supported(Dtype dt, int Q, int N) {

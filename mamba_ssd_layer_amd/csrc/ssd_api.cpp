@@ -75,8 +75,9 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   char* states = take(K * H * PN * esz);
   char* hin = take(K * H * PN * esz);
   const size_t NI = (size_t)p.Q / 32;
-  char* cb = take(K * (size_t)p.G * (NI * (NI + 1) / 2) * 64 * 16 * esz);
-  char* cop = take(K * (size_t)p.G * p.Q * p.N * esz);
+  const bool use_cb = chunk_output_reads_cb(p.dtype, p.Q, p.N);
+  char* cb = take(use_cb ? K * (size_t)p.G * (NI * (NI + 1) / 2) * 64 * 16 * esz : 0);
+  char* cop = take(use_cb ? K * (size_t)p.G * p.Q * p.N * esz : 0);
   if (ws && base) {
     ws->seq_off = reinterpret_cast<int32_t*>(seq_off);
     ws->seq_start = reinterpret_cast<int64_t*>(seq_start);
@@ -236,7 +237,7 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
         if (e != hipSuccess) break;
       }
     }
-    if (p.kmax > 0) {
+    if (p.kmax > 0 && chunk_output_reads_cb(p.dtype, p.Q, p.N)) {
       e = timed_launch(kK2ChunkCB, stream, [&] { return launch_chunk_cb(p, ws, stream); });
       if (e != hipSuccess) break;
     }

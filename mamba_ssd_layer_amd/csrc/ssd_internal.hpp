@@ -81,11 +81,15 @@ hipError_t launch_chunk_state(const Problem& p, const Workspace& ws, float* stat
                               hipStream_t s);
 // K4: state passing (-> hin, final_state); hin_f32 (nullable) receives an fp32 copy.
 hipError_t launch_state_pass(const Problem& p, const Workspace& ws, float* hin_f32, hipStream_t s);
-// K2 (first half): kernel matrix tiles C B^T of every chunk and group (-> cb).
+// K2 (first half): kernel matrix tiles C B^T of every chunk and group (-> cb, cop),
+// for the configurations whose chunk-output kernel does not form them itself.
 hipError_t launch_chunk_cb(const Problem& p, const Workspace& ws, hipStream_t s);
 // K2 + K5: diagonal blocks and state-to-output (-> y).
 hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s);
 bool chunk_state_supported(Dtype dt, int Q, int N);
 bool chunk_output_supported(Dtype dt, int Q, int N);
+// Whether the chunk-output kernel for (dtype, Q, N) reads the kernel-matrix pass's
+// tiles (ws.cb, ws.cop); otherwise it forms them itself and that pass is skipped.
+bool chunk_output_reads_cb(Dtype dt, int Q, int N);
 
 }  // namespace ssd
