@@ -11,14 +11,14 @@
 // of the whole.
 //
 // Design (gfx950): pure HBM streaming, bound by how many bytes are in flight.
-// A thread owns 2 consecutive (p, n) channels of one (sequence, head) and walks
+// A thread owns kCh consecutive (p, n) channels of one (sequence, head) and walks
 // the sequence's chunks in order; the loads of later chunks' states do not
-// depend on the running state, so they are issued a block of 8 chunks ahead
-// and only the FMA chain is serial.  Lanes of a wave cover 128 consecutive
-// channels: every access is a fully coalesced 4-byte (bf16) or 8-byte (fp32)
-// vector.  Chunk states are read and
-// Hin is written in the element dtype (the output kernel feeds Hin to the
-// matrix cores in that dtype); the running state stays fp32.
+// depend on the running state, so they are issued a block of kDepth chunks
+// ahead (the last block of a sequence may be partial) and only the FMA chain
+// is serial.  Lanes of a wave cover 64 kCh consecutive channels: every access
+// is a fully coalesced vector of kCh elements.  Chunk states are read and Hin
+// is written in the element dtype (the output kernel feeds Hin to the matrix
+// cores in that dtype); the running state stays fp32.
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -26,26 +26,50 @@ namespace ssd {
 constexpr int kCh = 2;      // channels per thread
 constexpr int kDepth = 8;   // chunks per block; one block of loads is in flight ahead of the scan
 
+// kCh consecutive channels in the element dtype <-> fp32 registers.
 template <class E>
-__device__ __forceinline__ float2 load2(const typename E::storage* ptr) {
+__device__ __forceinline__ void load_ch(const typename E::storage* ptr, float (&v)[kCh]) {
   if constexpr (E::kBytes == 2) {
-    const uint32_t q = *reinterpret_cast<const uint32_t*>(ptr);
-    return make_float2(bf16_lo(q), bf16_hi(q));
+    if constexpr (kCh == 2) {
+      const uint32_t q = *reinterpret_cast<const uint32_t*>(ptr);
+      v[0] = bf16_lo(q); v[1] = bf16_hi(q);
+    } else {
+      const uint2 q = *reinterpret_cast<const uint2*>(ptr);
+      v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    }
   } else {
-    return *reinterpret_cast<const float2*>(ptr);
+    if constexpr (kCh == 2) {
+      const float2 q = *reinterpret_cast<const float2*>(ptr);
+      v[0] = q.x; v[1] = q.y;
+    } else {
+      const float4 q = *reinterpret_cast<const float4*>(ptr);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
   }
 }
 
-// Stores 2 channels in the element dtype; returns the stored values as fp32.
+// Stores kCh channels in the element dtype; r receives the stored values as fp32.
 template <class E>
-__device__ __forceinline__ float2 store2(typename E::storage* ptr, float2 v) {
+__device__ __forceinline__ void store_ch(typename E::storage* ptr, const float (&v)[kCh], float (&r)[kCh]) {
   if constexpr (E::kBytes == 2) {
-    const uint32_t o = pack_bf16x2(v.x, v.y);
-    *reinterpret_cast<uint32_t*>(ptr) = o;
-    return make_float2(bf16_lo(o), bf16_hi(o));
+    uint32_t o[kCh / 2];
+#pragma unroll
+    for (int c = 0; c < kCh / 2; ++c) {
+      o[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
+      r[2 * c] = bf16_lo(o[c]);
+      r[2 * c + 1] = bf16_hi(o[c]);
+    }
+    if constexpr (kCh == 2)
+      *reinterpret_cast<uint32_t*>(ptr) = o[0];
+    else
+      *reinterpret_cast<uint2*>(ptr) = make_uint2(o[0], o[1]);
   } else {
-    *reinterpret_cast<float2*>(ptr) = v;
-    return v;
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) r[c] = v[c];
+    if constexpr (kCh == 2)
+      *reinterpret_cast<float2*>(ptr) = make_float2(v[0], v[1]);
+    else
+      *reinterpret_cast<float4*>(ptr) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -73,51 +97,68 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
   T* hin = reinterpret_cast<T*>(ws.hin) + blk0;
   float* hin32 = kDebug ? hin_f32 + blk0 : nullptr;
   const float* lam = ws.lam + k0 * H + h;
-  float2 st = make_float2(0.f, 0.f);
+  float st[kCh] = {};
   // Software pipeline over blocks of kDepth chunks with two register buffers
   // used in turn (no copies between them): the loads of the next block are in
   // flight while the current block is scanned, so only the FMA chain is serial.
-  float2 bufA[kDepth], bufB[kDepth];
-  float decA[kDepth], decB[kDepth];
+  float bufA[kDepth][kCh], bufB[kDepth][kCh];
+  // the block's log-decays: lane u holds chunk kb + u (a vector load, which
+  // completes in order with the state loads; a scalar load would be waited
+  // for together with every other scalar load in flight)
+  float decA, decB;
+  const int lane = threadIdx.x & 63;
   // Loads are unconditional (indices past the end are clamped to the last
   // chunk and never used) so that the loop body is straight-line code and each
   // wait covers exactly the block it needs.
-  auto load_block = [&](int kb, float2 (&sv)[kDepth], float (&dec)[kDepth]) {
+  auto load_block = [&](int kb, float (&sv)[kDepth][kCh], float& dec) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
       const int kk = min(kb + u, nk - 1);
-      sv[u] = load2<E>(st_in + (int64_t)kk * stride + lo);
-      dec[u] = lam[(int64_t)kk * H];
+      load_ch<E>(st_in + (int64_t)kk * stride + lo, sv[u]);
+    }
+    dec = lam[(int64_t)min(kb + (lane % kDepth), nk - 1) * H];
+  };
+  auto lane_dec = [&](float dec, int u) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec), u)); };
+  auto step = [&](int kk, const float (&sv)[kCh], float dec) {
+    float r[kCh];
+    store_ch<E>(hin + (int64_t)kk * stride + lo, st, r);
+    if constexpr (kDebug) {
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) hin32[(int64_t)kk * stride + lo + c] = r[c];
+    }
+    const float a = __expf(dec);
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) st[c] = a * st[c] + sv[c];
+  };
+  // blocks of kDepth chunks; the last one may be partial (its loads clamped,
+  // its steps past the end skipped)
+  auto scan_block = [&](int b, const float (&sv)[kDepth][kCh], float dec) {
+    if ((b + 1) * kDepth <= nk) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) step(b * kDepth + u, sv[u], lane_dec(dec, u));
+    } else {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u)
+        if (b * kDepth + u < nk) step(b * kDepth + u, sv[u], lane_dec(dec, u));
     }
   };
-  auto step = [&](int kk, float2 sv, float dec) {
-    const float2 r = store2<E>(hin + (int64_t)kk * stride + lo, st);
-    if constexpr (kDebug) *reinterpret_cast<float2*>(hin32 + (int64_t)kk * stride + lo) = r;
-    const float a = __expf(dec);
-    st.x = a * st.x + sv.x;
-    st.y = a * st.y + sv.y;
-  };
-  const int nfull = nk / kDepth;
-  if (nfull > 0) {
+  const int nb = (nk + kDepth - 1) / kDepth;
+  if (nb > 0) {
     load_block(0, bufA, decA);
     int b = 0;
-    for (; b + 2 <= nfull; b += 2) {
+    for (; b + 2 <= nb; b += 2) {
       load_block((b + 1) * kDepth, bufB, decB);
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) step(b * kDepth + u, bufA[u], decA[u]);
+      scan_block(b, bufA, decA);
       load_block((b + 2) * kDepth, bufA, decA);
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) step((b + 1) * kDepth + u, bufB[u], decB[u]);
+      scan_block(b + 1, bufB, decB);
     }
-    if (b < nfull) {
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) step(b * kDepth + u, bufA[u], decA[u]);
-    }
+    if (b < nb) scan_block(b, bufA, decA);
   }
-  for (int kk = nfull * kDepth; kk < nk; ++kk)
-    step(kk, load2<E>(st_in + (int64_t)kk * stride + lo), lam[(int64_t)kk * H]);
-  if (p.final_state != nullptr)
-    *reinterpret_cast<float2*>(p.final_state + (s * H + h) * (int64_t)PN + ch) = st;
+  if (p.final_state != nullptr) {
+    float* fs = p.final_state + (s * H + h) * (int64_t)PN + ch;
+#pragma unroll
+    for (int c = 0; c < kCh; c += 2) *reinterpret_cast<float2*>(fs + c) = make_float2(st[c], st[c + 1]);
+  }
 }
 
 hipError_t launch_state_pass(const Problem& p, const Workspace& ws, float* hin_f32,
