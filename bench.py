@@ -16,7 +16,6 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,22 +31,24 @@ METRIC = "SSD fwd tokens/s and TFLOP/s (% bf16 MFMA peak) at T=2K/16K, N=128"
 KERNELS = ["seq_table", "chunk_state", "state_pass", "chunk_output"]
 
 
-def kernel_work(w, seqlens):
+def kernel_work(w, seqlens, cb_pass):
     """Algorithmic FLOPs and HBM bytes per launch of each kernel.
 
     FLOPs follow the pages' batched-matmul count ("LLM(十一)——Mamba" §3.5.3),
     split by the kernel that performs each product, with q the chunk's real
-    length: chunk_cb 2 q^2 N per (chunk, B/C group) (C B^T is formed once for
-    the heads that share B and C), chunk_output 2 q^2 P + 2 q N P per (chunk,
-    head) ((L o G) X and C h), chunk_state 2 q N P per (chunk, head),
-    state_pass 2 N P per (chunk, head).  The headline TFLOP/s keeps the pages'
-    per-head count for every term.
+    length: C B^T 2 q^2 N per (chunk, B/C group) (formed once for the heads
+    that share B and C: by the kernel-matrix pass when it runs (cb_pass), else
+    counted once in chunk_output, which forms the tiles itself), chunk_output
+    2 q^2 P + 2 q N P per (chunk, head) ((L o G) X and C h), chunk_state 2 q N P
+    per (chunk, head), state_pass 2 N P per (chunk, head).  The headline
+    TFLOP/s keeps the pages' per-head count for every term.
     Bytes are each kernel's compulsory reads and writes (e = element bytes,
     Q-padded tables count Q entries per chunk):
       chunk_state  x, B, dt in; states (P N e per chunk-head), Acs (4Q), total (4) out
       chunk_cb     B, C in; causal 32x32 C B^T tiles (e per element) out
       state_pass   states, chunk totals in; passed states out, final state (fp32) out
-      chunk_output x, C, passed states, Acs, C B^T tiles in; y out
+      chunk_output x, B and C (or C and the C B^T tiles with cb_pass), passed
+                   states, Acs in; y out
     """
     H, P, N, G, Q = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     e = 2 if w.dtype == "bf16" else 4
@@ -61,17 +62,18 @@ def kernel_work(w, seqlens):
     S = len(seqlens)
     f = {"chunk_state": 0.0, "chunk_cb": 0.0, "state_pass": 0.0, "chunk_output": 0.0}
     for q in chunks:
-        f["chunk_cb"] += G * 2 * q * q * N
+        f["chunk_cb" if cb_pass else "chunk_output"] += G * 2 * q * q * N
         f["chunk_output"] += H * (2 * q * q * P + 2 * q * N * P)
         f["chunk_state"] += H * 2 * q * N * P
         f["state_pass"] += H * 2 * N * P
     state = K * H * P * N * e
+    tiles = K * G * nt * 1024 * e
     b = {
         "chunk_state": T * H * P * e + T * G * N * e + T * H * 4 + state + K * H * (Q + 1) * 4,
-        "chunk_cb": 2 * T * G * N * e + K * G * nt * 1024 * e,
+        "chunk_cb": (2 * T * G * N * e + tiles) if cb_pass else 0.0,
         "state_pass": state + K * H * 4 + state + S * H * P * N * 4,
-        "chunk_output": (T * H * P * e + T * G * N * e + state + K * H * Q * 4
-                         + K * G * nt * 1024 * e + T * H * P * e),
+        "chunk_output": (T * H * P * e + T * G * N * e * (1 if cb_pass else 2) + state + K * H * Q * 4
+                         + (tiles if cb_pass else 0) + T * H * P * e),
     }
     return f, b
 
@@ -82,23 +84,17 @@ def min_io_bytes(w, total_tokens, nseq):
     return total_tokens * H * (2 * P * e + 4) + 2 * total_tokens * G * N * e + nseq * H * P * N * 4
 
 
-def source_hash(name):
-    p = os.path.join(ROOT, "mamba_ssd_layer_amd", "csrc", name)
-    try:
-        return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
-    except OSError:
-        return None
-
-
-def load_traffic(kernel_src, workload):
-    """HBM traffic per launch from a committed rocprofv3 counter summary, used
-    only while the kernel source still matches the one the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def load_traffic(kernel, workload):
+    """HBM traffic per launch from a committed rocprofv3 counter summary
+    (mamba_ssd_layer_amd.prof_summary traffic), used only while the kernel's
+    sources still hash to the value the counters were taken on."""
+    from mamba_ssd_layer_amd.prof_summary import sources_hash
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     try:
         d = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if d.get("source_sha256_16") != source_hash(kernel_src):
+    if d.get("sources_sha256_16") != sources_hash(kernel):
         return None
     return d.get("bytes_per_launch")
 
@@ -188,7 +184,7 @@ def main():
 
     tokens = int(inp.total_tokens)
     fl = flops_pages(w, tokens, seqlens)
-    kfl, kby = kernel_work(w, seqlens)
+    kfl, kby = kernel_work(w, seqlens, cb_pass=kernel_ms.get("chunk_cb") is not None)
     sec = ms / 1e3
     tflops_a = fl["A_pages"] / sec / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -197,6 +193,8 @@ def main():
     kroof = {}
     for kname in kfl:
         kms = kernel_ms.get(kname)
+        if not kby[kname] and not kfl[kname]:
+            continue  # not launched for this configuration
         t_hbm = kby[kname] / (PEAK_HBM_GBS * 1e9)
         t_mfma = kfl[kname] / (peak * 1e12)
         bound = "hbm" if t_hbm >= t_mfma else "mfma"
@@ -210,7 +208,7 @@ def main():
                         "frac": (ach / pk) if ach else None, "avg_launch_ms": kms,
                         "bytes_per_launch": kby[kname], "flops_per_launch": kfl[kname]}
     dom = max((k for k in kroof if kroof[k]["avg_launch_ms"]), key=lambda k: kroof[k]["avg_launch_ms"])
-    traffic = load_traffic("k25_chunk_output.hip", w.name) if dom == "chunk_output" else None
+    traffic = load_traffic(dom, w.name)
     mio = min_io_bytes(w, tokens, nseq)
 
     result = {

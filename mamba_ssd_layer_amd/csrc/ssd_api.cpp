@@ -209,6 +209,79 @@ struct DebugOut {
   float* hin = nullptr;
 };
 
+// ------------------------------------------------------------ workspace ----
+// A small per-device pool of workspace allocations.  Allocating and freeing
+// per call (hipMallocAsync / hipFreeAsync) makes the host wait for the previous
+// call's free to be reached on the GPU, so the next call's launches would start
+// only after the GPU went idle.  Instead an entry is reused once the event
+// recorded after its last call has completed (so reuse is safe across streams),
+// a new one is allocated while fewer than kMaxWorkspaces exist, and otherwise
+// the host waits for the oldest entry.  Entries are kept until the process ends.
+namespace {
+constexpr int kMaxWorkspaces = 4;  // per device
+struct WsEntry {
+  int device;
+  void* ptr;
+  size_t bytes;
+  hipEvent_t done;   // recorded on the stream after the entry's last call
+  uint64_t last;     // use counter of that call (oldest = smallest)
+  bool in_use;       // taken by a call that has not recorded its event yet
+};
+std::mutex g_ws_mu;
+std::vector<WsEntry> g_ws;
+uint64_t g_ws_clock = 0;
+
+// Returns the index of an entry of >= bytes for the current device, or -1.
+int ws_acquire(int device, size_t bytes, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  int n_dev = 0, oldest = -1;
+  for (int i = 0; i < (int)g_ws.size(); ++i) {
+    WsEntry& w = g_ws[i];
+    if (w.device != device) continue;
+    ++n_dev;
+    if (w.in_use) continue;
+    if (w.ptr != nullptr && w.bytes >= bytes && hipEventQuery(w.done) == hipSuccess) {
+      w.in_use = true;
+      return i;
+    }
+    if (oldest < 0 || w.last < g_ws[oldest].last) oldest = i;
+  }
+  if (n_dev < kMaxWorkspaces || oldest < 0) {
+    WsEntry w{device, nullptr, bytes, nullptr, 0, true};
+    if (hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) return -1;
+    if (hipMallocAsync(&w.ptr, bytes > 0 ? bytes : 256, stream) != hipSuccess || w.ptr == nullptr) {
+      (void)hipEventDestroy(w.done);
+      return -1;
+    }
+    g_ws.push_back(w);
+    return (int)g_ws.size() - 1;
+  }
+  WsEntry& w = g_ws[oldest];
+  if (hipEventSynchronize(w.done) != hipSuccess) return -1;
+  if (w.ptr == nullptr || w.bytes < bytes) {  // its last call has completed: replace it in stream order
+    if (w.ptr != nullptr && hipFreeAsync(w.ptr, stream) != hipSuccess) return -1;
+    w.ptr = nullptr;
+    w.bytes = 0;
+    if (hipMallocAsync(&w.ptr, bytes, stream) != hipSuccess || w.ptr == nullptr) {
+      w.ptr = nullptr;  // the slot stays, empty
+      return -1;
+    }
+    w.bytes = bytes;
+  }
+  w.in_use = true;
+  return oldest;
+}
+
+hipError_t ws_release(int i, hipStream_t stream) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  WsEntry& w = g_ws[i];
+  const hipError_t e = hipEventRecord(w.done, stream);
+  w.last = ++g_ws_clock;
+  w.in_use = false;
+  return e;
+}
+}  // namespace
+
 static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg) {
   ssd_status st = validate(p);
   if (st != SSD_OK) return st;
@@ -216,11 +289,18 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
   if (st != SSD_OK) return st;
   if (p.nseq == 0) return SSD_OK;
   const size_t bytes = workspace_layout(p, nullptr, nullptr);
-  void* base = nullptr;
-  hipError_t e = hipMallocAsync(&base, bytes, stream);
-  if (e != hipSuccess || base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+  const int wi = ws_acquire(dev, bytes, stream);
+  if (wi < 0) return SSD_ERR_OUT_OF_MEMORY;
+  char* base;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    base = static_cast<char*>(g_ws[wi].ptr);
+  }
   Workspace ws;
-  workspace_layout(p, static_cast<char*>(base), &ws);
+  workspace_layout(p, base, &ws);
+  hipError_t e = hipSuccess;
   const size_t KH = (size_t)p.kmax * p.H;
   do {
     if (p.cu != nullptr) {
@@ -250,9 +330,9 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
       if (e != hipSuccess) break;
     }
   } while (false);
-  const hipError_t ef = hipFreeAsync(base, stream);
+  const hipError_t er = ws_release(wi, stream);
   if (e != hipSuccess) return map_err(e);
-  return map_err(ef);
+  return map_err(er);
 }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

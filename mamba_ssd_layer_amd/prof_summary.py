@@ -1,0 +1,142 @@
+"""Summaries of rocprofv3 output for the SSD kernels (text for profiles/).
+
+    python -m mamba_ssd_layer_amd.prof_summary kernels <trace_dir> [--first N]
+    python -m mamba_ssd_layer_amd.prof_summary traffic --fetch D --write D \
+        --cal-fetch D --cal-write D --kernel chunk_output --workload long_T16k [--command C ...]
+
+`kernels` prints a markdown table of the per-kernel durations (run_kernel_stats.csv)
+and the gaps between consecutive SSD kernels of one forward (run_kernel_trace.csv).
+`traffic` prints the JSON that bench.py reads for the roofline's `traffic` figure:
+FETCH_SIZE and WRITE_SIZE of one kernel per dispatch, each scaled by what the same
+counter reads for a plain device copy of known size (bench.py --calibrate-copy),
+stamped with a hash of the kernel's sources so that a stale figure is not used.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+# sources each kernel is built from (the hash covers all of them)
+KERNEL_SOURCES = {
+    "chunk_output": ["k25_chunk_output.hip", "ssd_stage.hpp", "ssd_device.hpp", "ssd_internal.hpp"],
+    "chunk_state": ["k3_chunk_state.hip", "ssd_stage.hpp", "ssd_device.hpp", "ssd_internal.hpp"],
+    "state_pass": ["k4_state_pass.hip", "ssd_device.hpp", "ssd_internal.hpp"],
+}
+KERNEL_SYMBOL = {
+    "chunk_output": "ssd::chunk_output_kernel",
+    "chunk_state": "ssd::chunk_state_kernel",
+    "state_pass": "ssd::state_pass_kernel",
+    "chunk_cb": "ssd::chunk_cb_kernel",
+    "seq_table": "ssd::seq_table_kernel",
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def sources_hash(kernel: str) -> str | None:
+    h = hashlib.sha256()
+    try:
+        for name in KERNEL_SOURCES[kernel]:
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError):
+        return None
+    return h.hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    return name.replace("void ", "").split("(")[0]
+
+
+def kernels_table(trace_dir: str, first: int = 0) -> str:
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    ssd = [r for r in rows if "ssd::" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in ssd)
+    out = ["| kernel | calls | avg us | min us | max us | share of SSD time |", "|---|---|---|---|---|---|"]
+    for r in sorted(ssd, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{100.0 * float(r['TotalDurationNs']) / total:.1f}% |")
+    # gaps between consecutive SSD dispatches (end of one to start of the next)
+    tr = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
+          if "ssd::" in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    if first:
+        tr = tr[:first]
+    gaps = [int(b["Start_Timestamp"]) - int(a["End_Timestamp"]) for a, b in zip(tr, tr[1:])]
+    gaps = [g for g in gaps if 0 <= g < 20000]  # within one forward (not across host syncs)
+    if gaps:
+        out.append("")
+        out.append(f"Gap between consecutive SSD kernels of a forward: median {statistics.median(gaps) / 1e3:.2f} us "
+                   f"over {len(gaps)} gaps" + (f" (first {first} SSD dispatches)." if first else "."))
+    return "\n".join(out)
+
+
+def _counter_per_dispatch(d: str, symbol: str, counter: str) -> float:
+    vals = {}
+    for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+        if symbol in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {symbol} in {d}")
+    return sum(vals.values()) / len(vals)
+
+
+def traffic(fetch: str, write: str, cal_fetch: str, cal_write: str, kernel: str, workload: str,
+            copy_mib: int, commands: list[str]) -> dict:
+    sym = KERNEL_SYMBOL[kernel]
+    f_kib = _counter_per_dispatch(fetch, sym, "FETCH_SIZE")
+    w_kib = _counter_per_dispatch(write, sym, "WRITE_SIZE")
+    moved_kib = copy_mib * 1024.0
+    cf = _counter_per_dispatch(cal_fetch, COPY_KERNEL, "FETCH_SIZE")
+    cw = _counter_per_dispatch(cal_write, COPY_KERNEL, "WRITE_SIZE")
+    fs, ws = moved_kib / cf, moved_kib / cw
+    name = next(r["Kernel_Name"] for r in csv.DictReader(open(os.path.join(fetch, "run_counter_collection.csv")))
+                if sym in r["Kernel_Name"])
+    return {
+        "kernel": _short(name),
+        "workload": workload,
+        "sources": KERNEL_SOURCES[kernel],
+        "sources_sha256_16": sources_hash(kernel),
+        "fetch_kib_per_launch": f_kib,
+        "write_kib_per_launch": w_kib,
+        "fetch_scale": fs,
+        "write_scale": ws,
+        "bytes_per_launch": (f_kib * fs + w_kib * ws) * 1024.0,
+        "scale_reference": (f"plain device copy of {copy_mib} MiB (bench.py --calibrate-copy {copy_mib}): "
+                            f"FETCH_SIZE {cf:.1f} KiB, WRITE_SIZE {cw:.1f} KiB per launch"),
+        "commands": commands,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("trace_dir")
+    k.add_argument("--first", type=int, default=0, help="gaps over the first N SSD dispatches only")
+    t = sub.add_parser("traffic")
+    for a in ("fetch", "write", "cal_fetch", "cal_write"):
+        t.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
+    t.add_argument("--kernel", default="chunk_output", choices=sorted(KERNEL_SOURCES))
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mib", type=int, default=256)
+    t.add_argument("--command", action="append", default=[])
+    a = ap.parse_args(argv)
+    if a.cmd == "kernels":
+        print(kernels_table(a.trace_dir, a.first))
+    else:
+        json.dump(traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.kernel, a.workload, a.copy_mib,
+                          a.command), sys.stdout, indent=1)
+        print()
+
+
+if __name__ == "__main__":
+    main()
