@@ -36,11 +36,18 @@
  *   - Arguments are validated on the host before anything is launched; on a
  *     validation failure nothing is written and no HIP call is made.
  *   - Execution is asynchronous on `stream` (a hipStream_t, NULL = default
- *     stream) with no host synchronisation.  Workspace is taken with
- *     hipMallocAsync from the device's default memory pool and released with
- *     hipFreeAsync on the same stream.  Errors of kernels that already ran
- *     surface at the caller's next synchronisation, as for any stream work.
- *   - Re-entrant: no global state except the optional kernel timing below.
+ *     stream) with no host synchronisation.  Errors of kernels that already
+ *     ran surface at the caller's next synchronisation, as for any stream work.
+ *   - Workspace: one device allocation per (device, stream), taken with
+ *     hipMallocAsync from the device's default memory pool on first use, grown
+ *     (stream-ordered free and allocation) when a larger problem arrives, and
+ *     otherwise reused by every later call on that stream; it is kept until
+ *     the process ends.  Stream order keeps calls on one stream apart; calls on
+ *     different streams use different workspaces.  Do not destroy a stream
+ *     while this library's work is pending on it and then reuse its handle
+ *     for a new stream before that work has finished.
+ *   - Thread-safe: the workspace table and the optional kernel timing below
+ *     are the only global state, both guarded by locks.
  *   - Return value: SSD_OK or an error code; nothing is thrown or aborted.
  */
 #ifndef SSD_H_

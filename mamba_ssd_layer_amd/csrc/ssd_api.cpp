@@ -210,75 +210,47 @@ struct DebugOut {
 };
 
 // ------------------------------------------------------------ workspace ----
-// A small per-device pool of workspace allocations.  Allocating and freeing
-// per call (hipMallocAsync / hipFreeAsync) makes the host wait for the previous
-// call's free to be reached on the GPU, so the next call's launches would start
-// only after the GPU went idle.  Instead an entry is reused once the event
-// recorded after its last call has completed (so reuse is safe across streams),
-// a new one is allocated while fewer than kMaxWorkspaces exist, and otherwise
-// the host waits for the oldest entry.  Entries are kept until the process ends.
+// The workspace is cached per (device, stream) and reused by the next call on
+// the same stream: stream order already keeps two calls on one stream from
+// overlapping, so no event or allocation is needed per call (allocating and
+// freeing per call made the host wait for the GPU, and an event recorded after
+// every call cost the GPU several microseconds).  Calls on different streams
+// use different workspaces.  A workspace grows (stream-ordered free and
+// allocation) when a larger problem arrives and is otherwise kept until the
+// process ends.  A stream destroyed while this library's work is still pending
+// on it must not have its handle reused by a new stream before that work
+// finishes (synchronise a stream before destroying it).
 namespace {
-constexpr int kMaxWorkspaces = 4;  // per device
 struct WsEntry {
   int device;
+  hipStream_t stream;
   void* ptr;
   size_t bytes;
-  hipEvent_t done;   // recorded on the stream after the entry's last call
-  uint64_t last;     // use counter of that call (oldest = smallest)
-  bool in_use;       // taken by a call that has not recorded its event yet
 };
 std::mutex g_ws_mu;
 std::vector<WsEntry> g_ws;
-uint64_t g_ws_clock = 0;
 
-// Returns the index of an entry of >= bytes for the current device, or -1.
-int ws_acquire(int device, size_t bytes, hipStream_t stream) {
+// Workspace of >= bytes for (device, stream), or nullptr on allocation failure.
+void* ws_acquire(int device, size_t bytes, hipStream_t stream) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  int n_dev = 0, oldest = -1;
-  for (int i = 0; i < (int)g_ws.size(); ++i) {
-    WsEntry& w = g_ws[i];
-    if (w.device != device) continue;
-    ++n_dev;
-    if (w.in_use) continue;
-    if (w.ptr != nullptr && w.bytes >= bytes && hipEventQuery(w.done) == hipSuccess) {
-      w.in_use = true;
-      return i;
-    }
-    if (oldest < 0 || w.last < g_ws[oldest].last) oldest = i;
-  }
-  if (n_dev < kMaxWorkspaces || oldest < 0) {
-    WsEntry w{device, nullptr, bytes, nullptr, 0, true};
-    if (hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) return -1;
-    if (hipMallocAsync(&w.ptr, bytes > 0 ? bytes : 256, stream) != hipSuccess || w.ptr == nullptr) {
-      (void)hipEventDestroy(w.done);
-      return -1;
-    }
-    g_ws.push_back(w);
-    return (int)g_ws.size() - 1;
-  }
-  WsEntry& w = g_ws[oldest];
-  if (hipEventSynchronize(w.done) != hipSuccess) return -1;
-  if (w.ptr == nullptr || w.bytes < bytes) {  // its last call has completed: replace it in stream order
-    if (w.ptr != nullptr && hipFreeAsync(w.ptr, stream) != hipSuccess) return -1;
+  for (WsEntry& w : g_ws) {
+    if (w.device != device || w.stream != stream) continue;
+    if (w.bytes >= bytes) return w.ptr;
+    // grow in stream order: the previous calls on this stream finish first
+    if (hipFreeAsync(w.ptr, stream) != hipSuccess) return nullptr;
     w.ptr = nullptr;
     w.bytes = 0;
     if (hipMallocAsync(&w.ptr, bytes, stream) != hipSuccess || w.ptr == nullptr) {
-      w.ptr = nullptr;  // the slot stays, empty
-      return -1;
+      w.ptr = nullptr;
+      return nullptr;
     }
     w.bytes = bytes;
+    return w.ptr;
   }
-  w.in_use = true;
-  return oldest;
-}
-
-hipError_t ws_release(int i, hipStream_t stream) {
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  WsEntry& w = g_ws[i];
-  const hipError_t e = hipEventRecord(w.done, stream);
-  w.last = ++g_ws_clock;
-  w.in_use = false;
-  return e;
+  void* ptr = nullptr;
+  if (hipMallocAsync(&ptr, bytes > 0 ? bytes : 256, stream) != hipSuccess || ptr == nullptr) return nullptr;
+  g_ws.push_back({device, stream, ptr, bytes});
+  return ptr;
 }
 }  // namespace
 
@@ -291,13 +263,8 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
   const size_t bytes = workspace_layout(p, nullptr, nullptr);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
-  const int wi = ws_acquire(dev, bytes, stream);
-  if (wi < 0) return SSD_ERR_OUT_OF_MEMORY;
-  char* base;
-  {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    base = static_cast<char*>(g_ws[wi].ptr);
-  }
+  char* base = static_cast<char*>(ws_acquire(dev, bytes, stream));
+  if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
   Workspace ws;
   workspace_layout(p, base, &ws);
   hipError_t e = hipSuccess;
@@ -330,9 +297,7 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
       if (e != hipSuccess) break;
     }
   } while (false);
-  const hipError_t er = ws_release(wi, stream);
-  if (e != hipSuccess) return map_err(e);
-  return map_err(er);
+  return map_err(e);
 }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
