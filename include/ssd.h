@@ -150,7 +150,11 @@ const char* ssd_status_string(ssd_status status);
  * ssd_kernel_timing_read synchronises those events, adds their elapsed times
  * to per-kernel totals and, if reset != 0, clears the totals afterwards.
  * kernel ids: 0 sequence table (varlen calls only), 1 chunk cumsum + chunk
- * states, 2 state passing, 3 chunk output (diagonal blocks + state-to-output).
+ * states, 2 state passing, 3 chunk output (kernel-matrix tiles, diagonal
+ * blocks, state-to-output), 4 separate kernel-matrix pass (only the
+ * configurations whose chunk-output kernel cannot hold the tiles in LDS:
+ * fp32, and bf16 with dstate 256 at chunk_len 256).  Ids 0..4; another id is
+ * SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
  * Not re-entrant with concurrent forward calls.
  */
 ssd_status ssd_kernel_timing_enable(int32_t enable);
