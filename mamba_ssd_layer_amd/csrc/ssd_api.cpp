@@ -42,11 +42,11 @@ int heads_per_block(const Problem& p) {
   const int cus = device_cus();
   int best = 1;
   double best_cost = -1.0;
-  for (int hb = 8; hb >= 1; hb /= 2) {
+  for (int hb = kMaxHeadsPerBlock; hb >= 1; --hb) {
     if (hpg % hb) continue;
     const double wgs = (double)p.kmax * (p.H / hb);
     const double rounds = std::ceil(wgs / (double)cus);
-    const double cost = rounds * (hb + 1);
+    const double cost = rounds * (hb + 2);  // start-up of a workgroup: about two heads' time
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
       best = hb;

@@ -62,9 +62,10 @@ struct Workspace {
 size_t workspace_layout(const Problem& p, char* base, Workspace* ws);
 
 // Heads per workgroup of the chunk-state and chunk-output kernels (one
-// workgroup per CU): a divisor of the heads of a group (8, 4, 2 or 1) chosen to
-// minimise rounds of workgroups x (heads per workgroup + one head's worth of
-// start-up work).  <= 8.
+// workgroup per CU): the divisor of the heads of a group, <= kMaxHeadsPerBlock,
+// that minimises rounds of workgroups x (heads per workgroup + two heads' worth
+// of start-up work).
+constexpr int kMaxHeadsPerBlock = 32;
 int heads_per_block(const Problem& p);
 
 // Whether (dtype, Q, N) has an instantiated kernel set that fits in LDS.
