@@ -178,3 +178,52 @@ def test_intermediates_match_chunked_reference(dev):
         assert np.all(hin[~nz] == 0)
         e = oracle.rel_l2_per_slice(hin[nz], ref["hin"][nz], slice_axes=(0, 1))
         assert np.max(e) < tol, np.max(e)
+
+
+# ---------------------------------------------------- head blocks / workspace ----
+@pytest.mark.parametrize("dtype,H,G,b,T,Q", [
+    ("bf16", 48, 2, 2, 8192, 256),   # 12 heads per workgroup on 256 CUs: scan groups of 8 + 4
+    ("bf16", 20, 1, 2, 12800, 256),  # 10: 8 + 2
+    ("bf16", 64, 1, 2, 16384, 256),  # 32: four full groups
+    ("bf16", 12, 1, 2, 8192, 256),   # 3
+    ("f32", 40, 1, 2, 10240, 128),   # 5
+    ("bf16", 6, 2, 2, 700, 256),     # 1 (small problem: one head per workgroup)
+])
+def test_head_block_shapes(dev, dtype, H, G, b, T, Q):
+    """Heads per workgroup is any divisor (<= 32) of the heads of a group, chosen
+    for the grid's rounds on the device; these shapes give blocks of 12, 10, 32,
+    3, 5 and 1 heads on a 256-CU MI355X, with the chunk-state scan in groups of 8
+    heads (partial last groups included)."""
+    w = SMALL.with_(dtype=dtype, nheads=H, ngroups=G, batch=b, seqlen=T, dstate=128, chunk_len=Q)
+    check_parity(make_inputs(w, 11), dev, label=f"head blocks H={H} G={G} b={b} T={T} Q={Q} {dtype}")
+
+
+def test_workspace_reuse_across_sizes_and_streams(dev):
+    """The workspace is cached per (device, stream) and grown in stream order:
+    a small problem, a larger one, the small one again, and the same on a second
+    stream, without synchronising in between, all give the results of separate
+    synchronised runs (bit for bit: the kernels are deterministic)."""
+    small = make_inputs(SMALL.with_(seqlen=400, dstate=128, chunk_len=128), 3)
+    large = make_inputs(SMALL.with_(seqlen=3000, nheads=8, dstate=128, chunk_len=256), 4)
+    log("[workspace] reference runs")
+    ref = {}
+    for name, inp in (("small", small), ("large", large)):
+        Q = inp.workload.chunk_len
+        ref[name] = run_gpu(inp, dev, Q)
+    ds = {name: to_device(inp, dev) for name, inp in (("small", small), ("large", large))}
+    s2 = torch.cuda.Stream(device=dev)
+    s2.wait_stream(torch.cuda.current_stream(dev))  # inputs were made on the current stream
+    outs = []
+    log("[workspace] interleaved sizes on two streams")
+    for stream in (torch.cuda.current_stream(dev), s2):
+        with torch.cuda.stream(stream):
+            for name in ("small", "large", "small", "large"):
+                d = ds[name]
+                Q = (small if name == "small" else large).workload.chunk_len
+                y, fs = bd.ssd_chunked_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], Q)
+                outs.append((name, y, fs))
+    torch.cuda.synchronize()
+    for name, y, fs in outs:
+        yr, fr = ref[name]
+        assert np.array_equal(y.float().cpu().numpy(), yr), name
+        assert np.array_equal(fs.cpu().numpy(), fr), name
