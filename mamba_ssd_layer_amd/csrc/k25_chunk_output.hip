@@ -12,43 +12,50 @@
 // whole sequence.
 //
 // Design (gfx950):
-//  * One workgroup of 4 waves per (chunk, block of HB heads of one group) and
-//    one workgroup per CU (HB is chosen so that the grid fills the CUs in few
-//    rounds).  The whole chunk's kernel-matrix tiles G = C B^T of the group
-//    (formed once per chunk and group by the kernel-matrix kernel) are copied
-//    into LDS when the workgroup starts and serve all HB heads; each wave's C
-//    rows stay in registers for all heads.  The next head's x tile and passed
-//    state are loaded into registers while the current head computes, so the
-//    compute phase reads only LDS and registers.  Blocks are ordered so that
-//    the head blocks of one chunk land on one XCD.
+//  * One workgroup of 8 waves (two per SIMD) per (chunk, block of HB heads of
+//    one group) and one workgroup per CU (HB is chosen so that the grid fills
+//    the CUs in few rounds).  The chunk's kernel-matrix tiles G = C B^T of the
+//    group are formed when the workgroup starts (B rows staged in LDS, each
+//    wave's C rows in registers, v_mfma_f32_32x32x16_bf16) and stay in LDS for
+//    all HB heads; the C rows stay in registers as well.  The next head's x
+//    tile and passed state are loaded into registers while the current head
+//    computes, so the compute phase reads only LDS and registers.  Blocks are
+//    ordered so that the head blocks of one chunk land on one XCD.  (fp32, and
+//    bf16 with N = Q = 256: the tiles do not fit in LDS next to the x tile and
+//    come from the kernel-matrix kernel through global memory.)
 //  * The output is built transposed, Y^T (P x Q), on 32x32 MFMA tiles.  A
 //    kernel tile as G^T leaves each lane ONE output token i and 16 input
 //    tokens j, which is exactly the B-operand layout of Y^T += X^T (L o G)^T;
 //    the K (token) order of that product is chosen to match, and x^T is staged
 //    with its tokens permuted in 16-groups so the A operand is one 16-byte read.
-//  * Causality: only tiles J <= I are used.  The mask factors as
-//    L[i,j] = exp(Acs_i - Acs_e) * exp(Acs_e - Acs_j), e the last token of j's
-//    32-token tile.  The second factor w_j (in (0, 1]) scales x when it is
-//    staged in LDS, once per head; the first is one exp per lane per tile, in
-//    (0, 1] below the diagonal.  On a diagonal tile it is >= 1 and bounded by
-//    the tile's own decay, so this form is used only while no tile decays by
-//    more than e^64; otherwise the head takes the exact path: x staged as is,
-//    the first factor times a w_j table below the diagonal and one exp per
-//    element on the diagonal.  Entries with j > i are a selected 0 (never
-//    exp(-inf) arithmetic).
+//  * Causality: only tiles J <= I are used; on the diagonal tile the entries
+//    with j > i are a selected (or masked-off) 0, never exp(-inf) arithmetic.
+//    The mask exp(Acs_i - Acs_j) is factored per head in one of three ways,
+//    chosen from the chunk's total decay and its largest 32-token-tile decay
+//    (both from the chunk-state kernel):
+//    - chunk (total decay <= e^64): x_j is staged scaled by exp(-Acs_j) (<= e^64)
+//      and the finished sums by exp(Acs_i), which Y_off needs as well; the
+//      kernel tiles go to the matrix cores as stored, with no per-tile work;
+//    - tile (no tile decays by more than e^64): with e the last token of j's
+//      tile, x_j is staged scaled by w_j = exp(Acs_e - Acs_j) in (0, 1] and each
+//      lane scales its tile values by exp(Acs_i - Acs_e), one exp per tile;
+//    - exact: x staged as is, the tile factor times a w_j table below the
+//      diagonal and one exp per element on it.
 //  * Y_off uses the same lane layout: Hin (P x N, element dtype) is the A
 //    operand, the lane's C row the B operand, exp(Acs_i) one scalar per lane.
 //  * LDS operand reads are issued ahead of the MFMAs that use them (pinned by
 //    scheduling barriers); each finished row tile of y is passed through the
 //    wave's own LDS rows and written as whole 128-byte rows.
-//  * fp32 accumulation; y rounded once to the element dtype.  (fp32 inputs:
-//    the kernel tiles do not fit in LDS next to the fp32 x tile and are read
-//    from global memory instead.)
+//  * fp32 accumulation; y rounded once to the element dtype.
 #include "ssd_stage.hpp"
 
 namespace ssd {
 
 constexpr int kCoThreads = 512;  // 8 waves: two per SIMD, one workgroup per CU
+// mask factorisation of a head (see the header)
+constexpr int kMaskChunk = 0;  // whole chunk: x scaled by exp(-Acs_j), y by exp(Acs_i)
+constexpr int kMaskTile = 1;   // per 32-token tile
+constexpr int kMaskExact = 2;  // per element
 
 template <class E, int Q, int N>
 struct ChunkOutputCfg {
@@ -173,6 +180,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // (a vector load, once: a scalar load in flight would hold up every later
   // wait for LDS reads)
   const float dmax_v = ws.dmax[k * H + h0 + lane % HB];
+  const float lam_v = ws.lam[k * H + h0 + lane % HB];  // the chunk's total log-decay, same lanes
 
   // C row of this lane's token as MFMA B-operand slices over N, kept in
   // registers for all heads: straight from C (rows past the chunk end clamped;
@@ -233,17 +241,21 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       acs_s[tid] = a_own;
       w_s[tid] = __expf(a_end - a_own);  // exp(Acs_e - Acs_j), e = end of j's tile
     }
-    // Fast path when no 32-token tile decays by more than e^64 (the largest
-    // tile decay comes from the chunk-state kernel): then x is staged
-    // pre-scaled by w_j and the mask needs no per-element exp (see the
-    // header); otherwise x is staged as is and every mask entry is exact.
-    const bool fast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dmax_v), hh)) <= 64.0f;
-    if (fast) {
+    // Mask factorisation of this head (see the header): by the whole chunk when
+    // its total decay is at most e^64, else by 32-token tile when no tile
+    // decays by more than e^64 (the largest tile decay comes from the
+    // chunk-state kernel), else exact.
+    const float lam_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_v), hh));
+    const float dmax_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dmax_v), hh));
+    const int mode = lam_h >= -64.0f ? kMaskChunk : (dmax_h <= 64.0f ? kMaskTile : kMaskExact);
+    (void)dmax_h;
+    if (mode != kMaskExact) {
+      // x_j scaled by exp(-Acs_j) (chunk) or exp(Acs_e - Acs_j) (tile)
       float sreg[XTile::NPT][4];
 #pragma unroll
       for (int i = 0; i < XTile::NPT; ++i)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf(xae[i] - xa4[i][rr]);
+        for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf((mode == kMaskTile ? xae[i] : 0.0f) - xa4[i][rr]);
       xt.template store<QP, 2, kBf16, false, kBf16>(XT, nullptr, sreg);
     } else {
       xt.template store<QP, 0, kBf16, false, kBf16>(XT, nullptr);
@@ -286,10 +298,12 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     }
     const float ai = acs_s[i_loc];
     const float eo = __expf(ai);
+    if (mode != kMaskChunk) {
 #pragma unroll
-    for (int j = 0; j < NPH; ++j)
+      for (int j = 0; j < NPH; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] *= eo;
+        for (int r = 0; r < 16; ++r) acc[j][r] *= eo;
+    }
 
     // diagonal block: kernel tiles J <= I of row tile I (consecutive tiles)
     const int tile0 = I * (I + 1) / 2;
@@ -326,11 +340,37 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       o.te = acs_s[J * 32 + 31];
     };
     // kDiag: the diagonal tile J == I (causal mask inside the tile)
-    auto tile = [&](int J, const TileOps& o, auto diag_tag) {
+    auto tile = [&](int J, const TileOps& o, auto diag_tag, auto mode_tag) {
       constexpr bool kDiag = decltype(diag_tag)::value;
+      constexpr int kMode = decltype(mode_tag)::value;
       const uint4 (&gv)[GV] = o.g;
       const uint4 (&xa)[2][NPH] = o.x;
-      // gt[r] = G[i_loc][j_r], j_r = 32J + 8(r/4) + 4 lg + r%4
+      // value r of this lane: G[i_loc][j_r], j_r = 32J + 8(r/4) + 4 lg + r%4
+      if constexpr (kBf16) {
+        if constexpr (kMode == kMaskChunk) {
+          // the tile is the B operand as stored (bf16 pairs); on the diagonal
+          // the entries with j > i are cleared
+          uint4 b[2] = {gv[0], gv[1]};
+          if constexpr (kDiag) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              uint32_t m[4];
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                const int r = 8 * q + 2 * d;
+                const int j0 = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J of values r, r+1
+                m[d] = (j0 <= lr ? 0x0000ffffu : 0u) | (j0 + 1 <= lr ? 0xffff0000u : 0u);
+              }
+              b[q].x &= m[0]; b[q].y &= m[1]; b[q].z &= m[2]; b[q].w &= m[3];
+            }
+          }
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x16(xa[kk][j], b[kk], acc[j]);
+          return;
+        }
+      }
       float gt[16];
       if constexpr (kBf16) {
 #pragma unroll
@@ -348,7 +388,14 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         }
       }
       float v[16];
-      if (fast) {
+      if constexpr (kMode == kMaskChunk) {
+        // (fp32) x^T carries exp(-Acs_j); exp(Acs_i) is applied to the sum
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
+          v[r] = (!kDiag || jr <= lr) ? gt[r] : 0.0f;
+        }
+      } else if (mode == kMaskTile) {
         // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
         // exp(Acs_i - Acs_e) (<= 1 below the diagonal, <= e^64 on it)
         const float u = __expf(ai - o.te);
@@ -406,21 +453,36 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // current one is masked and multiplied
     using Off = std::integral_constant<bool, false>;
     using Diag = std::integral_constant<bool, true>;
-    TileOps ob0, ob1;
-    load_ops(0, ob0);
-    int J = 0;
-    for (; J + 1 < I; J += 2) {
-      load_ops(J + 1, ob1);
-      tile(J, ob0, Off());
-      load_ops(J + 2, ob0);
-      tile(J + 1, ob1, Off());
-    }
-    if (J < I) {
-      load_ops(I, ob1);
-      tile(J, ob0, Off());
-      tile(I, ob1, Diag());
-    } else {
-      tile(I, ob0, Diag());
+    // one copy of the loop for the chunk factorisation (no per-tile work) and
+    // one for the other two
+    auto diag_blocks = [&](auto mode_tag) {
+      TileOps ob0, ob1;
+      load_ops(0, ob0);
+      int J = 0;
+      for (; J + 1 < I; J += 2) {
+        load_ops(J + 1, ob1);
+        tile(J, ob0, Off(), mode_tag);
+        load_ops(J + 2, ob0);
+        tile(J + 1, ob1, Off(), mode_tag);
+      }
+      if (J < I) {
+        load_ops(I, ob1);
+        tile(J, ob0, Off(), mode_tag);
+        tile(I, ob1, Diag(), mode_tag);
+      } else {
+        tile(I, ob0, Diag(), mode_tag);
+      }
+    };
+    if (mode == kMaskChunk)
+      diag_blocks(std::integral_constant<int, kMaskChunk>());
+    else  // tile or exact, chosen per tile at run time
+      diag_blocks(std::integral_constant<int, kMaskTile>());
+    if (mode == kMaskChunk) {
+      // both parts of y carry exp(Acs_i) as one factor
+#pragma unroll
+      for (int j = 0; j < NPH; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] *= eo;
     }
     // store: lane holds Y^T row pr = 32 (ph0 + j) + 8(r/4) + 4 lg + r%4 of token
     // i_loc; bf16 rows are permuted (lds_row_perm), so its p is pr ^ c with
