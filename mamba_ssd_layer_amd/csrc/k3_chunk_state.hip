@@ -14,10 +14,11 @@
 //    one (P x Q) . (Q x N) matrix product per (chunk, head).
 //
 // Design (gfx950): one workgroup of 8 waves per (chunk, block of HB heads of
-// one B/C group), one workgroup per CU.  The heads' log-decays are loaded a
-// group of 8 heads ahead and scanned a group at a time (one wave per head: Q/64
-// tokens per lane plus a wave-level scan); the scan writes Acs, the chunk total
-// and the largest 32-token-tile decay for the later kernels and keeps each head's
+// one B/C group), one workgroup per CU.  The prologue loads the log-decays of
+// all the block's heads at once (consecutive lanes on consecutive heads) and
+// scans them (one wave per head: Q/64 tokens per lane plus a wave-level scan);
+// the scan writes Acs, the chunk total and the largest 32-token-tile decay for
+// the later kernels and keeps each head's
 // decay-to-chunk-end weights w_l = exp(Acs_{L-1} - Acs_l) in LDS.  The chunk's
 // B tile is staged transposed in LDS once (tokens contiguous, as an MFMA
 // operand contracting over tokens needs); on the bf16 path every wave then
@@ -37,7 +38,6 @@
 namespace ssd {
 
 constexpr int kCsThreads = 512;  // 8 waves: two per SIMD
-constexpr int kHG = 8;            // heads per cumsum group: one wave each
 
 template <class E, int Q, int N>
 struct ChunkStateCfg {
@@ -58,8 +58,17 @@ struct ChunkStateCfg {
   static constexpr size_t bt_bytes = (size_t)NT * QP * sizeof(T);
   static constexpr size_t xs_bytes = ((size_t)P * QP + (size_t)P * SP) * sizeof(T);
   static constexpr size_t tile_bytes = kRegB ? (bt_bytes > xs_bytes ? bt_bytes : xs_bytes) : bt_bytes + xs_bytes;
-  static constexpr size_t lds_bytes = tile_bytes + (size_t)kHG * Q * sizeof(float);
-  static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
+  // log-decays, then decay weights, of every head of the block (LDS left over
+  // by the tiles bounds the heads per workgroup)
+  static constexpr int kMaxHB = (int)(((size_t)kLdsLimit - (tile_bytes < (size_t)kLdsLimit ? tile_bytes : kLdsLimit)) /
+                                      ((size_t)Q * sizeof(float))) < kMaxHeadsPerBlock
+                                    ? (int)(((size_t)kLdsLimit - (tile_bytes < (size_t)kLdsLimit ? tile_bytes : kLdsLimit)) /
+                                            ((size_t)Q * sizeof(float)))
+                                    : kMaxHeadsPerBlock;
+  static constexpr size_t lds_bytes = tile_bytes + (size_t)(kMaxHB > 0 ? kMaxHB : 1) * Q * sizeof(float);
+  static constexpr bool fits = kMaxHB >= 1 && lds_bytes <= (size_t)kLdsLimit;
+  // log-decay loads per thread: Q tokens x kMaxHB heads over the workgroup
+  static constexpr int kEllPT = (Q * (kMaxHB > 0 ? kMaxHB : 1) + kCsThreads - 1) / kCsThreads;
 };
 
 template <class E, int Q, int N, bool kDebug>
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   constexpr int PPW = Cfg::PPW, KSTEPS = Cfg::KSTEPS;
   constexpr int R = Q / 64;  // tokens per lane in the cumsum
   __shared__ __attribute__((aligned(16))) char smem[Cfg::tile_bytes];
-  __shared__ __attribute__((aligned(16))) float wbuf[kHG * Q];  // a group's log-decays, then weights w
+  __shared__ __attribute__((aligned(16))) float wbuf[(Cfg::kMaxHB > 0 ? Cfg::kMaxHB : 1) * Q];  // log-decays, then w
   T* bT = reinterpret_cast<T*>(smem);
   T* xwT = reinterpret_cast<T*>(smem + (kRegB ? 0 : Cfg::bt_bytes));
   T* Ss = xwT + P * QP;
@@ -97,35 +106,57 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   const int nt = Cfg::NTILES > 8 ? wid : wid % NTN;
   const int pt0 = Cfg::NTILES > 8 ? 0 : wid / NTN;
 
-  // ---- log-decays of a group of (up to) kHG heads: loaded a group ahead
-  // (clamped indices, so that every load is issued unconditionally), staged in
-  // LDS, then scanned one wave per head
-  float ell[kHG];
-  auto load_ell = [&](int hg) {
-    const float* dtrow = p.dt + (cd.t0 + min(tid, L - 1)) * H + h0;
+  // ---- issue the loads: log-decays of all HB heads (consecutive lanes read
+  // consecutive heads of a token row; indices clamped so that every load is
+  // issued unconditionally), B tile, first x tile
+  // element e = tid + i * 512 of the (token, head) table is token e / HB, head
+  // e % HB; both advance by a fixed step per i (no division in the loop)
+  const int et0 = tid / HB, eh0 = tid % HB;
+  const int dt_step = kCsThreads / HB, dh_step = kCsThreads % HB;
+  float ell[Cfg::kEllPT];
+  {
+    int t = et0, hh = eh0;
 #pragma unroll
-    for (int j = 0; j < kHG; ++j) {
-      const int hc = min(hg * kHG + j, HB - 1);
-      ell[j] = dtrow[hc] * p.A[h0 + hc];
+    for (int i = 0; i < Cfg::kEllPT; ++i) {
+      const bool in = t < Q;  // past the table: clamped to its last element
+      const int tc = in ? min(t, L - 1) : L - 1, hc = in ? hh : HB - 1;
+      ell[i] = p.dt[(cd.t0 + tc) * H + h0 + hc] * p.A[h0 + hc];
+      t += dt_step;
+      hh += dh_step;
+      if (hh >= HB) { hh -= HB; ++t; }
     }
-  };
-  auto store_ell = [&](int hg) {
-    if (tid < Q) {
+  }
+  using BTile = TransTile<E, Q, N, kCsThreads>;
+  using XTile = TransTile<E, Q, P, kCsThreads, 4>;
+  XTile xt;
+  {
+    BTile bt;
+    bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
+    xt.load(xbase + h0 * P, (int64_t)H * P, L);
+    int t = et0, hh = eh0;
 #pragma unroll
-      for (int j = 0; j < kHG; ++j) wbuf[j * Q + tid] = (tid < L && hg * kHG + j < HB) ? ell[j] : 0.0f;
+    for (int i = 0; i < Cfg::kEllPT; ++i) {
+      if (t < Q) wbuf[hh * Q + t] = t < L ? ell[i] : 0.0f;
+      t += dt_step;
+      hh += dh_step;
+      if (hh >= HB) { hh -= HB; ++t; }
     }
-  };
-  // K1: chunk-local inclusive cumsum of head hg*kHG + wid; entries past the
-  // chunk end repeat the last value (their log-decay is 0) and get weight 0
-  auto cumsum = [&](int hg) {
-    const int hh = hg * kHG + wid;
-    if (hh >= HB) return;
+    if (NT > N)
+      for (int i = tid; i < (NT - N) * QP; i += kCsThreads) bT[N * QP + i] = T(0);
+    bt.template store<QP, 0, false, SWZ>(bT, nullptr);
+  }
+  lds_barrier();
+
+  // ---- K1: chunk-local inclusive cumsum, one wave per head (waves take heads
+  // wid, wid + 8, ...); entries past the chunk end repeat the last value (their
+  // log-decay is 0) and get weight 0
+  for (int hh = wid; hh < HB; hh += kCsThreads / 64) {
     const int h = h0 + hh;
     float run[R];
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      acc += wbuf[wid * Q + lane * R + i];
+      acc += wbuf[hh * Q + lane * R + i];
       run[i] = acc;
     }
     const float incl = wave_inclusive_sum(acc);
@@ -136,7 +167,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
     for (int i = 0; i < R; ++i) {
       const float a = excl + run[i];
       gout[i] = a;
-      wbuf[wid * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
+      wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
     }
     if (lane == 63) ws.lam[k * H + h] = lam;
     // largest decay over a 32-token tile, Acs[32J] - Acs[32J + 31] (the output
@@ -149,25 +180,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
       dm = fmaxf(dm, first - last);
     }
     if (lane == 0) ws.dmax[k * H + h] = dm;
-  };
-
-  // ---- issue the loads: first group's log-decays, B tile, first x tile
-  load_ell(0);
-  using BTile = TransTile<E, Q, N, kCsThreads>;
-  using XTile = TransTile<E, Q, P, kCsThreads, 4>;
-  XTile xt;
-  {
-    BTile bt;
-    bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
-    xt.load(xbase + h0 * P, (int64_t)H * P, L);
-    store_ell(0);
-    if (NT > N)
-      for (int i = tid; i < (NT - N) * QP; i += kCsThreads) bT[N * QP + i] = T(0);
-    bt.template store<QP, 0, false, SWZ>(bT, nullptr);
   }
-  lds_barrier();
-  cumsum(0);
-  if (HB > kHG) load_ell(1);
 
   // ---- B^T operands of this wave's n tile, for all heads (bf16)
   uint4 bop[kRegB ? KSTEPS : 1];
@@ -187,16 +200,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
     lds_barrier();  // w ready; B^T read; the previous head's x^T and state rows no longer read
-    if (hh > 0 && hh % kHG == 0) {
-      // next group of heads: its log-decays (loaded a group ahead) are scanned
-      const int hg = hh / kHG;
-      store_ell(hg);
-      lds_barrier();
-      cumsum(hg);
-      if ((hg + 1) * kHG < HB) load_ell(hg + 1);
-      lds_barrier();
-    }
-    xt.template store<QP, 1, false, SWZ>(xwT, wbuf + (hh % kHG) * Q);
+    xt.template store<QP, 1, false, SWZ>(xwT, wbuf + hh * Q);
     lds_barrier();
     if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
 
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
 template <class E, int Q, int N>
 static hipError_t launch_cs(const Problem& p, const Workspace& ws, float* states_f32, hipStream_t s) {
   if constexpr (ChunkStateCfg<E, Q, N>::fits) {
-    const int HB = heads_per_block(p);
+    const int HB = heads_per_block(p, ChunkStateCfg<E, Q, N>::kMaxHB);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
     if (states_f32)
       hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, true>), dim3(blocks), dim3(kCsThreads), 0, s, p, ws,

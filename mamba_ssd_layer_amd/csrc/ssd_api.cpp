@@ -37,12 +37,12 @@ static int device_cus() {
   return cached[dev];
 }
 
-int heads_per_block(const Problem& p) {
+int heads_per_block(const Problem& p, int max_hb) {
   const int hpg = p.H / p.G;
   const int cus = device_cus();
   int best = 1;
   double best_cost = -1.0;
-  for (int hb = kMaxHeadsPerBlock; hb >= 1; --hb) {
+  for (int hb = max_hb < kMaxHeadsPerBlock ? max_hb : kMaxHeadsPerBlock; hb >= 1; --hb) {
     if (hpg % hb) continue;
     const double wgs = (double)p.kmax * (p.H / hb);
     const double rounds = std::ceil(wgs / (double)cus);

@@ -66,7 +66,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws);
 // that minimises rounds of workgroups x (heads per workgroup + two heads' worth
 // of start-up work).
 constexpr int kMaxHeadsPerBlock = 32;
-int heads_per_block(const Problem& p);
+int heads_per_block(const Problem& p, int max_hb = kMaxHeadsPerBlock);
 
 // Whether (dtype, Q, N) has an instantiated kernel set that fits in LDS.
 bool config_supported(Dtype dt, int Q, int N);
