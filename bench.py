@@ -102,8 +102,10 @@ def load_traffic(kernel, workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the GPU's clocks take some milliseconds of sustained work to settle; the
+    # untimed warmup covers that so the timed steps see the steady state
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="long_T16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

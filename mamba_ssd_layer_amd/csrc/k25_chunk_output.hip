@@ -46,7 +46,9 @@
 //  * LDS operand reads are issued ahead of the MFMAs that use them (pinned by
 //    scheduling barriers); each finished row tile of y is passed through the
 //    wave's own LDS rows and written as whole 128-byte rows.
-//  * fp32 accumulation; y rounded once to the element dtype.
+//  * fp32 accumulation; y rounded once to the element dtype and stored with the
+//    non-temporal hint (nothing here reads it again); Hin, read here for the
+//    last time, is loaded with that hint too.
 #include "ssd_stage.hpp"
 
 namespace ssd {
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   float xa4[XTile::NPT][4], xae[XTile::NPT];  // Acs of this thread's x rows and of their tile end
   auto prefetch = [&](int h) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
-    ht.load(hbase + h * (int64_t)(P * N), N, P);
+    ht.template load<true>(hbase + h * (int64_t)(P * N), N, P);  // Hin's last read
     if (tid < Q) {
       a_own = abase[h * Q + tid];
       a_end = abase[h * Q + (tid | 31)];
@@ -518,8 +520,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       const int i_row = I * 32 + row;
       const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
       if (i_row < L)
-        *reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))) =
-            val;
+        store_nt(reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))),
+                 val);
     }
     __builtin_amdgcn_wave_barrier();
   }

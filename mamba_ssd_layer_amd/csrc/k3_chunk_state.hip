@@ -32,7 +32,9 @@
 // lane ends with runs of 4 consecutive n of one p; the tile passes through LDS
 // in [p][n] order and leaves as whole 16-byte vectors, the (P x N) state of a
 // (chunk, head) being one contiguous block.  States are stored in the element
-// dtype (the state-passing kernel accumulates them in fp32).
+// dtype (the state-passing kernel accumulates them in fp32), with the
+// non-temporal hint when the forward's data exceeds the last-level cache (then
+// they would only displace x and B, which are read again).
 #include "ssd_stage.hpp"
 
 namespace ssd {
@@ -71,7 +73,9 @@ struct ChunkStateCfg {
   static constexpr int kEllPT = (Q * (kMaxHB > 0 ? kMaxHB : 1) + kCsThreads - 1) / kCsThreads;
 };
 
-template <class E, int Q, int N, bool kDebug>
+// kNT: the states are stored with the non-temporal hint (a compile-time choice:
+// a run-time one lets the compiler merge the two stores and drop the hint)
+template <class E, int Q, int N, bool kDebug, bool kNT>
 __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, Workspace ws, int HB,
                                                                     float* __restrict__ states_f32) {
   using Cfg = ChunkStateCfg<E, Q, N>;
@@ -268,7 +272,10 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
       if (NV % kCsThreads == 0 || v < NV) {
         const int row = v / (N / VEC), col = (v % (N / VEC)) * VEC;
         const uint4 val = *reinterpret_cast<const uint4*>(Ss + row * SP + col);
-        reinterpret_cast<uint4*>(out)[v] = val;
+        if constexpr (kNT)
+          store_nt(reinterpret_cast<uint4*>(out) + v, val);
+        else
+          reinterpret_cast<uint4*>(out)[v] = val;
         if constexpr (kDebug) {
           float* o32 = states_f32 + (k * H + h) * (int64_t)(P * N) + (int64_t)v * VEC;
           if constexpr (kBf16) {
@@ -290,11 +297,15 @@ static hipError_t launch_cs(const Problem& p, const Workspace& ws, float* states
   if constexpr (ChunkStateCfg<E, Q, N>::fits) {
     const int HB = heads_per_block(p, ChunkStateCfg<E, Q, N>::kMaxHB);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
+    // the fp32 copy for inspection goes with plain stores (the hint changes no value)
     if (states_f32)
-      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, true>), dim3(blocks), dim3(kCsThreads), 0, s, p, ws,
-                         HB, states_f32);
+      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, true, false>), dim3(blocks), dim3(kCsThreads), 0, s, p,
+                         ws, HB, states_f32);
+    else if (p.stream_states)
+      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, false, true>), dim3(blocks), dim3(kCsThreads), 0, s, p,
+                         ws, HB, states_f32);
     else
-      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, false>), dim3(blocks), dim3(kCsThreads), 0, s, p,
+      hipLaunchKernelGGL((chunk_state_kernel<E, Q, N, false, false>), dim3(blocks), dim3(kCsThreads), 0, s, p,
                          ws, HB, states_f32);
     return hipGetLastError();
   } else {

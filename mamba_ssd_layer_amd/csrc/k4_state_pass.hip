@@ -18,7 +18,8 @@
 // is serial.  Lanes of a wave cover 64 kCh consecutive channels: every access
 // is a fully coalesced vector of kCh elements.  Chunk states are read and Hin
 // is written in the element dtype (the output kernel feeds Hin to the matrix
-// cores in that dtype); the running state stays fp32.
+// cores in that dtype), with the non-temporal hint when the forward's data
+// exceeds the last-level cache; the running state stays fp32.
 #include "ssd_device.hpp"
 
 namespace ssd {
@@ -48,28 +49,28 @@ __device__ __forceinline__ void load_ch(const typename E::storage* ptr, float (&
   }
 }
 
-// Stores kCh channels in the element dtype; r receives the stored values as fp32.
+// Stores kCh channels in the element dtype (nt: with the non-temporal hint);
+// r receives the stored values as fp32.
 template <class E>
-__device__ __forceinline__ void store_ch(typename E::storage* ptr, const float (&v)[kCh], float (&r)[kCh]) {
+__device__ __forceinline__ void store_ch(typename E::storage* ptr, const float (&v)[kCh], float (&r)[kCh], bool nt) {
+  static_assert(kCh == 2, "two channels per thread");
+  uint32_t o0, o1 = 0;
   if constexpr (E::kBytes == 2) {
-    uint32_t o[kCh / 2];
-#pragma unroll
-    for (int c = 0; c < kCh / 2; ++c) {
-      o[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
-      r[2 * c] = bf16_lo(o[c]);
-      r[2 * c + 1] = bf16_hi(o[c]);
-    }
-    if constexpr (kCh == 2)
-      *reinterpret_cast<uint32_t*>(ptr) = o[0];
-    else
-      *reinterpret_cast<uint2*>(ptr) = make_uint2(o[0], o[1]);
+    o0 = pack_bf16x2(v[0], v[1]);
+    r[0] = bf16_lo(o0);
+    r[1] = bf16_hi(o0);
   } else {
-#pragma unroll
-    for (int c = 0; c < kCh; ++c) r[c] = v[c];
-    if constexpr (kCh == 2)
-      *reinterpret_cast<float2*>(ptr) = make_float2(v[0], v[1]);
-    else
-      *reinterpret_cast<float4*>(ptr) = make_float4(v[0], v[1], v[2], v[3]);
+    o0 = __float_as_uint(v[0]);
+    o1 = __float_as_uint(v[1]);
+    r[0] = v[0];
+    r[1] = v[1];
+  }
+  if constexpr (E::kBytes == 2) {
+    if (nt) store_nt(reinterpret_cast<uint32_t*>(ptr), o0);
+    else *reinterpret_cast<uint32_t*>(ptr) = o0;
+  } else {
+    if (nt) store_nt(reinterpret_cast<uint2*>(ptr), make_uint2(o0, o1));
+    else *reinterpret_cast<uint2*>(ptr) = make_uint2(o0, o1);
   }
 }
 
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
   float* hin32 = kDebug ? hin_f32 + blk0 : nullptr;
   const float* lam = ws.lam + k0 * H + h;
   float st[kCh] = {};
+  const bool nt = p.stream_states != 0;
   // Software pipeline over blocks of kDepth chunks with two register buffers
   // used in turn (no copies between them): the loads of the next block are in
   // flight while the current block is scanned, so only the FMA chain is serial.
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
   auto lane_dec = [&](float dec, int u) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dec), u)); };
   auto step = [&](int kk, const float (&sv)[kCh], float dec) {
     float r[kCh];
-    store_ch<E>(hin + (int64_t)kk * stride + lo, st, r);
+    store_ch<E>(hin + (int64_t)kk * stride + lo, st, r, nt);
     if constexpr (kDebug) {
 #pragma unroll
       for (int c = 0; c < kCh; ++c) hin32[(int64_t)kk * stride + lo + c] = r[c];

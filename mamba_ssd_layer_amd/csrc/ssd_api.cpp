@@ -25,6 +25,8 @@ bool config_supported(Dtype dt, int Q, int N) {
 
 static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
+constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
+
 static int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -333,6 +335,16 @@ static Problem make_problem(const void* x, const float* dt, const float* A_head,
   p.kmax = 0;
   if (chunk_len > 0 && nseq >= 0 && total >= 0)
     p.kmax = cu ? ceil_div(total, chunk_len) + nseq : nseq * ceil_div(seqlen, chunk_len);
+  // A forward touches x and y, the chunk states and the passed states (each
+  // (chunks, H, P, N)), B and C.  While that fits in the memory-side last-level
+  // cache (MI355X: 256 MiB of Infinity Cache) the states written by one kernel
+  // are still there when the next one reads them, and are stored normally;
+  // beyond it they are streamed out with the non-temporal hint so that they do
+  // not displace the inputs.
+  const double esz = p.dtype == Dtype::BF16 ? 2.0 : 4.0;
+  const double footprint = esz * ((double)p.total * p.H * p.P * 2.0 + (double)p.kmax * p.H * p.P * p.N * 2.0 +
+                                  (double)p.total * p.G * p.N * 2.0);
+  p.stream_states = footprint > kLastLevelCacheBytes ? 1 : 0;
   return p;
 }
 

@@ -45,6 +45,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Stores with the non-temporal hint: for data that the rest of the kernel (or
+// the next kernel) does not read back soon, so that it is streamed out instead
+// of displacing lines that are reused.  (The hint must be fixed at compile
+// time at each site: two otherwise equal stores under a run-time branch are
+// merged into one without it.)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt(uint4* p, const uint4& v) {
+  __builtin_nontemporal_store((u32x4_t){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_nt(uint2* p, const uint2& v) {
+  __builtin_nontemporal_store((u32x2_t){v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void store_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+// Load with the non-temporal hint: for the last read of data.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(q.x, q.y, q.z, q.w);
+}
+
 __device__ __forceinline__ floatx16_t mfma32x32x16(const uint4& a, const uint4& b, floatx16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);

@@ -39,6 +39,9 @@ struct Problem {
   int H, P, N, G, Q;
   Dtype dtype;
   int64_t kmax;           // chunk slots: exact when batched, a bound when varlen
+  int stream_states;      // 1: chunk states and passed states are stored with the
+                          // non-temporal hint (set when a forward's data exceeds the
+                          // last-level cache; y always is)
 };
 
 // Device workspace, carved out of one allocation (256-byte aligned pieces).

@@ -40,13 +40,16 @@ struct RowTile {
   uint4 v[NPT];
   int len;  // rows >= len are stored as zeros
 
-  // t: this thread's index among the NTHR staging threads
+  // t: this thread's index among the NTHR staging threads; NTL: loads with the
+  // non-temporal hint (the tile's last read)
+  template <bool NTL = false>
   __device__ __forceinline__ void load(const T* __restrict__ g, int64_t ld, int L, int t = threadIdx.x) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       const int idx = min(t + i * NTHR, NV - 1);
       const int r = idx / VPR, c = idx % VPR;
-      v[i] = *reinterpret_cast<const uint4*>(g + min(r, L - 1) * ld + c * VEC);
+      const uint4* src = reinterpret_cast<const uint4*>(g + min(r, L - 1) * ld + c * VEC);
+      v[i] = NTL ? load_nt(src) : *src;
     }
     len = L;
   }
