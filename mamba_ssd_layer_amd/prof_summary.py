@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the SSD kernels (text for profiles/).
 
-    python -m mamba_ssd_layer_amd.prof_summary kernels <trace_dir> [--first N]
+    python -m mamba_ssd_layer_amd.prof_summary kernels <trace_dir> [--first N] [--last N]
     python -m mamba_ssd_layer_amd.prof_summary traffic --fetch D --write D \
         --cal-fetch D --cal-write D --kernel chunk_output --workload long_T16k [--command C ...]
 
@@ -55,7 +55,7 @@ def _short(name: str) -> str:
     return name.replace("void ", "").split("(")[0]
 
 
-def kernels_table(trace_dir: str, first: int = 0) -> str:
+def kernels_table(trace_dir: str, first: int = 0, last: int = 0) -> str:
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
     ssd = [r for r in rows if "ssd::" in r["Name"]]
     total = sum(float(r["TotalDurationNs"]) for r in ssd)
@@ -76,6 +76,22 @@ def kernels_table(trace_dir: str, first: int = 0) -> str:
         out.append("")
         out.append(f"Gap between consecutive SSD kernels of a forward: median {statistics.median(gaps) / 1e3:.2f} us "
                    f"over {len(gaps)} gaps" + (f" (first {first} SSD dispatches)." if first else "."))
+    if last:
+        # the last `last` dispatches of each kernel: bench.py's event-timed pass
+        alltr = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
+                 if "ssd::" in r["Kernel_Name"]]
+        alltr.sort(key=lambda r: int(r["Start_Timestamp"]))
+        by = {}
+        for r in alltr:
+            by.setdefault(_short(r["Kernel_Name"]), []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        out.append("")
+        out.append(f"Average over the last {last} dispatches of each kernel (bench.py's event-timed pass):")
+        out.append("")
+        out.append("| kernel | dispatches | avg us |")
+        out.append("|---|---|---|")
+        for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1][-last:])):
+            tail = d[-last:]
+            out.append(f"| {name} | {len(tail)} | {sum(tail) / len(tail) / 1e3:.1f} |")
     return "\n".join(out)
 
 
@@ -122,6 +138,7 @@ def main(argv=None):
     k = sub.add_parser("kernels")
     k.add_argument("trace_dir")
     k.add_argument("--first", type=int, default=0, help="gaps over the first N SSD dispatches only")
+    k.add_argument("--last", type=int, default=0, help="also average the last N dispatches of each kernel")
     t = sub.add_parser("traffic")
     for a in ("fetch", "write", "cal_fetch", "cal_write"):
         t.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
@@ -131,7 +148,7 @@ def main(argv=None):
     t.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
-        print(kernels_table(a.trace_dir, a.first))
+        print(kernels_table(a.trace_dir, a.first, a.last))
     else:
         json.dump(traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.kernel, a.workload, a.copy_mib,
                           a.command), sys.stdout, indent=1)
