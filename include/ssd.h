@@ -10,14 +10,17 @@
  * The operation ([T] §2.4 recurrent form and §5.1; [M] §3.1.2): for every
  * sequence and head h, with a_t = exp(dt_t * A_h),
  *     h_t = a_t * h_{t-1} + x_t (outer) B_t       (state (P, N), zero before
- *                                                   the first token)
+ *                                                   the first token unless
+ *                                                   ssd_chunked_fwd_ex is
+ *                                                   given an initial state)
  *     y_t = h_t . C_t                              (P values)
  * computed exactly (up to rounding) by the chunked block decomposition of the
  * 1-semiseparable matrix M = L o (C B^T) of [M] §3.5: diagonal blocks in the
  * quadratic (attention-like) form, chunk states, a scan that passes states
  * between chunks, and a state-to-output product.  Head h reads B/C group
  * g = h * G / H (G divides H; [M] §3.6.2 grouped heads).  The first token's
- * a_t of every sequence multiplies a zero state and has no effect.
+ * a_t of every sequence multiplies the state before it: zero (no effect)
+ * unless an initial state is given.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
@@ -108,6 +111,34 @@ ssd_status ssd_chunked_fwd_varlen(const void* x, const float* dt, const float* A
                                   int32_t headdim, int32_t dstate, int32_t ngroups,
                                   int32_t chunk_len, ssd_dtype dtype, void* y,
                                   float* final_state, void* stream);
+
+/*
+ * Forward from given initial states, batched or packed ([M] §3.7.2 "Sequence
+ * Parallelism": a worker starts from the state its predecessor hands over and
+ * passes its final state on; the §3.5 listing's optional initial state, put
+ * in front of the chunk states before they are passed).  Splitting a sequence
+ * at any token and running the second part from the first part's final state
+ * gives the whole sequence's y and final state (up to rounding).
+ *   cu_seqlens     NULL: batched form, nseqs sequences of total_len / nseqs
+ *                  tokens each (total_len a multiple of nseqs; x (nseqs, T, H,
+ *                  P) ... as for ssd_chunked_fwd).  Otherwise as for
+ *                  ssd_chunked_fwd_varlen.
+ *   initial_state  (nseqs, nheads, headdim, dstate) fp32 DEVICE array,
+ *                  16-byte aligned: h_{-1} of each sequence, the state the
+ *                  first token's a_t multiplies; NULL means zero (then the
+ *                  call equals ssd_chunked_fwd / ssd_chunked_fwd_varlen).  It
+ *                  is read, never written, and may be the final_state buffer
+ *                  of an earlier call; it must not alias this call's
+ *                  final_state.  An empty sequence's final state is its
+ *                  initial state.
+ * Other arguments, errors and execution as for the entry points above.
+ */
+ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_head,
+                              const void* B, const void* C, const int32_t* cu_seqlens,
+                              int64_t nseqs, int64_t total_len, int32_t nheads,
+                              int32_t headdim, int32_t dstate, int32_t ngroups,
+                              int32_t chunk_len, ssd_dtype dtype, const float* initial_state,
+                              void* y, float* final_state, void* stream);
 
 /*
  * The same pass, also copying the intermediates of the block decomposition

@@ -31,6 +31,8 @@ SIGNATURES = {
                          _i32, _vp, _fp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_varlen": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _vp, _fp, _vp], ctypes.c_int),
+    "ssd_chunked_fwd_ex": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32, _i32,
+                            _i32, _i32, _fp, _vp, _fp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_intermediates": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _vp, _fp, _fp, _fp, _fp, _vp],
                                       ctypes.c_int),
@@ -166,6 +168,60 @@ def ssd_chunked_fwd_varlen(x, dt, A_head, B, C, cu_seqlens, chunk_len: int, y=No
                                       _dtype_code(x), _ptr(y), _ptr(final_state),
                                       ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_chunked_fwd_varlen")
+    return y, final_state
+
+
+def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, initial_state=None,
+                       y=None, final_state=None, return_final_state: bool = True):
+    """SSD forward from initial states.  Batched (4-D x (b,T,H,P), cu_seqlens None)
+    or packed (3-D x (Ttot,H,P) with cu_seqlens (S+1,) int32 on the device).
+    initial_state (S,H,P,N) fp32 or None (zero).  Returns (y, final_state (S,H,P,N) or None)."""
+    dev = x.device
+    if x.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens goes with packed 3-D inputs")
+        b, T, H, P = x.shape
+        S, Tt = b, b * T
+        lead = (b, T)
+    elif x.dim() == 3:
+        if cu_seqlens is None:
+            raise ValueError("packed 3-D inputs need cu_seqlens")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        Tt, H, P = x.shape
+        S = cu_seqlens.shape[0] - 1
+        lead = (Tt,)
+    else:
+        raise ValueError("x must be (b,T,H,P) or (Ttot,H,P)")
+    G, N = B.shape[-2:]
+    _need(x, "x", x.dtype, dev)
+    _need(dt, "dt", torch.float32, dev)
+    _need(A_head, "A_head", torch.float32, dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev)
+    if tuple(dt.shape) != lead + (H,) or tuple(A_head.shape) != (H,) or \
+            tuple(B.shape) != lead + (G, N) or tuple(C.shape) != lead + (G, N):
+        raise ValueError("inconsistent shapes")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if tuple(initial_state.shape) != (S, H, P, N):
+            raise ValueError("initial_state must be (S,H,P,N)")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, dev)
+        if y.shape != x.shape:
+            raise ValueError("y must have x's shape")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, dev)
+        if tuple(final_state.shape) != (S, H, P, N):
+            raise ValueError("final_state must be (S,H,P,N)")
+    rc = lib().ssd_chunked_fwd_ex(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), _ptr(cu_seqlens),
+                                  S, Tt, H, P, N, G, int(chunk_len), _dtype_code(x),
+                                  _ptr(initial_state), _ptr(y), _ptr(final_state),
+                                  ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_chunked_fwd_ex")
     return y, final_state
 
 

@@ -5,9 +5,12 @@
 // "Center factors" and step 3 of "SSD algorithm: chunking and state passing":
 // a scalar SSM (1-SS) recurrence over the chunks of each sequence, run on P*N
 // independent channels per head:
-//     Hin[first chunk] = 0,   Hin[c+1] = exp(lam_c) * Hin[c] + S_c,
+//     Hin[first chunk] = h0,  Hin[c+1] = exp(lam_c) * Hin[c] + S_c,
 // where lam_c is the chunk's total log-decay; the value after the last chunk is
-// the final state.  [M] §3.5.3 prices this scan at T*N*P/Q work, a small part
+// the final state.  h0 is the sequence's initial state (zero unless the caller
+// gives one: [M] §3.7.2 "Sequence Parallelism", where each worker starts from
+// the state its predecessor passes on; the §3.5 listing prepends the same
+// optional initial state to the chunk states before this scan).  [M] §3.5.3 prices this scan at T*N*P/Q work, a small part
 // of the whole.
 //
 // Design (gfx950): pure HBM streaming, bound by how many bytes are in flight.
@@ -98,7 +101,13 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
   T* hin = reinterpret_cast<T*>(ws.hin) + blk0;
   float* hin32 = kDebug ? hin_f32 + blk0 : nullptr;
   const float* lam = ws.lam + k0 * H + h;
+  // running state: the sequence's initial state (zero when none is given)
   float st[kCh] = {};
+  if (p.initial_state != nullptr) {
+    const float2 s0 = *reinterpret_cast<const float2*>(p.initial_state + (s * H + h) * (int64_t)PN + ch);
+    st[0] = s0.x;
+    st[1] = s0.y;
+  }
   const bool nt = p.stream_states != 0;
   // Software pipeline over blocks of kDepth chunks with two register buffers
   // used in turn (no copies between them): the loads of the next block are in

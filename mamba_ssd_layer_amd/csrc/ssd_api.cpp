@@ -190,6 +190,7 @@ static ssd_status validate(const Problem& p) {
       return SSD_ERR_INVALID_ARGUMENT;
   }
   if (p.final_state && !aligned(p.final_state, 16)) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.initial_state && !aligned(p.initial_state, 16)) return SSD_ERR_INVALID_ARGUMENT;
   if (p.cu && !aligned(p.cu, 4)) return SSD_ERR_INVALID_ARGUMENT;
   // sizes must keep every index and grid inside 32/64-bit ranges
   const int64_t lim = (int64_t)1 << 40;
@@ -325,10 +326,11 @@ static Problem make_problem(const void* x, const float* dt, const float* A_head,
                             const void* C, const int32_t* cu, int64_t nseq, int64_t seqlen,
                             int64_t total, int32_t nheads, int32_t headdim, int32_t dstate,
                             int32_t ngroups, int32_t chunk_len, ssd_dtype dtype, void* y,
-                            float* final_state) {
+                            float* final_state, const float* initial_state = nullptr) {
   Problem p;
   p.x = x; p.dt = dt; p.A = A_head; p.B = B; p.C = C; p.cu = cu; p.y = y;
   p.final_state = final_state;
+  p.initial_state = initial_state;
   p.nseq = nseq; p.seqlen = seqlen; p.total = total;
   p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups; p.Q = chunk_len;
   p.dtype = static_cast<Dtype>(dtype);
@@ -369,6 +371,22 @@ ssd_status ssd_chunked_fwd_varlen(const void* x, const float* dt, const float* A
   if (nseqs > 0 && cu_seqlens == nullptr) return SSD_ERR_INVALID_ARGUMENT;
   const Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, 0, total_len, nheads,
                                  headdim, dstate, ngroups, chunk_len, dtype, y, final_state);
+  return run(p, static_cast<hipStream_t>(stream), nullptr);
+}
+
+ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_head, const void* B,
+                              const void* C, const int32_t* cu_seqlens, int64_t nseqs,
+                              int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
+                              int32_t ngroups, int32_t chunk_len, ssd_dtype dtype,
+                              const float* initial_state, void* y, float* final_state,
+                              void* stream) {
+  if (nseqs < 0 || total_len < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs > 0 && total_len % nseqs != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs == 0 && total_len != 0) return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t seqlen = (cu_seqlens == nullptr && nseqs > 0) ? total_len / nseqs : 0;
+  const Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, seqlen, total_len, nheads,
+                                 headdim, dstate, ngroups, chunk_len, dtype, y, final_state,
+                                 initial_state);
   return run(p, static_cast<hipStream_t>(stream), nullptr);
 }
 

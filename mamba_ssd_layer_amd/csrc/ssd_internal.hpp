@@ -33,6 +33,7 @@ struct Problem {
   const int32_t* cu;      // (S+1) on the device, or nullptr (batched)
   void* y;                // (Ttot, H, P)  element dtype
   float* final_state;     // (S, H, P, N) or nullptr
+  const float* initial_state;  // (S, H, P, N): state before each sequence's first token, or nullptr (zero)
   int64_t nseq;           // S
   int64_t seqlen;         // T (batched form only)
   int64_t total;          // Ttot

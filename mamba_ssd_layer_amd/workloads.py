@@ -156,6 +156,14 @@ def make_inputs(w: Workload, seed: int = 0, seqlens=None) -> Inputs:
                   None if lens is None else np.asarray(lens, dtype=np.int64))
 
 
+def initial_states(nseqs: int, nheads: int, headdim: int, dstate: int, seed: int = 0) -> np.ndarray:
+    """Seeded initial states (nseqs, nheads, headdim, dstate) float32 ~ N(0, 1),
+    from their own generator (default_rng(seed + 1_000_003)) so that drawing
+    them leaves the input draws of make_inputs unchanged."""
+    rng = np.random.default_rng(seed + 1_000_003)
+    return rng.standard_normal((nseqs, nheads, headdim, dstate), dtype=np.float32)
+
+
 def flops_pages(w: Workload, total_tokens: int, seqlens=None) -> dict:
     """FLOP accountings of one forward pass (no arithmetic of the map itself).
 

@@ -109,6 +109,28 @@ def test_varlen_rejects_invalid_arguments(lib):
                                       256, 1, FAKE, None, None) == INVALID
 
 
+def call_ex(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, cu=None, S=2, T=512, H=4, P=64, N=128, G=1,
+             Q=256, dtype=1, h0=FAKE, y=FAKE, fs=FAKE)
+    a.update(kw)
+    return lib.ssd_chunked_fwd_ex(a["x"], a["dt"], a["A"], a["B"], a["C"], a["cu"], a["S"], a["T"],
+                                  a["H"], a["P"], a["N"], a["G"], a["Q"], a["dtype"], a["h0"], a["y"],
+                                  a["fs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h0=FAKE + 4), INVALID),       # misaligned initial state
+    (dict(S=3, T=512), INVALID),        # batched form: total_len not a multiple of nseqs
+    (dict(S=0, T=10), INVALID),
+    (dict(S=-1), INVALID),
+    (dict(cu=FAKE + 2), INVALID),       # misaligned cu_seqlens
+    (dict(N=48), UNSUPPORTED),
+    (dict(H=3, G=2), INVALID),
+])
+def test_ex_rejects_invalid_arguments(lib, kw, code):
+    assert call_ex(lib, **kw) == code
+
+
 def test_intermediates_rejects_uneven_batch(lib):
     assert lib.ssd_chunked_fwd_intermediates(FAKE, FAKE, FAKE, FAKE, FAKE, None, 3, 100, 4, 64, 128,
                                              1, 256, 1, FAKE, None, None, None, None, None) == INVALID

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from mamba_ssd_layer_amd import _binding as bd
-from mamba_ssd_layer_amd.workloads import WORKLOADS, Workload, make_inputs
+from mamba_ssd_layer_amd.workloads import WORKLOADS, Workload, initial_states, make_inputs
 
 from gpu_common import TOL, check_parity, log, max_rel_l2, require_gpu, run_gpu, run_oracle, to_device
 
@@ -227,3 +227,95 @@ def test_workspace_reuse_across_sizes_and_streams(dev):
         yr, fr = ref[name]
         assert np.array_equal(y.float().cpu().numpy(), yr), name
         assert np.array_equal(fs.cpu().numpy(), fr), name
+
+
+# ------------------------------------------------------- initial state ----
+def _oracle_with_init(inp, h0):
+    return oracle.recurrence(inp.x, inp.dt, inp.A, inp.B, inp.C, cu_seqlens=inp.packed_cu_seqlens(),
+                             init_state=h0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_initial_state_batched(dev, dtype):
+    """Batched forward from given initial states against the oracle's recurrence
+    started from the same states (the first token's decay now matters)."""
+    w = SMALL.with_(dtype=dtype, dstate=128, chunk_len=128, seqlen=700, batch=3, nheads=8, ngroups=2)
+    inp = make_inputs(w, 31)
+    h0 = initial_states(3, 8, 64, 128, seed=31)
+    log(f"[init] batched {dtype} b=3 T=700 H=8 N=128 Q=128")
+    d = to_device(inp, dev)
+    y, fs = bd.ssd_chunked_fwd_ex(d["x"], d["dt"], d["A"], d["B"], d["C"], 128,
+                                  initial_state=torch.from_numpy(h0).to(dev))
+    torch.cuda.synchronize()
+    yr, fr = _oracle_with_init(inp, h0)
+    ey, ef = max_rel_l2(y.float().cpu().numpy(), yr, fs.cpu().numpy(), fr, inp.packed_cu_seqlens())
+    log(f"[init]   max rel-L2 y={ey:.3e} final_state={ef:.3e}")
+    assert ey <= TOL[dtype] and ef <= TOL[dtype]
+
+
+def test_initial_state_varlen(dev):
+    """Packed sequences (empty ones included) from given initial states; an empty
+    sequence's final state is its initial state, exactly."""
+    lens = [300, 0, 1, 513, 64, 0, 77]
+    w = SMALL.with_(varlen=True, batch=len(lens), dstate=128, chunk_len=128, nheads=8, ngroups=2)
+    inp = make_inputs(w, 22, seqlens=lens)
+    h0 = initial_states(len(lens), 8, 64, 128, seed=22)
+    log("[init] varlen with empty sequences")
+    d = to_device(inp, dev)
+    y, fs = bd.ssd_chunked_fwd_ex(d["x"], d["dt"], d["A"], d["B"], d["C"], 128, cu_seqlens=d["cu"],
+                                  initial_state=torch.from_numpy(h0).to(dev))
+    torch.cuda.synchronize()
+    fg = fs.cpu().numpy()
+    yr, fr = _oracle_with_init(inp, h0)
+    ey, ef = max_rel_l2(y.float().cpu().numpy(), yr, fg, fr, inp.packed_cu_seqlens())
+    log(f"[init]   max rel-L2 y={ey:.3e} final_state={ef:.3e}")
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+    for s, L in enumerate(lens):
+        if L == 0:
+            np.testing.assert_array_equal(fg[s], h0[s])
+
+
+def test_ex_without_initial_state_matches_fwd(dev):
+    """ssd_chunked_fwd_ex with no initial state is the plain forward, bit for bit,
+    in both forms."""
+    inp = make_inputs(SMALL.with_(seqlen=600, dstate=128, chunk_len=128), 7)
+    d = to_device(inp, dev)
+    log("[init] ex(None) vs fwd, batched")
+    y0, f0 = bd.ssd_chunked_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], 128)
+    y1, f1 = bd.ssd_chunked_fwd_ex(d["x"], d["dt"], d["A"], d["B"], d["C"], 128)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    lens = [100, 0, 350]
+    vin = make_inputs(SMALL.with_(varlen=True, batch=3, dstate=128, chunk_len=128), 8, seqlens=lens)
+    dv = to_device(vin, dev)
+    log("[init] ex(None) vs fwd, varlen")
+    y0, f0 = bd.ssd_chunked_fwd_varlen(dv["x"], dv["dt"], dv["A"], dv["B"], dv["C"], dv["cu"], 128)
+    y1, f1 = bd.ssd_chunked_fwd_ex(dv["x"], dv["dt"], dv["A"], dv["B"], dv["C"], 128, cu_seqlens=dv["cu"])
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+
+
+@pytest.mark.parametrize("name,dtype,Q,T1", [
+    ("long_T16k", "bf16", 256, 8192),     # two halves of the long sequence (one GPU's share each)
+    ("long_T16k", "bf16", 256, 5000),     # a split inside a chunk
+    ("long_T16k", "f32", 128, 6001),
+    ("mamba2_2p7b_T2k", "bf16", 256, 1000),
+])
+def test_split_and_resume(dev, name, dtype, Q, T1):
+    """Running tokens [0, T1) and then [T1, T) from the first part's final state
+    gives the whole sequence's y and final state: the hand-over of context
+    parallelism, each part being one GPU's share at its real shape."""
+    w = WORKLOADS[name].with_(dtype=dtype, chunk_len=Q)
+    inp = make_inputs(w, 0)
+    d = to_device(inp, dev)
+    log(f"[split] {name} {dtype} Q={Q} at T1={T1}")
+    y1, f1 = bd.ssd_chunked_fwd(*(d[k][:, :T1].contiguous() for k in ("x", "dt")), d["A"],
+                                *(d[k][:, :T1].contiguous() for k in ("B", "C")), Q)
+    y2, f2 = bd.ssd_chunked_fwd_ex(*(d[k][:, T1:].contiguous() for k in ("x", "dt")), d["A"],
+                                   *(d[k][:, T1:].contiguous() for k in ("B", "C")), Q, initial_state=f1)
+    torch.cuda.synchronize()
+    y = torch.cat([y1, y2], dim=1).float().cpu().numpy()
+    yr, fr = run_oracle(inp)
+    ey, ef = max_rel_l2(y, yr, f2.cpu().numpy(), fr, inp.packed_cu_seqlens())
+    log(f"[split]   max rel-L2 y={ey:.3e} final_state={ef:.3e}")
+    assert ey <= TOL[dtype] and ef <= TOL[dtype]
