@@ -9,7 +9,10 @@ bracketed by torch.cuda.synchronize() on both sides.  A second pass of K steps
 with per-kernel HIP events (recorded by the library on its launch stream) gives
 each kernel's average duration; the roofline of the dominant kernel uses it.
 The fp64 CPU oracle is timed on the host cores on the same workload (rank 0)
-and its output also checks the GPU result.
+and its output also checks the GPU result.  The line also carries, under
+"decode", one recurrent decode step (ssd_decode_step) on 64 sequences of a
+Mamba-2-2.7B-like layer (H=80, N=128), with its own HBM roofline
+(--no-decode skips it).
 
 Prints ONE JSON line.
 """
@@ -78,6 +81,63 @@ def kernel_work(w, seqlens, cb_pass):
     return f, b
 
 
+def decode_work(w):
+    """Algorithmic FLOPs and HBM bytes of one decode step (ssd_decode_step) on
+    workload w (batch sequences of one token): per (sequence, head) the fp32
+    state is read and written once (8 P N bytes) and 4 P N FLOPs are done
+    (2 P N for the update, 2 P N for the output); x, y, dt, B and C are read or
+    written once."""
+    e = 2 if w.dtype == "bf16" else 4
+    b, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    flops = b * H * 4 * P * N
+    byts = b * H * (8 * P * N + 2 * P * e + 4) + H * 4 + 2 * b * G * N * e
+    return flops, byts
+
+
+def bench_decode(bd, torch, steps, warmup):
+    """One decode step per sequence on the decode workload, timed like the
+    forward (host clock over `steps` back-to-back steps after `warmup` untimed
+    ones), plus the kernel's average launch time from HIP events."""
+    from mamba_ssd_layer_amd.workloads import DECODE_WORKLOADS, initial_states, make_inputs
+    w = DECODE_WORKLOADS["decode_2p7b_b64"]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w, 0)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    x = torch.from_numpy(inp.x[:, 0]).to(dev).to(tdt).contiguous()
+    dt = torch.from_numpy(inp.dt[:, 0]).to(dev).contiguous()
+    A = torch.from_numpy(inp.A).to(dev)
+    B = torch.from_numpy(inp.B[:, 0]).to(dev).to(tdt).contiguous()
+    C = torch.from_numpy(inp.C[:, 0]).to(dev).to(tdt).contiguous()
+    state = torch.from_numpy(initial_states(w.batch, w.nheads, w.headdim, w.dstate, 0)).to(dev)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        bd.ssd_decode_step(x, dt, A, B, C, state, y=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bd.ssd_decode_step(x, dt, A, B, C, state, y=y)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    bd.kernel_timing_read(reset=True)
+    bd.kernel_timing_enable(True)
+    for _ in range(steps):
+        bd.ssd_decode_step(x, dt, A, B, C, state, y=y)
+    torch.cuda.synchronize()
+    bd.kernel_timing_enable(False)
+    kms = bd.kernel_timing_read(reset=True)["decode_step"]
+    kms = kms[0] / kms[1] if kms[1] else None
+    flops, byts = decode_work(w)
+    ach = byts / (kms / 1e3) / 1e9 if kms else None
+    return {
+        "workload": w.name, "batch": w.batch, "nheads": w.nheads, "headdim": w.headdim,
+        "dstate": w.dstate, "ngroups": w.ngroups, "dtype": w.dtype,
+        "us_per_step": sec * 1e6, "tokens_per_s": w.batch / sec,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS if ach else None, "traffic": None,
+                     "avg_launch_ms": kms, "bytes_per_launch": byts, "flops_per_launch": flops},
+    }
+
+
 def min_io_bytes(w, total_tokens, nseq):
     e = 2 if w.dtype == "bf16" else 4
     H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
@@ -108,6 +168,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="long_T16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step measurement reported under \"decode\"")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (--steps times), for "
                          "scaling the HBM byte counters of a profiler")
@@ -240,6 +302,9 @@ def main():
         "kernel_roofline": kroof,
         "cpu_baseline": None,
     }
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200))
 
     if not args.no_cpu_baseline:
         import oracle

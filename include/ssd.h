@@ -141,6 +141,34 @@ ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_hea
                               void* y, float* final_state, void* stream);
 
 /*
+ * One recurrent step for a batch of sequences: the decode (autoregressive
+ * inference) mode ([T] §2.1: inference runs the recurrent form one input step
+ * at a time with a constant-size state; [M] §3.5.3 cost table: N^2 FLOPs per
+ * step).  For every sequence b and head h, a = exp(dt[b,h] * A_head[h]) and g
+ * the head's group:
+ *     state[b,h] <- a * state[b,h] + x[b,h,:] (outer) B[b,g,:]
+ *     y[b,h,p]   <- sum_n state[b,h,p,n] * C[b,g,n]
+ * i.e. one more token of the forward pass: the final_state of a forward call
+ * continues here, and T steps equal a forward over those T tokens started
+ * from the same state (up to rounding).
+ *   x      (batch, nheads, headdim)          element dtype (one token each)
+ *   dt     (batch, nheads)                   fp32
+ *   A_head (nheads)                          fp32
+ *   B, C   (batch, ngroups, dstate)          element dtype
+ *   state  (batch, nheads, headdim, dstate)  fp32, read and overwritten in
+ *          place (the forward's final_state layout)
+ *   y      (batch, nheads, headdim)          element dtype, overwritten
+ *          (bf16: rounded to nearest even); must not alias an input
+ * headdim 64, dstate in {16, 32, 64, 128, 256}; no workspace.  Alignment,
+ * validation, execution and errors as for the forward.  batch == 0 is a
+ * no-op.
+ */
+ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, const void* B,
+                           const void* C, int64_t batch, int32_t nheads, int32_t headdim,
+                           int32_t dstate, int32_t ngroups, ssd_dtype dtype, float* state,
+                           void* y, void* stream);
+
+/*
  * The same pass, also copying the intermediates of the block decomposition
  * ([M] §3.5.2 "SSD algorithm: chunking and state passing") into caller
  * buffers, for checking each kernel on its own.  cu_seqlens == NULL selects
@@ -184,8 +212,8 @@ const char* ssd_status_string(ssd_status status);
  * states, 2 state passing, 3 chunk output (kernel-matrix tiles, diagonal
  * blocks, state-to-output), 4 separate kernel-matrix pass (only the
  * configurations whose chunk-output kernel cannot hold the tiles in LDS:
- * fp32, and bf16 with dstate 256 at chunk_len 256).  Ids 0..4; another id is
- * SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
+ * fp32, and bf16 with dstate 256 at chunk_len 256), 5 decode step.  Ids
+ * 0..5; another id is SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
  * Not re-entrant with concurrent forward calls.
  */
 ssd_status ssd_kernel_timing_enable(int32_t enable);

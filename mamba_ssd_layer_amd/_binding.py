@@ -33,6 +33,8 @@ SIGNATURES = {
                                 _i32, _i32, _i32, _vp, _fp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_ex": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32, _i32,
                             _i32, _i32, _fp, _vp, _fp, _vp], ctypes.c_int),
+    "ssd_decode_step": ([_vp, _fp, _fp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _fp, _vp, _vp],
+                        ctypes.c_int),
     "ssd_chunked_fwd_intermediates": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _vp, _fp, _fp, _fp, _fp, _vp],
                                       ctypes.c_int),
@@ -44,7 +46,7 @@ SIGNATURES = {
                                 ctypes.POINTER(ctypes.c_int64), _i32], ctypes.c_int),
 }
 
-KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb"]
+KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb", "decode_step"]
 
 
 class SSDError(RuntimeError):
@@ -223,6 +225,36 @@ def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, ini
                                   ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_chunked_fwd_ex")
     return y, final_state
+
+
+def ssd_decode_step(x, dt, A_head, B, C, state, y=None):
+    """One recurrent (decode) step.  x (b,H,P), dt (b,H) fp32, A_head (H,) fp32,
+    B/C (b,G,N) in x's dtype, state (b,H,P,N) fp32, updated in place.
+    Returns y (b,H,P) in x's dtype."""
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, nheads, headdim)")
+    b, H, P = x.shape
+    G, N = B.shape[-2:]
+    dev = x.device
+    _need(x, "x", x.dtype, dev)
+    _need(dt, "dt", torch.float32, dev)
+    _need(A_head, "A_head", torch.float32, dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev)
+    _need(state, "state", torch.float32, dev)
+    if tuple(dt.shape) != (b, H) or tuple(A_head.shape) != (H,) or tuple(B.shape) != (b, G, N) or \
+            tuple(C.shape) != (b, G, N) or tuple(state.shape) != (b, H, P, N):
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, dev)
+        if y.shape != x.shape:
+            raise ValueError("y must have x's shape")
+    rc = lib().ssd_decode_step(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), b, H, P, N, G,
+                               _dtype_code(x), _ptr(state), _ptr(y), ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_decode_step")
+    return y
 
 
 def ssd_chunked_fwd_intermediates(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None):

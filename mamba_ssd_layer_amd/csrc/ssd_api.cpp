@@ -410,6 +410,32 @@ ssd_status ssd_chunked_fwd_intermediates(const void* x, const float* dt, const f
   return run(p, static_cast<hipStream_t>(stream), &dbg);
 }
 
+ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, const void* B,
+                           const void* C, int64_t batch, int32_t nheads, int32_t headdim,
+                           int32_t dstate, int32_t ngroups, ssd_dtype dtype, float* state, void* y,
+                           void* stream) {
+  if (batch < 0 || nheads <= 0 || ngroups <= 0 || nheads % ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return SSD_ERR_INVALID_ARGUMENT;
+  if (headdim <= 0 || dstate <= 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (headdim != kHeadDim) return SSD_ERR_UNSUPPORTED;
+  if (!(dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128 || dstate == 256)) return SSD_ERR_UNSUPPORTED;
+  if (batch > ((int64_t)1 << 40) / nheads || batch * nheads > 0x7fffffffLL) return SSD_ERR_INVALID_ARGUMENT;
+  if (batch > 0) {
+    if (!x || !dt || !A_head || !B || !C || !state || !y) return SSD_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(state, 16) ||
+        !aligned(dt, 4) || !aligned(A_head, 4))
+      return SSD_ERR_INVALID_ARGUMENT;
+  }
+  ssd_status st = check_device();
+  if (st != SSD_OK) return st;
+  DecodeProblem d;
+  d.x = x; d.dt = dt; d.A = A_head; d.B = B; d.C = C; d.state = state; d.y = y;
+  d.batch = batch; d.H = nheads; d.P = headdim; d.N = dstate; d.G = ngroups;
+  d.dtype = static_cast<Dtype>(dtype);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return map_err(timed_launch(kK6DecodeStep, s, [&] { return launch_decode_step(d, s); }));
+}
+
 const char* ssd_status_string(ssd_status status) {
   switch (status) {
     case SSD_OK: return "SSD_OK";

@@ -45,6 +45,20 @@ struct Problem {
                           // last-level cache; y always is)
 };
 
+// One recurrent (decode) step for a batch of sequences.
+struct DecodeProblem {
+  const void* x;      // (batch, H, P)  element dtype
+  const float* dt;    // (batch, H)
+  const float* A;     // (H)
+  const void* B;      // (batch, G, N)  element dtype
+  const void* C;      // (batch, G, N)  element dtype
+  float* state;       // (batch, H, P, N) fp32, updated in place
+  void* y;            // (batch, H, P)  element dtype
+  int64_t batch;
+  int H, P, N, G;
+  Dtype dtype;
+};
+
 // Device workspace, carved out of one allocation (256-byte aligned pieces).
 struct Workspace {
   int32_t* seq_off = nullptr;    // (S+1) first chunk slot of each sequence; [S] = chunk count
@@ -77,7 +91,7 @@ bool config_supported(Dtype dt, int Q, int N);
 
 // Kernel launchers; each returns the launch status.  Kernel ids for timing.
 enum KernelId { kK0SeqTable = 0, kK13ChunkState = 1, kK4StatePass = 2, kK25ChunkOutput = 3,
-                kK2ChunkCB = 4, kNumKernels = 5 };
+                kK2ChunkCB = 4, kK6DecodeStep = 5, kNumKernels = 6 };
 // K0 (varlen only): per-sequence first token, length and first chunk slot.
 hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
 // K1 + K3: chunk-local log-decay cumsum (-> acs, lam, dmax), chunk states (-> states);
@@ -91,6 +105,8 @@ hipError_t launch_state_pass(const Problem& p, const Workspace& ws, float* hin_f
 hipError_t launch_chunk_cb(const Problem& p, const Workspace& ws, hipStream_t s);
 // K2 + K5: diagonal blocks and state-to-output (-> y).
 hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s);
+// K6: one recurrent step (decode): state update in place and y.
+hipError_t launch_decode_step(const DecodeProblem& d, hipStream_t s);
 bool chunk_state_supported(Dtype dt, int Q, int N);
 bool chunk_output_supported(Dtype dt, int Q, int N);
 // Whether the chunk-output kernel for (dtype, Q, N) reads the kernel-matrix pass's

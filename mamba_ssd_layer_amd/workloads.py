@@ -75,6 +75,18 @@ WORKLOADS = {
 }
 
 
+# Decode (one recurrent step per sequence) on a Mamba-2-2.7B-like layer at a
+# serving batch: 64 sequences of one token, H=80, P=64, N=128, G=1; x, B, C
+# bf16 and the fp32 state.  The pages give no decode configuration; this one
+# moves a 168 MB state per step.
+DECODE_WORKLOADS = {
+    "decode_2p7b_b64": Workload(
+        "decode_2p7b_b64", batch=64, seqlen=1, nheads=80, headdim=64, dstate=128,
+        ngroups=1, chunk_len=256, dtype="bf16",
+        note="decode step: batch 64, H=80, P=64, N=128, G=1, bf16 x/B/C, fp32 state"),
+}
+
+
 def bf16_round(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); float32 out.
 

@@ -131,6 +131,29 @@ def test_ex_rejects_invalid_arguments(lib, kw, code):
     assert call_ex(lib, **kw) == code
 
 
+def call_decode(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, b=4, H=8, P=64, N=128, G=2, dtype=1,
+             st=FAKE, y=FAKE)
+    a.update(kw)
+    return lib.ssd_decode_step(a["x"], a["dt"], a["A"], a["B"], a["C"], a["b"], a["H"], a["P"],
+                               a["N"], a["G"], a["dtype"], a["st"], a["y"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(st=FAKE + 8), INVALID),       # misaligned state
+    (dict(st=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(x=FAKE + 2), INVALID),
+    (dict(b=-1), INVALID),
+    (dict(H=6, G=4), INVALID),
+    (dict(dtype=3), INVALID),
+    (dict(P=32), UNSUPPORTED),
+    (dict(N=100), UNSUPPORTED),
+])
+def test_decode_rejects_invalid_arguments(lib, kw, code):
+    assert call_decode(lib, **kw) == code
+
+
 def test_intermediates_rejects_uneven_batch(lib):
     assert lib.ssd_chunked_fwd_intermediates(FAKE, FAKE, FAKE, FAKE, FAKE, None, 3, 100, 4, 64, 128,
                                              1, 256, 1, FAKE, None, None, None, None, None) == INVALID

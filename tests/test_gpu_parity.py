@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from mamba_ssd_layer_amd import _binding as bd
-from mamba_ssd_layer_amd.workloads import WORKLOADS, Workload, initial_states, make_inputs
+from mamba_ssd_layer_amd.workloads import DECODE_WORKLOADS, WORKLOADS, Workload, initial_states, make_inputs
 
 from gpu_common import TOL, check_parity, log, max_rel_l2, require_gpu, run_gpu, run_oracle, to_device
 
@@ -319,3 +319,82 @@ def test_split_and_resume(dev, name, dtype, Q, T1):
     ey, ef = max_rel_l2(y, yr, f2.cpu().numpy(), fr, inp.packed_cu_seqlens())
     log(f"[split]   max rel-L2 y={ey:.3e} final_state={ef:.3e}")
     assert ey <= TOL[dtype] and ef <= TOL[dtype]
+
+
+# --------------------------------------------------------- decode step ----
+def _slice_rel_l2(got, ref):
+    """Max relative L2 over the leading (sequence, head) slices."""
+    g = got.reshape(got.shape[0] * got.shape[1], -1).astype(np.float64)
+    r = ref.reshape(ref.shape[0] * ref.shape[1], -1).astype(np.float64)
+    return float(np.max(np.linalg.norm(g - r, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+def test_decode_step_vs_oracle(dev, dtype, N):
+    """One recurrent step from a random state against the oracle's recurrence
+    over one token started from the same state."""
+    w = SMALL.with_(dtype=dtype, dstate=N, seqlen=1, batch=5, nheads=8, ngroups=2)
+    inp = make_inputs(w, 40 + N)
+    h0 = initial_states(5, 8, 64, N, seed=40 + N)
+    d = to_device(inp, dev)
+    state = torch.from_numpy(h0).to(dev)
+    log(f"[decode] {dtype} N={N} batch 5 H=8 G=2")
+    y = bd.ssd_decode_step(d["x"][:, 0].contiguous(), d["dt"][:, 0].contiguous(), d["A"],
+                           d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), state)
+    torch.cuda.synchronize()
+    yr, fr = oracle.recurrence(inp.x, inp.dt, inp.A, inp.B, inp.C, init_state=h0)
+    ey = _slice_rel_l2(y.float().cpu().numpy(), yr[:, 0])
+    es = _slice_rel_l2(state.cpu().numpy(), fr)
+    log(f"[decode]   max rel-L2 y={ey:.3e} state={es:.3e}")
+    assert ey <= TOL[dtype]
+    assert es <= 1e-5  # the state stays fp32 on both paths
+
+
+def test_decode_continues_forward(dev):
+    """A forward over tokens [0, T0) and then one decode step per token equals the
+    forward over all tokens: y of the decoded tokens and the final state."""
+    T0, K = 300, 8
+    w = SMALL.with_(dtype="bf16", dstate=128, chunk_len=128, seqlen=T0 + K, batch=3, nheads=8, ngroups=2)
+    inp = make_inputs(w, 50)
+    d = to_device(inp, dev)
+    log(f"[decode] prefill {T0} tokens, then {K} steps")
+    _, st = bd.ssd_chunked_fwd(*(d[k][:, :T0].contiguous() for k in ("x", "dt")), d["A"],
+                               *(d[k][:, :T0].contiguous() for k in ("B", "C")), 128)
+    ys = [bd.ssd_decode_step(*(d[k][:, t].contiguous() for k in ("x", "dt")), d["A"],
+                             *(d[k][:, t].contiguous() for k in ("B", "C")), st)
+          for t in range(T0, T0 + K)]
+    torch.cuda.synchronize()
+    yr, fr = run_oracle(inp)
+    yd = torch.stack(ys, dim=1).float().cpu().numpy()        # (b, K, H, P)
+    ey = _slice_rel_l2(np.moveaxis(yd, 1, 2), np.moveaxis(yr[:, T0:], 1, 2))
+    es = _slice_rel_l2(st.cpu().numpy(), fr)
+    log(f"[decode]   max rel-L2 y={ey:.3e} state={es:.3e}")
+    assert ey <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_decode_bench_shape(dev):
+    """The decode shape bench.py times (64 sequences, H=80, N=128, bf16), every output."""
+    w = DECODE_WORKLOADS["decode_2p7b_b64"]
+    inp = make_inputs(w, 0)
+    h0 = initial_states(w.batch, w.nheads, w.headdim, w.dstate, seed=0)
+    d = to_device(inp, dev)
+    state = torch.from_numpy(h0).to(dev)
+    log("[decode] bench shape")
+    y = bd.ssd_decode_step(d["x"][:, 0].contiguous(), d["dt"][:, 0].contiguous(), d["A"],
+                           d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), state)
+    torch.cuda.synchronize()
+    yr, fr = oracle.recurrence(inp.x, inp.dt, inp.A, inp.B, inp.C, init_state=h0)
+    assert _slice_rel_l2(y.float().cpu().numpy(), yr[:, 0]) <= TOL["bf16"]
+    assert _slice_rel_l2(state.cpu().numpy(), fr) <= 1e-5
+
+
+def test_decode_empty_batch(dev):
+    log("[decode] batch 0")
+    x = torch.empty((0, 4, 64), dtype=torch.bfloat16, device=dev)
+    st = torch.empty((0, 4, 64, 128), dtype=torch.float32, device=dev)
+    y = bd.ssd_decode_step(x, torch.empty((0, 4), device=dev), torch.zeros(4, device=dev),
+                           torch.empty((0, 1, 128), dtype=torch.bfloat16, device=dev),
+                           torch.empty((0, 1, 128), dtype=torch.bfloat16, device=dev), st)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
