@@ -131,6 +131,16 @@ ssd_status ssd_chunked_fwd_varlen(const void* x, const float* dt, const float* A
  *                  of an earlier call; it must not alias this call's
  *                  final_state.  An empty sequence's final state is its
  *                  initial state.
+ *   D              (nheads) fp32 DEVICE array or NULL: adds the skip term
+ *                  y_t += D_h x_t on the raw input ([M] §1.2: D passes the
+ *                  input straight to the output, a skip connection; the SSM
+ *                  proper is usually written without it).  On the bf16 path
+ *                  it is added to the rounded SSM output, then rounded again.
+ *   x_times_dt     0 or 1.  1: the input enters the state as dt_t x_t, i.e.
+ *                  B_t is scaled by the step size (the first-order
+ *                  discretisation that Mamba-2 keeps from Mamba, [M]
+ *                  "离散化" after §3.5.4): h_t = a_t h_{t-1} + dt_t x_t B_t^T.
+ *                  D still multiplies the raw x.
  * Other arguments, errors and execution as for the entry points above.
  */
 ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_head,
@@ -138,7 +148,8 @@ ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_hea
                               int64_t nseqs, int64_t total_len, int32_t nheads,
                               int32_t headdim, int32_t dstate, int32_t ngroups,
                               int32_t chunk_len, ssd_dtype dtype, const float* initial_state,
-                              void* y, float* final_state, void* stream);
+                              const float* D, int32_t x_times_dt, void* y,
+                              float* final_state, void* stream);
 
 /*
  * One recurrent step for a batch of sequences: the decode (autoregressive
@@ -159,14 +170,15 @@ ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_hea
  *          place (the forward's final_state layout)
  *   y      (batch, nheads, headdim)          element dtype, overwritten
  *          (bf16: rounded to nearest even); must not alias an input
+ *   D, x_times_dt  as for ssd_chunked_fwd_ex (skip term, input as dt x)
  * headdim 64, dstate in {16, 32, 64, 128, 256}; no workspace.  Alignment,
  * validation, execution and errors as for the forward.  batch == 0 is a
  * no-op.
  */
 ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, const void* B,
                            const void* C, int64_t batch, int32_t nheads, int32_t headdim,
-                           int32_t dstate, int32_t ngroups, ssd_dtype dtype, float* state,
-                           void* y, void* stream);
+                           int32_t dstate, int32_t ngroups, ssd_dtype dtype, const float* D,
+                           int32_t x_times_dt, float* state, void* y, void* stream);
 
 /*
  * The same pass, also copying the intermediates of the block decomposition

@@ -32,9 +32,9 @@ SIGNATURES = {
     "ssd_chunked_fwd_varlen": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _vp, _fp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_ex": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32, _i32,
-                            _i32, _i32, _fp, _vp, _fp, _vp], ctypes.c_int),
-    "ssd_decode_step": ([_vp, _fp, _fp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _fp, _vp, _vp],
-                        ctypes.c_int),
+                            _i32, _i32, _fp, _fp, _i32, _vp, _fp, _vp], ctypes.c_int),
+    "ssd_decode_step": ([_vp, _fp, _fp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _fp, _i32, _fp,
+                         _vp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_intermediates": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _vp, _fp, _fp, _fp, _fp, _vp],
                                       ctypes.c_int),
@@ -174,10 +174,13 @@ def ssd_chunked_fwd_varlen(x, dt, A_head, B, C, cu_seqlens, chunk_len: int, y=No
 
 
 def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, initial_state=None,
-                       y=None, final_state=None, return_final_state: bool = True):
-    """SSD forward from initial states.  Batched (4-D x (b,T,H,P), cu_seqlens None)
-    or packed (3-D x (Ttot,H,P) with cu_seqlens (S+1,) int32 on the device).
-    initial_state (S,H,P,N) fp32 or None (zero).  Returns (y, final_state (S,H,P,N) or None)."""
+                       D=None, x_times_dt: bool = False, y=None, final_state=None,
+                       return_final_state: bool = True):
+    """SSD forward with the options of ssd_chunked_fwd_ex.  Batched (4-D x
+    (b,T,H,P), cu_seqlens None) or packed (3-D x (Ttot,H,P) with cu_seqlens (S+1,)
+    int32 on the device).  initial_state (S,H,P,N) fp32 or None (zero); D (H,) fp32
+    or None (skip term y += D_h x); x_times_dt: the input enters as dt x.
+    Returns (y, final_state (S,H,P,N) or None)."""
     dev = x.device
     if x.dim() == 4:
         if cu_seqlens is not None:
@@ -207,6 +210,10 @@ def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, ini
         _need(initial_state, "initial_state", torch.float32, dev)
         if tuple(initial_state.shape) != (S, H, P, N):
             raise ValueError("initial_state must be (S,H,P,N)")
+    if D is not None:
+        _need(D, "D", torch.float32, dev)
+        if tuple(D.shape) != (H,):
+            raise ValueError("D must be (H,)")
     if y is None:
         y = torch.empty_like(x)
     else:
@@ -221,16 +228,17 @@ def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, ini
             raise ValueError("final_state must be (S,H,P,N)")
     rc = lib().ssd_chunked_fwd_ex(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), _ptr(cu_seqlens),
                                   S, Tt, H, P, N, G, int(chunk_len), _dtype_code(x),
-                                  _ptr(initial_state), _ptr(y), _ptr(final_state),
+                                  _ptr(initial_state), _ptr(D), 1 if x_times_dt else 0,
+                                  _ptr(y), _ptr(final_state),
                                   ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_chunked_fwd_ex")
     return y, final_state
 
 
-def ssd_decode_step(x, dt, A_head, B, C, state, y=None):
+def ssd_decode_step(x, dt, A_head, B, C, state, y=None, D=None, x_times_dt: bool = False):
     """One recurrent (decode) step.  x (b,H,P), dt (b,H) fp32, A_head (H,) fp32,
-    B/C (b,G,N) in x's dtype, state (b,H,P,N) fp32, updated in place.
-    Returns y (b,H,P) in x's dtype."""
+    B/C (b,G,N) in x's dtype, state (b,H,P,N) fp32, updated in place; D and
+    x_times_dt as for ssd_chunked_fwd_ex.  Returns y (b,H,P) in x's dtype."""
     if x.dim() != 3:
         raise ValueError("x must be (batch, nheads, headdim)")
     b, H, P = x.shape
@@ -251,8 +259,13 @@ def ssd_decode_step(x, dt, A_head, B, C, state, y=None):
         _need(y, "y", x.dtype, dev)
         if y.shape != x.shape:
             raise ValueError("y must have x's shape")
+    if D is not None:
+        _need(D, "D", torch.float32, dev)
+        if tuple(D.shape) != (H,):
+            raise ValueError("D must be (H,)")
     rc = lib().ssd_decode_step(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), b, H, P, N, G,
-                               _dtype_code(x), _ptr(state), _ptr(y), ctypes.c_void_p(_stream_ptr(dev)))
+                               _dtype_code(x), _ptr(D), 1 if x_times_dt else 0, _ptr(state), _ptr(y),
+                               ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_decode_step")
     return y
 

@@ -46,6 +46,9 @@
 //  * LDS operand reads are issued ahead of the MFMAs that use them (pinned by
 //    scheduling barriers); each finished row tile of y is passed through the
 //    wave's own LDS rows and written as whole 128-byte rows.
+//  * Options: with the input entering as dt x, every x staging scale carries
+//    dt_j (the chunk-state kernel provides Acs_j - ln dt_j); the skip term
+//    D_h x is added to each finished 16-byte piece of y before its store.
 //  * fp32 accumulation; y rounded once to the element dtype and stored with the
 //    non-temporal hint (nothing here reads it again); Hin, read here for the
 //    last time, is loaded with that hint too.
@@ -90,7 +93,9 @@ struct ChunkOutputCfg {
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
 };
 
-template <class E, int Q, int N>
+// kOpts: the skip term and the dt-scaled input are handled (a separate
+// instantiation, so that the plain forward keeps every register it had)
+template <class E, int Q, int N, bool kOpts>
 __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
   using Cfg = ChunkOutputCfg<E, Q, N>;
   using T = typename E::storage;
@@ -139,6 +144,9 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   const T* xbase = reinterpret_cast<const T*>(p.x) + cd.t0 * H * P;
   const T* hbase = reinterpret_cast<const T*>(ws.hin) + k * H * (int64_t)(P * N);
   const float* abase = ws.acs + k * H * Q;
+  // log of the divisor x is staged with: Acs, or Acs - ln dt when the input
+  // enters as dt x (then every staging scale below carries dt)
+  const float* xlbase = (kOpts && p.x_times_dt) ? ws.xlog + k * H * Q : abase;
   // kernel tiles of the chunk's group: [tile][16-byte vector q][lane]
   const uint4* gsrc = reinterpret_cast<const uint4*>(ws.cb) + (k * G + g) * (int64_t)(NTILE * GV * 64);
   T* ybase = reinterpret_cast<T*>(p.y) + cd.t0 * H * P;
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
 #pragma unroll
     for (int i = 0; i < XTile::NPT; ++i) {
       const int r0 = XTile::first_row(i);
-      const float4 a4 = *reinterpret_cast<const float4*>(abase + h * Q + r0);
+      const float4 a4 = *reinterpret_cast<const float4*>(xlbase + h * Q + r0);
       xa4[i][0] = a4.x; xa4[i][1] = a4.y; xa4[i][2] = a4.z; xa4[i][3] = a4.w;
       xae[i] = abase[h * Q + (r0 | 31)];
     }
@@ -183,6 +191,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // wait for LDS reads)
   const float dmax_v = ws.dmax[k * H + h0 + lane % HB];
   const float lam_v = ws.lam[k * H + h0 + lane % HB];  // the chunk's total log-decay, same lanes
+  const float dskip_v = (kOpts && p.D != nullptr) ? p.D[h0 + lane % HB] : 0.0f;  // skip weight D_h, same lanes
 
   // C row of this lane's token as MFMA B-operand slices over N, kept in
   // registers for all heads: straight from C (rows past the chunk end clamped;
@@ -258,6 +267,16 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       for (int i = 0; i < XTile::NPT; ++i)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf((mode == kMaskTile ? xae[i] : 0.0f) - xa4[i][rr]);
+      xt.template store<QP, 2, kBf16, false, kBf16>(XT, nullptr, sreg);
+    } else if (kOpts && p.x_times_dt) {
+      // exact mask: x staged times dt_j, read as given (|Acs_j| is large here,
+      // so Acs_j - ln dt_j would not give ln dt_j back to fp32 precision)
+      float sreg[XTile::NPT][4];
+#pragma unroll
+      for (int i = 0; i < XTile::NPT; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          sreg[i][rr] = p.dt[(cd.t0 + min(XTile::first_row(i) + rr, L - 1)) * H + h];
       xt.template store<QP, 2, kBf16, false, kBf16>(XT, nullptr, sreg);
     } else {
       xt.template store<QP, 0, kBf16, false, kBf16>(XT, nullptr);
@@ -518,7 +537,15 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       const int row = s * RPI + lane / VPR;
       const int vec = lane % VPR;
       const int i_row = I * 32 + row;
-      const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
+      uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
+      if (kOpts && p.D != nullptr) {
+        // skip connection on the raw input: y += D_h x (added to the rounded
+        // sums, then rounded once more)
+        const float dh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dskip_v), hh));
+        const uint4 xv = *reinterpret_cast<const uint4*>(
+            xbase + (int64_t)min(i_row, L - 1) * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T)));
+        val = add_scaled<E>(val, xv, dh);
+      }
       if (i_row < L)
         store_nt(reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))),
                  val);
@@ -532,7 +559,10 @@ static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
     const int HB = heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    hipLaunchKernelGGL((chunk_output_kernel<E, Q, N>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+    if (p.D != nullptr || p.x_times_dt)
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, true>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+    else
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, false>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

@@ -167,11 +167,26 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
     const float excl = incl - acc;
     const float lam = __shfl(incl, 63);
     float* gout = ws.acs + (k * H + h) * Q + lane * R;
+    if (p.x_times_dt) {
+      // the input enters as dt_l x_l: the weights carry dt_l, and the output
+      // kernel divides its staged x by exp(Acs_l - ln dt_l) instead of exp(Acs_l)
+      const float* dtp = p.dt + cd.t0 * H + h;
+      float* xl = ws.xlog + (k * H + h) * Q + lane * R;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const float a = excl + run[i];
-      gout[i] = a;
-      wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
+      for (int i = 0; i < R; ++i) {
+        const float a = excl + run[i];
+        const float dtl = dtp[(int64_t)min(lane * R + i, L - 1) * H];
+        gout[i] = a;
+        xl[i] = a - __logf(dtl);
+        wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) * dtl : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float a = excl + run[i];
+        gout[i] = a;
+        wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
+      }
     }
     if (lane == 63) ws.lam[k * H + h] = lam;
     // largest decay over a 32-token tile, Acs[32J] - Acs[32J + 31] (the output

@@ -10,7 +10,9 @@
 //     state[b,h] <- a * state[b,h] + x[b,h,:] (outer) B[b,g,:]     (P x N, fp32)
 //     y[b,h,p]   <- sum_n state[b,h,p,n] * C[b,g,n]
 // the same update as one token of the forward pass, so a state from the
-// forward's final_state continues the sequence.
+// forward's final_state continues the sequence.  Options as in the forward:
+// the input may enter as dt x (B scaled by the step size) and y may get the
+// skip term D_h x.
 //
 // Design (gfx950): pure HBM streaming of the fp32 state, read and written once
 // (8PN bytes per head).  One workgroup of 256 threads per (sequence, head);
@@ -64,12 +66,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeProblem 
   const T* xrow = reinterpret_cast<const T*>(d.x) + bh * P;
   T* yrow = reinterpret_cast<T*>(d.y) + bh * P;
 
+  const float xs = d.x_times_dt ? d.dt[bh] : 1.0f;  // the input enters as dt x
+  const float dskip = d.D != nullptr ? d.D[h] : 0.0f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int p = row0 + i * RSTEP;
-    float xp;
-    if constexpr (E::kBytes == 2) xp = bf16_to_f32(xrow[p]);
-    else xp = xrow[p];
+    float xraw;
+    if constexpr (E::kBytes == 2) xraw = bf16_to_f32(xrow[p]);
+    else xraw = xrow[p];
+    const float xp = xs * xraw;
     float4 s = v[i];
     s.x = a * s.x + xp * bv[0];
     s.y = a * s.y + xp * bv[1];
@@ -80,6 +85,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeProblem 
 #pragma unroll
     for (int off = NV / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off);
     if (n4 == 0) {
+      part += dskip * xraw;  // skip connection on the raw input
       if constexpr (E::kBytes == 2) yrow[p] = (T)(pack_bf16x2(part, 0.0f) & 0xffffu);
       else yrow[p] = part;
     }

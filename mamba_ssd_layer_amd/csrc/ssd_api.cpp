@@ -74,6 +74,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   char* acs = take(K * H * p.Q * sizeof(float));
   char* lam = take(K * H * sizeof(float));
   char* dmax = take(K * H * sizeof(float));
+  char* xlog = take(p.x_times_dt ? K * H * p.Q * sizeof(float) : 0);
   char* states = take(K * H * PN * esz);
   char* hin = take(K * H * PN * esz);
   const size_t NI = (size_t)p.Q / 32;
@@ -88,6 +89,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->acs = reinterpret_cast<float*>(acs);
     ws->lam = reinterpret_cast<float*>(lam);
     ws->dmax = reinterpret_cast<float*>(dmax);
+    ws->xlog = p.x_times_dt ? reinterpret_cast<float*>(xlog) : nullptr;
     ws->states = states;
     ws->hin = hin;
     ws->cb = cb;
@@ -191,6 +193,8 @@ static ssd_status validate(const Problem& p) {
   }
   if (p.final_state && !aligned(p.final_state, 16)) return SSD_ERR_INVALID_ARGUMENT;
   if (p.initial_state && !aligned(p.initial_state, 16)) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.D && !aligned(p.D, 4)) return SSD_ERR_INVALID_ARGUMENT;
+  if (p.x_times_dt != 0 && p.x_times_dt != 1) return SSD_ERR_INVALID_ARGUMENT;
   if (p.cu && !aligned(p.cu, 4)) return SSD_ERR_INVALID_ARGUMENT;
   // sizes must keep every index and grid inside 32/64-bit ranges
   const int64_t lim = (int64_t)1 << 40;
@@ -326,11 +330,14 @@ static Problem make_problem(const void* x, const float* dt, const float* A_head,
                             const void* C, const int32_t* cu, int64_t nseq, int64_t seqlen,
                             int64_t total, int32_t nheads, int32_t headdim, int32_t dstate,
                             int32_t ngroups, int32_t chunk_len, ssd_dtype dtype, void* y,
-                            float* final_state, const float* initial_state = nullptr) {
+                            float* final_state, const float* initial_state = nullptr,
+                            const float* D = nullptr, int32_t x_times_dt = 0) {
   Problem p;
   p.x = x; p.dt = dt; p.A = A_head; p.B = B; p.C = C; p.cu = cu; p.y = y;
   p.final_state = final_state;
   p.initial_state = initial_state;
+  p.D = D;
+  p.x_times_dt = x_times_dt;
   p.nseq = nseq; p.seqlen = seqlen; p.total = total;
   p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups; p.Q = chunk_len;
   p.dtype = static_cast<Dtype>(dtype);
@@ -378,15 +385,15 @@ ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_hea
                               const void* C, const int32_t* cu_seqlens, int64_t nseqs,
                               int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
                               int32_t ngroups, int32_t chunk_len, ssd_dtype dtype,
-                              const float* initial_state, void* y, float* final_state,
-                              void* stream) {
+                              const float* initial_state, const float* D, int32_t x_times_dt,
+                              void* y, float* final_state, void* stream) {
   if (nseqs < 0 || total_len < 0) return SSD_ERR_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr && nseqs > 0 && total_len % nseqs != 0) return SSD_ERR_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr && nseqs == 0 && total_len != 0) return SSD_ERR_INVALID_ARGUMENT;
   const int64_t seqlen = (cu_seqlens == nullptr && nseqs > 0) ? total_len / nseqs : 0;
   const Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, seqlen, total_len, nheads,
                                  headdim, dstate, ngroups, chunk_len, dtype, y, final_state,
-                                 initial_state);
+                                 initial_state, D, x_times_dt);
   return run(p, static_cast<hipStream_t>(stream), nullptr);
 }
 
@@ -412,11 +419,12 @@ ssd_status ssd_chunked_fwd_intermediates(const void* x, const float* dt, const f
 
 ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, const void* B,
                            const void* C, int64_t batch, int32_t nheads, int32_t headdim,
-                           int32_t dstate, int32_t ngroups, ssd_dtype dtype, float* state, void* y,
-                           void* stream) {
+                           int32_t dstate, int32_t ngroups, ssd_dtype dtype, const float* D,
+                           int32_t x_times_dt, float* state, void* y, void* stream) {
   if (batch < 0 || nheads <= 0 || ngroups <= 0 || nheads % ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
   if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return SSD_ERR_INVALID_ARGUMENT;
   if (headdim <= 0 || dstate <= 0) return SSD_ERR_INVALID_ARGUMENT;
+  if ((x_times_dt != 0 && x_times_dt != 1) || (D && !aligned(D, 4))) return SSD_ERR_INVALID_ARGUMENT;
   if (headdim != kHeadDim) return SSD_ERR_UNSUPPORTED;
   if (!(dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128 || dstate == 256)) return SSD_ERR_UNSUPPORTED;
   if (batch > ((int64_t)1 << 40) / nheads || batch * nheads > 0x7fffffffLL) return SSD_ERR_INVALID_ARGUMENT;
@@ -431,6 +439,7 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, 
   DecodeProblem d;
   d.x = x; d.dt = dt; d.A = A_head; d.B = B; d.C = C; d.state = state; d.y = y;
   d.batch = batch; d.H = nheads; d.P = headdim; d.N = dstate; d.G = ngroups;
+  d.D = D; d.x_times_dt = x_times_dt;
   d.dtype = static_cast<Dtype>(dtype);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   return map_err(timed_launch(kK6DecodeStep, s, [&] { return launch_decode_step(d, s); }));

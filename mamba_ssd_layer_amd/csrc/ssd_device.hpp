@@ -59,6 +59,21 @@ __device__ __forceinline__ void store_nt(uint2* p, const uint2& v) {
   __builtin_nontemporal_store((u32x2_t){v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
 }
 __device__ __forceinline__ void store_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+// y + d * x on one 16-byte vector of the element type (fp32 arithmetic; bf16
+// results rounded to nearest even).
+template <class E>
+__device__ __forceinline__ uint4 add_scaled(const uint4& y, const uint4& x, float d) {
+  if constexpr (E::kBytes == 2) {
+    auto f = [&](uint32_t yw, uint32_t xw) {
+      return pack_bf16x2(bf16_lo(yw) + d * bf16_lo(xw), bf16_hi(yw) + d * bf16_hi(xw));
+    };
+    return make_uint4(f(y.x, x.x), f(y.y, x.y), f(y.z, x.z), f(y.w, x.w));
+  } else {
+    auto f = [&](uint32_t yw, uint32_t xw) { return __float_as_uint(__uint_as_float(yw) + d * __uint_as_float(xw)); };
+    return make_uint4(f(y.x, x.x), f(y.y, x.y), f(y.z, x.z), f(y.w, x.w));
+  }
+}
+
 // Load with the non-temporal hint: for the last read of data.
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));

@@ -34,6 +34,8 @@ struct Problem {
   void* y;                // (Ttot, H, P)  element dtype
   float* final_state;     // (S, H, P, N) or nullptr
   const float* initial_state;  // (S, H, P, N): state before each sequence's first token, or nullptr (zero)
+  const float* D;         // (H): y += D_h x (skip connection), or nullptr
+  int x_times_dt;         // 1: the input enters as dt_t x_t (B scaled by the step size)
   int64_t nseq;           // S
   int64_t seqlen;         // T (batched form only)
   int64_t total;          // Ttot
@@ -54,6 +56,8 @@ struct DecodeProblem {
   const void* C;      // (batch, G, N)  element dtype
   float* state;       // (batch, H, P, N) fp32, updated in place
   void* y;            // (batch, H, P)  element dtype
+  const float* D;     // (H) skip weights or nullptr
+  int x_times_dt;     // 1: the input enters as dt x
   int64_t batch;
   int H, P, N, G;
   Dtype dtype;
@@ -68,6 +72,8 @@ struct Workspace {
   float* acs = nullptr;          // (kmax, H, Q) chunk-local cumsum of dt*A
   float* lam = nullptr;          // (kmax, H)    its last entry (log of the chunk's decay)
   float* dmax = nullptr;         // (kmax, H)    largest decay (Acs difference) over a 32-token tile
+  float* xlog = nullptr;         // (kmax, H, Q) Acs - ln dt, the log of x's staging divisor
+                                 //              (only with x_times_dt)
   void* states = nullptr;        // (kmax, H, P, N) chunk states, element dtype
   void* hin = nullptr;           // (kmax, H, P, N) state entering each chunk, element dtype
   void* cb = nullptr;            // (kmax, G, NI(NI+1)/2 tiles, 16-byte vector, 64 lanes) kernel

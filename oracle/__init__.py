@@ -86,16 +86,28 @@ def _ptr(a, ctype=ctypes.c_double):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def recurrence(x, dt, A, B, C, cu_seqlens=None, init_state=None, nthreads=0):
+def recurrence(x, dt, A, B, C, cu_seqlens=None, init_state=None, nthreads=0, D=None,
+               x_times_dt=False):
     """O1: fp64 naive recurrence ([T] §2.4, §3.1 eq. (3), §5.1; [M] §3.1.2).
 
     Packed layout: x (Ttot,H,P), dt (Ttot,H), A (H,), B and C (Ttot,G,N),
     cu_seqlens (S+1,) with cu[0]=0 and cu[S]=Ttot (None: one sequence).
     A batched input (b,T,...) may be passed; it is treated as b sequences of
     length T.  init_state (S,H,P,N) or None (zero).
+    Options of the layer around the recurrence:
+      x_times_dt  the input enters the state as dt_t x_t (B scaled by the step
+                  size: the first-order discretisation Mamba-2 keeps from
+                  Mamba, [M] "离散化" after §3.5.4; the pages print no formula,
+                  so this reading is a convention: parity unpinned by the
+                  pages, pinned by the closed form in the tests);
+      D (H,)      skip term y_t += D_h x_t on the raw input ([M] §1.2: D
+                  passes the input straight to the output).
     Returns y with x's leading shape and final_state (S,H,P,N), both fp64.
     """
     x = _f64(x)
+    x_raw = x
+    if x_times_dt:
+        x = x * _f64(dt)[..., None]
     lead = x.shape[:-2]
     H, P = x.shape[-2:]
     if x.ndim == 4:  # (b, T, H, P) batched
@@ -128,7 +140,10 @@ def recurrence(x, dt, A, B, C, cu_seqlens=None, init_state=None, nthreads=0):
         int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
-    return y.reshape(*lead, H, P), fs
+    y = y.reshape(*lead, H, P)
+    if D is not None:
+        y = y + _f64(D).reshape(H)[:, None] * x_raw.reshape(*lead, H, P)
+    return y, fs
 
 
 def quadratic(x, dt, A, B, C):

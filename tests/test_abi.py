@@ -111,15 +111,17 @@ def test_varlen_rejects_invalid_arguments(lib):
 
 def call_ex(lib, **kw):
     a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, cu=None, S=2, T=512, H=4, P=64, N=128, G=1,
-             Q=256, dtype=1, h0=FAKE, y=FAKE, fs=FAKE)
+             Q=256, dtype=1, h0=FAKE, D=None, xdt=0, y=FAKE, fs=FAKE)
     a.update(kw)
     return lib.ssd_chunked_fwd_ex(a["x"], a["dt"], a["A"], a["B"], a["C"], a["cu"], a["S"], a["T"],
-                                  a["H"], a["P"], a["N"], a["G"], a["Q"], a["dtype"], a["h0"], a["y"],
-                                  a["fs"], None)
+                                  a["H"], a["P"], a["N"], a["G"], a["Q"], a["dtype"], a["h0"], a["D"],
+                                  a["xdt"], a["y"], a["fs"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(h0=FAKE + 4), INVALID),       # misaligned initial state
+    (dict(D=FAKE + 2), INVALID),        # misaligned skip weights
+    (dict(xdt=2), INVALID),             # the input-scaling flag is 0 or 1
     (dict(S=3, T=512), INVALID),        # batched form: total_len not a multiple of nseqs
     (dict(S=0, T=10), INVALID),
     (dict(S=-1), INVALID),
@@ -133,14 +135,16 @@ def test_ex_rejects_invalid_arguments(lib, kw, code):
 
 def call_decode(lib, **kw):
     a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, b=4, H=8, P=64, N=128, G=2, dtype=1,
-             st=FAKE, y=FAKE)
+             D=None, xdt=0, st=FAKE, y=FAKE)
     a.update(kw)
     return lib.ssd_decode_step(a["x"], a["dt"], a["A"], a["B"], a["C"], a["b"], a["H"], a["P"],
-                               a["N"], a["G"], a["dtype"], a["st"], a["y"], None)
+                               a["N"], a["G"], a["dtype"], a["D"], a["xdt"], a["st"], a["y"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(st=FAKE + 8), INVALID),       # misaligned state
+    (dict(D=FAKE + 1), INVALID),
+    (dict(xdt=-1), INVALID),
     (dict(st=None), INVALID),
     (dict(y=None), INVALID),
     (dict(x=FAKE + 2), INVALID),

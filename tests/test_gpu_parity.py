@@ -182,9 +182,9 @@ def test_intermediates_match_chunked_reference(dev):
 
 # ---------------------------------------------------- head blocks / workspace ----
 @pytest.mark.parametrize("dtype,H,G,b,T,Q", [
-    ("bf16", 48, 2, 2, 8192, 256),   # 12 heads per workgroup on 256 CUs: scan groups of 8 + 4
-    ("bf16", 20, 1, 2, 12800, 256),  # 10: 8 + 2
-    ("bf16", 64, 1, 2, 16384, 256),  # 32: four full groups
+    ("bf16", 48, 2, 2, 8192, 256),   # 12 heads per workgroup on 256 CUs
+    ("bf16", 20, 1, 2, 12800, 256),  # 10
+    ("bf16", 64, 1, 2, 16384, 256),  # 32
     ("bf16", 12, 1, 2, 8192, 256),   # 3
     ("f32", 40, 1, 2, 10240, 128),   # 5
     ("bf16", 6, 2, 2, 700, 256),     # 1 (small problem: one head per workgroup)
@@ -192,8 +192,8 @@ def test_intermediates_match_chunked_reference(dev):
 def test_head_block_shapes(dev, dtype, H, G, b, T, Q):
     """Heads per workgroup is any divisor (<= 32) of the heads of a group, chosen
     for the grid's rounds on the device; these shapes give blocks of 12, 10, 32,
-    3, 5 and 1 heads on a 256-CU MI355X, with the chunk-state scan in groups of 8
-    heads (partial last groups included)."""
+    3, 5 and 1 heads on a 256-CU MI355X (the chunk-state prologue scans all of
+    a block's heads, one wave per head, several heads per wave above 8)."""
     w = SMALL.with_(dtype=dtype, nheads=H, ngroups=G, batch=b, seqlen=T, dstate=128, chunk_len=Q)
     check_parity(make_inputs(w, 11), dev, label=f"head blocks H={H} G={G} b={b} T={T} Q={Q} {dtype}")
 
@@ -398,3 +398,95 @@ def test_decode_empty_batch(dev):
                            torch.empty((0, 1, 128), dtype=torch.bfloat16, device=dev), st)
     torch.cuda.synchronize()
     assert y.numel() == 0
+
+
+# ------------------------------------------- options: skip term, dt input ----
+def _run_ex(inp, dev, Q, h0=None, D=None, xdt=False):
+    d = to_device(inp, dev)
+    kw = dict(initial_state=None if h0 is None else torch.from_numpy(h0).to(dev),
+              D=None if D is None else torch.from_numpy(D).to(dev), x_times_dt=xdt)
+    if inp.cu_seqlens is not None:
+        kw["cu_seqlens"] = d["cu"]
+    y, fs = bd.ssd_chunked_fwd_ex(d["x"], d["dt"], d["A"], d["B"], d["C"], Q, **kw)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), fs.cpu().numpy()
+
+
+def _check_ex(inp, dev, Q, tol, label, h0=None, D=None, xdt=False):
+    log(f"[options] {label}")
+    yg, fg = _run_ex(inp, dev, Q, h0, D, xdt)
+    assert np.all(np.isfinite(yg)) and np.all(np.isfinite(fg))
+    yr, fr = oracle.recurrence(inp.x, inp.dt, inp.A, inp.B, inp.C, cu_seqlens=inp.packed_cu_seqlens(),
+                               init_state=h0, D=D, x_times_dt=xdt)
+    ey, ef = max_rel_l2(yg, yr, fg, fr, inp.packed_cu_seqlens())
+    log(f"[options]   max rel-L2 y={ey:.3e} final_state={ef:.3e}")
+    assert ey <= tol and ef <= tol
+
+
+@pytest.mark.parametrize("dtype,N,Q", [("f32", 64, 128), ("bf16", 128, 256), ("bf16", 256, 64),
+                                       ("bf16", 256, 256)])
+@pytest.mark.parametrize("D_on,xdt", [(True, False), (False, True), (True, True)])
+def test_options_batched(dev, dtype, N, Q, D_on, xdt):
+    """The skip term and the dt-scaled input, alone and together, with an initial
+    state, against the oracle's recurrence with the same options (bf16 N = Q = 256
+    takes the separate kernel-matrix pass)."""
+    w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=700, batch=2, nheads=8, ngroups=2)
+    inp = make_inputs(w, 60 + N)
+    h0 = initial_states(2, 8, 64, N, seed=60 + N)
+    D = np.random.default_rng(60 + N).standard_normal(8).astype(np.float32)
+    _check_ex(inp, dev, Q, TOL[dtype], f"batched {dtype} N={N} Q={Q} D={D_on} x*dt={xdt}",
+              h0=h0, D=D if D_on else None, xdt=xdt)
+
+
+def test_options_varlen(dev):
+    lens = [300, 0, 1, 513, 64, 77]
+    w = SMALL.with_(varlen=True, batch=len(lens), dstate=128, chunk_len=128, nheads=8, ngroups=2)
+    inp = make_inputs(w, 61, seqlens=lens)
+    D = np.random.default_rng(61).standard_normal(8).astype(np.float32)
+    _check_ex(inp, dev, 128, TOL["bf16"], "varlen D and x*dt", D=D, xdt=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ell", [-0.5, -8.0])
+def test_options_tile_and_exact_masks(dev, dtype, ell):
+    """The dt-scaled input under the per-tile (chunk decay beyond e^64, tile decays
+    within it: dt*A = -0.5 per token) and the exact (dt*A = -8: even a 32-token
+    tile decays past e^64) mask factorisations of the output kernel.
+
+    Far outside the workloads' decay range the fp32 bar follows from the
+    arithmetic: the mask exp(Acs_i - Acs_j) comes from fp32 chunk-local cumsums
+    of magnitude up to M = max |Acs|, so each difference carries an absolute
+    error of a few M 2^-24 (M = 1340 at dt*A = -8: 3e-4); the bar is the larger
+    of the stated tolerance and 4 M 2^-24."""
+    from mamba_ssd_layer_amd.workloads import Inputs
+    Q = 256 if dtype == "bf16" else 128
+    w = SMALL.with_(dtype=dtype, dstate=64, chunk_len=Q, seqlen=600, batch=2, nheads=4, ngroups=1)
+    inp = make_inputs(w, 62)
+    A = -np.full_like(inp.A, 4.0)
+    dt = (inp.dt / inp.dt.mean() * (-ell / 4.0)).astype(np.float32)  # mean dt*A = ell
+    z = Inputs(w, inp.x, dt, A, inp.B, inp.C)
+    ell_t = (dt.astype(np.float64) * A.astype(np.float64)).reshape(2, 600, 4)
+    M = max(np.abs(np.cumsum(ell_t[b, c0:c0 + Q], axis=0)).max() for b in range(2) for c0 in range(0, 600, Q))
+    tol = max(TOL[dtype], 4.0 * M * 2.0 ** -24)
+    D = np.linspace(-1.0, 1.0, 4).astype(np.float32)
+    _check_ex(z, dev, Q, tol, f"{dtype} dt*A~{ell} D and x*dt (max |Acs| {M:.0f}, bar {tol:.1e})", D=D, xdt=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_options(dev, dtype):
+    """Decode step with the skip term and the dt-scaled input against the oracle
+    over one token from the same state."""
+    w = SMALL.with_(dtype=dtype, dstate=128, seqlen=1, batch=6, nheads=8, ngroups=2)
+    inp = make_inputs(w, 63)
+    h0 = initial_states(6, 8, 64, 128, seed=63)
+    D = np.random.default_rng(63).standard_normal(8).astype(np.float32)
+    d = to_device(inp, dev)
+    state = torch.from_numpy(h0).to(dev)
+    log(f"[decode] options {dtype}")
+    y = bd.ssd_decode_step(d["x"][:, 0].contiguous(), d["dt"][:, 0].contiguous(), d["A"],
+                           d["B"][:, 0].contiguous(), d["C"][:, 0].contiguous(), state,
+                           D=torch.from_numpy(D).to(dev), x_times_dt=True)
+    torch.cuda.synchronize()
+    yr, fr = oracle.recurrence(inp.x, inp.dt, inp.A, inp.B, inp.C, init_state=h0, D=D, x_times_dt=True)
+    assert _slice_rel_l2(y.float().cpu().numpy(), yr[:, 0]) <= TOL[dtype]
+    assert _slice_rel_l2(state.cpu().numpy(), fr) <= 1e-5

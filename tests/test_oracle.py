@@ -191,6 +191,37 @@ def test_split_and_resume():
     assert relerr(fb, f) < 1e-13
 
 
+def test_skip_term_alone():
+    """D passes the input straight to the output ([M] §1.2): with B = 0 no input
+    reaches the state, so y = D_h x exactly, on the raw x also when the input
+    enters the state as dt x."""
+    rng = np.random.default_rng(12)
+    x, dt, A, B, C = rand_case(rng, 40, 3, 4, 5, 1)
+    B = np.zeros_like(B)
+    Dh = rng.standard_normal(3)
+    for xdt in (False, True):
+        y, f = oracle.recurrence(x, dt, A, B, C, D=Dh, x_times_dt=xdt)
+        np.testing.assert_array_equal(y, Dh[None, :, None] * x)
+        assert np.all(f == 0)
+
+
+def test_x_times_dt_is_weighted_prefix_sum():
+    """With the input entering as dt x, a == 1 (A = 0) and B = C = e_1:
+    y_t = sum_{s<=t} dt_s x_s (a weighted prefix sum), and the final state's
+    (p, 0) entries are its last row."""
+    rng = np.random.default_rng(13)
+    T, H, P, N = 45, 2, 3, 4
+    x = rng.standard_normal((T, H, P))
+    dt = rng.uniform(0.01, 2.0, size=(T, H))
+    B = np.zeros((T, 1, N)); B[:, 0, 0] = 1.0
+    C = B.copy()
+    y, f = oracle.recurrence(x, dt, np.zeros(H), B, C, x_times_dt=True)
+    ref = np.cumsum(dt[:, :, None] * x, axis=0)
+    assert relerr(y, ref) < 1e-13
+    assert relerr(f[0, :, :, 0], ref[-1]) < 1e-13
+    assert np.all(f[0, :, :, 1:] == 0)
+
+
 def test_varlen_equals_separate_runs():
     """Packed sequences with cu_seqlens restart from a zero state ([M] §3.7.3)
     and equal independent runs, bit for bit; an empty sequence has a zero
