@@ -12,10 +12,13 @@ Pages cited (titles as published):
   [M] "LLM(十一)——Mamba" (mztchaoqun.com.cn/posts/D49_Mamba).
   [S] "Mamba-2 状态空间对偶性理论" (metaphor-xennon.pages.dev).
 
-Three forms of the same map, all fp64:
+The map, its forms and its gradients, all fp64:
   recurrence()     O1, the oracle of record: the plain recurrence of [T] §2.4 /
                    §5.1 and [M] §3.1.2, in C (ssd_oracle.c) with OpenMP over
                    (sequence, head).
+  backward()       O4, the gradients of O1 (the adjoint recurrence, in C):
+                   the training direction the pages price but do not derive
+                   ([M] §3.5.3 cost table; pinned by finite differences).
   quadratic()      O2, the dual form Y = (L o C B^T) X of [T] §2.4 and [M]
                    §3.1.3 with L the 1-semiseparable matrix of [T] §3.2.2, by
                    brute force; tiny inputs only.
@@ -67,6 +70,11 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, dp, dp, dp,
             ctypes.c_int]
         lib.ssd_oracle_recurrence.restype = ctypes.c_int
+        lib.ssd_oracle_backward.argtypes = [
+            dp, dp, dp, dp, dp, i64p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp,
+            dp, dp, dp, dp, ctypes.c_int]
+        lib.ssd_oracle_backward.restype = ctypes.c_int
         lib.ssd_oracle_max_threads.argtypes = []
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -144,6 +152,67 @@ def recurrence(x, dt, A, B, C, cu_seqlens=None, init_state=None, nthreads=0, D=N
     if D is not None:
         y = y + _f64(D).reshape(H)[:, None] * x_raw.reshape(*lead, H, P)
     return y, fs
+
+
+def backward(x, dt, A, B, C, dy, cu_seqlens=None, init_state=None, dfinal=None, D=None,
+             x_times_dt=False, nthreads=0):
+    """O4: fp64 backward of O1 with its options: the gradients of a loss L with
+    dL/dy = dy and dL/d(final state) = dfinal (None: 0), by the adjoint
+    recurrence of ssd_oracle.c (the chain rule through h_t = a_t h_{t-1} +
+    x_t B_t^T, y_t = h_t C_t in reverse token order).  With x_times_dt the
+    recurrence sees x' = dt x, so dx = dt dx' and d(dt) gains x . dx'; with D,
+    y += D x adds D dy to dx and gives dD = sum_t x_t . dy_t.
+    Layouts as recurrence().  Returns a dict of fp64 arrays: dx (x's shape),
+    ddt (dt's shape), dA (H,), dB and dC (B's shape, summed over each group's
+    heads), dD (H,) or None, dinit (S,H,P,N).
+    """
+    x = _f64(x)
+    lead = x.shape[:-2]
+    H, P = x.shape[-2:]
+    if x.ndim == 4 and cu_seqlens is None:
+        b, T = x.shape[:2]
+        cu_seqlens = np.arange(b + 1, dtype=np.int64) * T
+    Ttot = int(np.prod(lead))
+    x = x.reshape(Ttot, H, P)
+    dtv = _f64(dt).reshape(Ttot, H)
+    A = _f64(A).reshape(H)
+    N = B.shape[-1]
+    G = B.shape[-2]
+    Bv = _f64(B).reshape(Ttot, G, N)
+    Cv = _f64(C).reshape(Ttot, G, N)
+    dyv = _f64(dy).reshape(Ttot, H, P)
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, Ttot], dtype=np.int64)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    S = cu.shape[0] - 1
+    xin = x * dtv[:, :, None] if x_times_dt else x
+    init = None if init_state is None else _f64(init_state).reshape(S, H, P, N)
+    dfin = None if dfinal is None else _f64(dfinal).reshape(S, H, P, N)
+    dxp = np.empty((Ttot, H, P))
+    ddt = np.empty((Ttot, H))
+    dA = np.empty((S, H))
+    dBh = np.empty((Ttot, H, N))
+    dCh = np.empty((Ttot, H, N))
+    dinit = np.empty((S, H, P, N))
+    rc = _load().ssd_oracle_backward(
+        _ptr(xin), _ptr(dtv), _ptr(A), _ptr(Bv), _ptr(Cv), _ptr(cu, ctypes.c_int64), S, H, P, N, G,
+        _ptr(init) if init is not None else None, _ptr(dyv), _ptr(dfin) if dfin is not None else None,
+        _ptr(dxp), _ptr(ddt), _ptr(dA), _ptr(dBh), _ptr(dCh), _ptr(dinit), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    dx = dxp
+    if x_times_dt:
+        ddt = ddt + np.einsum("thp,thp->th", x, dxp)
+        dx = dxp * dtv[:, :, None]
+    dD = None
+    if D is not None:
+        dx = dx + _f64(D).reshape(H)[None, :, None] * dyv
+        dD = np.einsum("thp,thp->h", x, dyv)
+    hpg = H // G
+    dB = dBh.reshape(Ttot, G, hpg, N).sum(axis=2)
+    dC = dCh.reshape(Ttot, G, hpg, N).sum(axis=2)
+    return dict(dx=dx.reshape(*lead, H, P), ddt=ddt.reshape(np.shape(dt)), dA=dA.sum(axis=0),
+                dB=dB.reshape(np.shape(B)), dC=dC.reshape(np.shape(C)), dD=dD, dinit=dinit)
 
 
 def quadratic(x, dt, A, B, C):

@@ -122,3 +122,153 @@ int ssd_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Backward pass of the recurrence above (the chain rule taken through it in
+ * reverse token order, i.e. the adjoint recurrence), for a loss whose
+ * gradients dy = dL/dy and dfinal = dL/dh_last are given:
+ *     G_t  = dy_t (outer) C_t + a_{t+1} G_{t+1}     (G = dL/dh_t, (P, N);
+ *                                                   G past the last token = dfinal)
+ *     dx_t = G_t . B_t            (sum over n)
+ *     dB_t += G_t^T x_t           (sum over p; per head here, the caller sums a group)
+ *     dC_t += h_t^T dy_t          (sum over p; per head)
+ *     da_t = <G_t, h_{t-1}>,  d(dt_t) = A_h a_t da_t,  dA_h += dt_t a_t da_t
+ *     dL/d(initial state) = a_first G_first
+ * The states h_t are recomputed from checkpoints kept every kCk tokens (no
+ * division by a_t, which may be 0).
+ * Layouts as for the forward; dy (Ttot, H, P); dfinal and dinit (S, H, P, N)
+ * or NULL; outputs dx (Ttot, H, P), ddt (Ttot, H), dA (S, H) per sequence,
+ * dB and dC (Ttot, H, N) per head.  Returns 0, or -1 on bad arguments or
+ * memory exhaustion.
+ */
+#define kCk 64
+int ssd_oracle_backward(const double *x, const double *dt, const double *A,
+                        const double *B, const double *C,
+                        const int64_t *cu_seqlens, int64_t nseq,
+                        int64_t H, int64_t P, int64_t N, int64_t G,
+                        const double *init_state, const double *dy,
+                        const double *dfinal, double *dx, double *ddt,
+                        double *dA, double *dB, double *dC, double *dinit,
+                        int nthreads)
+{
+    if (nseq < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0)
+        return -1;
+    if (nseq > 0 && cu_seqlens[0] != 0)
+        return -1;
+    int64_t maxlen = 0;
+    for (int64_t s = 0; s < nseq; ++s) {
+        if (cu_seqlens[s + 1] < cu_seqlens[s])
+            return -1;
+        if (cu_seqlens[s + 1] - cu_seqlens[s] > maxlen)
+            maxlen = cu_seqlens[s + 1] - cu_seqlens[s];
+    }
+    const int64_t heads_per_group = H / G;
+    const int64_t npairs = nseq * H;
+    const int64_t PN = P * N;
+    const int64_t nck_max = (maxlen + kCk - 1) / kCk + 1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *ck = (double *)malloc(sizeof(double) * (size_t)(nck_max * PN));
+        double *seg = (double *)malloc(sizeof(double) * (size_t)(kCk * PN));
+        double *g = (double *)malloc(sizeof(double) * (size_t)PN);
+        double *h = (double *)malloc(sizeof(double) * (size_t)PN);
+        if (!ck || !seg || !g || !h) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t pair = 0; pair < npairs; ++pair) {
+            if (!ck || !seg || !g || !h)
+                continue;
+            const int64_t s = pair / H;
+            const int64_t hd = pair % H;
+            const int64_t gr = hd / heads_per_group;
+            const int64_t t0 = cu_seqlens[s], L = cu_seqlens[s + 1] - t0;
+            const int64_t nck = (L + kCk - 1) / kCk;
+            /* forward: the state entering tokens t0, t0 + kCk, ... */
+            if (init_state != NULL)
+                memcpy(h, init_state + (s * H + hd) * PN, sizeof(double) * (size_t)PN);
+            else
+                memset(h, 0, sizeof(double) * (size_t)PN);
+            for (int64_t i = 0; i < L; ++i) {
+                const int64_t t = t0 + i;
+                if (i % kCk == 0)
+                    memcpy(ck + (i / kCk) * PN, h, sizeof(double) * (size_t)PN);
+                const double a = exp(dt[t * H + hd] * A[hd]);
+                for (int64_t p = 0; p < P; ++p)
+                    for (int64_t n = 0; n < N; ++n)
+                        h[p * N + n] = a * h[p * N + n] + x[(t * H + hd) * P + p] * B[(t * G + gr) * N + n];
+            }
+            /* backward, one checkpoint segment at a time */
+            if (dfinal != NULL)
+                memcpy(g, dfinal + (s * H + hd) * PN, sizeof(double) * (size_t)PN);
+            else
+                memset(g, 0, sizeof(double) * (size_t)PN);
+            double dA_acc = 0.0;
+            for (int64_t c = nck - 1; c >= 0; --c) {
+                const int64_t i0 = c * kCk;
+                const int64_t i1 = (i0 + kCk < L) ? i0 + kCk : L;
+                /* states after each token of the segment */
+                const double *prev = ck + c * PN;
+                for (int64_t i = i0; i < i1; ++i) {
+                    const int64_t t = t0 + i;
+                    const double a = exp(dt[t * H + hd] * A[hd]);
+                    double *cur = seg + (i - i0) * PN;
+                    for (int64_t p = 0; p < P; ++p)
+                        for (int64_t n = 0; n < N; ++n)
+                            cur[p * N + n] = a * prev[p * N + n] + x[(t * H + hd) * P + p] * B[(t * G + gr) * N + n];
+                    prev = cur;
+                }
+                for (int64_t i = i1 - 1; i >= i0; --i) {
+                    const int64_t t = t0 + i;
+                    const double a = exp(dt[t * H + hd] * A[hd]);
+                    const double *ht = seg + (i - i0) * PN;
+                    const double *hprev = (i > i0) ? seg + (i - 1 - i0) * PN : ck + c * PN;
+                    const double *xt = x + (t * H + hd) * P;
+                    const double *dyt = dy + (t * H + hd) * P;
+                    const double *Bt = B + (t * G + gr) * N;
+                    const double *Ct = C + (t * G + gr) * N;
+                    double *dBt = dB + (t * H + hd) * N;
+                    double *dCt = dC + (t * H + hd) * N;
+                    for (int64_t n = 0; n < N; ++n) {
+                        dBt[n] = 0.0;
+                        dCt[n] = 0.0;
+                    }
+                    double da = 0.0;
+                    for (int64_t p = 0; p < P; ++p) {
+                        double dxp = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            const double gv = g[p * N + n] + dyt[p] * Ct[n];
+                            g[p * N + n] = gv;
+                            dxp += gv * Bt[n];
+                            dBt[n] += gv * xt[p];
+                            dCt[n] += ht[p * N + n] * dyt[p];
+                            da += gv * hprev[p * N + n];
+                        }
+                        dx[(t * H + hd) * P + p] = dxp;
+                    }
+                    const double dl = a * da;
+                    ddt[t * H + hd] = A[hd] * dl;
+                    dA_acc += dt[t * H + hd] * dl;
+                    for (int64_t e = 0; e < PN; ++e)
+                        g[e] *= a;
+                }
+            }
+            dA[s * H + hd] = dA_acc;
+            if (dinit != NULL)
+                memcpy(dinit + (s * H + hd) * PN, g, sizeof(double) * (size_t)PN);
+        }
+        free(ck);
+        free(seg);
+        free(g);
+        free(h);
+    }
+    return failed ? -1 : 0;
+}

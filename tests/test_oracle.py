@@ -307,3 +307,70 @@ def test_rel_l2_metric():
     got[:, 1, :] *= 1.01
     e = oracle.rel_l2_per_slice(got, ref, slice_axes=(1,))
     np.testing.assert_allclose(e, [0.0, 0.01, 0.0], atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# O4 (backward) against finite differences of O1 and closed forms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("D_on,xdt", [(False, False), (True, False), (False, True), (True, True)])
+def test_backward_matches_finite_differences(D_on, xdt):
+    """Every gradient of L = sum(dy . y) + sum(dfinal . h_last) against central
+    differences of the forward recurrence (two packed sequences, two groups, an
+    initial state): an independent check of the adjoint recurrence."""
+    rng = np.random.default_rng(21 + 2 * D_on + xdt)
+    T, H, P, N, G = 12, 4, 3, 2, 2
+    x, dt, A, B, C = rand_case(rng, T, H, P, N, G, dt_lo=0.05, dt_hi=0.8)
+    cu = np.array([0, 7, 12])
+    h0 = rng.standard_normal((2, H, P, N))
+    dy = rng.standard_normal((T, H, P))
+    dfin = rng.standard_normal((2, H, P, N))
+    D = rng.standard_normal(H) if D_on else None
+
+    def loss(x_, dt_, A_, B_, C_, h0_, D_):
+        y, f = oracle.recurrence(x_, dt_, A_, B_, C_, cu_seqlens=cu, init_state=h0_, D=D_, x_times_dt=xdt)
+        return float(np.sum(dy * y) + np.sum(dfin * f))
+
+    g = oracle.backward(x, dt, A, B, C, dy, cu_seqlens=cu, init_state=h0, dfinal=dfin, D=D, x_times_dt=xdt)
+    args = [x, dt, A, B, C, h0, D]
+    names = ["dx", "ddt", "dA", "dB", "dC", "dinit", "dD"]
+    eps = 1e-6
+    for k, name in enumerate(names):
+        if args[k] is None:
+            continue
+        fd = np.zeros_like(args[k])
+        for idx in np.ndindex(args[k].shape):
+            up = [a.copy() if a is not None else None for a in args]
+            dn = [a.copy() if a is not None else None for a in args]
+            up[k][idx] += eps
+            dn[k][idx] -= eps
+            fd[idx] = (loss(*up) - loss(*dn)) / (2 * eps)
+        np.testing.assert_allclose(g[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_a_one_prefix_sum():
+    """a == 1 and B = C = e_1: y = cumsum(x), so dx is the reverse cumulative sum
+    of dy, exactly; the first-token decay of a sequence gets no gradient."""
+    rng = np.random.default_rng(22)
+    T, H, P, N = 30, 2, 3, 4
+    x = rng.integers(-4, 5, size=(T, H, P)).astype(np.float64)
+    dy = rng.integers(-4, 5, size=(T, H, P)).astype(np.float64)
+    B = np.zeros((T, 1, N)); B[:, 0, 0] = 1.0
+    g = oracle.backward(x, np.ones((T, H)), np.zeros(H), B, B.copy(), dy)
+    np.testing.assert_array_equal(g["dx"], np.cumsum(dy[::-1], axis=0)[::-1])
+    assert np.all(g["ddt"][0] == 0)
+
+
+def test_backward_a_zero_is_diagonal():
+    """a == 0 (dt A = -1e4): y_t = (C_t . B_t) x_t, so dx_t = (C_t . B_t) dy_t,
+    dC_t = sum_h (dy_t . x_t) B_t, dB_t = sum_h (dy_t . x_t) C_t, d(dt) = 0."""
+    rng = np.random.default_rng(23)
+    T, H, P, N = 20, 3, 4, 5
+    x, _, _, B, C = rand_case(rng, T, H, P, N, 1)
+    dy = rng.standard_normal((T, H, P))
+    g = oracle.backward(x, np.full((T, H), 1e4), -np.ones(H), B, C, dy)
+    cb = np.einsum("tgn,tgn->t", B, C)
+    s = np.einsum("thp,thp->t", dy, x)
+    assert relerr(g["dx"], cb[:, None, None] * dy) < 1e-14
+    assert relerr(g["dC"], s[:, None, None] * B) < 1e-14
+    assert relerr(g["dB"], s[:, None, None] * C) < 1e-14
+    assert np.all(g["ddt"] == 0)
