@@ -12,7 +12,8 @@ The fp64 CPU oracle is timed on the host cores on the same workload (rank 0)
 and its output also checks the GPU result.  The line also carries, under
 "decode", one recurrent decode step (ssd_decode_step) on 64 sequences of a
 Mamba-2-2.7B-like layer (H=80, N=128), with its own HBM roofline
-(--no-decode skips it).
+(--no-decode skips it), and under "backward" the gradient pass
+(ssd_chunked_bwd) on the same workload (--no-backward skips it).
 
 Prints ONE JSON line.
 """
@@ -138,6 +139,42 @@ def bench_decode(bd, torch, steps, warmup):
     }
 
 
+def bench_backward(bd, torch, w, x, dt, A, B, C, cu, steps, warmup):
+    """The backward pass (ssd_chunked_bwd) on the forward's workload and inputs,
+    with a seeded dy, timed like the forward.  Its roofline counts only the
+    compulsory bytes (x, dt, B, C, dy read; dx, d(dt), dB, dC written once):
+    the implementation moves several times more (a recompute and three more
+    forward-kernel passes on rearranged copies)."""
+    import numpy as np
+    from mamba_ssd_layer_amd.workloads import bf16_round
+    rng = np.random.default_rng(12345)
+    dy_np = rng.standard_normal(tuple(x.shape)).astype(np.float32)
+    if w.dtype == "bf16":
+        dy_np = bf16_round(dy_np)
+    dy = torch.from_numpy(dy_np).to(x.device).to(x.dtype)
+
+    def step():
+        return bd.ssd_chunked_bwd(x, dt, A, B, C, dy, w.chunk_len, cu_seqlens=cu)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    e = 2 if w.dtype == "bf16" else 4
+    T = int(x.numel() // (w.nheads * w.headdim))
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    byts = 2 * (T * H * P * e + T * H * 4 + 2 * T * G * N * e) + T * H * P * e
+    ach = byts / sec / 1e9
+    return {"workload": w.name, "us_per_step": sec * 1e6, "tokens_per_s": T / sec,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": ach / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": byts,
+                         "note": "compulsory bytes over the whole backward call (several launches)"}}
+
+
 def min_io_bytes(w, total_tokens, nseq):
     e = 2 if w.dtype == "bf16" else 4
     H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
@@ -168,6 +205,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="long_T16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement reported under \"backward\"")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step measurement reported under \"decode\"")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -305,6 +344,9 @@ def main():
 
     if not args.no_decode:
         result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200))
+    if not args.no_backward:
+        result["backward"] = bench_backward(bd, torch, w, x, dt, A, B, C, cu, min(args.steps, 50),
+                                            min(args.warmup, 20))
 
     if not args.no_cpu_baseline:
         import oracle

@@ -152,6 +152,44 @@ ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_hea
                               float* final_state, void* stream);
 
 /*
+ * Backward pass of ssd_chunked_fwd_ex: the gradients of a loss L given
+ * dy = dL/dy and, optionally, dfinal = dL/d(final state).  The gradients of
+ * the recurrence (chain rule in reverse token order; pages: the training
+ * direction [M] §3.5.3 prices, the same block decomposition of [M] §3.5):
+ *     G_t  = dy_t C_t^T + a_{t+1} G_{t+1}    (dL/dh_t; dfinal past the end)
+ *     dx_t = (dt_t if x_times_dt) G_t B_t + D_h dy_t
+ *     dB_t = sum over the group's heads of G_t^T x'_t,  dC_t = ... of h_t^T dy_t
+ *     d(dt_t), dA_h through a_t = exp(dt_t A_h) (and dt_t x_t with x_times_dt)
+ *     dD_h = sum_t x_t . dy_t,  d(initial state) = a_first G_first
+ * where x' is the input as the state sees it (dt x with x_times_dt).
+ * Inputs as for ssd_chunked_fwd_ex (initial_state, D nullable; x_times_dt 0/1).
+ *   dy               (total_len, nheads, headdim) element dtype
+ *   dfinal_state     (nseqs, nheads, headdim, dstate) fp32 or NULL (zero)
+ * Outputs (caller-owned, overwritten):
+ *   dx               like x            dB, dC   like B, C (element dtype)
+ *   ddt              like dt (fp32)    dA       (nheads) fp32, required
+ *   dD               (nheads) fp32 or NULL (skip)
+ *   dinitial_state   (nseqs, nheads, headdim, dstate) fp32 or NULL (skip)
+ * dA and dD are sums over all tokens formed with atomic additions: their last
+ * bits may differ between runs.  Implementation: a forward recompute and three
+ * more passes of the forward kernels on rearranged inputs (time-reversed
+ * with the decays shifted by one token for dx and dB; the roles of x and B
+ * exchanged for dB and dC), plus streaming glue kernels; it needs a second
+ * per-stream workspace of about 12 x-sized arrays.  headdim 64; every
+ * (dtype, dstate, chunk_len) the forward supports, provided (dtype, 64, Q) is
+ * built for some Q.  Alignment, validation, execution and errors as for the
+ * forward.
+ */
+ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, const void* B,
+                           const void* C, const int32_t* cu_seqlens, int64_t nseqs,
+                           int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
+                           int32_t ngroups, int32_t chunk_len, ssd_dtype dtype,
+                           const float* initial_state, const float* D, int32_t x_times_dt,
+                           const void* dy, const float* dfinal_state, void* dx, float* ddt,
+                           float* dA, void* dB, void* dC, float* dD, float* dinitial_state,
+                           void* stream);
+
+/*
  * One recurrent step for a batch of sequences: the decode (autoregressive
  * inference) mode ([T] §2.1: inference runs the recurrent form one input step
  * at a time with a constant-size state; [M] §3.5.3 cost table: N^2 FLOPs per
@@ -224,8 +262,9 @@ const char* ssd_status_string(ssd_status status);
  * states, 2 state passing, 3 chunk output (kernel-matrix tiles, diagonal
  * blocks, state-to-output), 4 separate kernel-matrix pass (only the
  * configurations whose chunk-output kernel cannot hold the tiles in LDS:
- * fp32, and bf16 with dstate 256 at chunk_len 256), 5 decode step.  Ids
- * 0..5; another id is SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
+ * fp32, and bf16 with dstate 256 at chunk_len 256), 5 decode step, 6 the
+ * backward pass's glue kernels (its forward-kernel passes count under 1-4).
+ * Ids 0..6; another id is SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
  * Not re-entrant with concurrent forward calls.
  */
 ssd_status ssd_kernel_timing_enable(int32_t enable);

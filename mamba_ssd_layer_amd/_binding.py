@@ -33,6 +33,9 @@ SIGNATURES = {
                                 _i32, _i32, _i32, _vp, _fp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_ex": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32, _i32,
                             _i32, _i32, _fp, _fp, _i32, _vp, _fp, _vp], ctypes.c_int),
+    "ssd_chunked_bwd": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                         _i32, _fp, _fp, _i32, _vp, _fp, _vp, _fp, _fp, _vp, _vp, _fp, _fp, _vp],
+                        ctypes.c_int),
     "ssd_decode_step": ([_vp, _fp, _fp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _fp, _i32, _fp,
                          _vp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_intermediates": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32,
@@ -46,7 +49,8 @@ SIGNATURES = {
                                 ctypes.POINTER(ctypes.c_int64), _i32], ctypes.c_int),
 }
 
-KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb", "decode_step"]
+KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb", "decode_step",
+                "backward_glue"]
 
 
 class SSDError(RuntimeError):
@@ -233,6 +237,49 @@ def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, ini
                                   ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_chunked_fwd_ex")
     return y, final_state
+
+
+def ssd_chunked_bwd(x, dt, A_head, B, C, dy, chunk_len: int, cu_seqlens=None, initial_state=None,
+                    D=None, x_times_dt: bool = False, dfinal_state=None, want_dD: bool = False,
+                    want_dinitial: bool = False):
+    """Gradients of the SSD forward (ssd_chunked_fwd_ex's arguments) given dy (x's
+    shape and dtype) and optionally dfinal_state (S,H,P,N) fp32.  Returns a dict
+    dx, ddt, dA, dB, dC, and dD / dinitial_state when asked for (None otherwise)."""
+    dev = x.device
+    if x.dim() == 4:
+        b, T, H, P = x.shape
+        S, Tt = b, b * T
+    elif x.dim() == 3:
+        if cu_seqlens is None:
+            raise ValueError("packed 3-D inputs need cu_seqlens")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        Tt, H, P = x.shape
+        S = cu_seqlens.shape[0] - 1
+    else:
+        raise ValueError("x must be (b,T,H,P) or (Ttot,H,P)")
+    G, N = B.shape[-2:]
+    for t, name, dtp in ((x, "x", x.dtype), (dt, "dt", torch.float32), (A_head, "A_head", torch.float32),
+                         (B, "B", x.dtype), (C, "C", x.dtype), (dy, "dy", x.dtype)):
+        _need(t, name, dtp, dev)
+    if dy.shape != x.shape or B.shape != C.shape or tuple(A_head.shape) != (H,):
+        raise ValueError("inconsistent shapes")
+    for t, name, shp in ((initial_state, "initial_state", (S, H, P, N)), (dfinal_state, "dfinal_state", (S, H, P, N)),
+                         (D, "D", (H,))):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} must be {shp}")
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dA=torch.empty((H,), dtype=torch.float32, device=dev),
+               dB=torch.empty_like(B), dC=torch.empty_like(C),
+               dD=torch.empty((H,), dtype=torch.float32, device=dev) if want_dD else None,
+               dinitial_state=torch.empty((S, H, P, N), dtype=torch.float32, device=dev) if want_dinitial else None)
+    rc = lib().ssd_chunked_bwd(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), _ptr(cu_seqlens), S, Tt, H, P,
+                               N, G, int(chunk_len), _dtype_code(x), _ptr(initial_state), _ptr(D),
+                               1 if x_times_dt else 0, _ptr(dy), _ptr(dfinal_state), _ptr(out["dx"]),
+                               _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                               _ptr(out["dD"]), _ptr(out["dinitial_state"]), ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_chunked_bwd")
+    return out
 
 
 def ssd_decode_step(x, dt, A_head, B, C, state, y=None, D=None, x_times_dt: bool = False):

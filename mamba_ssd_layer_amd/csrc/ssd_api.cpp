@@ -231,6 +231,7 @@ namespace {
 struct WsEntry {
   int device;
   hipStream_t stream;
+  int slot;  // 0: forward workspace, 1: backward temporaries
   void* ptr;
   size_t bytes;
 };
@@ -238,10 +239,10 @@ std::mutex g_ws_mu;
 std::vector<WsEntry> g_ws;
 
 // Workspace of >= bytes for (device, stream), or nullptr on allocation failure.
-void* ws_acquire(int device, size_t bytes, hipStream_t stream) {
+void* ws_acquire(int device, size_t bytes, hipStream_t stream, int slot = 0) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   for (WsEntry& w : g_ws) {
-    if (w.device != device || w.stream != stream) continue;
+    if (w.device != device || w.stream != stream || w.slot != slot) continue;
     if (w.bytes >= bytes) return w.ptr;
     // grow in stream order: the previous calls on this stream finish first
     if (hipFreeAsync(w.ptr, stream) != hipSuccess) return nullptr;
@@ -256,7 +257,7 @@ void* ws_acquire(int device, size_t bytes, hipStream_t stream) {
   }
   void* ptr = nullptr;
   if (hipMallocAsync(&ptr, bytes > 0 ? bytes : 256, stream) != hipSuccess || ptr == nullptr) return nullptr;
-  g_ws.push_back({device, stream, ptr, bytes});
+  g_ws.push_back({device, stream, slot, ptr, bytes});
   return ptr;
 }
 }  // namespace
@@ -443,6 +444,138 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, 
   d.dtype = static_cast<Dtype>(dtype);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   return map_err(timed_launch(kK6DecodeStep, s, [&] { return launch_decode_step(d, s); }));
+}
+
+ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, const void* B,
+                           const void* C, const int32_t* cu_seqlens, int64_t nseqs,
+                           int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
+                           int32_t ngroups, int32_t chunk_len, ssd_dtype dtype,
+                           const float* initial_state, const float* D, int32_t x_times_dt,
+                           const void* dy, const float* dfinal_state, void* dx, float* ddt,
+                           float* dA, void* dB, void* dC, float* dD, float* dinitial_state,
+                           void* stream) {
+  if (nseqs < 0 || total_len < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs > 0 && total_len % nseqs != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs == 0 && total_len != 0) return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t seqlen = (cu_seqlens == nullptr && nseqs > 0) ? total_len / nseqs : 0;
+  // the forward problem, with dx standing in for y (same shape and dtype)
+  Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, seqlen, total_len, nheads, headdim,
+                           dstate, ngroups, chunk_len, dtype, dx, nullptr, initial_state, D, x_times_dt);
+  ssd_status st = validate(p);
+  if (st != SSD_OK) return st;
+  if (dA == nullptr || !aligned(dA, 4) || (dD && !aligned(dD, 4))) return SSD_ERR_INVALID_ARGUMENT;
+  if ((dfinal_state && !aligned(dfinal_state, 16)) || (dinitial_state && !aligned(dinitial_state, 16)))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (total_len > 0) {
+    if (!dy || !ddt || !dB || !dC) return SSD_ERR_INVALID_ARGUMENT;
+    if (!aligned(dy, 16) || !aligned(dB, 16) || !aligned(dC, 16) || !aligned(ddt, 4))
+      return SSD_ERR_INVALID_ARGUMENT;
+  }
+  // chunk length of the two passes whose state is (64 x 64): the caller's if
+  // that configuration is built, else the longest that is (any partition gives
+  // the same sums)
+  int Q2 = 0, Qf = 0;
+  for (int q : {chunk_len, 256, 128, 64})
+    if (config_supported(p.dtype, q, kHeadDim)) {
+      Q2 = q;
+      break;
+    }
+  // the fp32 passes (recompute of y, reversed pass for dx')
+  for (int q : {chunk_len, 256, 128, 64})
+    if (config_supported(Dtype::F32, q, dstate)) {
+      Qf = q;
+      break;
+    }
+  if (Q2 == 0 || Qf == 0) return SSD_ERR_UNSUPPORTED;
+  const bool bf16 = dtype == SSD_DTYPE_BF16;
+  st = check_device();
+  if (st != SSD_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const int H = nheads, P = headdim, N = dstate, G = ngroups;
+  const int NK = (N + 63) / 64, W = 64 * NK;
+  const size_t T = (size_t)total_len, S = (size_t)nseqs, e = dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  size_t off = 0;
+  char* base = nullptr;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return base ? base + at : nullptr;
+  };
+  BwdProblem b;
+  auto layout = [&]() {
+    off = 0;
+    b.xr = take(T * H * P * e);
+    b.Br = take(T * G * N * e);
+    b.Cr = take(T * G * N * e);
+    b.dtr = reinterpret_cast<float*>(take(T * H * 4));
+    b.xc = take(T * H * W * e);
+    b.xb = take(T * H * W * e);
+    b.dtc = reinterpret_cast<float*>(take(T * H * NK * 4));
+    b.dtb = reinterpret_cast<float*>(take(T * H * NK * 4));
+    b.Ac = reinterpret_cast<float*>(take((size_t)H * NK * 4));
+    b.cb = take(T * H * P * e);
+    b.h0c = reinterpret_cast<float*>(take(initial_state ? S * H * NK * 4096 * 4 : 0));
+    b.dfb = reinterpret_cast<float*>(take(dfinal_state ? S * H * NK * 4096 * 4 : 0));
+    b.x32 = reinterpret_cast<float*>(take(bf16 ? T * H * P * 4 : 0));
+    b.xr32 = reinterpret_cast<float*>(take(bf16 ? T * H * P * 4 : 0));
+    b.B32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
+    b.C32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
+    b.Br32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
+    b.Cr32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
+    b.y_f = reinterpret_cast<float*>(take(T * H * P * 4));
+    b.hlast = reinterpret_cast<float*>(take(dfinal_state ? S * H * P * N * 4 : 0));
+    b.y_x = reinterpret_cast<float*>(take(T * H * P * 4));
+    b.g0 = reinterpret_cast<float*>(take(dinitial_state ? S * H * P * N * 4 : 0));
+    b.y_c = take(T * H * W * e);
+    b.y_b = take(T * H * W * e);
+    b.qd = reinterpret_cast<float*>(take(T * H * 4));
+    b.rd = reinterpret_cast<float*>(take(T * H * 4));
+    b.ud = reinterpret_cast<float*>(take(T * H * 4));
+  };
+  layout();
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+  base = static_cast<char*>(ws_acquire(dev, off > 0 ? off : 256, s, 1));
+  if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  layout();
+  if (!initial_state) b.h0c = nullptr;
+  if (!dfinal_state) b.dfb = nullptr, b.hlast = nullptr;
+  if (!dinitial_state) b.g0 = nullptr;
+  b.x = x; b.dt = dt; b.A = A_head; b.B = B; b.C = C; b.cu = cu_seqlens; b.h0 = initial_state;
+  b.dy = dy; b.dfinal = dfinal_state; b.D = D; b.x_times_dt = x_times_dt;
+  b.dx = dx; b.ddt = ddt; b.dA = dA; b.dB = dB; b.dC = dC; b.dD = dD; b.dinit = dinitial_state;
+  b.nseq = nseqs; b.seqlen = seqlen; b.total = total_len;
+  b.H = H; b.P = P; b.N = N; b.G = G; b.NK = NK; b.dtype = p.dtype;
+  if (!bf16) {
+    b.x32 = static_cast<const float*>(x);
+    b.B32 = static_cast<const float*>(B);
+    b.C32 = static_cast<const float*>(C);
+    b.xr32 = static_cast<const float*>(b.xr);
+    b.Br32 = static_cast<const float*>(b.Br);
+    b.Cr32 = static_cast<const float*>(b.Cr);
+  }
+
+  hipError_t err = timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 0, s); });
+  if (err != hipSuccess) return map_err(err);
+  if (nseqs == 0) return SSD_OK;
+  // forward recompute (fp32): y without the skip term, and the final state
+  Problem pf = make_problem(b.x32, dt, A_head, b.B32, b.C32, cu_seqlens, nseqs, seqlen, total_len, H, P, N,
+                            G, Qf, SSD_DTYPE_F32, b.y_f, b.hlast, initial_state, nullptr, x_times_dt);
+  // dx' (fp32): reversed in time, decays shifted, from dfinal
+  Problem px = make_problem(b.xr32, b.dtr, A_head, b.Br32, b.Cr32, cu_seqlens, nseqs, seqlen, total_len, H,
+                            P, N, G, Qf, SSD_DTYPE_F32, b.y_x, b.g0, dfinal_state, nullptr, 0);
+  // dC: x and B exchanged (per-head copies of B as the input), from h0^T
+  Problem pc = make_problem(b.xc, b.dtc, b.Ac, x, dy, cu_seqlens, nseqs, seqlen, total_len, H * NK,
+                            kHeadDim, P, H, Q2, dtype, b.y_c, nullptr, b.h0c, nullptr, x_times_dt);
+  // dB: as dC, reversed in time, from dfinal^T
+  Problem pb = make_problem(b.xb, b.dtb, b.Ac, b.xr, b.cb, cu_seqlens, nseqs, seqlen, total_len, H * NK,
+                            kHeadDim, P, H, Q2, dtype, b.y_b, nullptr, b.dfb, nullptr, 0);
+  for (const Problem* q : {&pf, &px, &pc, &pb}) {
+    st = run(*q, s, nullptr);
+    if (st != SSD_OK) return st;
+  }
+  return map_err(timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 1, s); }));
 }
 
 const char* ssd_status_string(ssd_status status) {

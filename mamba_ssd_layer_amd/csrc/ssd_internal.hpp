@@ -63,6 +63,39 @@ struct DecodeProblem {
   Dtype dtype;
 };
 
+// Backward pass: the caller's arrays and the rearranged inputs and outputs of
+// the three gradient passes (all in the element dtype unless noted).
+struct BwdProblem {
+  const void* x; const float* dt; const float* A; const void* B; const void* C;
+  const int32_t* cu;      // (S+1) or nullptr (batched)
+  const float* h0;        // (S, H, P, N) initial state or nullptr
+  const void* dy;         // (Ttot, H, P)
+  const float* dfinal;    // (S, H, P, N) gradient of the final state or nullptr
+  const float* D;         // (H) or nullptr
+  int x_times_dt;
+  void* dx; float* ddt; float* dA; void* dB; void* dC; float* dD; float* dinit;
+  int64_t nseq, seqlen, total;
+  int H, P, N, G;
+  int NK;                 // 64-column parts of N (N < 64: one, zero padded)
+  Dtype dtype;
+  // reversed pass (dx'): input dy reversed, B := C, C := B, shifted decays
+  void* xr; void* Br; void* Cr; float* dtr;
+  // C pass (in time) and B pass (reversed): per-head copies of B and C in 64-column parts
+  void* xc; float* dtc; float* Ac; void* xb; float* dtb;
+  void* cb;               // (Ttot, H, P) x' reversed: the B pass's C
+  float* h0c; float* dfb; // (S, H*NK, 64, 64) fp32 transposed parts, or nullptr
+  // fp32 inputs of the forward recompute and of the reversed pass (on the bf16
+  // path copies, on the fp32 path the arrays above): d(ell) is a running sum of
+  // differences of y and dx' terms, which bf16 outputs would not resolve
+  const float* x32; const float* B32; const float* C32;  // (Ttot,H,P), (Ttot,G,N)
+  const float* xr32; const float* Br32; const float* Cr32;
+  // outputs of the passes
+  float* y_f; float* hlast;    // forward recompute (fp32): y without D, final state
+  float* y_x; float* g0;       // reversed pass (fp32): dx' (reversed order), G_first
+  void* y_c; void* y_b;        // (Ttot, H*NK, 64) per-head parts of dC and (reversed) dB
+  float* qd; float* rd; float* ud;  // (H, Ttot) fp32 per-token terms
+};
+
 // Device workspace, carved out of one allocation (256-byte aligned pieces).
 struct Workspace {
   int32_t* seq_off = nullptr;    // (S+1) first chunk slot of each sequence; [S] = chunk count
@@ -97,7 +130,7 @@ bool config_supported(Dtype dt, int Q, int N);
 
 // Kernel launchers; each returns the launch status.  Kernel ids for timing.
 enum KernelId { kK0SeqTable = 0, kK13ChunkState = 1, kK4StatePass = 2, kK25ChunkOutput = 3,
-                kK2ChunkCB = 4, kK6DecodeStep = 5, kNumKernels = 6 };
+                kK2ChunkCB = 4, kK6DecodeStep = 5, kK7BackwardGlue = 6, kNumKernels = 7 };
 // K0 (varlen only): per-sequence first token, length and first chunk slot.
 hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
 // K1 + K3: chunk-local log-decay cumsum (-> acs, lam, dmax), chunk states (-> states);
@@ -113,6 +146,9 @@ hipError_t launch_chunk_cb(const Problem& p, const Workspace& ws, hipStream_t s)
 hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s);
 // K6: one recurrent step (decode): state update in place and y.
 hipError_t launch_decode_step(const DecodeProblem& d, hipStream_t s);
+// K7 backward glue: stage 0 builds the gradient passes' inputs (and zeroes dA,
+// dD), stage 1 turns their outputs into dx, dB, dC, d(dt), dA, dD, dh0.
+hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);
 bool chunk_state_supported(Dtype dt, int Q, int N);
 bool chunk_output_supported(Dtype dt, int Q, int N);
 // Whether the chunk-output kernel for (dtype, Q, N) reads the kernel-matrix pass's

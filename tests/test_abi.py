@@ -158,6 +158,26 @@ def test_decode_rejects_invalid_arguments(lib, kw, code):
     assert call_decode(lib, **kw) == code
 
 
+def test_backward_rejects_invalid_arguments(lib):
+    # x dt A B C cu S T H P N G Q dtype h0 D xdt dy dfinal dx ddt dA dB dC dD dinit stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 512, 4, 64, 128, 1, 256, 1, None, None, 0,
+            FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None]
+
+    def call(changes):
+        a = list(base)
+        for i, v in changes.items():
+            a[i] = v
+        return lib.ssd_chunked_bwd(*a)
+
+    assert call({17: None}) == INVALID        # dy missing
+    assert call({17: FAKE + 2}) == INVALID    # dy misaligned
+    assert call({21: None}) == INVALID        # dA missing
+    assert call({18: FAKE + 4}) == INVALID    # dfinal misaligned
+    assert call({6: 3}) == INVALID            # batched: 512 not a multiple of 3
+    assert call({10: 48}) == UNSUPPORTED
+    assert call({16: 5}) == INVALID           # x_times_dt is 0 or 1
+
+
 def test_intermediates_rejects_uneven_batch(lib):
     assert lib.ssd_chunked_fwd_intermediates(FAKE, FAKE, FAKE, FAKE, FAKE, None, 3, 100, 4, 64, 128,
                                              1, 256, 1, FAKE, None, None, None, None, None) == INVALID

@@ -490,3 +490,112 @@ def test_decode_options(dev, dtype):
     yr, fr = oracle.recurrence(inp.x, inp.dt, inp.A, inp.B, inp.C, init_state=h0, D=D, x_times_dt=True)
     assert _slice_rel_l2(y.float().cpu().numpy(), yr[:, 0]) <= TOL[dtype]
     assert _slice_rel_l2(state.cpu().numpy(), fr) <= 1e-5
+
+
+# ------------------------------------------------------------- backward ----
+def _grads_gpu(inp, dev, Q, dy, h0=None, D=None, xdt=False, dfinal=None):
+    d = to_device(inp, dev)
+    tdt = torch.bfloat16 if inp.workload.dtype == "bf16" else torch.float32
+    tt = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    g = bd.ssd_chunked_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], tt(dy).to(tdt), Q,
+                           cu_seqlens=d.get("cu"), initial_state=tt(h0), D=tt(D), x_times_dt=xdt,
+                           dfinal_state=tt(dfinal), want_dD=True, want_dinitial=True)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.float().cpu().numpy()) for k, v in g.items()}
+
+
+def _grad_errors(inp, g, r):
+    """Max relative L2 error per (sequence, head) slice for dx and d(dt), per
+    (sequence, group) slice for dB and dC, per (sequence, head) for the
+    initial-state gradient, and over the head vector for dA and dD."""
+    cu = inp.packed_cu_seqlens()
+    H, P = inp.x.shape[-2:]
+    G, N = inp.B.shape[-2:]
+
+    def per_seq(got, ref):
+        """got, ref (Ttot, W, K): max over sequences and W of the relative L2 over (tokens, K)."""
+        errs = []
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            if b > a:
+                num = np.sqrt(np.sum((got[a:b] - ref[a:b]) ** 2, axis=(0, 2)))
+                den = np.sqrt(np.sum(ref[a:b] ** 2, axis=(0, 2)))
+                errs.append(num / np.maximum(den, 1e-30))
+        return float(np.max(np.concatenate(errs))) if errs else 0.0
+
+    def vec(got, ref):
+        return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+    return {
+        "dx": per_seq(g["dx"].reshape(-1, H, P), r["dx"].reshape(-1, H, P)),
+        "ddt": per_seq(g["ddt"].reshape(-1, H, 1), r["ddt"].reshape(-1, H, 1)),
+        "dB": per_seq(g["dB"].reshape(-1, G, N), r["dB"].reshape(-1, G, N)),
+        "dC": per_seq(g["dC"].reshape(-1, G, N), r["dC"].reshape(-1, G, N)),
+        "dA": vec(g["dA"], r["dA"]),
+        "dD": vec(g["dD"], r["dD"]) if r["dD"] is not None else 0.0,
+        "dinit": float(np.max(oracle.rel_l2_per_slice(g["dinitial_state"], r["dinit"], slice_axes=(0, 1)))),
+    }
+
+
+def _check_bwd(inp, dev, Q, tol, label, seed, h0=None, D=None, xdt=False, dfinal=None):
+    from mamba_ssd_layer_amd.workloads import bf16_round
+    rng = np.random.default_rng(seed + 777)
+    dy = rng.standard_normal(inp.x.shape).astype(np.float32)
+    if inp.workload.dtype == "bf16":
+        dy = bf16_round(dy)
+    log(f"[bwd] {label}")
+    g = _grads_gpu(inp, dev, Q, dy, h0, D, xdt, dfinal)
+    for k, v in g.items():
+        assert v is None or np.all(np.isfinite(v)), k
+    r = oracle.backward(inp.x, inp.dt, inp.A, inp.B, inp.C, dy, cu_seqlens=inp.packed_cu_seqlens(),
+                        init_state=h0, dfinal=dfinal, D=D if D is not None else np.zeros(inp.A.shape),
+                        x_times_dt=xdt)
+    e = _grad_errors(inp, g, r)
+    # d(dt) and dA come from d(ell_t) = sum_{k>=t} (dy_k . y_k - x'_k . dx'_k): a
+    # running sum of differences whose terms are far larger than the result, so
+    # the fp32 recompute's relative error (~5e-7) is magnified by that
+    # cancellation (about 20x on these inputs); their fp32 bar is 5e-5
+    bars = {k: (max(tol, 5e-5) if k in ("ddt", "dA") else tol) for k in e}
+    log("[bwd]   max rel-L2 " + " ".join(f"{k}={v:.2e}" for k, v in e.items()) + f" (bar {tol:g})")
+    bad = {k: v for k, v in e.items() if not v <= bars[k]}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("dtype,N,Q", [("f32", 64, 64), ("f32", 32, 128), ("bf16", 128, 256),
+                                       ("bf16", 256, 128), ("bf16", 16, 64)])
+def test_backward_batched(dev, dtype, N, Q):
+    """Gradients of every input against the oracle's adjoint recurrence, plain
+    (no initial state, no dfinal, no options)."""
+    w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=520, batch=2, nheads=4, ngroups=2)
+    inp = make_inputs(w, 70 + N)
+    _check_bwd(inp, dev, Q, TOL[dtype], f"batched {dtype} N={N} Q={Q}", 70 + N)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_all_options(dev, dtype):
+    """With an initial state, a final-state gradient, the skip term and the
+    dt-scaled input: every gradient, the initial state's included."""
+    N, Q = (64, 128) if dtype == "f32" else (128, 256)
+    w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=700, batch=2, nheads=8, ngroups=2)
+    inp = make_inputs(w, 80)
+    h0 = initial_states(2, 8, 64, N, seed=80)
+    dfin = initial_states(2, 8, 64, N, seed=81)
+    D = np.random.default_rng(80).standard_normal(8).astype(np.float32)
+    _check_bwd(inp, dev, Q, TOL[dtype], f"options {dtype}", 80, h0=h0, D=D, xdt=True, dfinal=dfin)
+
+
+def test_backward_varlen(dev):
+    """Packed sequences, empty ones included (their initial-state gradient is
+    dfinal), N = 256 (four 64-column parts)."""
+    lens = [300, 0, 1, 513, 64, 0, 77]
+    w = SMALL.with_(varlen=True, batch=len(lens), dstate=256, chunk_len=128, nheads=4, ngroups=2)
+    inp = make_inputs(w, 82, seqlens=lens)
+    h0 = initial_states(len(lens), 4, 64, 256, seed=82)
+    dfin = initial_states(len(lens), 4, 64, 256, seed=83)
+    _check_bwd(inp, dev, 128, TOL["bf16"], "varlen bf16 N=256", 82, h0=h0, dfinal=dfin)
+
+
+def test_backward_full_2k(dev):
+    """The backward at the Mamba-2-2.7B-like layer's full size (bf16)."""
+    inp = make_inputs(WORKLOADS["mamba2_2p7b_T2k"], 0)
+    _check_bwd(inp, dev, 256, TOL["bf16"], "mamba2_2p7b_T2k full bf16", 0)
