@@ -46,7 +46,9 @@
 //  * LDS operand reads are issued ahead of the MFMAs that use them (pinned by
 //    scheduling barriers); each finished row tile of y is passed through the
 //    wave's own LDS rows and written as whole 128-byte rows.
-//  * Options: with the input entering as dt x, every x staging scale carries
+//  * Options: y may leave out each token's own term (C_i . B_i) x_i (the j == i
+//    entries of the diagonal tile are cleared too; the backward pass uses it);
+//    with the input entering as dt x, every x staging scale carries
 //    dt_j (the chunk-state kernel provides Acs_j - ln dt_j); the skip term
 //    D_h x is added to each finished 16-byte piece of y before its store.
 //  * fp32 accumulation; y rounded once to the element dtype and stored with the
@@ -147,6 +149,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // log of the divisor x is staged with: Acs, or Acs - ln dt when the input
   // enters as dt x (then every staging scale below carries dt)
   const float* xlbase = (kOpts && p.x_times_dt) ? ws.xlog + k * H * Q : abase;
+  // 1: the diagonal tile also clears j == i (y without each token's own term)
+  const int sd = kOpts ? p.strict_diag : 0;
   // kernel tiles of the chunk's group: [tile][16-byte vector q][lane]
   const uint4* gsrc = reinterpret_cast<const uint4*>(ws.cb) + (k * G + g) * (int64_t)(NTILE * GV * 64);
   T* ybase = reinterpret_cast<T*>(p.y) + cd.t0 * H * P;
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
               for (int d = 0; d < 4; ++d) {
                 const int r = 8 * q + 2 * d;
                 const int j0 = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J of values r, r+1
-                m[d] = (j0 <= lr ? 0x0000ffffu : 0u) | (j0 + 1 <= lr ? 0xffff0000u : 0u);
+                m[d] = (j0 + sd <= lr ? 0x0000ffffu : 0u) | (j0 + 1 + sd <= lr ? 0xffff0000u : 0u);
               }
               b[q].x &= m[0]; b[q].y &= m[1]; b[q].z &= m[2]; b[q].w &= m[3];
             }
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
-          v[r] = (!kDiag || jr <= lr) ? gt[r] : 0.0f;
+          v[r] = (!kDiag || jr + sd <= lr) ? gt[r] : 0.0f;
         }
       } else if (mode == kMaskTile) {
         // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
-            v[r] = (jr <= lr) ? gt[r] * u : 0.0f;
+            v[r] = (jr + sd <= lr) ? gt[r] * u : 0.0f;
           }
         }
       } else if constexpr (!kDiag) {
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         for (int r = 0; r < 16; ++r) {
           const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
           const float m = __expf(ai - acs_s[j]);
-          v[r] = (j <= i_loc) ? gt[r] * m : 0.0f;
+          v[r] = (j + sd <= i_loc) ? gt[r] * m : 0.0f;
         }
       }
       // Y^T += X^T (L o G)^T over the 32 tokens of tile J
@@ -559,7 +563,7 @@ static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
     const int HB = heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    if (p.D != nullptr || p.x_times_dt)
+    if (p.D != nullptr || p.x_times_dt || p.strict_diag)
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, true>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     else
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, false>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);

@@ -17,9 +17,14 @@
 // kernels unchanged:
 //   dx'  forward over the sequence reversed in time: input dy, B := C, C := B,
 //        decays shifted by one token (a~_j = a_{L-j}, a~_0 = 1), initial state
-//        dfinal; its output read back reversed is dx', its final state G_first
-//        (this pass and the recompute of y run in fp32: d(ell) sums differences
-//        of their terms, which bf16 results would not resolve);
+//        dfinal; its output read back reversed is dx', its final state G_first.
+//        This pass and the recompute of y run in fp32 (d(ell) below is a
+//        running sum of their terms, which bf16 results would not resolve:
+//        errors of several percent in d(dt)) and leave out each token's own term
+//        (C_t . B_t) x'_t (resp. dy_t): it appears in both dy . y and x' . dx'
+//        and, for fast decays, dominates both, so d(Acs) would be the small
+//        difference of two rounded large numbers; without it nothing cancels,
+//        and the term is added back to dx exactly;
 //   dC   forward in time with the roles of x and B exchanged: input B (each
 //        head's copy, in parts of 64 columns), B := x', C := dy, initial state
 //        h0 transposed; the outputs of a group's heads are summed;
@@ -76,6 +81,40 @@ __device__ __forceinline__ void st_e(void* p, int64_t i, float v) {
   else reinterpret_cast<float*>(p)[i] = v;
 }
 
+// A 16-byte vector of the element type times d (bf16: rounded to nearest even).
+template <class E>
+__device__ __forceinline__ uint4 scale_vec(const uint4& v, float d) {
+  if constexpr (E::kBytes == 2) {
+    auto f = [&](uint32_t w) { return pack_bf16x2(bf16_lo(w) * d, bf16_hi(w) * d); };
+    return make_uint4(f(v.x), f(v.y), f(v.z), f(v.w));
+  } else {
+    auto f = [&](uint32_t w) { return __float_as_uint(__uint_as_float(w) * d); };
+    return make_uint4(f(v.x), f(v.y), f(v.z), f(v.w));
+  }
+}
+// Eight bf16 values -> eight fp32 at dst (two 16-byte stores).
+__device__ __forceinline__ void store_f32x8(float* dst, const uint4& v) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+  reinterpret_cast<float4*>(dst)[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+}
+// 16-byte vector of the element type -> VEC fp32 values.
+template <class E>
+__device__ __forceinline__ void unpack_vec(const uint4& v, float (&o)[16 / E::kBytes]) {
+  if constexpr (E::kBytes == 2) {
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+  } else {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
+}
+template <class E>
+__device__ __forceinline__ uint4 pack_vec(const float (&o)[16 / E::kBytes]) {
+  if constexpr (E::kBytes == 2)
+    return make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+  else
+    return make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+}
+
 // One workgroup per packed token t (f: t's position reversed within its
 // sequence).  Writes the rearranged inputs of the three gradient passes.
 template <class E>
@@ -105,36 +144,49 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_kernel(BwdProblem b) {
       dc[v] = sb[v];  //                C := B
     }
   }
-  // x' reversed (input scaled by dt with the dt-scaled input), element-wise;
-  // on the bf16 path also the fp32 inputs of the recompute and reversed passes
-  for (int e = tid; e < H * P; e += kBwThreads) {
-    const int h = e / P;
-    const float xv = ld_e<E>(b.x, t * H * P + e);
-    st_e<E>(b.cb, f * H * P + e, b.x_times_dt ? xv * b.dt[t * H + h] : xv);
-    if constexpr (E::kBytes == 2) {
-      const_cast<float*>(b.x32)[t * H * P + e] = xv;
-      const_cast<float*>(b.xr32)[f * H * P + e] = ld_e<E>(b.dy, t * H * P + e);
+  // x' reversed (input scaled by dt with the dt-scaled input), and on the bf16
+  // path the fp32 inputs of the recompute and reversed passes, in 16-byte
+  // vectors (VEC elements, never straddling a head row)
+  for (int v = tid; v < H * P / VEC; v += kBwThreads) {
+    const int h = v * VEC / P;
+    const uint4 xv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.x) + t * H * P)[v];
+    uint4* cbv = reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.cb) + f * H * P) + v;
+    if (b.x_times_dt) {
+      const float d = b.dt[t * H + h];
+      *cbv = scale_vec<E>(xv, d);
+    } else {
+      *cbv = xv;
+    }
+    if constexpr (E::kBytes == 2) {  // fp32 inputs of the recompute and reversed passes
+      const uint4 dyv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.dy) + t * H * P)[v];
+      store_f32x8(const_cast<float*>(b.x32) + t * H * P + v * 8, xv);
+      store_f32x8(const_cast<float*>(b.xr32) + f * H * P + v * 8, dyv);
     }
   }
   if constexpr (E::kBytes == 2) {
-    for (int e = tid; e < G * N; e += kBwThreads) {
-      const float bv = ld_e<E>(b.B, t * G * N + e), cv = ld_e<E>(b.C, t * G * N + e);
-      const_cast<float*>(b.B32)[t * G * N + e] = bv;
-      const_cast<float*>(b.C32)[t * G * N + e] = cv;
-      const_cast<float*>(b.Br32)[f * G * N + e] = cv;  // reversed pass: B := C
-      const_cast<float*>(b.Cr32)[f * G * N + e] = bv;  //                C := B
+    for (int v = tid; v < G * N / VEC; v += kBwThreads) {
+      const uint4 bv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.B) + t * G * N)[v];
+      const uint4 cv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.C) + t * G * N)[v];
+      store_f32x8(const_cast<float*>(b.B32) + t * G * N + v * 8, bv);
+      store_f32x8(const_cast<float*>(b.C32) + t * G * N + v * 8, cv);
+      store_f32x8(const_cast<float*>(b.Br32) + f * G * N + v * 8, cv);  // reversed pass: B := C
+      store_f32x8(const_cast<float*>(b.Cr32) + f * G * N + v * 8, bv);  //                C := B
     }
   }
   // per-head copies of B (in time) and C (reversed), 64-column parts, zero
   // padded past N
   const int W = 64 * NK;
-  for (int e = tid; e < H * W; e += kBwThreads) {
-    const int h = e / W, n = e % W;
+  const int WV = W / VEC;
+  for (int v = tid; v < H * WV; v += kBwThreads) {
+    const int h = v / WV, n0 = (v % WV) * VEC;
     const int g = h / hpg;
-    const float vb = n < N ? ld_e<E>(b.B, (t * G + g) * N + n) : 0.0f;
-    const float vc = n < N ? ld_e<E>(b.C, (t * G + g) * N + n) : 0.0f;
-    st_e<E>(b.xc, t * H * W + e, vb);
-    st_e<E>(b.xb, f * H * W + e, vc);
+    uint4 vb = make_uint4(0, 0, 0, 0), vc = vb;
+    if (n0 < N) {
+      vb = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.B) + (t * G + g) * N + n0);
+      vc = *reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.C) + (t * G + g) * N + n0);
+    }
+    reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.xc) + t * H * W)[v] = vb;
+    reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.xb) + f * H * W)[v] = vc;
   }
   // step sizes: reversed and shifted by one token (the first reversed token
   // has a~ = 1), and per-part copies
@@ -181,21 +233,58 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_states_kernel(BwdProblem 
 // same from the B pass output read at the reversed position.  fp32 sums.
 template <class E>
 __global__ __launch_bounds__(kBwThreads) void bwd_reduce_kernel(BwdProblem b) {
+  using T = typename E::storage;
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float pc[kBwThreads][VEC], pb[kBwThreads][VEC];
   const int64_t t = blockIdx.x;
   const int H = b.H, N = b.N, G = b.G, W = 64 * b.NK;
   const int hpg = H / G;
   const TokSeq q = token_seq(b, t);
   const int64_t f = q.t0 + (q.L - 1 - (t - q.t0));
-  for (int e = threadIdx.x; e < G * N; e += kBwThreads) {
-    const int g = e / N, n = e % N;
-    float sc = 0.0f, sb = 0.0f;
-    for (int j = 0; j < hpg; ++j) {
-      const int h = g * hpg + j;
-      sc += ld_e<E>(b.y_c, (t * H + h) * W + n);
-      sb += ld_e<E>(b.y_b, (f * H + h) * W + n);
+  const T* yc = reinterpret_cast<const T*>(b.y_c);
+  const T* yb = reinterpret_cast<const T*>(b.y_b);
+  const int nvec = G * N / VEC;
+  // with few output vectors the heads of a group are split into `slices`
+  // interleaved subsets summed by different threads, then combined in LDS
+  const int slices = nvec < kBwThreads ? kBwThreads / nvec : 1;
+  for (int v0 = 0; v0 < nvec; v0 += kBwThreads / slices) {
+    const int v = v0 + threadIdx.x % (kBwThreads / slices);
+    const int sl = threadIdx.x / (kBwThreads / slices);
+    float sc[VEC] = {}, sb[VEC] = {};
+    if (v < nvec && sl < slices) {
+      const int g = v * VEC / N, n0 = v * VEC % N;
+      for (int j = sl; j < hpg; j += slices) {
+        const int h = g * hpg + j;
+        float a[VEC], c[VEC];
+        unpack_vec<E>(*reinterpret_cast<const uint4*>(yc + (t * H + h) * W + n0), a);
+        unpack_vec<E>(*reinterpret_cast<const uint4*>(yb + (f * H + h) * W + n0), c);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          sc[k] += a[k];
+          sb[k] += c[k];
+        }
+      }
     }
-    st_e<E>(b.dC, t * G * N + e, sc);
-    st_e<E>(b.dB, t * G * N + e, sb);
+    if (slices > 1) {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        pc[threadIdx.x][k] = sc[k];
+        pb[threadIdx.x][k] = sb[k];
+      }
+      __syncthreads();
+      if (sl == 0)
+        for (int r = 1; r < slices; ++r)
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) {
+            sc[k] += pc[threadIdx.x + r * (kBwThreads / slices)][k];
+            sb[k] += pb[threadIdx.x + r * (kBwThreads / slices)][k];
+          }
+      __syncthreads();
+    }
+    if (v < nvec && sl == 0) {
+      reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.dC) + t * G * N)[v] = pack_vec<E>(sc);
+      reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.dB) + t * G * N)[v] = pack_vec<E>(sb);
+    }
   }
 }
 
@@ -204,27 +293,64 @@ __global__ __launch_bounds__(kBwThreads) void bwd_reduce_kernel(BwdProblem b) {
 // Eight lanes share one head row (8 values each); one workgroup per token.
 template <class E>
 __global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
+  using T = typename E::storage;
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float cbs[kMaxBwdGroups];
   const int64_t t = blockIdx.x;
-  const int H = b.H, P = b.P;
+  const int H = b.H, P = b.P, N = b.N, G = b.G;
+  const int hpg = H / G;
   const TokSeq q = token_seq(b, t);
   const int64_t f = q.t0 + (q.L - 1 - (t - q.t0));
-  const int lane8 = threadIdx.x % 8;
+  // c_g = C_t . B_t per group: the weight of each token's own term
+  {
+    const int wid = threadIdx.x / 64, lane = threadIdx.x % 64;
+    for (int g = wid; g < G; g += kBwThreads / 64) {
+      float acc = 0.0f;
+      for (int n = lane; n < N; n += 64)
+        acc += ld_e<E>(b.C, (t * G + g) * N + n) * ld_e<E>(b.B, (t * G + g) * N + n);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0) cbs[g] = acc;
+    }
+    __syncthreads();
+  }
+  const int lane8 = threadIdx.x % 8;  // eight lanes per head row, 8 values each
   for (int h = threadIdx.x / 8; h < H; h += kBwThreads / 8) {
     const float dth = b.dt[t * H + h];
     const float sx = b.x_times_dt ? dth : 1.0f;
     const float dh = b.D != nullptr ? b.D[h] : 0.0f;
-    float s_dyy = 0.0f, s_xdx = 0.0f, s_xdy = 0.0f;
-    for (int p = lane8; p < P; p += 8) {
-      const int64_t o = (t * H + h) * P + p;
-      const float xv = ld_e<E>(b.x, o);
-      const float dyv = ld_e<E>(b.dy, o);
-      const float yv = b.y_f[o];
-      const float dxp = b.y_x[(f * H + h) * P + p];  // dx' = reversed pass output
-      s_dyy += dyv * yv;
-      s_xdx += xv * dxp;
-      s_xdy += xv * dyv;
-      st_e<E>(b.dx, o, sx * dxp + dh * dyv);
+    const float cg = cbs[h / hpg];
+    const int64_t o = (t * H + h) * P + lane8 * 8;
+    const int64_t orev = (f * H + h) * P + lane8 * 8;  // dx' comes reversed
+    float xv[8], dyv[8], yv[8], dxs[8], dx[8];
+#pragma unroll
+    for (int c = 0; c < 8 / VEC; ++c) {
+      unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.x) + o + c * VEC),
+                    *reinterpret_cast<float(*)[VEC]>(xv + c * VEC));
+      unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.dy) + o + c * VEC),
+                    *reinterpret_cast<float(*)[VEC]>(dyv + c * VEC));
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float4 a = reinterpret_cast<const float4*>(b.y_f + o)[c];
+      const float4 d = reinterpret_cast<const float4*>(b.y_x + orev)[c];
+      yv[4 * c] = a.x; yv[4 * c + 1] = a.y; yv[4 * c + 2] = a.z; yv[4 * c + 3] = a.w;
+      dxs[4 * c] = d.x; dxs[4 * c + 1] = d.y; dxs[4 * c + 2] = d.z; dxs[4 * c + 3] = d.w;
+    }
+    // with the own terms left out of y and dx', d(Acs_t) = dy . y - x' . dx'
+    // has nothing that cancels itself; dx' = dx's + c_g dy exactly
+    float s_dyy = 0.0f, s_xdx = 0.0f, s_xdy = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s_dyy += dyv[k] * yv[k];
+      s_xdx += xv[k] * dxs[k];
+      s_xdy += xv[k] * dyv[k];
+      dx[k] = sx * (dxs[k] + cg * dyv[k]) + dh * dyv[k];
+    }
+#pragma unroll
+    for (int c = 0; c < 8 / VEC; ++c)
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.dx) + o + c * VEC) =
+          pack_vec<E>(*reinterpret_cast<float(*)[VEC]>(dx + c * VEC));
 #pragma unroll
     for (int off = 4; off >= 1; off >>= 1) {
       s_dyy += __shfl_xor(s_dyy, off);
@@ -232,9 +358,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
       s_xdy += __shfl_xor(s_xdy, off);
     }
     if (lane8 == 0) {
-      b.qd[h * b.total + t] = s_dyy - sx * s_xdx;  // d(Acs_t): dy . y - x' . dx'
-      b.rd[h * b.total + t] = s_xdx;               // x . dx' (d(dt) term of the dt-scaled input)
-      b.ud[h * b.total + t] = s_xdy;               // x . dy (dD term)
+      b.qd[h * b.total + t] = s_dyy - sx * s_xdx;      // d(Acs_t)
+      b.rd[h * b.total + t] = s_xdx + cg * s_xdy;      // x . dx' (full): d(dt) term of the dt-scaled input
+      b.ud[h * b.total + t] = s_xdy;                   // x . dy (dD term)
     }
   }
 }
@@ -253,67 +379,112 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// Per (sequence, head): <dfinal, h_last>, dh0 = a_first G_first, then
-// d(ell_t) = sum_{k>=t} d(Acs_k) (plus <dfinal, h_last> at the last token) by
-// a reverse prefix sum, d(dt), and the sequence's shares of dA and dD.
+// Token range [t0, t0 + L) of sequence s, clamped into [0, Ttot] (invalid
+// cu_seqlens contents: unspecified results, every access in bounds).
+__device__ __forceinline__ void seq_range(const BwdProblem& b, int64_t s, int64_t* t0, int64_t* L) {
+  if (b.cu == nullptr) {
+    *t0 = s * b.seqlen;
+    *L = b.seqlen;
+  } else {
+    *t0 = min(max((int64_t)b.cu[s], (int64_t)0), b.total);
+    *L = max(min((int64_t)b.cu[s + 1], b.total) - *t0, (int64_t)0);
+  }
+}
+
+// d(ell_t) = sum_{k>=t} d(Acs_k) (+ <dfinal, h_last>) is a reverse prefix sum
+// over each sequence, split into segments of kSeg tokens so that long
+// sequences spread over many workgroups.  Sums are fp64: d(ell) is a sum of up
+// to T terms of both signs.
+constexpr int kSeg = kBwdScanSeg;
+
+// Pass 1, one workgroup per (sequence, head, segment): the segment's sum; the
+// first segment's workgroup also forms <dfinal, h_last> and dh0 = a_first G_first.
+__global__ __launch_bounds__(kBwThreads) void bwd_segsum_kernel(BwdProblem b) {
+  __shared__ float red[kBwThreads / 64];
+  __shared__ double redd[kBwThreads / 64];
+  const int64_t blk = blockIdx.x;
+  const int64_t sh = blk / b.nseg;
+  const int seg = (int)(blk % b.nseg);
+  const int h = (int)(sh % b.H);
+  const int tid = threadIdx.x;
+  int64_t t0, L;
+  seq_range(b, sh / b.H, &t0, &L);
+  if (seg == 0) {
+    const int64_t PN = (int64_t)b.P * b.N;
+    if (b.dfinal != nullptr) {
+      float acc = 0.0f;
+      for (int64_t i = tid; i < PN; i += kBwThreads) acc += b.dfinal[sh * PN + i] * b.hlast[sh * PN + i];
+      acc = block_sum(acc, red);
+      if (tid == 0) b.edot[sh] = acc;
+    }
+    if (b.dinit != nullptr) {
+      const float a0 = L > 0 ? __expf(b.dt[t0 * b.H + h] * b.A[h]) : 1.0f;
+      for (int64_t i = tid; i < PN; i += kBwThreads) b.dinit[sh * PN + i] = a0 * b.g0[sh * PN + i];
+    }
+  }
+  const int64_t i0 = (int64_t)seg * kSeg, i1 = min(i0 + kSeg, L);
+  double acc = 0.0;
+  for (int64_t i = i0 + tid; i < i1; i += kBwThreads) acc += b.qd[h * b.total + t0 + i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (tid % 64 == 0) redd[tid / 64] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double s = 0.0;
+    for (int w = 0; w < kBwThreads / 64; ++w) s += redd[w];
+    b.segsum[blk] = s;
+  }
+}
+
+// Pass 2, one workgroup per (sequence, head, segment): offset from the later
+// segments, the in-segment reverse prefix sum (kSeg / 256 tokens per thread),
+// d(dt), and the segment's shares of dA and dD.
 __global__ __launch_bounds__(kBwThreads) void bwd_scan_kernel(BwdProblem b) {
   __shared__ float red[kBwThreads / 64];
   __shared__ double part[kBwThreads];
-  const int64_t sh = blockIdx.x;
+  constexpr int TPT = kSeg / kBwThreads;
+  const int64_t blk = blockIdx.x;
+  const int64_t sh = blk / b.nseg;
+  const int seg = (int)(blk % b.nseg);
   const int H = b.H;
   const int h = (int)(sh % H);
-  const int64_t s = sh / H;
   const int tid = threadIdx.x;
   int64_t t0, L;
-  if (b.cu == nullptr) {
-    t0 = s * b.seqlen;
-    L = b.seqlen;
-  } else {
-    // clamped into [0, Ttot] (invalid contents: unspecified results, in bounds)
-    t0 = min(max((int64_t)b.cu[s], (int64_t)0), b.total);
-    L = max(min((int64_t)b.cu[s + 1], b.total) - t0, (int64_t)0);
-  }
-  const int64_t PN = (int64_t)b.P * b.N;
-  float e = 0.0f;
-  if (b.dfinal != nullptr) {
-    float acc = 0.0f;
-    for (int64_t i = tid; i < PN; i += kBwThreads) acc += b.dfinal[sh * PN + i] * b.hlast[sh * PN + i];
-    e = block_sum(acc, red);
-  }
-  if (b.dinit != nullptr) {
-    const float a0 = L > 0 ? __expf(b.dt[t0 * H + h] * b.A[h]) : 1.0f;
-    for (int64_t i = tid; i < PN; i += kBwThreads) b.dinit[sh * PN + i] = a0 * b.g0[sh * PN + i];
-  }
-  if (L == 0) return;
-  // thread r owns tokens [r c, (r + 1) c) of the sequence
-  const int64_t c = (L + kBwThreads - 1) / kBwThreads;
-  const int64_t i0 = min((int64_t)tid * c, L), i1 = min(i0 + c, L);
-  // the running sums are fp64: d(ell) is a sum of up to T terms of both signs
+  seq_range(b, sh / H, &t0, &L);
+  const int64_t i0 = (int64_t)seg * kSeg;
+  if (i0 >= L) return;  // uniform: the whole workgroup leaves
+  double after = b.dfinal != nullptr ? (double)b.edot[sh] : 0.0;
+  for (int r = seg + 1; r < b.nseg; ++r) after += b.segsum[sh * b.nseg + r];
   const float* qd = b.qd + h * b.total + t0;
+  const int64_t j0 = i0 + (int64_t)tid * TPT, j1 = min(j0 + TPT, L);
   double local = 0.0;
-  for (int64_t i = i0; i < i1; ++i) local += qd[i];
+  for (int64_t i = j0; i < j1; ++i) local += qd[i];
+  // inclusive suffix sums of the threads' parts (Hillis-Steele in LDS)
   part[tid] = local;
   __syncthreads();
-  // suffix sum of the parts after this thread's range (a plain loop over at
-  // most 255 values from LDS: the scan is a small part of the backward)
-  double after = e;
-  for (int r = tid + 1; r < kBwThreads; ++r) after += part[r];
+  for (int off = 1; off < kBwThreads; off <<= 1) {
+    const double add = tid + off < kBwThreads ? part[tid + off] : 0.0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  double run = after + part[tid] - local;  // everything after this thread's tokens
   const float* rd = b.rd + h * b.total + t0;
   const float* ud = b.ud + h * b.total + t0;
   const float Ah = b.A[h];
-  double run = after, sdA = 0.0, sdD = 0.0;
-  for (int64_t i = i1 - 1; i >= i0; --i) {
+  double sdA = 0.0, sdD = 0.0;
+  for (int64_t i = j1 - 1; i >= j0; --i) {
     run += qd[i];
     const float dtv = b.dt[(t0 + i) * H + h];
     b.ddt[(t0 + i) * H + h] = Ah * (float)run + (b.x_times_dt ? rd[i] : 0.0f);
     sdA += dtv * run;
     sdD += ud[i];
   }
-  sdA = block_sum((float)sdA, red);
-  sdD = block_sum((float)sdD, red);
+  const float fa = block_sum((float)sdA, red);
+  const float fd = block_sum((float)sdD, red);
   if (tid == 0) {
-    atomicAdd(b.dA + h, sdA);
-    if (b.dD != nullptr) atomicAdd(b.dD + h, sdD);
+    atomicAdd(b.dA + h, fa);
+    if (b.dD != nullptr) atomicAdd(b.dD + h, fd);
   }
 }
 
@@ -332,7 +503,11 @@ static hipError_t launch_glue(const BwdProblem& b, int stage, hipStream_t s) {
         hipLaunchKernelGGL((bwd_reduce_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
         hipLaunchKernelGGL((bwd_token_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
       }
-      if (b.nseq > 0) hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(b.nseq * b.H)), blk, 0, s, b);
+      if (b.nseq > 0) {
+        const dim3 grid((unsigned)(b.nseq * b.H * b.nseg));
+        hipLaunchKernelGGL(bwd_segsum_kernel, grid, blk, 0, s, b);
+        hipLaunchKernelGGL(bwd_scan_kernel, grid, blk, 0, s, b);
+      }
       break;
     default:
       return hipErrorInvalidValue;

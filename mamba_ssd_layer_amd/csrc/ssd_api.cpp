@@ -9,6 +9,7 @@
 //   K4 state passing -> K2+K5 diagonal blocks fused with state-to-output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <string.h>
@@ -332,13 +333,14 @@ static Problem make_problem(const void* x, const float* dt, const float* A_head,
                             int64_t total, int32_t nheads, int32_t headdim, int32_t dstate,
                             int32_t ngroups, int32_t chunk_len, ssd_dtype dtype, void* y,
                             float* final_state, const float* initial_state = nullptr,
-                            const float* D = nullptr, int32_t x_times_dt = 0) {
+                            const float* D = nullptr, int32_t x_times_dt = 0, int strict_diag = 0) {
   Problem p;
   p.x = x; p.dt = dt; p.A = A_head; p.B = B; p.C = C; p.cu = cu; p.y = y;
   p.final_state = final_state;
   p.initial_state = initial_state;
   p.D = D;
   p.x_times_dt = x_times_dt;
+  p.strict_diag = strict_diag;
   p.nseq = nseq; p.seqlen = seqlen; p.total = total;
   p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups; p.Q = chunk_len;
   p.dtype = static_cast<Dtype>(dtype);
@@ -474,19 +476,20 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   // chunk length of the two passes whose state is (64 x 64): the caller's if
   // that configuration is built, else the longest that is (any partition gives
   // the same sums)
-  int Q2 = 0, Qf = 0;
+  int Q2 = 0;
   for (int q : {chunk_len, 256, 128, 64})
     if (config_supported(p.dtype, q, kHeadDim)) {
       Q2 = q;
       break;
     }
   // the fp32 passes (recompute of y, reversed pass for dx')
+  int Qf = 0;
   for (int q : {chunk_len, 256, 128, 64})
     if (config_supported(Dtype::F32, q, dstate)) {
       Qf = q;
       break;
     }
-  if (Q2 == 0 || Qf == 0) return SSD_ERR_UNSUPPORTED;
+  if (Q2 == 0 || Qf == 0 || ngroups > kMaxBwdGroups) return SSD_ERR_UNSUPPORTED;
   const bool bf16 = dtype == SSD_DTYPE_BF16;
   st = check_device();
   if (st != SSD_OK) return st;
@@ -502,7 +505,13 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
     off = align_up(off + bytes);
     return base ? base + at : nullptr;
   };
+  // longest possible sequence: seqlen (batched), total_len (packed)
+  const int64_t maxlen = cu_seqlens == nullptr ? seqlen : total_len;
+  const int64_t nseg64 = std::max<int64_t>(1, (maxlen + kBwdScanSeg - 1) / kBwdScanSeg);
+  if (nseqs * (int64_t)nheads * nseg64 > 0x7fffffffLL) return SSD_ERR_INVALID_ARGUMENT;
+  const int nseg = (int)nseg64;
   BwdProblem b;
+  b.nseg = nseg;
   auto layout = [&]() {
     off = 0;
     b.xr = take(T * H * P * e);
@@ -532,6 +541,8 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
     b.qd = reinterpret_cast<float*>(take(T * H * 4));
     b.rd = reinterpret_cast<float*>(take(T * H * 4));
     b.ud = reinterpret_cast<float*>(take(T * H * 4));
+    b.segsum = reinterpret_cast<double*>(take(S * H * (size_t)nseg * 8));
+    b.edot = reinterpret_cast<float*>(take(S * H * 4));
   };
   layout();
   int dev = 0;
@@ -559,12 +570,12 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   hipError_t err = timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 0, s); });
   if (err != hipSuccess) return map_err(err);
   if (nseqs == 0) return SSD_OK;
-  // forward recompute (fp32): y without the skip term, and the final state
+  // forward recompute (fp32): y without the skip term and the own terms, final state
   Problem pf = make_problem(b.x32, dt, A_head, b.B32, b.C32, cu_seqlens, nseqs, seqlen, total_len, H, P, N,
-                            G, Qf, SSD_DTYPE_F32, b.y_f, b.hlast, initial_state, nullptr, x_times_dt);
-  // dx' (fp32): reversed in time, decays shifted, from dfinal
+                            G, Qf, SSD_DTYPE_F32, b.y_f, b.hlast, initial_state, nullptr, x_times_dt, 1);
+  // dx' (fp32) without the own terms: reversed in time, decays shifted, from dfinal
   Problem px = make_problem(b.xr32, b.dtr, A_head, b.Br32, b.Cr32, cu_seqlens, nseqs, seqlen, total_len, H,
-                            P, N, G, Qf, SSD_DTYPE_F32, b.y_x, b.g0, dfinal_state, nullptr, 0);
+                            P, N, G, Qf, SSD_DTYPE_F32, b.y_x, b.g0, dfinal_state, nullptr, 0, 1);
   // dC: x and B exchanged (per-head copies of B as the input), from h0^T
   Problem pc = make_problem(b.xc, b.dtc, b.Ac, x, dy, cu_seqlens, nseqs, seqlen, total_len, H * NK,
                             kHeadDim, P, H, Q2, dtype, b.y_c, nullptr, b.h0c, nullptr, x_times_dt);

@@ -36,6 +36,7 @@ struct Problem {
   const float* initial_state;  // (S, H, P, N): state before each sequence's first token, or nullptr (zero)
   const float* D;         // (H): y += D_h x (skip connection), or nullptr
   int x_times_dt;         // 1: the input enters as dt_t x_t (B scaled by the step size)
+  int strict_diag;        // 1: y leaves out each token's own term (C_t . B_t) x_t (backward's use)
   int64_t nseq;           // S
   int64_t seqlen;         // T (batched form only)
   int64_t total;          // Ttot
@@ -63,6 +64,11 @@ struct DecodeProblem {
   Dtype dtype;
 };
 
+// tokens per segment of the backward's reverse prefix sums
+constexpr int kBwdScanSeg = 1024;
+// B/C groups the backward supports (its per-token kernel keeps one value per group in LDS)
+constexpr int kMaxBwdGroups = 256;
+
 // Backward pass: the caller's arrays and the rearranged inputs and outputs of
 // the three gradient passes (all in the element dtype unless noted).
 struct BwdProblem {
@@ -84,16 +90,20 @@ struct BwdProblem {
   void* xc; float* dtc; float* Ac; void* xb; float* dtb;
   void* cb;               // (Ttot, H, P) x' reversed: the B pass's C
   float* h0c; float* dfb; // (S, H*NK, 64, 64) fp32 transposed parts, or nullptr
-  // fp32 inputs of the forward recompute and of the reversed pass (on the bf16
-  // path copies, on the fp32 path the arrays above): d(ell) is a running sum of
-  // differences of y and dx' terms, which bf16 outputs would not resolve
-  const float* x32; const float* B32; const float* C32;  // (Ttot,H,P), (Ttot,G,N)
+  // The recompute of y and the reversed pass run in fp32 (on the bf16 path on
+  // fp32 copies of their inputs; on the fp32 path these point at the arrays
+  // above): d(ell) is a running sum of their terms, which bf16 results would
+  // not resolve.  Both leave out each token's own term (strict_diag), which
+  // d(ell) would otherwise subtract from itself; the glue adds it back to dx.
+  const float* x32; const float* B32; const float* C32;    // (Ttot,H,P), (Ttot,G,N)
   const float* xr32; const float* Br32; const float* Cr32;
-  // outputs of the passes
-  float* y_f; float* hlast;    // forward recompute (fp32): y without D, final state
-  float* y_x; float* g0;       // reversed pass (fp32): dx' (reversed order), G_first
+  float* y_f; float* hlast;    // recompute: y without D and own term; final state
+  float* y_x; float* g0;       // reversed pass: dx' without own term (reversed order); G_first
   void* y_c; void* y_b;        // (Ttot, H*NK, 64) per-head parts of dC and (reversed) dB
   float* qd; float* rd; float* ud;  // (H, Ttot) fp32 per-token terms
+  int nseg;                    // scan segments per (sequence, head): ceil(longest sequence / kBwdScanSeg)
+  double* segsum;              // (S, H, nseg) fp64 segment sums of d(Acs)
+  float* edot;                 // (S, H) <dfinal, h_last>
 };
 
 // Device workspace, carved out of one allocation (256-byte aligned pieces).
