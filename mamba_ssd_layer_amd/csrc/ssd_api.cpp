@@ -28,7 +28,7 @@ static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
 
-static int device_cus() {
+int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -134,6 +134,8 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws);
 // of start-up work).
 constexpr int kMaxHeadsPerBlock = 32;
 int heads_per_block(const Problem& p, int max_hb = kMaxHeadsPerBlock);
+// Compute units of the current device (cached per device).
+int device_cus();
 
 // Whether (dtype, Q, N) has an instantiated kernel set that fits in LDS.
 bool config_supported(Dtype dt, int Q, int N);
