@@ -98,6 +98,18 @@ def test_fwd_rejects_invalid_arguments(lib, kw, code):
     assert call_fwd(lib, **kw) == code
 
 
+@pytest.mark.parametrize("kw", [
+    dict(b=1, T=1 << 41),          # more tokens than the index arithmetic allows
+    dict(b=1 << 31, T=2),          # more sequences than the grids allow
+    dict(b=1 << 20, T=1 << 21),    # b * T beyond 2^40
+    dict(H=1 << 30, G=1),          # chunk slots x heads beyond a 32-bit grid
+])
+def test_fwd_rejects_oversized_problems(lib, kw):
+    """Sizes past what the kernels index with their integer widths are refused on
+    the host, before any allocation or launch."""
+    assert call_fwd(lib, **kw) == INVALID
+
+
 def test_varlen_rejects_invalid_arguments(lib):
     # null cu_seqlens with sequences
     assert lib.ssd_chunked_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 100, 4, 64, 128, 1,
