@@ -2,8 +2,8 @@
 
 Argument marshalling only: shapes and dtypes are checked, outputs allocated
 with torch on the input's device, and the C entry point is called on torch's
-current stream.  Every step of the forward pass runs in the library's HIP
-kernels; there is no fallback of any kind.
+current stream.  Every step of the forward, backward and decode passes runs
+in the library's HIP kernels; there is no fallback of any kind.
 """
 from __future__ import annotations
 

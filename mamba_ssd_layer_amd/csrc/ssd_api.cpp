@@ -1,12 +1,14 @@
 // ssd_api.cpp -- the C ABI of libssd.so (declared in include/ssd.h).
 //
 // Host side only: argument validation (before any HIP call), workspace
-// layout, the launch sequence of the five kernels on the caller's stream, and
-// the optional per-kernel event timing.  The sequence follows the four steps of
-// the block decomposition in "LLM(十一)——Mamba" (mztchaoqun.com.cn) §3.5.2
-// "SSD algorithm: chunking and state passing", with the chunk tables first:
+// layout, the launch sequences on the caller's stream, and the optional
+// per-kernel event timing.  The forward follows the four steps of the block
+// decomposition in "LLM(十一)——Mamba" (mztchaoqun.com.cn) §3.5.2 "SSD
+// algorithm: chunking and state passing", with the chunk tables first:
 //   [K0 sequence table, varlen only] -> K1+K3 chunk cumsum and chunk states ->
 //   K4 state passing -> K2+K5 diagonal blocks fused with state-to-output.
+// The decode step is one kernel (K6); the backward is glue (K7) around four
+// runs of the forward sequence on rearranged inputs.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
