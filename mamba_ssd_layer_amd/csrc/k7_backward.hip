@@ -157,13 +157,13 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_kernel(BwdProblem b) {
     } else {
       *cbv = xv;
     }
-    if constexpr (E::kBytes == 2) {  // fp32 inputs of the recompute and reversed passes
+    if (E::kBytes == 2 && !b.chunked_dl) {  // fp32 inputs of the recompute and reversed passes
       const uint4 dyv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.dy) + t * H * P)[v];
       store_f32x8(const_cast<float*>(b.x32) + t * H * P + v * 8, xv);
       store_f32x8(const_cast<float*>(b.xr32) + f * H * P + v * 8, dyv);
     }
   }
-  if constexpr (E::kBytes == 2) {
+  if (E::kBytes == 2 && !b.chunked_dl) {
     for (int v = tid; v < G * N / VEC; v += kBwThreads) {
       const uint4 bv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.B) + t * G * N)[v];
       const uint4 cv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.C) + t * G * N)[v];
@@ -291,80 +291,6 @@ __global__ __launch_bounds__(kBwThreads) void bwd_reduce_kernel(BwdProblem b) {
 // Per (token, head): dx = dx' (times dt with the dt-scaled input) + D dy, and
 // the per-token terms of d(ell), d(dt), dD, stored head-major (H, Ttot).
 // Eight lanes share one head row (8 values each); one workgroup per token.
-template <class E>
-__global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
-  using T = typename E::storage;
-  constexpr int VEC = 16 / sizeof(T);
-  __shared__ float cbs[kMaxBwdGroups];
-  const int64_t t = blockIdx.x;
-  const int H = b.H, P = b.P, N = b.N, G = b.G;
-  const int hpg = H / G;
-  const TokSeq q = token_seq(b, t);
-  const int64_t f = q.t0 + (q.L - 1 - (t - q.t0));
-  // c_g = C_t . B_t per group: the weight of each token's own term
-  {
-    const int wid = threadIdx.x / 64, lane = threadIdx.x % 64;
-    for (int g = wid; g < G; g += kBwThreads / 64) {
-      float acc = 0.0f;
-      for (int n = lane; n < N; n += 64)
-        acc += ld_e<E>(b.C, (t * G + g) * N + n) * ld_e<E>(b.B, (t * G + g) * N + n);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      if (lane == 0) cbs[g] = acc;
-    }
-    __syncthreads();
-  }
-  const int lane8 = threadIdx.x % 8;  // eight lanes per head row, 8 values each
-  for (int h = threadIdx.x / 8; h < H; h += kBwThreads / 8) {
-    const float dth = b.dt[t * H + h];
-    const float sx = b.x_times_dt ? dth : 1.0f;
-    const float dh = b.D != nullptr ? b.D[h] : 0.0f;
-    const float cg = cbs[h / hpg];
-    const int64_t o = (t * H + h) * P + lane8 * 8;
-    const int64_t orev = (f * H + h) * P + lane8 * 8;  // dx' comes reversed
-    float xv[8], dyv[8], yv[8], dxs[8], dx[8];
-#pragma unroll
-    for (int c = 0; c < 8 / VEC; ++c) {
-      unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.x) + o + c * VEC),
-                    *reinterpret_cast<float(*)[VEC]>(xv + c * VEC));
-      unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.dy) + o + c * VEC),
-                    *reinterpret_cast<float(*)[VEC]>(dyv + c * VEC));
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const float4 a = reinterpret_cast<const float4*>(b.y_f + o)[c];
-      const float4 d = reinterpret_cast<const float4*>(b.y_x + orev)[c];
-      yv[4 * c] = a.x; yv[4 * c + 1] = a.y; yv[4 * c + 2] = a.z; yv[4 * c + 3] = a.w;
-      dxs[4 * c] = d.x; dxs[4 * c + 1] = d.y; dxs[4 * c + 2] = d.z; dxs[4 * c + 3] = d.w;
-    }
-    // with the own terms left out of y and dx', d(Acs_t) = dy . y - x' . dx'
-    // has nothing that cancels itself; dx' = dx's + c_g dy exactly
-    float s_dyy = 0.0f, s_xdx = 0.0f, s_xdy = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      s_dyy += dyv[k] * yv[k];
-      s_xdx += xv[k] * dxs[k];
-      s_xdy += xv[k] * dyv[k];
-      dx[k] = sx * (dxs[k] + cg * dyv[k]) + dh * dyv[k];
-    }
-#pragma unroll
-    for (int c = 0; c < 8 / VEC; ++c)
-      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.dx) + o + c * VEC) =
-          pack_vec<E>(*reinterpret_cast<float(*)[VEC]>(dx + c * VEC));
-#pragma unroll
-    for (int off = 4; off >= 1; off >>= 1) {
-      s_dyy += __shfl_xor(s_dyy, off);
-      s_xdx += __shfl_xor(s_xdx, off);
-      s_xdy += __shfl_xor(s_xdy, off);
-    }
-    if (lane8 == 0) {
-      b.qd[h * b.total + t] = s_dyy - sx * s_xdx;      // d(Acs_t)
-      b.rd[h * b.total + t] = s_xdx + cg * s_xdy;      // x . dx' (full): d(dt) term of the dt-scaled input
-      b.ud[h * b.total + t] = s_xdy;                   // x . dy (dD term)
-    }
-  }
-}
-
 // Block-wide sum of v over the 256 threads (result valid in every thread).
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
@@ -388,6 +314,110 @@ __device__ __forceinline__ void seq_range(const BwdProblem& b, int64_t s, int64_
   } else {
     *t0 = min(max((int64_t)b.cu[s], (int64_t)0), b.total);
     *L = max(min((int64_t)b.cu[s + 1], b.total) - *t0, (int64_t)0);
+  }
+}
+
+template <class E>
+__global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
+  using T = typename E::storage;
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float cbs[kMaxBwdGroups];
+  const int64_t t = blockIdx.x;
+  const int H = b.H, P = b.P, N = b.N, G = b.G;
+  const int hpg = H / G;
+  const TokSeq q = token_seq(b, t);
+  const int64_t f = q.t0 + (q.L - 1 - (t - q.t0));
+  // c_g = C_t . B_t per group: the weight of each token's own term, which the
+  // fp32 passes leave out of y and dx' (the chunk-local d(ell) path keeps it)
+  if (!b.chunked_dl) {
+    const int wid = threadIdx.x / 64, lane = threadIdx.x % 64;
+    for (int g = wid; g < G; g += kBwThreads / 64) {
+      float acc = 0.0f;
+      for (int n = lane; n < N; n += 64)
+        acc += ld_e<E>(b.C, (t * G + g) * N + n) * ld_e<E>(b.B, (t * G + g) * N + n);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0) cbs[g] = acc;
+    }
+    __syncthreads();
+  }
+  const int lane8 = threadIdx.x % 8;  // eight lanes per head row, 8 values each
+  for (int h = threadIdx.x / 8; h < H; h += kBwThreads / 8) {
+    const float dth = b.dt[t * H + h];
+    const float sx = b.x_times_dt ? dth : 1.0f;
+    const float dh = b.D != nullptr ? b.D[h] : 0.0f;
+    const float cg = b.chunked_dl ? 0.0f : cbs[h / hpg];
+    const int64_t o = (t * H + h) * P + lane8 * 8;
+    const int64_t orev = (f * H + h) * P + lane8 * 8;  // dx' comes reversed
+    float xv[8], dyv[8], yv[8] = {}, dxs[8], dx[8];
+#pragma unroll
+    for (int c = 0; c < 8 / VEC; ++c) {
+      unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.x) + o + c * VEC),
+                    *reinterpret_cast<float(*)[VEC]>(xv + c * VEC));
+      unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.dy) + o + c * VEC),
+                    *reinterpret_cast<float(*)[VEC]>(dyv + c * VEC));
+    }
+    if (b.chunked_dl) {
+      // dx' from the element-dtype reversed pass (own terms included)
+#pragma unroll
+      for (int c = 0; c < 8 / VEC; ++c)
+        unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.y_x8) + orev + c * VEC),
+                      *reinterpret_cast<float(*)[VEC]>(dxs + c * VEC));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float4 a = reinterpret_cast<const float4*>(b.y_f + o)[c];
+        const float4 d = reinterpret_cast<const float4*>(b.y_x + orev)[c];
+        yv[4 * c] = a.x; yv[4 * c + 1] = a.y; yv[4 * c + 2] = a.z; yv[4 * c + 3] = a.w;
+        dxs[4 * c] = d.x; dxs[4 * c + 1] = d.y; dxs[4 * c + 2] = d.z; dxs[4 * c + 3] = d.w;
+      }
+    }
+    // without the own terms in y and dx', d(Acs_t) = dy . y - x' . dx' has
+    // nothing that cancels itself; dx' = dx's + c_g dy exactly
+    float s_dyy = 0.0f, s_xdx = 0.0f, s_xdy = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s_dyy += dyv[k] * yv[k];
+      s_xdx += xv[k] * dxs[k];
+      s_xdy += xv[k] * dyv[k];
+      dx[k] = sx * (dxs[k] + cg * dyv[k]) + dh * dyv[k];
+    }
+#pragma unroll
+    for (int c = 0; c < 8 / VEC; ++c)
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.dx) + o + c * VEC) =
+          pack_vec<E>(*reinterpret_cast<float(*)[VEC]>(dx + c * VEC));
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+      s_dyy += __shfl_xor(s_dyy, off);
+      s_xdx += __shfl_xor(s_xdx, off);
+      s_xdy += __shfl_xor(s_xdy, off);
+    }
+    if (lane8 == 0) {
+      if (!b.chunked_dl) b.qd[h * b.total + t] = s_dyy - sx * s_xdx;  // d(Acs_t)
+      b.rd[h * b.total + t] = s_xdx + cg * s_xdy;  // x . dx' (full): d(dt) term of the dt-scaled input
+      b.ud[h * b.total + t] = s_xdy;               // x . dy (dD term)
+    }
+  }
+}
+
+// dD (chunk-local d(ell) path): per (sequence, head) the sum of x . dy, and
+// dh0 = a_first G_first.
+__global__ __launch_bounds__(kBwThreads) void bwd_seqsum_kernel(BwdProblem b) {
+  __shared__ float red[kBwThreads / 64];
+  const int64_t sh = blockIdx.x;
+  const int h = (int)(sh % b.H);
+  int64_t t0, L;
+  seq_range(b, sh / b.H, &t0, &L);
+  const int64_t PN = (int64_t)b.P * b.N;
+  if (b.dinit != nullptr) {
+    const float a0 = L > 0 ? __expf(b.dt[t0 * b.H + h] * b.A[h]) : 1.0f;
+    for (int64_t i = threadIdx.x; i < PN; i += kBwThreads) b.dinit[sh * PN + i] = a0 * b.g0[sh * PN + i];
+  }
+  if (b.dD != nullptr) {
+    float acc = 0.0f;
+    for (int64_t i = threadIdx.x; i < L; i += kBwThreads) acc += b.ud[h * b.total + t0 + i];
+    acc = block_sum(acc, red);
+    if (threadIdx.x == 0) atomicAdd(b.dD + h, acc);
   }
 }
 
@@ -503,7 +533,14 @@ static hipError_t launch_glue(const BwdProblem& b, int stage, hipStream_t s) {
         hipLaunchKernelGGL((bwd_reduce_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
         hipLaunchKernelGGL((bwd_token_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
       }
-      if (b.nseq > 0) {
+      if (b.chunked_dl) {
+        if (b.total > 0) {
+          const hipError_t e = launch_backward_dl(b, s);
+          if (e != hipSuccess) return e;
+        }
+        if (b.nseq > 0 && (b.dD != nullptr || b.dinit != nullptr))
+          hipLaunchKernelGGL(bwd_seqsum_kernel, dim3((unsigned)(b.nseq * b.H)), blk, 0, s, b);
+      } else if (b.nseq > 0) {
         const dim3 grid((unsigned)(b.nseq * b.H * b.nseg));
         hipLaunchKernelGGL(bwd_segsum_kernel, grid, blk, 0, s, b);
         hipLaunchKernelGGL(bwd_scan_kernel, grid, blk, 0, s, b);

@@ -217,6 +217,8 @@ struct DebugOut {
   float* acs = nullptr;
   float* states = nullptr;
   float* hin = nullptr;
+  bool states_only = false;  // stop after the state passing (no y)
+  void* hin_buf = nullptr;   // keep the passed states here (element dtype, (kmax, H, P, N))
 };
 
 // ------------------------------------------------------------ workspace ----
@@ -278,6 +280,7 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
   if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
   Workspace ws;
   workspace_layout(p, base, &ws);
+  if (dbg && dbg->hin_buf) ws.hin = dbg->hin_buf;
   hipError_t e = hipSuccess;
   const size_t KH = (size_t)p.kmax * p.H;
   do {
@@ -295,7 +298,8 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
         if (e != hipSuccess) break;
       }
     }
-    if (p.kmax > 0 && chunk_output_reads_cb(p.dtype, p.Q, p.N)) {
+    const bool states_only = dbg != nullptr && dbg->states_only;
+    if (p.kmax > 0 && !states_only && chunk_output_reads_cb(p.dtype, p.Q, p.N)) {
       e = timed_launch(kK2ChunkCB, stream, [&] { return launch_chunk_cb(p, ws, stream); });
       if (e != hipSuccess) break;
     }
@@ -303,7 +307,7 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
       return launch_state_pass(p, ws, dbg ? dbg->hin : nullptr, stream);
     });
     if (e != hipSuccess) break;
-    if (p.kmax > 0) {
+    if (p.kmax > 0 && !states_only) {
       e = timed_launch(kK25ChunkOutput, stream, [&] { return launch_chunk_output(p, ws, stream); });
       if (e != hipSuccess) break;
     }
@@ -492,6 +496,18 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
       break;
     }
   if (Q2 == 0 || Qf == 0 || ngroups > kMaxBwdGroups) return SSD_ERR_UNSUPPORTED;
+  // Chunk-local d(ell) for bf16 inputs when every sequence is a whole number
+  // of chunks of a built length Qd (then the reversed pass's chunks coincide
+  // with the forward's): its passes run in bf16, and no fp32 recompute or
+  // reversed pass is needed.
+  int Qd = 0;
+  if (cu_seqlens == nullptr && seqlen > 0)
+    for (int q : {chunk_len, 256, 128, 64})
+      if (seqlen % q == 0 && backward_dl_supported(p.dtype, q, dstate) && config_supported(p.dtype, q, dstate)) {
+        Qd = q;
+        break;
+      }
+  const bool cdl = Qd > 0;
   const bool bf16 = dtype == SSD_DTYPE_BF16;
   st = check_device();
   if (st != SSD_OK) return st;
@@ -500,6 +516,9 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   const int H = nheads, P = headdim, N = dstate, G = ngroups;
   const int NK = (N + 63) / 64, W = 64 * NK;
   const size_t T = (size_t)total_len, S = (size_t)nseqs, e = dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  const size_t Kd = cdl ? T / Qd : 0;                   // chunks of the d(ell) path
+  const bool f32c = bf16 && !cdl;                       // fp32 copies of the inputs
+  const bool fpass = !cdl;                              // fp32 recompute and reversed passes
   size_t off = 0;
   char* base = nullptr;
   auto take = [&](size_t bytes) {
@@ -528,23 +547,30 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
     b.cb = take(T * H * P * e);
     b.h0c = reinterpret_cast<float*>(take(initial_state ? S * H * NK * 4096 * 4 : 0));
     b.dfb = reinterpret_cast<float*>(take(dfinal_state ? S * H * NK * 4096 * 4 : 0));
-    b.x32 = reinterpret_cast<float*>(take(bf16 ? T * H * P * 4 : 0));
-    b.xr32 = reinterpret_cast<float*>(take(bf16 ? T * H * P * 4 : 0));
-    b.B32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
-    b.C32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
-    b.Br32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
-    b.Cr32 = reinterpret_cast<float*>(take(bf16 ? T * G * N * 4 : 0));
-    b.y_f = reinterpret_cast<float*>(take(T * H * P * 4));
-    b.hlast = reinterpret_cast<float*>(take(dfinal_state ? S * H * P * N * 4 : 0));
-    b.y_x = reinterpret_cast<float*>(take(T * H * P * 4));
+    b.x32 = reinterpret_cast<float*>(take(f32c ? T * H * P * 4 : 0));
+    b.xr32 = reinterpret_cast<float*>(take(f32c ? T * H * P * 4 : 0));
+    b.B32 = reinterpret_cast<float*>(take(f32c ? T * G * N * 4 : 0));
+    b.C32 = reinterpret_cast<float*>(take(f32c ? T * G * N * 4 : 0));
+    b.Br32 = reinterpret_cast<float*>(take(f32c ? T * G * N * 4 : 0));
+    b.Cr32 = reinterpret_cast<float*>(take(f32c ? T * G * N * 4 : 0));
+    b.y_f = reinterpret_cast<float*>(take(fpass ? T * H * P * 4 : 0));
+    b.hlast = reinterpret_cast<float*>(take(fpass && dfinal_state ? S * H * P * N * 4 : 0));
+    b.y_x = reinterpret_cast<float*>(take(fpass ? T * H * P * 4 : 0));
+    b.y_x8 = take(cdl ? T * H * P * e : 0);
+    b.hin_e = take(Kd * H * P * N * e);
+    b.gin_e = take(Kd * H * P * N * e);
+    b.dl_v = reinterpret_cast<float*>(take(cdl ? T * H * 4 : 0));
+    b.dl_cols = reinterpret_cast<float*>(take(cdl ? 2 * T * H * 4 : 0));
+    b.dl_u = reinterpret_cast<float*>(take(cdl ? T * H * 4 : 0));
+    b.dl_kc = reinterpret_cast<float*>(take(Kd * H * 4));
     b.g0 = reinterpret_cast<float*>(take(dinitial_state ? S * H * P * N * 4 : 0));
     b.y_c = take(T * H * W * e);
     b.y_b = take(T * H * W * e);
-    b.qd = reinterpret_cast<float*>(take(T * H * 4));
+    b.qd = reinterpret_cast<float*>(take(fpass ? T * H * 4 : 0));
     b.rd = reinterpret_cast<float*>(take(T * H * 4));
     b.ud = reinterpret_cast<float*>(take(T * H * 4));
-    b.segsum = reinterpret_cast<double*>(take(S * H * (size_t)nseg * 8));
-    b.edot = reinterpret_cast<float*>(take(S * H * 4));
+    b.segsum = reinterpret_cast<double*>(take(fpass ? S * H * (size_t)nseg * 8 : 0));
+    b.edot = reinterpret_cast<float*>(take(fpass ? S * H * 4 : 0));
   };
   layout();
   int dev = 0;
@@ -560,6 +586,7 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   b.dx = dx; b.ddt = ddt; b.dA = dA; b.dB = dB; b.dC = dC; b.dD = dD; b.dinit = dinitial_state;
   b.nseq = nseqs; b.seqlen = seqlen; b.total = total_len;
   b.H = H; b.P = P; b.N = N; b.G = G; b.NK = NK; b.dtype = p.dtype;
+  b.chunked_dl = cdl; b.Q = Qd;
   if (!bf16) {
     b.x32 = static_cast<const float*>(x);
     b.B32 = static_cast<const float*>(B);
@@ -572,6 +599,29 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   hipError_t err = timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 0, s); });
   if (err != hipSuccess) return map_err(err);
   if (nseqs == 0) return SSD_OK;
+  if (cdl) {
+    // passed states of the forward (fp32 copies of the stored values)
+    Problem pf = make_problem(x, dt, A_head, B, C, nullptr, nseqs, seqlen, total_len, H, P, N, G, Qd, dtype,
+                              dx, nullptr, initial_state, nullptr, x_times_dt);
+    // reversed pass in the element dtype: dx' (own terms in), its passed states
+    // (the adjoint after each chunk) and G_first
+    Problem px = make_problem(b.xr, b.dtr, A_head, b.Br, b.Cr, nullptr, nseqs, seqlen, total_len, H, P, N, G,
+                              Qd, dtype, const_cast<void*>(b.y_x8), b.g0, dfinal_state, nullptr, 0);
+    Problem pc = make_problem(b.xc, b.dtc, b.Ac, x, dy, nullptr, nseqs, seqlen, total_len, H * NK, kHeadDim, P,
+                              H, Q2, dtype, b.y_c, nullptr, b.h0c, nullptr, x_times_dt);
+    Problem pb = make_problem(b.xb, b.dtb, b.Ac, b.xr, b.cb, nullptr, nseqs, seqlen, total_len, H * NK,
+                              kHeadDim, P, H, Q2, dtype, b.y_b, nullptr, b.dfb, nullptr, 0);
+    DebugOut df, dxo;
+    df.hin_buf = const_cast<void*>(b.hin_e);
+    df.states_only = true;
+    dxo.hin_buf = const_cast<void*>(b.gin_e);
+    for (auto [q, d] : {std::pair<const Problem*, const DebugOut*>{&pf, &df}, {&px, &dxo}, {&pc, nullptr},
+                        {&pb, nullptr}}) {
+      st = run(*q, s, d);
+      if (st != SSD_OK) return st;
+    }
+    return map_err(timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 1, s); }));
+  }
   // forward recompute (fp32): y without the skip term and the own terms, final state
   Problem pf = make_problem(b.x32, dt, A_head, b.B32, b.C32, cu_seqlens, nseqs, seqlen, total_len, H, P, N,
                             G, Qf, SSD_DTYPE_F32, b.y_f, b.hlast, initial_state, nullptr, x_times_dt, 1);

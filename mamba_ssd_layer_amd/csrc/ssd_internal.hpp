@@ -101,6 +101,16 @@ struct BwdProblem {
   float* y_x; float* g0;       // reversed pass: dx' without own term (reversed order); G_first
   void* y_c; void* y_b;        // (Ttot, H*NK, 64) per-head parts of dC and (reversed) dB
   float* qd; float* rd; float* ud;  // (H, Ttot) fp32 per-token terms
+  // chunk-local d(ell) (bf16, every sequence a whole number of chunks of Q): the
+  // forward's and the reversed pass's passed states as those passes store them
+  bool chunked_dl;
+  int Q;
+  const void* hin_e; const void* gin_e;   // (K, H, P, N) element dtype
+  const void* y_x8;            // reversed pass in the element dtype: dx' (own terms in), reversed order
+  float* dl_v;                 // (H, Ttot) row sums of W + yterm
+  float* dl_cols;              // (2, H, Ttot) column sums of W, per workgroup of the chunk
+  float* dl_u;                 // (H, Ttot) dterm
+  float* dl_kc;                // (K, H) <Gout, exp(Lam) Hin>
   int nseg;                    // scan segments per (sequence, head): ceil(longest sequence / kBwdScanSeg)
   double* segsum;              // (S, H, nseg) fp64 segment sums of d(Acs)
   float* edot;                 // (S, H) <dfinal, h_last>
@@ -161,6 +171,9 @@ hipError_t launch_decode_step(const DecodeProblem& d, hipStream_t s);
 // K7 backward glue: stage 0 builds the gradient passes' inputs (and zeroes dA,
 // dD), stage 1 turns their outputs into dx, dB, dC, d(dt), dA, dD, dh0.
 hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);
+// K8: chunk-local d(ell) -> d(dt), dA (BwdProblem::chunked_dl).
+hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s);
+bool backward_dl_supported(Dtype dt, int Q, int N);
 bool chunk_state_supported(Dtype dt, int Q, int N);
 bool chunk_output_supported(Dtype dt, int Q, int N);
 // Whether the chunk-output kernel for (dtype, Q, N) reads the kernel-matrix pass's
