@@ -22,6 +22,8 @@ The map, its forms and its gradients, all fp64:
   quadratic()      O2, the dual form Y = (L o C B^T) X of [T] §2.4 and [M]
                    §3.1.3 with L the 1-semiseparable matrix of [T] §3.2.2, by
                    brute force; tiny inputs only.
+  selective_scan() O5, the comparator: the selective scan with a diagonal
+                   transition of Mamba-1 ([M] §3.1.1-3.1.2, §2.1.2-2.1.3), in C.
   chunked_steps()  O3, the four steps of the block decomposition of [M] §3.5
                    ("SSD algorithm: chunking and state passing"), exposing the
                    per-chunk log-decay cumsum, chunk states and passed states
@@ -75,6 +77,10 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp,
             dp, dp, dp, dp, ctypes.c_int]
         lib.ssd_oracle_backward.restype = ctypes.c_int
+        lib.ssd_oracle_selective_scan.argtypes = [
+            dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, dp, dp, ctypes.c_int]
+        lib.ssd_oracle_selective_scan.restype = ctypes.c_int
         lib.ssd_oracle_max_threads.argtypes = []
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -213,6 +219,32 @@ def backward(x, dt, A, B, C, dy, cu_seqlens=None, init_state=None, dfinal=None, 
     dC = dCh.reshape(Ttot, G, hpg, N).sum(axis=2)
     return dict(dx=dx.reshape(*lead, H, P), ddt=ddt.reshape(np.shape(dt)), dA=dA.sum(axis=0),
                 dB=dB.reshape(np.shape(B)), dC=dC.reshape(np.shape(C)), dD=dD, dinit=dinit)
+
+
+def selective_scan(x, delta, A, B, C, nthreads=0):
+    """O5: fp64 selective scan with a diagonal transition (Mamba-1's S6), the
+    comparator of the SSD layer ([M] §3.1.1-3.1.2: a diagonal A, of which SSD
+    keeps one scalar; §2.1.2-2.1.3: one SSM per channel, Delta per token and
+    channel, B and C per token).  h_t = exp(Delta_t A) o h_{t-1} + Delta_t x_t B_t
+    per channel (state N), y_t = C_t . h_t, zero state per sequence.
+
+    x, delta (b, T, D); A (D, N); B, C (b, T, N).  Returns y (b, T, D) and the
+    final state (b, D, N), fp64.
+    """
+    x = _f64(x)
+    nb, T, D = x.shape
+    N = A.shape[-1]
+    delta = _f64(delta).reshape(nb, T, D)
+    A = _f64(A).reshape(D, N)
+    B = _f64(B).reshape(nb, T, N)
+    C = _f64(C).reshape(nb, T, N)
+    y = np.empty((nb, T, D), dtype=np.float64)
+    fs = np.empty((nb, D, N), dtype=np.float64)
+    rc = _load().ssd_oracle_selective_scan(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                           nb, T, D, N, _ptr(y), _ptr(fs), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return y, fs
 
 
 def quadratic(x, dt, A, B, C):

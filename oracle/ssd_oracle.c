@@ -272,3 +272,61 @@ int ssd_oracle_backward(const double *x, const double *dt, const double *A,
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Selective scan with a diagonal transition (Mamba-1's S6 layer), the
+ * comparator of the SSD layer: [M] §3.1.1 (diagonal structure, A stored as its
+ * N diagonal entries), §3.1.2 (SSD restricts that diagonal to one scalar) and
+ * §2.1.2-2.1.3 (an independent SSM per channel d of D, step size Delta per
+ * token and channel, B and C per token shared by the channels).  With
+ * a_t[d][n] = exp(Delta_t[d] * A[d][n]) and the first-order input term:
+ *       h_t[d][n] = a_t[d][n] * h_{t-1}[d][n] + Delta_t[d] * B_t[n] * x_t[d]
+ *       y_t[d]    = sum_n C_t[n] * h_t[d][n]
+ * from a zero state at the start of every sequence.  SSD with the dt-scaled
+ * input is the special case A[d][n] = A_h for every n and Delta_t[d] = dt_t[h]
+ * for the channels d of head h.
+ * Layouts: x, Delta (b, T, D); A (D, N); B, C (b, T, N); y (b, T, D);
+ * final_state (b, D, N) or NULL.  Returns 0, or -1 on bad sizes.
+ * OpenMP over the independent (sequence, channel) pairs.
+ */
+int ssd_oracle_selective_scan(const double *x, const double *delta, const double *A,
+                              const double *B, const double *C, int64_t nbatch,
+                              int64_t T, int64_t D, int64_t N, double *y,
+                              double *final_state, int nthreads)
+{
+    if (nbatch < 0 || T < 0 || D <= 0 || N <= 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int64_t pairs = nbatch * D;
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)N * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t q = 0; q < pairs; ++q) {
+            const int64_t b = q / D, d = q % D;
+            for (int64_t n = 0; n < N; ++n)
+                h[n] = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t tok = b * T + t;
+                const double dl = delta[tok * D + d];
+                const double u = dl * x[tok * D + d];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    h[n] = exp(dl * A[d * N + n]) * h[n] + u * B[tok * N + n];
+                    acc += C[tok * N + n] * h[n];
+                }
+                y[tok * D + d] = acc;
+            }
+            if (final_state)
+                for (int64_t n = 0; n < N; ++n)
+                    final_state[(b * D + d) * N + n] = h[n];
+        }
+        free(h);
+    }
+    return 0;
+}

@@ -374,3 +374,70 @@ def test_backward_a_zero_is_diagonal():
     assert relerr(g["dC"], s[:, None, None] * B) < 1e-14
     assert relerr(g["dB"], s[:, None, None] * C) < 1e-14
     assert np.all(g["ddt"] == 0)
+
+
+# --------------------------------------------------------------------------
+# O5 (selective scan with a diagonal transition, the comparator), [M] §3.1.1-
+# 3.1.2 and §2.1.2-2.1.3
+# --------------------------------------------------------------------------
+def scan_case(rng, nb, T, D, N):
+    x = rng.standard_normal((nb, T, D))
+    delta = np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), size=(nb, T, D)))
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), size=(D, N)))
+    B = rng.standard_normal((nb, T, N))
+    C = rng.standard_normal((nb, T, N))
+    return x, delta, A, B, C
+
+
+def test_selective_scan_scalar_diagonal_is_ssd():
+    """With every diagonal entry of a channel's A equal to its head's A_h and
+    Delta the head's step size, the diagonal SSM is SSD ([M] §3.1.2) with the
+    dt-scaled input: the two oracles agree (O1 is pinned on its own above)."""
+    rng = np.random.default_rng(50)
+    nb, T, H, P, N = 2, 37, 3, 4, 5
+    x, dt, A, B, C = rand_case(rng, nb * T, H, P, N, 1)
+    x = x.reshape(nb, T, H, P)
+    dt = dt.reshape(nb, T, H)
+    B = B.reshape(nb, T, 1, N)
+    C = C.reshape(nb, T, 1, N)
+    y_ssd, fs_ssd = oracle.recurrence(x, dt, A, B, C, x_times_dt=True)
+    delta = np.repeat(dt[..., None], P, axis=-1).reshape(nb, T, H * P)
+    Ad = np.repeat(A[:, None], P * N).reshape(H * P, N)
+    y, fs = oracle.selective_scan(x.reshape(nb, T, H * P), delta, Ad, B[:, :, 0], C[:, :, 0])
+    assert relerr(y, y_ssd.reshape(nb, T, H * P)) < 1e-13
+    assert relerr(fs, fs_ssd.reshape(nb, H * P, N)) < 1e-13
+
+
+def test_selective_scan_a_zero_is_prefix_sum():
+    """A = 0 (no decay): h_t = sum_{s<=t} Delta_s x_s B_s, so y_t = C_t . that
+    (a closed form by cumulative sums)."""
+    rng = np.random.default_rng(51)
+    x, delta, A, B, C = scan_case(rng, 2, 30, 3, 4)
+    A = np.zeros_like(A)
+    y, fs = oracle.selective_scan(x, delta, A, B, C)
+    h = np.cumsum((delta * x)[..., None] * B[:, :, None, :], axis=1)  # (b, T, D, N)
+    assert relerr(y, np.einsum("btn,btdn->btd", C, h)) < 1e-13
+    assert relerr(fs, h[:, -1]) < 1e-13
+
+
+def test_selective_scan_brute_force_per_state():
+    """Brute force by explicit products: y_t[d] = sum_n C_t[n] sum_{s<=t}
+    (prod_{s<r<=t} exp(Delta_r[d] A[d,n])) Delta_s[d] B_s[n] x_s[d].  Distinct
+    decays per state entry make a wrong n index or a shared decay fail."""
+    rng = np.random.default_rng(52)
+    nb, T, D, N = 1, 9, 2, 3
+    x, delta, A, B, C = scan_case(rng, nb, T, D, N)
+    y, _ = oracle.selective_scan(x, delta, A, B, C)
+    ref = np.zeros((nb, T, D))
+    for b in range(nb):
+        for d in range(D):
+            for t in range(T):
+                acc = 0.0
+                for n in range(N):
+                    for s in range(t + 1):
+                        w = 1.0
+                        for r in range(s + 1, t + 1):
+                            w *= math.exp(delta[b, r, d] * A[d, n])
+                        acc += C[b, t, n] * w * delta[b, s, d] * B[b, s, n] * x[b, s, d]
+                ref[b, t, d] = acc
+    assert relerr(y, ref) < 1e-13
