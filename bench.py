@@ -12,8 +12,11 @@ The fp64 CPU oracle is timed on the host cores on the same workload (rank 0)
 and its output also checks the GPU result.  The line also carries, under
 "decode", one recurrent decode step (ssd_decode_step) on 64 sequences of a
 Mamba-2-2.7B-like layer (H=80, N=128), with its own HBM roofline
-(--no-decode skips it), and under "backward" the gradient pass
-(ssd_chunked_bwd) on the same workload (--no-backward skips it).
+(--no-decode skips it), under "backward" the gradient pass
+(ssd_chunked_bwd) on the same workload (--no-backward skips it), and under
+"comparator" the diagonal selective scan (ssd_selective_scan, Mamba-1's S6) on
+a workload of the same size (one channel per head dimension, the same N and
+dtype) with SSD's speed-up over it (--no-comparator skips it).
 
 Prints ONE JSON line.
 """
@@ -175,6 +178,56 @@ def bench_backward(bd, torch, w, x, dt, A, B, C, cu, steps, warmup):
                          "note": "compulsory bytes over the whole backward call (several launches)"}}
 
 
+# v_exp_f32 runs at a quarter of the fp32 lane rate: 256 CUs x 4 SIMDs x 16
+# lanes / 4 x 2.4 GHz
+PEAK_EXP_GPS = 256 * 4 * 16 / 4 * 2.4
+
+
+def bench_comparator(bd, torch, w, sec_ssd, steps, warmup):
+    """The diagonal selective scan on SSD's workload size: batch and length of
+    the workload, D = nheads * headdim channels, the same dstate and dtype.
+    Its bound is the exp per (token, channel, state entry) on the vector ALU."""
+    import numpy as np
+    from mamba_ssd_layer_amd.workloads import scan_inputs
+    if w.varlen or w.dstate not in (64, 128, 256):
+        return None
+    b, T, D, N = w.batch, w.seqlen, w.nheads * w.headdim, w.dstate
+    x, delta, A, B, C = scan_inputs(b, T, D, N, w.dtype, 0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    xg = torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1))).to(dev).to(tdt)
+    dg = torch.from_numpy(np.ascontiguousarray(delta.transpose(0, 2, 1))).to(dev)
+    Ag = torch.from_numpy(A).to(dev)
+    Bg = torch.from_numpy(B).to(dev).to(tdt)
+    Cg = torch.from_numpy(C).to(dev).to(tdt)
+    del x, delta, B, C
+    y = torch.empty_like(xg)
+    for _ in range(warmup):
+        bd.ssd_selective_scan(xg, dg, Ag, Bg, Cg, y=y, want_final_state=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bd.ssd_selective_scan(xg, dg, Ag, Bg, Cg, y=y, want_final_state=False)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    bd.kernel_timing_read(reset=True)
+    bd.kernel_timing_enable(True)
+    for _ in range(steps):
+        bd.ssd_selective_scan(xg, dg, Ag, Bg, Cg, y=y, want_final_state=False)
+    torch.cuda.synchronize()
+    bd.kernel_timing_enable(False)
+    kms = bd.kernel_timing_read(reset=True)["selective_scan"]
+    kms = kms[0] / kms[1] if kms[1] else None
+    exps = b * T * D * N
+    ach = exps / (kms / 1e3) / 1e9 if kms else None
+    return {"kernel": "selective_scan (diagonal A)", "batch": b, "seqlen": T, "channels": D, "dstate": N,
+            "dtype": w.dtype, "us_per_step": sec * 1e6, "tokens_per_s": b * T / sec,
+            "ssd_speedup": sec / sec_ssd,
+            "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_EXP_GPS, "unit": "Gexp/s",
+                         "frac": ach / PEAK_EXP_GPS if ach else None, "traffic": None,
+                         "avg_launch_ms": kms, "exps_per_launch": exps}}
+
+
 def min_io_bytes(w, total_tokens, nseq):
     e = 2 if w.dtype == "bf16" else 4
     H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
@@ -207,6 +260,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement reported under \"backward\"")
+    ap.add_argument("--no-comparator", action="store_true",
+                    help="skip the selective-scan comparison reported under \"comparator\"")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step measurement reported under \"decode\"")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -344,6 +399,8 @@ def main():
 
     if not args.no_decode:
         result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200))
+    if not args.no_comparator:
+        result["comparator"] = bench_comparator(bd, torch, w, sec, min(args.steps, 20), 3)
     if not args.no_backward:
         result["backward"] = bench_backward(bd, torch, w, x, dt, A, B, C, cu, min(args.steps, 50),
                                             min(args.warmup, 20))

@@ -219,6 +219,31 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, 
                            int32_t x_times_dt, float* state, void* y, void* stream);
 
 /*
+ * The comparator of the SSD layer: a selective scan with a diagonal
+ * transition (Mamba-1's S6; [M] §3.1.1: a diagonal transition stored as its N
+ * entries, of which SSD keeps one scalar, §3.1.2; §2.1.2-2.1.3: one SSM per
+ * channel, step size per token and channel, B and C per token).  For every
+ * sequence b, channel d and state entry n, from a zero state:
+ *     h[n] <- exp(delta[b,d,t] * A[d,n]) h[n] + delta[b,d,t] x[b,d,t] B[b,t,n]
+ *     y[b,d,t] = sum_n C[b,t,n] h[n]
+ * It is not part of the SSD path: it exists to time the pages' speed claim
+ * for SSD against this scan on the same GPU.
+ *   x, y   (batch, channels, seqlen)  element dtype, channel-major; y is
+ *          overwritten (bf16: rounded to nearest even) and must not alias
+ *   delta  (batch, channels, seqlen)  fp32
+ *   A      (channels, dstate)         fp32
+ *   B, C   (batch, seqlen, dstate)    element dtype
+ *   final_state (batch, channels, dstate) fp32, or NULL to skip
+ * dstate in {64, 128, 256}, any channels >= 1 and seqlen >= 0; pointers
+ * aligned to their element size.  Validation, execution and errors as for the
+ * forward; no workspace.  batch == 0 is a no-op.
+ */
+ssd_status ssd_selective_scan(const void* x, const float* delta, const float* A, const void* B,
+                              const void* C, int64_t batch, int64_t seqlen, int32_t channels,
+                              int32_t dstate, ssd_dtype dtype, void* y, float* final_state,
+                              void* stream);
+
+/*
  * The same pass, also copying the intermediates of the block decomposition
  * ([M] §3.5.2 "SSD algorithm: chunking and state passing") into caller
  * buffers, for checking each kernel on its own.  cu_seqlens == NULL selects

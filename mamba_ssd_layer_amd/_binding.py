@@ -38,6 +38,8 @@ SIGNATURES = {
                         ctypes.c_int),
     "ssd_decode_step": ([_vp, _fp, _fp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _fp, _i32, _fp,
                          _vp, _vp], ctypes.c_int),
+    "ssd_selective_scan": ([_vp, _fp, _fp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _fp, _vp],
+                           ctypes.c_int),
     "ssd_chunked_fwd_intermediates": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32,
                                        _i32, _i32, _i32, _i32, _vp, _fp, _fp, _fp, _fp, _vp],
                                       ctypes.c_int),
@@ -50,7 +52,7 @@ SIGNATURES = {
 }
 
 KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb", "decode_step",
-                "backward_glue"]
+                "backward_glue", "selective_scan"]
 
 
 class SSDError(RuntimeError):
@@ -315,6 +317,37 @@ def ssd_decode_step(x, dt, A_head, B, C, state, y=None, D=None, x_times_dt: bool
                                ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_decode_step")
     return y
+
+
+def ssd_selective_scan(x, delta, A, B, C, y=None, want_final_state: bool = True):
+    """The comparator: selective scan with a diagonal transition.  x (b,D,T)
+    and delta (b,D,T) channel-major (delta fp32), A (D,N) fp32, B/C (b,T,N) in
+    x's dtype.  Returns y (b,D,T) in x's dtype and the final state (b,D,N) fp32
+    (None unless want_final_state)."""
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, channels, seqlen)")
+    b, D, T = x.shape
+    N = A.shape[-1]
+    dev = x.device
+    _need(x, "x", x.dtype, dev)
+    _need(delta, "delta", torch.float32, dev)
+    _need(A, "A", torch.float32, dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev)
+    if tuple(delta.shape) != (b, D, T) or tuple(A.shape) != (D, N) or tuple(B.shape) != (b, T, N) or \
+            tuple(C.shape) != (b, T, N):
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, dev)
+        if y.shape != x.shape:
+            raise ValueError("y must have x's shape")
+    fs = torch.empty((b, D, N), dtype=torch.float32, device=dev) if want_final_state else None
+    rc = lib().ssd_selective_scan(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), b, T, D, N,
+                                  _dtype_code(x), _ptr(y), _ptr(fs), ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_selective_scan")
+    return y, fs
 
 
 def ssd_chunked_fwd_intermediates(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None):

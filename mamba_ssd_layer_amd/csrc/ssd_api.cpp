@@ -454,6 +454,36 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, 
   return map_err(timed_launch(kK6DecodeStep, s, [&] { return launch_decode_step(d, s); }));
 }
 
+ssd_status ssd_selective_scan(const void* x, const float* delta, const float* A, const void* B,
+                              const void* C, int64_t batch, int64_t seqlen, int32_t channels,
+                              int32_t dstate, ssd_dtype dtype, void* y, float* final_state,
+                              void* stream) {
+  if (batch < 0 || seqlen < 0 || channels <= 0 || dstate <= 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (dtype != SSD_DTYPE_F32 && dtype != SSD_DTYPE_BF16) return SSD_ERR_INVALID_ARGUMENT;
+  if (!(dstate == 64 || dstate == 128 || dstate == 256)) return SSD_ERR_UNSUPPORTED;
+  // every index (b, d, t) and (b, t, n) stays below 2^40; the grid below 2^31
+  if (batch > 0 && (batch > ((int64_t)1 << 40) / channels || seqlen > ((int64_t)1 << 40) / (batch * channels) ||
+                    seqlen > ((int64_t)1 << 40) / (batch * dstate) || batch * channels > 0x7fffffffLL))
+    return SSD_ERR_INVALID_ARGUMENT;
+  const size_t e = dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  if (batch > 0) {
+    if (!A || !aligned(A, 4) || (final_state && !aligned(final_state, 4))) return SSD_ERR_INVALID_ARGUMENT;
+    if (seqlen > 0) {
+      if (!x || !delta || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+      if (!aligned(x, e) || !aligned(B, e) || !aligned(C, e) || !aligned(y, e) || !aligned(delta, 4))
+        return SSD_ERR_INVALID_ARGUMENT;
+    }
+  }
+  ssd_status st = check_device();
+  if (st != SSD_OK) return st;
+  ScanProblem p;
+  p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.y = y; p.final_state = final_state;
+  p.batch = batch; p.seqlen = seqlen; p.D = channels; p.N = dstate;
+  p.dtype = static_cast<Dtype>(dtype);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return map_err(timed_launch(kK10SelectiveScan, s, [&] { return launch_selective_scan(p, s); }));
+}
+
 ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, const void* B,
                            const void* C, const int32_t* cu_seqlens, int64_t nseqs,
                            int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,

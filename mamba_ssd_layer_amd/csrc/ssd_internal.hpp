@@ -49,6 +49,20 @@ struct Problem {
 };
 
 // One recurrent (decode) step for a batch of sequences.
+// Selective scan with a diagonal transition (the comparator; k10).
+struct ScanProblem {
+  const void* x;         // (batch, D, T) element dtype, channel-major
+  const float* delta;    // (batch, D, T)
+  const float* A;        // (D, N)
+  const void* B;         // (batch, T, N) element dtype
+  const void* C;         // (batch, T, N) element dtype
+  void* y;               // (batch, D, T) element dtype
+  float* final_state;    // (batch, D, N) or nullptr
+  int64_t batch, seqlen;
+  int D, N;
+  Dtype dtype;
+};
+
 struct DecodeProblem {
   const void* x;      // (batch, H, P)  element dtype
   const float* dt;    // (batch, H)
@@ -152,7 +166,8 @@ bool config_supported(Dtype dt, int Q, int N);
 
 // Kernel launchers; each returns the launch status.  Kernel ids for timing.
 enum KernelId { kK0SeqTable = 0, kK13ChunkState = 1, kK4StatePass = 2, kK25ChunkOutput = 3,
-                kK2ChunkCB = 4, kK6DecodeStep = 5, kK7BackwardGlue = 6, kNumKernels = 7 };
+                kK2ChunkCB = 4, kK6DecodeStep = 5, kK7BackwardGlue = 6,
+                kK10SelectiveScan = 7, kNumKernels = 8 };
 // K0 (varlen only): per-sequence first token, length and first chunk slot.
 hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
 // K1 + K3: chunk-local log-decay cumsum (-> acs, lam, dmax), chunk states (-> states);
@@ -168,6 +183,7 @@ hipError_t launch_chunk_cb(const Problem& p, const Workspace& ws, hipStream_t s)
 hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_t s);
 // K6: one recurrent step (decode): state update in place and y.
 hipError_t launch_decode_step(const DecodeProblem& d, hipStream_t s);
+hipError_t launch_selective_scan(const ScanProblem& p, hipStream_t s);
 // K7 backward glue: stage 0 builds the gradient passes' inputs (and zeroes dA,
 // dD), stage 1 turns their outputs into dx, dB, dC, d(dt), dA, dD, dh0.
 hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);

@@ -176,6 +176,24 @@ def initial_states(nseqs: int, nheads: int, headdim: int, dstate: int, seed: int
     return rng.standard_normal((nseqs, nheads, headdim, dstate), dtype=np.float32)
 
 
+def scan_inputs(batch: int, seqlen: int, channels: int, dstate: int, dtype: str, seed: int = 0):
+    """Seeded inputs of the diagonal selective scan (the comparator), drawn like
+    the SSD workloads: x, B, C ~ N(0, 1) (rounded to bf16 when dtype is bf16),
+    the step size log-uniform in [1e-3, 1e-1] per token and channel, and
+    A = -exp(U[0, ln 16]) per (channel, state entry).  Token-major layouts:
+    x and delta (batch, seqlen, channels), A (channels, dstate), B and C
+    (batch, seqlen, dstate), all float32."""
+    rng = np.random.default_rng(seed + 2_000_029)
+    x = rng.standard_normal((batch, seqlen, channels), dtype=np.float32)
+    B = rng.standard_normal((batch, seqlen, dstate), dtype=np.float32)
+    C = rng.standard_normal((batch, seqlen, dstate), dtype=np.float32)
+    delta = np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), (batch, seqlen, channels))).astype(np.float32)
+    A = (-np.exp(rng.uniform(0.0, math.log(16.0), (channels, dstate)))).astype(np.float32)
+    if dtype == "bf16":
+        x, B, C = bf16_round(x), bf16_round(B), bf16_round(C)
+    return x, delta, A, B, C
+
+
 def flops_pages(w: Workload, total_tokens: int, seqlens=None) -> dict:
     """FLOP accountings of one forward pass (no arithmetic of the map itself).
 

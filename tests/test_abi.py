@@ -170,6 +170,32 @@ def test_decode_rejects_invalid_arguments(lib, kw, code):
     assert call_decode(lib, **kw) == code
 
 
+def call_scan(lib, **kw):
+    a = dict(x=FAKE, dl=FAKE, A=FAKE, B=FAKE, C=FAKE, b=2, T=512, D=256, N=128, dtype=1, y=FAKE, fs=None)
+    a.update(kw)
+    return lib.ssd_selective_scan(a["x"], a["dl"], a["A"], a["B"], a["C"], a["b"], a["T"], a["D"],
+                                  a["N"], a["dtype"], a["y"], a["fs"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dl=FAKE + 2), INVALID),      # delta is fp32
+    (dict(x=FAKE + 1), INVALID),       # bf16 elements
+    (dict(dtype=0, B=FAKE + 2), INVALID),
+    (dict(fs=FAKE + 2), INVALID),
+    (dict(A=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(b=-1), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(D=0), INVALID),
+    (dict(dtype=3), INVALID),
+    (dict(N=16), UNSUPPORTED),
+    (dict(N=96), UNSUPPORTED),
+    (dict(b=1 << 20, T=1 << 20), INVALID),  # indices past 2^40
+])
+def test_selective_scan_rejects_invalid_arguments(lib, kw, code):
+    assert call_scan(lib, **kw) == code
+
+
 def test_backward_rejects_invalid_arguments(lib):
     # x dt A B C cu S T H P N G Q dtype h0 D xdt dy dfinal dx ddt dA dB dC dD dinit stream
     base = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 512, 4, 64, 128, 1, 256, 1, None, None, 0,

@@ -616,3 +616,50 @@ def test_backward_full_2k(dev):
     """The backward at the Mamba-2-2.7B-like layer's full size (bf16)."""
     inp = make_inputs(WORKLOADS["mamba2_2p7b_T2k"], 0)
     _check_bwd(inp, dev, 256, TOL["bf16"], "mamba2_2p7b_T2k full bf16", 0)
+
+
+# ------------------------------------------------ selective scan (comparator) ----
+def _scan_gpu(dev, x, delta, A, B, C, dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    cv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    xg = cv(x.transpose(0, 2, 1)).to(tdt)          # channel-major (b, D, T)
+    dg = cv(delta.transpose(0, 2, 1))
+    y, fs = bd.ssd_selective_scan(xg, dg, cv(A), cv(B).to(tdt), cv(C).to(tdt))
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().transpose(0, 2, 1), fs.cpu().numpy()
+
+
+def _scan_check(dev, b, T, D, N, dtype, seed, chans=None):
+    from mamba_ssd_layer_amd.workloads import scan_inputs
+    x, delta, A, B, C = scan_inputs(b, T, D, N, dtype, seed)
+    log(f"[scan] b={b} T={T} D={D} N={N} {dtype} seed={seed}")
+    y, fs = _scan_gpu(dev, x, delta, A, B, C, dtype)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(fs))
+    sel = slice(None) if chans is None else chans   # channels are independent: check a subset
+    yr, fr = oracle.selective_scan(x[:, :, sel], delta[:, :, sel], A[sel], B, C)
+    tol = TOL[dtype]
+    if T > 0:
+        ey = float(np.max(oracle.rel_l2_per_slice(y[:, :, sel], yr, slice_axes=(0, 2))))
+        assert ey <= tol, ey
+    ef = float(np.max(oracle.rel_l2_per_slice(fs[:, sel], fr, slice_axes=(0, 1))))
+    assert ef <= tol or (T == 0 and np.all(fs == 0)), ef
+
+
+@pytest.mark.parametrize("b,T,D,N,dtype", [(2, 200, 6, 64, "f32"), (1, 300, 8, 128, "bf16"),
+                                           (3, 65, 5, 256, "f32"), (2, 64, 3, 128, "f32"),
+                                           (1, 1, 4, 64, "bf16")])
+def test_selective_scan_against_oracle(dev, b, T, D, N, dtype):
+    """The comparator against its oracle: blocks of 64 tokens with a ragged
+    tail, one to four waves per channel, a partial last workgroup."""
+    _scan_check(dev, b, T, D, N, dtype, 90 + T)
+
+
+def test_selective_scan_empty_sequence(dev):
+    """T = 0: no output, the final state is the zero initial state."""
+    _scan_check(dev, 2, 0, 4, 128, "f32", 91)
+
+
+def test_selective_scan_full_shape(dev):
+    """The comparison shape (one 16384-token sequence, 2048 channels = 32 heads
+    of 64, N = 128, bf16), checked on a sample of channels."""
+    _scan_check(dev, 1, 16384, 2048, 128, "bf16", 0, chans=np.array([0, 1, 777, 2047]))
