@@ -22,6 +22,8 @@ The map, its forms and its gradients, all fp64:
   quadratic()      O2, the dual form Y = (L o C B^T) X of [T] §2.4 and [M]
                    §3.1.3 with L the 1-semiseparable matrix of [T] §3.2.2, by
                    brute force; tiny inputs only.
+  normalized()     O6, the output divided by its denominator term M 1 (one
+                   more column of ones on X), [T]/[M] normalisation term.
   selective_scan() O5, the comparator: the selective scan with a diagonal
                    transition of Mamba-1 ([M] §3.1.1-3.1.2, §2.1.2-2.1.3), in C.
   chunked_steps()  O3, the four steps of the block decomposition of [M] §3.5
@@ -219,6 +221,32 @@ def backward(x, dt, A, B, C, dy, cu_seqlens=None, init_state=None, dfinal=None, 
     dC = dCh.reshape(Ttot, G, hpg, N).sum(axis=2)
     return dict(dx=dx.reshape(*lead, H, P), ddt=ddt.reshape(np.shape(dt)), dA=dA.sum(axis=0),
                 dB=dB.reshape(np.shape(B)), dC=dC.reshape(np.shape(C)), dD=dD, dinit=dinit)
+
+
+def normalized(x, dt, A, B, C, cu_seqlens=None, D=None, x_times_dt=False, nthreads=0):
+    """O6: the SSD output normalised by its denominator term ([T]/[M]
+    "Incorporating a Normalization (Denominator) Term", next to the kernel
+    feature maps): the denominator of Y = M X is M 1, found by giving X one
+    more column of ones, (T, P) -> (T, P + 1); the output is the first P
+    columns divided by the last.  The extra column enters the state like x (so
+    it is dt-scaled with the dt-scaled input) from a zero state; the skip term
+    D x is added after the division.  The pages require a positive feature
+    map so that the denominators are positive; callers pass such B and C.
+
+    Layout as recurrence().  Returns (y, final_state, denom) with final_state
+    (S, H, P, N) the state of the P columns of x and denom (Ttot, H)."""
+    x = _f64(x)
+    lead = x.shape[:-2]
+    H, P = x.shape[-2:]
+    ones = np.ones(lead + (H, 1))
+    xe = np.concatenate([x, ones], axis=-1)
+    ye, fse = recurrence(xe, dt, A, B, C, cu_seqlens=cu_seqlens, nthreads=nthreads,
+                         x_times_dt=x_times_dt)
+    denom = ye[..., P]
+    y = ye[..., :P] / denom[..., None]
+    if D is not None:
+        y = y + _f64(D).reshape(H)[:, None] * x
+    return y, fse[..., :P, :], denom.reshape(-1, H)
 
 
 def selective_scan(x, delta, A, B, C, nthreads=0):

@@ -441,3 +441,61 @@ def test_selective_scan_brute_force_per_state():
                         acc += C[b, t, n] * w * delta[b, s, d] * B[b, s, n] * x[b, s, d]
                 ref[b, t, d] = acc
     assert relerr(y, ref) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# O6 (output normalised by the denominator term M 1), [T]/[M] "Incorporating
+# a Normalization (Denominator) Term"
+# --------------------------------------------------------------------------
+def positive_case(rng, T, H, P, N, G):
+    """Inputs with a positive feature map on B and C (the pages' condition for
+    positive denominators)."""
+    x, dt, A, B, C = rand_case(rng, T, H, P, N, G)
+    return x, dt, A, np.abs(B) + 0.05, np.abs(C) + 0.05
+
+
+def test_normalized_ones_input_is_one():
+    """X = 1: every output is M 1 / M 1 = 1."""
+    rng = np.random.default_rng(60)
+    x, dt, A, B, C = positive_case(rng, 50, 3, 4, 5, 1)
+    y, _, d = oracle.normalized(np.ones_like(x), dt, A, B, C)
+    assert np.max(np.abs(y - 1.0)) < 1e-13
+    assert np.all(d > 0)
+
+
+def test_normalized_brute_force_denominator():
+    """The denominator against explicit sums: d_t = sum_{j<=t} (prod_{j<r<=t}
+    a_r) C_t . B_j, and y_t = (sum_j (...) x_j) / d_t, by loops."""
+    rng = np.random.default_rng(61)
+    T, H, P, N = 8, 2, 3, 4
+    x, dt, A, B, C = positive_case(rng, T, H, P, N, 1)
+    y, _, d = oracle.normalized(x, dt, A, B, C)
+    for h in range(H):
+        for t in range(T):
+            num = np.zeros(P)
+            den = 0.0
+            for j in range(t + 1):
+                w = 1.0
+                for r in range(j + 1, t + 1):
+                    w *= math.exp(dt[r, h] * A[h])
+                cb = float(np.dot(C[t, 0], B[j, 0]))
+                num += w * cb * x[j, h]
+                den += w * cb
+            assert abs(d[t, h] - den) <= 1e-12 * abs(den)
+            assert np.max(np.abs(y[t, h] - num / den)) <= 1e-12 * max(1.0, np.max(np.abs(num / den)))
+
+
+def test_normalized_scale_invariance_and_no_decay_limit():
+    """Scaling B (or C) by a positive constant leaves the normalised output
+    unchanged; with decays that kill all history (a -> 0) M is diagonal and
+    the output is x itself; the skip term is added after the division."""
+    rng = np.random.default_rng(62)
+    x, dt, A, B, C = positive_case(rng, 40, 2, 3, 4, 1)
+    y, _, _ = oracle.normalized(x, dt, A, B, C)
+    y2, _, _ = oracle.normalized(x, dt, A, 3.0 * B, 0.5 * C)
+    assert relerr(y2, y) < 1e-13
+    y0, _, _ = oracle.normalized(x, dt, np.full_like(A, -1e7), B, C)  # dt*A <= -1e4
+    assert relerr(y0, x) < 1e-13
+    D = np.array([0.5, -2.0])
+    yd, _, _ = oracle.normalized(x, dt, A, B, C, D=D)
+    assert relerr(yd, y + D[None, :, None] * x) < 1e-13
