@@ -16,7 +16,10 @@ Mamba-2-2.7B-like layer (H=80, N=128), with its own HBM roofline
 (ssd_chunked_bwd) on the same workload (--no-backward skips it), and under
 "comparator" the diagonal selective scan (ssd_selective_scan, Mamba-1's S6) on
 a workload of the same size (one channel per head dimension, the same N and
-dtype) with SSD's speed-up over it (--no-comparator skips it).
+dtype) with SSD's speed-up over it (--no-comparator skips it), and under
+"normalized" the forward with the output divided by its denominator term
+(ssd_chunked_fwd_normalized) on the same workload with positive B and C
+(--no-normalized skips it).
 
 Prints ONE JSON line.
 """
@@ -228,6 +231,38 @@ def bench_comparator(bd, torch, w, sec_ssd, steps, warmup):
                          "avg_launch_ms": kms, "exps_per_launch": exps}}
 
 
+def bench_normalized(bd, torch, w, x, dt, A, B, C, cu, sec_ssd, steps, warmup):
+    """The normalised forward (y / M 1) on the forward's workload, with B and C
+    made positive (|.| + 0.05, the pages' positive feature map), timed like the
+    forward; the denominator kernels' share from HIP events."""
+    Bp = (B.float().abs() + 0.05).to(B.dtype)
+    Cp = (C.float().abs() + 0.05).to(C.dtype)
+
+    def step():
+        return bd.ssd_chunked_fwd_normalized(x, dt, A, Bp, Cp, w.chunk_len, cu_seqlens=cu,
+                                             return_final_state=False)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    bd.kernel_timing_read(reset=True)
+    bd.kernel_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    bd.kernel_timing_enable(False)
+    kt = bd.kernel_timing_read(reset=True)
+    den = kt["denominator"]
+    return {"us_per_step": sec * 1e6, "tokens_per_s": int(x.numel() // (w.nheads * w.headdim)) / sec,
+            "overhead_vs_forward": sec / sec_ssd - 1.0,
+            "denominator_us": den[0] / den[1] * 1e3 if den[1] else None}
+
+
 def min_io_bytes(w, total_tokens, nseq):
     e = 2 if w.dtype == "bf16" else 4
     H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
@@ -260,6 +295,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement reported under \"backward\"")
+    ap.add_argument("--no-normalized", action="store_true",
+                    help="skip the normalised-output measurement reported under \"normalized\"")
     ap.add_argument("--no-comparator", action="store_true",
                     help="skip the selective-scan comparison reported under \"comparator\"")
     ap.add_argument("--no-decode", action="store_true",
@@ -399,6 +436,9 @@ def main():
 
     if not args.no_decode:
         result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200))
+    if not args.no_normalized:
+        result["normalized"] = bench_normalized(bd, torch, w, x, dt, A, B, C, cu, sec, min(args.steps, 100),
+                                                min(args.warmup, 50))
     if not args.no_comparator:
         result["comparator"] = bench_comparator(bd, torch, w, sec, min(args.steps, 20), 3)
     if not args.no_backward:

@@ -219,6 +219,27 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A_head, 
                            int32_t x_times_dt, float* state, void* y, void* stream);
 
 /*
+ * The forward pass with the output normalised by its denominator term ([T] /
+ * [M] "Incorporating a Normalization (Denominator) Term": the denominator of
+ * Y = M X is M 1, the output of one more input column of ones).  With X~ =
+ * [X, 1] run through the layer (the ones column dt-scaled too when
+ * x_times_dt is set, from a zero state in every sequence):
+ *     denom[t,h] = (M 1)[t,h]        y[t,h,:] = (M X)[t,h,:] / denom[t,h] + D_h x[t,h,:]
+ * The pages ask for a positive kernel feature map on B and C so that the
+ * denominators are positive; the library does not check it (a zero
+ * denominator gives inf or nan in y).  Arguments as ssd_chunked_fwd_ex
+ * without an initial state, plus
+ *   denom  (total_len, nheads) fp32, written; required when total_len > 0.
+ * final_state is the state of the P columns of x, as in the plain forward.
+ */
+ssd_status ssd_chunked_fwd_normalized(const void* x, const float* dt, const float* A_head, const void* B,
+                                      const void* C, const int32_t* cu_seqlens, int64_t nseqs,
+                                      int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
+                                      int32_t ngroups, int32_t chunk_len, ssd_dtype dtype, const float* D,
+                                      int32_t x_times_dt, void* y, float* final_state, float* denom,
+                                      void* stream);
+
+/*
  * The comparator of the SSD layer: a selective scan with a diagonal
  * transition (Mamba-1's S6; [M] §3.1.1: a diagonal transition stored as its N
  * entries, of which SSD keeps one scalar, §3.1.2; §2.1.2-2.1.3: one SSM per

@@ -38,6 +38,8 @@ SIGNATURES = {
                         ctypes.c_int),
     "ssd_decode_step": ([_vp, _fp, _fp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _fp, _i32, _fp,
                          _vp, _vp], ctypes.c_int),
+    "ssd_chunked_fwd_normalized": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _fp, _i32, _vp, _fp, _fp, _vp], ctypes.c_int),
     "ssd_selective_scan": ([_vp, _fp, _fp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _fp, _vp],
                            ctypes.c_int),
     "ssd_chunked_fwd_intermediates": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32,
@@ -52,7 +54,7 @@ SIGNATURES = {
 }
 
 KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb", "decode_step",
-                "backward_glue", "selective_scan"]
+                "backward_glue", "selective_scan", "denominator"]
 
 
 class SSDError(RuntimeError):
@@ -239,6 +241,52 @@ def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, ini
                                   ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_chunked_fwd_ex")
     return y, final_state
+
+
+def ssd_chunked_fwd_normalized(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, D=None,
+                               x_times_dt: bool = False, return_final_state: bool = True):
+    """SSD forward with the output divided by its denominator term M 1
+    (ssd_chunked_fwd_normalized).  Inputs as ssd_chunked_fwd_ex without an
+    initial state; B and C should come from a positive feature map.  Returns
+    (y, final_state (S,H,P,N) or None, denom (Ttot,H) fp32)."""
+    dev = x.device
+    if x.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens goes with packed 3-D inputs")
+        b, T, H, P = x.shape
+        S, Tt = b, b * T
+        lead = (b, T)
+    elif x.dim() == 3:
+        if cu_seqlens is None:
+            raise ValueError("packed 3-D inputs need cu_seqlens")
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        Tt, H, P = x.shape
+        S = cu_seqlens.shape[0] - 1
+        lead = (Tt,)
+    else:
+        raise ValueError("x must be (b,T,H,P) or (Ttot,H,P)")
+    G, N = B.shape[-2:]
+    _need(x, "x", x.dtype, dev)
+    _need(dt, "dt", torch.float32, dev)
+    _need(A_head, "A_head", torch.float32, dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev)
+    if tuple(dt.shape) != lead + (H,) or tuple(A_head.shape) != (H,) or \
+            tuple(B.shape) != lead + (G, N) or tuple(C.shape) != lead + (G, N):
+        raise ValueError("inconsistent shapes")
+    if D is not None:
+        _need(D, "D", torch.float32, dev)
+        if tuple(D.shape) != (H,):
+            raise ValueError("D must be (H,)")
+    y = torch.empty_like(x)
+    final_state = torch.empty((S, H, P, N), dtype=torch.float32, device=dev) if return_final_state else None
+    denom = torch.empty((Tt, H), dtype=torch.float32, device=dev)
+    rc = lib().ssd_chunked_fwd_normalized(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), _ptr(cu_seqlens),
+                                          S, Tt, H, P, N, G, int(chunk_len), _dtype_code(x), _ptr(D),
+                                          1 if x_times_dt else 0, _ptr(y), _ptr(final_state), _ptr(denom),
+                                          ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_chunked_fwd_normalized")
+    return y, final_state, denom
 
 
 def ssd_chunked_bwd(x, dt, A_head, B, C, dy, chunk_len: int, cu_seqlens=None, initial_state=None,

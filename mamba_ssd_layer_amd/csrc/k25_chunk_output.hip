@@ -509,6 +509,16 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[j][r] *= eo;
     }
+    if constexpr (kOpts) {
+      // normalised output: divided by the token's denominator before rounding
+      if (p.denom != nullptr) {
+        const float inv = 1.0f / p.denom[(cd.t0 + min(i_loc, L - 1)) * H + h];
+#pragma unroll
+        for (int j = 0; j < NPH; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][r] *= inv;
+      }
+    }
     // store: lane holds Y^T row pr = 32 (ph0 + j) + 8(r/4) + 4 lg + r%4 of token
     // i_loc; bf16 rows are permuted (lds_row_perm), so its p is pr ^ c with
     // c = 4 ((ph0 + j) & 1) + r/4: the four values of a group r/4 = q land in
@@ -563,7 +573,7 @@ static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
     const int HB = heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    if (p.D != nullptr || p.x_times_dt || p.strict_diag)
+    if (p.D != nullptr || p.x_times_dt || p.strict_diag || p.denom != nullptr)
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, true>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     else
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, false>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);

@@ -92,10 +92,17 @@ template <class E, int kCh, bool kDebug>
 __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspace ws,
                                                               float* __restrict__ hin_f32) {
   using T = typename E::storage;
-  const int PN = p.P * p.N;
-  const int cblocks = (PN + kCh * kThreads - 1) / (kCh * kThreads);
+  // channel blocks of the (P, N) states, then (normalised output only) those of
+  // the ones column's N-vector states, passed the same way
+  const int PNs = p.P * p.N;
+  const int cbS = (PNs + kCh * kThreads - 1) / (kCh * kThreads);
+  const int cbZ = ws.zs != nullptr ? (p.N + kCh * kThreads - 1) / (kCh * kThreads) : 0;
+  const int cblocks = cbS + cbZ;
   const int64_t bid = blockIdx.x;
-  const int cb = (int)(bid % cblocks);
+  const int cbg = (int)(bid % cblocks);
+  const bool zc = cbg >= cbS;  // uniform per block
+  const int cb = zc ? cbg - cbS : cbg;
+  const int PN = zc ? p.N : PNs;
   const int h = (int)((bid / cblocks) % p.H);
   const int64_t s = bid / ((int64_t)cblocks * p.H);
   const int ch = (cb * kThreads + threadIdx.x) * kCh;
@@ -108,13 +115,14 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
   // uniform (per-block) bases; the lane's own offset stays a 32-bit add
   const int64_t blk0 = (k0 * H + h) * PN + (int64_t)cb * kThreads * kCh;
   const int lo = threadIdx.x * kCh;
-  const T* st_in = reinterpret_cast<const T*>(ws.states) + blk0;
-  T* hin = reinterpret_cast<T*>(ws.hin) + blk0;
-  float* hin32 = kDebug ? hin_f32 + blk0 : nullptr;
+  const T* st_in = reinterpret_cast<const T*>(zc ? ws.zs : ws.states) + blk0;
+  T* hin = reinterpret_cast<T*>(zc ? ws.zin : ws.hin) + blk0;
+  float* hin32 = (kDebug && !zc) ? hin_f32 + blk0 : nullptr;
   const float* lam = ws.lam + k0 * H + h;
-  // running state: the sequence's initial state (zero when none is given)
+  // running state: the sequence's initial state (zero when none is given; the
+  // ones column always starts from zero)
   float st[kCh] = {};
-  if (p.initial_state != nullptr) {
+  if (p.initial_state != nullptr && !zc) {
 #pragma unroll
     for (int c = 0; c < kCh; c += 2) {
       const float2 s0 = *reinterpret_cast<const float2*>(p.initial_state + (s * H + h) * (int64_t)PN + ch + c);
@@ -148,8 +156,10 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
     float r[kCh];
     store_ch<E, kCh>(hin + (int64_t)kk * stride + lo, st, r, nt);
     if constexpr (kDebug) {
+      if (hin32 != nullptr) {
 #pragma unroll
-      for (int c = 0; c < kCh; ++c) hin32[(int64_t)kk * stride + lo + c] = r[c];
+        for (int c = 0; c < kCh; ++c) hin32[(int64_t)kk * stride + lo + c] = r[c];
+      }
     }
     const float a = __expf(dec);
 #pragma unroll
@@ -179,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
     }
     if (b < nb) scan_block(b, bufA, decA);
   }
-  if (p.final_state != nullptr) {
+  if (p.final_state != nullptr && !zc) {
     float* fs = p.final_state + (s * H + h) * (int64_t)PN + ch;
 #pragma unroll
     for (int c = 0; c < kCh; c += 2) *reinterpret_cast<float2*>(fs + c) = make_float2(st[c], st[c + 1]);
@@ -189,7 +199,8 @@ __global__ __launch_bounds__(kThreads) void state_pass_kernel(Problem p, Workspa
 template <class E, int kCh>
 static hipError_t launch_sp(const Problem& p, const Workspace& ws, float* hin_f32, hipStream_t s) {
   const int PN = p.P * p.N;
-  const int64_t cblocks = (PN + kCh * kThreads - 1) / (kCh * kThreads);
+  const int64_t cblocks = (PN + kCh * kThreads - 1) / (kCh * kThreads) +
+                          (ws.zs != nullptr ? (p.N + kCh * kThreads - 1) / (kCh * kThreads) : 0);
   const dim3 grid((unsigned)(p.nseq * p.H * cblocks)), block(kThreads);
   if (hin_f32) hipLaunchKernelGGL((state_pass_kernel<E, kCh, true>), grid, block, 0, s, p, ws, hin_f32);
   else hipLaunchKernelGGL((state_pass_kernel<E, kCh, false>), grid, block, 0, s, p, ws, hin_f32);

@@ -84,6 +84,8 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   const bool use_cb = chunk_output_reads_cb(p.dtype, p.Q, p.N);
   char* cb = take(use_cb ? K * (size_t)p.G * (NI * (NI + 1) / 2) * 64 * 16 * esz : 0);
   char* cop = take(use_cb ? K * (size_t)p.G * p.Q * p.N * esz : 0);
+  char* zs = take(p.denom ? K * H * p.N * esz : 0);
+  char* zin = take(p.denom ? K * H * p.N * esz : 0);
   if (ws && base) {
     ws->seq_off = reinterpret_cast<int32_t*>(seq_off);
     ws->seq_start = reinterpret_cast<int64_t*>(seq_start);
@@ -97,6 +99,8 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->hin = hin;
     ws->cb = cb;
     ws->cop = cop;
+    ws->zs = p.denom ? zs : nullptr;
+    ws->zin = p.denom ? zin : nullptr;
   }
   return off;
 }
@@ -303,10 +307,18 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
       e = timed_launch(kK2ChunkCB, stream, [&] { return launch_chunk_cb(p, ws, stream); });
       if (e != hipSuccess) break;
     }
+    if (p.kmax > 0 && p.denom != nullptr) {
+      e = timed_launch(kK11Denominator, stream, [&] { return launch_zstate(p, ws, stream); });
+      if (e != hipSuccess) break;
+    }
     e = timed_launch(kK4StatePass, stream, [&] {
       return launch_state_pass(p, ws, dbg ? dbg->hin : nullptr, stream);
     });
     if (e != hipSuccess) break;
+    if (p.kmax > 0 && p.denom != nullptr) {
+      e = timed_launch(kK11Denominator, stream, [&] { return launch_denominator(p, ws, stream); });
+      if (e != hipSuccess) break;
+    }
     if (p.kmax > 0 && !states_only) {
       e = timed_launch(kK25ChunkOutput, stream, [&] { return launch_chunk_output(p, ws, stream); });
       if (e != hipSuccess) break;
@@ -347,6 +359,7 @@ static Problem make_problem(const void* x, const float* dt, const float* A_head,
   p.D = D;
   p.x_times_dt = x_times_dt;
   p.strict_diag = strict_diag;
+  p.denom = nullptr;
   p.nseq = nseq; p.seqlen = seqlen; p.total = total;
   p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups; p.Q = chunk_len;
   p.dtype = static_cast<Dtype>(dtype);
@@ -403,6 +416,23 @@ ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_hea
   const Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, seqlen, total_len, nheads,
                                  headdim, dstate, ngroups, chunk_len, dtype, y, final_state,
                                  initial_state, D, x_times_dt);
+  return run(p, static_cast<hipStream_t>(stream), nullptr);
+}
+
+ssd_status ssd_chunked_fwd_normalized(const void* x, const float* dt, const float* A_head, const void* B,
+                                      const void* C, const int32_t* cu_seqlens, int64_t nseqs,
+                                      int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
+                                      int32_t ngroups, int32_t chunk_len, ssd_dtype dtype, const float* D,
+                                      int32_t x_times_dt, void* y, float* final_state, float* denom,
+                                      void* stream) {
+  if (nseqs < 0 || total_len < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs > 0 && total_len % nseqs != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens == nullptr && nseqs == 0 && total_len != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (total_len > 0 && (denom == nullptr || !aligned(denom, 4))) return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t seqlen = (cu_seqlens == nullptr && nseqs > 0) ? total_len / nseqs : 0;
+  Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, seqlen, total_len, nheads, headdim, dstate,
+                           ngroups, chunk_len, dtype, y, final_state, nullptr, D, x_times_dt);
+  p.denom = total_len > 0 ? denom : nullptr;
   return run(p, static_cast<hipStream_t>(stream), nullptr);
 }
 

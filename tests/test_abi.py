@@ -170,6 +170,17 @@ def test_decode_rejects_invalid_arguments(lib, kw, code):
     assert call_decode(lib, **kw) == code
 
 
+def test_normalized_needs_denominator_buffer(lib):
+    # x dt A B C cu S T H P N G Q dtype D xdt y fs denom stream
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 512, 4, 64, 128, 1, 256, 1, None, 0, FAKE, None, None, None]
+    assert lib.ssd_chunked_fwd_normalized(*args) == INVALID          # denom missing
+    args[18] = FAKE + 2
+    assert lib.ssd_chunked_fwd_normalized(*args) == INVALID          # denom misaligned
+    args[18] = FAKE
+    args[10] = 48
+    assert lib.ssd_chunked_fwd_normalized(*args) == UNSUPPORTED
+
+
 def call_scan(lib, **kw):
     a = dict(x=FAKE, dl=FAKE, A=FAKE, B=FAKE, C=FAKE, b=2, T=512, D=256, N=128, dtype=1, y=FAKE, fs=None)
     a.update(kw)

@@ -663,3 +663,69 @@ def test_selective_scan_full_shape(dev):
     """The comparison shape (one 16384-token sequence, 2048 channels = 32 heads
     of 64, N = 128, bf16), checked on a sample of channels."""
     _scan_check(dev, 1, 16384, 2048, 128, "bf16", 0, chans=np.array([0, 1, 777, 2047]))
+
+
+# ---------------------------------------------- normalised output (denominator) ----
+def _positive(inp):
+    """The same inputs with a positive feature map on B and C (|.| + 0.05,
+    re-rounded to bf16 on the bf16 path), the pages' condition for positive
+    denominators."""
+    from mamba_ssd_layer_amd.workloads import bf16_round
+    f = (lambda a: bf16_round(np.abs(a) + 0.05)) if inp.workload.dtype == "bf16" else (lambda a: np.abs(a) + 0.05)
+    inp.B = f(inp.B).astype(np.float32)
+    inp.C = f(inp.C).astype(np.float32)
+    return inp
+
+
+def _check_normalized(inp, dev, Q, label, D=None, xdt=False):
+    tol = TOL[inp.workload.dtype]
+    d = to_device(inp, dev)
+    tt = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    log(f"[norm] {label}")
+    y, fs, den = bd.ssd_chunked_fwd_normalized(d["x"], d["dt"], d["A"], d["B"], d["C"], Q,
+                                               cu_seqlens=d.get("cu"), D=tt(D), x_times_dt=xdt)
+    torch.cuda.synchronize()
+    y, fs, den = y.float().cpu().numpy(), fs.cpu().numpy(), den.cpu().numpy()
+    yr, fr, dr = oracle.normalized(inp.x, inp.dt, inp.A, inp.B, inp.C,
+                                   cu_seqlens=inp.packed_cu_seqlens(), D=D, x_times_dt=xdt)
+    H, P = inp.x.shape[-2:]
+    cu = inp.packed_cu_seqlens()
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(den))
+    ey, ef = max_rel_l2(y.reshape(-1, H, P), yr.reshape(-1, H, P), fs, fr, cu)
+    ed = float(np.max(oracle.rel_l2_per_slice(den.reshape(-1, H), dr.reshape(-1, H), slice_axes=(1,))))
+    log(f"[norm]   max rel-L2 y {ey:.2e} final_state {ef:.2e} denom {ed:.2e} (bar {tol:g})")
+    assert ey <= tol and ef <= tol and ed <= tol
+
+
+@pytest.mark.parametrize("dtype,N,Q,L", [("f32", 64, 64, 520), ("bf16", 128, 256, 700),
+                                         ("bf16", 16, 64, 300), ("f32", 256, 64, 200)])
+def test_normalized_batched(dev, dtype, N, Q, L):
+    """y / (M 1) against the oracle's extra column of ones: ragged chunks,
+    dstate 16..256, several heads per group."""
+    w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=L, batch=2, nheads=12, ngroups=2)
+    inp = _positive(make_inputs(w, 100 + N))
+    _check_normalized(inp, dev, Q, f"batched {dtype} N={N} Q={Q} L={L}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_normalized_options(dev, dtype):
+    """With the dt-scaled input (the ones column dt-scaled too) and the skip term."""
+    w = SMALL.with_(dtype=dtype, dstate=128, chunk_len=128, seqlen=600, batch=2, nheads=8, ngroups=1)
+    inp = _positive(make_inputs(w, 110))
+    D = np.random.default_rng(110).standard_normal(8).astype(np.float32)
+    _check_normalized(inp, dev, 128, f"options {dtype}", D=D, xdt=True)
+
+
+def test_normalized_varlen(dev):
+    """Packed sequences, empty and one-token ones included."""
+    lens = [300, 0, 1, 513, 64, 77]
+    w = SMALL.with_(dtype="bf16", varlen=True, batch=len(lens), dstate=256, chunk_len=128, nheads=4, ngroups=2)
+    inp = _positive(make_inputs(w, 111, seqlens=lens))
+    _check_normalized(inp, dev, 128, "varlen bf16 N=256")
+
+
+def test_normalized_long(dev):
+    """4096 tokens x 16 heads, bf16, N = 128, chunk 256 (64 chunks of state passing)."""
+    w = SMALL.with_(dtype="bf16", dstate=128, chunk_len=256, seqlen=4096, batch=1, nheads=16, ngroups=1)
+    inp = _positive(make_inputs(w, 112))
+    _check_normalized(inp, dev, 256, "long bf16")
