@@ -150,12 +150,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_kernel(BwdProblem b) {
   for (int v = tid; v < H * P / VEC; v += kBwThreads) {
     const int h = v * VEC / P;
     const uint4 xv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.x) + t * H * P)[v];
-    uint4* cbv = reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.cb) + f * H * P) + v;
-    if (b.x_times_dt) {
-      const float d = b.dt[t * H + h];
-      *cbv = scale_vec<E>(xv, d);
-    } else {
-      *cbv = xv;
+    if (b.cb != nullptr) {
+      uint4* cbv = reinterpret_cast<uint4*>(reinterpret_cast<T*>(b.cb) + f * H * P) + v;
+      if (b.x_times_dt) {
+        const float d = b.dt[t * H + h];
+        *cbv = scale_vec<E>(xv, d);
+      } else {
+        *cbv = xv;
+      }
     }
     if (E::kBytes == 2 && !b.chunked_dl) {  // fp32 inputs of the recompute and reversed passes
       const uint4 dyv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.dy) + t * H * P)[v];
@@ -174,10 +176,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_kernel(BwdProblem b) {
     }
   }
   // per-head copies of B (in time) and C (reversed), 64-column parts, zero
-  // padded past N
+  // padded past N (absent, like the B pass's x' and the per-part step sizes,
+  // when dB and dC are formed per chunk instead)
   const int W = 64 * NK;
   const int WV = W / VEC;
-  for (int v = tid; v < H * WV; v += kBwThreads) {
+  for (int v = tid; b.xc != nullptr && v < H * WV; v += kBwThreads) {
     const int h = v / WV, n0 = (v % WV) * VEC;
     const int g = h / hpg;
     uint4 vb = make_uint4(0, 0, 0, 0), vc = vb;
@@ -193,13 +196,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_kernel(BwdProblem b) {
   for (int h = tid; h < H; h += kBwThreads) {
     const float dtr = (i == q.L - 1) ? 0.0f : b.dt[(t + 1) * H + h];
     b.dtr[f * H + h] = dtr;
+    if (b.dtc == nullptr) continue;
     const float dtt = b.dt[t * H + h];
     for (int k = 0; k < NK; ++k) {
       b.dtc[t * H * NK + h * NK + k] = dtt;
       b.dtb[f * H * NK + h * NK + k] = dtr;
     }
   }
-  if (t == 0)
+  if (t == 0 && b.Ac != nullptr)
     for (int e = tid; e < H * NK; e += kBwThreads) b.Ac[e] = b.A[e / NK];
 }
 
@@ -530,7 +534,7 @@ static hipError_t launch_glue(const BwdProblem& b, int stage, hipStream_t s) {
       break;
     case 1:
       if (b.total > 0) {
-        hipLaunchKernelGGL((bwd_reduce_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
+        if (b.y_c != nullptr) hipLaunchKernelGGL((bwd_reduce_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
         hipLaunchKernelGGL((bwd_token_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
       }
       if (b.chunked_dl) {

@@ -568,6 +568,9 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
         break;
       }
   const bool cdl = Qd > 0;
+  // dB and dC per chunk, summed over heads before the products with B and C
+  // (then no role-exchanged passes and none of their per-head copies)
+  const bool dbdc = cdl && backward_dbdc_supported(p.dtype, Qd, dstate);
   const bool bf16 = dtype == SSD_DTYPE_BF16;
   st = check_device();
   if (st != SSD_OK) return st;
@@ -577,6 +580,8 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   const int NK = (N + 63) / 64, W = 64 * NK;
   const size_t T = (size_t)total_len, S = (size_t)nseqs, e = dtype == SSD_DTYPE_BF16 ? 2 : 4;
   const size_t Kd = cdl ? T / Qd : 0;                   // chunks of the d(ell) path
+  const int nsub = dbdc ? backward_dbdc_subsets((int64_t)Kd, G, H, N) : 0;
+  const bool rx = !dbdc;                                // role-exchanged dB, dC passes
   const bool f32c = bf16 && !cdl;                       // fp32 copies of the inputs
   const bool fpass = !cdl;                              // fp32 recompute and reversed passes
   size_t off = 0;
@@ -593,20 +598,21 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   const int nseg = (int)nseg64;
   BwdProblem b;
   b.nseg = nseg;
+  float* part = nullptr;  // fp32 partial dC, dB of the head subsets
   auto layout = [&]() {
     off = 0;
     b.xr = take(T * H * P * e);
     b.Br = take(T * G * N * e);
     b.Cr = take(T * G * N * e);
     b.dtr = reinterpret_cast<float*>(take(T * H * 4));
-    b.xc = take(T * H * W * e);
-    b.xb = take(T * H * W * e);
-    b.dtc = reinterpret_cast<float*>(take(T * H * NK * 4));
-    b.dtb = reinterpret_cast<float*>(take(T * H * NK * 4));
-    b.Ac = reinterpret_cast<float*>(take((size_t)H * NK * 4));
-    b.cb = take(T * H * P * e);
-    b.h0c = reinterpret_cast<float*>(take(initial_state ? S * H * NK * 4096 * 4 : 0));
-    b.dfb = reinterpret_cast<float*>(take(dfinal_state ? S * H * NK * 4096 * 4 : 0));
+    b.xc = take(rx ? T * H * W * e : 0);
+    b.xb = take(rx ? T * H * W * e : 0);
+    b.dtc = reinterpret_cast<float*>(take(rx ? T * H * NK * 4 : 0));
+    b.dtb = reinterpret_cast<float*>(take(rx ? T * H * NK * 4 : 0));
+    b.Ac = reinterpret_cast<float*>(take(rx ? (size_t)H * NK * 4 : 0));
+    b.cb = take(rx ? T * H * P * e : 0);
+    b.h0c = reinterpret_cast<float*>(take(rx && initial_state ? S * H * NK * 4096 * 4 : 0));
+    b.dfb = reinterpret_cast<float*>(take(rx && dfinal_state ? S * H * NK * 4096 * 4 : 0));
     b.x32 = reinterpret_cast<float*>(take(f32c ? T * H * P * 4 : 0));
     b.xr32 = reinterpret_cast<float*>(take(f32c ? T * H * P * 4 : 0));
     b.B32 = reinterpret_cast<float*>(take(f32c ? T * G * N * 4 : 0));
@@ -624,8 +630,9 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
     b.dl_u = reinterpret_cast<float*>(take(cdl ? T * H * 4 : 0));
     b.dl_kc = reinterpret_cast<float*>(take(Kd * H * 4));
     b.g0 = reinterpret_cast<float*>(take(dinitial_state ? S * H * P * N * 4 : 0));
-    b.y_c = take(T * H * W * e);
-    b.y_b = take(T * H * W * e);
+    b.y_c = take(rx ? T * H * W * e : 0);
+    b.y_b = take(rx ? T * H * W * e : 0);
+    part = reinterpret_cast<float*>(take(nsub > 1 ? 2 * (size_t)nsub * T * G * N * 4 : 0));
     b.qd = reinterpret_cast<float*>(take(fpass ? T * H * 4 : 0));
     b.rd = reinterpret_cast<float*>(take(T * H * 4));
     b.ud = reinterpret_cast<float*>(take(T * H * 4));
@@ -640,6 +647,8 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   layout();
   if (!initial_state) b.h0c = nullptr;
   if (!dfinal_state) b.dfb = nullptr, b.hlast = nullptr;
+  if (!rx) b.xc = b.xb = b.cb = b.y_c = b.y_b = nullptr, b.dtc = b.dtb = b.Ac = b.h0c = b.dfb = nullptr;
+  if (nsub <= 1) part = nullptr;
   if (!dinitial_state) b.g0 = nullptr;
   b.x = x; b.dt = dt; b.A = A_head; b.B = B; b.C = C; b.cu = cu_seqlens; b.h0 = initial_state;
   b.dy = dy; b.dfinal = dfinal_state; b.D = D; b.x_times_dt = x_times_dt;
@@ -677,8 +686,13 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
     dxo.hin_buf = const_cast<void*>(b.gin_e);
     for (auto [q, d] : {std::pair<const Problem*, const DebugOut*>{&pf, &df}, {&px, &dxo}, {&pc, nullptr},
                         {&pb, nullptr}}) {
+      if (!rx && (q == &pc || q == &pb)) continue;
       st = run(*q, s, d);
       if (st != SSD_OK) return st;
+    }
+    if (dbdc) {
+      err = timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_dbdc(b, part, nsub, s); });
+      if (err != hipSuccess) return map_err(err);
     }
     return map_err(timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 1, s); }));
   }

@@ -199,6 +199,12 @@ hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);
 // K8: chunk-local d(ell) -> d(dt), dA (BwdProblem::chunked_dl).
 hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s);
 bool backward_dl_supported(Dtype dt, int Q, int N);
+// dB and dC of the chunk-local path summed over heads per chunk (bf16, whole
+// chunks of b.Q, N in {64, 128, 256}); with nsub > 1 head subsets, part holds
+// (nsub, 2, Ttot, G, N) fp32 partial sums
+hipError_t launch_backward_dbdc(const BwdProblem& b, float* part, int nsub, hipStream_t s);
+bool backward_dbdc_supported(Dtype dt, int Q, int N);
+int backward_dbdc_subsets(int64_t chunks, int G, int H, int N);
 bool chunk_state_supported(Dtype dt, int Q, int N);
 bool chunk_output_supported(Dtype dt, int Q, int N);
 // Whether the chunk-output kernel for (dtype, Q, N) reads the kernel-matrix pass's
