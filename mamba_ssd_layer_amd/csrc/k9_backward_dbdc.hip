@@ -65,18 +65,18 @@ __device__ __forceinline__ void tri_tile(int k, int& I, int& J) {
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu); }
 
+// eight bf16 times d, rounded to nearest even
+__device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float d) {
+  return make_uint4(pack_bf16x2(bf16_lo(v.x) * d, bf16_hi(v.x) * d), pack_bf16x2(bf16_lo(v.y) * d, bf16_hi(v.y) * d),
+                    pack_bf16x2(bf16_lo(v.z) * d, bf16_hi(v.z) * d), pack_bf16x2(bf16_lo(v.w) * d, bf16_hi(v.w) * d));
+}
+
 // v unchanged, but opaque to the compiler: per-lane addresses derived from it
 // inside a loop are recomputed there instead of being hoisted out of it (with
 // every hoisted address a live register, the loop would spill)
 __device__ __forceinline__ int opaque_lane(int v) {
   asm volatile("" : "+v"(v));
   return v;
-}
-
-// eight bf16 times d, rounded to nearest even
-__device__ __forceinline__ uint4 scale_bf16x8(const uint4& v, float d) {
-  return make_uint4(pack_bf16x2(bf16_lo(v.x) * d, bf16_hi(v.x) * d), pack_bf16x2(bf16_lo(v.y) * d, bf16_hi(v.y) * d),
-                    pack_bf16x2(bf16_lo(v.z) * d, bf16_hi(v.z) * d), pack_bf16x2(bf16_lo(v.w) * d, bf16_hi(v.w) * d));
 }
 
 template <int Q>
@@ -97,7 +97,8 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   __shared__ __align__(16) float acs[2][Q];    // per head (two in flight): chunk-local cumsum of dt A
   __shared__ __align__(16) float fd[2][Q];     // exp(a_J - Acs_j) (x dt_j): j-factor of a decay
   __shared__ __align__(16) float dts[2][Q];
-  __shared__ float scal[2][2];                 // Lam, a_next
+  __shared__ __align__(16) float ec[2][Q];     // exp(Acs_t): decay of Hin into token t
+  __shared__ __align__(16) float eb[2][Q];     // a_next exp(Lam - Acs_j) (x dt_j): of x'_j into Gout
 
   const int H = b.H, G = b.G, N = b.N;
   const int hpg = H / G;
@@ -199,15 +200,17 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
         acs[bs][lane * R + i] = incl - acc + run[i];
         dts[bs][lane * R + i] = dtl[i];
       }
+      const float lam = __shfl(incl, 63);
+      const float anext = c + 1 < CPS ? __expf(dtn * Ah) : 1.0f;
       // the same wave reads back the tile ends it wrote
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int j = lane * R + i;
-        fd[bs][j] = __expf(acs[bs][32 * (j / 32) + 31] - acs[bs][j]) * (xdt ? dtl[i] : 1.0f);
-      }
-      if (lane == 63) {
-        scal[bs][0] = incl;
-        scal[bs][1] = c + 1 < CPS ? __expf(dtn * Ah) : 1.0f;
+        const float aj = incl - acc + run[i];
+        const float dtf = xdt ? dtl[i] : 1.0f;
+        fd[bs][j] = __expf(acs[bs][32 * (j / 32) + 31] - aj) * dtf;
+        ec[bs][j] = __expf(aj);
+        eb[bs][j] = anext * __expf(lam - aj) * dtf;
       }
     }
   };
@@ -218,14 +221,23 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) accC[nt] = accB[nt] = zero16();
 
+  // Byte offset, within a block of 32 rows of x or dy (or of hT, gT), of the
+  // vector a lane reads for k-step st of an MFMA operand: row lr, vector
+  // 2 st + lg, swizzled.  Row 32 B + lr of a buffer is then at 4096 B + this.
+  auto operand_offsets = [&](int ln, int (&fo)[4]) {
+    const int lr = ln & 31, lg = ln >> 5;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) fo[st] = 16 * swz_slot<V>(lr, 2 * st + lg);
+  };
+  auto ldv = [](const uint4* base, int off) { return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off); };
+
   // this wave's tiles of M_h, decayed, into Msum.  Tile (I, J): A = x_J rows
   // (m = j), B = dy_I rows (n = t): the lane holds token t = 32 I + lr, value r
   // holds j = 32 J + 8 (r / 4) + 4 lg + r % 4.  Off the diagonal the decay
-  // exp(Acs_t - Acs_j) (x dt_j) factors into exp(Acs_t - a_J) <= 1 on the dy row
-  // and fd_j on the x row (a_J = Acs at the end of tile J), so the scaled
-  // operands accumulate straight into Msum; a diagonal tile is masked (j <= t)
-  // and decayed element by element.
-  auto head_tiles = [&](int ln, const uint4* xb, const uint4* yb, int bs) {
+  // exp(Acs_t - Acs_j) (x dt_j) factors into exp(Acs_t - a_J) <= 1, one per lane,
+  // and fd_j (a_J = Acs at the end of tile J); a diagonal tile is masked
+  // (j <= t) and decayed element by element.
+  auto head_tiles = [&](int ln, const int (&fo)[4], const uint4* xb, const uint4* yb, int bs) {
     const int lr = ln & 31, lg = ln >> 5;
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
@@ -233,17 +245,12 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
       if (kt < NT) {
         int I, J;
         tri_tile(kt, I, J);
-        uint4 a[4], bb[4];
+        floatx16_t sv = zero16();
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          a[st] = xb[swz_slot<V>(32 * J + lr, 2 * st + lg)];
-          bb[st] = yb[swz_slot<V>(32 * I + lr, 2 * st + lg)];
-        }
+        for (int st = 0; st < 4; ++st)
+          sv = mfma32x32x16(ldv(xb, 4096 * J + fo[st]), ldv(yb, 4096 * I + fo[st]), sv);
         const float at = acs[bs][32 * I + lr];
         if (I == J) {
-          floatx16_t sv = zero16();
-#pragma unroll
-          for (int st = 0; st < 4; ++st) sv = mfma32x32x16(a[st], bb[st], sv);
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4) {
             const int jl = 8 * a4 + 4 * lg;
@@ -258,10 +265,14 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
           }
         } else {
           const float ft = __expf(at - acs[bs][32 * J + 31]);
-          const float fj = fd[bs][32 * J + lr];
 #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            msum[u] = mfma32x32x16(scale_bf16x8(a[st], fj), scale_bf16x8(bb[st], ft), msum[u]);
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const float4 f = *reinterpret_cast<const float4*>(&fd[bs][32 * J + 8 * a4 + 4 * lg]);
+            msum[u][4 * a4] += ft * f.x * sv[4 * a4];
+            msum[u][4 * a4 + 1] += ft * f.y * sv[4 * a4 + 1];
+            msum[u][4 * a4 + 2] += ft * f.z * sv[4 * a4 + 2];
+            msum[u][4 * a4 + 3] += ft * f.w * sv[4 * a4 + 3];
+          }
         }
       }
       // one tile's operands at a time: hoisting every tile's loads would take
@@ -272,27 +283,23 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   // state terms of the wave's tile: A = dy rows t scaled by exp(Acs_t) (x rows j
   // scaled by a_next exp(Lam - Acs_j) (x dt_j)), B = Hin^T (Gout^T) rows n; the
   // lane holds column n = 32 nt + lr, value r token 32 wid + 8 (r / 4) + 4 lg + r % 4
-  auto head_states = [&](int ln, const uint4* xb, const uint4* yb, int bs) {
-    const int lr = ln & 31, lg = ln >> 5;
-    const int tr = 32 * wid + lr;  // the lane's operand row
-    const float ar = acs[bs][tr];
-    const float ec = __expf(ar);
-    const float eb = scal[bs][1] * __expf(scal[bs][0] - ar) * (xdt ? dts[bs][tr] : 1.0f);
+  auto head_states = [&](int ln, const int (&fo)[4], const uint4* xb, const uint4* yb, int bs) {
+    const int tr = 32 * wid + (ln & 31);  // the lane's operand row
     uint4 a[4];
+    const float fc = ec[bs][tr];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) a[st] = scale_bf16x8(yb[swz_slot<V>(tr, 2 * st + lg)], ec);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        accC[nt] = mfma32x32x16(a[st], hT[swz_slot<V>(32 * nt + lr, 2 * st + lg)], accC[nt]);
-#pragma unroll
-    for (int st = 0; st < 4; ++st) a[st] = scale_bf16x8(xb[swz_slot<V>(tr, 2 * st + lg)], eb);
+    for (int st = 0; st < 4; ++st) a[st] = scale_bf16x8(ldv(yb, 4096 * wid + fo[st]), fc);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        accB[nt] = mfma32x32x16(a[st], gT[swz_slot<V>(32 * nt + lr, 2 * st + lg)], accB[nt]);
+      for (int st = 0; st < 4; ++st) accC[nt] = mfma32x32x16(a[st], ldv(hT, 4096 * nt + fo[st]), accC[nt]);
+    const float fb = eb[bs][tr];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) a[st] = scale_bf16x8(ldv(xb, 4096 * wid + fo[st]), fb);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) accB[nt] = mfma32x32x16(a[st], ldv(gT, 4096 * nt + fo[st]), accB[nt]);
   };
   // one head: its copies were issued one head earlier into (cx, cy); the next
   // head's go into (nx, ny)
@@ -306,8 +313,10 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
       load_dt(h_lo + u + 1);
       issue_xy(ln, h_lo + u + 1, nx, ny);
     }
-    head_tiles(ln, cx, cy, bs);
-    head_states(ln, cx, cy, bs);
+    int fo[4];
+    operand_offsets(ln, fo);
+    head_tiles(ln, fo, cx, cy, bs);
+    head_states(ln, fo, cx, cy, bs);
     if (more) {
       make_tables(h_lo + u + 1, bs ^ 1);
       dl_barrier();  // every wave is done with hT, gT of head u

@@ -601,6 +601,15 @@ def test_backward_chunk_aligned(dev, dtype, N, Q, L, opts):
     _check_bwd(inp, dev, Q, TOL[dtype], f"aligned {dtype} N={N} Q={Q} L={L} opts={opts}", seed, **kw)
 
 
+def test_backward_chunk_aligned_single_subset(dev):
+    """Enough chunks x groups x 64-column slices (8 x 16 x 2 x 2 = 512) that
+    the per-chunk dB, dC kernel takes each group's heads in one workgroup and
+    stores bf16 directly (no partial sums)."""
+    w = SMALL.with_(dstate=128, chunk_len=64, seqlen=1024, batch=8, nheads=4, ngroups=2)
+    inp = make_inputs(w, 95)
+    _check_bwd(inp, dev, 64, TOL["bf16"], "aligned bf16 one head subset", 95, D=np.ones(4, np.float32), xdt=True)
+
+
 def test_backward_varlen(dev):
     """Packed sequences, empty ones included (their initial-state gradient is
     dfinal), N = 256 (four 64-column parts)."""
