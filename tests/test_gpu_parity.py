@@ -610,6 +610,14 @@ def test_backward_chunk_aligned_single_subset(dev):
     _check_bwd(inp, dev, 64, TOL["bf16"], "aligned bf16 one head subset", 95, D=np.ones(4, np.float32), xdt=True)
 
 
+def test_backward_chunk_aligned_uneven_subsets(dev):
+    """64 chunks x 1 group x 2 column slices: the per-chunk dB, dC kernel splits
+    the group's 5 heads into subsets of 2 and 3 whose fp32 partial sums are added."""
+    w = SMALL.with_(dstate=128, chunk_len=64, seqlen=1024, batch=4, nheads=5, ngroups=1)
+    inp = make_inputs(w, 96)
+    _check_bwd(inp, dev, 64, TOL["bf16"], "aligned bf16 uneven head subsets", 96)
+
+
 def test_backward_varlen(dev):
     """Packed sequences, empty ones included (their initial-state gradient is
     dfinal), N = 256 (four 64-column parts)."""
