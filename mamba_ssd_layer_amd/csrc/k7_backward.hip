@@ -535,7 +535,7 @@ static hipError_t launch_glue(const BwdProblem& b, int stage, hipStream_t s) {
     case 1:
       if (b.total > 0) {
         if (b.y_c != nullptr) hipLaunchKernelGGL((bwd_reduce_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
-        hipLaunchKernelGGL((bwd_token_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
+        if (!b.tokens_in_dbdc) hipLaunchKernelGGL((bwd_token_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
       }
       if (b.chunked_dl) {
         if (b.total > 0) {

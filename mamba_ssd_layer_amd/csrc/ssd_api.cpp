@@ -656,6 +656,7 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   b.nseq = nseqs; b.seqlen = seqlen; b.total = total_len;
   b.H = H; b.P = P; b.N = N; b.G = G; b.NK = NK; b.dtype = p.dtype;
   b.chunked_dl = cdl; b.Q = Qd;
+  b.tokens_in_dbdc = dbdc;
   if (!bf16) {
     b.x32 = static_cast<const float*>(x);
     b.B32 = static_cast<const float*>(B);
