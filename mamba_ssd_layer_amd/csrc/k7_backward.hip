@@ -522,6 +522,126 @@ __global__ __launch_bounds__(kBwThreads) void bwd_scan_kernel(BwdProblem b) {
   }
 }
 
+// ---- packed sequences padded to whole chunks (chunk-local path) ----
+// clamped bounds of packed sequence s (invalid cu: unspecified results, every
+// access in bounds)
+__device__ __forceinline__ void packed_seq(const PadArgs& a, int64_t s, int64_t* lo, int64_t* L) {
+  const int64_t c0 = min(max((int64_t)a.cu[s], (int64_t)0), a.T);
+  const int64_t c1 = min(max((int64_t)a.cu[s + 1], (int64_t)0), a.T);
+  *lo = c0;
+  *L = max(c1 - c0, (int64_t)0);
+}
+
+// One workgroup: cup[s] = sum over s' < s of ceil(L_s' / Q) Q (runs of
+// sequences per thread, then a block-wide scan), cup[S + 1] = Tp.
+__global__ __launch_bounds__(kBwThreads) void bwd_pad_offsets_kernel(PadArgs a) {
+  __shared__ int64_t part[kBwThreads];
+  const int tid = threadIdx.x;
+  const int64_t per = (a.S + kBwThreads - 1) / kBwThreads;
+  const int64_t s0 = min(a.S, (int64_t)tid * per), s1 = min(a.S, s0 + per);
+  auto padded = [&](int64_t s) {
+    int64_t lo, L;
+    packed_seq(a, s, &lo, &L);
+    return (L + a.Q - 1) / a.Q * a.Q;
+  };
+  int64_t sum = 0;
+  for (int64_t s = s0; s < s1; ++s) sum += padded(s);
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kBwThreads; off <<= 1) {  // inclusive scan
+    const int64_t add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int64_t run = part[tid] - sum;
+  for (int64_t s = s0; s < s1; ++s) {
+    a.cup[s] = (int32_t)min(run, a.Tp);
+    run += padded(s);
+  }
+  if (tid == kBwThreads - 1) {
+    a.cup[a.S] = (int32_t)min(part[tid], a.Tp);
+    a.cup[a.S + 1] = (int32_t)a.Tp;
+  }
+}
+
+// rows of n 16-byte vectors: copy from src (or zeros when src is null)
+__device__ __forceinline__ void copy_row(const void* src, void* dst, int n) {
+  for (int v = threadIdx.x; v < n; v += kBwThreads)
+    reinterpret_cast<uint4*>(dst)[v] = src ? reinterpret_cast<const uint4*>(src)[v] : make_uint4(0, 0, 0, 0);
+}
+
+// One workgroup per padded token: its source token, or the padding.
+__global__ __launch_bounds__(kBwThreads) void bwd_pad_kernel(PadArgs a) {
+  const int64_t tp = blockIdx.x;
+  int64_t lo = 0, hi = a.S + 1;  // last s in [0, S] with cup[s] <= tp
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if (a.cup[mid] <= tp) lo = mid;
+    else hi = mid;
+  }
+  int64_t src = -1;
+  if (lo < a.S) {
+    int64_t c0, L;
+    packed_seq(a, lo, &c0, &L);
+    const int64_t i = tp - a.cup[lo];
+    if (i >= 0 && i < L) src = c0 + i;
+  }
+  const int eb = a.dtype == Dtype::BF16 ? 2 : 4;
+  const int64_t xr = (int64_t)a.H * a.P * eb, br = (int64_t)a.G * a.N * eb;  // row bytes
+  auto row = [&](const void* base, int64_t bytes) {
+    return src >= 0 ? static_cast<const char*>(base) + src * bytes : nullptr;
+  };
+  copy_row(row(a.x, xr), static_cast<char*>(a.xp) + tp * xr, (int)(xr / 16));
+  copy_row(row(a.dy, xr), static_cast<char*>(a.dyp) + tp * xr, (int)(xr / 16));
+  copy_row(row(a.B, br), static_cast<char*>(a.Bp) + tp * br, (int)(br / 16));
+  copy_row(row(a.C, br), static_cast<char*>(a.Cp) + tp * br, (int)(br / 16));
+  for (int h = threadIdx.x; h < a.H; h += kBwThreads) a.dtp[tp * a.H + h] = src >= 0 ? a.dt[src * a.H + h] : 0.0f;
+}
+
+// One workgroup per token: its results from the padded layout.
+__global__ __launch_bounds__(kBwThreads) void bwd_unpad_kernel(PadArgs a) {
+  const int64_t t = blockIdx.x;
+  int64_t lo = 0, hi = a.S;  // last s with cu[s] <= t (clamped)
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if (min(max((int64_t)a.cu[mid], (int64_t)0), a.T) <= t) lo = mid;
+    else hi = mid;
+  }
+  int64_t c0, L;
+  packed_seq(a, lo, &c0, &L);
+  const int64_t tp = min(max((int64_t)a.cup[lo] + (t - c0), (int64_t)0), a.Tp - 1);
+  const int eb = a.dtype == Dtype::BF16 ? 2 : 4;
+  const int64_t xr = (int64_t)a.H * a.P * eb, br = (int64_t)a.G * a.N * eb;
+  copy_row(static_cast<const char*>(a.dxp) + tp * xr, static_cast<char*>(a.dx) + t * xr, (int)(xr / 16));
+  copy_row(static_cast<const char*>(a.dBp) + tp * br, static_cast<char*>(a.dB) + t * br, (int)(br / 16));
+  copy_row(static_cast<const char*>(a.dCp) + tp * br, static_cast<char*>(a.dC) + t * br, (int)(br / 16));
+  for (int h = threadIdx.x; h < a.H; h += kBwThreads) a.ddt[t * a.H + h] = a.ddtp[tp * a.H + h];
+}
+
+__global__ __launch_bounds__(kBwThreads) void fill_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)kBwThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBwThreads)
+    p[i] = 0.0f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + kBwThreads - 1) / kBwThreads, 1024);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kBwThreads), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_pad(const PadArgs& a, int stage, hipStream_t s) {
+  const dim3 blk(kBwThreads);
+  if (stage == 0) {
+    hipLaunchKernelGGL(bwd_pad_offsets_kernel, dim3(1), blk, 0, s, a);
+    if (a.Tp > 0) hipLaunchKernelGGL(bwd_pad_kernel, dim3((unsigned)a.Tp), blk, 0, s, a);
+  } else {
+    if (a.T > 0) hipLaunchKernelGGL(bwd_unpad_kernel, dim3((unsigned)a.T), blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <class E>
 static hipError_t launch_glue(const BwdProblem& b, int stage, hipStream_t s) {
   const dim3 blk(kBwThreads);

@@ -155,15 +155,15 @@ void bwd_dl_kernel(BwdProblem b) {
   __shared__ float dterm[Q];
   __shared__ float red[kDlThreads / 64];
   const int H = b.H, G = b.G;
-  const int64_t CPS = b.seqlen / Q;  // chunks per sequence (a whole number here)
+
   // the workgroups of one chunk on one XCD: they share its B and C rows in L2
   const int64_t bid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int half = (int)(bid % NS);
   const int64_t kh = bid / NS;
   const int h = (int)(kh % H);
   const int64_t k = kh / H;
-  const int64_t s = k / CPS, c = k % CPS;
-  const int64_t t0 = s * b.seqlen + c * Q;
+  const BwdChunk ch = bwd_chunk(b, k, Q);
+  const int64_t CPS = ch.CPS, c = ch.c, t0 = ch.t0;
   const int g = h / (H / G);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const float Ah = b.A[h];
@@ -179,7 +179,7 @@ void bwd_dl_kernel(BwdProblem b) {
   // CPS-1-c; after the last chunk it is dfinal itself (no decay)
   const uint16_t* hin = reinterpret_cast<const uint16_t*>(b.hin_e) + (k * H + h) * (int64_t)(P * N);
   const uint16_t* gout =
-      reinterpret_cast<const uint16_t*>(b.gin_e) + ((s * CPS + (CPS - 1 - c)) * H + h) * (int64_t)(P * N);
+      reinterpret_cast<const uint16_t*>(b.gin_e) + ((ch.s0 / Q + (CPS - 1 - c)) * H + h) * (int64_t)(P * N);
 
   // j-side tile J into ring buffer J % RB.  Instruction q < NBB copies rows
   // 64 q / VB .. of B_J (LDS slots 64 q + lane), the others rows of X_J after
@@ -409,8 +409,7 @@ __global__ __launch_bounds__(64) void bwd_dl_scan_kernel(BwdProblem b) {
   const int64_t kh = blockIdx.x;
   const int h = (int)(kh % H);
   const int64_t k = kh / H;
-  const int64_t CPS = b.seqlen / Q;
-  const int64_t t0 = (k / CPS) * b.seqlen + (k % CPS) * Q;
+  const int64_t t0 = k * Q;
   const int lane = threadIdx.x;
   const float Ah = b.A[h];
   const int64_t base = h * b.total + t0 + lane * R;
@@ -464,7 +463,8 @@ static void launch_dl_q(const BwdProblem& b, int64_t chunks, hipStream_t s) {
 }
 
 hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s) {
-  if (!backward_dl_supported(b.dtype, b.Q, b.N) || b.seqlen % b.Q != 0) return hipErrorInvalidValue;
+  if (!backward_dl_supported(b.dtype, b.Q, b.N) || b.total % b.Q != 0 || (b.cu == nullptr && b.seqlen % b.Q != 0))
+    return hipErrorInvalidValue;
   const int64_t chunks = b.total / b.Q;
   if (chunks == 0) return hipSuccess;
   switch (b.Q) {

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
 
   const int H = b.H, G = b.G, N = b.N;
   const int hpg = H / G;
-  const int64_t CPS = b.seqlen / Q;  // chunks per sequence (a whole number here)
+
   // the column slices of one chunk and head subset run on one XCD: they read
   // the same x and dy through its L2
   const int64_t bid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
@@ -112,8 +112,8 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   rest /= nsub;
   const int g = (int)(rest % G);
   const int64_t k = rest / G;
-  const int64_t s = k / CPS, c = k % CPS;
-  const int64_t t0 = s * b.seqlen + c * Q;
+  const BwdChunk ch = bwd_chunk(b, k, Q);
+  const int64_t CPS = ch.CPS, c = ch.c, t0 = ch.t0;
   const int n0 = Cfg::NW * ns;
   const int h_lo = g * hpg + (sub * hpg) / nsub;
   const int nh = g * hpg + ((sub + 1) * hpg) / nsub - h_lo;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   const uint16_t* yg = reinterpret_cast<const uint16_t*>(b.dy) + t0 * xs;
   const int64_t PN = (int64_t)P * N;
   const uint16_t* hin0 = reinterpret_cast<const uint16_t*>(b.hin_e) + k * H * PN + n0;
-  const uint16_t* gout0 = reinterpret_cast<const uint16_t*>(b.gin_e) + (s * CPS + (CPS - 1 - c)) * H * PN + n0;
+  const uint16_t* gout0 = reinterpret_cast<const uint16_t*>(b.gin_e) + (ch.s0 / Q + (CPS - 1 - c)) * H * PN + n0;
 
   // x and dy of head h into (xb, yb): instruction q copies rows 8 q .. 8 q + 7 of
   // the chunk (LDS slots 64 q + lane); lane L takes row 8 q + L / 8 and the
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   const bool tok_wave = b.tokens_in_dbdc && (wid % nsplit) == ns;
   auto load_dxp = [&](int ln, int h, uint4 (&dv)[4]) {
     const int lr = ln & 31, lg = ln >> 5;
-    const int64_t f = s * b.seqlen + (b.seqlen - 1 - (c * Q + 32 * wid + lr));
+    const int64_t f = ch.s0 + (ch.L - 1 - (c * Q + 32 * wid + lr));  // reversed position in the sequence
     const uint16_t* src = reinterpret_cast<const uint16_t*>(b.y_x8) + (f * H + h) * P + 8 * lg;
 #pragma unroll
     for (int st = 0; st < 4; ++st) dv[st] = *reinterpret_cast<const uint4*>(src + 16 * st);
@@ -529,7 +529,8 @@ static void launch_dbdc_q(const BwdProblem& b, float* part, int nsub, hipStream_
 }
 
 hipError_t launch_backward_dbdc(const BwdProblem& b, float* part, int nsub, hipStream_t s) {
-  if (!backward_dbdc_supported(b.dtype, b.Q, b.N) || b.seqlen % b.Q != 0 || nsub < 1 || (nsub > 1 && !part))
+  if (!backward_dbdc_supported(b.dtype, b.Q, b.N) || b.total % b.Q != 0 || (b.cu == nullptr && b.seqlen % b.Q != 0) ||
+      nsub < 1 || (nsub > 1 && !part))
     return hipErrorInvalidValue;
   const int64_t chunks = b.total / b.Q;
   if (chunks == 0) return hipSuccess;

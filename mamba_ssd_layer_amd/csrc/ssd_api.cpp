@@ -514,14 +514,18 @@ ssd_status ssd_selective_scan(const void* x, const float* delta, const float* A,
   return map_err(timed_launch(kK10SelectiveScan, s, [&] { return launch_selective_scan(p, s); }));
 }
 
-ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, const void* B,
+// The backward, arguments as ssd_chunked_bwd.  aligned_q > 0: the caller
+// guarantees that every packed sequence is a whole number of chunks of
+// aligned_q = chunk_len (the padded layout below), so the chunk-local path
+// takes cu_seqlens too.
+static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, const void* B,
                            const void* C, const int32_t* cu_seqlens, int64_t nseqs,
                            int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
                            int32_t ngroups, int32_t chunk_len, ssd_dtype dtype,
                            const float* initial_state, const float* D, int32_t x_times_dt,
                            const void* dy, const float* dfinal_state, void* dx, float* ddt,
                            float* dA, void* dB, void* dC, float* dD, float* dinitial_state,
-                           void* stream) {
+                           void* stream, int aligned_q) {
   if (nseqs < 0 || total_len < 0) return SSD_ERR_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr && nseqs > 0 && total_len % nseqs != 0) return SSD_ERR_INVALID_ARGUMENT;
   if (cu_seqlens == nullptr && nseqs == 0 && total_len != 0) return SSD_ERR_INVALID_ARGUMENT;
@@ -561,7 +565,10 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   // with the forward's): its passes run in bf16, and no fp32 recompute or
   // reversed pass is needed.
   int Qd = 0;
-  if (cu_seqlens == nullptr && seqlen > 0)
+  if (aligned_q > 0 && aligned_q == chunk_len && backward_dl_supported(p.dtype, aligned_q, dstate) &&
+      config_supported(p.dtype, aligned_q, dstate))
+    Qd = aligned_q;
+  else if (cu_seqlens == nullptr && seqlen > 0)
     for (int q : {chunk_len, 256, 128, 64})
       if (seqlen % q == 0 && backward_dl_supported(p.dtype, q, dstate) && config_supported(p.dtype, q, dstate)) {
         Qd = q;
@@ -579,8 +586,9 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   const int H = nheads, P = headdim, N = dstate, G = ngroups;
   const int NK = (N + 63) / 64, W = 64 * NK;
   const size_t T = (size_t)total_len, S = (size_t)nseqs, e = dtype == SSD_DTYPE_BF16 ? 2 : 4;
-  const size_t Kd = cdl ? T / Qd : 0;                   // chunks of the d(ell) path
-  const int nsub = dbdc ? backward_dbdc_subsets((int64_t)Kd, G, H, N) : 0;
+  // chunk slots of the d(ell) path's passed states (packed: the forward's bound)
+  const size_t Kd = cdl ? (cu_seqlens ? T / Qd + S : T / Qd) : 0;
+  const int nsub = dbdc ? backward_dbdc_subsets((int64_t)(T / Qd), G, H, N) : 0;
   const bool rx = !dbdc;                                // role-exchanged dB, dC passes
   const bool f32c = bf16 && !cdl;                       // fp32 copies of the inputs
   const bool fpass = !cdl;                              // fp32 recompute and reversed passes
@@ -671,11 +679,11 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   if (nseqs == 0) return SSD_OK;
   if (cdl) {
     // passed states of the forward (fp32 copies of the stored values)
-    Problem pf = make_problem(x, dt, A_head, B, C, nullptr, nseqs, seqlen, total_len, H, P, N, G, Qd, dtype,
+    Problem pf = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, seqlen, total_len, H, P, N, G, Qd, dtype,
                               dx, nullptr, initial_state, nullptr, x_times_dt);
     // reversed pass in the element dtype: dx' (own terms in), its passed states
     // (the adjoint after each chunk) and G_first
-    Problem px = make_problem(b.xr, b.dtr, A_head, b.Br, b.Cr, nullptr, nseqs, seqlen, total_len, H, P, N, G,
+    Problem px = make_problem(b.xr, b.dtr, A_head, b.Br, b.Cr, cu_seqlens, nseqs, seqlen, total_len, H, P, N, G,
                               Qd, dtype, const_cast<void*>(b.y_x8), b.g0, dfinal_state, nullptr, 0);
     Problem pc = make_problem(b.xc, b.dtc, b.Ac, x, dy, nullptr, nseqs, seqlen, total_len, H * NK, kHeadDim, P,
                               H, Q2, dtype, b.y_c, nullptr, b.h0c, nullptr, x_times_dt);
@@ -714,6 +722,121 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
     if (st != SSD_OK) return st;
   }
   return map_err(timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 1, s); }));
+}
+
+// Packed bf16 sequences take the chunk-local path through a padded copy: each
+// sequence is padded on the device to a whole number of chunks (dt = 0, zero
+// x, dy, B, C: decay 1, no input, no output, so every gradient and the final
+// state are unchanged), one zero sequence fills the rest of the host's bound
+// on the padded length, and the results are copied back.  The bound needs no
+// host read of cu_seqlens: T + S (Q - 1).  Used when that at most doubles the
+// tokens and the configuration is built.
+static int padded_bwd_chunk(const int32_t* cu_seqlens, int64_t nseqs, int64_t total_len, int32_t dstate,
+                            int32_t ngroups, int32_t chunk_len, ssd_dtype dtype) {
+  if (cu_seqlens == nullptr || total_len <= 0 || nseqs <= 0 || dtype != SSD_DTYPE_BF16 || ngroups > kMaxBwdGroups)
+    return 0;
+  for (int q : {chunk_len, 256, 128, 64}) {
+    if (q != 64 && q != 128 && q != 256) continue;
+    const int64_t tp = (total_len + nseqs * (int64_t)(q - 1) + q - 1) / q * q;
+    if (nseqs * (int64_t)(q - 1) <= total_len && tp < 0x7fffffffLL && backward_dl_supported(Dtype::BF16, q, dstate) &&
+        backward_dbdc_supported(Dtype::BF16, q, dstate) && config_supported(Dtype::BF16, q, dstate))
+      return q;
+  }
+  return 0;
+}
+
+ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, const void* B,
+                           const void* C, const int32_t* cu_seqlens, int64_t nseqs,
+                           int64_t total_len, int32_t nheads, int32_t headdim, int32_t dstate,
+                           int32_t ngroups, int32_t chunk_len, ssd_dtype dtype,
+                           const float* initial_state, const float* D, int32_t x_times_dt,
+                           const void* dy, const float* dfinal_state, void* dx, float* ddt,
+                           float* dA, void* dB, void* dC, float* dD, float* dinitial_state,
+                           void* stream) {
+  const int Qp = padded_bwd_chunk(cu_seqlens, nseqs, total_len, dstate, ngroups, chunk_len, dtype);
+  if (Qp == 0)
+    return bwd_impl(x, dt, A_head, B, C, cu_seqlens, nseqs, total_len, nheads, headdim, dstate, ngroups, chunk_len,
+                    dtype, initial_state, D, x_times_dt, dy, dfinal_state, dx, ddt, dA, dB, dC, dD, dinitial_state,
+                    stream, 0);
+  // the caller's arguments are checked as for the unpadded call
+  {
+    Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, 0, total_len, nheads, headdim, dstate, ngroups,
+                             chunk_len, dtype, dx, nullptr, initial_state, D, x_times_dt);
+    ssd_status st = validate(p);
+    if (st != SSD_OK) return st;
+    if (dA == nullptr || !aligned(dA, 4) || (dD && !aligned(dD, 4))) return SSD_ERR_INVALID_ARGUMENT;
+    if ((dfinal_state && !aligned(dfinal_state, 16)) || (dinitial_state && !aligned(dinitial_state, 16)))
+      return SSD_ERR_INVALID_ARGUMENT;
+    if (!dy || !ddt || !dB || !dC || !aligned(dy, 16) || !aligned(dB, 16) || !aligned(dC, 16) || !aligned(ddt, 4))
+      return SSD_ERR_INVALID_ARGUMENT;
+    st = check_device();
+    if (st != SSD_OK) return st;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t S = nseqs, T = total_len, S1 = nseqs + 1;
+  const int64_t Tp = (T + S * (Qp - 1) + Qp - 1) / Qp * Qp;
+  const size_t H = nheads, P = headdim, N = dstate, G = ngroups, PN = P * N;
+  size_t off = 0;
+  char* base = nullptr;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return base ? base + at : nullptr;
+  };
+  PadArgs a;
+  float *h0p = nullptr, *dfp = nullptr, *dinitp = nullptr;
+  auto layout = [&]() {
+    off = 0;
+    a.cup = reinterpret_cast<int32_t*>(take((size_t)(S + 2) * 4));
+    a.xp = take(Tp * H * P * 2);
+    a.dyp = take(Tp * H * P * 2);
+    a.Bp = take(Tp * G * N * 2);
+    a.Cp = take(Tp * G * N * 2);
+    a.dtp = reinterpret_cast<float*>(take(Tp * H * 4));
+    a.dxp = take(Tp * H * P * 2);
+    a.dBp = take(Tp * G * N * 2);
+    a.dCp = take(Tp * G * N * 2);
+    a.ddtp = reinterpret_cast<float*>(take(Tp * H * 4));
+    h0p = reinterpret_cast<float*>(take(initial_state ? S1 * H * PN * 4 : 0));
+    dfp = reinterpret_cast<float*>(take(dfinal_state ? S1 * H * PN * 4 : 0));
+    dinitp = reinterpret_cast<float*>(take(dinitial_state ? S1 * H * PN * 4 : 0));
+  };
+  layout();
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+  base = static_cast<char*>(ws_acquire(dev, off, s, 2));
+  if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  layout();
+  // absent optional arrays stay absent (a zero-byte piece still has an address)
+  if (!initial_state) h0p = nullptr;
+  if (!dfinal_state) dfp = nullptr;
+  if (!dinitial_state) dinitp = nullptr;
+  a.cu = cu_seqlens;
+  a.S = S; a.T = T; a.Tp = Tp;
+  a.H = nheads; a.P = headdim; a.G = ngroups; a.N = dstate; a.Q = Qp;
+  a.dtype = Dtype::BF16;
+  a.x = x; a.dt = dt; a.B = B; a.C = C; a.dy = dy;
+  a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC;
+  hipError_t err = timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_pad(a, 0, s); });
+  if (err != hipSuccess) return map_err(err);
+  // per-sequence states with a zero entry for the filling sequence
+  for (auto [src, dst] : {std::pair<const float*, float*>{initial_state, h0p}, {dfinal_state, dfp}}) {
+    if (src == nullptr) continue;
+    if (hipMemcpyAsync(dst, src, S * H * PN * 4, hipMemcpyDeviceToDevice, s) != hipSuccess) return SSD_ERR_HIP;
+    err = launch_fill_zero(dst + S * H * PN, H * PN, s);
+    if (err != hipSuccess) return map_err(err);
+  }
+  ssd_status st = bwd_impl(a.xp, a.dtp, A_head, a.Bp, a.Cp, a.cup, S1, Tp, nheads, headdim, dstate, ngroups, Qp,
+                           dtype, h0p, D, x_times_dt, a.dyp, dfp, const_cast<void*>(a.dxp),
+                           const_cast<float*>(a.ddtp), dA, const_cast<void*>(a.dBp), const_cast<void*>(a.dCp), dD,
+                           dinitp, stream, Qp);
+  if (st != SSD_OK) return st;
+  err = timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_pad(a, 1, s); });
+  if (err != hipSuccess) return map_err(err);
+  if (dinitial_state &&
+      hipMemcpyAsync(dinitial_state, dinitp, S * H * PN * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return SSD_ERR_HIP;
+  return SSD_OK;
 }
 
 const char* ssd_status_string(ssd_status status) {

@@ -200,6 +200,24 @@ hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);
 // K8: chunk-local d(ell) -> d(dt), dA (BwdProblem::chunked_dl).
 hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s);
 bool backward_dl_supported(Dtype dt, int Q, int N);
+// Packed sequences padded to whole chunks of Q for the chunk-local backward:
+// sequence s starts at cup[s] in the padded layout (cup has S + 2 entries;
+// [cup[S], cup[S + 1] = Tp) is one zero sequence up to the host's bound Tp).
+// The padding has dt = 0 (decay 1) and zero x, dy, B, C.
+struct PadArgs {
+  const int32_t* cu; int32_t* cup;
+  int64_t S, T, Tp;
+  int H, P, G, N, Q;
+  Dtype dtype;
+  const void* x; const float* dt; const void* B; const void* C; const void* dy;  // (T, ...) in
+  void* xp; float* dtp; void* Bp; void* Cp; void* dyp;                            // (Tp, ...) padded
+  const void* dxp; const float* ddtp; const void* dBp; const void* dCp;          // (Tp, ...) results
+  void* dx; float* ddt; void* dB; void* dC;                                        // (T, ...) out
+};
+// stage 0: cup, then the padded inputs; stage 1: the results back to (T, ...)
+hipError_t launch_backward_pad(const PadArgs& a, int stage, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);  // p[0, n) = 0 (a kernel, no memset node)
+
 // dB and dC of the chunk-local path summed over heads per chunk (bf16, whole
 // chunks of b.Q, N in {64, 128, 256}); with nsub > 1 head subsets, part holds
 // (nsub, 2, Ttot, G, N) fp32 partial sums

@@ -1,7 +1,8 @@
 // ssd_lds.hpp -- load-to-LDS copies and the waits and barriers around them
-// (gfx950), shared by the backward kernels that stream tiles through LDS.
+// (gfx950), and the chunk map, shared by the chunk-local backward kernels.
 #pragma once
 #include "ssd_device.hpp"
+#include "ssd_internal.hpp"
 
 namespace ssd {
 
@@ -39,6 +40,43 @@ template <int V>
 __device__ __forceinline__ int swz_slot(int r, int q) {
   const int x = V >= 16 ? (r & 15) : ((r / (16 / V)) % V);
   return r * V + (q ^ x);
+}
+
+// Chunk k of the chunk-local backward path.  Every sequence there is a whole
+// number of chunks (batched: seqlen a multiple of Q; packed: padded so), so
+// chunk k covers tokens [kQ, kQ + Q) of one sequence, which starts at token s0,
+// has L tokens (CPS chunks) and holds the chunk as its chunk c.  Packed
+// sequences are found in cu by binary search (empty ones share their start
+// with the next).  A cu that breaks the alignment gives unspecified results,
+// never an index outside [0, total): such a chunk is taken as a sequence of
+// its own.
+struct BwdChunk {
+  int64_t t0, s0, L, CPS, c;
+};
+__device__ __forceinline__ BwdChunk bwd_chunk(const BwdProblem& b, int64_t k, int Q) {
+  BwdChunk r;
+  r.t0 = k * Q;
+  if (b.cu == nullptr) {
+    r.L = b.seqlen;
+    r.s0 = b.seqlen > 0 ? (r.t0 / b.seqlen) * b.seqlen : r.t0;
+  } else {
+    int64_t lo = 0, hi = b.nseq;  // last s with cu[s] <= t0
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) / 2;
+      if (b.cu[mid] <= r.t0) lo = mid;
+      else hi = mid;
+    }
+    r.s0 = b.cu[lo];
+    r.L = (int64_t)b.cu[lo + 1] - r.s0;
+  }
+  if (r.s0 < 0 || r.s0 > r.t0 || r.L < Q || r.L % Q != 0 || (r.t0 - r.s0) % Q != 0 || r.s0 + r.L < r.t0 + Q ||
+      r.s0 + r.L > b.total) {
+    r.s0 = r.t0;
+    r.L = Q;
+  }
+  r.CPS = r.L / Q;
+  r.c = (r.t0 - r.s0) / Q;
+  return r;
 }
 
 }  // namespace ssd

@@ -493,13 +493,13 @@ def test_decode_options(dev, dtype):
 
 
 # ------------------------------------------------------------- backward ----
-def _grads_gpu(inp, dev, Q, dy, h0=None, D=None, xdt=False, dfinal=None):
+def _grads_gpu(inp, dev, Q, dy, h0=None, D=None, xdt=False, dfinal=None, optional=True):
     d = to_device(inp, dev)
     tdt = torch.bfloat16 if inp.workload.dtype == "bf16" else torch.float32
     tt = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     g = bd.ssd_chunked_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], tt(dy).to(tdt), Q,
                            cu_seqlens=d.get("cu"), initial_state=tt(h0), D=tt(D), x_times_dt=xdt,
-                           dfinal_state=tt(dfinal), want_dD=True, want_dinitial=True)
+                           dfinal_state=tt(dfinal), want_dD=optional, want_dinitial=optional)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.float().cpu().numpy()) for k, v in g.items()}
 
@@ -532,19 +532,20 @@ def _grad_errors(inp, g, r):
         "dB": per_seq(g["dB"].reshape(-1, G, N), r["dB"].reshape(-1, G, N)),
         "dC": per_seq(g["dC"].reshape(-1, G, N), r["dC"].reshape(-1, G, N)),
         "dA": vec(g["dA"], r["dA"]),
-        "dD": vec(g["dD"], r["dD"]) if r["dD"] is not None else 0.0,
-        "dinit": float(np.max(oracle.rel_l2_per_slice(g["dinitial_state"], r["dinit"], slice_axes=(0, 1)))),
+        "dD": vec(g["dD"], r["dD"]) if r["dD"] is not None and g["dD"] is not None else 0.0,
+        "dinit": (float(np.max(oracle.rel_l2_per_slice(g["dinitial_state"], r["dinit"], slice_axes=(0, 1))))
+                  if g["dinitial_state"] is not None else 0.0),
     }
 
 
-def _check_bwd(inp, dev, Q, tol, label, seed, h0=None, D=None, xdt=False, dfinal=None):
+def _check_bwd(inp, dev, Q, tol, label, seed, h0=None, D=None, xdt=False, dfinal=None, optional=True):
     from mamba_ssd_layer_amd.workloads import bf16_round
     rng = np.random.default_rng(seed + 777)
     dy = rng.standard_normal(inp.x.shape).astype(np.float32)
     if inp.workload.dtype == "bf16":
         dy = bf16_round(dy)
     log(f"[bwd] {label}")
-    g = _grads_gpu(inp, dev, Q, dy, h0, D, xdt, dfinal)
+    g = _grads_gpu(inp, dev, Q, dy, h0, D, xdt, dfinal, optional)
     for k, v in g.items():
         assert v is None or np.all(np.isfinite(v)), k
     r = oracle.backward(inp.x, inp.dt, inp.A, inp.B, inp.C, dy, cu_seqlens=inp.packed_cu_seqlens(),
@@ -627,6 +628,32 @@ def test_backward_varlen(dev):
     h0 = initial_states(len(lens), 4, 64, 256, seed=82)
     dfin = initial_states(len(lens), 4, 64, 256, seed=83)
     _check_bwd(inp, dev, 128, TOL["bf16"], "varlen bf16 N=256", 82, h0=h0, dfinal=dfin)
+
+
+@pytest.mark.parametrize("optional", [False, True])
+def test_backward_varlen_padded(dev, optional):
+    """Packed bf16 sequences through the chunk-local path (each sequence padded
+    on the device to whole 256-token chunks, an empty sequence among them),
+    with and without the optional arrays (initial state, final-state
+    gradient, dD and the initial-state gradient)."""
+    lens = [700, 0, 45, 1300, 256, 3]
+    w = SMALL.with_(varlen=True, batch=len(lens), dstate=128, chunk_len=256, nheads=4, ngroups=2)
+    inp = make_inputs(w, 97, seqlens=lens)
+    kw = {}
+    if optional:
+        kw = dict(h0=initial_states(len(lens), 4, 64, 128, seed=97),
+                  dfinal=initial_states(len(lens), 4, 64, 128, seed=98),
+                  D=np.random.default_rng(97).standard_normal(4).astype(np.float32), xdt=True)
+    _check_bwd(inp, dev, 256, TOL["bf16"], f"varlen padded optional={optional}", 97, optional=optional, **kw)
+
+
+def test_backward_varlen_many_short(dev):
+    """Many short packed sequences (padding them to whole chunks would more than
+    double the tokens): the role-exchanged passes with fp32 d(ell) instead."""
+    lens = [5, 0, 17, 1, 30, 2, 9, 40, 3, 11]
+    w = SMALL.with_(varlen=True, batch=len(lens), dstate=64, chunk_len=64, nheads=4, ngroups=2)
+    inp = make_inputs(w, 99, seqlens=lens)
+    _check_bwd(inp, dev, 64, TOL["bf16"], "varlen many short", 99)
 
 
 def test_backward_full_2k(dev):
