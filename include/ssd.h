@@ -171,14 +171,19 @@ ssd_status ssd_chunked_fwd_ex(const void* x, const float* dt, const float* A_hea
  *   dD               (nheads) fp32 or NULL (skip)
  *   dinitial_state   (nseqs, nheads, headdim, dstate) fp32 or NULL (skip)
  * dA and dD are sums over all tokens formed with atomic additions: their last
- * bits may differ between runs.  Implementation: a forward recompute and three
- * more passes of the forward kernels on rearranged inputs (time-reversed
- * with the decays shifted by one token for dx and dB; the roles of x and B
- * exchanged for dB and dC), plus streaming glue kernels; it needs a second
- * per-stream workspace of about 12 x-sized arrays.  headdim 64; every
- * (dtype, dstate, chunk_len) the forward supports, provided (dtype, 64, Q) is
- * built for some Q.  Alignment, validation, execution and errors as for the
- * forward.
+ * bits may differ between runs.  Implementation: passes of the forward
+ * kernels on rearranged inputs (the forward's passed states; the sequence
+ * reversed in time with the decays shifted by one token, for dx and the
+ * adjoint states), then, for bf16 inputs whose sequences are whole numbers
+ * of chunks, per-chunk kernels for dB, dC, dx and d(dt) (packed bf16
+ * sequences are padded on the device to whole chunks for this, when that at
+ * most doubles the tokens: up to total_len + nseqs (chunk_len - 1) padded
+ * tokens of workspace); otherwise fp32 passes and role-exchanged passes (the
+ * roles of x and B exchanged for dB and dC).  It needs a second per-stream
+ * workspace of a few x-sized arrays (about 12 on the fp32 route).  headdim
+ * 64; every (dtype, dstate, chunk_len) the forward supports, provided
+ * (dtype, 64, Q) is built for some Q.  Alignment, validation, execution and
+ * errors as for the forward.
  */
 ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, const void* B,
                            const void* C, const int32_t* cu_seqlens, int64_t nseqs,
