@@ -526,6 +526,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_scan_kernel(BwdProblem b) {
 // clamped bounds of packed sequence s (invalid cu: unspecified results, every
 // access in bounds)
 __device__ __forceinline__ void packed_seq(const PadArgs& a, int64_t s, int64_t* lo, int64_t* L) {
+  if (a.cu == nullptr) {  // batched
+    *lo = s * a.seqlen;
+    *L = a.seqlen;
+    return;
+  }
   const int64_t c0 = min(max((int64_t)a.cu[s], (int64_t)0), a.T);
   const int64_t c1 = min(max((int64_t)a.cu[s + 1], (int64_t)0), a.T);
   *lo = c0;
@@ -603,10 +608,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_pad_kernel(PadArgs a) {
 __global__ __launch_bounds__(kBwThreads) void bwd_unpad_kernel(PadArgs a) {
   const int64_t t = blockIdx.x;
   int64_t lo = 0, hi = a.S;  // last s with cu[s] <= t (clamped)
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) / 2;
-    if (min(max((int64_t)a.cu[mid], (int64_t)0), a.T) <= t) lo = mid;
-    else hi = mid;
+  if (a.cu == nullptr) {
+    lo = min(t / max(a.seqlen, (int64_t)1), a.S - 1);
+  } else {
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) / 2;
+      if (min(max((int64_t)a.cu[mid], (int64_t)0), a.T) <= t) lo = mid;
+      else hi = mid;
+    }
   }
   int64_t c0, L;
   packed_seq(a, lo, &c0, &L);

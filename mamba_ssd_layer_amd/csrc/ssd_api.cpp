@@ -724,8 +724,9 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
   return map_err(timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_glue(b, 1, s); }));
 }
 
-// Packed bf16 sequences take the chunk-local path through a padded copy: each
-// sequence is padded on the device to a whole number of chunks (dt = 0, zero
+// bf16 sequences that are not whole numbers of chunks (packed, or batched
+// with a length no built chunk length divides) take the chunk-local path
+// through a padded copy: each sequence is padded on the device to a whole number of chunks (dt = 0, zero
 // x, dy, B, C: decay 1, no input, no output, so every gradient and the final
 // state are unchanged), one zero sequence fills the rest of the host's bound
 // on the padded length, and the results are copied back.  The bound needs no
@@ -733,8 +734,15 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
 // tokens and the configuration is built.
 static int padded_bwd_chunk(const int32_t* cu_seqlens, int64_t nseqs, int64_t total_len, int32_t dstate,
                             int32_t ngroups, int32_t chunk_len, ssd_dtype dtype) {
-  if (cu_seqlens == nullptr || total_len <= 0 || nseqs <= 0 || dtype != SSD_DTYPE_BF16 || ngroups > kMaxBwdGroups)
-    return 0;
+  if (total_len <= 0 || nseqs <= 0 || dtype != SSD_DTYPE_BF16 || ngroups > kMaxBwdGroups) return 0;
+  if (cu_seqlens == nullptr) {
+    // batched: only when no built chunk length divides the sequence length
+    if (total_len % nseqs != 0) return 0;
+    const int64_t seqlen = total_len / nseqs;
+    for (int q : {chunk_len, 256, 128, 64})
+      if (seqlen % q == 0 && backward_dl_supported(Dtype::BF16, q, dstate) && config_supported(Dtype::BF16, q, dstate))
+        return 0;
+  }
   for (int q : {chunk_len, 256, 128, 64}) {
     if (q != 64 && q != 128 && q != 256) continue;
     const int64_t tp = (total_len + nseqs * (int64_t)(q - 1) + q - 1) / q * q;
@@ -760,8 +768,9 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
                     stream, 0);
   // the caller's arguments are checked as for the unpadded call
   {
-    Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, 0, total_len, nheads, headdim, dstate, ngroups,
-                             chunk_len, dtype, dx, nullptr, initial_state, D, x_times_dt);
+    Problem p = make_problem(x, dt, A_head, B, C, cu_seqlens, nseqs, cu_seqlens ? 0 : total_len / nseqs, total_len,
+                             nheads, headdim, dstate, ngroups, chunk_len, dtype, dx, nullptr, initial_state, D,
+                             x_times_dt);
     ssd_status st = validate(p);
     if (st != SSD_OK) return st;
     if (dA == nullptr || !aligned(dA, 4) || (dD && !aligned(dD, 4))) return SSD_ERR_INVALID_ARGUMENT;
@@ -812,7 +821,7 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   if (!dfinal_state) dfp = nullptr;
   if (!dinitial_state) dinitp = nullptr;
   a.cu = cu_seqlens;
-  a.S = S; a.T = T; a.Tp = Tp;
+  a.S = S; a.T = T; a.Tp = Tp; a.seqlen = cu_seqlens ? 0 : T / S;
   a.H = nheads; a.P = headdim; a.G = ngroups; a.N = dstate; a.Q = Qp;
   a.dtype = Dtype::BF16;
   a.x = x; a.dt = dt; a.B = B; a.C = C; a.dy = dy;

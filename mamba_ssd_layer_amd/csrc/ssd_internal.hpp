@@ -200,13 +200,13 @@ hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);
 // K8: chunk-local d(ell) -> d(dt), dA (BwdProblem::chunked_dl).
 hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s);
 bool backward_dl_supported(Dtype dt, int Q, int N);
-// Packed sequences padded to whole chunks of Q for the chunk-local backward:
+// Sequences padded to whole chunks of Q for the chunk-local backward:
 // sequence s starts at cup[s] in the padded layout (cup has S + 2 entries;
 // [cup[S], cup[S + 1] = Tp) is one zero sequence up to the host's bound Tp).
 // The padding has dt = 0 (decay 1) and zero x, dy, B, C.
 struct PadArgs {
-  const int32_t* cu; int32_t* cup;
-  int64_t S, T, Tp;
+  const int32_t* cu; int32_t* cup;  // cu null: batched, S sequences of seqlen tokens
+  int64_t S, T, Tp, seqlen;
   int H, P, G, N, Q;
   Dtype dtype;
   const void* x; const float* dt; const void* B; const void* C; const void* dy;  // (T, ...) in

@@ -566,7 +566,8 @@ def _check_bwd(inp, dev, Q, tol, label, seed, h0=None, D=None, xdt=False, dfinal
                                        ("bf16", 256, 128), ("bf16", 16, 64)])
 def test_backward_batched(dev, dtype, N, Q):
     """Gradients of every input against the oracle's adjoint recurrence, plain
-    (no initial state, no dfinal, no options)."""
+    (no initial state, no dfinal, no options); 520 tokens are not a whole
+    number of chunks (bf16 with N >= 64: the padded chunk-local route)."""
     w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=520, batch=2, nheads=4, ngroups=2)
     inp = make_inputs(w, 70 + N)
     _check_bwd(inp, dev, Q, TOL[dtype], f"batched {dtype} N={N} Q={Q}", 70 + N)
@@ -654,6 +655,15 @@ def test_backward_varlen_many_short(dev):
     w = SMALL.with_(varlen=True, batch=len(lens), dstate=64, chunk_len=64, nheads=4, ngroups=2)
     inp = make_inputs(w, 99, seqlens=lens)
     _check_bwd(inp, dev, 64, TOL["bf16"], "varlen many short", 99)
+
+
+def test_backward_batched_short_fallback(dev):
+    """bf16 sequences of 40 tokens with 64-token chunks: too short to pad (the
+    padding would more than double them), so the role-exchanged passes with
+    fp32 d(ell) run."""
+    w = SMALL.with_(dtype="bf16", dstate=64, chunk_len=64, seqlen=40, batch=3, nheads=4, ngroups=2)
+    inp = make_inputs(w, 100)
+    _check_bwd(inp, dev, 64, TOL["bf16"], "batched short fallback", 100, D=np.ones(4, np.float32), xdt=True)
 
 
 def test_backward_full_2k(dev):
