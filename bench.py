@@ -306,7 +306,7 @@ def main():
                          "scaling the HBM byte counters of a profiler")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the SSD path would shard over (batch, head) with no communication",
               file=sys.stderr)
         sys.exit(2)
