@@ -147,7 +147,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_kernel(BwdProblem b) {
   // x' reversed (input scaled by dt with the dt-scaled input), and on the bf16
   // path the fp32 inputs of the recompute and reversed passes, in 16-byte
   // vectors (VEC elements, never straddling a head row)
-  for (int v = tid; v < H * P / VEC; v += kBwThreads) {
+  const bool x_copies = b.cb != nullptr || (E::kBytes == 2 && !b.chunked_dl);  // else x is not read here
+  for (int v = tid; x_copies && v < H * P / VEC; v += kBwThreads) {
     const int h = v * VEC / P;
     const uint4 xv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.x) + t * H * P)[v];
     if (b.cb != nullptr) {
