@@ -290,6 +290,12 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     if (!active) continue;
 
     const int i_loc = I * 32 + lr;
+    // normalised output: the token's denominator, loaded here so that the
+    // head's products hide the load
+    float den = 1.0f;
+    if constexpr (kOpts) {
+      if (p.denom != nullptr) den = p.denom[(cd.t0 + min(i_loc, L - 1)) * H + h];
+    }
     floatx16_t acc[NPH];
 #pragma unroll
     for (int j = 0; j < NPH; ++j) acc[j] = zero16();
@@ -512,7 +518,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     if constexpr (kOpts) {
       // normalised output: divided by the token's denominator before rounding
       if (p.denom != nullptr) {
-        const float inv = 1.0f / p.denom[(cd.t0 + min(i_loc, L - 1)) * H + h];
+        const float inv = 1.0f / den;
 #pragma unroll
         for (int j = 0; j < NPH; ++j)
 #pragma unroll
