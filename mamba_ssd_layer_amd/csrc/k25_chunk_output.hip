@@ -95,12 +95,16 @@ struct ChunkOutputCfg {
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
 };
 
-// kOpts: the skip term and the dt-scaled input are handled (a separate
-// instantiation, so that the plain forward keeps every register it had)
-template <class E, int Q, int N, bool kOpts>
+// kOpt: 0 plain; 1 the skip term, the dt-scaled input, the strict diagonal
+// and the normalised output's division; 2 that division only.  Separate
+// instantiations, so that the plain forward keeps every register it had and
+// the normalised output alone does not carry the other options' registers.
+template <class E, int Q, int N, int kOpt>
 __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
   using Cfg = ChunkOutputCfg<E, Q, N>;
   using T = typename E::storage;
+  constexpr bool kOpts = kOpt == 1;  // skip term, dt-scaled input, strict diagonal
+  constexpr bool kDen = kOpt != 0;   // normalised output
   constexpr int P = Cfg::P, NP = Cfg::NP, QP = Cfg::QP, KS = Cfg::KS, GV = Cfg::GV, YP = Cfg::YP;
   constexpr bool kBf16 = Cfg::kBf16;
   constexpr int NI = Cfg::NI, NTILE = Cfg::NTILE, NPH = Cfg::NPH;
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // normalised output: the token's denominator, loaded here so that the
     // head's products hide the load
     float den = 1.0f;
-    if constexpr (kOpts) {
+    if constexpr (kDen) {
       if (p.denom != nullptr) den = p.denom[(cd.t0 + min(i_loc, L - 1)) * H + h];
     }
     floatx16_t acc[NPH];
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[j][r] *= eo;
     }
-    if constexpr (kOpts) {
+    if constexpr (kDen) {
       // normalised output: divided by the token's denominator before rounding
       if (p.denom != nullptr) {
         const float inv = 1.0f / den;
@@ -579,10 +583,12 @@ static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
     const int HB = heads_per_block(p);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    if (p.D != nullptr || p.x_times_dt || p.strict_diag || p.denom != nullptr)
-      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, true>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+    if (p.D != nullptr || p.x_times_dt || p.strict_diag)
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 1>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+    else if (p.denom != nullptr)
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 2>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     else
-      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, false>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 0>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
