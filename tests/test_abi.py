@@ -227,6 +227,31 @@ def test_backward_rejects_invalid_arguments(lib):
     assert call({16: 5}) == INVALID           # x_times_dt is 0 or 1
 
 
+@pytest.mark.parametrize("route", ["packed", "batched_unaligned"])
+def test_backward_padded_route_rejects_invalid_arguments(lib, route):
+    """bf16 calls that take the padded route (packed sequences; a batched length
+    that no chunk length divides) check their arguments before any HIP call."""
+    # x dt A B C cu S T H P N G Q dtype h0 D xdt dy dfinal dx ddt dA dB dC dD dinit stream
+    cu, T = (FAKE, 512) if route == "packed" else (None, 600)
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, cu, 2, T, 4, 64, 128, 1, 256, 1, None, None, 0,
+            FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None]
+
+    def call(changes):
+        a = list(base)
+        for i, v in changes.items():
+            a[i] = v
+        return lib.ssd_chunked_bwd(*a)
+
+    assert call({17: None}) == INVALID        # dy missing
+    assert call({17: FAKE + 2}) == INVALID    # dy misaligned
+    assert call({21: None}) == INVALID        # dA missing
+    assert call({22: FAKE + 2}) == INVALID    # dB misaligned
+    assert call({18: FAKE + 4}) == INVALID    # dfinal misaligned
+    assert call({25: FAKE + 4}) == INVALID    # dinitial_state misaligned
+    assert call({16: 5}) == INVALID           # x_times_dt is 0 or 1
+    assert call({10: 48}) == UNSUPPORTED
+
+
 def test_intermediates_rejects_uneven_batch(lib):
     assert lib.ssd_chunked_fwd_intermediates(FAKE, FAKE, FAKE, FAKE, FAKE, None, 3, 100, 4, 64, 128,
                                              1, 256, 1, FAKE, None, None, None, None, None) == INVALID
