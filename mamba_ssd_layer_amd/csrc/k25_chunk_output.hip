@@ -333,6 +333,25 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     }
     const float ai = acs_s[i_loc];
     const float eo = __expf(ai);
+    // skip term D_h x_i as an extra diagonal entry of the tile product: x^T_i
+    // is x_i times a staging scale that the output factor undoes, so the entry
+    // is D_h, over dt_i when the input enters as dt x (x^T_i then carries dt_i),
+    // times the denominator when the output is normalised (divided out again).
+    // A token with dt_i = 0 has x^T_i = 0 there: a pass after this kernel adds
+    // its term (skip_zero_dt_kernel).
+    float dsk = 0.0f;
+    if constexpr (kOpts) {
+      if (p.D != nullptr) {
+        dsk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dskip_v), hh));
+        if constexpr (kDen) {
+          if (p.denom != nullptr) dsk *= den;
+        }
+        if (p.x_times_dt) {
+          const float dti = p.dt[(cd.t0 + min(i_loc, L - 1)) * H + h];
+          dsk = dti == 0.0f ? 0.0f : dsk / dti;
+        }
+      }
+    }
     if (mode != kMaskChunk) {
 #pragma unroll
       for (int j = 0; j < NPH; ++j)
@@ -398,6 +417,24 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
               }
               b[q].x &= m[0]; b[q].y &= m[1]; b[q].z &= m[2]; b[q].w &= m[3];
             }
+            if constexpr (kOpts) {
+              if (p.D != nullptr) {
+                // the skip weight on the entry j == i, as an operand of its own
+                const uint32_t sw = pack_bf16x2(dsk, 0.0f);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                  uint32_t w[4];
+#pragma unroll
+                  for (int d = 0; d < 4; ++d) {
+                    const int j0 = ((8 * q + 2 * d) >> 2) * 8 + lg * 4 + (2 * d & 3);
+                    w[d] = (j0 == lr ? sw : 0u) | (j0 + 1 == lr ? sw << 16 : 0u);
+                  }
+                  const uint4 bd = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+                  for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x16(xa[q][j], bd, acc[j]);
+                }
+              }
+            }
           }
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk)
@@ -429,6 +466,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         for (int r = 0; r < 16; ++r) {
           const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
           v[r] = (!kDiag || jr + sd <= lr) ? gt[r] : 0.0f;
+          if (kOpts && kDiag && jr == lr) v[r] += dsk;
         }
       } else if (mode == kMaskTile) {
         // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
@@ -442,6 +480,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           for (int r = 0; r < 16; ++r) {
             const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
             v[r] = (jr + sd <= lr) ? gt[r] * u : 0.0f;
+            if (kOpts && jr == lr) v[r] += dsk * u;
           }
         }
       } else if constexpr (!kDiag) {
@@ -460,6 +499,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
           const float m = __expf(ai - acs_s[j]);
           v[r] = (j + sd <= i_loc) ? gt[r] * m : 0.0f;
+          if (kOpts && j == i_loc) v[r] += dsk;
         }
       }
       // Y^T += X^T (L o G)^T over the 32 tokens of tile J
@@ -561,21 +601,29 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       const int row = s * RPI + lane / VPR;
       const int vec = lane % VPR;
       const int i_row = I * 32 + row;
-      uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
-      if (kOpts && p.D != nullptr) {
-        // skip connection on the raw input: y += D_h x (added to the rounded
-        // sums, then rounded once more)
-        const float dh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dskip_v), hh));
-        const uint4 xv = *reinterpret_cast<const uint4*>(
-            xbase + (int64_t)min(i_row, L - 1) * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T)));
-        val = add_scaled<E>(val, xv, dh);
-      }
+      const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
       if (i_row < L)
         store_nt(reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))),
                  val);
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Skip term of the tokens with dt = 0 when the input enters as dt x: their
+// staged x^T is zero, so the output kernel cannot carry D_h x for them; this
+// pass adds it to the stored output (rounded once more), one thread per
+// (token, head) and 16-byte vectors over the head's P values.
+template <class E>
+__global__ __launch_bounds__(256) void skip_zero_dt_kernel(Problem p) {
+  using T = typename E::storage;
+  const int64_t th = blockIdx.x * 256LL + threadIdx.x;
+  if (th >= p.total * p.H) return;
+  if (p.dt[th] != 0.0f) return;
+  const float dh = p.D[th % p.H];
+  const uint4* xv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(p.x) + th * p.P);
+  uint4* yv = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.y) + th * p.P);
+  for (int v = 0; v < p.P * (int)sizeof(T) / 16; ++v) yv[v] = add_scaled<E>(yv[v], xv[v], dh);
 }
 
 template <class E, int Q, int N>
@@ -589,6 +637,11 @@ static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 2>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
     else
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 0>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+    if (p.D != nullptr && p.x_times_dt && p.total > 0) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((skip_zero_dt_kernel<E>), dim3((unsigned)((p.total * p.H + 255) / 256)), dim3(256), 0, s, p);
+    }
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

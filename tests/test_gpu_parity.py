@@ -438,6 +438,23 @@ def test_options_batched(dev, dtype, N, Q, D_on, xdt):
               h0=h0, D=D if D_on else None, xdt=xdt)
 
 
+@pytest.mark.parametrize("dtype,N,Q", [("f32", 64, 128), ("bf16", 128, 256)])
+def test_options_zero_dt(dev, dtype, N, Q):
+    """Tokens with dt = 0 under the dt-scaled input and the skip term: their
+    input enters the scan as zero, so the output kernel's diagonal cannot carry
+    D_h x for them and the pass after it adds the term (every seventh token of
+    every head, and a run of 40 tokens of head 1)."""
+    from mamba_ssd_layer_amd.workloads import Inputs
+    w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=600, batch=2, nheads=4, ngroups=1)
+    inp = make_inputs(w, 63)
+    dt = inp.dt.copy().reshape(2, 600, 4)
+    dt[:, 3::7, :] = 0.0
+    dt[1, 100:140, 1] = 0.0
+    z = Inputs(w, inp.x, dt.reshape(inp.dt.shape), inp.A, inp.B, inp.C)
+    D = np.linspace(-1.0, 1.0, 4).astype(np.float32)
+    _check_ex(z, dev, Q, TOL[dtype], f"{dtype} N={N} Q={Q} dt = 0 tokens, D and x*dt", D=D, xdt=True)
+
+
 def test_options_varlen(dev):
     lens = [300, 0, 1, 513, 64, 77]
     w = SMALL.with_(varlen=True, batch=len(lens), dstate=128, chunk_len=128, nheads=8, ngroups=2)
