@@ -19,7 +19,9 @@ a workload of the same size (one channel per head dimension, the same N and
 dtype) with SSD's speed-up over it (--no-comparator skips it), and under
 "normalized" the forward with the output divided by its denominator term
 (ssd_chunked_fwd_normalized) on the same workload with positive B and C
-(--no-normalized skips it).
+(--no-normalized skips it), and under "options" the forward with the skip
+term D and the dt-scaled input, as a Mamba-2 layer calls it
+(ssd_chunked_fwd_ex), on the same workload (--no-options skips it).
 
 Prints ONE JSON line.
 """
@@ -263,6 +265,37 @@ def bench_normalized(bd, torch, w, x, dt, A, B, C, cu, sec_ssd, steps, warmup):
             "denominator_us": den[0] / den[1] * 1e3 if den[1] else None}
 
 
+def bench_options(bd, torch, w, x, dt, A, B, C, cu, sec_ssd, steps, warmup):
+    """The forward with the skip term D (one weight per head) and the input
+    entering as dt x, on the forward's workload, timed like the forward; the
+    output kernel's share from HIP events."""
+    D = torch.linspace(-1.0, 1.0, w.nheads, device=x.device, dtype=torch.float32)
+
+    def step():
+        return bd.ssd_chunked_fwd_ex(x, dt, A, B, C, w.chunk_len, cu_seqlens=cu, D=D, x_times_dt=True,
+                                     return_final_state=False)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    bd.kernel_timing_read(reset=True)
+    bd.kernel_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    bd.kernel_timing_enable(False)
+    co = bd.kernel_timing_read(reset=True)["chunk_output"]
+    return {"options": "D and x*dt", "us_per_step": sec * 1e6,
+            "tokens_per_s": int(x.numel() // (w.nheads * w.headdim)) / sec,
+            "overhead_vs_forward": sec / sec_ssd - 1.0,
+            "chunk_output_us": co[0] / co[1] * 1e3 if co[1] else None}
+
+
 def min_io_bytes(w, total_tokens, nseq):
     e = 2 if w.dtype == "bf16" else 4
     H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
@@ -295,6 +328,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement reported under \"backward\"")
+    ap.add_argument("--no-options", action="store_true",
+                    help="skip the forward-with-options measurement reported under \"options\"")
     ap.add_argument("--no-normalized", action="store_true",
                     help="skip the normalised-output measurement reported under \"normalized\"")
     ap.add_argument("--no-comparator", action="store_true",
@@ -439,6 +474,9 @@ def main():
     if not args.no_normalized:
         result["normalized"] = bench_normalized(bd, torch, w, x, dt, A, B, C, cu, sec, min(args.steps, 100),
                                                 min(args.warmup, 50))
+    if not args.no_options:
+        result["options"] = bench_options(bd, torch, w, x, dt, A, B, C, cu, sec, min(args.steps, 100),
+                                          min(args.warmup, 50))
     if not args.no_comparator:
         result["comparator"] = bench_comparator(bd, torch, w, sec, min(args.steps, 20), 3)
     if not args.no_backward:
