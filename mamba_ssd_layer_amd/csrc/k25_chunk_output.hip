@@ -30,17 +30,21 @@
 //    with its tokens permuted in 16-groups so the A operand is one 16-byte read.
 //  * Causality: only tiles J <= I are used; on the diagonal tile the entries
 //    with j > i are a selected (or masked-off) 0, never exp(-inf) arithmetic.
-//    The mask exp(Acs_i - Acs_j) is factored per head in one of three ways,
-//    chosen from the chunk's total decay and its largest 32-token-tile decay
-//    (both from the chunk-state kernel):
-//    - chunk (total decay <= e^64): x_j is staged scaled by exp(-Acs_j) (<= e^64)
-//      and the finished sums by exp(Acs_i), which Y_off needs as well; the
-//      kernel tiles go to the matrix cores as stored, with no per-tile work;
-//    - tile (no tile decays by more than e^64): with e the last token of j's
-//      tile, x_j is staged scaled by w_j = exp(Acs_e - Acs_j) in (0, 1] and each
-//      lane scales its tile values by exp(Acs_i - Acs_e), one exp per tile;
-//    - exact: x staged as is, the tile factor times a w_j table below the
-//      diagonal and one exp per element on it.
+//    The mask is exp of the sum of ell = dt*A over the tokens (j, i], formed
+//    per head in one of two ways, chosen from the chunk's total log-decay
+//    (mask_by_chunk):
+//    - chunk (total decay within e^64 on the bf16 path, e^16 on fp32): x_j is
+//      staged scaled by exp(-Acs_j) and the finished sums by exp(Acs_i), which
+//      Y_off needs as well; the kernel tiles go to the matrix cores as stored,
+//      with no per-tile work;
+//    - per element, by additions only ([M] §3.5.4: segment sums formed without
+//      subtracting cumsums): below the diagonal the sum over (j, i] is the sum
+//      over j's later tokens in its 32-token tile (r_j, a table exp(r_j)), plus
+//      the totals of the whole tiles between, plus the sum over i's tile up to
+//      i (a lane scan), three terms of one sign, so the exponent carries a few
+//      ulps of its own size however large the decays; on the diagonal tile each
+//      lane adds up its own sums from its token down.  x is staged as is.  The
+//      chunk-state kernel writes ell, r and the tile totals for these heads.
 //  * Y_off uses the same lane layout: Hin (P x N, element dtype) is the A
 //    operand, the lane's C row the B operand, exp(Acs_i) one scalar per lane.
 //  * LDS operand reads are issued ahead of the MFMAs that use them (pinned by
@@ -49,11 +53,15 @@
 //  * Options: y may leave out each token's own term (C_i . B_i) x_i (the j == i
 //    entries of the diagonal tile are cleared too; the backward pass uses it);
 //    with the input entering as dt x, every x staging scale carries
-//    dt_j (the chunk-state kernel provides Acs_j - ln dt_j); the skip term
-//    D_h x is added to each finished 16-byte piece of y before its store.
+//    dt_j (the chunk-state kernel provides Acs_j - ln dt_j; the per-element
+//    mask stages x_j dt_j); the skip term D_h x is one more operand of the
+//    diagonal tile's product (entry j == i), and a pass after the kernel adds
+//    it for the tokens whose dt is too small to divide by.
 //  * fp32 accumulation; y rounded once to the element dtype and stored with the
 //    non-temporal hint (nothing here reads it again); Hin, read here for the
-//    last time, is loaded with that hint too.
+//    last time, is loaded with that hint too.  (fp32 stores y straight from
+//    the accumulators, 16 bytes per lane, so that its tiles fit in LDS at every
+//    built chunk length and state size.)
 #include "ssd_stage.hpp"
 
 namespace ssd {
@@ -61,8 +69,11 @@ namespace ssd {
 constexpr int kCoThreads = 512;  // 8 waves: two per SIMD, one workgroup per CU
 // mask factorisation of a head (see the header)
 constexpr int kMaskChunk = 0;  // whole chunk: x scaled by exp(-Acs_j), y by exp(Acs_i)
-constexpr int kMaskTile = 1;   // per 32-token tile
-constexpr int kMaskExact = 2;  // per element
+constexpr int kMaskExact = 2;  // per element, from addition-only segment sums
+// |dt| below which the skip term of a token is not carried through the entry
+// D_h / dt_i of the diagonal tile (it would overflow or lose x dt_i to
+// underflow); the pass after the kernel adds D_h x for those tokens
+constexpr float kSkipTinyDt = 0x1p-64f;
 
 template <class E, int Q, int N>
 struct ChunkOutputCfg {
@@ -81,9 +92,10 @@ struct ChunkOutputCfg {
   // work of a wave: one row tile; with 8 row tiles both 32-wide halves of P,
   // with fewer row tiles one half (two waves share a row tile)
   static constexpr int NPH = NI == 8 ? 2 : 1;
-  // X^T | Hin | output staging, one region (it holds the chunk's B rows while
-  // the kernel tiles are formed)
-  static constexpr size_t tiles_bytes = ((size_t)P * QP + (size_t)P * NP + (size_t)NW * 32 * YP) * sizeof(T);
+  // X^T | Hin | output staging (bf16), one region (it holds the chunk's B rows
+  // while the kernel tiles are formed)
+  static constexpr size_t tiles_bytes =
+      ((size_t)P * QP + (size_t)P * NP + (kBf16 ? (size_t)NW * 32 * YP : 0)) * sizeof(T);
   static constexpr size_t base_bytes = tiles_bytes + 2 * Q * sizeof(float);
   static constexpr size_t g_bytes = (size_t)NTILE * GV * 64 * 16;
   static constexpr bool kGLds = base_bytes + g_bytes <= (size_t)kLdsLimit;  // kernel tiles in LDS
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::tiles_bytes];
   T* XT = reinterpret_cast<T*>(smem);
   T* Hs = XT + P * QP;
-  T* Ys = Hs + P * NP;
+  T* Ys = Hs + P * NP;  // bf16 only
   __shared__ __attribute__((aligned(16))) uint4 Gs[Cfg::kGLds ? NTILE * GV * 64 : 1];
   __shared__ __attribute__((aligned(16))) float acs_s[Q];
   __shared__ __attribute__((aligned(16))) float w_s[Q];
@@ -176,45 +188,57 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   using XTile = TransTile<E, Q, P, kCoThreads, 4>;
   XTile xt;
   RowTile<E, P, N, kCoThreads> ht;
-  float a_own = 0.f, a_end = 0.f;
-  float xa4[XTile::NPT][4], xae[XTile::NPT];  // Acs of this thread's x rows and of their tile end
-  auto prefetch = [&](int h) {
+  // the chunk's total log-decay of head h0 + (lane % HB), read per head with
+  // readlane (a vector load, once: a scalar load in flight would hold up every
+  // later wait for LDS reads); it selects each head's mask factorisation
+  const float lam_v = ws.lam[k * H + h0 + lane % HB];
+  auto head_by_chunk = [&](int hh) {
+    return mask_by_chunk<E>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_v), hh)));
+  };
+  float a_own = 0.f;
+  // chunk mask: log of the staging divisor of this thread's x rows.
+  // per-element mask, in the same registers: [0][0] r of token tid (tid < Q),
+  // [0][1] dt*A of this lane's output token (lanes 0-31) or the chunk's tile
+  // totals (lane 32 + m: tile m)
+  float xa4[XTile::NPT][4];
+  const int i_tab = max(I, 0) * 32 + lr;  // this lane's token in the tables (idle waves: any)
+  auto prefetch = [&](int h, bool by_chunk) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
     ht.template load<true>(hbase + h * (int64_t)(P * N), N, P);  // Hin's last read
-    if (tid < Q) {
-      a_own = abase[h * Q + tid];
-      a_end = abase[h * Q + (tid | 31)];
-    }
+    if (tid < Q) a_own = abase[h * Q + tid];
+    if (by_chunk) {
 #pragma unroll
-    for (int i = 0; i < XTile::NPT; ++i) {
-      const int r0 = XTile::first_row(i);
-      const float4 a4 = *reinterpret_cast<const float4*>(xlbase + h * Q + r0);
-      xa4[i][0] = a4.x; xa4[i][1] = a4.y; xa4[i][2] = a4.z; xa4[i][3] = a4.w;
-      xae[i] = abase[h * Q + (r0 | 31)];
+      for (int i = 0; i < XTile::NPT; ++i) {
+        const int r0 = XTile::first_row(i);
+        const float4 a4 = *reinterpret_cast<const float4*>(xlbase + h * Q + r0);
+        xa4[i][0] = a4.x; xa4[i][1] = a4.y; xa4[i][2] = a4.z; xa4[i][3] = a4.w;
+      }
+    } else {
+      const int64_t kh = k * H + h;
+      xa4[0][0] = ws.rsuf[kh * Q + min(tid, Q - 1)];
+      const float* et_src = lane < 32 ? ws.ell + kh * Q + i_tab : ws.ttot + kh * 8 + (lane & 7);
+      xa4[0][1] = *et_src;
     }
   };
-  prefetch(h0);
-  // largest tile decay of head h0 + (lane % HB), read per head with readlane
-  // (a vector load, once: a scalar load in flight would hold up every later
-  // wait for LDS reads)
-  const float dmax_v = ws.dmax[k * H + h0 + lane % HB];
-  const float lam_v = ws.lam[k * H + h0 + lane % HB];  // the chunk's total log-decay, same lanes
+  prefetch(h0, head_by_chunk(0));
   const float dskip_v = (kOpts && p.D != nullptr) ? p.D[h0 + lane % HB] : 0.0f;  // skip weight D_h, same lanes
 
   // C row of this lane's token as MFMA B-operand slices over N, kept in
   // registers for all heads: straight from C (rows past the chunk end clamped;
   // their outputs are never stored), or in lane order from the kernel-matrix
-  // pass (coalesced)
-  CReg creg[KS];
-  if (active) {
+  // pass (coalesced).  fp32 with N > 64: read from that pass's copy at each
+  // use instead (the slices would take N/2 registers).
+  constexpr bool kCRegs = kBf16 || KS <= 32;
+  const CReg* cop_g = reinterpret_cast<const CReg*>(ws.cop) + (k * G + g) * (int64_t)(NI * KS * 64) + lane;
+  CReg creg[kCRegs ? KS : 1];
+  if (active && kCRegs) {
     if constexpr (Cfg::kGInline) {
       const T* crow = reinterpret_cast<const T*>(p.C) + ((cd.t0 + min(I * 32 + lr, L - 1)) * G + g) * N + lg * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) creg[ks] = *reinterpret_cast<const CReg*>(crow + ks * 16);
     } else {
-      const CReg* cop = reinterpret_cast<const CReg*>(ws.cop) + (k * G + g) * (int64_t)(NI * KS * 64) + lane;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) creg[ks] = cop[(I * KS + ks) * 64];
+      for (int ks = 0; ks < (kCRegs ? KS : 1); ++ks) creg[ks] = cop_g[(I * KS + ks) * 64];
     }
   }
   if constexpr (kCopyG) {
@@ -256,29 +280,25 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     const int h = h0 + hh;
     lds_barrier();  // every wave is done with the previous head's tiles
     ht.template store<NP, kBf16>(Hs);
+    // mask factorisation of this head (see the header)
+    const bool by_chunk = head_by_chunk(hh);
     if (tid < Q) {
       acs_s[tid] = a_own;
-      w_s[tid] = __expf(a_end - a_own);  // exp(Acs_e - Acs_j), e = end of j's tile
+      // exp of the sum of dt*A over the later tokens of j's tile
+      if (!by_chunk) w_s[tid] = __expf(xa4[0][0]);
     }
-    // Mask factorisation of this head (see the header): by the whole chunk when
-    // its total decay is at most e^64, else by 32-token tile when no tile
-    // decays by more than e^64 (the largest tile decay comes from the
-    // chunk-state kernel), else exact.
-    const float lam_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_v), hh));
-    const float dmax_h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dmax_v), hh));
-    const int mode = lam_h >= -64.0f ? kMaskChunk : (dmax_h <= 64.0f ? kMaskTile : kMaskExact);
-    (void)dmax_h;
-    if (mode != kMaskExact) {
-      // x_j scaled by exp(-Acs_j) (chunk) or exp(Acs_e - Acs_j) (tile)
+    if (by_chunk) {
+      // x_j scaled by exp(-Acs_j)
       float sreg[XTile::NPT][4];
 #pragma unroll
       for (int i = 0; i < XTile::NPT; ++i)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf((mode == kMaskTile ? xae[i] : 0.0f) - xa4[i][rr]);
+        for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf(-xa4[i][rr]);
       xt.template store<QP, 2, kBf16, false, kBf16>(XT, nullptr, sreg);
     } else if (kOpts && p.x_times_dt) {
-      // exact mask: x staged times dt_j, read as given (|Acs_j| is large here,
-      // so Acs_j - ln dt_j would not give ln dt_j back to fp32 precision)
+      // per-element mask: x staged times dt_j, read as given (|Acs_j| may be
+      // large here, so Acs_j - ln dt_j would not give ln dt_j back to fp32
+      // precision)
       float sreg[XTile::NPT][4];
 #pragma unroll
       for (int i = 0; i < XTile::NPT; ++i)
@@ -290,7 +310,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       xt.template store<QP, 0, kBf16, false, kBf16>(XT, nullptr);
     }
     lds_barrier();
-    if (hh + 1 < HB) prefetch(h + 1);
+    const float et = xa4[0][1];  // this head's dt*A / tile totals (per-element mask)
+    if (hh + 1 < HB) prefetch(h + 1, head_by_chunk(hh + 1));
     if (!active) continue;
 
     const int i_loc = I * 32 + lr;
@@ -326,10 +347,12 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+#pragma unroll 8
+      for (int ks = 0; ks < KS; ++ks) {
+        const float c = kCRegs ? creg[kCRegs ? ks : 0] : cop_g[(I * KS + ks) * 64];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x2(Hs[prow(j) * NP + ks * 2 + lg], creg[ks], acc[j]);
+        for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x2(Hs[prow(j) * NP + ks * 2 + lg], c, acc[j]);
+      }
     }
     const float ai = acs_s[i_loc];
     const float eo = __expf(ai);
@@ -347,12 +370,19 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           if (p.denom != nullptr) dsk *= den;
         }
         if (p.x_times_dt) {
+          // x^T_i carries dt_i: a dt too small to divide by (zero included)
+          // leaves the term to the pass after this kernel
           const float dti = p.dt[(cd.t0 + min(i_loc, L - 1)) * H + h];
-          dsk = dti == 0.0f ? 0.0f : dsk / dti;
+          dsk = fabsf(dti) < kSkipTinyDt ? 0.0f : dsk / dti;
         }
       }
     }
-    if (mode != kMaskChunk) {
+    // per-element mask: the sum of dt*A over this lane's tile up to its token
+    // (a scan over lanes 0-31, which hold the tile's tokens; lane half 1 takes
+    // the value of its row from half 0)
+    const float ci = by_chunk ? 0.0f : __shfl(seg_inclusive_sum<32>(et), lr);
+    float gsum = 0.0f;
+    if (!by_chunk) {
 #pragma unroll
       for (int j = 0; j < NPH; ++j)
 #pragma unroll
@@ -382,16 +412,14 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         }
       }
     };
-    // operands of one kernel tile: G values, x^T operands, Acs at the tile's end
+    // operands of one kernel tile: G values, x^T operands
     struct TileOps {
       uint4 g[GV];
       uint4 x[2][NPH];
-      float te;
     };
     auto load_ops = [&](int J, TileOps& o) {
       load_g(J, o.g);
       load_x(J, o.x);
-      o.te = acs_s[J * 32 + 31];
     };
     // kDiag: the diagonal tile J == I (causal mask inside the tile)
     auto tile = [&](int J, const TileOps& o, auto diag_tag, auto mode_tag) {
@@ -468,23 +496,11 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           v[r] = (!kDiag || jr + sd <= lr) ? gt[r] : 0.0f;
           if (kOpts && kDiag && jr == lr) v[r] += dsk;
         }
-      } else if (mode == kMaskTile) {
-        // x^T already carries w_j = exp(Acs_e - Acs_j); the lane factor is
-        // exp(Acs_i - Acs_e) (<= 1 below the diagonal, <= e^64 on it)
-        const float u = __expf(ai - o.te);
-        if constexpr (!kDiag) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = gt[r] * u;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
-            v[r] = (jr + sd <= lr) ? gt[r] * u : 0.0f;
-            if (kOpts && jr == lr) v[r] += dsk * u;
-          }
-        }
       } else if constexpr (!kDiag) {
-        const float u = __expf(ai - o.te);
+        // the sum over (j, i] is r_j (the w table holds exp(r_j)) + the totals
+        // of the whole tiles strictly between J and I (gsum) + ci: three sums
+        // of one sign, each factor in (0, 1]
+        const float u = __expf(ci + gsum);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 w4 = *reinterpret_cast<const float4*>(w_s + J * 32 + q * 8 + lg * 4);
@@ -494,12 +510,26 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           v[4 * q + 3] = gt[4 * q + 3] * (u * w4.w);
         }
       } else {
+        // diagonal tile: the lane adds dt*A from its own token i down, and
+        // takes the running sum over (j, i] at each of its 16 columns j
+        // (columns 8q + e for lane half 0, 8q + 4 + e for half 1, e < 4: the
+        // half-1 column's sum waits in sq[e] for the half-0 column 4 below; a
+        // column past i gets an empty sum and is masked)
+        float sq[4];
+        float run = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = J * 32 + (r >> 2) * 8 + lg * 4 + (r & 3);
-          const float m = __expf(ai - acs_s[j]);
-          v[r] = (j + sd <= i_loc) ? gt[r] * m : 0.0f;
-          if (kOpts && j == i_loc) v[r] += dsk;
+        for (int jj = 31; jj >= 0; --jj) {
+          if ((jj >> 2) & 1) {
+            sq[jj & 3] = run;
+          } else {
+            const int r = (jj >> 3) * 4 + (jj & 3);
+            const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);  // j - 32J
+            const float sr = lg ? sq[jj & 3] : run;
+            v[r] = (jr + sd <= lr) ? gt[r] * __expf(sr) : 0.0f;
+            if (kOpts && jr == lr) v[r] += dsk;
+          }
+          const float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(et), jj));
+          run += jj <= lr ? e : 0.0f;
         }
       }
       // Y^T += X^T (L o G)^T over the 32 tokens of tile J
@@ -548,11 +578,27 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         tile(I, ob0, Diag(), mode_tag);
       }
     };
-    if (mode == kMaskChunk)
+    // per-element mask: the diagonal tile first, then J = I - 1 down to 0, so
+    // that gsum, the sum over the whole tiles strictly between J and I, grows
+    // by one tile total per step (additions only).  One operand buffer: the
+    // per-element work already hides the LDS reads, and a second buffer's
+    // registers would be held through the whole kernel.
+    auto diag_blocks_exact = [&]() {
+      using M = std::integral_constant<int, kMaskExact>;
+      TileOps ob;
+      load_ops(I, ob);
+      tile(I, ob, Diag(), M());
+      for (int J = I - 1; J >= 0; --J) {
+        load_ops(J, ob);
+        tile(J, ob, Off(), M());
+        gsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(et), 32 + J));
+      }
+    };
+    if (by_chunk)
       diag_blocks(std::integral_constant<int, kMaskChunk>());
-    else  // tile or exact, chosen per tile at run time
-      diag_blocks(std::integral_constant<int, kMaskTile>());
-    if (mode == kMaskChunk) {
+    else
+      diag_blocks_exact();
+    if (by_chunk) {
       // both parts of y carry exp(Acs_i) as one factor
 #pragma unroll
       for (int j = 0; j < NPH; ++j)
@@ -570,56 +616,68 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       }
     }
     // store: lane holds Y^T row pr = 32 (ph0 + j) + 8(r/4) + 4 lg + r%4 of token
-    // i_loc; bf16 rows are permuted (lds_row_perm), so its p is pr ^ c with
-    // c = 4 ((ph0 + j) & 1) + r/4: the four values of a group r/4 = q land in
-    // the 4-group 8q + 4 (lg ^ ((ph0 + j) & 1)), value e at position e ^ q.
-    // The row tile goes through this wave's LDS rows so that global stores are
-    // whole rows (of the wave's part of P) instead of scattered pieces.
-    T* ys = Ys + wid * 32 * YP;
+    // i_loc.
+    if constexpr (!kBf16) {
+      // fp32: four consecutive p per 16-byte store, straight from the accumulators
+      if (i_loc < L) {
+        T* yrow = ybase + (int64_t)i_loc * H * P + h * P;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+        for (int j = 0; j < NPH; ++j)
 #pragma unroll
-      for (int j = 0; j < NPH; ++j) {
-        if constexpr (kBf16) {
+          for (int q = 0; q < 4; ++q) {
+            const float4 v4 = make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
+            store_nt(reinterpret_cast<uint4*>(yrow + 32 * (ph0 + j) + 8 * q + 4 * lg),
+                     make_uint4(__float_as_uint(v4.x), __float_as_uint(v4.y), __float_as_uint(v4.z),
+                                __float_as_uint(v4.w)));
+          }
+      }
+    } else {
+      // bf16 rows are permuted (lds_row_perm), so its p is pr ^ c with
+      // c = 4 ((ph0 + j) & 1) + r/4: the four values of a group r/4 = q land in
+      // the 4-group 8q + 4 (lg ^ ((ph0 + j) & 1)), value e at position e ^ q.
+      // The row tile goes through this wave's LDS rows so that global stores are
+      // whole rows (of the wave's part of P) instead of scattered pieces.
+      T* ys = Ys + wid * 32 * YP;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int j = 0; j < NPH; ++j) {
           const int pp = q * 8 + 4 * (lg ^ ((ph0 + j) & 1));
           const floatx16_t& a = acc[j];
           *reinterpret_cast<uint2*>(ys + lr * YP + 32 * j + pp) =
               make_uint2(pack_bf16x2(a[4 * q + (0 ^ q)], a[4 * q + (1 ^ q)]),
                          pack_bf16x2(a[4 * q + (2 ^ q)], a[4 * q + (3 ^ q)]));
-        } else {
-          const int pp = q * 8 + lg * 4;
-          *reinterpret_cast<float4*>(ys + lr * YP + 32 * j + pp) =
-              make_float4(acc[j][4 * q + 0], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
         }
       }
-    }
-    __builtin_amdgcn_wave_barrier();
-    constexpr int VPR = NPH * 32 * sizeof(T) / 16;  // 16-byte vectors per output row
-    constexpr int RPI = 64 / VPR;                   // rows per store instruction
+      __builtin_amdgcn_wave_barrier();
+      constexpr int VPR = NPH * 32 * sizeof(T) / 16;  // 16-byte vectors per output row
+      constexpr int RPI = 64 / VPR;                   // rows per store instruction
 #pragma unroll
-    for (int s = 0; s < 32 / RPI; ++s) {
-      const int row = s * RPI + lane / VPR;
-      const int vec = lane % VPR;
-      const int i_row = I * 32 + row;
-      const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
-      if (i_row < L)
-        store_nt(reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))),
-                 val);
+      for (int s = 0; s < 32 / RPI; ++s) {
+        const int row = s * RPI + lane / VPR;
+        const int vec = lane % VPR;
+        const int i_row = I * 32 + row;
+        const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
+        if (i_row < L)
+          store_nt(reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))),
+                   val);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
-// Skip term of the tokens with dt = 0 when the input enters as dt x: their
-// staged x^T is zero, so the output kernel cannot carry D_h x for them; this
-// pass adds it to the stored output (rounded once more), one thread per
-// (token, head) and 16-byte vectors over the head's P values.
+// Skip term of the tokens whose |dt| is below kSkipTinyDt (zero included) when
+// the input enters as dt x: their staged x^T is zero or too small to carry
+// D_h x through the entry D_h / dt_i, so the output kernel leaves the term out
+// and this pass adds it to the stored output (rounded once more), one thread
+// per (token, head) and 16-byte vectors over the head's P values.
 template <class E>
 __global__ __launch_bounds__(256) void skip_zero_dt_kernel(Problem p) {
   using T = typename E::storage;
   const int64_t th = blockIdx.x * 256LL + threadIdx.x;
   if (th >= p.total * p.H) return;
-  if (p.dt[th] != 0.0f) return;
+  if (!(fabsf(p.dt[th]) < kSkipTinyDt)) return;
   const float dh = p.D[th % p.H];
   const uint4* xv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(p.x) + th * p.P);
   uint4* yv = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.y) + th * p.P);

@@ -41,6 +41,17 @@ namespace ssd {
 
 constexpr int kCsThreads = 512;  // 8 waves: two per SIMD
 
+// fp32 token blocks per chunk: the fewest whose transposed B and x blocks, the
+// staged state rows and one head's weights fit in LDS
+constexpr int cs_f32_split(int Q, int N) {
+  const int NT = N < 32 ? 32 : N;
+  for (int s = 1; s < 8; s *= 2) {
+    const int kb = Q / s + 4;
+    if ((size_t)(NT * kb + kHeadDim * kb + kHeadDim * (N + 4)) * 4 + (size_t)Q * 4 <= (size_t)kLdsLimit) return s;
+  }
+  return 8;
+}
+
 template <class E, int Q, int N>
 struct ChunkStateCfg {
   using T = typename E::storage;
@@ -49,14 +60,18 @@ struct ChunkStateCfg {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr bool SWZ = kBf16;            // bf16: swizzled, unpadded transposed tiles
   static constexpr bool kRegB = kBf16;          // B^T operands kept in registers, LDS reused
-  static constexpr int QP = SWZ ? Q : Q + PAD;  // LDS pitch of the transposed tiles
+  // fp32: the chunk's tokens go through LDS in KSPL blocks of KB (B^T and x^T
+  // staged again for every block and head); bf16: one block
+  static constexpr int KSPL = kBf16 ? 1 : cs_f32_split(Q, N);
+  static constexpr int KB = Q / KSPL;
+  static constexpr int QP = SWZ ? Q : KB + PAD;  // LDS pitch of the transposed tiles
   static constexpr int NT = N < 32 ? 32 : N;    // B^T rows, padded to an MFMA tile
   static constexpr int SP = N + PAD;            // LDS pitch of the staged state rows
   static constexpr int NTN = NT / 32;           // n tiles
   static constexpr int NTILES = NTN * (P / 32);
   // a wave's tiles: one n tile and, with more than 8 tiles, both p tiles
   static constexpr int PPW = NTILES > 8 ? 2 : 1;
-  static constexpr int KSTEPS = Q / E::kMfmaK;
+  static constexpr int KSTEPS = KB / E::kMfmaK;
   static constexpr size_t bt_bytes = (size_t)NT * QP * sizeof(T);
   static constexpr size_t xs_bytes = ((size_t)P * QP + (size_t)P * SP) * sizeof(T);
   static constexpr size_t tile_bytes = kRegB ? (bt_bytes > xs_bytes ? bt_bytes : xs_bytes) : bt_bytes + xs_bytes;
@@ -82,8 +97,9 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   using T = typename E::storage;
   constexpr bool kBf16 = Cfg::kBf16, SWZ = Cfg::SWZ, kRegB = Cfg::kRegB;
   constexpr int P = Cfg::P, QP = Cfg::QP, NT = Cfg::NT, SP = Cfg::SP, NTN = Cfg::NTN;
-  constexpr int PPW = Cfg::PPW, KSTEPS = Cfg::KSTEPS;
-  constexpr int R = Q / 64;  // tokens per lane in the cumsum
+  constexpr int PPW = Cfg::PPW, KSTEPS = Cfg::KSTEPS, KSPL = Cfg::KSPL, KB = Cfg::KB;
+  constexpr int R = Q / 64;    // tokens per lane in the cumsum
+  constexpr int SEG = 32 / R;  // lanes per 32-token tile in the cumsum
   __shared__ __attribute__((aligned(16))) char smem[Cfg::tile_bytes];
   __shared__ __attribute__((aligned(16))) float wbuf[(Cfg::kMaxHB > 0 ? Cfg::kMaxHB : 1) * Q];  // log-decays, then w
   T* bT = reinterpret_cast<T*>(smem);
@@ -130,13 +146,17 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
       if (hh >= HB) { hh -= HB; ++t; }
     }
   }
-  using BTile = TransTile<E, Q, N, kCsThreads>;
-  using XTile = TransTile<E, Q, P, kCsThreads, 4>;
+  // one token block of B and x (bf16: the whole chunk, loaded here; fp32: per
+  // block and head in the head loop)
+  using BTile = TransTile<E, KB, N, kCsThreads>;
+  using XTile = TransTile<E, KB, P, kCsThreads, 4>;
   XTile xt;
   {
     BTile bt;
-    bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
-    xt.load(xbase + h0 * P, (int64_t)H * P, L);
+    if constexpr (kBf16) {
+      bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
+      xt.load(xbase + h0 * P, (int64_t)H * P, L);
+    }
     int t = et0, hh = eh0;
 #pragma unroll
     for (int i = 0; i < Cfg::kEllPT; ++i) {
@@ -147,25 +167,35 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
     }
     if (NT > N)
       for (int i = tid; i < (NT - N) * QP; i += kCsThreads) bT[N * QP + i] = T(0);
-    bt.template store<QP, 0, false, SWZ>(bT, nullptr);
+    if constexpr (kBf16) bt.template store<QP, 0, false, SWZ>(bT, nullptr);
   }
   lds_barrier();
 
   // ---- K1: chunk-local inclusive cumsum, one wave per head (waves take heads
   // wid, wid + 8, ...); entries past the chunk end repeat the last value (their
-  // log-decay is 0) and get weight 0
+  // log-decay is 0) and get weight 0.  Every sum here only adds terms of one
+  // sign (dt*A <= 0): the weight of token l is exp of the sum of dt*A over the
+  // chunk's later tokens, summed as such ([M] §3.5.4: segment sums without
+  // differences of cumsums), never exp(Acs_end - Acs_l).
   for (int hh = wid; hh < HB; hh += kCsThreads / 64) {
     const int h = h0 + hh;
-    float run[R];
+    float el[R], run[R], sfx[R];
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      acc += wbuf[hh * Q + lane * R + i];
+      el[i] = wbuf[hh * Q + lane * R + i];
+      acc += el[i];
       run[i] = acc;
     }
-    const float incl = wave_inclusive_sum(acc);
-    const float excl = incl - acc;
-    const float lam = __shfl(incl, 63);
+    float acc2 = 0.0f;  // the lane's tokens from the last: sfx[i] sums those after i
+#pragma unroll
+    for (int i = R - 1; i >= 0; --i) {
+      sfx[i] = acc2;
+      acc2 += el[i];
+    }
+    const float excl = seg_exclusive_sum<64>(acc);          // the earlier lanes' tokens
+    const float sxcl = seg_exclusive_suffix_sum<64>(acc2);  // the later lanes' tokens
+    const float lam = __shfl(excl + run[R - 1], 63);
     float* gout = ws.acs + (k * H + h) * Q + lane * R;
     if (p.x_times_dt) {
       // the input enters as dt_l x_l: the weights carry dt_l, and the output
@@ -178,27 +208,29 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
         const float dtl = dtp[(int64_t)min(lane * R + i, L - 1) * H];
         gout[i] = a;
         xl[i] = a - __logf(dtl);
-        wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) * dtl : 0.0f;
+        wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(sxcl + sfx[i]) * dtl : 0.0f;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const float a = excl + run[i];
-        gout[i] = a;
-        wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(lam - a) : 0.0f;
+        gout[i] = excl + run[i];
+        wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(sxcl + sfx[i]) : 0.0f;
       }
     }
     if (lane == 63) ws.lam[k * H + h] = lam;
-    // largest decay over a 32-token tile, Acs[32J] - Acs[32J + 31] (the output
-    // kernel's choice of mask factorisation depends on it)
-    float dm = 0.0f;
+    if (!mask_by_chunk<E>(lam)) {
+      // the output kernel forms this head's mask per element: dt*A, its sum
+      // over the later tokens of each 32-token tile, and the tile totals
+      const float tsx = seg_exclusive_suffix_sum<SEG>(acc2);
+      float* eo = ws.ell + (k * H + h) * Q + lane * R;
+      float* ro = ws.rsuf + (k * H + h) * Q + lane * R;
 #pragma unroll
-    for (int J = 0; J < Q / 32; ++J) {
-      const float first = __shfl(excl + run[(32 * J) % R], (32 * J) / R);
-      const float last = __shfl(excl + run[(32 * J + 31) % R], (32 * J + 31) / R);
-      dm = fmaxf(dm, first - last);
+      for (int i = 0; i < R; ++i) {
+        eo[i] = el[i];
+        ro[i] = tsx + sfx[i];
+      }
+      if ((lane & (SEG - 1)) == 0) ws.ttot[(k * H + h) * 8 + lane / SEG] = tsx + acc2;
     }
-    if (lane == 0) ws.dmax[k * H + h] = dm;
   }
 
   // ---- B^T operands of this wave's n tile, for all heads (bf16)
@@ -216,70 +248,9 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   constexpr int NV = P * N / VEC;
   constexpr int VPT = (NV + kCsThreads - 1) / kCsThreads;
 
-  for (int hh = 0; hh < HB; ++hh) {
-    const int h = h0 + hh;
-    lds_barrier();  // w ready; B^T read; the previous head's x^T and state rows no longer read
-    xt.template store<QP, 1, false, SWZ>(xwT, wbuf + hh * Q);
-    lds_barrier();
-    if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
-
-    // ---- K3: S^T = B^T (w o X) on this wave's tiles
-    if (active) {
-      floatx16_t acc[PPW];
-#pragma unroll
-      for (int j = 0; j < PPW; ++j) acc[j] = zero16();
-      if constexpr (kBf16) {
-        // x^T operands of step ks + 2 are read while step ks multiplies (LDS
-        // latency is several MFMA steps): a ring of three register sets
-        int xkey[PPW];
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) xkey[j] = lds_swizzle<Q>((pt0 + j) * 32 + lr);
-        uint4 b[3][PPW];
-        auto read_x = [&](int ks, uint4 (&br)[PPW]) {
-#pragma unroll
-          for (int j = 0; j < PPW; ++j)
-            br[j] = *reinterpret_cast<const uint4*>(xwT + ((pt0 + j) * 32 + lr) * QP + ((2 * ks + lg) ^ xkey[j]) * 8);
-        };
-        read_x(0, b[0]);
-        if (KSTEPS > 1) read_x(1, b[1]);
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          if (ks + 2 < KSTEPS) read_x(ks + 2, b[(ks + 2) % 3]);
-          // keep the reads ahead: the scheduler would otherwise sink each read
-          // next to its MFMA and wait for it there
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int j = 0; j < PPW; ++j) acc[j] = mfma32x32x16(bop[ks], b[ks % 3][j], acc[j]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll 8
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const float a = bT[(nt * 32 + lr) * QP + ks * 2 + lg];
-#pragma unroll
-          for (int j = 0; j < PPW; ++j)
-            acc[j] = mfma32x32x2(a, xwT[((pt0 + j) * 32 + lr) * QP + ks * 2 + lg], acc[j]);
-        }
-      }
-      // acc[j][4q + e] = S[p = 32 (pt0 + j) + lr][n = 32 nt + 8q + 4lg + e]
-#pragma unroll
-      for (int j = 0; j < PPW; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n0 = nt * 32 + 8 * q + 4 * lg;
-          if (NT == N || n0 < N) {
-            T* dst = Ss + ((pt0 + j) * 32 + lr) * SP + n0;
-            const floatx16_t& c = acc[j];
-            if constexpr (kBf16)
-              *reinterpret_cast<uint2*>(dst) =
-                  make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
-            else
-              *reinterpret_cast<float4*>(dst) = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
-          }
-        }
-    }
-    lds_barrier();
-    // the state of (chunk, head) is one contiguous (P x N) block: whole 16-byte vectors
+  // the staged state of (chunk, head h) is one contiguous (P x N) block:
+  // whole 16-byte vectors
+  auto store_state = [&](int h) {
     T* out = reinterpret_cast<T*>(ws.states) + (k * H + h) * (int64_t)(P * N);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -303,6 +274,99 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
           }
         }
       }
+    }
+  };
+
+  // acc[j][4q + e] = S[p = 32 (pt0 + j) + lr][n = 32 nt + 8q + 4lg + e] -> Ss
+  auto stage_state = [&](const floatx16_t (&acc)[PPW]) {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n0 = nt * 32 + 8 * q + 4 * lg;
+        if (NT == N || n0 < N) {
+          T* dst = Ss + ((pt0 + j) * 32 + lr) * SP + n0;
+          const floatx16_t& c = acc[j];
+          if constexpr (kBf16)
+            *reinterpret_cast<uint2*>(dst) =
+                make_uint2(pack_bf16x2(c[4 * q], c[4 * q + 1]), pack_bf16x2(c[4 * q + 2], c[4 * q + 3]));
+          else
+            *reinterpret_cast<float4*>(dst) = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+        }
+      }
+  };
+
+  if constexpr (kBf16) {
+    for (int hh = 0; hh < HB; ++hh) {
+      const int h = h0 + hh;
+      lds_barrier();  // w ready; B^T read; the previous head's x^T and state rows no longer read
+      xt.template store<QP, 1, false, SWZ>(xwT, wbuf + hh * Q);
+      lds_barrier();
+      if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
+
+      // ---- K3: S^T = B^T (w o X) on this wave's tiles
+      if (active) {
+        floatx16_t acc[PPW];
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) acc[j] = zero16();
+        // x^T operands of step ks + 2 are read while step ks multiplies (LDS
+        // latency is several MFMA steps): a ring of three register sets
+        int xkey[PPW];
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) xkey[j] = lds_swizzle<Q>((pt0 + j) * 32 + lr);
+        uint4 b[3][PPW];
+        auto read_x = [&](int ks, uint4 (&br)[PPW]) {
+#pragma unroll
+          for (int j = 0; j < PPW; ++j)
+            br[j] = *reinterpret_cast<const uint4*>(xwT + ((pt0 + j) * 32 + lr) * QP + ((2 * ks + lg) ^ xkey[j]) * 8);
+        };
+        read_x(0, b[0]);
+        if (KSTEPS > 1) read_x(1, b[1]);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          if (ks + 2 < KSTEPS) read_x(ks + 2, b[(ks + 2) % 3]);
+          // keep the reads ahead: the scheduler would otherwise sink each read
+          // next to its MFMA and wait for it there
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < PPW; ++j) acc[j] = mfma32x32x16(bop[ks], b[ks % 3][j], acc[j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        stage_state(acc);
+      }
+      lds_barrier();
+      store_state(h);
+    }
+  } else {
+    // fp32: KSPL token blocks per head, B^T and x^T of each staged in turn
+    for (int hh = 0; hh < HB; ++hh) {
+      const int h = h0 + hh;
+      floatx16_t acc[PPW];
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) acc[j] = zero16();
+      for (int kb = 0; kb < KSPL; ++kb) {
+        const int Lb = min(KB, L - kb * KB);
+        if (Lb <= 0) break;  // past the chunk's end (the same for every thread)
+        BTile bt;
+        bt.load(reinterpret_cast<const T*>(p.B) + ((cd.t0 + kb * KB) * G + g) * N, (int64_t)G * N, Lb);
+        xt.load(xbase + (int64_t)kb * KB * H * P + h * P, (int64_t)H * P, Lb);
+        lds_barrier();  // weights ready; the previous block's tiles no longer read
+        bt.template store<QP, 0>(bT, nullptr);
+        xt.template store<QP, 1>(xwT, wbuf + hh * Q + kb * KB);
+        lds_barrier();
+        if (active) {
+#pragma unroll 8
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+            const float a = bT[(nt * 32 + lr) * QP + ks * 2 + lg];
+#pragma unroll
+            for (int j = 0; j < PPW; ++j)
+              acc[j] = mfma32x32x2(a, xwT[((pt0 + j) * 32 + lr) * QP + ks * 2 + lg], acc[j]);
+          }
+        }
+      }
+      if (active) stage_state(acc);
+      lds_barrier();
+      store_state(h);
     }
   }
 }

@@ -76,7 +76,9 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
   char* chunks = take(K * sizeof(ChunkDesc));
   char* acs = take(K * H * p.Q * sizeof(float));
   char* lam = take(K * H * sizeof(float));
-  char* dmax = take(K * H * sizeof(float));
+  char* ell = take(K * H * p.Q * sizeof(float));
+  char* rsuf = take(K * H * p.Q * sizeof(float));
+  char* ttot = take(K * H * 8 * sizeof(float));
   char* xlog = take(p.x_times_dt ? K * H * p.Q * sizeof(float) : 0);
   char* states = take(K * H * PN * esz);
   char* hin = take(K * H * PN * esz);
@@ -93,7 +95,9 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->chunks = reinterpret_cast<ChunkDesc*>(chunks);
     ws->acs = reinterpret_cast<float*>(acs);
     ws->lam = reinterpret_cast<float*>(lam);
-    ws->dmax = reinterpret_cast<float*>(dmax);
+    ws->ell = reinterpret_cast<float*>(ell);
+    ws->rsuf = reinterpret_cast<float*>(rsuf);
+    ws->ttot = reinterpret_cast<float*>(ttot);
     ws->xlog = p.x_times_dt ? reinterpret_cast<float*>(xlog) : nullptr;
     ws->states = states;
     ws->hin = hin;

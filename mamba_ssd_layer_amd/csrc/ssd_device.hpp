@@ -128,6 +128,58 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
   return v;
 }
 
+// Scans over segments of SEG consecutive lanes (SEG a power of two, <= 64).
+// They only add: an exclusive sum is the inclusive sum of the shifted values,
+// never an inclusive sum minus the lane's own value, so a sum of terms of one
+// sign carries a relative rounding error of a few ulps whatever the size of
+// the terms around it.
+template <int SEG>
+__device__ __forceinline__ float seg_inclusive_sum(float v) {
+  const int pos = threadIdx.x & (SEG - 1);
+#pragma unroll
+  for (int off = 1; off < SEG; off <<= 1) {
+    const float o = __shfl_up(v, off, kWave);
+    if (pos >= off) v += o;
+  }
+  return v;
+}
+template <int SEG>
+__device__ __forceinline__ float seg_inclusive_suffix_sum(float v) {
+  const int pos = threadIdx.x & (SEG - 1);
+#pragma unroll
+  for (int off = 1; off < SEG; off <<= 1) {
+    const float o = __shfl_down(v, off, kWave);
+    if (pos + off < SEG) v += o;
+  }
+  return v;
+}
+// sum over the lanes before this one in its segment (0 for the first)
+template <int SEG>
+__device__ __forceinline__ float seg_exclusive_sum(float v) {
+  const float e = __shfl_up(v, 1, kWave);
+  return seg_inclusive_sum<SEG>((threadIdx.x & (SEG - 1)) == 0 ? 0.0f : e);
+}
+// sum over the lanes after this one in its segment (0 for the last)
+template <int SEG>
+__device__ __forceinline__ float seg_exclusive_suffix_sum(float v) {
+  const float e = __shfl_down(v, 1, kWave);
+  return seg_inclusive_suffix_sum<SEG>((threadIdx.x & (SEG - 1)) == SEG - 1 ? 0.0f : e);
+}
+
+// Mask factorisation of one (chunk, head) of the diagonal block: by the whole
+// chunk (x_j staged times exp(-Acs_j), the finished sums times exp(Acs_i)) when
+// the chunk's total log-decay lam is at least -limit, else per element from
+// addition-only segment sums.  The limit bounds both factors (e^limit) and the
+// fp32 rounding of the cumsums they come from (an absolute error of a few
+// limit * 2^-24 in the exponent): 64 on the bf16 path, whose operands are
+// rounded to 2^-9 anyway, 16 on the fp32 path.  The chunk-state kernel (which
+// writes the per-element kernel's tables) and the output kernel decide with
+// this one function on the same stored lam.
+template <class E>
+__device__ __forceinline__ bool mask_by_chunk(float lam) {
+  return lam >= (E::kBytes == 2 ? -64.0f : -16.0f);
+}
+
 // Chunk descriptor of slot k.  Batched problems (no cu_seqlens) compute it:
 // sequence s = k / nc owns slots [s*nc, (s+1)*nc), nc = ceil(T/Q); varlen
 // problems read the table the cumsum kernel filled.

@@ -140,7 +140,12 @@ struct Workspace {
   ChunkDesc* chunks = nullptr;   // (kmax) varlen only: written by the chunk-state kernel
   float* acs = nullptr;          // (kmax, H, Q) chunk-local cumsum of dt*A
   float* lam = nullptr;          // (kmax, H)    its last entry (log of the chunk's decay)
-  float* dmax = nullptr;         // (kmax, H)    largest decay (Acs difference) over a 32-token tile
+  // Tables of the output kernel's per-element mask, written by the chunk-state
+  // kernel only for the (chunk, head) pairs that do not take the whole-chunk
+  // factorisation (mask_by_chunk false); elsewhere they are left unwritten.
+  float* ell = nullptr;          // (kmax, H, Q) dt*A per token
+  float* rsuf = nullptr;         // (kmax, H, Q) sum of dt*A over the later tokens of its 32-token tile
+  float* ttot = nullptr;         // (kmax, H, 8) sum of dt*A over each 32-token tile
   float* xlog = nullptr;         // (kmax, H, Q) Acs - ln dt, the log of x's staging divisor
                                  //              (only with x_times_dt)
   void* states = nullptr;        // (kmax, H, P, N) chunk states, element dtype

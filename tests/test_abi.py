@@ -55,12 +55,12 @@ def test_supported_set(lib):
     assert lib.ssd_config_supported(1, 128, 256) == 1
     assert lib.ssd_config_supported(1, 256, 128) == 1
     assert lib.ssd_config_supported(0, 16, 64) == 1
-    # bf16: every (N, Q) of the table, N = 256 at Q = 256 included
-    assert all(lib.ssd_config_supported(1, n, q) == 1 for n in (16, 32, 64, 128, 256) for q in (64, 128, 256))
-    # fp32 tiles that cannot fit in 160 KB of LDS
-    assert lib.ssd_config_supported(0, 128, 256) == 0
-    assert lib.ssd_config_supported(0, 256, 128) == 0
+    # every (N, Q) of the table in both dtypes, N = 256 at Q = 256 included
+    for dt in (0, 1):
+        assert all(lib.ssd_config_supported(dt, n, q) == 1 for n in (16, 32, 64, 128, 256) for q in (64, 128, 256))
+    # outside the table
     assert lib.ssd_config_supported(0, 48, 64) == 0
+    assert lib.ssd_config_supported(1, 128, 96) == 0
     assert lib.ssd_config_supported(5, 128, 64) == 0
 
 
@@ -86,7 +86,7 @@ def call_fwd(lib, **kw):
     (dict(N=48), UNSUPPORTED),
     (dict(Q=100), UNSUPPORTED),
     (dict(Q=0), INVALID),
-    (dict(N=128, Q=256, dtype=0), UNSUPPORTED),  # fp32 tiles past LDS
+    (dict(N=128, Q=64, P=32, dtype=0), UNSUPPORTED),  # head dim other than 64, fp32
     (dict(x=FAKE + 4), INVALID),        # misaligned
     (dict(y=FAKE + 8), INVALID),
     (dict(fs=FAKE + 4), INVALID),
