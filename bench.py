@@ -5,9 +5,16 @@
 One step = one full forward pass (every kernel: sequence table for varlen
 batches, chunk cumsum + chunk states, state passing, chunk output) over one batch of seeded
 synthetic inputs already resident in HBM.  The timed region is K steps
-bracketed by torch.cuda.synchronize() on both sides.  A second pass of K steps
-with per-kernel HIP events (recorded by the library on its launch stream) gives
-each kernel's average duration; the roofline of the dominant kernel uses it.
+bracketed by torch.cuda.synchronize() on both sides; before each step a 512 MiB
+read (twice the last-level cache) evicts every cached input, and HIP events on
+the launch stream around each step give its time: `value` and `ms_per_step` are
+that cold figure (mean; p10/p50/p90 under "timing"), which puts every input
+byte on the HBM.  The warm figure (K steps back to back, inputs and
+intermediates free to stay in the 256 MiB last-level cache) is reported beside
+it, labelled.  A further cold pass of K steps with per-kernel HIP events
+(recorded by the library on its launch stream) gives each kernel's average
+duration; the roofline of the dominant kernel uses it.  Under "configs" the
+other workloads' forward passes are timed the same way (T=2K among them).
 The fp64 CPU oracle is timed on the host cores on the same workload (rank 0)
 and its output also checks the GPU result.  The line also carries, under
 "decode", one recurrent decode step (ssd_decode_step) on 64 sequences of a
@@ -225,11 +232,18 @@ def bench_comparator(bd, torch, w, sec_ssd, steps, warmup):
     kms = kms[0] / kms[1] if kms[1] else None
     exps = b * T * D * N
     ach = exps / (kms / 1e3) / 1e9 if kms else None
+    frac = ach / PEAK_EXP_GPS if ach else None
+    # the speed-up at the scan's own bound: what a scan at its exp-rate peak would leave
+    bound_sec = exps / (PEAK_EXP_GPS * 1e9)
     return {"kernel": "selective_scan (diagonal A)", "batch": b, "seqlen": T, "channels": D, "dstate": N,
             "dtype": w.dtype, "us_per_step": sec * 1e6, "tokens_per_s": b * T / sec,
             "ssd_speedup": sec / sec_ssd,
+            "scan_frac_of_its_bound": frac,
+            "ssd_speedup_over_scan_at_its_bound": bound_sec / sec_ssd,
+            "note": "both warm; the scan runs below its exp-rate bound, so ssd_speedup overstates the gap "
+                    "a scan at its bound would leave (ssd_speedup_over_scan_at_its_bound)",
             "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_EXP_GPS, "unit": "Gexp/s",
-                         "frac": ach / PEAK_EXP_GPS if ach else None, "traffic": None,
+                         "frac": frac, "traffic": None,
                          "avg_launch_ms": kms, "exps_per_launch": exps}}
 
 
@@ -317,6 +331,156 @@ def load_traffic(kernel, workload):
     return d.get("bytes_per_launch")
 
 
+def load_counters(kernel, workload):
+    """Matrix-core utilisation and memory-side request counts of one kernel per
+    launch from a committed rocprofv3 counter summary (mamba_ssd_layer_amd.
+    prof_summary counters), used only while the kernel's sources still hash to
+    the value the counters were taken on; empty otherwise."""
+    from mamba_ssd_layer_amd.prof_summary import sources_hash
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{workload}.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return {"mfma_util": None, "dram_bytes": None}
+    if d.get("sources_sha256_16") != sources_hash(kernel):
+        return {"mfma_util": None, "dram_bytes": None}
+    return {"mfma_util": d.get("mfma_util"), "dram_bytes": d.get("dram_bytes_per_launch"),
+            "mfma_flops_counted_per_launch": d.get("mfma_flops_bf16_per_launch")}
+
+
+class Flusher:
+    """Reads a buffer of twice the 256 MiB last-level cache (the Infinity Cache)
+    between timed steps, so that each step finds none of its inputs in any
+    cache: its reads come from HBM.  Reads leave no dirty lines for the next
+    kernel to write back first."""
+
+    def __init__(self, torch, dev, mib=512):
+        self.buf = torch.ones((mib << 20) // 4, dtype=torch.float32, device=dev)
+        self.out = torch.empty((), dtype=torch.float32, device=dev)
+        self.torch = torch
+
+    def __call__(self):
+        self.torch.sum(self.buf, dim=0, out=self.out)
+
+
+def percentiles(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(a.mean()), "p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def time_steps(torch, step, K, flush=None):
+    """K steps bracketed by torch.cuda.synchronize() on both sides, each between
+    two HIP events on the launch stream (torch's current stream, which the
+    binding launches on); with a flush, the cache flush runs before each step's
+    first event.  Returns the per-step GPU times (ms) and the host wall time of
+    the whole region (s)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in ev], wall
+
+
+def time_back_to_back(torch, step, K):
+    """K steps back to back, host clock between two synchronisations (ms per step)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / K
+
+
+def kernel_times(bd, torch, step, K, flush=None):
+    """Average launch duration of each library kernel (ms) from the HIP events
+    the library records around its launches on the launch stream, over K steps
+    (cold when a flush runs before each step)."""
+    bd.kernel_timing_read(reset=True)
+    bd.kernel_timing_enable(True)
+    torch.cuda.synchronize()
+    for _ in range(K):
+        if flush is not None:
+            flush()
+        step()
+    torch.cuda.synchronize()
+    bd.kernel_timing_enable(False)
+    kt = bd.kernel_timing_read(reset=True)
+    return {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+
+
+def forward_setup(bd, torch, w, seed=0):
+    """Device inputs of workload w and a step() running one forward pass."""
+    import numpy as np
+    from mamba_ssd_layer_amd.workloads import make_inputs
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w, seed)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {"x": torch.from_numpy(inp.x).to(dev).to(tdt), "dt": torch.from_numpy(inp.dt).to(dev),
+         "A": torch.from_numpy(inp.A).to(dev), "B": torch.from_numpy(inp.B).to(dev).to(tdt),
+         "C": torch.from_numpy(inp.C).to(dev).to(tdt), "cu": None}
+    if inp.cu_seqlens is not None:
+        t["cu"] = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
+        seqlens = np.diff(inp.cu_seqlens).tolist()
+    else:
+        seqlens = [w.seqlen] * w.batch
+    y = torch.empty_like(t["x"])
+    fs = torch.empty((len(seqlens), w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    x, dt, A, B, C, cu = t["x"], t["dt"], t["A"], t["B"], t["C"], t["cu"]
+
+    def step():
+        if cu is None:
+            bd.ssd_chunked_fwd(x, dt, A, B, C, w.chunk_len, y=y, final_state=fs)
+        else:
+            bd.ssd_chunked_fwd_varlen(x, dt, A, B, C, cu, w.chunk_len, y=y, final_state=fs)
+
+    return inp, t, seqlens, y, step
+
+
+def flop_report(w, tokens, seqlens, sec):
+    """TFLOP/s by the executed count (C: causal halves, C B^T once per group,
+    what the kernels run) and, labelled, by the pages' per-head count (A)."""
+    from mamba_ssd_layer_amd.workloads import flops_pages
+    fl = flops_pages(w, tokens, seqlens)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    c, a = fl["C_shared_cbt"] / sec / 1e12, fl["A_pages"] / sec / 1e12
+    return {"executed_C": c, "pct_peak_executed_C": 100.0 * c / peak,
+            "pages_A": a, "pct_peak_pages_A": 100.0 * a / peak,
+            "causal_B": fl["B_causal"] / sec / 1e12, "peak": peak,
+            "note": "C: the products the kernels execute (causal tiles, C B^T once per B/C group); "
+                    "A: the per-head batched-matmul count of the pages' cost table (full Q x Q blocks)"}
+
+
+def config_line(bd, torch, w, K, W, flush):
+    """Forward of another workload: cold (cache flushed before each step) and
+    warm (back to back) times with percentiles, throughput and FLOP rates."""
+    inp, t, seqlens, y, step = forward_setup(bd, torch, w)
+    for _ in range(W):
+        step()
+    cold, _ = time_steps(torch, step, K, flush)
+    warm_ms = time_back_to_back(torch, step, K)
+    tokens = int(inp.total_tokens)
+    c = percentiles(cold)
+    sec = c["mean"] / 1e3
+    mio = min_io_bytes(w, tokens, len(seqlens))
+    del t, y
+    return {"workload": w.name, "tokens": tokens, "seqlen": w.seqlen if not w.varlen else None,
+            "batch": w.batch, "nheads": w.nheads, "dstate": w.dstate, "ngroups": w.ngroups,
+            "chunk_len": w.chunk_len, "dtype": w.dtype,
+            "cold_ms": c, "tokens_per_s": tokens / sec, "warm_ms_per_step": warm_ms,
+            "warm_tokens_per_s": tokens / (warm_ms / 1e3),
+            "tflops": flop_report(w, tokens, seqlens, sec),
+            "hbm_min_io": {"bytes": mio, "GBps": mio / sec / 1e9, "pct_peak": 100.0 * mio / sec / 1e9 / PEAK_HBM_GBS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +500,8 @@ def main():
                     help="skip the selective-scan comparison reported under \"comparator\"")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step measurement reported under \"decode\"")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' forward lines reported under \"configs\"")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (--steps times), for "
                          "scaling the HBM byte counters of a profiler")
@@ -361,62 +527,35 @@ def main():
         return
 
     from mamba_ssd_layer_amd import _binding as bd
-    from mamba_ssd_layer_amd.workloads import WORKLOADS, flops_pages, make_inputs
+    from mamba_ssd_layer_amd.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    inp = make_inputs(w, 0)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    x = torch.from_numpy(inp.x).to(dev).to(tdt)
-    dt = torch.from_numpy(inp.dt).to(dev)
-    A = torch.from_numpy(inp.A).to(dev)
-    B = torch.from_numpy(inp.B).to(dev).to(tdt)
-    C = torch.from_numpy(inp.C).to(dev).to(tdt)
-    cu = None
-    if inp.cu_seqlens is not None:
-        cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
-        seqlens = np.diff(inp.cu_seqlens).tolist()
-    else:
-        seqlens = [w.seqlen] * w.batch
+    flush = Flusher(torch, dev)
+    inp, t, seqlens, y, step = forward_setup(bd, torch, w)
+    x, dt, A, B, C, cu = t["x"], t["dt"], t["A"], t["B"], t["C"], t["cu"]
     nseq = len(seqlens)
-    y = torch.empty_like(x)
     H, P, N = w.nheads, w.headdim, w.dstate
-    fs = torch.empty((nseq, H, P, N), dtype=torch.float32, device=dev)
-
-    def step():
-        if cu is None:
-            bd.ssd_chunked_fwd(x, dt, A, B, C, w.chunk_len, y=y, final_state=fs)
-        else:
-            bd.ssd_chunked_fwd_varlen(x, dt, A, B, C, cu, w.chunk_len, y=y, final_state=fs)
+    K = args.steps
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-
-    # per-kernel durations from HIP events recorded on the launch stream
-    bd.kernel_timing_read(reset=True)
-    bd.kernel_timing_enable(True)
-    torch.cuda.synchronize()
-    te0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    te1 = time.perf_counter()
-    bd.kernel_timing_enable(False)
-    kt = bd.kernel_timing_read(reset=True)
-    kernel_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+    # warm: back to back (every input and intermediate may sit in the caches)
+    warm_ms = time_back_to_back(torch, step, K)
+    warm_ev, _ = time_steps(torch, step, K)
+    # cold (the headline): the last-level cache flushed before each step
+    cold_ev, cold_wall = time_steps(torch, step, K, flush)
+    cold = percentiles(cold_ev)
+    ms = cold["mean"]
+    # per-kernel durations, cold, from the library's events on its launch stream
+    kernel_ms = kernel_times(bd, torch, step, K, flush)
+    kernel_ms_warm = kernel_times(bd, torch, step, K)
+    # the output, for the oracle's check below (every step writes the same y)
+    y_host = None if args.no_cpu_baseline else y.float().cpu().numpy()
 
     tokens = int(inp.total_tokens)
-    fl = flops_pages(w, tokens, seqlens)
     kfl, kby = kernel_work(w, seqlens, cb_pass=kernel_ms.get("chunk_cb") is not None)
     sec = ms / 1e3
-    tflops_a = fl["A_pages"] / sec / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     # per-kernel roofline: the bound is whichever of HBM time and matrix-core
     # time is longer for the kernel's algorithmic bytes and FLOPs
@@ -436,9 +575,12 @@ def main():
         kroof[kname] = {"bound": bound, "achieved": ach, "peak": pk,
                         "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
                         "frac": (ach / pk) if ach else None, "avg_launch_ms": kms,
-                        "bytes_per_launch": kby[kname], "flops_per_launch": kfl[kname]}
+                        "avg_launch_ms_warm": kernel_ms_warm.get(kname),
+                        "bytes_per_launch": kby[kname], "flops_per_launch": kfl[kname],
+                        "mfma_tflops_executed": kfl[kname] / (kms / 1e3) / 1e12 if kms else None}
     dom = max((k for k in kroof if kroof[k]["avg_launch_ms"]), key=lambda k: kroof[k]["avg_launch_ms"])
     traffic = load_traffic(dom, w.name)
+    counters = load_counters(dom, w.name)
     mio = min_io_bytes(w, tokens, nseq)
 
     result = {
@@ -446,7 +588,7 @@ def main():
         "value": tokens / sec,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
@@ -457,14 +599,17 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen if not w.varlen else None,
                    "tokens": tokens, "nheads": H, "headdim": P, "dstate": N, "ngroups": w.ngroups,
                    "chunk_len": w.chunk_len, "varlen": w.varlen, "parallelism": "none (1 GPU)"},
-        "tflops": {"pages_A": tflops_a, "causal_B": fl["B_causal"] / sec / 1e12,
-                   "shared_cbt_C": fl["C_shared_cbt"] / sec / 1e12,
-                   "pct_peak_A": 100.0 * tflops_a / peak, "peak": peak},
+        "timing": {"value_from": "cold: mean of per-step HIP-event times, a 512 MiB read flushing the "
+                                 "last-level cache before each step (not timed)",
+                   "cold_ms": cold, "cold_wall_ms_per_step_with_flush": cold_wall * 1e3 / K,
+                   "warm_ms_per_step": warm_ms, "warm_tokens_per_s": tokens / (warm_ms / 1e3),
+                   "warm_ms": percentiles(warm_ev)},
+        "tflops": flop_report(w, tokens, seqlens, sec),
         "hbm_min_io": {"bytes": mio, "GBps": mio / sec / 1e9,
                        "pct_peak": 100.0 * mio / sec / 1e9 / PEAK_HBM_GBS},
         "kernel_ms": kernel_ms,
-        "events_pass_ms_per_step": (te1 - te0) * 1e3 / args.steps,
-        "roofline": dict(kroof[dom], kernel=dom, traffic=traffic),
+        "kernel_ms_warm": kernel_ms_warm,
+        "roofline": dict(kroof[dom], kernel=dom, traffic=traffic, **counters),
         "kernel_roofline": kroof,
         "cpu_baseline": None,
     }
@@ -472,16 +617,26 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200))
     if not args.no_normalized:
-        result["normalized"] = bench_normalized(bd, torch, w, x, dt, A, B, C, cu, sec, min(args.steps, 100),
-                                                min(args.warmup, 50))
+        result["normalized"] = bench_normalized(bd, torch, w, x, dt, A, B, C, cu, warm_ms / 1e3,
+                                                min(args.steps, 100), min(args.warmup, 50))
     if not args.no_options:
-        result["options"] = bench_options(bd, torch, w, x, dt, A, B, C, cu, sec, min(args.steps, 100),
-                                          min(args.warmup, 50))
+        result["options"] = bench_options(bd, torch, w, x, dt, A, B, C, cu, warm_ms / 1e3,
+                                          min(args.steps, 100), min(args.warmup, 50))
     if not args.no_comparator:
-        result["comparator"] = bench_comparator(bd, torch, w, sec, min(args.steps, 20), 3)
+        result["comparator"] = bench_comparator(bd, torch, w, warm_ms / 1e3, min(args.steps, 20), 3)
     if not args.no_backward:
         result["backward"] = bench_backward(bd, torch, w, x, dt, A, B, C, cu, min(args.steps, 50),
                                             min(args.warmup, 20))
+
+    if not args.no_configs:
+        del t, x, dt, A, B, C, y
+        result["configs"] = {}
+        for name in ("mamba2_2p7b_T2k", "large_state_T4k", "varlen_16seq", "long_T16k"):
+            if name == w.name:
+                continue
+            result["configs"][name] = config_line(bd, torch, WORKLOADS[name], min(K, 100),
+                                                  min(args.warmup, 200), flush)
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         import oracle
@@ -508,7 +663,7 @@ def main():
         t_o1 = time.perf_counter()
         scale = H / hs
         o_sec = (t_o1 - t_o0) / reps * scale
-        ycpu = y.float().cpu().numpy().reshape(-1, H, P)[:, sel]
+        ycpu = y_host.reshape(-1, H, P)[:, sel]
         err = float(np.max(oracle.rel_l2_per_slice(ycpu, yo, slice_axes=(1,))))
         result["cpu_baseline"] = {
             "value": tokens / o_sec, "unit": "tokens/s", "cores": oracle.max_threads(),

@@ -10,6 +10,15 @@ and the gaps between consecutive SSD kernels of one forward (run_kernel_trace.cs
 FETCH_SIZE and WRITE_SIZE of one kernel per dispatch, each scaled by what the same
 counter reads for a plain device copy of known size (bench.py --calibrate-copy),
 stamped with a hash of the kernel's sources so that a stale figure is not used.
+`counters` prints the JSON that bench.py reads for the roofline's `mfma_util` and
+`dram_bytes`: from one pass of matrix-core counters (SQ_VALU_MFMA_BUSY_CYCLES,
+SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) and one of the L2's memory-side
+request counters (TCC_EA0_RDREQ_DRAM_sum, TCC_EA0_WRREQ_DRAM_sum), the latter
+scaled to bytes by what they read for the plain device copy.  Those requests
+leave the L2 for the memory fabric: the Infinity Cache behind it may still
+serve them, so they bound the HBM traffic from above, as the cold timing of
+bench.py (the last-level cache flushed before each step) bounds it from the
+time side.
 """
 from __future__ import annotations
 
@@ -95,14 +104,62 @@ def kernels_table(trace_dir: str, first: int = 0, last: int = 0) -> str:
     return "\n".join(out)
 
 
-def _counter_per_dispatch(d: str, symbol: str, counter: str) -> float:
+def _counter_per_dispatch(d: str, symbol: str, counter: str, reduce: str = "sum") -> float:
+    """Average over the kernel's dispatches of the counter, its instances summed
+    (reduce "sum") or their largest taken (reduce "max": clocks such as
+    GRBM_GUI_ACTIVE, one per accelerator die)."""
     vals = {}
     for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
         if symbol in r["Kernel_Name"] and r["Counter_Name"] == counter:
-            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            v = float(r["Counter_Value"])
+            k = r["Dispatch_Id"]
+            if reduce == "max":
+                vals[k] = max(vals.get(k, 0.0), v)
+            else:
+                vals[k] = vals.get(k, 0.0) + v
     if not vals:
         raise SystemExit(f"no {counter} rows for {symbol} in {d}")
     return sum(vals.values()) / len(vals)
+
+
+SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
+
+
+def counters(mfma: str, dram: str, cal_dram: str, kernel: str, workload: str, copy_mib: int,
+             commands: list[str]) -> dict:
+    sym = KERNEL_SYMBOL[kernel]
+    busy = _counter_per_dispatch(mfma, sym, "SQ_VALU_MFMA_BUSY_CYCLES")
+    mops = _counter_per_dispatch(mfma, sym, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    active = _counter_per_dispatch(mfma, sym, "GRBM_GUI_ACTIVE", "max")
+    rd = _counter_per_dispatch(dram, sym, "TCC_EA0_RDREQ_DRAM_sum")
+    wr = _counter_per_dispatch(dram, sym, "TCC_EA0_WRREQ_DRAM_sum")
+    crd = _counter_per_dispatch(cal_dram, COPY_KERNEL, "TCC_EA0_RDREQ_DRAM_sum")
+    cwr = _counter_per_dispatch(cal_dram, COPY_KERNEL, "TCC_EA0_WRREQ_DRAM_sum")
+    moved = copy_mib * float(1 << 20)
+    rs, ws = moved / crd, moved / cwr
+    name = next(r["Kernel_Name"] for r in csv.DictReader(open(os.path.join(mfma, "run_counter_collection.csv")))
+                if sym in r["Kernel_Name"])
+    return {
+        "kernel": _short(name),
+        "workload": workload,
+        "sources": KERNEL_SOURCES[kernel],
+        "sources_sha256_16": sources_hash(kernel),
+        "mfma_busy_cycles_per_launch": busy,
+        "gpu_active_cycles_per_launch": active,
+        "mfma_util": busy / (active * SIMDS),
+        "mfma_flops_bf16_per_launch": mops * 512.0,
+        "dram_read_requests_per_launch": rd,
+        "dram_write_requests_per_launch": wr,
+        "read_bytes_per_request": rs,
+        "write_bytes_per_request": ws,
+        "dram_bytes_per_launch": rd * rs + wr * ws,
+        "note": ("mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); dram bytes = "
+                 "TCC_EA0_{RD,WR}REQ_DRAM_sum scaled by a plain device copy's bytes per request "
+                 "(requests that leave the L2; the Infinity Cache may still serve some)"),
+        "scale_reference": (f"plain device copy of {copy_mib} MiB (bench.py --calibrate-copy {copy_mib}): "
+                            f"{crd:.0f} read and {cwr:.0f} write requests per launch"),
+        "commands": commands,
+    }
 
 
 def traffic(fetch: str, write: str, cal_fetch: str, cal_write: str, kernel: str, workload: str,
@@ -146,9 +203,20 @@ def main(argv=None):
     t.add_argument("--workload", required=True)
     t.add_argument("--copy-mib", type=int, default=256)
     t.add_argument("--command", action="append", default=[])
+    c = sub.add_parser("counters")
+    for a_ in ("mfma", "dram", "cal_dram"):
+        c.add_argument("--" + a_.replace("_", "-"), dest=a_, required=True)
+    c.add_argument("--kernel", default="chunk_output", choices=sorted(KERNEL_SOURCES))
+    c.add_argument("--workload", required=True)
+    c.add_argument("--copy-mib", type=int, default=256)
+    c.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
         print(kernels_table(a.trace_dir, a.first, a.last))
+    elif a.cmd == "counters":
+        json.dump(counters(a.mfma, a.dram, a.cal_dram, a.kernel, a.workload, a.copy_mib, a.command),
+                  sys.stdout, indent=1)
+        print()
     else:
         json.dump(traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.kernel, a.workload, a.copy_mib,
                           a.command), sys.stdout, indent=1)
