@@ -33,15 +33,16 @@
  *   - dt * A_h <= 0 is expected (a_t in (0, 1], [T] §2.4); inputs must be
  *     finite, else results are undefined.
  *   - Supported shapes: headdim P = 64; dstate N in {16, 32, 64, 128, 256};
- *     chunk_len Q in {64, 128, 256}, minus the (dtype, Q, N) pairs whose tiles
- *     exceed the 160 KB of LDS per workgroup (ssd_config_supported tells).
- *     Any sequence length >= 0; a partial last chunk is handled.
+ *     chunk_len Q in {64, 128, 256}; every (dtype, Q, N) of these is built
+ *     (ssd_config_supported tells).  Any sequence length >= 0; a partial last
+ *     chunk is handled.
  *   - Arguments are validated on the host before anything is launched; on a
  *     validation failure nothing is written and no HIP call is made.
  *   - Execution is asynchronous on `stream` (a hipStream_t, NULL = default
  *     stream) with no host synchronisation.  Errors of kernels that already
  *     ran surface at the caller's next synchronisation, as for any stream work.
- *   - Workspace: one device allocation per (device, stream), taken with
+ *   - Workspace (every entry point but ssd_chunked_fwd_noalloc): one device
+ *     allocation per (device, stream), taken with
  *     hipMallocAsync from the device's default memory pool on first use, grown
  *     (stream-ordered free and allocation) when a larger problem arrives, and
  *     otherwise reused by every later call on that stream; it is kept until
@@ -49,8 +50,11 @@
  *     different streams use different workspaces.  Do not destroy a stream
  *     while this library's work is pending on it and then reuse its handle
  *     for a new stream before that work has finished.
- *   - Thread-safe: the workspace table and the optional kernel timing below
- *     are the only global state, both guarded by locks.
+ *   - Thread-safe: the workspace table, the per-device address of the
+ *     no-allocation entry point's scratch and the optional kernel timing
+ *     below are the only host-side global state, each guarded by a lock (the
+ *     scratch array itself is shared on the device: see
+ *     ssd_chunked_fwd_noalloc).
  *   - Return value: SSD_OK or an error code; nothing is thrown or aborted.
  */
 #ifndef SSD_H_
@@ -67,7 +71,8 @@ typedef enum ssd_status {
   SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, H % G != 0 */
   SSD_ERR_UNSUPPORTED = 2,      /* shape/dtype outside the built set, or not a gfx950 device */
   SSD_ERR_HIP = 3,              /* a HIP runtime call or kernel launch failed */
-  SSD_ERR_OUT_OF_MEMORY = 4     /* workspace allocation failed */
+  SSD_ERR_OUT_OF_MEMORY = 4,    /* workspace allocation failed */
+  SSD_ERR_SCRATCH_LIMIT = 5     /* ssd_chunked_fwd_noalloc: the workspace exceeds its static scratch */
 } ssd_status;
 
 typedef enum ssd_dtype { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
@@ -89,6 +94,31 @@ ssd_status ssd_chunked_fwd(const void* x, const float* dt, const float* A_head,
                            int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
                            int32_t chunk_len, ssd_dtype dtype, void* y, float* final_state,
                            void* stream);
+
+/*
+ * ssd_chunked_fwd without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Arguments, results and kernels are those of
+ * ssd_chunked_fwd (the caller passes every input and output); the workspace
+ * (chunk cumsums, chunk states, passed states) lives in a static device array
+ * of SSD_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends, in place of the per-stream cached allocation.
+ * The call makes no hipMalloc, hipFree or other allocating call.
+ *   - A problem whose workspace exceeds the array returns
+ *     SSD_ERR_SCRATCH_LIMIT, checked on the host before any HIP call (at
+ *     nheads 32, dstate 128, bf16, chunk_len 256 the limit is about 28K
+ *     tokens; the workspace grows with tokens x nheads x dstate).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (on different streams, or from several host threads)
+ *     race on it and give undefined results; issue them on one stream.  The
+ *     array keeps the last call's contents; nothing in it needs clearing.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((int64_t)128 << 20)
+ssd_status ssd_chunked_fwd_noalloc(const void* x, const float* dt, const float* A_head,
+                                   const void* B, const void* C, int64_t batch, int64_t seqlen,
+                                   int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                   int32_t chunk_len, ssd_dtype dtype, void* y, float* final_state,
+                                   void* stream);
 
 /*
  * Variable-length forward ([M] §3.7.3: the batch is one packed sequence with
@@ -314,8 +344,10 @@ const char* ssd_status_string(ssd_status status);
  * blocks, state-to-output), 4 separate kernel-matrix pass (only the
  * configurations whose chunk-output kernel cannot hold the tiles in LDS:
  * fp32, and bf16 with dstate 256 at chunk_len 256), 5 decode step, 6 the
- * backward pass's glue kernels (its forward-kernel passes count under 1-4).
- * Ids 0..6; another id is SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
+ * backward pass's glue kernels (its forward-kernel passes count under 1-4),
+ * 7 the diagonal selective scan (ssd_selective_scan), 8 the normalised
+ * output's ones-column chunk states and denominator.  Ids 0..8; another id
+ * is SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
  * Not re-entrant with concurrent forward calls.
  */
 ssd_status ssd_kernel_timing_enable(int32_t enable);

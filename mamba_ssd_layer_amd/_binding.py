@@ -21,7 +21,7 @@ SSD_OK = 0
 SSD_DTYPE_F32 = 0
 SSD_DTYPE_BF16 = 1
 _STATUS = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARGUMENT", 2: "SSD_ERR_UNSUPPORTED",
-           3: "SSD_ERR_HIP", 4: "SSD_ERR_OUT_OF_MEMORY"}
+           3: "SSD_ERR_HIP", 4: "SSD_ERR_OUT_OF_MEMORY", 5: "SSD_ERR_SCRATCH_LIMIT"}
 
 # Every function include/ssd.h declares, with its ctypes signature.
 _vp, _fp, _i32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
@@ -29,6 +29,8 @@ _i64, _i32 = ctypes.c_int64, ctypes.c_int32
 SIGNATURES = {
     "ssd_chunked_fwd": ([_vp, _fp, _fp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                          _i32, _vp, _fp, _vp], ctypes.c_int),
+    "ssd_chunked_fwd_noalloc": ([_vp, _fp, _fp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _vp, _fp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_varlen": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _vp, _fp, _vp], ctypes.c_int),
     "ssd_chunked_fwd_ex": ([_vp, _fp, _fp, _vp, _vp, _i32p, _i64, _i64, _i32, _i32, _i32, _i32,
@@ -148,6 +150,32 @@ def ssd_chunked_fwd(x, dt, A_head, B, C, chunk_len: int, y=None, final_state=Non
                                G, int(chunk_len), _dtype_code(x), _ptr(y), _ptr(final_state),
                                ctypes.c_void_p(_stream_ptr(dev)))
     _check(rc, "ssd_chunked_fwd")
+    return y, final_state
+
+
+def ssd_chunked_fwd_noalloc(x, dt, A_head, B, C, chunk_len: int, y, final_state=None):
+    """ssd_chunked_fwd through the entry point that allocates nothing (its
+    workspace is the library's static device scratch): the caller passes y and
+    optionally final_state, and nothing is allocated here either."""
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, nheads, headdim)")
+    b, T, H, P = x.shape
+    G, N = B.shape[-2:]
+    dev = x.device
+    for t, n, d in ((x, "x", x.dtype), (dt, "dt", torch.float32), (A_head, "A_head", torch.float32),
+                    (B, "B", x.dtype), (C, "C", x.dtype), (y, "y", x.dtype)):
+        _need(t, n, d, dev)
+    if tuple(dt.shape) != (b, T, H) or tuple(A_head.shape) != (H,) or \
+            tuple(B.shape) != (b, T, G, N) or tuple(C.shape) != (b, T, G, N) or y.shape != x.shape:
+        raise ValueError("inconsistent shapes")
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, dev)
+        if tuple(final_state.shape) != (b, H, P, N):
+            raise ValueError("final_state must be (b,H,P,N)")
+    rc = lib().ssd_chunked_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), b, T, H, P, N,
+                                       G, int(chunk_len), _dtype_code(x), _ptr(y), _ptr(final_state),
+                                       ctypes.c_void_p(_stream_ptr(dev)))
+    _check(rc, "ssd_chunked_fwd_noalloc")
     return y, final_state
 
 

@@ -275,17 +275,22 @@ void* ws_acquire(int device, size_t bytes, hipStream_t stream, int slot = 0) {
 }
 }  // namespace
 
-static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg) {
+// fixed_base: the workspace to use (at least workspace_layout's bytes, checked
+// by the caller), in place of the per-stream cached allocation.
+static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg, char* fixed_base = nullptr) {
   ssd_status st = validate(p);
   if (st != SSD_OK) return st;
   st = check_device();
   if (st != SSD_OK) return st;
   if (p.nseq == 0) return SSD_OK;
   const size_t bytes = workspace_layout(p, nullptr, nullptr);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
-  char* base = static_cast<char*>(ws_acquire(dev, bytes, stream));
-  if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  char* base = fixed_base;
+  if (base == nullptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    base = static_cast<char*>(ws_acquire(dev, bytes, stream));
+    if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  }
   Workspace ws;
   workspace_layout(p, base, &ws);
   if (dbg && dbg->hin_buf) ws.hin = dbg->hin_buf;
@@ -332,6 +337,37 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg)
 }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------ static scratch ----
+// The workspace of ssd_chunked_fwd_noalloc: a file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends.  In
+// host code `scratch` is a host-side stand-in for the symbol, not a device
+// address: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// passed to kernels.
+constexpr size_t kScratchBytes = (size_t)SSD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[64] = {nullptr};
+}  // namespace
+
+// Device address of the current device's scratch array (looked up on the
+// device's first call).
+static ssd_status scratch_base(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SSD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SSD_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return SSD_OK;
+}
 
 }  // namespace ssd
 
@@ -392,6 +428,28 @@ ssd_status ssd_chunked_fwd(const void* x, const float* dt, const float* A_head, 
   const Problem p = make_problem(x, dt, A_head, B, C, nullptr, batch, seqlen, batch * seqlen,
                                  nheads, headdim, dstate, ngroups, chunk_len, dtype, y, final_state);
   return run(p, static_cast<hipStream_t>(stream), nullptr);
+}
+
+ssd_status ssd_chunked_fwd_noalloc(const void* x, const float* dt, const float* A_head,
+                                   const void* B, const void* C, int64_t batch, int64_t seqlen,
+                                   int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                   int32_t chunk_len, ssd_dtype dtype, void* y, float* final_state,
+                                   void* stream) {
+  if (batch < 0 || seqlen < 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && seqlen > ((int64_t)1 << 40) / batch) return SSD_ERR_INVALID_ARGUMENT;
+  const Problem p = make_problem(x, dt, A_head, B, C, nullptr, batch, seqlen, batch * seqlen,
+                                 nheads, headdim, dstate, ngroups, chunk_len, dtype, y, final_state);
+  // host-side checks first: nothing is looked up or launched for a problem
+  // that is invalid or does not fit
+  ssd_status st = validate(p);
+  if (st != SSD_OK) return st;
+  if (workspace_layout(p, nullptr, nullptr) > kScratchBytes) return SSD_ERR_SCRATCH_LIMIT;
+  st = check_device();
+  if (st != SSD_OK) return st;
+  char* base = nullptr;
+  st = scratch_base(&base);
+  if (st != SSD_OK) return st;
+  return run(p, static_cast<hipStream_t>(stream), nullptr, base);
 }
 
 ssd_status ssd_chunked_fwd_varlen(const void* x, const float* dt, const float* A_head,
@@ -859,6 +917,7 @@ const char* ssd_status_string(ssd_status status) {
     case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
     case SSD_ERR_HIP: return "SSD_ERR_HIP";
     case SSD_ERR_OUT_OF_MEMORY: return "SSD_ERR_OUT_OF_MEMORY";
+    case SSD_ERR_SCRATCH_LIMIT: return "SSD_ERR_SCRATCH_LIMIT";
   }
   return "SSD_ERR_UNKNOWN";
 }

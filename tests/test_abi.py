@@ -261,3 +261,27 @@ def test_timing_read_rejects_bad_kernel(lib):
     ms = ctypes.c_double(0)
     n = ctypes.c_int64(0)
     assert lib.ssd_kernel_timing_read(9, ctypes.byref(ms), ctypes.byref(n), 0) == INVALID
+
+
+def call_noalloc(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, b=1, T=256, H=4, P=64, N=128, G=1, Q=256,
+             dtype=1, y=FAKE, fs=None)
+    a.update(kw)
+    return lib.ssd_chunked_fwd_noalloc(a["x"], a["dt"], a["A"], a["B"], a["C"], a["b"], a["T"], a["H"],
+                                       a["P"], a["N"], a["G"], a["Q"], a["dtype"], a["y"], a["fs"], None)
+
+
+SCRATCH_LIMIT = 5
+
+
+def test_noalloc_rejects_beyond_its_scratch(lib):
+    """The entry point that allocates nothing refuses, on the host and before any
+    HIP call, a problem whose workspace exceeds its static scratch, and
+    validates its arguments as ssd_chunked_fwd does before that."""
+    assert lib.ssd_status_string(SCRATCH_LIMIT) == b"SSD_ERR_SCRATCH_LIMIT"
+    # 64K tokens of 32 heads, dstate 128, bf16, chunk 256: about twice the scratch
+    assert call_noalloc(lib, b=1, T=65536, H=32) == SCRATCH_LIMIT
+    assert call_noalloc(lib, b=8, T=2048, H=80) == SCRATCH_LIMIT
+    for kw, code in ((dict(H=3, G=2), INVALID), (dict(N=48), UNSUPPORTED), (dict(x=FAKE + 4), INVALID),
+                     (dict(b=-1), INVALID), (dict(H=32, T=65536, y=None), INVALID)):
+        assert call_noalloc(lib, **kw) == code, kw
