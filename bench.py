@@ -502,6 +502,9 @@ def main():
                     help="skip the decode-step measurement reported under \"decode\"")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads' forward lines reported under \"configs\"")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="time the forward only with the cache flushed (no warm passes): for profiler "
+                         "runs whose per-dispatch averages should see cold steps only")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (--steps times), for "
                          "scaling the HBM byte counters of a profiler")
@@ -541,15 +544,18 @@ def main():
     for _ in range(args.warmup):
         step()
     # warm: back to back (every input and intermediate may sit in the caches)
-    warm_ms = time_back_to_back(torch, step, K)
-    warm_ev, _ = time_steps(torch, step, K)
+    if args.cold_only:
+        warm_ms, warm_ev = float("nan"), [float("nan")]
+    else:
+        warm_ms = time_back_to_back(torch, step, K)
+        warm_ev, _ = time_steps(torch, step, K)
     # cold (the headline): the last-level cache flushed before each step
     cold_ev, cold_wall = time_steps(torch, step, K, flush)
     cold = percentiles(cold_ev)
     ms = cold["mean"]
     # per-kernel durations, cold, from the library's events on its launch stream
     kernel_ms = kernel_times(bd, torch, step, K, flush)
-    kernel_ms_warm = kernel_times(bd, torch, step, K)
+    kernel_ms_warm = {} if args.cold_only else kernel_times(bd, torch, step, K)
     # the output, for the oracle's check below (every step writes the same y)
     y_host = None if args.no_cpu_baseline else y.float().cpu().numpy()
 

@@ -335,6 +335,20 @@ int32_t ssd_config_supported(ssd_dtype dtype, int32_t dstate, int32_t chunk_len)
 const char* ssd_status_string(ssd_status status);
 
 /*
+ * Host-side check of the workspace layouts (no device needed, nothing is
+ * allocated or launched): every entry point that takes a workspace (forward
+ * in all its forms, the no-allocation forward, the normalised forward, the
+ * backward's routes) is run over a grid of dtypes, chunk lengths, state sizes,
+ * lengths, head/group counts and options with fake device pointers, up to the
+ * point where its workspace is carved; each carving is checked to put every
+ * non-null piece inside the allocation and no two pieces on the same bytes,
+ * with absent (zero-byte) pieces null.  The same check runs on every real
+ * call before anything is launched (a failure there returns SSD_ERR_HIP and
+ * launches nothing).  Returns the number of failed layouts (0: all pass).
+ */
+int32_t ssd_workspace_selfcheck(void);
+
+/*
  * Optional per-kernel timing (process-wide, off by default).  While enabled,
  * every launch is bracketed by two HIP events recorded on the launch stream.
  * ssd_kernel_timing_read synchronises those events, adds their elapsed times

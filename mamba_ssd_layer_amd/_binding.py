@@ -50,6 +50,7 @@ SIGNATURES = {
     "ssd_chunk_slots": ([_i64, _i64, _i32, _i32], ctypes.c_int64),
     "ssd_config_supported": ([_i32, _i32, _i32], ctypes.c_int32),
     "ssd_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "ssd_workspace_selfcheck": ([], ctypes.c_int32),
     "ssd_kernel_timing_enable": ([_i32], ctypes.c_int),
     "ssd_kernel_timing_read": ([_i32, ctypes.POINTER(ctypes.c_double),
                                 ctypes.POINTER(ctypes.c_int64), _i32], ctypes.c_int),

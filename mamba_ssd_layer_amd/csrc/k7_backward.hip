@@ -641,6 +641,18 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(kBwThreads) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)kBwThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBwThreads)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + kBwThreads - 1) / kBwThreads, 4096);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(kBwThreads), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_backward_pad(const PadArgs& a, int stage, hipStream_t s) {
   const dim3 blk(kBwThreads);
   if (stage == 0) {

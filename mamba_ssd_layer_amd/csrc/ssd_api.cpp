@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <stdlib.h>
 #include <string.h>
 #include <vector>
 
@@ -27,6 +28,14 @@ bool config_supported(Dtype dt, int Q, int N) {
 }
 
 static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool poison_workspace() {
+  static const bool on = [] {
+    const char* v = getenv("SSD_POISON_WORKSPACE");
+    return v != nullptr && v[0] == '1';
+  }();
+  return on;
+}
 
 constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
 
@@ -60,16 +69,14 @@ int heads_per_block(const Problem& p, int max_hb) {
   return best;
 }
 
-size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
+size_t workspace_layout(const Problem& p, char* base, Workspace* ws, Carver* carver) {
   const size_t S = (size_t)p.nseq, K = (size_t)p.kmax, H = (size_t)p.H;
   const size_t PN = (size_t)p.P * p.N;
   const size_t esz = p.dtype == Dtype::BF16 ? 2 : 4;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = align_up(off + bytes);
-    return base ? base + at : nullptr;
-  };
+  Carver local;
+  Carver& cv = carver ? *carver : local;
+  cv.reset(base);
+  auto take = [&](size_t bytes) { return cv.take(bytes); };
   char* seq_off = take((S + 1) * sizeof(int32_t));
   char* seq_start = take(S * sizeof(int64_t));
   char* seq_len = take(S * sizeof(int64_t));
@@ -106,7 +113,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws) {
     ws->zs = p.denom ? zs : nullptr;
     ws->zin = p.denom ? zin : nullptr;
   }
-  return off;
+  return cv.off;
 }
 
 // ------------------------------------------------------------ timing ----
@@ -160,8 +167,32 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
 }
 }  // namespace
 
+// ------------------------------------------------------------- dry run ----
+// Layout check without a device: while g_dry is set on a thread, the entry
+// points validate and carve their workspaces from a fake base address, check
+// the pieces (Carver::check; a failure counts in g_dry_bad) and return before
+// any HIP call.  Used by workspace_selfcheck only.
+namespace {
+thread_local bool g_dry = false;
+thread_local int g_dry_bad = 0;
+thread_local int64_t g_dry_checks = 0;
+char* const kDryBase = reinterpret_cast<char*>((uintptr_t)1 << 40);
+}  // namespace
+
+// In a dry run: count a failed layout check.  Otherwise: whether the carved
+// pieces passed (a failure is a layout defect; the caller launches nothing).
+static bool layout_ok(const Carver& cv, size_t capacity) {
+  const bool ok = cv.check(capacity);
+  if (g_dry) {
+    ++g_dry_checks;
+    if (!ok) ++g_dry_bad;
+  }
+  return ok;
+}
+
 // ----------------------------------------------------------- device check ----
 static ssd_status check_device() {
+  if (g_dry) return SSD_OK;
   static std::mutex mu;
   static int known[64] = {0};  // 0 unknown, 1 gfx950, -1 other
   int dev = 0;
@@ -284,7 +315,7 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg,
   if (st != SSD_OK) return st;
   if (p.nseq == 0) return SSD_OK;
   const size_t bytes = workspace_layout(p, nullptr, nullptr);
-  char* base = fixed_base;
+  char* base = g_dry ? kDryBase : fixed_base;
   if (base == nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
@@ -292,7 +323,14 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg,
     if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
   }
   Workspace ws;
-  workspace_layout(p, base, &ws);
+  Carver cv;
+  workspace_layout(p, base, &ws, &cv);
+  if (!layout_ok(cv, bytes)) return g_dry ? SSD_OK : SSD_ERR_HIP;  // a layout defect: launch nothing
+  if (g_dry) return SSD_OK;
+  if (poison_workspace()) {
+    const hipError_t pe = launch_fill_u32(reinterpret_cast<uint32_t*>(base), (int64_t)(bytes / 4), kPoisonNaN, stream);
+    if (pe != hipSuccess) return map_err(pe);
+  }
   if (dbg && dbg->hin_buf) ws.hin = dbg->hin_buf;
   hipError_t e = hipSuccess;
   const size_t KH = (size_t)p.kmax * p.H;
@@ -447,8 +485,10 @@ ssd_status ssd_chunked_fwd_noalloc(const void* x, const float* dt, const float* 
   st = check_device();
   if (st != SSD_OK) return st;
   char* base = nullptr;
-  st = scratch_base(&base);
-  if (st != SSD_OK) return st;
+  if (!g_dry) {
+    st = scratch_base(&base);
+    if (st != SSD_OK) return st;
+  }
   return run(p, static_cast<hipStream_t>(stream), nullptr, base);
 }
 
@@ -654,13 +694,9 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
   const bool rx = !dbdc;                                // role-exchanged dB, dC passes
   const bool f32c = bf16 && !cdl;                       // fp32 copies of the inputs
   const bool fpass = !cdl;                              // fp32 recompute and reversed passes
-  size_t off = 0;
+  Carver cv;
   char* base = nullptr;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = align_up(off + bytes);
-    return base ? base + at : nullptr;
-  };
+  auto take = [&](size_t bytes) { return cv.take(bytes); };
   // longest possible sequence: seqlen (batched), total_len (packed)
   const int64_t maxlen = cu_seqlens == nullptr ? seqlen : total_len;
   const int64_t nseg64 = std::max<int64_t>(1, (maxlen + kBwdScanSeg - 1) / kBwdScanSeg);
@@ -670,7 +706,7 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
   b.nseg = nseg;
   float* part = nullptr;  // fp32 partial dC, dB of the head subsets
   auto layout = [&]() {
-    off = 0;
+    cv.reset(base);
     b.xr = take(T * H * P * e);
     b.Br = take(T * G * N * e);
     b.Cr = take(T * G * N * e);
@@ -710,11 +746,22 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
     b.edot = reinterpret_cast<float*>(take(fpass ? S * H * 4 : 0));
   };
   layout();
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
-  base = static_cast<char*>(ws_acquire(dev, off > 0 ? off : 256, s, 1));
-  if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  const size_t off = cv.off;
+  if (g_dry) {
+    base = kDryBase;
+  } else {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    base = static_cast<char*>(ws_acquire(dev, off > 0 ? off : 256, s, 1));
+    if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  }
   layout();
+  if (!layout_ok(cv, off)) return g_dry ? SSD_OK : SSD_ERR_HIP;  // a layout defect: launch nothing
+  if (g_dry) return SSD_OK;
+  if (poison_workspace()) {
+    const hipError_t pe = launch_fill_u32(reinterpret_cast<uint32_t*>(base), (int64_t)(off / 4), kPoisonNaN, s);
+    if (pe != hipSuccess) return map_err(pe);
+  }
   if (!initial_state) b.h0c = nullptr;
   if (!dfinal_state) b.dfb = nullptr, b.hlast = nullptr;
   if (!rx) b.xc = b.xb = b.cb = b.y_c = b.y_b = nullptr, b.dtc = b.dtb = b.Ac = b.h0c = b.dfb = nullptr;
@@ -847,17 +894,13 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
   const int64_t S = nseqs, T = total_len, S1 = nseqs + 1;
   const int64_t Tp = (T + S * (Qp - 1) + Qp - 1) / Qp * Qp;
   const size_t H = nheads, P = headdim, N = dstate, G = ngroups, PN = P * N;
-  size_t off = 0;
+  Carver cv;
   char* base = nullptr;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = align_up(off + bytes);
-    return base ? base + at : nullptr;
-  };
+  auto take = [&](size_t bytes) { return cv.take(bytes); };
   PadArgs a;
   float *h0p = nullptr, *dfp = nullptr, *dinitp = nullptr;
   auto layout = [&]() {
-    off = 0;
+    cv.reset(base);
     a.cup = reinterpret_cast<int32_t*>(take((size_t)(S + 2) * 4));
     a.xp = take(Tp * H * P * 2);
     a.dyp = take(Tp * H * P * 2);
@@ -873,21 +916,31 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
     dinitp = reinterpret_cast<float*>(take(dinitial_state ? S1 * H * PN * 4 : 0));
   };
   layout();
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
-  base = static_cast<char*>(ws_acquire(dev, off, s, 2));
-  if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
-  layout();
-  // absent optional arrays stay absent (a zero-byte piece still has an address)
-  if (!initial_state) h0p = nullptr;
-  if (!dfinal_state) dfp = nullptr;
-  if (!dinitial_state) dinitp = nullptr;
+  const size_t off = cv.off;
+  if (g_dry) {
+    base = kDryBase;
+  } else {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    base = static_cast<char*>(ws_acquire(dev, off, s, 2));
+    if (base == nullptr) return SSD_ERR_OUT_OF_MEMORY;
+  }
+  layout();  // absent optional arrays are zero-byte pieces: null pointers
+  if (!layout_ok(cv, off)) return g_dry ? SSD_OK : SSD_ERR_HIP;  // a layout defect: launch nothing
   a.cu = cu_seqlens;
   a.S = S; a.T = T; a.Tp = Tp; a.seqlen = cu_seqlens ? 0 : T / S;
   a.H = nheads; a.P = headdim; a.G = ngroups; a.N = dstate; a.Q = Qp;
   a.dtype = Dtype::BF16;
   a.x = x; a.dt = dt; a.B = B; a.C = C; a.dy = dy;
   a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC;
+  if (!g_dry && poison_workspace()) {
+    const hipError_t pe = launch_fill_u32(reinterpret_cast<uint32_t*>(base), (int64_t)(off / 4), kPoisonNaN, s);
+    if (pe != hipSuccess) return map_err(pe);
+  }
+  if (g_dry)  // the padded pass's own layout only: its inputs are fakes too
+    return bwd_impl(a.xp, a.dtp, A_head, a.Bp, a.Cp, a.cup, S1, Tp, nheads, headdim, dstate, ngroups, Qp, dtype, h0p,
+                    D, x_times_dt, a.dyp, dfp, const_cast<void*>(a.dxp), const_cast<float*>(a.ddtp), dA,
+                    const_cast<void*>(a.dBp), const_cast<void*>(a.dCp), dD, dinitp, stream, Qp);
   hipError_t err = timed_launch(kK7BackwardGlue, s, [&] { return launch_backward_pad(a, 0, s); });
   if (err != hipSuccess) return map_err(err);
   // per-sequence states with a zero entry for the filling sequence
@@ -922,6 +975,8 @@ const char* ssd_status_string(ssd_status status) {
   return "SSD_ERR_UNKNOWN";
 }
 
+int32_t ssd_workspace_selfcheck(void) { return workspace_selfcheck(); }
+
 ssd_status ssd_kernel_timing_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_timing = enable != 0;
@@ -953,3 +1008,57 @@ ssd_status ssd_kernel_timing_read(int32_t kernel, double* total_ms, int64_t* lau
 }
 
 }  // extern "C"
+
+namespace ssd {
+
+int workspace_selfcheck() {
+  g_dry = true;
+  g_dry_bad = 0;
+  int bad = 0;
+  // fake, aligned, never dereferenced: the dry run launches nothing
+  void* const F = reinterpret_cast<void*>((uintptr_t)1 << 32);
+  float* const Ff = static_cast<float*>(F);
+  const int32_t* const Fi = static_cast<const int32_t*>(F);
+  // every call must return SSD_OK after carving (and checking) at least one workspace
+  auto expect_ok = [&](ssd_status st) {
+    static thread_local int64_t seen = 0;
+    if (st != SSD_OK || g_dry_checks <= seen) ++bad;
+    seen = g_dry_checks;
+  };
+  for (ssd_dtype dt : {SSD_DTYPE_F32, SSD_DTYPE_BF16})
+    for (int Q : {64, 128, 256})
+      for (int N : {16, 32, 64, 128, 256})
+        for (int64_t T : {(int64_t)1, (int64_t)300, (int64_t)1024})
+          for (auto hg : {std::pair<int, int>{4, 1}, {8, 2}}) {
+            const int H = hg.first, G = hg.second;
+            const int64_t b = 3;
+            expect_ok(ssd_chunked_fwd(F, Ff, Ff, F, F, b, T, H, 64, N, G, Q, dt, F, Ff, nullptr));
+            expect_ok(ssd_chunked_fwd_noalloc(F, Ff, Ff, F, F, b, T, H, 64, N, G, Q, dt, F, nullptr, nullptr));
+            expect_ok(ssd_chunked_fwd_varlen(F, Ff, Ff, F, F, Fi, 5, b * T, H, 64, N, G, Q, dt, F, Ff, nullptr));
+            for (int opt = 0; opt < 4; ++opt) {
+              const float* Dp = (opt & 1) ? Ff : nullptr;
+              const int xdt = (opt >> 1) & 1;
+              expect_ok(ssd_chunked_fwd_ex(F, Ff, Ff, F, F, nullptr, b, b * T, H, 64, N, G, Q, dt, Ff, Dp, xdt, F,
+                                           Ff, nullptr));
+              expect_ok(ssd_chunked_fwd_ex(F, Ff, Ff, F, F, Fi, 5, b * T, H, 64, N, G, Q, dt, nullptr, Dp, xdt, F,
+                                           Ff, nullptr));
+              expect_ok(ssd_chunked_fwd_normalized(F, Ff, Ff, F, F, (opt & 2) ? Fi : nullptr, (opt & 2) ? 5 : b,
+                                                   b * T, H, 64, N, G, Q, dt, Dp, xdt, F, Ff, Ff, nullptr));
+              for (int opt2 = 0; opt2 < 4; ++opt2) {
+                const float* h0 = (opt2 & 1) ? Ff : nullptr;
+                const float* dfin = (opt2 & 2) ? Ff : nullptr;
+                float* dD = (opt & 1) ? Ff : nullptr;
+                float* dinit = (opt2 & 1) ? Ff : nullptr;
+                // batched (whole chunks when T % Q == 0, else ragged) and packed
+                expect_ok(ssd_chunked_bwd(F, Ff, Ff, F, F, nullptr, b, b * T, H, 64, N, G, Q, dt, h0, Dp, xdt, F,
+                                          dfin, F, Ff, Ff, F, F, dD, dinit, nullptr));
+                expect_ok(ssd_chunked_bwd(F, Ff, Ff, F, F, Fi, 5, b * T, H, 64, N, G, Q, dt, h0, Dp, xdt, F, dfin,
+                                          F, Ff, Ff, F, F, dD, dinit, nullptr));
+              }
+            }
+          }
+  g_dry = false;
+  return bad + g_dry_bad;
+}
+
+}  // namespace ssd

@@ -159,8 +159,46 @@ struct Workspace {
                                  // C rows in MFMA B-operand order, element dtype
 };
 
-// Bytes of workspace for p; fills *ws from base when base != nullptr.
-size_t workspace_layout(const Problem& p, char* base, Workspace* ws);
+// Carves 256-byte-aligned pieces out of one workspace allocation (host
+// side).  A piece of zero bytes is a null pointer, never an address inside
+// (or one past) the allocation: a kernel handed a non-null pointer may write
+// through it.  Every piece is logged so that check() can verify, before
+// anything is launched, that each non-null piece lies inside the allocation
+// and that no two pieces overlap.  No allocation of its own (fixed log).
+struct Carver {
+  static constexpr int kMaxPieces = 64;
+  char* base = nullptr;  // nullptr: only the size is computed
+  size_t off = 0;        // bytes carved so far (aligned)
+  int n = 0;
+  bool overflow = false;
+  size_t at[kMaxPieces], bytes[kMaxPieces];
+  void reset(char* b) { base = b; off = 0; n = 0; overflow = false; }
+  char* take(size_t nbytes) {
+    const size_t a = off;
+    off = (off + nbytes + 255) & ~(size_t)255;
+    if (nbytes == 0) return nullptr;
+    if (n < kMaxPieces) { at[n] = a; bytes[n] = nbytes; ++n; } else { overflow = true; }
+    return base ? base + a : nullptr;
+  }
+  // every logged piece inside [0, capacity), no two overlapping
+  bool check(size_t capacity) const {
+    if (overflow) return false;
+    for (int i = 0; i < n; ++i) {
+      if (at[i] > capacity || bytes[i] > capacity - at[i]) return false;
+      for (int j = 0; j < i; ++j)
+        if (at[i] < at[j] + bytes[j] && at[j] < at[i] + bytes[i]) return false;
+    }
+    return true;
+  }
+};
+
+// Bytes of workspace for p; fills *ws from base when base != nullptr.  With
+// a carver given, the pieces are logged in it (for Carver::check).
+size_t workspace_layout(const Problem& p, char* base, Workspace* ws, Carver* carver = nullptr);
+// Host self-check of the workspace layouts of the forward and the backward
+// over a set of shapes and options (fake base address, nothing launched):
+// returns the number of layouts whose pieces fail Carver::check.
+int workspace_selfcheck();
 
 // Heads per workgroup of the chunk-state and chunk-output kernels (one
 // workgroup per CU): the divisor of the heads of a group, <= kMaxHeadsPerBlock,
@@ -222,6 +260,13 @@ struct PadArgs {
 // stage 0: cup, then the padded inputs; stage 1: the results back to (T, ...)
 hipError_t launch_backward_pad(const PadArgs& a, int stage, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);  // p[0, n) = 0 (a kernel, no memset node)
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);  // p[0, n) = v (a kernel)
+// Poisoning of every workspace before use (SSD_POISON_WORKSPACE=1 in the
+// environment, read once): each call fills its workspace with quiet NaNs
+// before its kernels run, so that a kernel reading a piece it did not write
+// first turns its results into NaN.  A checking mode; off by default.
+constexpr uint32_t kPoisonNaN = 0x7fc00000u;
+bool poison_workspace();
 
 // dB and dC of the chunk-local path summed over heads per chunk (bf16, whole
 // chunks of b.Q, N in {64, 128, 256}); with nsub > 1 head subsets, part holds

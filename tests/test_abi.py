@@ -285,3 +285,11 @@ def test_noalloc_rejects_beyond_its_scratch(lib):
     for kw, code in ((dict(H=3, G=2), INVALID), (dict(N=48), UNSUPPORTED), (dict(x=FAKE + 4), INVALID),
                      (dict(b=-1), INVALID), (dict(H=32, T=65536, y=None), INVALID)):
         assert call_noalloc(lib, **kw) == code, kw
+
+
+def test_workspace_layouts_selfcheck(lib):
+    """Every workspace carving of every entry point (forward forms, the
+    no-allocation forward, the normalised forward, the backward's routes) over
+    a grid of shapes and options puts each non-null piece inside its allocation
+    with no overlap, absent pieces null (dry: fake pointers, nothing launched)."""
+    assert lib.ssd_workspace_selfcheck() == 0
