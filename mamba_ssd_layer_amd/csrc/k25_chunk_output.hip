@@ -171,8 +171,14 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   const uint4* gsrc = reinterpret_cast<const uint4*>(ws.cb) + (k * G + g) * (int64_t)(NTILE * GV * 64);
   T* ybase = reinterpret_cast<T*>(p.y) + cd.t0 * H * P;
 
-  // ---- issue the loads: B rows (kernel tiles formed here) or the kernel
-  // tiles themselves (to LDS), first head's x / Hin / Acs, C rows
+  // ---- issue the loads, in the order they are needed: the heads' chunk
+  // decays, B rows (kernel tiles formed here) or the kernel tiles themselves
+  // (to LDS), C rows, then the first head's x / Hin / Acs (which the tile
+  // formation does not wait for)
+  // the chunk's total log-decay of head h0 + (lane % HB), read per head with
+  // readlane (a vector load, once: a scalar load in flight would hold up every
+  // later wait for LDS reads); it selects each head's mask factorisation
+  const float lam_v = ws.lam[k * H + h0 + lane % HB];
   constexpr bool kCopyG = Cfg::kGLds && !Cfg::kGInline;
   constexpr int GNV = kCopyG ? NTILE * GV * 64 : 1;
   constexpr int GVPT = (GNV + kCoThreads - 1) / kCoThreads;
@@ -188,10 +194,6 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   using XTile = TransTile<E, Q, P, kCoThreads, 4>;
   XTile xt;
   RowTile<E, P, N, kCoThreads> ht;
-  // the chunk's total log-decay of head h0 + (lane % HB), read per head with
-  // readlane (a vector load, once: a scalar load in flight would hold up every
-  // later wait for LDS reads); it selects each head's mask factorisation
-  const float lam_v = ws.lam[k * H + h0 + lane % HB];
   auto head_by_chunk = [&](int hh) {
     return mask_by_chunk<E>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_v), hh)));
   };
@@ -220,9 +222,6 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       xa4[0][1] = *et_src;
     }
   };
-  prefetch(h0, head_by_chunk(0));
-  const float dskip_v = (kOpts && p.D != nullptr) ? p.D[h0 + lane % HB] : 0.0f;  // skip weight D_h, same lanes
-
   // C row of this lane's token as MFMA B-operand slices over N, kept in
   // registers for all heads: straight from C (rows past the chunk end clamped;
   // their outputs are never stored), or in lane order from the kernel-matrix
@@ -241,6 +240,9 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       for (int ks = 0; ks < (kCRegs ? KS : 1); ++ks) creg[ks] = cop_g[(I * KS + ks) * 64];
     }
   }
+  prefetch(h0, head_by_chunk(0));
+  const float dskip_v = (kOpts && p.D != nullptr) ? p.D[h0 + lane % HB] : 0.0f;  // skip weight D_h, same lanes
+
   if constexpr (kCopyG) {
 #pragma unroll
     for (int i = 0; i < GVPT; ++i)
