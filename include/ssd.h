@@ -359,8 +359,8 @@ int32_t ssd_workspace_selfcheck(void);
  * configurations whose chunk-output kernel cannot hold the tiles in LDS:
  * fp32, and bf16 with dstate 256 at chunk_len 256), 5 decode step, 6 the
  * backward pass's glue kernels (its forward-kernel passes count under 1-4),
- * 7 the diagonal selective scan (ssd_selective_scan), 8 the normalised
- * output's ones-column chunk states and denominator.  Ids 0..8; another id
+ * 7 the diagonal selective scan (ssd_selective_scan).  The normalised
+ * output's extra work runs inside kernels 1, 2 and 3.  Ids 0..7; another id
  * is SSD_ERR_INVALID_ARGUMENT.  The events add a few microseconds per launch.
  * Not re-entrant with concurrent forward calls.
  */

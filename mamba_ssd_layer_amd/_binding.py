@@ -57,7 +57,7 @@ SIGNATURES = {
 }
 
 KERNEL_NAMES = ["seq_table", "chunk_state", "state_pass", "chunk_output", "chunk_cb", "decode_step",
-                "backward_glue", "selective_scan", "denominator"]
+                "backward_glue", "selective_scan"]
 
 
 class SSDError(RuntimeError):

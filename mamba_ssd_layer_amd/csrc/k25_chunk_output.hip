@@ -74,6 +74,9 @@ constexpr int kMaskExact = 2;  // per element, from addition-only segment sums
 // D_h / dt_i of the diagonal tile (it would overflow or lose x dt_i to
 // underflow); the pass after the kernel adds D_h x for those tokens
 constexpr float kSkipTinyDt = 0x1p-64f;
+// heads per workgroup of the normalised output (its denominator's passed-state
+// term is formed for all of them at once: one MFMA row block)
+constexpr int kDenHeads = 8;
 
 template <class E, int Q, int N>
 struct ChunkOutputCfg {
@@ -92,10 +95,14 @@ struct ChunkOutputCfg {
   // work of a wave: one row tile; with 8 row tiles both 32-wide halves of P,
   // with fewer row tiles one half (two waves share a row tile)
   static constexpr int NPH = NI == 8 ? 2 : 1;
-  // X^T | Hin | output staging (bf16), one region (it holds the chunk's B rows
-  // while the kernel tiles are formed)
+  // normalised output with the dt-scaled input: the ones column's dt per token
+  static constexpr size_t den_bytes = (size_t)Q * sizeof(float);
+  static constexpr size_t ys_bytes = (size_t)NW * 32 * YP * sizeof(T);
+  // X^T | Hin | output staging (bf16; with the normalised output and the
+  // options, its dt table there instead, after them on fp32), one region (it
+  // holds the chunk's B rows while the kernel tiles are formed)
   static constexpr size_t tiles_bytes =
-      ((size_t)P * QP + (size_t)P * NP + (kBf16 ? (size_t)NW * 32 * YP : 0)) * sizeof(T);
+      ((size_t)P * QP + (size_t)P * NP) * sizeof(T) + (kBf16 ? (ys_bytes > den_bytes ? ys_bytes : den_bytes) : den_bytes);
   static constexpr size_t base_bytes = tiles_bytes + 2 * Q * sizeof(float);
   static constexpr size_t g_bytes = (size_t)NTILE * GV * 64 * 16;
   static constexpr bool kGLds = base_bytes + g_bytes <= (size_t)kLdsLimit;  // kernel tiles in LDS
@@ -107,16 +114,17 @@ struct ChunkOutputCfg {
   static constexpr bool fits = lds_bytes <= (size_t)kLdsLimit;
 };
 
-// kOpt: 0 plain; 1 the skip term, the dt-scaled input, the strict diagonal
-// and the normalised output's division; 2 that division only.  Separate
-// instantiations, so that the plain forward keeps every register it had and
-// the normalised output alone does not carry the other options' registers.
+// kOpt: bit 0 the skip term, the dt-scaled input, the strict diagonal; bit 1
+// the normalised output (its denominator formed here, y divided by it).
+// Separate instantiations, so that the plain forward keeps every register it
+// had and the normalised output alone does not carry the other options'
+// registers.
 template <class E, int Q, int N, int kOpt>
 __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, Workspace ws, int HB) {
   using Cfg = ChunkOutputCfg<E, Q, N>;
   using T = typename E::storage;
-  constexpr bool kOpts = kOpt == 1;  // skip term, dt-scaled input, strict diagonal
-  constexpr bool kDen = kOpt != 0;   // normalised output
+  constexpr bool kOpts = (kOpt & 1) != 0;  // skip term, dt-scaled input, strict diagonal
+  constexpr bool kDen = (kOpt & 2) != 0;   // normalised output
   constexpr int P = Cfg::P, NP = Cfg::NP, QP = Cfg::QP, KS = Cfg::KS, GV = Cfg::GV, YP = Cfg::YP;
   constexpr bool kBf16 = Cfg::kBf16;
   constexpr int NI = Cfg::NI, NTILE = Cfg::NTILE, NPH = Cfg::NPH;
@@ -124,7 +132,13 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::tiles_bytes];
   T* XT = reinterpret_cast<T*>(smem);
   T* Hs = XT + P * QP;
-  T* Ys = Hs + P * NP;  // bf16 only
+  T* Ys = Hs + P * NP;  // bf16 output staging (all but the normalised output with options)
+  // normalised output with options: dt_j of the ones column
+  float* const dt_s = reinterpret_cast<float*>(Ys);
+  // the normalised output with options finds its denominator in a pass of its
+  // own before the products (the skip term's entry needs it); without options
+  // the row sums ride along with the products
+  constexpr bool kDenPre = kDen && kOpts;
   __shared__ __attribute__((aligned(16))) uint4 Gs[Cfg::kGLds ? NTILE * GV * 64 : 1];
   __shared__ __attribute__((aligned(16))) float acs_s[Q];
   __shared__ __attribute__((aligned(16))) float w_s[Q];
@@ -198,6 +212,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     return mask_by_chunk<E>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_v), hh)));
   };
   float a_own = 0.f;
+  float dt_own = 1.0f;  // normalised output with the dt-scaled input: dt of token tid
   // chunk mask: log of the staging divisor of this thread's x rows.
   // per-element mask, in the same registers: [0][0] r of token tid (tid < Q),
   // [0][1] dt*A of this lane's output token (lanes 0-31) or the chunk's tile
@@ -208,6 +223,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     xt.load(xbase + h * P, (int64_t)H * P, L);
     ht.template load<true>(hbase + h * (int64_t)(P * N), N, P);  // Hin's last read
     if (tid < Q) a_own = abase[h * Q + tid];
+    if (kDen && kOpts && p.x_times_dt && tid < Q) dt_own = p.dt[(cd.t0 + min(tid, L - 1)) * H + h];
     if (by_chunk) {
 #pragma unroll
       for (int i = 0; i < XTile::NPT; ++i) {
@@ -277,6 +293,39 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // the head loop's first barrier orders these tiles before their use and
     // the B rows' last read before x^T and Hin overwrite them
   }
+  // normalised output: this lane's token's passed-state term of the
+  // denominator for heads 4 lg + e (e < 4), in registers for the head loop
+  float dofv[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kDen) {
+    // ---- normalised output: the passed-state term of the denominator for
+    // all the block's heads at once, Doff^T (heads x tokens) = Zin C^T, Zin
+    // of each head (its ones column's passed state, N values) an A-operand
+    // row and the lane's C row the B operand, as for Y_off
+    lds_barrier();  // the tile formation's B rows (same region) are no longer read
+    {
+      RowTile<E, 32, N, kCoThreads> zt;  // rows past HB stored as zeros
+      zt.load(reinterpret_cast<const T*>(ws.zin) + (k * H + h0) * (int64_t)N, N, HB);
+      zt.template store<NP>(XT);
+    }
+    lds_barrier();
+    if (active) {  // both waves of a shared row tile keep the term
+      floatx16_t accd = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (kBf16) {
+          accd = mfma32x32x16(*reinterpret_cast<const uint4*>(XT + lr * NP + ks * 16 + lg * 8), creg[ks], accd);
+        } else {
+          const float c = kCRegs ? creg[kCRegs ? ks : 0] : cop_g[(I * KS + ks) * 64];
+          accd = mfma32x32x2(XT[lr * NP + ks * 2 + lg], c, accd);
+        }
+      }
+      // accd[e] = Doff[head 4 lg + e][token 32 I + lr], kept for the head loop
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dofv[e] = accd[e];
+    }
+    // the head loop's first barrier orders the Zin rows' last read before
+    // x^T overwrites them
+  }
 
   for (int hh = 0; hh < HB; ++hh) {
     const int h = h0 + hh;
@@ -288,6 +337,23 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       acs_s[tid] = a_own;
       // exp of the sum of dt*A over the later tokens of j's tile
       if (!by_chunk) w_s[tid] = __expf(xa4[0][0]);
+      if constexpr (kDen) {
+        // the ones column's staging: exp(-Acs_j) dt_j (chunk mask; w_s is
+        // free there), dt_j (per-element mask).  bf16 without options: the
+        // chunk mask's values as bf16 pairs (j, j + 1) in word j / 2, for the
+        // products' row sums on v_dot2_f32_bf16
+        if (by_chunk) {
+          const float sj = __expf(-a_own) * dt_own;
+          if constexpr (kBf16 && !kDenPre) {
+            const float sn = __shfl_down(sj, 1, kWave);
+            if ((tid & 1) == 0) reinterpret_cast<uint32_t*>(w_s)[tid >> 1] = pack_bf16x2(sj, sn);
+          } else {
+            w_s[tid] = sj;
+          }
+        } else if (kDenPre) {
+          dt_s[tid] = dt_own;
+        }
+      }
     }
     if (by_chunk) {
       // x_j scaled by exp(-Acs_j)
@@ -317,11 +383,109 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     if (!active) continue;
 
     const int i_loc = I * 32 + lr;
-    // normalised output: the token's denominator, loaded here so that the
-    // head's products hide the load
+    // per-element mask: the sum of dt*A over this lane's tile up to its token
+    // (a scan over lanes 0-31, which hold the tile's tokens; lane half 1 takes
+    // the value of its row from half 0)
+    const float ci = by_chunk ? 0.0f : __shfl(seg_inclusive_sum<32>(et), lr);
+    // kernel tile J of row tile I as 16 fp32 values: G[i_loc][32J + 8(r/4) + 4lg + r%4]
+    auto g_values = [&](int J, float (&g)[16]) {
+      const int tl = I * (I + 1) / 2 + J;
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint4 v = Cfg::kGLds ? Gs[(tl * GV + q) * 64 + lane] : gsrc[(tl * GV + q) * 64 + lane];
+          g[8 * q + 0] = bf16_lo(v.x); g[8 * q + 1] = bf16_hi(v.x);
+          g[8 * q + 2] = bf16_lo(v.y); g[8 * q + 3] = bf16_hi(v.y);
+          g[8 * q + 4] = bf16_lo(v.z); g[8 * q + 5] = bf16_hi(v.z);
+          g[8 * q + 6] = bf16_lo(v.w); g[8 * q + 7] = bf16_hi(v.w);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = Cfg::kGLds ? Gs[(tl * GV + q) * 64 + lane] : gsrc[(tl * GV + q) * 64 + lane];
+          g[4 * q + 0] = __uint_as_float(v.x); g[4 * q + 1] = __uint_as_float(v.y);
+          g[4 * q + 2] = __uint_as_float(v.z); g[4 * q + 3] = __uint_as_float(v.w);
+        }
+      }
+    };
+    // normalised output: the token's denominator d_i, the output of the ones
+    // column, before the products (the skip term's entry and the division
+    // need it):
+    //   chunk mask:   d_i = exp(Acs_i) (Doff_i + sum_{j<=i} G_ij s_j),
+    //                 s_j = exp(-Acs_j) w_j (w_s), w_j = dt_j or 1
+    //   per element:  d_i = exp(Acs_i) Doff_i + sum_{j<=i} L_ij G_ij w_j (w_j in dt_s)
+    // with the same mask sums as the products below; the two lane halves
+    // hold different columns j of row i and add their partial sums.
     float den = 1.0f;
+    // the passed-state term of head hh at this lane's token (held by the lane
+    // of the same token in half hh / 4)
+    float dof = 0.0f;
     if constexpr (kDen) {
-      if (p.denom != nullptr) den = p.denom[(cd.t0 + min(i_loc, L - 1)) * H + h];
+      const int e = hh & 3;
+      const float mine = e == 0 ? dofv[0] : e == 1 ? dofv[1] : e == 2 ? dofv[2] : dofv[3];
+      dof = __shfl(mine, lr + 32 * (hh >> 2));
+    }
+    // row sums of the masked tiles against the ones column (both lane halves):
+    // in a pass of their own before the products with options (the skip
+    // term's entry needs the denominator) and for the per-element mask (the
+    // sums ride along the chunk mask's products only)
+    float rs = 0.0f;
+    if (kDenPre || (kDen && !by_chunk)) {
+      if (by_chunk) {
+        for (int J = 0; J <= I; ++J) {
+          float g[16];
+          g_values(J, g);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 s4 = *reinterpret_cast<const float4*>(w_s + J * 32 + q * 8 + lg * 4);
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int jr = q * 8 + lg * 4 + e;
+              rs += (J < I || jr + sd <= lr) ? g[4 * q + e] * sv[e] : 0.0f;
+            }
+          }
+        }
+        rs += __shfl_xor(rs, 32);
+        den = __expf(acs_s[i_loc]) * (dof + rs);
+      } else {
+        float gs = 0.0f;  // the whole tiles strictly between J and I
+        for (int J = I - 1; J >= 0; --J) {
+          float g[16];
+          g_values(J, g);
+          const float u = __expf(ci + gs);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 w4 = *reinterpret_cast<const float4*>(w_s + J * 32 + q * 8 + lg * 4);
+            const float4 d4 = (kOpts && p.x_times_dt) ? *reinterpret_cast<const float4*>(dt_s + J * 32 + q * 8 + lg * 4)
+                                                      : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            rs += g[4 * q + 0] * (u * w4.x) * d4.x + g[4 * q + 1] * (u * w4.y) * d4.y +
+                  g[4 * q + 2] * (u * w4.z) * d4.z + g[4 * q + 3] * (u * w4.w) * d4.w;
+          }
+          gs += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(et), 32 + J));
+        }
+        // the diagonal tile: the lane's own sums over (j, i], as in the products
+        float g[16];
+        g_values(I, g);
+        float sq[4];
+        float run = 0.0f;
+#pragma unroll
+        for (int jj = 31; jj >= 0; --jj) {
+          if ((jj >> 2) & 1) {
+            sq[jj & 3] = run;
+          } else {
+            const int r = (jj >> 3) * 4 + (jj & 3);
+            const int jr = (r >> 2) * 8 + lg * 4 + (r & 3);
+            const float sr = lg ? sq[jj & 3] : run;
+            rs += (jr + sd <= lr) ? g[r] * __expf(sr) * ((kOpts && p.x_times_dt) ? dt_s[I * 32 + jr] : 1.0f) : 0.0f;
+          }
+          const float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(et), jj));
+          run += jj <= lr ? e : 0.0f;
+        }
+        rs += __shfl_xor(rs, 32);
+        den = __expf(acs_s[i_loc]) * dof + rs;
+      }
+      if (ph0 == 0 && lg == 0 && i_loc < L) p.denom[(cd.t0 + i_loc) * H + h] = den;
     }
     floatx16_t acc[NPH];
 #pragma unroll
@@ -368,9 +532,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     if constexpr (kOpts) {
       if (p.D != nullptr) {
         dsk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dskip_v), hh));
-        if constexpr (kDen) {
-          if (p.denom != nullptr) dsk *= den;
-        }
+        if constexpr (kDen) dsk *= den;
         if (p.x_times_dt) {
           // x^T_i carries dt_i: a dt too small to divide by (zero included)
           // leaves the term to the pass after this kernel
@@ -379,10 +541,6 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         }
       }
     }
-    // per-element mask: the sum of dt*A over this lane's tile up to its token
-    // (a scan over lanes 0-31, which hold the tile's tokens; lane half 1 takes
-    // the value of its row from half 0)
-    const float ci = by_chunk ? 0.0f : __shfl(seg_inclusive_sum<32>(et), lr);
     float gsum = 0.0f;
     if (!by_chunk) {
 #pragma unroll
@@ -470,6 +628,21 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int j = 0; j < NPH; ++j) acc[j] = mfma32x32x16(xa[kk][j], b[kk], acc[j]);
+          if constexpr (kDen && !kDenPre) {
+            // the denominator's row sums: the masked tile against s_j (bf16
+            // pairs in w_s), two products per v_dot2_f32_bf16
+            const uint32_t* sw = reinterpret_cast<const uint32_t*>(w_s) + J * 16 + lg * 2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint2 s2 = *reinterpret_cast<const uint2*>(sw + q * 4);
+              const uint4& bq = b[q >> 1];
+              const uint32_t w0 = (q & 1) ? bq.z : bq.x, w1 = (q & 1) ? bq.w : bq.y;
+              rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), __builtin_bit_cast(bf16x2_t, s2.x),
+                                                   rs, false);
+              rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), __builtin_bit_cast(bf16x2_t, s2.y),
+                                                   rs, false);
+            }
+          }
           return;
         }
       }
@@ -534,6 +707,14 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
           run += jj <= lr ? e : 0.0f;
         }
       }
+      if constexpr (kDen && !kDenPre && kMode == kMaskChunk) {
+        // the denominator's row sums (fp32, chunk mask): against s_j (w_s)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 s4 = *reinterpret_cast<const float4*>(w_s + J * 32 + q * 8 + lg * 4);
+          rs += v[4 * q] * s4.x + v[4 * q + 1] * s4.y + v[4 * q + 2] * s4.z + v[4 * q + 3] * s4.w;
+        }
+      }
       // Y^T += X^T (L o G)^T over the 32 tokens of tile J
       if constexpr (kBf16) {
 #pragma unroll
@@ -563,6 +744,18 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // one copy of the loop for the chunk factorisation (no per-tile work) and
     // one for the other two
     auto diag_blocks = [&](auto mode_tag) {
+      if constexpr (kDen) {
+        // normalised output: one operand buffer (the row sums' registers
+        // would otherwise push the double-buffered loop into spills)
+        TileOps ob;
+        for (int J = 0; J < I; ++J) {
+          load_ops(J, ob);
+          tile(J, ob, Off(), mode_tag);
+        }
+        load_ops(I, ob);
+        tile(I, ob, Diag(), mode_tag);
+        return;
+      }
       TileOps ob0, ob1;
       load_ops(0, ob0);
       int J = 0;
@@ -600,6 +793,11 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       diag_blocks(std::integral_constant<int, kMaskChunk>());
     else
       diag_blocks_exact();
+    if (kDen && !kDenPre && by_chunk) {
+      rs += __shfl_xor(rs, 32);
+      den = eo * (dof + rs);
+      if (ph0 == 0 && lg == 0 && i_loc < L) p.denom[(cd.t0 + i_loc) * H + h] = den;
+    }
     if (by_chunk) {
       // both parts of y carry exp(Acs_i) as one factor
 #pragma unroll
@@ -609,13 +807,11 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     }
     if constexpr (kDen) {
       // normalised output: divided by the token's denominator before rounding
-      if (p.denom != nullptr) {
-        const float inv = 1.0f / den;
+      const float inv = 1.0f / den;
 #pragma unroll
-        for (int j = 0; j < NPH; ++j)
+      for (int j = 0; j < NPH; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[j][r] *= inv;
-      }
+        for (int r = 0; r < 16; ++r) acc[j][r] *= inv;
     }
     // store: lane holds Y^T row pr = 32 (ph0 + j) + 8(r/4) + 4 lg + r%4 of token
     // i_loc.
@@ -631,6 +827,23 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
             store_nt(reinterpret_cast<uint4*>(yrow + 32 * (ph0 + j) + 8 * q + 4 * lg),
                      make_uint4(__float_as_uint(v4.x), __float_as_uint(v4.y), __float_as_uint(v4.z),
                                 __float_as_uint(v4.w)));
+          }
+      }
+    } else if constexpr (kDenPre) {
+      // bf16, normalised output with options (its dt table occupies the
+      // staging rows): the four values of each group straight to y as 8 bytes
+      // (p permuted as below)
+      if (i_loc < L) {
+        T* yrow = ybase + (int64_t)i_loc * H * P + h * P;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < NPH; ++j) {
+            const int pp = q * 8 + 4 * (lg ^ ((ph0 + j) & 1));
+            const floatx16_t& a = acc[j];
+            *reinterpret_cast<uint2*>(yrow + 32 * (ph0 + j) + pp) =
+                make_uint2(pack_bf16x2(a[4 * q + (0 ^ q)], a[4 * q + (1 ^ q)]),
+                           pack_bf16x2(a[4 * q + (2 ^ q)], a[4 * q + (3 ^ q)]));
           }
       }
     } else {
@@ -689,14 +902,21 @@ __global__ __launch_bounds__(256) void skip_zero_dt_kernel(Problem p) {
 template <class E, int Q, int N>
 static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s) {
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
-    const int HB = heads_per_block(p);
+    const bool den = p.denom != nullptr;
+    const bool opts = p.D != nullptr || p.x_times_dt || p.strict_diag;
+    // the normalised output forms its denominator's passed-state term for at
+    // most kDenHeads heads at once
+    const int HB = heads_per_block(p, den ? kDenHeads : kMaxHeadsPerBlock);
     const unsigned blocks = (unsigned)(p.kmax * (p.H / HB));
-    if (p.D != nullptr || p.x_times_dt || p.strict_diag)
-      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 1>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
-    else if (p.denom != nullptr)
-      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 2>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+    const dim3 grid(blocks), blk(kCoThreads);
+    if (den && opts)
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 3>), grid, blk, 0, s, p, ws, HB);
+    else if (den)
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 2>), grid, blk, 0, s, p, ws, HB);
+    else if (opts)
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 1>), grid, blk, 0, s, p, ws, HB);
     else
-      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 0>), dim3(blocks), dim3(kCoThreads), 0, s, p, ws, HB);
+      hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 0>), grid, blk, 0, s, p, ws, HB);
     if (p.D != nullptr && p.x_times_dt && p.total > 0) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

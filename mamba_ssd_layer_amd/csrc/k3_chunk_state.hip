@@ -41,13 +41,21 @@ namespace ssd {
 
 constexpr int kCsThreads = 512;  // 8 waves: two per SIMD
 
+// x^T rows in LDS: the P rows of x, then one MFMA tile of 32 rows whose first
+// row carries the decay weights alone (the ones column of the normalised
+// output's denominator, [T]/[M] "Incorporating a Normalization (Denominator)
+// Term": its chunk state is the weighted sum of B rows).  The tile's other 31
+// rows are left as they are: each feeds only its own output column, and those
+// columns are not stored.
+constexpr int kXRows = kHeadDim + 32;
+
 // fp32 token blocks per chunk: the fewest whose transposed B and x blocks, the
 // staged state rows and one head's weights fit in LDS
 constexpr int cs_f32_split(int Q, int N) {
   const int NT = N < 32 ? 32 : N;
   for (int s = 1; s < 8; s *= 2) {
     const int kb = Q / s + 4;
-    if ((size_t)(NT * kb + kHeadDim * kb + kHeadDim * (N + 4)) * 4 + (size_t)Q * 4 <= (size_t)kLdsLimit) return s;
+    if ((size_t)(NT * kb + kXRows * kb + kHeadDim * (N + 4)) * 4 + (size_t)Q * 4 <= (size_t)kLdsLimit) return s;
   }
   return 8;
 }
@@ -73,7 +81,7 @@ struct ChunkStateCfg {
   static constexpr int PPW = NTILES > 8 ? 2 : 1;
   static constexpr int KSTEPS = KB / E::kMfmaK;
   static constexpr size_t bt_bytes = (size_t)NT * QP * sizeof(T);
-  static constexpr size_t xs_bytes = ((size_t)P * QP + (size_t)P * SP) * sizeof(T);
+  static constexpr size_t xs_bytes = ((size_t)kXRows * QP + (size_t)P * SP) * sizeof(T);
   static constexpr size_t tile_bytes = kRegB ? (bt_bytes > xs_bytes ? bt_bytes : xs_bytes) : bt_bytes + xs_bytes;
   // log-decays, then decay weights, of every head of the block (LDS left over
   // by the tiles bounds the heads per workgroup)
@@ -104,7 +112,10 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   __shared__ __attribute__((aligned(16))) float wbuf[(Cfg::kMaxHB > 0 ? Cfg::kMaxHB : 1) * Q];  // log-decays, then w
   T* bT = reinterpret_cast<T*>(smem);
   T* xwT = reinterpret_cast<T*>(smem + (kRegB ? 0 : Cfg::bt_bytes));
-  T* Ss = xwT + P * QP;
+  T* Ss = xwT + kXRows * QP;
+  // normalised output: the chunk state of the ones column (the weighted sum of
+  // the chunk's B rows) of every head goes to ws.zs
+  const bool zcol = ws.zs != nullptr;
 
   const int H = p.H, G = p.G;
   const int nhb = H / HB;
@@ -296,11 +307,38 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
       }
   };
 
+  // the ones column's chunk state from its MFMA tile: lanes of row 0 (lr == 0)
+  // hold Zs[n = 32 nt + 8q + 4lg + e] at accz[4q + e]
+  const bool zwave = zcol && active && pt0 == 0;
+  auto store_z = [&](int h, const floatx16_t& accz) {
+    if (lr != 0) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = nt * 32 + 8 * q + 4 * lg + e;
+        if (NT == N || n < N) {
+          T* dst = reinterpret_cast<T*>(ws.zs) + (k * H + h) * (int64_t)N + n;
+          if constexpr (kBf16)
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16x2(accz[4 * q + e], 0.0f) & 0xffffu);
+          else
+            *dst = accz[4 * q + e];
+        }
+      }
+  };
+
   if constexpr (kBf16) {
     for (int hh = 0; hh < HB; ++hh) {
       const int h = h0 + hh;
       lds_barrier();  // w ready; B^T read; the previous head's x^T and state rows no longer read
       xt.template store<QP, 1, false, SWZ>(xwT, wbuf + hh * Q);
+      if (zcol && tid < Q / 8) {
+        // the weights row of the ones column, 8 tokens per 16-byte block
+        const float* wr = wbuf + hh * Q + tid * 8;
+        const uint4 v = make_uint4(pack_bf16x2(wr[0], wr[1]), pack_bf16x2(wr[2], wr[3]),
+                                   pack_bf16x2(wr[4], wr[5]), pack_bf16x2(wr[6], wr[7]));
+        *reinterpret_cast<uint4*>(xwT + P * QP + (tid ^ lds_swizzle<Q>(P)) * 8) = v;
+      }
       lds_barrier();
       if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
 
@@ -334,6 +372,16 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
         }
         stage_state(acc);
       }
+      if (zwave) {
+        // the ones column: B^T times its weights row (output column P only)
+        floatx16_t accz = zero16();
+        const int zkey = lds_swizzle<Q>(P + lr);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+          accz = mfma32x32x16(bop[ks], *reinterpret_cast<const uint4*>(xwT + (P + lr) * QP + ((2 * ks + lg) ^ zkey) * 8),
+                              accz);
+        store_z(h, accz);
+      }
       lds_barrier();
       store_state(h);
     }
@@ -344,6 +392,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
       floatx16_t acc[PPW];
 #pragma unroll
       for (int j = 0; j < PPW; ++j) acc[j] = zero16();
+      floatx16_t accz = zero16();
       for (int kb = 0; kb < KSPL; ++kb) {
         const int Lb = min(KB, L - kb * KB);
         if (Lb <= 0) break;  // past the chunk's end (the same for every thread)
@@ -353,6 +402,8 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
         lds_barrier();  // weights ready; the previous block's tiles no longer read
         bt.template store<QP, 0>(bT, nullptr);
         xt.template store<QP, 1>(xwT, wbuf + hh * Q + kb * KB);
+        // the weights row of the ones column (zero past the chunk's end)
+        if (zcol && tid < KB) xwT[P * QP + tid] = wbuf[hh * Q + kb * KB + tid];
         lds_barrier();
         if (active) {
 #pragma unroll 8
@@ -361,10 +412,12 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
 #pragma unroll
             for (int j = 0; j < PPW; ++j)
               acc[j] = mfma32x32x2(a, xwT[((pt0 + j) * 32 + lr) * QP + ks * 2 + lg], acc[j]);
+            if (zwave) accz = mfma32x32x2(a, xwT[(P + lr) * QP + ks * 2 + lg], accz);
           }
         }
       }
       if (active) stage_state(acc);
+      if (zwave) store_z(h, accz);
       lds_barrier();
       store_state(h);
     }

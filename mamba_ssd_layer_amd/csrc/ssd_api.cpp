@@ -354,18 +354,10 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg,
       e = timed_launch(kK2ChunkCB, stream, [&] { return launch_chunk_cb(p, ws, stream); });
       if (e != hipSuccess) break;
     }
-    if (p.kmax > 0 && p.denom != nullptr) {
-      e = timed_launch(kK11Denominator, stream, [&] { return launch_zstate(p, ws, stream); });
-      if (e != hipSuccess) break;
-    }
     e = timed_launch(kK4StatePass, stream, [&] {
       return launch_state_pass(p, ws, dbg ? dbg->hin : nullptr, stream);
     });
     if (e != hipSuccess) break;
-    if (p.kmax > 0 && p.denom != nullptr) {
-      e = timed_launch(kK11Denominator, stream, [&] { return launch_denominator(p, ws, stream); });
-      if (e != hipSuccess) break;
-    }
     if (p.kmax > 0 && !states_only) {
       e = timed_launch(kK25ChunkOutput, stream, [&] { return launch_chunk_output(p, ws, stream); });
       if (e != hipSuccess) break;

@@ -37,7 +37,8 @@ struct Problem {
   const float* D;         // (H): y += D_h x (skip connection), or nullptr
   int x_times_dt;         // 1: the input enters as dt_t x_t (B scaled by the step size)
   int strict_diag;        // 1: y leaves out each token's own term (C_t . B_t) x_t (backward's use)
-  float* denom;           // (Ttot, H) fp32: y is divided by this denominator (normalised output), or nullptr
+  float* denom;           // (Ttot, H) fp32: normalised output: its denominator, formed by the output
+                          // kernel (y is divided by it), or nullptr
   int64_t nseq;           // S
   int64_t seqlen;         // T (batched form only)
   int64_t total;          // Ttot
@@ -153,8 +154,9 @@ struct Workspace {
   void* cb = nullptr;            // (kmax, G, NI(NI+1)/2 tiles, 16-byte vector, 64 lanes) kernel
                                  // tiles of C B^T, element dtype, NI = Q/32 (16 values per lane)
   void* zs = nullptr;            // (kmax, H, N) normalised output only: chunk states of the ones
-  void* zin = nullptr;           //   column and their passed states, element dtype (state passing
-                                 //   carries them as N more channels per head)
+  void* zin = nullptr;           //   column (the chunk-state kernel's extra MFMA tile) and their
+                                 //   passed states, element dtype (state passing carries them as
+                                 //   N more channels per head)
   void* cop = nullptr;           // (kmax, G, NI, N/K steps, 64 lanes, one MFMA operand slice)
                                  // C rows in MFMA B-operand order, element dtype
 };
@@ -215,8 +217,7 @@ bool config_supported(Dtype dt, int Q, int N);
 // Kernel launchers; each returns the launch status.  Kernel ids for timing.
 enum KernelId { kK0SeqTable = 0, kK13ChunkState = 1, kK4StatePass = 2, kK25ChunkOutput = 3,
                 kK2ChunkCB = 4, kK6DecodeStep = 5, kK7BackwardGlue = 6,
-                kK10SelectiveScan = 7,
-                kK11Denominator = 8, kNumKernels = 9 };
+                kK10SelectiveScan = 7, kNumKernels = 8 };
 // K0 (varlen only): per-sequence first token, length and first chunk slot.
 hipError_t launch_seq_table(const Problem& p, const Workspace& ws, hipStream_t s);
 // K1 + K3: chunk-local log-decay cumsum (-> acs, lam, dmax), chunk states (-> states);
@@ -233,10 +234,6 @@ hipError_t launch_chunk_output(const Problem& p, const Workspace& ws, hipStream_
 // K6: one recurrent step (decode): state update in place and y.
 hipError_t launch_decode_step(const DecodeProblem& d, hipStream_t s);
 hipError_t launch_selective_scan(const ScanProblem& p, hipStream_t s);
-// K11 (normalised output only): chunk states of the ones column (-> ws.zs), run
-// before the state passing, and the denominator (-> p.denom) from ws.zin, after it.
-hipError_t launch_zstate(const Problem& p, const Workspace& ws, hipStream_t s);
-hipError_t launch_denominator(const Problem& p, const Workspace& ws, hipStream_t s);
 // K7 backward glue: stage 0 builds the gradient passes' inputs (and zeroes dA,
 // dD), stage 1 turns their outputs into dx, dB, dC, d(dt), dA, dD, dh0.
 hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);

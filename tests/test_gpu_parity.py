@@ -808,3 +808,18 @@ def test_normalized_long(dev):
     w = SMALL.with_(dtype="bf16", dstate=128, chunk_len=256, seqlen=4096, batch=1, nheads=16, ngroups=1)
     inp = _positive(make_inputs(w, 112))
     _check_normalized(inp, dev, 256, "long bf16")
+
+
+@pytest.mark.parametrize("dtype,Q", [("f32", 128), ("bf16", 256)])
+@pytest.mark.parametrize("ell", [-0.05, -0.5, -8.0])
+@pytest.mark.parametrize("opts", [False, True])
+def test_normalized_decays(dev, dtype, Q, ell, opts):
+    """The denominator under the whole-chunk mask (dt*A = -0.05 per token) and
+    the per-element mask (-0.5: the chunk decays past the factorisation's
+    limit; -8: every tile does), with and without the skip term and the
+    dt-scaled input; 16 heads (two workgroups' head blocks of the normalised
+    output)."""
+    w = SMALL.with_(dtype=dtype, dstate=64, chunk_len=Q, seqlen=700, batch=2, nheads=16, ngroups=2)
+    inp = _positive(_scaled_decay(make_inputs(w, 113), ell))
+    D = np.linspace(-1.0, 1.0, 16).astype(np.float32) if opts else None
+    _check_normalized(inp, dev, Q, f"{dtype} Q={Q} dt*A~{ell} options={opts}", D=D, xdt=opts)
