@@ -208,16 +208,13 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   using XTile = TransTile<E, Q, P, kCoThreads, 4>;
   XTile xt;
   RowTile<E, P, N, kCoThreads> ht;
-  auto head_by_chunk = [&](int hh) {
-    return mask_by_chunk<E>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_v), hh)));
-  };
   float a_own = 0.f;
   float dt_own = 1.0f;  // normalised output with the dt-scaled input: dt of token tid
   // chunk mask: log of the staging divisor of this thread's x rows.
-  // per-element mask, in the same registers: [0][0] r of token tid (tid < Q),
-  // [0][1] dt*A of this lane's output token (lanes 0-31) or the chunk's tile
-  // totals (lane 32 + m: tile m)
   float xa4[XTile::NPT][4];
+  // per-element mask: r of token tid (tid < Q); dt*A of this lane's output
+  // token (lanes 0-31) or the chunk's tile totals (lane 32 + m: tile m)
+  float ex_r = 0.0f, ex_e = 0.0f;
   const int i_tab = max(I, 0) * 32 + lr;  // this lane's token in the tables (idle waves: any)
   auto prefetch = [&](int h, bool by_chunk) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
@@ -233,9 +230,9 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       }
     } else {
       const int64_t kh = k * H + h;
-      xa4[0][0] = ws.rsuf[kh * Q + min(tid, Q - 1)];
+      ex_r = ws.rsuf[kh * Q + min(tid, Q - 1)];
       const float* et_src = lane < 32 ? ws.ell + kh * Q + i_tab : ws.ttot + kh * 8 + (lane & 7);
-      xa4[0][1] = *et_src;
+      ex_e = *et_src;
     }
   };
   // C row of this lane's token as MFMA B-operand slices over N, kept in
@@ -256,7 +253,19 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       for (int ks = 0; ks < (kCRegs ? KS : 1); ++ks) creg[ks] = cop_g[(I * KS + ks) * 64];
     }
   }
-  prefetch(h0, head_by_chunk(0));
+  // the block's heads by mask factorisation (uniform bit masks over hh):
+  // the chunk heads are done first, in a loop built for that factorisation
+  // alone, then the per-element heads in a loop of their own, so that the
+  // chunk path's registers and schedule are not shaped by the other's code
+  const uint64_t hb_bits = HB >= 64 ? ~0ull : ((1ull << HB) - 1);
+  const uint64_t exact_bits = __builtin_amdgcn_ballot_w64(!mask_by_chunk<E>(lam_v)) & hb_bits;
+  const uint64_t chunk_bits = hb_bits & ~exact_bits;
+  const int first_exact = exact_bits ? (int)__builtin_ctzll(exact_bits) : -1;
+  // the first head's loads, of the chunk kind whatever its factorisation (a
+  // conditional prefetch here would make the tile formation below wait for
+  // it); a block of per-element heads only issues them again, with its
+  // tables, between the two loops below
+  prefetch(h0 + (chunk_bits ? (int)__builtin_ctzll(chunk_bits) : first_exact), true);
   const float dskip_v = (kOpts && p.D != nullptr) ? p.D[h0 + lane % HB] : 0.0f;  // skip weight D_h, same lanes
 
   if constexpr (kCopyG) {
@@ -327,16 +336,22 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // x^T overwrites them
   }
 
-  for (int hh = 0; hh < HB; ++hh) {
+  // one head hh of the block; nxt: the next head of the same factorisation
+  // (its loads are issued here, under this head's products), -1 for none.
+  // The prefetch's kind is fixed per loop: loads of either kind into shared
+  // registers would need copies where the two kinds join, and those wait for
+  // every load in flight.
+  auto head_iter = [&](const int hh, const int nxt, auto by_chunk_tag)
+                       __attribute__((always_inline)) {
+    constexpr bool by_chunk = decltype(by_chunk_tag)::value;
     const int h = h0 + hh;
     lds_barrier();  // every wave is done with the previous head's tiles
     ht.template store<NP, kBf16>(Hs);
     // mask factorisation of this head (see the header)
-    const bool by_chunk = head_by_chunk(hh);
     if (tid < Q) {
       acs_s[tid] = a_own;
       // exp of the sum of dt*A over the later tokens of j's tile
-      if (!by_chunk) w_s[tid] = __expf(xa4[0][0]);
+      if (!by_chunk) w_s[tid] = __expf(ex_r);
       if constexpr (kDen) {
         // the ones column's staging: exp(-Acs_j) dt_j (chunk mask; w_s is
         // free there), dt_j (per-element mask).  bf16 without options: the
@@ -378,9 +393,9 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       xt.template store<QP, 0, kBf16, false, kBf16>(XT, nullptr);
     }
     lds_barrier();
-    const float et = xa4[0][1];  // this head's dt*A / tile totals (per-element mask)
-    if (hh + 1 < HB) prefetch(h + 1, head_by_chunk(hh + 1));
-    if (!active) continue;
+    const float et = ex_e;  // this head's dt*A / tile totals (per-element mask)
+    if (nxt >= 0) prefetch(h0 + nxt, by_chunk);
+    if (!active) return;
 
     const int i_loc = I * 32 + lr;
     // per-element mask: the sum of dt*A over this lane's tile up to its token
@@ -879,6 +894,17 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       }
       __builtin_amdgcn_wave_barrier();
     }
+  };
+  for (uint64_t m = chunk_bits; m;) {
+    const int hh = (int)__builtin_ctzll(m);
+    m &= m - 1;
+    head_iter(hh, m ? (int)__builtin_ctzll(m) : -1, std::true_type());
+  }
+  if (exact_bits) prefetch(h0 + first_exact, false);
+  for (uint64_t m = exact_bits; m;) {
+    const int hh = (int)__builtin_ctzll(m);
+    m &= m - 1;
+    head_iter(hh, m ? (int)__builtin_ctzll(m) : -1, std::false_type());
   }
 }
 
