@@ -106,8 +106,7 @@ def kernels_table(trace_dir: str, first: int = 0, last: int = 0) -> str:
 
 def _counter_per_dispatch(d: str, symbol: str, counter: str, reduce: str = "sum") -> float:
     """Average over the kernel's dispatches of the counter, its instances summed
-    (reduce "sum") or their largest taken (reduce "max": clocks such as
-    GRBM_GUI_ACTIVE, one per accelerator die)."""
+    (reduce "sum") or their largest taken (reduce "max")."""
     vals = {}
     for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
         if symbol in r["Kernel_Name"] and r["Counter_Name"] == counter:
@@ -123,6 +122,7 @@ def _counter_per_dispatch(d: str, symbol: str, counter: str, reduce: str = "sum"
 
 
 SIMDS = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8  # accelerator dies; GRBM_GUI_ACTIVE comes back as the sum of their busy clocks
 
 
 def counters(mfma: str, dram: str, cal_dram: str, kernel: str, workload: str, copy_mib: int,
@@ -130,7 +130,9 @@ def counters(mfma: str, dram: str, cal_dram: str, kernel: str, workload: str, co
     sym = KERNEL_SYMBOL[kernel]
     busy = _counter_per_dispatch(mfma, sym, "SQ_VALU_MFMA_BUSY_CYCLES")
     mops = _counter_per_dispatch(mfma, sym, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
-    active = _counter_per_dispatch(mfma, sym, "GRBM_GUI_ACTIVE", "max")
+    # one die's busy clocks: rocprofv3 reports GRBM_GUI_ACTIVE summed over the
+    # dies (about 8 x 2.4 GHz x the dispatch's begin..end time)
+    active = _counter_per_dispatch(mfma, sym, "GRBM_GUI_ACTIVE", "max") / XCDS
     rd = _counter_per_dispatch(dram, sym, "TCC_EA0_RDREQ_DRAM_sum")
     wr = _counter_per_dispatch(dram, sym, "TCC_EA0_WRREQ_DRAM_sum")
     crd = _counter_per_dispatch(cal_dram, COPY_KERNEL, "TCC_EA0_RDREQ_DRAM_sum")
@@ -153,7 +155,9 @@ def counters(mfma: str, dram: str, cal_dram: str, kernel: str, workload: str, co
         "read_bytes_per_request": rs,
         "write_bytes_per_request": ws,
         "dram_bytes_per_launch": rd * rs + wr * ws,
-        "note": ("mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); dram bytes = "
+        "note": ("mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 dies x 1024 SIMDs); "
+                 "mfma_flops_bf16_per_launch = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, the products "
+                 "the kernel executes; dram bytes = "
                  "TCC_EA0_{RD,WR}REQ_DRAM_sum scaled by a plain device copy's bytes per request "
                  "(requests that leave the L2; the Infinity Cache may still serve some)"),
         "scale_reference": (f"plain device copy of {copy_mib} MiB (bench.py --calibrate-copy {copy_mib}): "
