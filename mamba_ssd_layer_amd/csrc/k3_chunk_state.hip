@@ -161,12 +161,20 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   // block and head in the head loop)
   using BTile = TransTile<E, KB, N, kCsThreads>;
   using XTile = TransTile<E, KB, P, kCsThreads, 4>;
-  XTile xt;
+  // bf16: the x tiles of the next kXDepth heads are in flight at any time (a
+  // head's products take far less than a load's latency, so one tile ahead
+  // would leave each head waiting out most of it); register set d holds the
+  // heads d, d + kXDepth, ...  fp32 uses set 0 alone.
+  constexpr int kXDepth = kBf16 ? 2 : 1;
+  XTile xr[kXDepth];
+  XTile& xt = xr[0];
   {
     BTile bt;
     if constexpr (kBf16) {
       bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
-      xt.load(xbase + h0 * P, (int64_t)H * P, L);
+#pragma unroll
+      for (int d = 0; d < kXDepth; ++d)
+        if (d < HB) xr[d].load(xbase + (h0 + d) * P, (int64_t)H * P, L);
     }
     int t = et0, hh = eh0;
 #pragma unroll
@@ -328,10 +336,12 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   };
 
   if constexpr (kBf16) {
-    for (int hh = 0; hh < HB; ++hh) {
+    // head hh, its x tile in register set xh (head hh + kXDepth is loaded
+    // into the same set once it is staged)
+    auto head = [&](const int hh, XTile& xh) __attribute__((always_inline)) {
       const int h = h0 + hh;
       lds_barrier();  // w ready; B^T read; the previous head's x^T and state rows no longer read
-      xt.template store<QP, 1, false, SWZ>(xwT, wbuf + hh * Q);
+      xh.template store<QP, 1, false, SWZ>(xwT, wbuf + hh * Q);
       if (zcol && tid < Q / 8) {
         // the weights row of the ones column, 8 tokens per 16-byte block
         const float* wr = wbuf + hh * Q + tid * 8;
@@ -340,7 +350,7 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
         *reinterpret_cast<uint4*>(xwT + P * QP + (tid ^ lds_swizzle<Q>(P)) * 8) = v;
       }
       lds_barrier();
-      if (hh + 1 < HB) xt.load(xbase + (h + 1) * P, (int64_t)H * P, L);
+      if (hh + kXDepth < HB) xh.load(xbase + (h + kXDepth) * P, (int64_t)H * P, L);
 
       // ---- K3: S^T = B^T (w o X) on this wave's tiles
       if (active) {
@@ -384,6 +394,11 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
       }
       lds_barrier();
       store_state(h);
+    };
+    for (int hb = 0; hb < HB; hb += kXDepth) {
+#pragma unroll
+      for (int d = 0; d < kXDepth; ++d)
+        if (hb + d < HB) head(hb + d, xr[d]);
     }
   } else {
     // fp32: KSPL token blocks per head, B^T and x^T of each staged in turn
