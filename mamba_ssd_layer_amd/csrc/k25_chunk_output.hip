@@ -55,8 +55,8 @@
 //    with the input entering as dt x, every x staging scale carries
 //    dt_j (the chunk-state kernel provides Acs_j - ln dt_j; the per-element
 //    mask stages x_j dt_j); the skip term D_h x is one more operand of the
-//    diagonal tile's product (entry j == i), and a pass after the kernel adds
-//    it for the tokens whose dt is too small to divide by.
+//    diagonal tile's product (entry j == i), added instead to the finished
+//    value before its store for the tokens whose dt is too small to divide by.
 //  * fp32 accumulation; y rounded once to the element dtype and stored with the
 //    non-temporal hint (nothing here reads it again); Hin, read here for the
 //    last time, is loaded with that hint too.  (fp32 stores y straight from
@@ -72,7 +72,7 @@ constexpr int kMaskChunk = 0;  // whole chunk: x scaled by exp(-Acs_j), y by exp
 constexpr int kMaskExact = 2;  // per element, from addition-only segment sums
 // |dt| below which the skip term of a token is not carried through the entry
 // D_h / dt_i of the diagonal tile (it would overflow or lose x dt_i to
-// underflow); the pass after the kernel adds D_h x for those tokens
+// underflow); D_h x is added to those tokens' finished values instead
 constexpr float kSkipTinyDt = 0x1p-64f;
 // heads per workgroup of the normalised output (its denominator's passed-state
 // term is formed for all of them at once: one MFMA row block)
@@ -216,11 +216,24 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // token (lanes 0-31) or the chunk's tile totals (lane 32 + m: tile m)
   float ex_r = 0.0f, ex_e = 0.0f;
   const int i_tab = max(I, 0) * 32 + lr;  // this lane's token in the tables (idle waves: any)
+  float dt_row = 1.0f;  // options: dt of this lane's output token (the skip term's entry)
+  float d_head = 0.0f;  // options: the skip weight D_h of the prefetched head
   auto prefetch = [&](int h, bool by_chunk) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
     ht.template load<true>(hbase + h * (int64_t)(P * N), N, P);  // Hin's last read
     if (tid < Q) a_own = abase[h * Q + tid];
-    if (kDen && kOpts && p.x_times_dt && tid < Q) dt_own = p.dt[(cd.t0 + min(tid, L - 1)) * H + h];
+    // options: dt of token tid (the normalised output's ones column), the
+    // skip term's weight D_h, and the dt of this lane's output token its entry
+    // divides by, loaded with the head's other values and whatever the
+    // run-time options (D_h from dt when there is no D; the options decide at
+    // the use).  A load from before the head loop read inside it, or a load
+    // under a run-time condition, would make every head wait for all the
+    // loads in flight, the next head's among them.
+    if constexpr (kOpts) {
+      if constexpr (kDen) dt_own = p.dt[(cd.t0 + min(tid, L - 1)) * H + h];
+      d_head = *(p.D != nullptr ? p.D + h : p.dt);
+      dt_row = p.dt[(cd.t0 + min(i_tab, L - 1)) * H + h];
+    }
     if (by_chunk) {
 #pragma unroll
       for (int i = 0; i < XTile::NPT; ++i) {
@@ -261,12 +274,16 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   const uint64_t exact_bits = __builtin_amdgcn_ballot_w64(!mask_by_chunk<E>(lam_v)) & hb_bits;
   const uint64_t chunk_bits = hb_bits & ~exact_bits;
   const int first_exact = exact_bits ? (int)__builtin_ctzll(exact_bits) : -1;
+  // normalised output: the Zin rows of the block's heads (rows past HB stored
+  // as zeros), issued ahead of the first head's loads so that the
+  // denominator's product below does not wait for those
+  RowTile<E, 32, N, kCoThreads> zt;
+  if constexpr (kDen) zt.load(reinterpret_cast<const T*>(ws.zin) + (k * H + h0) * (int64_t)N, N, HB);
   // the first head's loads, of the chunk kind whatever its factorisation (a
   // conditional prefetch here would make the tile formation below wait for
   // it); a block of per-element heads only issues them again, with its
   // tables, between the two loops below
   prefetch(h0 + (chunk_bits ? (int)__builtin_ctzll(chunk_bits) : first_exact), true);
-  const float dskip_v = (kOpts && p.D != nullptr) ? p.D[h0 + lane % HB] : 0.0f;  // skip weight D_h, same lanes
 
   if constexpr (kCopyG) {
 #pragma unroll
@@ -311,11 +328,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // of each head (its ones column's passed state, N values) an A-operand
     // row and the lane's C row the B operand, as for Y_off
     lds_barrier();  // the tile formation's B rows (same region) are no longer read
-    {
-      RowTile<E, 32, N, kCoThreads> zt;  // rows past HB stored as zeros
-      zt.load(reinterpret_cast<const T*>(ws.zin) + (k * H + h0) * (int64_t)N, N, HB);
-      zt.template store<NP>(XT);
-    }
+    zt.template store<NP>(XT);
     lds_barrier();
     if (active) {  // both waves of a shared row tile keep the term
       floatx16_t accd = zero16();
@@ -358,7 +371,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         // chunk mask's values as bf16 pairs (j, j + 1) in word j / 2, for the
         // products' row sums on v_dot2_f32_bf16
         if (by_chunk) {
-          const float sj = __expf(-a_own) * dt_own;
+          const float sj = __expf(-a_own) * (kOpts && p.x_times_dt ? dt_own : 1.0f);
           if constexpr (kBf16 && !kDenPre) {
             const float sn = __shfl_down(sj, 1, kWave);
             if ((tid & 1) == 0) reinterpret_cast<uint32_t*>(w_s)[tid >> 1] = pack_bf16x2(sj, sn);
@@ -394,6 +407,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     }
     lds_barrier();
     const float et = ex_e;  // this head's dt*A / tile totals (per-element mask)
+    const float dti = dt_row;  // (options) this head's, before the next head's prefetch
+    const float dh = d_head;
     if (nxt >= 0) prefetch(h0 + nxt, by_chunk);
     if (!active) return;
 
@@ -541,17 +556,16 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // is x_i times a staging scale that the output factor undoes, so the entry
     // is D_h, over dt_i when the input enters as dt x (x^T_i then carries dt_i),
     // times the denominator when the output is normalised (divided out again).
-    // A token with dt_i = 0 has x^T_i = 0 there: a pass after this kernel adds
-    // its term (skip_zero_dt_kernel).
+    // A token with dt_i = 0 has x^T_i = 0 there: its term is added to the
+    // finished value before the store.
     float dsk = 0.0f;
     if constexpr (kOpts) {
       if (p.D != nullptr) {
-        dsk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dskip_v), hh));
+        dsk = dh;
         if constexpr (kDen) dsk *= den;
         if (p.x_times_dt) {
           // x^T_i carries dt_i: a dt too small to divide by (zero included)
-          // leaves the term to the pass after this kernel
-          const float dti = p.dt[(cd.t0 + min(i_loc, L - 1)) * H + h];
+          // leaves the term to the store
           dsk = fabsf(dti) < kSkipTinyDt ? 0.0f : dsk / dti;
         }
       }
@@ -759,9 +773,10 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // one copy of the loop for the chunk factorisation (no per-tile work) and
     // one for the other two
     auto diag_blocks = [&](auto mode_tag) {
-      if constexpr (kDen) {
-        // normalised output: one operand buffer (the row sums' registers
-        // would otherwise push the double-buffered loop into spills)
+      if constexpr (kDen && (kOpts || !Cfg::kGInline)) {
+        // normalised output with options, or with the tiles from the
+        // kernel-matrix pass: one operand buffer (a second one's registers
+        // would push the loop into spills)
         TileOps ob;
         for (int J = 0; J < I; ++J) {
           load_ops(J, ob);
@@ -830,15 +845,25 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     }
     // store: lane holds Y^T row pr = 32 (ph0 + j) + 8(r/4) + 4 lg + r%4 of token
     // i_loc.
+    // options, input entering as dt x, with the skip term: a token whose |dt|
+    // is too small to carry the term through the diagonal entry gets D_h x_i
+    // added here to its finished value (x read from memory for those only)
+    const bool skip_late = kOpts && p.x_times_dt && p.D != nullptr;
+    const T* xhead = xbase + h * P;
     if constexpr (!kBf16) {
       // fp32: four consecutive p per 16-byte store, straight from the accumulators
       if (i_loc < L) {
         T* yrow = ybase + (int64_t)i_loc * H * P + h * P;
+        const bool late = skip_late && fabsf(dti) < kSkipTinyDt;
 #pragma unroll
         for (int j = 0; j < NPH; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 v4 = make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
+            float4 v4 = make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
+            if (late) {
+              const float4 x4 = *reinterpret_cast<const float4*>(xhead + (int64_t)i_loc * H * P + 32 * (ph0 + j) + 8 * q + 4 * lg);
+              v4.x += dh * x4.x; v4.y += dh * x4.y; v4.z += dh * x4.z; v4.w += dh * x4.w;
+            }
             store_nt(reinterpret_cast<uint4*>(yrow + 32 * (ph0 + j) + 8 * q + 4 * lg),
                      make_uint4(__float_as_uint(v4.x), __float_as_uint(v4.y), __float_as_uint(v4.z),
                                 __float_as_uint(v4.w)));
@@ -850,15 +875,18 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       // (p permuted as below)
       if (i_loc < L) {
         T* yrow = ybase + (int64_t)i_loc * H * P + h * P;
+        const bool late = skip_late && fabsf(dti) < kSkipTinyDt;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int j = 0; j < NPH; ++j) {
             const int pp = q * 8 + 4 * (lg ^ ((ph0 + j) & 1));
             const floatx16_t& a = acc[j];
-            *reinterpret_cast<uint2*>(yrow + 32 * (ph0 + j) + pp) =
-                make_uint2(pack_bf16x2(a[4 * q + (0 ^ q)], a[4 * q + (1 ^ q)]),
-                           pack_bf16x2(a[4 * q + (2 ^ q)], a[4 * q + (3 ^ q)]));
+            uint2 v2 = make_uint2(pack_bf16x2(a[4 * q + (0 ^ q)], a[4 * q + (1 ^ q)]),
+                                  pack_bf16x2(a[4 * q + (2 ^ q)], a[4 * q + (3 ^ q)]));
+            if (late)
+              v2 = add_scaled<E>(v2, *reinterpret_cast<const uint2*>(xhead + (int64_t)i_loc * H * P + 32 * (ph0 + j) + pp), dh);
+            *reinterpret_cast<uint2*>(yrow + 32 * (ph0 + j) + pp) = v2;
           }
       }
     } else {
@@ -887,7 +915,12 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         const int row = s * RPI + lane / VPR;
         const int vec = lane % VPR;
         const int i_row = I * 32 + row;
-        const uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
+        uint4 val = *reinterpret_cast<const uint4*>(ys + row * YP + vec * (16 / sizeof(T)));
+        if (skip_late) {
+          const float dtr = __shfl(dti, row);  // lane `row` holds that token's dt
+          if (i_row < L && fabsf(dtr) < kSkipTinyDt)
+            val = add_scaled<E>(val, *reinterpret_cast<const uint4*>(xhead + (int64_t)i_row * H * P + ph0 * 32 + vec * (16 / sizeof(T))), dh);
+        }
         if (i_row < L)
           store_nt(reinterpret_cast<uint4*>(ybase + (int64_t)i_row * H * P + h * P + ph0 * 32 + vec * (16 / sizeof(T))),
                    val);
@@ -908,23 +941,6 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   }
 }
 
-// Skip term of the tokens whose |dt| is below kSkipTinyDt (zero included) when
-// the input enters as dt x: their staged x^T is zero or too small to carry
-// D_h x through the entry D_h / dt_i, so the output kernel leaves the term out
-// and this pass adds it to the stored output (rounded once more), one thread
-// per (token, head) and 16-byte vectors over the head's P values.
-template <class E>
-__global__ __launch_bounds__(256) void skip_zero_dt_kernel(Problem p) {
-  using T = typename E::storage;
-  const int64_t th = blockIdx.x * 256LL + threadIdx.x;
-  if (th >= p.total * p.H) return;
-  if (!(fabsf(p.dt[th]) < kSkipTinyDt)) return;
-  const float dh = p.D[th % p.H];
-  const uint4* xv = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(p.x) + th * p.P);
-  uint4* yv = reinterpret_cast<uint4*>(reinterpret_cast<T*>(p.y) + th * p.P);
-  for (int v = 0; v < p.P * (int)sizeof(T) / 16; ++v) yv[v] = add_scaled<E>(yv[v], xv[v], dh);
-}
-
 template <class E, int Q, int N>
 static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s) {
   if constexpr (ChunkOutputCfg<E, Q, N>::fits) {
@@ -943,11 +959,6 @@ static hipError_t launch_co(const Problem& p, const Workspace& ws, hipStream_t s
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 1>), grid, blk, 0, s, p, ws, HB);
     else
       hipLaunchKernelGGL((chunk_output_kernel<E, Q, N, 0>), grid, blk, 0, s, p, ws, HB);
-    if (p.D != nullptr && p.x_times_dt && p.total > 0) {
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((skip_zero_dt_kernel<E>), dim3((unsigned)((p.total * p.H + 255) / 256)), dim3(256), 0, s, p);
-    }
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

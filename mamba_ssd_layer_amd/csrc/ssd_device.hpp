@@ -74,6 +74,13 @@ __device__ __forceinline__ uint4 add_scaled(const uint4& y, const uint4& x, floa
   }
 }
 
+// The same on one 8-byte vector.
+template <class E>
+__device__ __forceinline__ uint2 add_scaled(const uint2& y, const uint2& x, float d) {
+  const uint4 r = add_scaled<E>(make_uint4(y.x, y.y, 0u, 0u), make_uint4(x.x, x.y, 0u, 0u), d);
+  return make_uint2(r.x, r.y);
+}
+
 // Load with the non-temporal hint: for the last read of data.
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
