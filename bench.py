@@ -247,70 +247,96 @@ def bench_comparator(bd, torch, w, sec_ssd, steps, warmup):
                          "avg_launch_ms": kms, "exps_per_launch": exps}}
 
 
-def bench_normalized(bd, torch, w, x, dt, A, B, C, cu, sec_ssd, steps, warmup):
-    """The normalised forward (y / M 1) on the forward's workload, with B and C
-    made positive (|.| + 0.05, the pages' positive feature map), timed like the
-    forward; the output and chunk-state kernels' times from HIP events."""
-    Bp = (B.float().abs() + 0.05).to(B.dtype)
-    Cp = (C.float().abs() + 0.05).to(C.dtype)
+def time_gpu_back_to_back(torch, step, K):
+    """K steps back to back between two HIP events on the current stream (ms
+    per step): the GPU's time, whatever the host spends per call."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
 
-    def step():
-        return bd.ssd_chunked_fwd_normalized(x, dt, A, Bp, Cp, w.chunk_len, cu_seqlens=cu,
-                                             return_final_state=False)
 
+def variant_vs_forward(bd, torch, plain, variant, steps, warmup, kernels):
+    """A forward variant against the plain forward on the same inputs, both
+    warm, outputs preallocated, timed alike (HIP events around back-to-back
+    steps, the two alternated three times, each one's best taken); the named
+    kernels' launch times of the variant from the library's events."""
     for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
+        plain()
+        variant()
+    tp, tv = [], []
+    for _ in range(3):
+        tp.append(time_gpu_back_to_back(torch, plain, steps))
+        tv.append(time_gpu_back_to_back(torch, variant, steps))
     bd.kernel_timing_read(reset=True)
     bd.kernel_timing_enable(True)
     for _ in range(steps):
-        step()
+        variant()
     torch.cuda.synchronize()
     bd.kernel_timing_enable(False)
     kt = bd.kernel_timing_read(reset=True)
-    co, cs = kt["chunk_output"], kt["chunk_state"]
-    return {"us_per_step": sec * 1e6, "tokens_per_s": int(x.numel() // (w.nheads * w.headdim)) / sec,
-            "overhead_vs_forward": sec / sec_ssd - 1.0,
-            "note": "warm, like the forward it is compared with; the denominator is formed inside the "
-                    "chunk-state (ones-column states), state-passing and output kernels",
-            "chunk_output_us": co[0] / co[1] * 1e3 if co[1] else None,
-            "chunk_state_us": cs[0] / cs[1] * 1e3 if cs[1] else None}
+    ms_p, ms_v = min(tp), min(tv)
+    out = {"us_per_step": ms_v * 1e3, "forward_us_per_step": ms_p * 1e3,
+           "overhead_vs_forward": ms_v / ms_p - 1.0}
+    for k in kernels:
+        out[k + "_us"] = kt[k][0] / kt[k][1] * 1e3 if kt[k][1] else None
+    return out
 
 
-def bench_options(bd, torch, w, x, dt, A, B, C, cu, sec_ssd, steps, warmup):
+def bench_normalized(bd, torch, w, x, dt, A, B, C, cu, steps, warmup):
+    """The normalised forward (y / M 1) on the forward's workload, with B and C
+    made positive (|.| + 0.05, the pages' positive feature map), against the
+    plain forward on the same inputs, timed alike."""
+    Bp = (B.float().abs() + 0.05).to(B.dtype)
+    Cp = (C.float().abs() + 0.05).to(C.dtype)
+    y = torch.empty_like(x)
+    den = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device).reshape(-1, w.nheads)
+
+    def plain():
+        if cu is None:
+            bd.ssd_chunked_fwd(x, dt, A, Bp, Cp, w.chunk_len, y=y)
+        else:
+            bd.ssd_chunked_fwd_varlen(x, dt, A, Bp, Cp, cu, w.chunk_len, y=y)
+
+    def variant():
+        bd.ssd_chunked_fwd_normalized(x, dt, A, Bp, Cp, w.chunk_len, cu_seqlens=cu, return_final_state=False,
+                                      y=y, denom=den)
+
+    r = variant_vs_forward(bd, torch, plain, variant, steps, warmup, ("chunk_output", "chunk_state"))
+    r["tokens_per_s"] = int(x.numel() // (w.nheads * w.headdim)) / (r["us_per_step"] * 1e-6)
+    r["note"] = ("warm, against the plain forward on the same positive B and C, both timed by HIP events "
+                 "around back-to-back steps; the denominator is formed inside the chunk-state "
+                 "(ones-column states), state-passing and output kernels")
+    return r
+
+
+def bench_options(bd, torch, w, x, dt, A, B, C, cu, steps, warmup):
     """The forward with the skip term D (one weight per head) and the input
-    entering as dt x, on the forward's workload, timed like the forward; the
-    output kernel's share from HIP events."""
+    entering as dt x, on the forward's workload, against the plain forward,
+    timed alike."""
     D = torch.linspace(-1.0, 1.0, w.nheads, device=x.device, dtype=torch.float32)
+    y = torch.empty_like(x)
 
-    def step():
-        return bd.ssd_chunked_fwd_ex(x, dt, A, B, C, w.chunk_len, cu_seqlens=cu, D=D, x_times_dt=True,
-                                     return_final_state=False)
+    def plain():
+        if cu is None:
+            bd.ssd_chunked_fwd(x, dt, A, B, C, w.chunk_len, y=y)
+        else:
+            bd.ssd_chunked_fwd_varlen(x, dt, A, B, C, cu, w.chunk_len, y=y)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
-    bd.kernel_timing_read(reset=True)
-    bd.kernel_timing_enable(True)
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    bd.kernel_timing_enable(False)
-    co = bd.kernel_timing_read(reset=True)["chunk_output"]
-    return {"options": "D and x*dt", "us_per_step": sec * 1e6,
-            "tokens_per_s": int(x.numel() // (w.nheads * w.headdim)) / sec,
-            "overhead_vs_forward": sec / sec_ssd - 1.0,
-            "chunk_output_us": co[0] / co[1] * 1e3 if co[1] else None}
+    def variant():
+        bd.ssd_chunked_fwd_ex(x, dt, A, B, C, w.chunk_len, cu_seqlens=cu, D=D, x_times_dt=True, y=y,
+                              return_final_state=False)
+
+    r = variant_vs_forward(bd, torch, plain, variant, steps, warmup, ("chunk_output", "chunk_state"))
+    r["options"] = "D and x*dt"
+    r["tokens_per_s"] = int(x.numel() // (w.nheads * w.headdim)) / (r["us_per_step"] * 1e-6)
+    return r
+
 
 
 def min_io_bytes(w, total_tokens, nseq):
@@ -630,10 +656,10 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200))
     if not args.no_normalized:
-        result["normalized"] = bench_normalized(bd, torch, w, x, dt, A, B, C, cu, warm_ms / 1e3,
+        result["normalized"] = bench_normalized(bd, torch, w, x, dt, A, B, C, cu,
                                                 min(args.steps, 100), min(args.warmup, 50))
     if not args.no_options:
-        result["options"] = bench_options(bd, torch, w, x, dt, A, B, C, cu, warm_ms / 1e3,
+        result["options"] = bench_options(bd, torch, w, x, dt, A, B, C, cu,
                                           min(args.steps, 100), min(args.warmup, 50))
     if not args.no_comparator:
         result["comparator"] = bench_comparator(bd, torch, w, warm_ms / 1e3, min(args.steps, 20), 3)

@@ -273,11 +273,13 @@ def ssd_chunked_fwd_ex(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, ini
 
 
 def ssd_chunked_fwd_normalized(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=None, D=None,
-                               x_times_dt: bool = False, return_final_state: bool = True):
+                               x_times_dt: bool = False, return_final_state: bool = True, y=None,
+                               denom=None):
     """SSD forward with the output divided by its denominator term M 1
     (ssd_chunked_fwd_normalized).  Inputs as ssd_chunked_fwd_ex without an
-    initial state; B and C should come from a positive feature map.  Returns
-    (y, final_state (S,H,P,N) or None, denom (Ttot,H) fp32)."""
+    initial state; B and C should come from a positive feature map.  y (x's
+    shape and dtype) and denom ((Ttot,H) fp32) may be given to be written in
+    place.  Returns (y, final_state (S,H,P,N) or None, denom (Ttot,H) fp32)."""
     dev = x.device
     if x.dim() == 4:
         if cu_seqlens is not None:
@@ -307,9 +309,19 @@ def ssd_chunked_fwd_normalized(x, dt, A_head, B, C, chunk_len: int, cu_seqlens=N
         _need(D, "D", torch.float32, dev)
         if tuple(D.shape) != (H,):
             raise ValueError("D must be (H,)")
-    y = torch.empty_like(x)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, dev)
+        if y.shape != x.shape:
+            raise ValueError("y must have x's shape")
     final_state = torch.empty((S, H, P, N), dtype=torch.float32, device=dev) if return_final_state else None
-    denom = torch.empty((Tt, H), dtype=torch.float32, device=dev)
+    if denom is None:
+        denom = torch.empty((Tt, H), dtype=torch.float32, device=dev)
+    else:
+        _need(denom, "denom", torch.float32, dev)
+        if tuple(denom.shape) != (Tt, H):
+            raise ValueError("denom must be (Ttot, H)")
     rc = lib().ssd_chunked_fwd_normalized(_ptr(x), _ptr(dt), _ptr(A_head), _ptr(B), _ptr(C), _ptr(cu_seqlens),
                                           S, Tt, H, P, N, G, int(chunk_len), _dtype_code(x), _ptr(D),
                                           1 if x_times_dt else 0, _ptr(y), _ptr(final_state), _ptr(denom),
