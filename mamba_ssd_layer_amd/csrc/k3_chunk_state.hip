@@ -172,9 +172,11 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
     BTile bt;
     if constexpr (kBf16) {
       bt.load(reinterpret_cast<const T*>(p.B) + (cd.t0 * G + g) * N, (int64_t)G * N, L);
+      // unconditional (a block of fewer heads reloads its last one): a load
+      // under a condition would make the B tile's staging below wait for
+      // these too
 #pragma unroll
-      for (int d = 0; d < kXDepth; ++d)
-        if (d < HB) xr[d].load(xbase + (h0 + d) * P, (int64_t)H * P, L);
+      for (int d = 0; d < kXDepth; ++d) xr[d].load(xbase + (h0 + min(d, HB - 1)) * P, (int64_t)H * P, L);
     }
     int t = et0, hh = eh0;
 #pragma unroll
