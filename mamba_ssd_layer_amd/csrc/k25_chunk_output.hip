@@ -69,6 +69,7 @@ namespace ssd {
 constexpr int kCoThreads = 512;  // 8 waves: two per SIMD, one workgroup per CU
 // mask factorisation of a head (see the header)
 constexpr int kMaskChunk = 0;  // whole chunk: x scaled by exp(-Acs_j), y by exp(Acs_i)
+constexpr int kMaskTile = 1;   // per 32-token tile, from the per-element kind's one-signed sums
 constexpr int kMaskExact = 2;  // per element, from addition-only segment sums
 // |dt| below which the skip term of a token is not carried through the entry
 // D_h / dt_i of the diagonal tile (it would overflow or lose x dt_i to
@@ -193,6 +194,11 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // readlane (a vector load, once: a scalar load in flight would hold up every
   // later wait for LDS reads); it selects each head's mask factorisation
   const float lam_v = ws.lam[k * H + h0 + lane % HB];
+  // the plain bf16 forward factors a per-element head's mask by 32-token tile
+  // when no tile of its chunk decays by more than the factorisation limit
+  // (its largest tile decay, same lanes; written only for such heads)
+  constexpr bool kTileMode = kBf16 && kOpt == 0 && Cfg::kGInline;
+  const float tmax_v = kTileMode ? ws.tmax[k * H + h0 + lane % HB] : 0.0f;
   constexpr bool kCopyG = Cfg::kGLds && !Cfg::kGInline;
   constexpr int GNV = kCopyG ? NTILE * GV * 64 : 1;
   constexpr int GVPT = (GNV + kCoThreads - 1) / kCoThreads;
@@ -218,10 +224,12 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   const int i_tab = max(I, 0) * 32 + lr;  // this lane's token in the tables (idle waves: any)
   float dt_row = 1.0f;  // options: dt of this lane's output token (the skip term's entry)
   float d_head = 0.0f;  // options: the skip weight D_h of the prefetched head
-  auto prefetch = [&](int h, bool by_chunk) {
+  // kind: the head's mask factorisation (a constant at every call)
+  auto prefetch = [&](int h, int kind) {
     xt.load(xbase + h * P, (int64_t)H * P, L);
     ht.template load<true>(hbase + h * (int64_t)(P * N), N, P);  // Hin's last read
-    if (tid < Q) a_own = abase[h * Q + tid];
+    // token tid's Acs (the tile kind: its r, the LDS table of the row factors)
+    if (tid < Q) a_own = (kind == kMaskTile ? ws.rsuf + (k * H + h) * Q : abase + h * Q)[tid];
     // options: dt of token tid (the normalised output's ones column), the
     // skip term's weight D_h, and the dt of this lane's output token its entry
     // divides by, loaded with the head's other values and whatever the
@@ -234,13 +242,17 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       d_head = *(p.D != nullptr ? p.D + h : p.dt);
       dt_row = p.dt[(cd.t0 + min(i_tab, L - 1)) * H + h];
     }
-    if (by_chunk) {
+    if (kind != kMaskExact) {
+      // the log of x's staging scale: -Acs (chunk) or r (tile) of the thread's rows
+      const float* src = kind == kMaskChunk ? xlbase + h * Q : ws.rsuf + (k * H + h) * Q;
 #pragma unroll
       for (int i = 0; i < XTile::NPT; ++i) {
         const int r0 = XTile::first_row(i);
-        const float4 a4 = *reinterpret_cast<const float4*>(xlbase + h * Q + r0);
+        const float4 a4 = *reinterpret_cast<const float4*>(src + r0);
         xa4[i][0] = a4.x; xa4[i][1] = a4.y; xa4[i][2] = a4.z; xa4[i][3] = a4.w;
       }
+      // the tile kind's tile totals, threads 0-7
+      if (kind == kMaskTile && tid < 8) ex_e = ws.ttot[(k * H + h) * 8 + tid];
     } else {
       const int64_t kh = k * H + h;
       ex_r = ws.rsuf[kh * Q + min(tid, Q - 1)];
@@ -273,6 +285,9 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   const uint64_t hb_bits = HB >= 64 ? ~0ull : ((1ull << HB) - 1);
   const uint64_t exact_bits = __builtin_amdgcn_ballot_w64(!mask_by_chunk<E>(lam_v)) & hb_bits;
   const uint64_t chunk_bits = hb_bits & ~exact_bits;
+  const uint64_t tile_bits =
+      kTileMode ? (__builtin_amdgcn_ballot_w64(!mask_by_chunk<E>(lam_v) && tmax_v <= 64.0f) & hb_bits) : 0;
+  const uint64_t walk_bits = exact_bits & ~tile_bits;
   const int first_exact = exact_bits ? (int)__builtin_ctzll(exact_bits) : -1;
   // normalised output: the Zin rows of the block's heads (rows past HB stored
   // as zeros), issued ahead of the first head's loads so that the
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // conditional prefetch here would make the tile formation below wait for
   // it); a block of per-element heads only issues them again, with its
   // tables, between the two loops below
-  prefetch(h0 + (chunk_bits ? (int)__builtin_ctzll(chunk_bits) : first_exact), true);
+  prefetch(h0 + (chunk_bits ? (int)__builtin_ctzll(chunk_bits) : first_exact), kMaskChunk);
 
   if constexpr (kCopyG) {
 #pragma unroll
@@ -354,17 +369,20 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   // The prefetch's kind is fixed per loop: loads of either kind into shared
   // registers would need copies where the two kinds join, and those wait for
   // every load in flight.
-  auto head_iter = [&](const int hh, const int nxt, auto by_chunk_tag)
-                       __attribute__((always_inline)) {
-    constexpr bool by_chunk = decltype(by_chunk_tag)::value;
+  auto head_iter = [&](const int hh, const int nxt, auto kind_tag) __attribute__((always_inline)) {
+    constexpr int kind = decltype(kind_tag)::value;
+    constexpr bool by_chunk = kind == kMaskChunk, by_tile = kind == kMaskTile, by_elem = kind == kMaskExact;
     const int h = h0 + hh;
     lds_barrier();  // every wave is done with the previous head's tiles
     ht.template store<NP, kBf16>(Hs);
     // mask factorisation of this head (see the header)
     if (tid < Q) {
-      acs_s[tid] = a_own;
+      acs_s[tid] = a_own;  // Acs; the tile kind: r (the row factors' exponents)
       // exp of the sum of dt*A over the later tokens of j's tile
-      if (!by_chunk) w_s[tid] = __expf(ex_r);
+      if (by_elem) w_s[tid] = __expf(ex_r);
+      // the tile kind's tile totals (its w_s is otherwise unused), written
+      // here so that their registers are free for the next head's loads
+      if (by_tile && tid < 8) w_s[tid] = ex_e;
       if constexpr (kDen) {
         // the ones column's staging: exp(-Acs_j) dt_j (chunk mask; w_s is
         // free there), dt_j (per-element mask).  bf16 without options: the
@@ -383,13 +401,14 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         }
       }
     }
-    if (by_chunk) {
-      // x_j scaled by exp(-Acs_j)
+    if (by_chunk || by_tile) {
+      // x_j scaled by exp(-Acs_j) (chunk) or exp(r_j) (tile: the sum of dt*A
+      // over j's later tokens in its tile, in (0, 1])
       float sreg[XTile::NPT][4];
 #pragma unroll
       for (int i = 0; i < XTile::NPT; ++i)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf(-xa4[i][rr]);
+        for (int rr = 0; rr < 4; ++rr) sreg[i][rr] = __expf(by_chunk ? -xa4[i][rr] : xa4[i][rr]);
       xt.template store<QP, 2, kBf16, false, kBf16>(XT, nullptr, sreg);
     } else if (kOpts && p.x_times_dt) {
       // per-element mask: x staged times dt_j, read as given (|Acs_j| may be
@@ -409,14 +428,14 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     const float et = ex_e;  // this head's dt*A / tile totals (per-element mask)
     const float dti = dt_row;  // (options) this head's, before the next head's prefetch
     const float dh = d_head;
-    if (nxt >= 0) prefetch(h0 + nxt, by_chunk);
+    if (nxt >= 0) prefetch(h0 + nxt, kind);
     if (!active) return;
 
     const int i_loc = I * 32 + lr;
     // per-element mask: the sum of dt*A over this lane's tile up to its token
     // (a scan over lanes 0-31, which hold the tile's tokens; lane half 1 takes
     // the value of its row from half 0)
-    const float ci = by_chunk ? 0.0f : __shfl(seg_inclusive_sum<32>(et), lr);
+    const float ci = by_elem ? __shfl(seg_inclusive_sum<32>(et), lr) : 0.0f;
     // kernel tile J of row tile I as 16 fp32 values: G[i_loc][32J + 8(r/4) + 4lg + r%4]
     auto g_values = [&](int J, float (&g)[16]) {
       const int tl = I * (I + 1) / 2 + J;
@@ -571,7 +590,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       }
     }
     float gsum = 0.0f;
-    if (!by_chunk) {
+    if (by_elem) {
 #pragma unroll
       for (int j = 0; j < NPH; ++j)
 #pragma unroll
@@ -819,8 +838,55 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         gsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(et), 32 + J));
       }
     };
-    if (by_chunk)
+    // tile factorisation (plain bf16): with x_j staged times exp(r_j), the
+    // sum over (j, i] for j in tile J < I is r_j + the totals of the tiles
+    // strictly between + c_i, and c_i = T_I - r_i, so that
+    //   y_i = exp(-r_i) [e_0..e_I (C h)_i + sum_J<I e_(J+1)..e_I P_J + P_I]
+    // with e_g = exp(T_g) (tile totals, one-signed sums) and P_J the tile
+    // products with the kernel tiles as stored: the accumulator is scaled by
+    // e_J before each tile J is added (Horner), then by exp(-r_i) once.  Every
+    // factor is a one-signed sum's exp: e_g and exp(r_j) in (0, 1], exp(-r_i)
+    // within e^64 (the largest tile decay of such a head).
+    auto diag_blocks_tile = [&]() {
+      using M = std::integral_constant<int, kMaskChunk>;  // tiles to the matrix cores as stored
+      auto scale = [&](int g) {
+        const float e = __expf(w_s[g]);  // e_g, the same for every lane
+#pragma unroll
+        for (int j = 0; j < NPH; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][r] *= e;
+      };
+      TileOps ob0, ob1;
+      load_ops(0, ob0);
+      int J = 0;
+      for (; J + 1 < I; J += 2) {
+        load_ops(J + 1, ob1);
+        scale(J);
+        tile(J, ob0, Off(), M());
+        load_ops(J + 2, ob0);
+        scale(J + 1);
+        tile(J + 1, ob1, Off(), M());
+      }
+      if (J < I) {
+        load_ops(I, ob1);
+        scale(J);
+        tile(J, ob0, Off(), M());
+        scale(I);
+        tile(I, ob1, Diag(), M());
+      } else {
+        scale(I);
+        tile(I, ob0, Diag(), M());
+      }
+      const float er = __expf(-ai);  // ai holds r of this lane's token (the tile kind)
+#pragma unroll
+      for (int j = 0; j < NPH; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] *= er;
+    };
+    if constexpr (by_chunk)
       diag_blocks(std::integral_constant<int, kMaskChunk>());
+    else if constexpr (by_tile)
+      diag_blocks_tile();
     else
       diag_blocks_exact();
     if (kDen && !kDenPre && by_chunk) {
@@ -928,16 +994,27 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
       __builtin_amdgcn_wave_barrier();
     }
   };
+  using KChunk = std::integral_constant<int, kMaskChunk>;
+  using KTile = std::integral_constant<int, kMaskTile>;
+  using KElem = std::integral_constant<int, kMaskExact>;
   for (uint64_t m = chunk_bits; m;) {
     const int hh = (int)__builtin_ctzll(m);
     m &= m - 1;
-    head_iter(hh, m ? (int)__builtin_ctzll(m) : -1, std::true_type());
+    head_iter(hh, m ? (int)__builtin_ctzll(m) : -1, KChunk());
   }
-  if (exact_bits) prefetch(h0 + first_exact, false);
-  for (uint64_t m = exact_bits; m;) {
+  if constexpr (kTileMode) {
+    if (tile_bits) prefetch(h0 + (int)__builtin_ctzll(tile_bits), kMaskTile);
+    for (uint64_t m = tile_bits; m;) {
+      const int hh = (int)__builtin_ctzll(m);
+      m &= m - 1;
+      head_iter(hh, m ? (int)__builtin_ctzll(m) : -1, KTile());
+    }
+  }
+  if (walk_bits) prefetch(h0 + (int)__builtin_ctzll(walk_bits), kMaskExact);
+  for (uint64_t m = walk_bits; m;) {
     const int hh = (int)__builtin_ctzll(m);
     m &= m - 1;
-    head_iter(hh, m ? (int)__builtin_ctzll(m) : -1, std::false_type());
+    head_iter(hh, m ? (int)__builtin_ctzll(m) : -1, KElem());
   }
 }
 

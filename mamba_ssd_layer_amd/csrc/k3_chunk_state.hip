@@ -250,7 +250,14 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
         eo[i] = el[i];
         ro[i] = tsx + sfx[i];
       }
-      if ((lane & (SEG - 1)) == 0) ws.ttot[(k * H + h) * 8 + lane / SEG] = tsx + acc2;
+      const bool tile_lane = (lane & (SEG - 1)) == 0;
+      if (tile_lane) ws.ttot[(k * H + h) * 8 + lane / SEG] = tsx + acc2;
+      // the largest tile decay (-min of the tile sums), which decides whether
+      // the output kernel may factor this head's mask by 32-token tile
+      float td = tile_lane ? -(tsx + acc2) : 0.0f;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) td = fmaxf(td, __shfl_xor(td, off, kWave));
+      if (lane == 0) ws.tmax[k * H + h] = td;
     }
   }
 

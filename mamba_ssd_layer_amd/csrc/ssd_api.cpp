@@ -86,6 +86,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws, Carver* car
   char* ell = take(K * H * p.Q * sizeof(float));
   char* rsuf = take(K * H * p.Q * sizeof(float));
   char* ttot = take(K * H * 8 * sizeof(float));
+  char* tmax = take(K * H * sizeof(float));
   char* xlog = take(p.x_times_dt ? K * H * p.Q * sizeof(float) : 0);
   char* states = take(K * H * PN * esz);
   char* hin = take(K * H * PN * esz);
@@ -105,6 +106,7 @@ size_t workspace_layout(const Problem& p, char* base, Workspace* ws, Carver* car
     ws->ell = reinterpret_cast<float*>(ell);
     ws->rsuf = reinterpret_cast<float*>(rsuf);
     ws->ttot = reinterpret_cast<float*>(ttot);
+    ws->tmax = reinterpret_cast<float*>(tmax);
     ws->xlog = p.x_times_dt ? reinterpret_cast<float*>(xlog) : nullptr;
     ws->states = states;
     ws->hin = hin;

@@ -147,6 +147,7 @@ struct Workspace {
   float* ell = nullptr;          // (kmax, H, Q) dt*A per token
   float* rsuf = nullptr;         // (kmax, H, Q) sum of dt*A over the later tokens of its 32-token tile
   float* ttot = nullptr;         // (kmax, H, 8) sum of dt*A over each 32-token tile
+  float* tmax = nullptr;         // (kmax, H)    the largest decay of a 32-token tile, -min of ttot
   float* xlog = nullptr;         // (kmax, H, Q) Acs - ln dt, the log of x's staging divisor
                                  //              (only with x_times_dt)
   void* states = nullptr;        // (kmax, H, P, N) chunk states, element dtype

@@ -158,15 +158,36 @@ def _scaled_decay(inp, ell):
 
 
 @pytest.mark.parametrize("dtype,Q", [("f32", 128), ("f32", 256), ("bf16", 256), ("bf16", 128)])
-@pytest.mark.parametrize("ell", [-0.05, -0.2, -0.5, -8.0])
+@pytest.mark.parametrize("ell", [-0.05, -0.2, -0.5, -1.0, -2.5, -8.0])
 def test_large_decays_plain(dev, dtype, Q, ell):
     """The plain forward (ssd_chunked_fwd) with per-token decays from mild to
     extreme: a chunk's total decay of e^(Q ell) selects the whole-chunk mask
-    factorisation (within e^16 on fp32, e^64 on bf16) or the per-element mask
-    from addition-only segment sums ("LLM(十一)——Mamba" §3.5.4); both hold the
-    stated bar (dt*A = -8 per token: even one 32-token tile decays by e^-256)."""
+    factorisation (within e^16 on fp32, e^64 on bf16), else on bf16 the
+    per-tile factorisation when no 32-token tile decays by more than e^64
+    (about 32 ell), else the per-element mask, all from one-signed sums
+    ("LLM(十一)——Mamba" §3.5.4); each holds the stated bar (dt*A = -8 per
+    token: even one 32-token tile decays by e^-256)."""
     w = SMALL.with_(dtype=dtype, dstate=128, chunk_len=Q, seqlen=700, batch=2, nheads=4, ngroups=1)
     check_parity(_scaled_decay(make_inputs(w, 64), ell), dev, label=f"plain {dtype} Q={Q} dt*A~{ell}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mixed_mask_kinds(dev, dtype):
+    """Heads whose decays span the mask factorisations inside one workgroup
+    (whole chunk, 32-token tile, per element: A from -0.5 to -40 at dt about
+    0.1), so that the output kernel's head loops hand over between kinds, in
+    batched and packed form."""
+    from mamba_ssd_layer_amd.workloads import Inputs
+    w = SMALL.with_(dtype=dtype, dstate=128, chunk_len=256, seqlen=900, batch=2, nheads=8, ngroups=1)
+    inp = make_inputs(w, 71)
+    A = (-np.exp(np.linspace(np.log(0.5), np.log(40.0), w.nheads))).astype(np.float32)
+    dt = (inp.dt / inp.dt.mean() * 0.1).astype(np.float32)
+    mixed = Inputs(w, inp.x, dt, A, inp.B, inp.C)
+    check_parity(mixed, dev, label=f"mixed kinds {dtype}")
+    wv = w.with_(varlen=True, batch=3)
+    vin = make_inputs(wv, 72, seqlens=[300, 0, 1100])
+    dtv = (vin.dt / vin.dt.mean() * 0.1).astype(np.float32)
+    check_parity(Inputs(wv, vin.x, dtv, A, vin.B, vin.C, vin.cu_seqlens), dev, label=f"mixed kinds packed {dtype}")
 
 
 def test_intermediates_match_chunked_reference(dev):
