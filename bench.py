@@ -110,10 +110,13 @@ def decode_work(w):
     return flops, byts
 
 
-def bench_decode(bd, torch, steps, warmup):
-    """One decode step per sequence on the decode workload, timed like the
-    forward (host clock over `steps` back-to-back steps after `warmup` untimed
-    ones), plus the kernel's average launch time from HIP events."""
+def bench_decode(bd, torch, steps, warmup, flush):
+    """One decode step per sequence on the decode workload: cold (the
+    last-level cache flushed before each step, HIP events per step; the
+    roofline uses this) and warm (host clock over back-to-back steps), plus the
+    kernel's average launch time from the library's HIP events, both ways.
+    The fp32 state (168 MB) fits the 256 MiB last-level cache, so only the cold
+    figure speaks for HBM."""
     from mamba_ssd_layer_amd.workloads import DECODE_WORKLOADS, initial_states, make_inputs
     w = DECODE_WORKLOADS["decode_2p7b_b64"]
     dev = torch.device("cuda:0")
@@ -126,31 +129,29 @@ def bench_decode(bd, torch, steps, warmup):
     C = torch.from_numpy(inp.C[:, 0]).to(dev).to(tdt).contiguous()
     state = torch.from_numpy(initial_states(w.batch, w.nheads, w.headdim, w.dstate, 0)).to(dev)
     y = torch.empty_like(x)
+
+    def step():
+        bd.ssd_decode_step(x, dt, A, B, C, state, y=y)
+
     for _ in range(warmup):
-        bd.ssd_decode_step(x, dt, A, B, C, state, y=y)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        bd.ssd_decode_step(x, dt, A, B, C, state, y=y)
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
-    bd.kernel_timing_read(reset=True)
-    bd.kernel_timing_enable(True)
-    for _ in range(steps):
-        bd.ssd_decode_step(x, dt, A, B, C, state, y=y)
-    torch.cuda.synchronize()
-    bd.kernel_timing_enable(False)
-    kms = bd.kernel_timing_read(reset=True)["decode_step"]
-    kms = kms[0] / kms[1] if kms[1] else None
+        step()
+    warm_ms = time_back_to_back(torch, step, steps)
+    cold_ev, _ = time_steps(torch, step, steps, flush)
+    cold = percentiles(cold_ev)
+    kms = kernel_times(bd, torch, step, steps, flush).get("decode_step")
+    kms_warm = kernel_times(bd, torch, step, steps).get("decode_step")
     flops, byts = decode_work(w)
     ach = byts / (kms / 1e3) / 1e9 if kms else None
     return {
         "workload": w.name, "batch": w.batch, "nheads": w.nheads, "headdim": w.headdim,
         "dstate": w.dstate, "ngroups": w.ngroups, "dtype": w.dtype,
-        "us_per_step": sec * 1e6, "tokens_per_s": w.batch / sec,
+        "us_per_step": cold["mean"] * 1e3, "tokens_per_s": w.batch / (cold["mean"] / 1e3),
+        "cold_ms": cold, "warm_us_per_step": warm_ms * 1e3, "warm_tokens_per_s": w.batch / (warm_ms / 1e3),
         "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ach / PEAK_HBM_GBS if ach else None, "traffic": None,
-                     "avg_launch_ms": kms, "bytes_per_launch": byts, "flops_per_launch": flops},
+                     "avg_launch_ms": kms, "avg_launch_ms_warm": kms_warm, "bytes_per_launch": byts,
+                     "flops_per_launch": flops,
+                     "note": "cold: the state comes from HBM; warm launches partly hit the last-level cache"},
     }
 
 
@@ -654,7 +655,7 @@ def main():
     }
 
     if not args.no_decode:
-        result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200))
+        result["decode"] = bench_decode(bd, torch, args.steps, min(args.warmup, 200), flush)
     if not args.no_normalized:
         result["normalized"] = bench_normalized(bd, torch, w, x, dt, A, B, C, cu,
                                                 min(args.steps, 100), min(args.warmup, 50))
