@@ -31,12 +31,20 @@
 //  * Causality: only tiles J <= I are used; on the diagonal tile the entries
 //    with j > i are a selected (or masked-off) 0, never exp(-inf) arithmetic.
 //    The mask is exp of the sum of ell = dt*A over the tokens (j, i], formed
-//    per head in one of two ways, chosen from the chunk's total log-decay
-//    (mask_by_chunk):
+//    per head in one of three ways, chosen from the chunk's total log-decay
+//    (mask_by_chunk) and, on the plain bf16 path, its largest 32-token-tile
+//    decay; each kind runs in a head loop of its own (chunk heads first, then
+//    tile, then per element), so that the chunk path's registers, schedule and
+//    load waits are not shaped by the other kinds' code:
 //    - chunk (total decay within e^64 on the bf16 path, e^16 on fp32): x_j is
 //      staged scaled by exp(-Acs_j) and the finished sums by exp(Acs_i), which
 //      Y_off needs as well; the kernel tiles go to the matrix cores as stored,
 //      with no per-tile work;
+//    - tile (plain bf16, no tile decaying by more than e^64): x_j staged times
+//      exp(r_j) (r_j: the sum over j's later tokens in its 32-token tile), the
+//      kernel tiles as stored, the accumulator scaled by exp(tile total) before
+//      each tile's product and each row once by exp(-r_i) (details at
+//      diag_blocks_tile); every factor the exp of a one-signed sum;
 //    - per element, by additions only ([M] §3.5.4: segment sums formed without
 //      subtracting cumsums): below the diagonal the sum over (j, i] is the sum
 //      over j's later tokens in its 32-token tile (r_j, a table exp(r_j)), plus
