@@ -491,16 +491,23 @@ def flop_report(w, tokens, seqlens, sec):
 
 def config_line(bd, torch, w, K, W, flush):
     """Forward of another workload: cold (cache flushed before each step) and
-    warm (back to back) times with percentiles, throughput and FLOP rates."""
+    warm (back to back) times with percentiles, throughput and FLOP rates, and
+    each kernel's cold launch time against its algorithmic bytes."""
     inp, t, seqlens, y, step = forward_setup(bd, torch, w)
     for _ in range(W):
         step()
     cold, _ = time_steps(torch, step, K, flush)
     warm_ms = time_back_to_back(torch, step, K)
+    kms = kernel_times(bd, torch, step, K, flush)
     tokens = int(inp.total_tokens)
     c = percentiles(cold)
     sec = c["mean"] / 1e3
     mio = min_io_bytes(w, tokens, len(seqlens))
+    kfl, kby = kernel_work(w, seqlens, cb_pass=kms.get("chunk_cb") is not None)
+    # per kernel: cold launch time (events) and its algorithmic bytes' share of 8 TB/s
+    kern = {k: {"avg_launch_ms": kms[k], "bytes_per_launch": kby[k],
+                "hbm_frac": kby[k] / (kms[k] / 1e3) / 1e9 / PEAK_HBM_GBS}
+            for k in kby if kby[k] and kms.get(k)}
     del t, y
     return {"workload": w.name, "tokens": tokens, "seqlen": w.seqlen if not w.varlen else None,
             "batch": w.batch, "nheads": w.nheads, "dstate": w.dstate, "ngroups": w.ngroups,
@@ -508,7 +515,8 @@ def config_line(bd, torch, w, K, W, flush):
             "cold_ms": c, "tokens_per_s": tokens / sec, "warm_ms_per_step": warm_ms,
             "warm_tokens_per_s": tokens / (warm_ms / 1e3),
             "tflops": flop_report(w, tokens, seqlens, sec),
-            "hbm_min_io": {"bytes": mio, "GBps": mio / sec / 1e9, "pct_peak": 100.0 * mio / sec / 1e9 / PEAK_HBM_GBS}}
+            "hbm_min_io": {"bytes": mio, "GBps": mio / sec / 1e9, "pct_peak": 100.0 * mio / sec / 1e9 / PEAK_HBM_GBS},
+            "kernels_cold": kern}
 
 
 def main():
