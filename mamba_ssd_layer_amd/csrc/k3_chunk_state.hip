@@ -83,14 +83,18 @@ struct ChunkStateCfg {
   static constexpr size_t bt_bytes = (size_t)NT * QP * sizeof(T);
   static constexpr size_t xs_bytes = ((size_t)kXRows * QP + (size_t)P * SP) * sizeof(T);
   static constexpr size_t tile_bytes = kRegB ? (bt_bytes > xs_bytes ? bt_bytes : xs_bytes) : bt_bytes + xs_bytes;
-  // log-decays, then decay weights, of every head of the block (LDS left over
-  // by the tiles bounds the heads per workgroup)
+  // bf16: the step sizes of the block's heads are kept in LDS too (the
+  // dt-scaled input's weights need them in the scan)
+  static constexpr bool kDtLds = kBf16;
+  static constexpr size_t head_bytes = (kDtLds ? 2 : 1) * (size_t)Q * sizeof(float);
+  // log-decays, then decay weights (and step sizes), of every head of the
+  // block (LDS left over by the tiles bounds the heads per workgroup)
   static constexpr int kMaxHB = (int)(((size_t)kLdsLimit - (tile_bytes < (size_t)kLdsLimit ? tile_bytes : kLdsLimit)) /
-                                      ((size_t)Q * sizeof(float))) < kMaxHeadsPerBlock
+                                      head_bytes) < kMaxHeadsPerBlock
                                     ? (int)(((size_t)kLdsLimit - (tile_bytes < (size_t)kLdsLimit ? tile_bytes : kLdsLimit)) /
-                                            ((size_t)Q * sizeof(float)))
+                                            head_bytes)
                                     : kMaxHeadsPerBlock;
-  static constexpr size_t lds_bytes = tile_bytes + (size_t)(kMaxHB > 0 ? kMaxHB : 1) * Q * sizeof(float);
+  static constexpr size_t lds_bytes = tile_bytes + (size_t)(kMaxHB > 0 ? kMaxHB : 1) * head_bytes;
   static constexpr bool fits = kMaxHB >= 1 && lds_bytes <= (size_t)kLdsLimit;
   // log-decay loads per thread: Q tokens x kMaxHB heads over the workgroup
   static constexpr int kEllPT = (Q * (kMaxHB > 0 ? kMaxHB : 1) + kCsThreads - 1) / kCsThreads;
@@ -110,6 +114,8 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   constexpr int SEG = 32 / R;  // lanes per 32-token tile in the cumsum
   __shared__ __attribute__((aligned(16))) char smem[Cfg::tile_bytes];
   __shared__ __attribute__((aligned(16))) float wbuf[(Cfg::kMaxHB > 0 ? Cfg::kMaxHB : 1) * Q];  // log-decays, then w
+  // bf16: the step sizes dt (clamped past the chunk's end as the decays are)
+  __shared__ __attribute__((aligned(16))) float dtbuf[Cfg::kDtLds ? (Cfg::kMaxHB > 0 ? Cfg::kMaxHB : 1) * Q : 1];
   T* bT = reinterpret_cast<T*>(smem);
   T* xwT = reinterpret_cast<T*>(smem + (kRegB ? 0 : Cfg::bt_bytes));
   T* Ss = xwT + kXRows * QP;
@@ -144,14 +150,15 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
   // e % HB; both advance by a fixed step per i (no division in the loop)
   const int et0 = tid / HB, eh0 = tid % HB;
   const int dt_step = kCsThreads / HB, dh_step = kCsThreads % HB;
-  float ell[Cfg::kEllPT];
+  float ell[Cfg::kEllPT], dte[Cfg::kEllPT];
   {
     int t = et0, hh = eh0;
 #pragma unroll
     for (int i = 0; i < Cfg::kEllPT; ++i) {
       const bool in = t < Q;  // past the table: clamped to its last element
       const int tc = in ? min(t, L - 1) : L - 1, hc = in ? hh : HB - 1;
-      ell[i] = p.dt[(cd.t0 + tc) * H + h0 + hc] * p.A[h0 + hc];
+      dte[i] = p.dt[(cd.t0 + tc) * H + h0 + hc];
+      ell[i] = dte[i] * p.A[h0 + hc];
       t += dt_step;
       hh += dh_step;
       if (hh >= HB) { hh -= HB; ++t; }
@@ -181,7 +188,10 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
     int t = et0, hh = eh0;
 #pragma unroll
     for (int i = 0; i < Cfg::kEllPT; ++i) {
-      if (t < Q) wbuf[hh * Q + t] = t < L ? ell[i] : 0.0f;
+      if (t < Q) {
+        wbuf[hh * Q + t] = t < L ? ell[i] : 0.0f;
+        if (Cfg::kDtLds && p.x_times_dt) dtbuf[hh * Q + t] = dte[i];
+      }
       t += dt_step;
       hh += dh_step;
       if (hh >= HB) { hh -= HB; ++t; }
@@ -226,7 +236,9 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const float a = excl + run[i];
-        const float dtl = dtp[(int64_t)min(lane * R + i, L - 1) * H];
+        // (bf16: from the LDS table, so that the scan waits for no load still
+        // in flight, the first heads' x tiles among them)
+        const float dtl = Cfg::kDtLds ? dtbuf[hh * Q + lane * R + i] : dtp[(int64_t)min(lane * R + i, L - 1) * H];
         gout[i] = a;
         xl[i] = a - __logf(dtl);
         wbuf[hh * Q + lane * R + i] = (lane * R + i < L) ? __expf(sxcl + sfx[i]) * dtl : 0.0f;
