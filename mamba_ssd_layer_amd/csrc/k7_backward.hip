@@ -124,6 +124,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_prep_kernel(BwdProblem b) {
   const int tid = threadIdx.x;
   const int H = b.H, P = b.P, N = b.N, G = b.G, NK = b.NK;
   const int hpg = H / G;
+  // the head-sum gradients, accumulated by later kernels, start at zero
+  if (t == 0)
+    for (int h = tid; h < H; h += kBwThreads) {
+      b.dA[h] = 0.0f;
+      if (b.dD != nullptr) b.dD[h] = 0.0f;
+    }
   const TokSeq q = token_seq(b, t);
   const int64_t i = t - q.t0;
   const int64_t f = q.t0 + (q.L - 1 - i);
@@ -669,8 +675,12 @@ static hipError_t launch_glue(const BwdProblem& b, int stage, hipStream_t s) {
   const dim3 blk(kBwThreads);
   switch (stage) {
     case 0:
-      hipLaunchKernelGGL(bwd_zero_kernel, dim3(1), blk, 0, s, b);
-      if (b.total > 0) hipLaunchKernelGGL((bwd_prep_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
+      // the prep kernel's first workgroup clears dA and dD; without tokens a
+      // kernel of its own does
+      if (b.total > 0)
+        hipLaunchKernelGGL((bwd_prep_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
+      else
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3(1), blk, 0, s, b);
       if ((b.h0c != nullptr || b.dfb != nullptr) && b.nseq > 0)
         hipLaunchKernelGGL(bwd_prep_states_kernel, dim3((unsigned)(b.nseq * b.H * b.NK)), blk, 0, s, b);
       break;
