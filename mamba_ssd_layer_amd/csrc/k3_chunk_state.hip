@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kCsThreads, 1) void chunk_state_kernel(Problem p, W
       sfx[i] = acc2;
       acc2 += el[i];
     }
-    const float excl = seg_exclusive_sum<64>(acc);          // the earlier lanes' tokens
-    const float sxcl = seg_exclusive_suffix_sum<64>(acc2);  // the later lanes' tokens
+    const float excl = wave_prefix_excl_dpp(acc);    // the earlier lanes' tokens
+    const float sxcl = wave_suffix_excl_dpp(acc2);   // the later lanes' tokens
     const float lam = __shfl(excl + run[R - 1], 63);
     float* gout = ws.acs + (k * H + h) * Q + lane * R;
     if (p.x_times_dt) {

@@ -173,6 +173,49 @@ __device__ __forceinline__ float seg_exclusive_suffix_sum(float v) {
   return seg_inclusive_suffix_sum<SEG>((threadIdx.x & (SEG - 1)) == SEG - 1 ? 0.0f : e);
 }
 
+// Scans over a whole 64-lane wave on DPP lane moves (VALU latency, no LDS
+// round trip per step): Hillis-Steele within each row of 16 lanes, the rows
+// then joined by their totals (readlane).  Addition only, as above.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move0(float v) {  // lanes without a source read 0
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// sum over this lane and the lanes before it
+__device__ __forceinline__ float wave_prefix_incl_dpp(float v) {
+  v += dpp_move0<0x111>(v);  // row_shr:1
+  v += dpp_move0<0x112>(v);  // row_shr:2
+  v += dpp_move0<0x114>(v);  // row_shr:4
+  v += dpp_move0<0x118>(v);  // row_shr:8
+  const float t0 = lane_value(v, 15), t1 = lane_value(v, 31), t2 = lane_value(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  const float o2 = t0 + t1;
+  return row == 0 ? v : v + (row == 1 ? t0 : row == 2 ? o2 : o2 + t2);
+}
+// sum over the lanes before this one (0 for lane 0): the inclusive sum of the
+// values shifted up by one lane
+__device__ __forceinline__ float wave_prefix_excl_dpp(float v) {
+  return wave_prefix_incl_dpp(dpp_move0<0x138>(v));  // wave_shr:1: lane i reads lane i - 1
+}
+// sum over the lanes after this one; TILE32: only those of its 32-lane half
+template <bool TILE32 = false>
+__device__ __forceinline__ float wave_suffix_excl_dpp(float v) {
+  const int lane = threadIdx.x & 63;
+  float u = dpp_move0<0x130>(v);  // wave_shl:1: lane i reads lane i + 1 (lane 63 reads 0)
+  if (TILE32 && (lane & 31) == 31) u = 0.0f;
+  u += dpp_move0<0x101>(u);  // row_shl:1
+  u += dpp_move0<0x102>(u);  // row_shl:2
+  u += dpp_move0<0x104>(u);  // row_shl:4
+  u += dpp_move0<0x108>(u);  // row_shl:8
+  const float t1 = lane_value(u, 16), t2 = lane_value(u, 32), t3 = lane_value(u, 48);
+  const int row = lane >> 4;
+  if (TILE32) return (row & 1) ? u : u + (row == 0 ? t1 : t3);
+  const float o1 = t3 + t2;
+  return row == 3 ? u : u + (row == 2 ? t3 : row == 1 ? o1 : o1 + t1);
+}
+
 // Mask factorisation of one (chunk, head) of the diagonal block: by the whole
 // chunk (x_j staged times exp(-Acs_j), the finished sums times exp(Acs_i)) when
 // the chunk's total log-decay lam is at least -limit, else per element from

@@ -142,7 +142,30 @@ struct TransTile {
 #pragma unroll
       for (int rr = 0; rr < RPB; ++rr)
         sc[rr] = SCALE == 1 ? scale[rb * RPB + rr] : SCALE == 2 ? sreg[i][rr] : 1.0f;
-      if constexpr (kBf16) {
+      if constexpr (kBf16 && SCALE == 0 && RPB == 8 && !PERM16) {
+        // no scale: a pure 16-bit transpose, each output word two halves of
+        // input words picked by v_perm_b32 (low halves for even columns,
+        // high halves for odd ones), no conversion
+        uint32_t w[8][4];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const uint4 q = row(i, rb, rr);
+          w[rr][0] = q.x; w[rr][1] = q.y; w[rr][2] = q.z; w[rr][3] = q.w;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          uint4 o;
+          o.x = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], sel);
+          o.y = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], sel);
+          o.z = __builtin_amdgcn_perm(w[5][c >> 1], w[4][c >> 1], sel);
+          o.w = __builtin_amdgcn_perm(w[7][c >> 1], w[6][c >> 1], sel);
+          const int r = cb * 8 + c;
+          T* lrow = lds + (ROWPERM ? lds_row_perm(r) : r) * DP;
+          const int key = SWZ ? lds_swizzle<ROWS>(r) : 0;
+          *reinterpret_cast<uint4*>(lrow + (rb ^ key) * 8) = o;
+        }
+      } else if constexpr (kBf16) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           float f[RPB];
