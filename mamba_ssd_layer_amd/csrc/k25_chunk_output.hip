@@ -223,7 +223,12 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   XTile xt;
   RowTile<E, P, N, kCoThreads> ht;
   float a_own = 0.f;
+  // bf16 options on the chunk (and tile) kinds: the step sizes come from the
+  // coalesced table of Acs - ln dt (|Acs| <= 64 there, so exp(Acs - (Acs - ln dt))
+  // gives dt to a few 1e-6), not from gathered loads of dt, one cache line per token
+  constexpr bool kXlDt = kBf16;
   float dt_own = 1.0f;  // normalised output with the dt-scaled input: dt of token tid
+                        // (kXlDt, chunk kind: Acs - ln dt of token tid instead)
   // chunk mask: log of the staging divisor of this thread's x rows.
   float xa4[XTile::NPT][4];
   // per-element mask: r of token tid (tid < Q); dt*A of this lane's output
@@ -231,6 +236,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
   float ex_r = 0.0f, ex_e = 0.0f;
   const int i_tab = max(I, 0) * 32 + lr;  // this lane's token in the tables (idle waves: any)
   float dt_row = 1.0f;  // options: dt of this lane's output token (the skip term's entry)
+                        // (kXlDt, chunk kind: Acs - ln dt of that token instead)
   float d_head = 0.0f;  // options: the skip weight D_h of the prefetched head
   // kind: the head's mask factorisation (a constant at every call)
   auto prefetch = [&](int h, int kind) {
@@ -246,9 +252,11 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     // under a run-time condition, would make every head wait for all the
     // loads in flight, the next head's among them.
     if constexpr (kOpts) {
-      if constexpr (kDen) dt_own = p.dt[(cd.t0 + min(tid, L - 1)) * H + h];
+      const bool from_xl = kXlDt && kind != kMaskExact;
+      if constexpr (kDen)
+        dt_own = from_xl ? (xlbase + h * Q)[min(tid, Q - 1)] : p.dt[(cd.t0 + min(tid, L - 1)) * H + h];
       d_head = *(p.D != nullptr ? p.D + h : p.dt);
-      dt_row = p.dt[(cd.t0 + min(i_tab, L - 1)) * H + h];
+      dt_row = from_xl ? (xlbase + h * Q)[i_tab] : p.dt[(cd.t0 + min(i_tab, L - 1)) * H + h];
     }
     if (kind != kMaskExact) {
       // the log of x's staging scale: -Acs (chunk) or r (tile) of the thread's rows
@@ -397,7 +405,9 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
         // chunk mask's values as bf16 pairs (j, j + 1) in word j / 2, for the
         // products' row sums on v_dot2_f32_bf16
         if (by_chunk) {
-          const float sj = __expf(-a_own) * (kOpts && p.x_times_dt ? dt_own : 1.0f);
+          // (kXlDt: dt_own holds Acs - ln dt, or Acs without the dt-scaled input)
+          const float sj = kOpts ? (kXlDt ? __expf(-dt_own) : __expf(-a_own) * (p.x_times_dt ? dt_own : 1.0f))
+                                 : __expf(-a_own);
           if constexpr (kBf16 && !kDenPre) {
             const float sn = __shfl_down(sj, 1, kWave);
             if ((tid & 1) == 0) reinterpret_cast<uint32_t*>(w_s)[tid >> 1] = pack_bf16x2(sj, sn);
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     }
     lds_barrier();
     const float et = ex_e;  // this head's dt*A / tile totals (per-element mask)
-    const float dti = dt_row;  // (options) this head's, before the next head's prefetch
+    const float dt_cap = dt_row;  // (options) this head's, before the next head's prefetch
     const float dh = d_head;
     if (nxt >= 0) prefetch(h0 + nxt, kind);
     if (!active) return;
@@ -579,6 +589,8 @@ __global__ __launch_bounds__(kCoThreads, 1) void chunk_output_kernel(Problem p, 
     }
     const float ai = acs_s[i_loc];
     const float eo = __expf(ai);
+    // options: dt of this lane's token (kXlDt, chunk kind: from Acs - ln dt)
+    const float dti = (kXlDt && !by_elem) ? __expf(ai - dt_cap) : dt_cap;
     // skip term D_h x_i as an extra diagonal entry of the tile product: x^T_i
     // is x_i times a staging scale that the output factor undoes, so the entry
     // is D_h, over dt_i when the input enters as dt x (x^T_i then carries dt_i),
