@@ -399,47 +399,89 @@ void bwd_dl_kernel(BwdProblem b) {
   }
 }
 
-// Kernel 2, one wave per (chunk, head):
+// Kernel 2, one wave per (chunk, head), the heads of a block of HB in one
+// workgroup:
 //   d(ell_t) = Vtot + K + sum_{k<t} (u_k - v_k),  v = row - col + yterm, u = dterm
+// dt and d(dt) are token-major (Ttot, H): the block's (token, head) values go
+// through an LDS tile, loaded and stored with consecutive threads on
+// consecutive heads of a token row, instead of one cache line per token and head.
+constexpr int kDlScanHeads = 8;
 template <int Q>
-__global__ __launch_bounds__(64) void bwd_dl_scan_kernel(BwdProblem b) {
+__global__ __launch_bounds__(64 * kDlScanHeads) void bwd_dl_scan_kernel(BwdProblem b, int HB) {
   constexpr int R = Q / 64;
   constexpr int NS = Q == 256 ? 2 : 1;
+  constexpr int TP = kDlScanHeads + 1;  // LDS pitch of a token row (odd: a column read hits distinct banks)
+  __shared__ float tile[Q * TP];
   const int H = b.H;
-  const int64_t kh = blockIdx.x;
-  const int h = (int)(kh % H);
-  const int64_t k = kh / H;
+  const int nhb = H / HB;
+  const int64_t k = blockIdx.x / nhb;
+  const int h0 = (int)(blockIdx.x % nhb) * HB;
   const int64_t t0 = k * Q;
-  const int lane = threadIdx.x;
-  const float Ah = b.A[h];
-  const int64_t base = h * b.total + t0 + lane * R;
-  float du[R], dtv[R], vsum = 0.0f, wsum = 0.0f;
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  // step sizes of the block: element e = token e / HB, head e % HB
+  for (int e = tid; e < Q * HB; e += 64 * kDlScanHeads)
+    tile[(e / HB) * TP + e % HB] = b.dt[(t0 + e / HB) * H + h0 + e % HB];
+  __syncthreads();
+  const bool active = wid < HB;  // waves past the block's heads only help with the tile
+  const int h = h0 + (active ? wid : 0);
+  float run = 0.0f, sdA = 0.0f;
+  float du[R], dd[R];
+  if (active) {
+    const float Ah = b.A[h];
+    const int64_t base = h * b.total + t0 + lane * R;
+    float dtv[R], vsum = 0.0f, wsum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    float v = b.dl_v[base + i];
+    for (int i = 0; i < R; ++i) {
+      float v = b.dl_v[base + i];
 #pragma unroll
-    for (int hf = 0; hf < NS; ++hf) v -= b.dl_cols[(int64_t)hf * H * b.total + base + i];
-    vsum += v;
-    du[i] = b.dl_u[base + i] - v;
-    wsum += du[i];
-    dtv[i] = b.dt[(t0 + lane * R + i) * H + h];
+      for (int hf = 0; hf < NS; ++hf) v -= b.dl_cols[(int64_t)hf * H * b.total + base + i];
+      vsum += v;
+      du[i] = b.dl_u[base + i] - v;
+      wsum += du[i];
+      dtv[i] = tile[(lane * R + i) * TP + wid];
+    }
+    float vtot = vsum;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vtot += __shfl_xor(vtot, off);
+    const float incl = wave_inclusive_sum(wsum);
+    run = vtot + b.dl_kc[k * H + h] + (incl - wsum);  // everything before this lane's tokens
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t tok = t0 + lane * R + i;
+      dd[i] = Ah * run + (b.x_times_dt ? b.rd[h * b.total + tok] : 0.0f);
+      sdA += dtv[i] * run;
+      run += du[i];
+    }
   }
-  float vtot = vsum;
+  __syncthreads();  // every wave has read its step sizes
+  if (active) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) vtot += __shfl_xor(vtot, off);
-  const float incl = wave_inclusive_sum(wsum);
-  float run = vtot + b.dl_kc[kh] + (incl - wsum);  // everything before this lane's tokens
-  float sdA = 0.0f;
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int64_t tok = t0 + lane * R + i;
-    b.ddt[tok * H + h] = Ah * run + (b.x_times_dt ? b.rd[h * b.total + tok] : 0.0f);
-    sdA += dtv[i] * run;
-    run += du[i];
+    for (int i = 0; i < R; ++i) tile[(lane * R + i) * TP + wid] = dd[i];
   }
+  __syncthreads();
+  for (int e = tid; e < Q * HB; e += 64 * kDlScanHeads)
+    b.ddt[(t0 + e / HB) * H + h0 + e % HB] = tile[(e / HB) * TP + e % HB];
+  if (active) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sdA += __shfl_xor(sdA, off);
-  if (lane == 0) atomicAdd(b.dA + h, sdA);
+    for (int off = 32; off >= 1; off >>= 1) sdA += __shfl_xor(sdA, off);
+    // the chunk's share of dA, in place of the term read above (summed over
+    // the chunks by bwd_dA_sum_kernel: one value per (chunk, head), no
+    // atomics on the H addresses of dA, which every chunk would contend for)
+    if (lane == 0) b.dl_kc[k * H + h] = sdA;
+  }
+}
+
+// dA_h = the sum of the chunks' shares, in chunk order (fp64 accumulation)
+__global__ __launch_bounds__(256) void bwd_dA_sum_kernel(BwdProblem b, int64_t chunks) {
+  __shared__ double red[4];
+  const int h = blockIdx.x;
+  double acc = 0.0;
+  for (int64_t k = threadIdx.x; k < chunks; k += 256) acc += b.dl_kc[k * b.H + h];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) b.dA[h] = (float)(red[0] + red[1] + red[2] + red[3]);
 }
 
 bool backward_dl_supported(Dtype dt, int Q, int N) {
@@ -459,7 +501,13 @@ static void launch_dl_q(const BwdProblem& b, int64_t chunks, hipStream_t s) {
       if constexpr (Q <= 128) hipLaunchKernelGGL((bwd_dl_kernel<Q, 256>), grid, block, 0, s, b);
       break;
   }
-  hipLaunchKernelGGL((bwd_dl_scan_kernel<Q>), dim3((unsigned)(chunks * b.H)), dim3(64), 0, s, b);
+  // heads per scan workgroup: the largest divisor of H up to kDlScanHeads
+  int hb = 1;
+  for (int d = kDlScanHeads; d >= 1; --d)
+    if (b.H % d == 0) { hb = d; break; }
+  hipLaunchKernelGGL((bwd_dl_scan_kernel<Q>), dim3((unsigned)(chunks * (b.H / hb))), dim3(64 * kDlScanHeads), 0, s, b,
+                     hb);
+  hipLaunchKernelGGL(bwd_dA_sum_kernel, dim3((unsigned)b.H), dim3(256), 0, s, b, chunks);
 }
 
 hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s) {

@@ -127,7 +127,7 @@ struct BwdProblem {
   float* dl_v;                 // (H, Ttot) row sums of W + yterm
   float* dl_cols;              // (2, H, Ttot) column sums of W, per workgroup of the chunk
   float* dl_u;                 // (H, Ttot) dterm
-  float* dl_kc;                // (K, H) <Gout, exp(Lam) Hin>
+  float* dl_kc;                // (K, H) <Gout, exp(Lam) Hin>, then (after the d(ell) scan) each chunk's share of dA
   int nseg;                    // scan segments per (sequence, head): ceil(longest sequence / kBwdScanSeg)
   double* segsum;              // (S, H, nseg) fp64 segment sums of d(Acs)
   float* edot;                 // (S, H) <dfinal, h_last>
