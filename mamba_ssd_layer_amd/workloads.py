@@ -194,6 +194,29 @@ def scan_inputs(batch: int, seqlen: int, channels: int, dstate: int, dtype: str,
     return x, delta, A, B, C
 
 
+def long_device_inputs(seqlen: int, nheads: int, headdim: int, dstate: int, step: float, seed: int, device):
+    """Seeded inputs of one very long bf16 sequence, drawn on the device (for a
+    tensor too large for host arrays): x, B, C ~ N(0, 1) rounded to bf16 by
+    round-to-nearest-even (torch's cast), one B/C group; dt = step * (1 + 0.1 u),
+    u ~ U(0, 1) per token and head; A_head = -1.  Draw order from
+    torch.Generator(device).manual_seed(seed): x in blocks of 2^18 tokens, B,
+    C, u.  Returns device tensors x (1,T,H,P), dt (1,T,H), A (H,), B, C (1,T,1,N)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.empty((1, seqlen, nheads, headdim), dtype=torch.bfloat16, device=device)
+    blk = 1 << 18
+    for t in range(0, seqlen, blk):
+        n = min(blk, seqlen - t)
+        x[0, t:t + n] = torch.randn((n, nheads, headdim), generator=gen, device=device).to(torch.bfloat16)
+    B = torch.randn((1, seqlen, 1, dstate), generator=gen, device=device).to(torch.bfloat16)
+    C = torch.randn((1, seqlen, 1, dstate), generator=gen, device=device).to(torch.bfloat16)
+    dt = step * (1.0 + 0.1 * torch.rand((1, seqlen, nheads), generator=gen, device=device))
+    A = -torch.ones(nheads, dtype=torch.float32, device=device)
+    return x, dt.float().contiguous(), A, B, C
+
+
 def flops_pages(w: Workload, total_tokens: int, seqlens=None) -> dict:
     """FLOP accountings of one forward pass (no arithmetic of the map itself).
 

@@ -119,6 +119,43 @@ def test_varlen_equals_separate_runs(dev):
         np.testing.assert_array_equal(fs[0], fg[s])
 
 
+def test_offsets_beyond_int32(dev):
+    """One bf16 sequence of 2^21 + 4173 tokens and 16 heads: x and y hold more
+    than 2^31 elements, so every token, head and state offset past that point
+    needs 64-bit arithmetic.  Each token decays by about e^-0.2, a chunk of 256
+    tokens by more than e^-51 (the whole-chunk mask), so history older than two
+    chunks weighs less than e^-100, far below fp32 resolution: y over any window
+    equals the oracle run on that window and the two chunks before it from a
+    zero state.  Checked at the start, in the middle, past the 2^31-element
+    mark and on the ragged last chunk, and likewise the final state."""
+    from mamba_ssd_layer_amd.workloads import long_device_inputs
+    T, H, P, N, Q = (1 << 21) + 4173, 16, 64, 16, 256
+    assert T * H * P > 2 ** 31
+    log(f"[int64] drawing {T} tokens x {H} heads on the device")
+    x, dt, A, B, C = long_device_inputs(T, H, P, N, 0.2, 11, dev)
+    y, fs = bd.ssd_chunked_fwd(x, dt, A, B, C, Q)
+    torch.cuda.synchronize()
+    An = A.cpu().numpy()
+    past = (2 ** 31) // (H * P) + 300  # a token whose x offset is past 2^31 elements
+    for t_s in (0, 1 << 20, past, T - 77):
+        t_e = min(t_s + Q, T)
+        w0 = max(0, t_s - 2 * Q)
+        log(f"[int64] window [{t_s}, {t_e}) from {w0}")
+        sl = slice(w0, t_e)
+        yr, fr = oracle.recurrence(x[0, sl].float().cpu().numpy(), dt[0, sl].cpu().numpy(), An,
+                                   B[0, sl].float().cpu().numpy(), C[0, sl].float().cpu().numpy())
+        yg = y[0, t_s:t_e].float().cpu().numpy()
+        yw = yr[t_s - w0:]
+        err = np.linalg.norm(yg - yw, axis=(0, 2)) / np.linalg.norm(yw, axis=(0, 2))
+        log(f"[int64]   max rel-L2 over heads {err.max():.3e}")
+        assert err.max() < 2e-2
+        if t_e == T:
+            f = fs[0].cpu().numpy()
+            ef = np.linalg.norm((f - fr[0]).reshape(H, -1), axis=1) / np.linalg.norm(fr[0].reshape(H, -1), axis=1)
+            log(f"[int64]   final state max rel-L2 {ef.max():.3e}")
+            assert ef.max() < 2e-2
+
+
 def test_group_replication(dev):
     """G = H with B, C replicated per head equals G = 1, bit for bit."""
     w = SMALL.with_(ngroups=1, nheads=4, seqlen=400, dstate=128, chunk_len=128)
