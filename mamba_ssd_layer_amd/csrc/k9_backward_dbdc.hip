@@ -177,14 +177,14 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   // step sizes of head h (wave 0), and the tables built from them
   float dtl[R];
   float dtn = 0.0f;
-  auto load_dt = [&](int h) {
+  auto load_dt = [&](int ln, int h) {
     if (wid == 0) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) dtl[i] = b.dt[(t0 + lane * R + i) * H + h];
+      for (int i = 0; i < R; ++i) dtl[i] = b.dt[(t0 + ln * R + i) * H + h];
       dtn = c + 1 < CPS ? b.dt[(t0 + Q) * H + h] : 0.0f;
     }
   };
-  auto make_tables = [&](int h, int bs) {
+  auto make_tables = [&](int ln, int h, int bs) {
     if (wid == 0) {
       const float Ah = b.A[h];
       float run[R];
@@ -197,15 +197,15 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
       const float incl = wave_inclusive_sum(acc);
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        acs[bs][lane * R + i] = incl - acc + run[i];
-        dts[bs][lane * R + i] = dtl[i];
+        acs[bs][ln * R + i] = incl - acc + run[i];
+        dts[bs][ln * R + i] = dtl[i];
       }
       const float lam = __shfl(incl, 63);
       const float anext = c + 1 < CPS ? __expf(dtn * Ah) : 1.0f;
       // the same wave reads back the tile ends it wrote
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int j = lane * R + i;
+        const int j = ln * R + i;
         const float aj = incl - acc + run[i];
         const float dtf = xdt ? dtl[i] : 1.0f;
         fd[bs][j] = __expf(acs[bs][32 * (j / 32) + 31] - aj) * dtf;
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
     const bool more = u + 1 < nh;
     if (more) {
       load_states(ln, h_lo + u + 1);
-      load_dt(h_lo + u + 1);
+      load_dt(ln, h_lo + u + 1);
       issue_xy(ln, h_lo + u + 1, nx, ny);
     }
     int fo[4];
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
       head_tokens(ln, fo, cx, cy, bs, h_lo + u, dv);
     }
     if (more) {
-      make_tables(h_lo + u + 1, bs ^ 1);
+      make_tables(ln, h_lo + u + 1, bs ^ 1);
       dl_barrier();  // every wave is done with hT, gT of head u
       store_states(ln);
     }
@@ -376,9 +376,9 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
 
   if (nh > 0) {
     load_states(lane, h_lo);
-    load_dt(h_lo);
+    load_dt(lane, h_lo);
     issue_xy(lane, h_lo, xs0, ys0);
-    make_tables(h_lo, 0);
+    make_tables(lane, h_lo, 0);
     store_states(lane);
   }
   for (int u = 0; u < nh; u += 2) {
