@@ -695,6 +695,22 @@ def test_backward_chunk_aligned_single_subset(dev):
     _check_bwd(inp, dev, 64, TOL["bf16"], "aligned bf16 one head subset", 95, D=np.ones(4, np.float32), xdt=True)
 
 
+def test_backward_repeatable(dev):
+    """The chunk-local bf16 backward gives the same gradients bit for bit on two
+    calls: dA is summed per head in chunk order (no atomics), dB and dC from the
+    head subsets' partial sums in subset order, the rest per element."""
+    from mamba_ssd_layer_amd.workloads import bf16_round
+    w = SMALL.with_(dtype="bf16", dstate=128, chunk_len=256, seqlen=2048, batch=2, nheads=8, ngroups=1)
+    inp = make_inputs(w, 97)
+    dy = bf16_round(np.random.default_rng(97).standard_normal(inp.x.shape).astype(np.float32))
+    log("[bwd] repeatable: two calls")
+    g1 = _grads_gpu(inp, dev, 256, dy, None, None, True, None, False)
+    g2 = _grads_gpu(inp, dev, 256, dy, None, None, True, None, False)
+    for k in g1:
+        if g1[k] is not None:
+            np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+
+
 def test_backward_chunk_aligned_uneven_subsets(dev):
     """64 chunks x 1 group x 2 column slices: the per-chunk dB, dC kernel splits
     the group's 5 heads into subsets of 2 and 3 whose fp32 partial sums are added."""
