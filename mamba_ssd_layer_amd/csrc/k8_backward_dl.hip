@@ -59,29 +59,45 @@ __device__ __forceinline__ floatx16_t prod(const uint4 (&a)[K / 16], const uint4
   return acc;
 }
 
+// DPP move within rows of 16 lanes, written only to the lanes of the banks
+// in BM (bank i: lanes 4i .. 4i + 3 of each row); the other lanes keep old.
+template <int CTRL, int BM>
+__device__ __forceinline__ float dpp_banks(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xf, BM, false));
+}
+
 // Sum of v[r] over the 32 lanes of each lane half: returns the sum for
 // r = 8 b4 + 4 b3 + 2 b2 + b1 (bits of lr), the same in lanes lr and lr ^ 1.
+// Each level halves the values a lane holds: it keeps the half its bit
+// selects and adds its partner's copy of that half.  No level goes through
+// LDS: lane distance 16 by v_permlane16_swap (it exchanges the odd 16-lane row
+// of its first operand with the even row of its second, so after exchanging
+// (v[k], v[8 + k]) the two results add up to the pair's v[k] in the lower row
+// and its v[8 + k] in the upper), distance 8 by a row rotation, distance 4 by
+// two bank-masked row shifts, distances 2 and 1 by quad permutations.
 __device__ __forceinline__ float lane_col_sums(const float (&v)[16], int lr) {
   float v8[8], v4[4], v2[2];
-  const bool b4 = lr & 16, b3 = lr & 8, b2 = lr & 4, b1 = lr & 2;
+  const bool b3 = lr & 8, b2 = lr & 4, b1 = lr & 2;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float keep = b4 ? v[8 + k] : v[k], send = b4 ? v[k] : v[8 + k];
-    v8[k] = keep + __shfl_xor(send, 16);
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]), __float_as_uint(v[8 + k]), false, false);
+    v8[k] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float keep = b3 ? v8[4 + k] : v8[k], send = b3 ? v8[k] : v8[4 + k];
-    v4[k] = keep + __shfl_xor(send, 8);
+    v4[k] = keep + dpp_move0<0x128>(send);  // row_ror:8
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const float keep = b2 ? v4[2 + k] : v4[k], send = b2 ? v4[k] : v4[2 + k];
-    v2[k] = keep + __shfl_xor(send, 4);
+    // lanes 4..7 of every 8 read lane - 4 (row_shr:4), lanes 0..3 lane + 4 (row_shl:4)
+    const float recv = dpp_banks<0x104, 0x5>(dpp_banks<0x114, 0xA>(0.0f, send), send);
+    v2[k] = keep + recv;
   }
   const float keep = b1 ? v2[1] : v2[0], send = b1 ? v2[0] : v2[1];
-  float v1 = keep + __shfl_xor(send, 2);
-  return v1 + __shfl_xor(v1, 1);
+  const float v1 = keep + dpp_move0<0x4E>(send);  // quad_perm [2, 3, 0, 1]
+  return v1 + dpp_move0<0xB1>(v1);                // quad_perm [1, 0, 3, 2]
 }
 
 template <int Q, int N>
@@ -165,7 +181,8 @@ void bwd_dl_kernel(BwdProblem b) {
   const BwdChunk ch = bwd_chunk(b, k, Q);
   const int64_t CPS = ch.CPS, c = ch.c, t0 = ch.t0;
   const int g = h / (H / G);
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave choices in scalar registers
   const float Ah = b.A[h];
   const bool xdt = b.x_times_dt != 0;
   const int I = dl_tile<NI>(half, wid);
@@ -185,23 +202,32 @@ void bwd_dl_kernel(BwdProblem b) {
   // 64 q / VB .. of B_J (LDS slots 64 q + lane), the others rows of X_J after
   // them; lane L takes the vector that the swizzle puts in its slot.  Wave w
   // issues instructions w, w + 4, ... (a repeated one, when NB is not a
-  // multiple of 4, copies the same bytes again).
+  // multiple of 4, copies the same bytes again).  A lane's byte offset from the
+  // tile's first row is the same for every tile (computed once, 32-bit: the
+  // host bounds 32 token rows of x below 2^31 bytes); the tile's own offset is
+  // uniform.
   constexpr int VB = Cfg::VB, VX = Cfg::VX;
   auto slot = [&](int r) -> uint4* { return r == 0 ? ring0 : (r == 1 ? ring1 : ring2); };
+  uint32_t coff[Cfg::DPW];
+#pragma unroll
+  for (int u = 0; u < Cfg::DPW; ++u) {
+    const int q = (wid + 4 * u) % NB;
+    if (q < NBB) {
+      const int r = (64 * q + lane) / VB, c = lane % VB;
+      coff[u] = 2u * ((uint32_t)r * (uint32_t)bs + 8u * (uint32_t)(c ^ (swz_slot<VB>(r, 0) - r * VB)));
+    } else {
+      const int r = (64 * (q - NBB) + lane) / VX, c = lane % VX;
+      coff[u] = 2u * ((uint32_t)r * (uint32_t)xs + 8u * (uint32_t)(c ^ (swz_slot<VX>(r, 0) - r * VX)));
+    }
+  }
   auto issue_tile = [&](int J) {
     uint4* dst = slot(J % RB);
 #pragma unroll
     for (int u = 0; u < Cfg::DPW; ++u) {
       const int q = (wid + 4 * u) % NB;
-      const uint16_t* src;
-      if (q < NBB) {
-        const int r = (64 * q + lane) / VB, c = lane % VB;
-        src = Bb + (32 * J + r) * bs + 8 * (c ^ (swz_slot<VB>(r, 0) - r * VB));
-      } else {
-        const int r = (64 * (q - NBB) + lane) / VX, c = lane % VX;
-        src = xb + (32 * J + r) * xs + 8 * (c ^ (swz_slot<VX>(r, 0) - r * VX));
-      }
-      lds_copy16(src, dst + q * 64);
+      const char* tile = q < NBB ? reinterpret_cast<const char*>(Bb + 32 * J * bs)
+                                 : reinterpret_cast<const char*>(xb + 32 * J * xs);
+      lds_copy16(reinterpret_cast<const uint16_t*>(tile + coff[u]), dst + q * 64);
     }
   };
   // Hin or Gout (P rows of N, contiguous): instruction q copies slots 64 q ..
@@ -484,8 +510,8 @@ __global__ __launch_bounds__(256) void bwd_dA_sum_kernel(BwdProblem b, int64_t c
   if (threadIdx.x == 0) b.dA[h] = (float)(red[0] + red[1] + red[2] + red[3]);
 }
 
-bool backward_dl_supported(Dtype dt, int Q, int N) {
-  return dt == Dtype::BF16 && (Q == 64 || Q == 128 || Q == 256) &&
+bool backward_dl_supported(Dtype dt, int Q, int N, int64_t H) {
+  return dt == Dtype::BF16 && H > 0 && H <= ((int64_t)1 << 19) && (Q == 64 || Q == 128 || Q == 256) &&
          (N == 16 || N == 32 || N == 64 || N == 128 || N == 256) && !(Q == 256 && N == 256);
 }
 
@@ -511,7 +537,7 @@ static void launch_dl_q(const BwdProblem& b, int64_t chunks, hipStream_t s) {
 }
 
 hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s) {
-  if (!backward_dl_supported(b.dtype, b.Q, b.N) || b.total % b.Q != 0 || (b.cu == nullptr && b.seqlen % b.Q != 0))
+  if (!backward_dl_supported(b.dtype, b.Q, b.N, b.H) || b.total % b.Q != 0 || (b.cu == nullptr && b.seqlen % b.Q != 0))
     return hipErrorInvalidValue;
   const int64_t chunks = b.total / b.Q;
   if (chunks == 0) return hipSuccess;

@@ -661,12 +661,12 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
   // with the forward's): its passes run in bf16, and no fp32 recompute or
   // reversed pass is needed.
   int Qd = 0;
-  if (aligned_q > 0 && aligned_q == chunk_len && backward_dl_supported(p.dtype, aligned_q, dstate) &&
+  if (aligned_q > 0 && aligned_q == chunk_len && backward_dl_supported(p.dtype, aligned_q, dstate, nheads) &&
       config_supported(p.dtype, aligned_q, dstate))
     Qd = aligned_q;
   else if (cu_seqlens == nullptr && seqlen > 0)
     for (int q : {chunk_len, 256, 128, 64})
-      if (seqlen % q == 0 && backward_dl_supported(p.dtype, q, dstate) && config_supported(p.dtype, q, dstate)) {
+      if (seqlen % q == 0 && backward_dl_supported(p.dtype, q, dstate, nheads) && config_supported(p.dtype, q, dstate)) {
         Qd = q;
         break;
       }
@@ -835,21 +835,21 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
 // on the padded length, and the results are copied back.  The bound needs no
 // host read of cu_seqlens: T + S (Q - 1).  Used when that at most doubles the
 // tokens and the configuration is built.
-static int padded_bwd_chunk(const int32_t* cu_seqlens, int64_t nseqs, int64_t total_len, int32_t dstate,
-                            int32_t ngroups, int32_t chunk_len, ssd_dtype dtype) {
+static int padded_bwd_chunk(const int32_t* cu_seqlens, int64_t nseqs, int64_t total_len, int32_t nheads,
+                            int32_t dstate, int32_t ngroups, int32_t chunk_len, ssd_dtype dtype) {
   if (total_len <= 0 || nseqs <= 0 || dtype != SSD_DTYPE_BF16 || ngroups > kMaxBwdGroups) return 0;
   if (cu_seqlens == nullptr) {
     // batched: only when no built chunk length divides the sequence length
     if (total_len % nseqs != 0) return 0;
     const int64_t seqlen = total_len / nseqs;
     for (int q : {chunk_len, 256, 128, 64})
-      if (seqlen % q == 0 && backward_dl_supported(Dtype::BF16, q, dstate) && config_supported(Dtype::BF16, q, dstate))
+      if (seqlen % q == 0 && backward_dl_supported(Dtype::BF16, q, dstate, nheads) && config_supported(Dtype::BF16, q, dstate))
         return 0;
   }
   for (int q : {chunk_len, 256, 128, 64}) {
     if (q != 64 && q != 128 && q != 256) continue;
     const int64_t tp = (total_len + nseqs * (int64_t)(q - 1) + q - 1) / q * q;
-    if (nseqs * (int64_t)(q - 1) <= total_len && tp < 0x7fffffffLL && backward_dl_supported(Dtype::BF16, q, dstate) &&
+    if (nseqs * (int64_t)(q - 1) <= total_len && tp < 0x7fffffffLL && backward_dl_supported(Dtype::BF16, q, dstate, nheads) &&
         backward_dbdc_supported(Dtype::BF16, q, dstate) && config_supported(Dtype::BF16, q, dstate))
       return q;
   }
@@ -864,7 +864,7 @@ ssd_status ssd_chunked_bwd(const void* x, const float* dt, const float* A_head, 
                            const void* dy, const float* dfinal_state, void* dx, float* ddt,
                            float* dA, void* dB, void* dC, float* dD, float* dinitial_state,
                            void* stream) {
-  const int Qp = padded_bwd_chunk(cu_seqlens, nseqs, total_len, dstate, ngroups, chunk_len, dtype);
+  const int Qp = padded_bwd_chunk(cu_seqlens, nseqs, total_len, nheads, dstate, ngroups, chunk_len, dtype);
   if (Qp == 0)
     return bwd_impl(x, dt, A_head, B, C, cu_seqlens, nseqs, total_len, nheads, headdim, dstate, ngroups, chunk_len,
                     dtype, initial_state, D, x_times_dt, dy, dfinal_state, dx, ddt, dA, dB, dC, dD, dinitial_state,

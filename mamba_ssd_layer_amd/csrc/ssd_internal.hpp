@@ -240,7 +240,9 @@ hipError_t launch_selective_scan(const ScanProblem& p, hipStream_t s);
 hipError_t launch_backward_glue(const BwdProblem& b, int stage, hipStream_t s);
 // K8: chunk-local d(ell) -> d(dt), dA (BwdProblem::chunked_dl).
 hipError_t launch_backward_dl(const BwdProblem& b, hipStream_t s);
-bool backward_dl_supported(Dtype dt, int Q, int N);
+// H: the kernel's copies take 32-bit offsets within 32 token rows of x (at
+// most 2^19 heads of 64 channels).
+bool backward_dl_supported(Dtype dt, int Q, int N, int64_t H);
 // Sequences padded to whole chunks of Q for the chunk-local backward:
 // sequence s starts at cup[s] in the padded layout (cup has S + 2 entries;
 // [cup[S], cup[S + 1] = Tp) is one zero sequence up to the host's bound Tp).
