@@ -339,8 +339,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
   const TokSeq q = token_seq(b, t);
   const int64_t f = q.t0 + (q.L - 1 - (t - q.t0));
   // c_g = C_t . B_t per group: the weight of each token's own term, which the
-  // fp32 passes leave out of y and dx' (the chunk-local d(ell) path keeps it)
-  if (!b.chunked_dl) {
+  // fp32 passes leave out of y and dx'
+  {
     const int wid = threadIdx.x / 64, lane = threadIdx.x % 64;
     for (int g = wid; g < G; g += kBwThreads / 64) {
       float acc = 0.0f;
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
     const float dth = b.dt[t * H + h];
     const float sx = b.x_times_dt ? dth : 1.0f;
     const float dh = b.D != nullptr ? b.D[h] : 0.0f;
-    const float cg = b.chunked_dl ? 0.0f : cbs[h / hpg];
+    const float cg = cbs[h / hpg];
     const int64_t o = (t * H + h) * P + lane8 * 8;
     const int64_t orev = (f * H + h) * P + lane8 * 8;  // dx' comes reversed
     float xv[8], dyv[8], yv[8] = {}, dxs[8], dx[8];
@@ -368,20 +368,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
       unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.dy) + o + c * VEC),
                     *reinterpret_cast<float(*)[VEC]>(dyv + c * VEC));
     }
-    if (b.chunked_dl) {
-      // dx' from the element-dtype reversed pass (own terms included)
 #pragma unroll
-      for (int c = 0; c < 8 / VEC; ++c)
-        unpack_vec<E>(*reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(b.y_x8) + orev + c * VEC),
-                      *reinterpret_cast<float(*)[VEC]>(dxs + c * VEC));
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float4 a = reinterpret_cast<const float4*>(b.y_f + o)[c];
-        const float4 d = reinterpret_cast<const float4*>(b.y_x + orev)[c];
-        yv[4 * c] = a.x; yv[4 * c + 1] = a.y; yv[4 * c + 2] = a.z; yv[4 * c + 3] = a.w;
-        dxs[4 * c] = d.x; dxs[4 * c + 1] = d.y; dxs[4 * c + 2] = d.z; dxs[4 * c + 3] = d.w;
-      }
+    for (int c = 0; c < 2; ++c) {
+      const float4 a = reinterpret_cast<const float4*>(b.y_f + o)[c];
+      const float4 d = reinterpret_cast<const float4*>(b.y_x + orev)[c];
+      yv[4 * c] = a.x; yv[4 * c + 1] = a.y; yv[4 * c + 2] = a.z; yv[4 * c + 3] = a.w;
+      dxs[4 * c] = d.x; dxs[4 * c + 1] = d.y; dxs[4 * c + 2] = d.z; dxs[4 * c + 3] = d.w;
     }
     // without the own terms in y and dx', d(Acs_t) = dy . y - x' . dx' has
     // nothing that cancels itself; dx' = dx's + c_g dy exactly
@@ -404,7 +396,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_token_kernel(BwdProblem b) {
       s_xdy += __shfl_xor(s_xdy, off);
     }
     if (lane8 == 0) {
-      if (!b.chunked_dl) b.qd[h * b.total + t] = s_dyy - sx * s_xdx;  // d(Acs_t)
+      b.qd[h * b.total + t] = s_dyy - sx * s_xdx;  // d(Acs_t)
       b.rd[h * b.total + t] = s_xdx + cg * s_xdy;  // x . dx' (full): d(dt) term of the dt-scaled input
       b.ud[h * b.total + t] = s_xdy;               // x . dy (dD term)
     }
@@ -687,7 +679,8 @@ static hipError_t launch_glue(const BwdProblem& b, int stage, hipStream_t s) {
     case 1:
       if (b.total > 0) {
         if (b.y_c != nullptr) hipLaunchKernelGGL((bwd_reduce_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
-        if (!b.tokens_in_dbdc) hipLaunchKernelGGL((bwd_token_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
+        // (the chunk-local d(ell) kernel forms the per-token terms itself)
+        if (!b.chunked_dl) hipLaunchKernelGGL((bwd_token_kernel<E>), dim3((unsigned)b.total), blk, 0, s, b);
       }
       if (b.chunked_dl) {
         if (b.total > 0) {

@@ -59,6 +59,12 @@ __device__ __forceinline__ floatx16_t prod(const uint4 (&a)[K / 16], const uint4
   return acc;
 }
 
+// c + a.lo b.lo + a.hi b.hi for two packed bf16 pairs (one instruction)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 // DPP move within rows of 16 lanes, written only to the lanes of the banks
 // in BM (bank i: lanes 4i .. 4i + 3 of each row); the other lanes keep old.
 template <int CTRL, int BM>
@@ -114,7 +120,7 @@ struct DlCfg {
   static constexpr int NBS = P * VB / 64;         // instructions of Hin (and of Gout)
   static constexpr int SPW = (NBS + 3) / 4;
   // loads a wave issues after the step sizes of the prologue
-  static constexpr int kAfterDt = N / 16 + P / 16 + DPW * (kRing < NI ? kRing : NI) + 2 * SPW;
+  static constexpr int kAfterDt = N / 16 + 2 * (P / 16) + DPW * (kRing < NI ? kRing : NI) + 2 * SPW;
   // loads a wave issues after j-side tile J and before the wait at the top of
   // step J (tiles J+1 .. of the prologue or of earlier steps, and Hin)
   static constexpr int after(int J) {
@@ -185,6 +191,7 @@ void bwd_dl_kernel(BwdProblem b) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave choices in scalar registers
   const float Ah = b.A[h];
   const bool xdt = b.x_times_dt != 0;
+  const float Dh = b.D != nullptr ? b.D[h] : 0.0f;
   const int I = dl_tile<NI>(half, wid);
 
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(b.x) + (t0 * H + h) * P;
@@ -240,10 +247,10 @@ void bwd_dl_kernel(BwdProblem b) {
     }
   };
 
-  // ---- prologue: the step sizes and the i-side rows of this wave's row tile
-  // (a wave without one loads tile 0 and leaves it unused), then tile 0, Gout,
-  // tiles 1 .. RB - 1 and Hin into LDS (in this order: the waits count them);
-  // chunk-local cumsum of dt A (wave 0)
+  // ---- prologue: the step sizes, the i-side rows of this wave's row tile and
+  // their dx' rows (a wave without one loads tile 0 and leaves it unused), then
+  // tile 0, Gout, tiles 1 .. RB - 1 and Hin into LDS (in this order: the waits
+  // count them); chunk-local cumsum of dt A (wave 0)
   constexpr int R = Q / 64;
   float dtl[R];
   if (wid == 0) {
@@ -252,12 +259,19 @@ void bwd_dl_kernel(BwdProblem b) {
   }
   const float dtnext = c + 1 < CPS ? b.dt[(t0 + Q) * H + h] : 0.0f;
   RowOps<N> io;
+  uint4 dxr[P / 16];  // dx' rows of the i-side tokens, as io.xd (then dx)
+  float sxd = 0.0f, sxy = 0.0f;  // partial x . dx' and x . dy of the lane's token
   {
     const int i = 32 * max(I, 0) + lr;
 #pragma unroll
     for (int st = 0; st < N / 16; ++st) io.bc[st] = *reinterpret_cast<const uint4*>(Cb + i * bs + 16 * st + 8 * lg);
 #pragma unroll
     for (int st = 0; st < P / 16; ++st) io.xd[st] = *reinterpret_cast<const uint4*>(dyb + i * xs + 16 * st + 8 * lg);
+    // dx' of token i comes from the reversed pass at the reversed position
+    const int64_t f = ch.s0 + (ch.L - 1 - (c * Q + i));
+    const uint16_t* dxp = reinterpret_cast<const uint16_t*>(b.y_x8) + (f * H + h) * P + 8 * lg;
+#pragma unroll
+    for (int st = 0; st < P / 16; ++st) dxr[st] = *reinterpret_cast<const uint4*>(dxp + 16 * st);
   }
   issue_tile(0);
   issue_state(gout, Gs);
@@ -347,6 +361,37 @@ void bwd_dl_kernel(BwdProblem b) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) rowpart += w[r];
         colreg[J] = lane_col_sums(w, lr);
+        if (I == J) {
+          // per-token terms of the row tile (its x rows are tile J's here):
+          // dx = sx dx' + D dy (sx = dt with the dt-scaled input, else 1),
+          // x . dx' (a d(dt) term) and x . dy (the dD term); stored after the
+          // steps (a store would hold up the next step's wait for its tile:
+          // the wait counts stores too)
+#pragma unroll
+          for (int st = 0; st < P / 16; ++st) {
+            const uint32_t xw[4] = {jo.xd[st].x, jo.xd[st].y, jo.xd[st].z, jo.xd[st].w};
+            const uint32_t yw[4] = {io.xd[st].x, io.xd[st].y, io.xd[st].z, io.xd[st].w};
+            const uint32_t dw[4] = {dxr[st].x, dxr[st].y, dxr[st].z, dxr[st].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sxd = dot2_bf16(xw[e], dw[e], sxd);
+              sxy = dot2_bf16(xw[e], yw[e], sxy);
+            }
+          }
+          if (xdt || Dh != 0.0f) {  // else dx = dx' as it is
+            const float sx = xdt ? dts[i_l] : 1.0f;
+#pragma unroll
+            for (int st = 0; st < P / 16; ++st) {
+              const uint32_t yw[4] = {io.xd[st].x, io.xd[st].y, io.xd[st].z, io.xd[st].w};
+              const uint32_t dw[4] = {dxr[st].x, dxr[st].y, dxr[st].z, dxr[st].w};
+              uint32_t ow[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                ow[e] = pack_bf16x2(sx * bf16_lo(dw[e]) + Dh * bf16_lo(yw[e]), sx * bf16_hi(dw[e]) + Dh * bf16_hi(yw[e]));
+              dxr[st] = make_uint4(ow[0], ow[1], ow[2], ow[3]);  // dx' in, dx out
+            }
+          }
+        }
       }
       if (wid == dw) {
         // dterm_j = exp(Lam - Acs_j) x'_j . (Gout B_j): A = Gout rows p, B = B_J
@@ -422,6 +467,18 @@ void bwd_dl_kernel(BwdProblem b) {
     if (lane == 0) red[wid] = kpart;
     __syncthreads();
     if (tid == 0) b.dl_kc[k * H + h] = anext * __expf(lam) * (red[0] + red[1] + red[2] + red[3]);
+  }
+  // ---- the row tile's per-token terms, stored last: no later wait or barrier
+  // of this workgroup then waits for these stores
+  if (I >= 0) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(b.dx) + ((t0 + i_l) * H + h) * P + 8 * lg;
+#pragma unroll
+    for (int st = 0; st < P / 16; ++st) *reinterpret_cast<uint4*>(dst + 16 * st) = dxr[st];
+    const float sd = sxd + __shfl_xor(sxd, 32), sy = sxy + __shfl_xor(sxy, 32);
+    if (lg == 0) {
+      b.rd[(int64_t)h * b.total + t0 + i_l] = sd;
+      b.ud[(int64_t)h * b.total + t0 + i_l] = sy;
+    }
   }
 }
 

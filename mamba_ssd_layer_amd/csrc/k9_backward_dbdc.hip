@@ -301,51 +301,6 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
 #pragma unroll
       for (int st = 0; st < 4; ++st) accB[nt] = mfma32x32x16(a[st], ldv(gT, 4096 * nt + fo[st]), accB[nt]);
   };
-  // Per-token terms of head h for the wave's row tile (the column slice
-  // ns = wid % nsplit takes them): dx = sx dx' + D dy (sx = dt with the
-  // dt-scaled input, else 1; dx' from the reversed pass, read at the reversed
-  // position), x . dx' (a d(dt) term) and x . dy (the dD term).  The lane holds
-  // token 32 wid + lr, vectors 2 st + lg of its x, dy and dx' rows.
-  const bool tok_wave = b.tokens_in_dbdc && (wid % nsplit) == ns;
-  auto load_dxp = [&](int ln, int h, uint4 (&dv)[4]) {
-    const int lr = ln & 31, lg = ln >> 5;
-    const int64_t f = ch.s0 + (ch.L - 1 - (c * Q + 32 * wid + lr));  // reversed position in the sequence
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(b.y_x8) + (f * H + h) * P + 8 * lg;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) dv[st] = *reinterpret_cast<const uint4*>(src + 16 * st);
-  };
-  auto head_tokens = [&](int ln, const int (&fo)[4], const uint4* xb, const uint4* yb, int bs, int h,
-                         const uint4 (&dv)[4]) {
-    const int lr = ln & 31, lg = ln >> 5;
-    const int i = 32 * wid + lr;
-    const float sx = xdt ? dts[bs][i] : 1.0f;
-    const float dh = b.D != nullptr ? b.D[h] : 0.0f;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(b.dx) + ((t0 + i) * H + h) * P + 8 * lg;
-    float sxd = 0.0f, sxy = 0.0f;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const uint4 xv = ldv(xb, 4096 * wid + fo[st]), yv = ldv(yb, 4096 * wid + fo[st]);
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, yw[4] = {yv.x, yv.y, yv.z, yv.w};
-      const uint32_t dw[4] = {dv[st].x, dv[st].y, dv[st].z, dv[st].w};
-      uint32_t ow[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x0 = bf16_lo(xw[k]), x1 = bf16_hi(xw[k]);
-        const float y0 = bf16_lo(yw[k]), y1 = bf16_hi(yw[k]);
-        const float d0 = bf16_lo(dw[k]), d1 = bf16_hi(dw[k]);
-        sxd += x0 * d0 + x1 * d1;
-        sxy += x0 * y0 + x1 * y1;
-        ow[k] = pack_bf16x2(sx * d0 + dh * y0, sx * d1 + dh * y1);
-      }
-      *reinterpret_cast<uint4*>(dst + 16 * st) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-    }
-    sxd += __shfl_xor(sxd, 32);
-    sxy += __shfl_xor(sxy, 32);
-    if (lg == 0) {
-      b.rd[(int64_t)h * b.total + t0 + i] = sxd;
-      b.ud[(int64_t)h * b.total + t0 + i] = sxy;
-    }
-  };
   // one head: its copies were issued one head earlier into (cx, cy); the next
   // head's go into (nx, ny)
   auto step = [&](int u, const uint4* cx, const uint4* cy, int bs, uint4* nx, uint4* ny) {
@@ -362,11 +317,6 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
     operand_offsets(ln, fo);
     head_tiles(ln, fo, cx, cy, bs);
     head_states(ln, fo, cx, cy, bs);
-    if (tok_wave) {
-      uint4 dv[4];
-      load_dxp(ln, h_lo + u, dv);
-      head_tokens(ln, fo, cx, cy, bs, h_lo + u, dv);
-    }
     if (more) {
       make_tables(ln, h_lo + u + 1, bs ^ 1);
       dl_barrier();  // every wave is done with hT, gT of head u

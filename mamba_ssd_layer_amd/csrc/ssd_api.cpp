@@ -767,7 +767,6 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
   b.nseq = nseqs; b.seqlen = seqlen; b.total = total_len;
   b.H = H; b.P = P; b.N = N; b.G = G; b.NK = NK; b.dtype = p.dtype;
   b.chunked_dl = cdl; b.Q = Qd;
-  b.tokens_in_dbdc = dbdc;
   if (!bf16) {
     b.x32 = static_cast<const float*>(x);
     b.B32 = static_cast<const float*>(B);

@@ -120,7 +120,6 @@ struct BwdProblem {
   // chunk-local d(ell) (bf16, every sequence a whole number of chunks of Q): the
   // forward's and the reversed pass's passed states as those passes store them
   bool chunked_dl;
-  bool tokens_in_dbdc;         // dx and the per-token terms come from the per-chunk dB/dC kernel
   int Q;
   const void* hin_e; const void* gin_e;   // (K, H, P, N) element dtype
   const void* y_x8;            // reversed pass in the element dtype: dx' (own terms in), reversed order
