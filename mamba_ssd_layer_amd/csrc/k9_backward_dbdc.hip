@@ -132,13 +132,16 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   // vector the swizzle puts in its slot, (L % 8) ^ ((4 q + L / 16) % 8), which
   // depends on q only through its parity: the per-lane offsets of even and odd
   // q are computed once.  Wave w issues q = w, w + NI, ...: x in the first half.
-  auto issue_xy = [&](int ln, int h, uint4* xb, uint4* yb) {
+  // copies u0 .. u1 - 1 of this wave's DPW (the step spreads them over its
+  // tiles: a burst of them stalls the wave at issue)
+  auto issue_xy = [&](int ln, int h, uint4* xb, uint4* yb, int u0 = 0, int u1 = Cfg::DPW) {
     int xoff[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par)
       xoff[par] = (ln / 8) * (int)xs + h * P + 8 * ((ln % 8) ^ ((4 * par + ln / 16) % 8));
 #pragma unroll
     for (int u = 0; u < Cfg::DPW; ++u) {
+      if (u < u0 || u >= u1) continue;
       const bool isx = u < Cfg::DPW / 2;
       const int q = wid + NI * (isx ? u : u - Cfg::DPW / 2);
       const uint16_t* row = (isx ? xg : yg) + (int64_t)(8 * q) * xs;  // uniform
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
   // exp(Acs_t - Acs_j) (x dt_j) factors into exp(Acs_t - a_J) <= 1, one per lane,
   // and fd_j (a_J = Acs at the end of tile J); a diagonal tile is masked
   // (j <= t) and decayed element by element.
-  auto head_tiles = [&](int ln, const int (&fo)[4], const uint4* xb, const uint4* yb, int bs) {
+  auto head_tiles = [&](int ln, const int (&fo)[4], const uint4* xb, const uint4* yb, int bs, auto after_tile) {
     const int lr = ln & 31, lg = ln >> 5;
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
@@ -275,6 +278,7 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
           }
         }
       }
+      after_tile(u);
       // one tile's operands at a time: hoisting every tile's loads would take
       // the registers that hold Msum
       __builtin_amdgcn_sched_barrier(0);
@@ -311,11 +315,14 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
     if (more) {
       load_states(ln, h_lo + u + 1);
       load_dt(ln, h_lo + u + 1);
-      issue_xy(ln, h_lo + u + 1, nx, ny);
     }
     int fo[4];
     operand_offsets(ln, fo);
-    head_tiles(ln, fo, cx, cy, bs);
+    // the next head's copies, CPT after each tile
+    constexpr int CPT = (Cfg::DPW + MT - 1) / MT;
+    head_tiles(ln, fo, cx, cy, bs, [&](int t) {
+      if (more) issue_xy(ln, h_lo + u + 1, nx, ny, t * CPT, (t + 1) * CPT);
+    });
     head_states(ln, fo, cx, cy, bs);
     if (more) {
       make_tables(ln, h_lo + u + 1, bs ^ 1);
