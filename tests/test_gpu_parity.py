@@ -706,17 +706,25 @@ def test_backward_all_options(dev, dtype):
 @pytest.mark.parametrize("dtype,N,Q,L,opts", [("f32", 64, 64, 512, False), ("bf16", 128, 256, 512, False),
                                                 ("bf16", 256, 128, 384, False), ("bf16", 16, 64, 256, False),
                                                 ("f32", 64, 128, 512, True), ("bf16", 128, 256, 768, True),
-                                                ("bf16", 64, 64, 320, True)])
+                                                ("bf16", 64, 64, 320, True), ("bf16", 128, 256, 512, "D"),
+                                                ("bf16", 128, 256, 512, "xdt")])
 def test_backward_chunk_aligned(dev, dtype, N, Q, L, opts):
     """Sequences a whole number of chunks long (the chunk-local d(ell) path),
-    plain and with every option."""
+    plain, with every option, and with the skip term or the dt-scaled input
+    alone (dx = dx' unchanged needs neither; dx = dt dx' + D dy otherwise)."""
     w = SMALL.with_(dtype=dtype, dstate=N, chunk_len=Q, seqlen=L, batch=2, nheads=8, ngroups=2)
     seed = 90 + N + L
     inp = make_inputs(w, seed)
     kw = {}
-    if opts:
+    if opts is True:
         kw = dict(h0=initial_states(2, 8, 64, N, seed=seed), dfinal=initial_states(2, 8, 64, N, seed=seed + 1),
                   D=np.random.default_rng(seed).standard_normal(8).astype(np.float32), xdt=True)
+    elif opts == "D":
+        D = np.random.default_rng(seed).standard_normal(8).astype(np.float32)
+        D[3] = 0.0  # a head whose skip term is zero: dx = dx' there
+        kw = dict(D=D)
+    elif opts == "xdt":
+        kw = dict(xdt=True)
     _check_bwd(inp, dev, Q, TOL[dtype], f"aligned {dtype} N={N} Q={Q} L={L} opts={opts}", seed, **kw)
 
 
