@@ -299,9 +299,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_reduce_kernel(BwdProblem b) {
   }
 }
 
-// Per (token, head): dx = dx' (times dt with the dt-scaled input) + D dy, and
+// bwd_token_kernel (below; the paths other than the chunk-local d(ell) one,
+// whose kernel forms these itself): per (token, head) dx = dx' (with the
+// token's own term added back, times dt with the dt-scaled input) + D dy, and
 // the per-token terms of d(ell), d(dt), dD, stored head-major (H, Ttot).
 // Eight lanes share one head row (8 values each); one workgroup per token.
+
 // Block-wide sum of v over the 256 threads (result valid in every thread).
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
