@@ -21,8 +21,9 @@
 // processed in blocks of 64: the wave loads the block's Delta and x (channel-
 // major layout, one 64-token row each) and reads token s's values from lane s;
 // B_t and C_t are loaded per token as 64 consecutive entries.  Each lane keeps
-// its C_t h_t for the 64 tokens in registers; a butterfly of 63 shuffles then
-// sums them over the lanes, leaving token s's partial sum in lane s, and the
+// its C_t h_t for the 64 tokens in registers; a butterfly of 63 lane
+// exchanges (none through LDS) then sums them over the lanes, leaving token s's
+// partial sum in lane s, and the
 // waves of one channel (N / 64 of them, in one workgroup) add theirs in LDS.
 // Layouts: x, Delta, y (b, D, T) channel-major; A (D, N); B, C (b, T, N);
 // final state (b, D, N) fp32.
@@ -46,15 +47,37 @@ __device__ __forceinline__ void st_y(void* p, int64_t i, float v) {
 }
 
 // One butterfly stage: lanes with bit O set keep the upper half of v[0, 2 O)
-// and send the lower half to their partner, which does the opposite.
+// and add their partner's copy of it; the partner does the opposite.  No
+// stage goes through LDS.  Distances 32 and 16 exchange whole 32- and 16-lane
+// rows (v_permlane32_swap / v_permlane16_swap swap the upper row of their
+// first operand with the lower row of their second, so after exchanging
+// (v[i], v[O + i]) the two results add up to the pair's v[i] in the lower row
+// and its v[O + i] in the upper); 8 is a row rotation, 4 two bank-masked row
+// shifts, 2 and 1 quad permutations.  Every stage adds the same two values as
+// a lane exchange would, so the sums do not depend on how they are moved.
+template <int CTRL, int BM>
+__device__ __forceinline__ float scan_dpp(float old, float v) {  // lanes of the banks in BM; the others keep old
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xf, BM, false));
+}
 template <int O>
 __device__ __forceinline__ void sum_stage(float (&v)[kScanBlock], int lane) {
   const bool up = lane & O;
 #pragma unroll
   for (int i = 0; i < O; ++i) {
-    const float keep = up ? v[O + i] : v[i];
-    const float send = up ? v[i] : v[O + i];
-    v[i] = keep + __shfl_xor(send, O);
+    if constexpr (O == 32 || O == 16) {
+      const auto sw = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[O + i]), false, false)
+                              : __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[O + i]), false, false);
+      v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    } else {
+      const float keep = up ? v[O + i] : v[i];
+      const float send = up ? v[i] : v[O + i];
+      float recv;
+      if constexpr (O == 8) recv = scan_dpp<0x128, 0xf>(0.0f, send);  // row_ror:8
+      else if constexpr (O == 4) recv = scan_dpp<0x104, 0x5>(scan_dpp<0x114, 0xA>(0.0f, send), send);  // shr:4 / shl:4
+      else if constexpr (O == 2) recv = scan_dpp<0x4E, 0xf>(0.0f, send);  // quad_perm [2, 3, 0, 1]
+      else recv = scan_dpp<0xB1, 0xf>(0.0f, send);                         // quad_perm [1, 0, 3, 2]
+      v[i] = keep + recv;
+    }
   }
 }
 
