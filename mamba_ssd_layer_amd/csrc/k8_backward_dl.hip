@@ -20,8 +20,10 @@
 // every sequence is a whole number of chunks (then the reversed pass's chunks
 // coincide with the forward's).
 //
-// Kernel 1, per (chunk, head, row-tile set): the row and column sums of W
-// and the passed-state terms.  Each of the 4 waves owns one row tile I of 32
+// Kernel 1, per (chunk, head, row-tile set): the row and column sums of W,
+// the passed-state terms, and the per-token terms of the row tiles' tokens
+// (dx = sx dx' + D dy, x . dx', x . dy: sx = dt with the dt-scaled input, else
+// 1; dx' from the reversed pass).  Each of the 4 waves owns one row tile I of 32
 // tokens and keeps its i-side rows (C_I, dY_I) in registers as MFMA operands
 // (lane: one token row, 8 consecutive k).  The j-side tiles (B_J, X_J) and the
 // passed states Hin, Gout are copied straight from memory into LDS by the

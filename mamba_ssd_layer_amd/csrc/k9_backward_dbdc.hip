@@ -18,8 +18,9 @@
 // Workgroup: one chunk, one group, 64 columns of N and a subset of the group's
 // heads; one wave per 32-token tile of the chunk (Q / 32 waves).  Per head, x
 // and dy of the chunk are copied into LDS by the load-to-LDS instruction
-// (double buffered: the next head's copies run during this head's products;
-// rows XOR-swizzled so that operand reads hit distinct banks).  Each wave
+// (double buffered: the next head's copies, issued a few at a time between
+// this head's tiles, run during its products; rows XOR-swizzled so that
+// operand reads hit distinct banks).  Each wave
 // forms its share of the 32x32 tiles of M_h on the matrix cores (fp32) and adds
 // them, decayed, to Msum in registers; then the state terms of its own tile,
 // as products with the 64-column slices of Hin_h and Gout_h, which are loaded
