@@ -431,6 +431,20 @@ void bwd_dl_kernel(BwdProblem b) {
   __syncthreads();
   if (I >= 0) {
     const float rp = rowpart + __shfl_xor(rowpart, 32);
+    // dy of token i at p = 16 st + 8 h + 4 lg .. + 3 for both halves h, from the
+    // dy rows in registers (io.xd[st] of lane half h holds p = 16 st + 8 h ..):
+    // v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+    // the lower 32 of its second, so after exchanging (words 0 and 2), (words 1
+    // and 3) of io.xd[st] the first results hold every lane's words for h = 0
+    // and the second for h = 1
+    uint2 dyh[P / 16][2];
+#pragma unroll
+    for (int st = 0; st < P / 16; ++st) {
+      const auto s02 = __builtin_amdgcn_permlane32_swap(io.xd[st].x, io.xd[st].z, false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(io.xd[st].y, io.xd[st].w, false, false);
+      dyh[st][0] = make_uint2(s02[0], s13[0]);
+      dyh[st][1] = make_uint2(s02[1], s13[1]);
+    }
     float yt = 0.0f;
 #pragma unroll
     for (int pt = 0; pt < P / 32; ++pt) {
@@ -441,7 +455,7 @@ void bwd_dl_kernel(BwdProblem b) {
       const floatx16_t hy = prod<N>(ha, io.bc);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const uint2 dv = *reinterpret_cast<const uint2*>(dyb + i_l * xs + 32 * pt + 8 * a + 4 * lg);
+        const uint2 dv = dyh[2 * pt + a / 2][a % 2];  // p = 32 pt + 8 a + 4 lg .. + 3
         yt += hy[4 * a] * bf16_lo(dv.x) + hy[4 * a + 1] * bf16_hi(dv.x) + hy[4 * a + 2] * bf16_lo(dv.y) +
               hy[4 * a + 3] * bf16_hi(dv.y);
       }
