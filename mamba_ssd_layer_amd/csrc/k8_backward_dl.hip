@@ -252,12 +252,18 @@ void bwd_dl_kernel(BwdProblem b) {
   // ---- prologue: the step sizes, the i-side rows of this wave's row tile and
   // their dx' rows (a wave without one loads tile 0 and leaves it unused), then
   // tile 0, Gout, tiles 1 .. RB - 1 and Hin into LDS (in this order: the waits
-  // count them); chunk-local cumsum of dt A (wave 0)
+  // count them).  The chunk-local cumsums of dt A come from the forward's
+  // chunk-state kernel (contiguous per (chunk, head)); the step sizes (one
+  // cache line per token) only with the dt-scaled input (wave 0)
   constexpr int R = Q / 64;
-  float dtl[R];
+  float acl[R], dtl[R];
   if (wid == 0) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) dtl[i] = b.dt[(t0 + lane * R + i) * H + h];
+    for (int i = 0; i < R; ++i) acl[i] = b.acs_f[(k * H + h) * Q + lane * R + i];
+    if (xdt) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) dtl[i] = b.dt[(t0 + lane * R + i) * H + h];
+    }
   }
   const float dtnext = c + 1 < CPS ? b.dt[(t0 + Q) * H + h] : 0.0f;
   RowOps<N> io;
@@ -280,19 +286,13 @@ void bwd_dl_kernel(BwdProblem b) {
 #pragma unroll
   for (int J = 1; J < RB && J < NI; ++J) issue_tile(J);
   issue_state(hin, Hs);
-  wait_vm<Cfg::kAfterDt>();  // the step sizes (loaded first)
+  wait_vm<Cfg::kAfterDt>();  // the cumsums and step sizes (loaded first)
   if (wid == 0) {
-    float run[R];
-    float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      dts[lane * R + i] = dtl[i];
-      acc += dtl[i] * Ah;
-      run[i] = acc;
+      acs[lane * R + i] = acl[i];
+      if (xdt) dts[lane * R + i] = dtl[i];
     }
-    const float incl = wave_inclusive_sum(acc);
-#pragma unroll
-    for (int i = 0; i < R; ++i) acs[lane * R + i] = incl - acc + run[i];
   }
   dl_barrier();
   for (int i = tid; i < Q; i += kDlThreads)

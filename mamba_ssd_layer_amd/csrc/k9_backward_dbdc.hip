@@ -178,39 +178,38 @@ __global__ __launch_bounds__(DbdcCfg<Q>::THREADS) void bwd_dbdc_kernel(BwdProble
       }
     }
   };
-  // step sizes of head h (wave 0), and the tables built from them
-  float dtl[R];
+  // the cumsums (and step sizes) of head h in wave 0, and the tables built from them
+  float acl[R], dtl[R];
   float dtn = 0.0f;
+  // head h's chunk-local cumsums of dt A (from the forward's chunk-state
+  // kernel, contiguous) and, with the dt-scaled input, its step sizes (one
+  // cache line per token): wave 0, R tokens per lane
   auto load_dt = [&](int ln, int h) {
     if (wid == 0) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) dtl[i] = b.dt[(t0 + ln * R + i) * H + h];
+      for (int i = 0; i < R; ++i) acl[i] = b.acs_f[(k * H + h) * Q + ln * R + i];
+      if (xdt) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) dtl[i] = b.dt[(t0 + ln * R + i) * H + h];
+      }
       dtn = c + 1 < CPS ? b.dt[(t0 + Q) * H + h] : 0.0f;
     }
   };
   auto make_tables = [&](int ln, int h, int bs) {
     if (wid == 0) {
       const float Ah = b.A[h];
-      float run[R];
-      float acc = 0.0f;
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        acc += dtl[i] * Ah;
-        run[i] = acc;
+        acs[bs][ln * R + i] = acl[i];
+        if (xdt) dts[bs][ln * R + i] = dtl[i];
       }
-      const float incl = wave_inclusive_sum(acc);
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        acs[bs][ln * R + i] = incl - acc + run[i];
-        dts[bs][ln * R + i] = dtl[i];
-      }
-      const float lam = __shfl(incl, 63);
+      const float lam = __shfl(acl[R - 1], 63);
       const float anext = c + 1 < CPS ? __expf(dtn * Ah) : 1.0f;
       // the same wave reads back the tile ends it wrote
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const int j = ln * R + i;
-        const float aj = incl - acc + run[i];
+        const float aj = acl[i];
         const float dtf = xdt ? dtl[i] : 1.0f;
         fd[bs][j] = __expf(acs[bs][32 * (j / 32) + 31] - aj) * dtf;
         ec[bs][j] = __expf(aj);

@@ -260,6 +260,7 @@ struct DebugOut {
   float* hin = nullptr;
   bool states_only = false;  // stop after the state passing (no y)
   void* hin_buf = nullptr;   // keep the passed states here (element dtype, (kmax, H, P, N))
+  float* acs_buf = nullptr;  // keep the chunk-local cumsums here ((kmax, H, Q) fp32)
 };
 
 // ------------------------------------------------------------ workspace ----
@@ -334,6 +335,7 @@ static ssd_status run(const Problem& p, hipStream_t stream, const DebugOut* dbg,
     if (pe != hipSuccess) return map_err(pe);
   }
   if (dbg && dbg->hin_buf) ws.hin = dbg->hin_buf;
+  if (dbg && dbg->acs_buf) ws.acs = dbg->acs_buf;
   hipError_t e = hipSuccess;
   const size_t KH = (size_t)p.kmax * p.H;
   do {
@@ -725,6 +727,7 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
     b.y_x8 = take(cdl ? T * H * P * e : 0);
     b.hin_e = take(Kd * H * P * N * e);
     b.gin_e = take(Kd * H * P * N * e);
+    b.acs_f = reinterpret_cast<float*>(take(Kd * H * (size_t)Qd * 4));
     b.dl_v = reinterpret_cast<float*>(take(cdl ? T * H * 4 : 0));
     b.dl_cols = reinterpret_cast<float*>(take(cdl ? 2 * T * H * 4 : 0));
     b.dl_u = reinterpret_cast<float*>(take(cdl ? T * H * 4 : 0));
@@ -793,6 +796,7 @@ static ssd_status bwd_impl(const void* x, const float* dt, const float* A_head, 
                               kHeadDim, P, H, Q2, dtype, b.y_b, nullptr, b.dfb, nullptr, 0);
     DebugOut df, dxo;
     df.hin_buf = const_cast<void*>(b.hin_e);
+    df.acs_buf = const_cast<float*>(b.acs_f);  // read by the d(ell) and dB/dC kernels
     df.states_only = true;
     dxo.hin_buf = const_cast<void*>(b.gin_e);
     for (auto [q, d] : {std::pair<const Problem*, const DebugOut*>{&pf, &df}, {&px, &dxo}, {&pc, nullptr},

@@ -122,6 +122,7 @@ struct BwdProblem {
   bool chunked_dl;
   int Q;
   const void* hin_e; const void* gin_e;   // (K, H, P, N) element dtype
+  const float* acs_f;          // (K, H, Q) chunk-local cumsums of dt A, as the forward's chunk-state kernel forms them
   const void* y_x8;            // reversed pass in the element dtype: dx' (own terms in), reversed order
   float* dl_v;                 // (H, Ttot) row sums of W + yterm
   float* dl_cols;              // (2, H, Ttot) column sums of W, per workgroup of the chunk
