@@ -19,7 +19,8 @@
 // 64 entries); lane n carries h[n] through all T tokens (one exp per element,
 // the least any scan does; a chunk-parallel scan would need two).  Tokens are
 // processed in blocks of 64: the wave loads the block's Delta and x (channel-
-// major layout, one 64-token row each) and reads token s's values from lane s;
+// major layout, one 64-token row each) and puts (Delta, Delta x) in LDS, where
+// every lane reads token s's pair with one broadcast read;
 // B_t and C_t are loaded per token as 64 consecutive entries.  Each lane keeps
 // its C_t h_t for the 64 tokens in registers; a butterfly of 63 lane
 // exchanges (none through LDS) then sums them over the lanes, leaving token s's
@@ -97,6 +98,9 @@ __global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProble
   constexpr int NB = N / 64;               // waves per channel
   constexpr int CPB = kScanThreads / N;    // channels per workgroup
   __shared__ float ysum[CPB][NB][kScanBlock];
+  // per wave: the block's (Delta_t, Delta_t x_t), read by every lane as one
+  // broadcast LDS read per token (the vector ALU then does no lane broadcasts)
+  __shared__ float2 du_s[kScanThreads / 64][kScanBlock];
   const int wid = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int cl = wid / NB, nb = wid % NB;  // channel within the workgroup, entry block
   const int64_t chan = (int64_t)blockIdx.x * CPB + cl;  // (sequence, channel)
@@ -132,8 +136,10 @@ __global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProble
   const int64_t Tfull = T / kScanBlock * kScanBlock;
   for (int64_t t0 = 0; t0 < Tfull; t0 += kScanBlock) {
     // whole block: straight-line code; B and C one sub-block ahead
-    const float dl = drow[t0 + lane];
-    const float ul = dl * ld_elem<E>(p.x, xrow + t0 + lane);
+    {
+      const float dl = drow[t0 + lane];
+      du_s[wid][lane] = make_float2(dl, dl * ld_elem<E>(p.x, xrow + t0 + lane));
+    }
     float yp[kScanBlock];
     float bq[SB], cq[SB];
 #pragma unroll
@@ -154,7 +160,8 @@ __global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProble
 #pragma unroll
       for (int s = 0; s < SB; ++s) {
         const int k = sb * SB + s;
-        h = __builtin_amdgcn_exp2f(lane_val(dl, k) * a2) * h + lane_val(ul, k) * bq[s];
+        const float2 du = du_s[wid][k];  // (written above by this wave; LDS is in order per wave)
+        h = __builtin_amdgcn_exp2f(du.x * a2) * h + du.y * bq[s];
         yp[k] = cq[s] * h;
       }
       if (sb + 1 < kScanBlock / SB) {
