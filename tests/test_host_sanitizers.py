@@ -8,7 +8,6 @@
   tests/sanitize/host_driver.cpp; no kernel is launched.
 Each driver exits 0 when its checks hold; a sanitizer report fails it.
 """
-import glob
 import os
 import shutil
 import subprocess
@@ -40,10 +39,17 @@ def test_oracle_under_asan_ubsan(tmp_path):
                     reason="hipcc not available")
 def test_host_logic_under_asan_ubsan(tmp_path):
     from mamba_ssd_layer_amd import build as b
-    objs = [o for o in glob.glob(os.path.join(b.BUILD, "*.o")) if not os.path.basename(o).startswith("ssd_api")]
+
+    def kernel_objects():
+        # the objects build.py makes, one per kernel source (not any other file
+        # a build with --asm leaves in the folder)
+        names = [os.path.basename(src) + ".o" for src in b.sources() if not os.path.basename(src).startswith("ssd_api")]
+        return [os.path.join(b.BUILD, n) for n in names if os.path.exists(os.path.join(b.BUILD, n))]
+
+    objs = kernel_objects()
     if len(objs) < len(b.sources()) - 1:
         b.build()
-        objs = [o for o in glob.glob(os.path.join(b.BUILD, "*.o")) if not os.path.basename(o).startswith("ssd_api")]
+        objs = kernel_objects()
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
     flags = ["-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={b.ARCH}", "-Xclang", "-target-feature",
