@@ -3,6 +3,7 @@
     python -m mamba_ssd_layer_amd.prof_summary kernels <trace_dir> [--first N] [--last N]
     python -m mamba_ssd_layer_amd.prof_summary traffic --fetch D --write D \
         --cal-fetch D --cal-write D --kernel chunk_output --workload long_T16k [--command C ...]
+    python -m mamba_ssd_layer_amd.prof_summary busy <sq_counter_dir> --symbol S [--symbol S ...]
 
 `kernels` prints a markdown table of the per-kernel durations (run_kernel_stats.csv)
 and the gaps between consecutive SSD kernels of one forward (run_kernel_trace.csv).
@@ -10,6 +11,8 @@ and the gaps between consecutive SSD kernels of one forward (run_kernel_trace.cs
 FETCH_SIZE and WRITE_SIZE of one kernel per dispatch, each scaled by what the same
 counter reads for a plain device copy of known size (bench.py --calibrate-copy),
 stamped with a hash of the kernel's sources so that a stale figure is not used.
+`busy` prints, for any kernels named, the matrix-core busy fraction, the share of
+wave time spent waiting to issue and the LDS instructions, from one SQ pass.
 `counters` prints the JSON that bench.py reads for the roofline's `mfma_util` and
 `dram_bytes`: from one pass of matrix-core counters (SQ_VALU_MFMA_BUSY_CYCLES,
 SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) and one of the L2's memory-side
@@ -193,6 +196,27 @@ def traffic(fetch: str, write: str, cal_fetch: str, cal_write: str, kernel: str,
     }
 
 
+def busy_table(mfma: str, symbols: list[str]) -> str:
+    """Per kernel (a substring of its name), from one SQ counter pass: matrix-core
+    busy fraction (as in counters()), the fraction of wave time spent waiting
+    to issue an instruction (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, both in wave
+    cycles), and LDS instructions per launch."""
+    out = ["| kernel | MFMA util | executed MFMA GFLOP | wave time waiting to issue | LDS instructions (M) |",
+           "|---|---|---|---|---|"]
+    for sym in symbols:
+        busy = _counter_per_dispatch(mfma, sym, "SQ_VALU_MFMA_BUSY_CYCLES")
+        mops = _counter_per_dispatch(mfma, sym, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        active = _counter_per_dispatch(mfma, sym, "GRBM_GUI_ACTIVE", "max") / XCDS
+        wait = _counter_per_dispatch(mfma, sym, "SQ_WAIT_INST_ANY")
+        wave = _counter_per_dispatch(mfma, sym, "SQ_WAVE_CYCLES")
+        lds = _counter_per_dispatch(mfma, sym, "SQ_INSTS_LDS")
+        name = next(r["Kernel_Name"] for r in csv.DictReader(open(os.path.join(mfma, "run_counter_collection.csv")))
+                    if sym in r["Kernel_Name"])
+        out.append(f"| {_short(name)} | {busy / (active * SIMDS):.3f} | {mops * 512.0 / 1e9:.2f} | "
+                   f"{wait / wave:.2f} | {lds / 1e6:.2f} |")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -200,6 +224,9 @@ def main(argv=None):
     k.add_argument("trace_dir")
     k.add_argument("--first", type=int, default=0, help="gaps over the first N SSD dispatches only")
     k.add_argument("--last", type=int, default=0, help="also average the last N dispatches of each kernel")
+    bz = sub.add_parser("busy")
+    bz.add_argument("mfma_dir")
+    bz.add_argument("--symbol", action="append", required=True, help="a substring of a kernel name (repeatable)")
     t = sub.add_parser("traffic")
     for a in ("fetch", "write", "cal_fetch", "cal_write"):
         t.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
@@ -217,6 +244,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "kernels":
         print(kernels_table(a.trace_dir, a.first, a.last))
+    elif a.cmd == "busy":
+        print(busy_table(a.mfma_dir, a.symbol))
     elif a.cmd == "counters":
         json.dump(counters(a.mfma, a.dram, a.cal_dram, a.kernel, a.workload, a.copy_mib, a.command),
                   sys.stdout, indent=1)
