@@ -17,23 +17,32 @@
 // decay, so each (token, channel, entry) costs one exp on the vector ALU and
 // nothing maps to the matrix cores.  One wave per (sequence, channel, block of
 // 64 entries); lane n carries h[n] through all T tokens (one exp per element,
-// the least any scan does; a chunk-parallel scan would need two).  Tokens are
+// the least any scan does; a chunk-parallel scan would need two).  A
+// workgroup of 16 waves holds 1024 / N channels of one sequence, which share
+// B and C: each sub-block of 4096 / N tokens of them is loaded once by the
+// workgroup (16-byte vectors), converted to fp32 and stored in LDS as
+// (B_t[n], C_t[n]) pairs, double buffered (the next sub-block's loads in
+// flight during this one's products), and each lane reads its pair with one
+// 8-byte LDS read: no global load and no conversion per element.  Tokens are
 // processed in blocks of 64: the wave loads the block's Delta and x (channel-
 // major layout, one 64-token row each) and puts (Delta, Delta x) in LDS, where
-// every lane reads token s's pair with one broadcast read;
-// B_t and C_t are loaded per token as 64 consecutive entries.  Each lane keeps
+// every lane reads token s's pair with one broadcast read.  Each lane keeps
 // its C_t h_t for the 64 tokens in registers; a butterfly of 63 lane
 // exchanges (none through LDS) then sums them over the lanes, leaving token s's
-// partial sum in lane s, and the
-// waves of one channel (N / 64 of them, in one workgroup) add theirs in LDS.
+// partial sum in lane s, and the waves of one channel (N / 64 of them) add
+// theirs in LDS.  Per element that leaves Delta A, the exp, the input term,
+// the state update and C h on the vector ALU, 2.5 butterfly operations, and
+// 8 bytes of LDS reads (a transposed sum through LDS instead of the butterfly,
+// or the pairs kept as bf16, each measured slower: the kernel is bound by both).
 // Layouts: x, Delta, y (b, D, T) channel-major; A (D, N); B, C (b, T, N);
 // final state (b, D, N) fp32.
 #include "ssd_device.hpp"
 
 namespace ssd {
 
-constexpr int kScanThreads = 256;
-constexpr int kScanBlock = 64;  // tokens per block
+constexpr int kScanThreads = 1024;  // 16 waves
+constexpr int kScanBlock = 64;     // tokens per block
+constexpr int kScanStaged = 4096;  // (token, entry) pairs of B and C staged at once
 
 template <class E>
 __device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
@@ -93,28 +102,86 @@ __device__ __forceinline__ float wave_sum_transpose(float (&v)[kScanBlock], int 
   return v[0];
 }
 
-template <class E, int N>
-__global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProblem p) {
+// Staged B and C: the workgroup's channels share one batch, so each sub-block of
+// SB tokens is loaded once, converted to fp32 and stored as (B_t[n], C_t[n])
+// pairs in LDS; every lane then reads its pair with one 8-byte LDS read.  Each
+// thread stages VEC consecutive entries of one token (a 16-byte vector of B
+// and one of C when kVec, else element loads), written as two pairs per
+// 16-byte LDS store.  The loads keep raw bits (converted at the store, so a
+// load in flight is not waited for before the products it overlaps); tokens
+// at or past T stage zeros.
+__device__ __forceinline__ uint32_t raw_bits(uint16_t v) { return v; }
+__device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v); }
+
+template <class E, int N, bool kVec>
+struct ScanStage {
+  static constexpr int VEC = 16 / E::kBytes;     // entries per thread
+  static constexpr int SB = kScanStaged / N;     // tokens per sub-block
+  static constexpr int POS = kScanStaged / VEC;  // staging threads
+  static_assert(POS <= kScanThreads && SB * N == kScanStaged && kScanBlock % SB == 0, "staging split");
+  static constexpr int W = kVec ? 4 : VEC;       // raw 32-bit words per matrix
+  uint32_t rb[W], rc[W];
+  __device__ __forceinline__ void load(const ScanProblem& p, int64_t b, int64_t t0, int tid) {
+    const int e0 = tid * VEC, s = e0 / N, n0 = e0 % N;
+    const int64_t t = t0 + s;
+    const bool in = tid < POS && t < p.seqlen;
+    const int64_t o = (b * p.seqlen + (in ? t : 0)) * N + n0;
+    using S = typename E::storage;
+    if constexpr (kVec) {
+      uint4 vb = make_uint4(0, 0, 0, 0), vc = vb;
+      if (in) {
+        vb = *reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.B) + o);
+        vc = *reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.C) + o);
+      }
+      rb[0] = vb.x; rb[1] = vb.y; rb[2] = vb.z; rb[3] = vb.w;
+      rc[0] = vc.x; rc[1] = vc.y; rc[2] = vc.z; rc[3] = vc.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        rb[k] = in ? raw_bits(reinterpret_cast<const S*>(p.B)[o + k]) : 0u;
+        rc[k] = in ? raw_bits(reinterpret_cast<const S*>(p.C)[o + k]) : 0u;
+      }
+    }
+  }
+  // entry k of the thread's VEC as fp32
+  __device__ __forceinline__ float val(const uint32_t (&r)[W], int k) const {
+    if constexpr (kVec && E::kBytes == 2) return k & 1 ? bf16_hi(r[k / 2]) : bf16_lo(r[k / 2]);
+    else if constexpr (E::kBytes == 2) return __uint_as_float(r[k] << 16);
+    else return __uint_as_float(r[k]);
+  }
+  __device__ __forceinline__ void store(float4* buf, int tid) const {
+    if (tid >= POS) return;
+#pragma unroll
+    for (int k = 0; k < VEC; k += 2)
+      buf[(tid * VEC + k) / 2] = make_float4(val(rb, k), val(rc, k), val(rb, k + 1), val(rc, k + 1));
+  }
+};
+
+template <class E, int N, bool kVec>
+__global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProblem p, int dblocks) {
+  using St = ScanStage<E, N, kVec>;
   constexpr int NB = N / 64;               // waves per channel
   constexpr int CPB = kScanThreads / N;    // channels per workgroup
+  constexpr int SB = St::SB, NSB = kScanBlock / SB;
   __shared__ float ysum[CPB][NB][kScanBlock];
   // per wave: the block's (Delta_t, Delta_t x_t), read by every lane as one
   // broadcast LDS read per token (the vector ALU then does no lane broadcasts)
   __shared__ float2 du_s[kScanThreads / 64][kScanBlock];
-  const int wid = threadIdx.x / 64, lane = threadIdx.x % 64;
+  __shared__ float4 bc_s[2][kScanStaged / 2];  // (B, C) pairs of a sub-block, double buffered
+  const int tid = threadIdx.x;
+  const int wid = tid / 64, lane = tid % 64;
   const int cl = wid / NB, nb = wid % NB;  // channel within the workgroup, entry block
-  const int64_t chan = (int64_t)blockIdx.x * CPB + cl;  // (sequence, channel)
-  const bool active = chan < p.batch * p.D;
-  const int64_t b = active ? chan / p.D : 0;
-  const int64_t d = active ? chan % p.D : 0;
+  const int64_t b = blockIdx.x / dblocks;
+  const int64_t d = (int64_t)(blockIdx.x % dblocks) * CPB + cl;
+  const bool active = d < p.D;
+  const int64_t dc = active ? d : 0;
   const int n = nb * 64 + lane;
   const int64_t T = p.seqlen;
-  const float a2 = p.A[d * N + n] * kLog2e;  // exp(Delta A) = 2^(Delta A log2 e)
-  const float* drow = p.delta + (b * p.D + d) * T;
-  const int64_t xrow = (b * p.D + d) * T;
-  const int64_t bc0 = b * T * N + n;
+  const float a2 = p.A[dc * N + n] * kLog2e;  // exp(Delta A) = 2^(Delta A log2 e)
+  const float* drow = p.delta + (b * p.D + dc) * T;
+  const int64_t xrow = (b * p.D + dc) * T;
+  const float2* bcf = reinterpret_cast<const float2*>(&bc_s[0][0]);
   float h = 0.0f;
-  auto lane_val = [](float v, int s) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s)); };
   // y of one block: this wave's partial sums, then the channel's waves added
   auto finish = [&](float (&yp)[kScanBlock], int64_t t0, int nt) {
     const float ys = wave_sum_transpose(yp, lane);  // token t0 + lane, this wave's entries
@@ -132,79 +199,72 @@ __global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProble
       __syncthreads();
     }
   };
-  constexpr int SB = 16;  // tokens whose B and C are loaded together
-  const int64_t Tfull = T / kScanBlock * kScanBlock;
-  for (int64_t t0 = 0; t0 < Tfull; t0 += kScanBlock) {
-    // whole block: straight-line code; B and C one sub-block ahead
+  St st;
+  if (T > 0) {
+    st.load(p, b, 0, tid);
+    st.store(bc_s[0], tid);
+  }
+  __syncthreads();
+  // blocks of 64 tokens; a ragged last block runs whole on zero Delta, B and
+  // C past T (decay 1, no input: the state is unchanged) and stores nt outputs
+  int64_t sub = 0;  // the sub-block being computed: its pairs are in buffer sub & 1
+  for (int64_t t0 = 0; t0 < T; t0 += kScanBlock) {
+    const int nt = (int)(T - t0 < kScanBlock ? T - t0 : kScanBlock);
     {
-      const float dl = drow[t0 + lane];
-      du_s[wid][lane] = make_float2(dl, dl * ld_elem<E>(p.x, xrow + t0 + lane));
+      const bool in = active && lane < nt;
+      const float dl = in ? drow[t0 + lane] : 0.0f;
+      du_s[wid][lane] = make_float2(dl, in ? dl * ld_elem<E>(p.x, xrow + t0 + lane) : 0.0f);
     }
     float yp[kScanBlock];
-    float bq[SB], cq[SB];
 #pragma unroll
-    for (int s = 0; s < SB; ++s) {
-      bq[s] = ld_elem<E>(p.B, bc0 + (t0 + s) * N);
-      cq[s] = ld_elem<E>(p.C, bc0 + (t0 + s) * N);
-    }
-#pragma unroll
-    for (int sb = 0; sb < kScanBlock / SB; ++sb) {
-      float bn[SB], cn[SB];
-      if (sb + 1 < kScanBlock / SB) {
-#pragma unroll
-        for (int s = 0; s < SB; ++s) {
-          bn[s] = ld_elem<E>(p.B, bc0 + (t0 + (sb + 1) * SB + s) * N);
-          cn[s] = ld_elem<E>(p.C, bc0 + (t0 + (sb + 1) * SB + s) * N);
-        }
-      }
+    for (int j = 0; j < NSB; ++j, ++sub) {
+      // the next sub-block: staged within this block always (zeros past T),
+      // the next block's first only when it exists
+      const int64_t tn = t0 + (j + 1) * SB;
+      const bool next = j + 1 < NSB || tn < T;
+      if (next) st.load(p, b, tn, tid);
+      const float2* cur = bcf + (sub & 1) * kScanStaged;
 #pragma unroll
       for (int s = 0; s < SB; ++s) {
-        const int k = sb * SB + s;
+        const int k = j * SB + s;
         const float2 du = du_s[wid][k];  // (written above by this wave; LDS is in order per wave)
-        h = __builtin_amdgcn_exp2f(du.x * a2) * h + du.y * bq[s];
-        yp[k] = cq[s] * h;
+        const float2 bc = cur[s * N + n];
+        h = __builtin_amdgcn_exp2f(du.x * a2) * h + du.y * bc.x;
+        yp[k] = bc.y * h;
+        // formed here: left to the compiler, the products sink below the
+        // barriers to the block's end, every pair read kept live until then
+        asm volatile("" : "+v"(yp[k]));
       }
-      if (sb + 1 < kScanBlock / SB) {
-#pragma unroll
-        for (int s = 0; s < SB; ++s) bq[s] = bn[s], cq[s] = cn[s];
-      }
-    }
-    finish(yp, t0, kScanBlock);
-  }
-  if (Tfull < T) {
-    // ragged last block
-    const int64_t t0 = Tfull;
-    const int nt = (int)(T - t0);
-    const float dl = lane < nt ? drow[t0 + lane] : 0.0f;
-    const float ul = lane < nt ? dl * ld_elem<E>(p.x, xrow + t0 + lane) : 0.0f;
-    float yp[kScanBlock];
-#pragma unroll
-    for (int s = 0; s < kScanBlock; ++s) {
-      if (s < nt) {
-        const int64_t o = bc0 + (t0 + s) * N;
-        h = __builtin_amdgcn_exp2f(lane_val(dl, s) * a2) * h + lane_val(ul, s) * ld_elem<E>(p.B, o);
-        yp[s] = ld_elem<E>(p.C, o) * h;
-      } else {
-        yp[s] = 0.0f;
-      }
+      if (next) st.store(bc_s[(sub + 1) & 1], tid);
+      __syncthreads();
     }
     finish(yp, t0, nt);
   }
   if (active && p.final_state != nullptr) p.final_state[(b * p.D + d) * N + n] = h;
 }
 
+template <class E, int N>
+static hipError_t launch_scan_n(const ScanProblem& p, hipStream_t s) {
+  constexpr int CPB = kScanThreads / N;
+  const int64_t dblocks = (p.D + CPB - 1) / CPB;
+  const dim3 grid((unsigned)(p.batch * dblocks)), block(kScanThreads);
+  // 16-byte staging loads need 16-byte aligned B and C (every row offset is a
+  // multiple of N entries, itself a multiple of the vector)
+  if (((reinterpret_cast<uintptr_t>(p.B) | reinterpret_cast<uintptr_t>(p.C)) & 15) == 0)
+    hipLaunchKernelGGL((selective_scan_kernel<E, N, true>), grid, block, 0, s, p, (int)dblocks);
+  else
+    hipLaunchKernelGGL((selective_scan_kernel<E, N, false>), grid, block, 0, s, p, (int)dblocks);
+  return hipGetLastError();
+}
+
 template <class E>
 static hipError_t launch_scan_e(const ScanProblem& p, hipStream_t s) {
-  const int64_t chans = p.batch * p.D;
-  const int cpb = kScanThreads / p.N;
-  const dim3 grid((unsigned)((chans + cpb - 1) / cpb)), block(kScanThreads);
   switch (p.N) {
-    case 64: hipLaunchKernelGGL((selective_scan_kernel<E, 64>), grid, block, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((selective_scan_kernel<E, 128>), grid, block, 0, s, p); break;
-    case 256: hipLaunchKernelGGL((selective_scan_kernel<E, 256>), grid, block, 0, s, p); break;
+    case 64: return launch_scan_n<E, 64>(p, s);
+    case 128: return launch_scan_n<E, 128>(p, s);
+    case 256: return launch_scan_n<E, 256>(p, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_selective_scan(const ScanProblem& p, hipStream_t s) {

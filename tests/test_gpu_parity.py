@@ -814,21 +814,30 @@ def test_backward_full_2k(dev):
 
 
 # ------------------------------------------------ selective scan (comparator) ----
-def _scan_gpu(dev, x, delta, A, B, C, dtype):
+def _scan_gpu(dev, x, delta, A, B, C, dtype, offset=0):
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     cv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     xg = cv(x.transpose(0, 2, 1)).to(tdt)          # channel-major (b, D, T)
     dg = cv(delta.transpose(0, 2, 1))
-    y, fs = bd.ssd_selective_scan(xg, dg, cv(A), cv(B).to(tdt), cv(C).to(tdt))
+
+    def bc(a):  # B or C, starting `offset` elements into its allocation
+        t = cv(a).to(tdt)
+        if offset == 0:
+            return t
+        buf = torch.zeros(t.numel() + offset, dtype=tdt, device=dev)
+        v = buf[offset:].view(t.shape)
+        v.copy_(t)
+        return v
+    y, fs = bd.ssd_selective_scan(xg, dg, cv(A), bc(B), bc(C))
     torch.cuda.synchronize()
     return y.float().cpu().numpy().transpose(0, 2, 1), fs.cpu().numpy()
 
 
-def _scan_check(dev, b, T, D, N, dtype, seed, chans=None):
+def _scan_check(dev, b, T, D, N, dtype, seed, chans=None, offset=0):
     from mamba_ssd_layer_amd.workloads import scan_inputs
     x, delta, A, B, C = scan_inputs(b, T, D, N, dtype, seed)
-    log(f"[scan] b={b} T={T} D={D} N={N} {dtype} seed={seed}")
-    y, fs = _scan_gpu(dev, x, delta, A, B, C, dtype)
+    log(f"[scan] b={b} T={T} D={D} N={N} {dtype} seed={seed} B/C offset={offset}")
+    y, fs = _scan_gpu(dev, x, delta, A, B, C, dtype, offset)
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(fs))
     sel = slice(None) if chans is None else chans   # channels are independent: check a subset
     yr, fr = oracle.selective_scan(x[:, :, sel], delta[:, :, sel], A[sel], B, C)
@@ -847,6 +856,14 @@ def test_selective_scan_against_oracle(dev, b, T, D, N, dtype):
     """The comparator against its oracle: blocks of 64 tokens with a ragged
     tail, one to four waves per channel, a partial last workgroup."""
     _scan_check(dev, b, T, D, N, dtype, 90 + T)
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 128), ("f32", 64), ("bf16", 256)])
+def test_selective_scan_unaligned_b_c(dev, dtype, N):
+    """B and C one element past a 16-byte boundary (aligned to their element
+    only, which the interface allows): the kernel then stages them with
+    element loads instead of 16-byte vectors."""
+    _scan_check(dev, 2, 150, 9, N, dtype, 95, offset=1)
 
 
 def test_selective_scan_empty_sequence(dev):
