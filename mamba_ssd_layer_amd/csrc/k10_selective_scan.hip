@@ -15,32 +15,34 @@
 //
 // Design (gfx950): with a diagonal transition every state entry has its own
 // decay, so each (token, channel, entry) costs one exp on the vector ALU and
-// nothing maps to the matrix cores.  One wave per (sequence, channel, block of
-// 64 entries); lane n carries h[n] through all T tokens (one exp per element,
-// the least any scan does; a chunk-parallel scan would need two).  A
-// workgroup of 16 waves holds 1024 / N channels of one sequence, which share
-// B and C: each sub-block of 4096 / N tokens of them is loaded once by the
-// workgroup (16-byte vectors), converted to fp32 and stored in LDS as
-// (B_t[n], C_t[n]) pairs, double buffered (the next sub-block's loads in
-// flight during this one's products), and each lane reads its pair with one
-// 8-byte LDS read: no global load and no conversion per element.  Tokens are
-// processed in blocks of 64: the wave loads the block's Delta and x (channel-
-// major layout, one 64-token row each) and puts (Delta, Delta x) in LDS, where
-// every lane reads token s's pair with one broadcast read.  Each lane keeps
-// its C_t h_t for the 64 tokens in registers; a butterfly of 63 lane
-// exchanges (none through LDS) then sums them over the lanes, leaving token s's
-// partial sum in lane s, and the waves of one channel (N / 64 of them) add
-// theirs in LDS.  Per element that leaves Delta A, the exp, the input term,
-// the state update and C h on the vector ALU, 2.5 butterfly operations, and
-// 8 bytes of LDS reads (a transposed sum through LDS instead of the butterfly,
-// or the pairs kept as bf16, each measured slower: the kernel is bound by both).
+// nothing maps to the matrix cores.  One wave per (sequence, channel); lane l
+// carries the N / 64 entries n = l, l + 64, ... through all T tokens (one exp
+// per element, the least any scan does; a chunk-parallel scan would need two)
+// and forms its part of C_t h_t over them.  A workgroup of 8 waves holds 8
+// channels of one sequence, which share B and C: each sub-block of 4096 / N
+// tokens of them is loaded once by the workgroup (16-byte vectors), converted
+// to fp32 and stored in LDS as (B_t[n], C_t[n]) pairs, double buffered (the
+// next sub-block's loads in flight during this one's products), and each lane
+// reads a pair with one 8-byte LDS read: no global load and no conversion per
+// element.  Tokens are processed in blocks of 64: the wave loads the block's
+// Delta and x (channel-major layout, one 64-token row each) and puts
+// (Delta, Delta x) in LDS, where every lane reads token s's pair with one
+// broadcast read.  Each lane keeps its part of C_t h_t for the 64 tokens in
+// registers; a butterfly of 63 lane exchanges (none through LDS) then sums
+// them over the lanes, leaving token s's y in lane s.  Per element that leaves
+// Delta A, the exp, the input term, the state update and C h on the vector
+// ALU, 2.5 / (N / 64) butterfly operations, and 8 bytes of LDS reads.
+// Measured slower and not kept: one wave per 64 entries (16 waves of 8
+// channels per workgroup, the waves of a channel adding their parts in LDS),
+// a transposed sum through LDS instead of the butterfly (LDS traffic), the
+// staged pairs kept as bf16 (two conversions per element).
 // Layouts: x, Delta, y (b, D, T) channel-major; A (D, N); B, C (b, T, N);
 // final state (b, D, N) fp32.
 #include "ssd_device.hpp"
 
 namespace ssd {
 
-constexpr int kScanThreads = 1024;  // 16 waves
+constexpr int kScanThreads = 512;   // 8 waves
 constexpr int kScanBlock = 64;     // tokens per block
 constexpr int kScanStaged = 4096;  // (token, entry) pairs of B and C staged at once
 
@@ -105,9 +107,9 @@ __device__ __forceinline__ float wave_sum_transpose(float (&v)[kScanBlock], int 
 // Staged B and C: the workgroup's channels share one batch, so each sub-block of
 // SB tokens is loaded once, converted to fp32 and stored as (B_t[n], C_t[n])
 // pairs in LDS; every lane then reads its pair with one 8-byte LDS read.  Each
-// thread stages VEC consecutive entries of one token (a 16-byte vector of B
-// and one of C when kVec, else element loads), written as two pairs per
-// 16-byte LDS store.  The loads keep raw bits (converted at the store, so a
+// thread stages RPT runs of VEC consecutive entries of one token (a 16-byte
+// vector of B and one of C when kVec, else element loads), each written as two
+// pairs per 16-byte LDS store.  The loads keep raw bits (converted at the store, so a
 // load in flight is not waited for before the products it overlaps); tokens
 // at or past T stage zeros.
 __device__ __forceinline__ uint32_t raw_bits(uint16_t v) { return v; }
@@ -115,90 +117,80 @@ __device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v
 
 template <class E, int N, bool kVec>
 struct ScanStage {
-  static constexpr int VEC = 16 / E::kBytes;     // entries per thread
+  static constexpr int VEC = 16 / E::kBytes;     // entries per vector
   static constexpr int SB = kScanStaged / N;     // tokens per sub-block
-  static constexpr int POS = kScanStaged / VEC;  // staging threads
-  static_assert(POS <= kScanThreads && SB * N == kScanStaged && kScanBlock % SB == 0, "staging split");
+  static constexpr int POS = kScanStaged / VEC;  // vectors per sub-block
+  static constexpr int RPT = (POS + kScanThreads - 1) / kScanThreads;  // per thread
+  static_assert(POS % kScanThreads == 0 || POS < kScanThreads, "staging split");
+  static_assert(SB * N == kScanStaged && kScanBlock % SB == 0, "staging split");
   static constexpr int W = kVec ? 4 : VEC;       // raw 32-bit words per matrix
-  uint32_t rb[W], rc[W];
+  uint32_t rb[RPT][W], rc[RPT][W];
   __device__ __forceinline__ void load(const ScanProblem& p, int64_t b, int64_t t0, int tid) {
-    const int e0 = tid * VEC, s = e0 / N, n0 = e0 % N;
-    const int64_t t = t0 + s;
-    const bool in = tid < POS && t < p.seqlen;
-    const int64_t o = (b * p.seqlen + (in ? t : 0)) * N + n0;
     using S = typename E::storage;
-    if constexpr (kVec) {
-      uint4 vb = make_uint4(0, 0, 0, 0), vc = vb;
-      if (in) {
-        vb = *reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.B) + o);
-        vc = *reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.C) + o);
-      }
-      rb[0] = vb.x; rb[1] = vb.y; rb[2] = vb.z; rb[3] = vb.w;
-      rc[0] = vc.x; rc[1] = vc.y; rc[2] = vc.z; rc[3] = vc.w;
-    } else {
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) {
-        rb[k] = in ? raw_bits(reinterpret_cast<const S*>(p.B)[o + k]) : 0u;
-        rc[k] = in ? raw_bits(reinterpret_cast<const S*>(p.C)[o + k]) : 0u;
+    for (int r = 0; r < RPT; ++r) {
+      const int v = tid + r * kScanThreads;
+      const int e0 = v * VEC, s = e0 / N, n0 = e0 % N;
+      const int64_t t = t0 + s;
+      const bool in = v < POS && t < p.seqlen;
+      const int64_t o = (b * p.seqlen + (in ? t : 0)) * N + n0;
+      if constexpr (kVec) {
+        uint4 vb = make_uint4(0, 0, 0, 0), vc = vb;
+        if (in) {
+          vb = *reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.B) + o);
+          vc = *reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.C) + o);
+        }
+        rb[r][0] = vb.x; rb[r][1] = vb.y; rb[r][2] = vb.z; rb[r][3] = vb.w;
+        rc[r][0] = vc.x; rc[r][1] = vc.y; rc[r][2] = vc.z; rc[r][3] = vc.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          rb[r][k] = in ? raw_bits(reinterpret_cast<const S*>(p.B)[o + k]) : 0u;
+          rc[r][k] = in ? raw_bits(reinterpret_cast<const S*>(p.C)[o + k]) : 0u;
+        }
       }
     }
   }
-  // entry k of the thread's VEC as fp32
   __device__ __forceinline__ float val(const uint32_t (&r)[W], int k) const {
     if constexpr (kVec && E::kBytes == 2) return k & 1 ? bf16_hi(r[k / 2]) : bf16_lo(r[k / 2]);
     else if constexpr (E::kBytes == 2) return __uint_as_float(r[k] << 16);
     else return __uint_as_float(r[k]);
   }
   __device__ __forceinline__ void store(float4* buf, int tid) const {
-    if (tid >= POS) return;
 #pragma unroll
-    for (int k = 0; k < VEC; k += 2)
-      buf[(tid * VEC + k) / 2] = make_float4(val(rb, k), val(rc, k), val(rb, k + 1), val(rc, k + 1));
+    for (int r = 0; r < RPT; ++r) {
+      const int v = tid + r * kScanThreads;
+      if (v >= POS) break;
+#pragma unroll
+      for (int k = 0; k < VEC; k += 2)
+        buf[(v * VEC + k) / 2] = make_float4(val(rb[r], k), val(rc[r], k), val(rb[r], k + 1), val(rc[r], k + 1));
+    }
   }
 };
 
 template <class E, int N, bool kVec>
 __global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProblem p, int dblocks) {
   using St = ScanStage<E, N, kVec>;
-  constexpr int NB = N / 64;               // waves per channel
-  constexpr int CPB = kScanThreads / N;    // channels per workgroup
+  constexpr int EN = N / 64;                 // state entries per lane
+  constexpr int CPB = kScanThreads / 64;     // channels per workgroup, one wave each
   constexpr int SB = St::SB, NSB = kScanBlock / SB;
-  __shared__ float ysum[CPB][NB][kScanBlock];
   // per wave: the block's (Delta_t, Delta_t x_t), read by every lane as one
   // broadcast LDS read per token (the vector ALU then does no lane broadcasts)
-  __shared__ float2 du_s[kScanThreads / 64][kScanBlock];
+  __shared__ float2 du_s[CPB][kScanBlock];
   __shared__ float4 bc_s[2][kScanStaged / 2];  // (B, C) pairs of a sub-block, double buffered
   const int tid = threadIdx.x;
   const int wid = tid / 64, lane = tid % 64;
-  const int cl = wid / NB, nb = wid % NB;  // channel within the workgroup, entry block
   const int64_t b = blockIdx.x / dblocks;
-  const int64_t d = (int64_t)(blockIdx.x % dblocks) * CPB + cl;
+  const int64_t d = (int64_t)(blockIdx.x % dblocks) * CPB + wid;
   const bool active = d < p.D;
   const int64_t dc = active ? d : 0;
-  const int n = nb * 64 + lane;
   const int64_t T = p.seqlen;
-  const float a2 = p.A[dc * N + n] * kLog2e;  // exp(Delta A) = 2^(Delta A log2 e)
+  float a2[EN], h[EN];
+#pragma unroll
+  for (int e = 0; e < EN; ++e) a2[e] = p.A[dc * N + e * 64 + lane] * kLog2e, h[e] = 0.0f;
   const float* drow = p.delta + (b * p.D + dc) * T;
   const int64_t xrow = (b * p.D + dc) * T;
   const float2* bcf = reinterpret_cast<const float2*>(&bc_s[0][0]);
-  float h = 0.0f;
-  // y of one block: this wave's partial sums, then the channel's waves added
-  auto finish = [&](float (&yp)[kScanBlock], int64_t t0, int nt) {
-    const float ys = wave_sum_transpose(yp, lane);  // token t0 + lane, this wave's entries
-    if constexpr (NB == 1) {
-      if (active && lane < nt) st_y<E>(p.y, xrow + t0 + lane, ys);
-    } else {
-      ysum[cl][nb][lane] = ys;
-      __syncthreads();
-      if (nb == 0 && active && lane < nt) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NB; ++k) acc += ysum[cl][k][lane];
-        st_y<E>(p.y, xrow + t0 + lane, acc);
-      }
-      __syncthreads();
-    }
-  };
   St st;
   if (T > 0) {
     st.load(p, b, 0, tid);
@@ -228,9 +220,14 @@ __global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProble
       for (int s = 0; s < SB; ++s) {
         const int k = j * SB + s;
         const float2 du = du_s[wid][k];  // (written above by this wave; LDS is in order per wave)
-        const float2 bc = cur[s * N + n];
-        h = __builtin_amdgcn_exp2f(du.x * a2) * h + du.y * bc.x;
-        yp[k] = bc.y * h;
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EN; ++e) {
+          const float2 bc = cur[s * N + e * 64 + lane];
+          h[e] = __builtin_amdgcn_exp2f(du.x * a2[e]) * h[e] + du.y * bc.x;
+          acc = e == 0 ? bc.y * h[e] : acc + bc.y * h[e];
+        }
+        yp[k] = acc;
         // formed here: left to the compiler, the products sink below the
         // barriers to the block's end, every pair read kept live until then
         asm volatile("" : "+v"(yp[k]));
@@ -238,14 +235,17 @@ __global__ __launch_bounds__(kScanThreads) void selective_scan_kernel(ScanProble
       if (next) st.store(bc_s[(sub + 1) & 1], tid);
       __syncthreads();
     }
-    finish(yp, t0, nt);
+    const float ys = wave_sum_transpose(yp, lane);  // token t0 + lane
+    if (active && lane < nt) st_y<E>(p.y, xrow + t0 + lane, ys);
   }
-  if (active && p.final_state != nullptr) p.final_state[(b * p.D + d) * N + n] = h;
+  if (active && p.final_state != nullptr)
+#pragma unroll
+    for (int e = 0; e < EN; ++e) p.final_state[(b * p.D + d) * N + e * 64 + lane] = h[e];
 }
 
 template <class E, int N>
 static hipError_t launch_scan_n(const ScanProblem& p, hipStream_t s) {
-  constexpr int CPB = kScanThreads / N;
+  constexpr int CPB = kScanThreads / 64;
   const int64_t dblocks = (p.D + CPB - 1) / CPB;
   const dim3 grid((unsigned)(p.batch * dblocks)), block(kScanThreads);
   // 16-byte staging loads need 16-byte aligned B and C (every row offset is a

@@ -854,7 +854,7 @@ def _scan_check(dev, b, T, D, N, dtype, seed, chans=None, offset=0):
                                            (1, 1, 4, 64, "bf16")])
 def test_selective_scan_against_oracle(dev, b, T, D, N, dtype):
     """The comparator against its oracle: blocks of 64 tokens with a ragged
-    tail, one to four waves per channel, a partial last workgroup."""
+    tail, one to four state entries per lane, a partial last workgroup."""
     _scan_check(dev, b, T, D, N, dtype, 90 + T)
 
 
